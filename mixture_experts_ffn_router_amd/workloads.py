@@ -1,0 +1,175 @@
+"""Seeded synthetic workloads for the fused MoE forward.
+
+This module only draws random inputs of the shapes and distributions the
+workloads name; it holds none of the method's arithmetic.  The HIP path and
+the CPU oracle both consume the tensors it returns, already rounded to
+their storage types, so parity never depends on the random generator.
+
+Distribution notation: N(mu, v) takes the second argument as the variance
+(fan-in initialisation N(0, 1/H) means standard deviation 1/sqrt(H)).
+
+Two inputs are upstream of the fused MoE rather than part of it and are
+prepared here with library calls only:
+  * fp8 weights: per-output-channel scale amax/448 and a cast through
+    torch.float8_e4m3fn (weights are quantised once, at load time);
+  * the batched format's token layout: the dispatcher that produced it ran
+    a top-k of (logits + per-expert offset) (torch.topk) and packed each
+    expert's tokens in ascending token order.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class MoeConfig:
+    name: str
+    M: int
+    H: int
+    I: int
+    E: int
+    top_k: int
+    fmt: str = "contiguous"          # "contiguous" (M,K) or "batched" (E,max_tokens,K)
+    act: str = "bf16"                # activation storage: f32 | bf16
+    weight: str = "bf16"             # f32 | bf16 | fp8 (per-output-channel scales)
+    scoring: str = "softmax"         # softmax | sigmoid
+    renormalize: bool = True
+    group_count: int = 1
+    k_group: int = 1
+    group_select_mode: int = 0
+    routed_scaling_factor: float = 1.0
+    bias: bool = False
+    expert_bias_var: float = 0.0     # per-expert logit offset ~ N(0, var)
+    zipf_s: float = 0.0              # per-expert logit offset -s*ln(rank+1)
+    max_tokens: int = 0              # batched: rows per expert slab (0 = M)
+
+    @property
+    def logits_dtype(self) -> str:
+        return "f32" if self.act == "f32" else "bf16"
+
+    @property
+    def out_dtype(self) -> str:
+        return "f32" if self.act == "f32" else "bf16"
+
+    def routed_rows(self) -> int:
+        return self.M * self.top_k
+
+    def flops(self, valid_rows: Optional[int] = None) -> float:
+        """Algorithmic FLOPs of the two expert contractions."""
+        rows = self.routed_rows() if valid_rows is None else valid_rows
+        return 2.0 * rows * 3.0 * self.H * self.I
+
+    def scaled(self, **kw) -> "MoeConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads.  Shapes follow the pages' examples: Mixtral-like
+# (MindIE-SD single-card example: H 4096, I 14336, E 8, top-2) and
+# DeepSeek-V3-like (MoonEP notation table: H 7168, H' 2048, E 256, top-8).
+TINY_F32 = MoeConfig("tiny_f32", M=16, H=64, I=128, E=8, top_k=2, act="f32", weight="f32")
+MIXTRAL_PREFILL = MoeConfig("mixtral_prefill_bf16", M=512, H=4096, I=14336, E=8, top_k=2)
+DECODE_SMALL_EXPERTS = MoeConfig("decode_e128_bf16", M=32, H=2048, I=768, E=128, top_k=8)
+DEEPSEEK_GROUPED = MoeConfig("deepseek_grouped_sigmoid_bf16", M=4096, H=7168, I=2048, E=256,
+                             top_k=8, scoring="sigmoid", renormalize=False, group_count=8,
+                             k_group=4, group_select_mode=1, routed_scaling_factor=2.5,
+                             bias=True, expert_bias_var=0.5)
+BATCHED_FP8 = MoeConfig("batched_fp8_skewed", M=8192, H=2048, I=1408, E=64, top_k=6,
+                        fmt="batched", weight="fp8", renormalize=False, zipf_s=1.1)
+
+CONFIGS = [TINY_F32, MIXTRAL_PREFILL, DECODE_SMALL_EXPERTS, DEEPSEEK_GROUPED, BATCHED_FP8]
+BY_NAME = {c.name: c for c in CONFIGS}
+
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _randn(shape, gen, device, std=1.0, dtype=torch.float32):
+    t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(dtype)
+
+
+def quantize_weight_fp8(w: torch.Tensor):
+    """Per-output-channel (last dim) fp8 e4m3fn codes + float32 scales.
+    w: [E, K, N] float32 -> (codes float8_e4m3fn [E, K, N], scale [E, N])."""
+    amax = w.abs().amax(dim=1)                                   # [E, N]
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    codes = (w / scale[:, None, :]).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return codes, scale.to(torch.float32)
+
+
+def make_inputs(cfg: MoeConfig, seed: int, device="cpu") -> dict:
+    """Draws every input of one forward.  Order of draws: hidden, logits
+    (+ offsets), w13, w2, w13_bias, w2_bias."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    M, H, I, E = cfg.M, cfg.H, cfg.I, cfg.E
+    act_dt = _TORCH_DT[cfg.act]
+    out = {"cfg": cfg, "seed": seed}
+
+    hidden = _randn((M, H), gen, device, dtype=act_dt)
+    logits = _randn((M, E), gen, device)
+    if cfg.expert_bias_var > 0:
+        logits += _randn((E,), gen, device, std=math.sqrt(cfg.expert_bias_var))[None, :]
+    if cfg.zipf_s > 0:
+        perm = torch.randperm(E, generator=gen, device=device)
+        offset = -cfg.zipf_s * torch.log(perm.to(torch.float32) + 1.0)
+        logits += offset[None, :]
+    logits = logits.to(_TORCH_DT[cfg.logits_dtype])
+
+    w_dt = torch.float32 if cfg.weight == "fp8" else _TORCH_DT[cfg.weight]
+    w13 = _randn((E, H, 2 * I), gen, device, std=1.0 / math.sqrt(H), dtype=w_dt)
+    w2 = _randn((E, I, H), gen, device, std=1.0 / math.sqrt(I), dtype=w_dt)
+    if cfg.weight == "fp8":
+        out["w13"], out["w13_scale"] = quantize_weight_fp8(w13)
+        del w13
+        out["w2"], out["w2_scale"] = quantize_weight_fp8(w2)
+        del w2
+    else:
+        out["w13"], out["w2"] = w13, w2
+    if cfg.bias:
+        bdt = act_dt
+        out["w13_bias"] = _randn((E, 2 * I), gen, device, std=0.1, dtype=bdt)
+        out["w2_bias"] = _randn((E, H), gen, device, std=0.1, dtype=bdt)
+    else:
+        out["w13_bias"] = out["w2_bias"] = None
+
+    if cfg.fmt == "batched":
+        out.update(_batched_layout(cfg, hidden, logits))
+    else:
+        out["hidden"] = hidden
+        out["logits"] = logits
+    return out
+
+
+def _batched_layout(cfg: MoeConfig, hidden: torch.Tensor, logits: torch.Tensor) -> dict:
+    """Packs the tokens the way a dispatcher hands them to batched experts:
+    slab e holds, in ascending token order, the tokens whose top-k (of the
+    offset logits) contains e.  Rows past expert_num_tokens[e] are NaN."""
+    E, M, K = cfg.E, cfg.M, cfg.top_k
+    T = cfg.max_tokens or M
+    lg = logits.float()
+    ids = torch.topk(lg, K, dim=-1).indices.to(torch.int32)             # [M, K]
+    probs = torch.softmax(lg, dim=-1)
+    w = torch.gather(probs, 1, ids.long())
+    if cfg.renormalize:
+        w = w / w.sum(-1, keepdim=True)
+    w = (w * cfg.routed_scaling_factor).to(torch.float32)
+    flat = ids.reshape(-1).long()
+    order = torch.sort(flat, stable=True).indices                       # routed items by expert
+    counts = torch.bincount(flat, minlength=E)
+    starts = torch.cumsum(counts, 0) - counts
+    e_sorted = flat[order]
+    slot = torch.arange(flat.numel(), device=flat.device) - starts[e_sorted]
+    assert int(counts.max()) <= T, "max_tokens too small for this routing"
+    xb = torch.full((E, T, cfg.H), float("nan"), dtype=hidden.dtype, device=hidden.device)
+    xb[e_sorted, slot] = hidden[order // K]
+    token_map = torch.empty(M * K, dtype=torch.int32, device=flat.device)
+    token_map[order] = (e_sorted * T + slot).to(torch.int32)
+    return {"hidden": xb, "expert_num_tokens": counts.to(torch.int32),
+            "token_map": token_map.view(M, K), "token_map_w": w,
+            "tokens": hidden, "topk_ids": ids, "max_tokens": T}

@@ -1,0 +1,273 @@
+"""CPU oracle for the fused MoE forward -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library
+and its Python binding) never imports, links or calls it, and shares no
+code with it.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C, double precision);
+this module only builds it with gcc and marshals numpy / torch CPU arrays.
+Each C function's header comment cites the passage of the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+F32, BF16, FP8 = 0, 1, 2
+SOFTMAX, SIGMOID = 0, 1
+_DT = {"f32": F32, "bf16": BF16, "fp8": FP8}
+
+
+def build() -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+           "-shared", "-std=c11", "-Wall", "-o", _LIB + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+class _Routing(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("scoring", ctypes.c_int32), ("renormalize", ctypes.c_int32),
+                ("group_count", ctypes.c_int32), ("k_group", ctypes.c_int32),
+                ("group_select_mode", ctypes.c_int32), ("logits_dtype", ctypes.c_int32),
+                ("routed_scaling_factor", ctypes.c_double)]
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("w_dtype", ctypes.c_int32), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+                ("bias_dtype", ctypes.c_int32), ("w13_bias", ctypes.c_void_p),
+                ("w2_bias", ctypes.c_void_p), ("requant_z", ctypes.c_int32)]
+
+
+class _Acts(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("data", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p), ("quantize", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.oracle_fp8_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_fp8_decode.restype = ctypes.c_double
+    lib.oracle_fp8_encode.argtypes = [ctypes.c_float]
+    lib.oracle_fp8_encode.restype = ctypes.c_uint8
+    lib.oracle_quant_row_fp8.argtypes = [P, i64, P, P]
+    lib.oracle_quant_row_fp8.restype = None
+    lib.oracle_route.argtypes = [ctypes.POINTER(_Routing), P, i64, P, P]
+    lib.oracle_route.restype = ctypes.c_int
+    lib.oracle_group_keys.argtypes = [ctypes.POINTER(_Routing), P, i64, P]
+    lib.oracle_group_keys.restype = ctypes.c_int
+    lib.oracle_align.argtypes = [P, i64, i32, i32, P, P, i64, P, i64, P]
+    lib.oracle_align.restype = ctypes.c_int
+    lib.oracle_forward_tokens.argtypes = [ctypes.POINTER(_Experts), ctypes.POINTER(_Acts), i32,
+                                          P, P, P, i64, P, i32]
+    lib.oracle_forward_tokens.restype = ctypes.c_int
+    lib.oracle_expert_rows.argtypes = [ctypes.POINTER(_Experts), ctypes.POINTER(_Acts), P, P,
+                                       i64, P, i32]
+    lib.oracle_expert_rows.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- marshalling
+
+def _np(x, want=None):
+    """torch (CPU) or numpy -> contiguous numpy, bf16 as uint16 bits, fp8 as uint8 codes."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if x.dtype == torch.bfloat16:
+                x = x.view(torch.int16).numpy().view(np.uint16)
+            elif x.dtype == torch.float8_e4m3fn:
+                x = x.view(torch.uint8).numpy()
+            else:
+                x = x.numpy()
+    except ImportError:
+        pass
+    x = np.ascontiguousarray(x)
+    if want is not None:
+        x = np.ascontiguousarray(x, dtype=want)
+    return x
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.uint8:
+        return FP8
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError(f"unsupported oracle input dtype {a.dtype}")
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+# ---------------------------------------------------------------- scalar formats
+
+def fp8_decode(codes) -> np.ndarray:
+    lib = load()
+    c = _np(codes, np.uint8)
+    return np.array([lib.oracle_fp8_decode(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def fp8_encode(x) -> np.ndarray:
+    lib = load()
+    a = _np(x, np.float32)
+    return np.array([lib.oracle_fp8_encode(float(v)) for v in a.ravel()],
+                    dtype=np.uint8).reshape(a.shape)
+
+
+def quant_rows_fp8(x):
+    """Per-row dynamic fp8: returns (codes uint8 [R, H], scale float32 [R])."""
+    lib = load()
+    a = _np(x, np.float32)
+    R, H = a.shape
+    q = np.empty((R, H), np.uint8)
+    s = np.empty(R, np.float32)
+    for r in range(R):
+        row = np.ascontiguousarray(a[r])
+        lib.oracle_quant_row_fp8(row.ctypes.data, H, q[r].ctypes.data, s[r:].ctypes.data)
+    return q, s
+
+
+# ---------------------------------------------------------------- routing / align
+
+def _routing(E, top_k, scoring, renormalize, group_count, k_group, group_select_mode, rsf,
+             logits_dtype):
+    return _Routing(E, top_k, SIGMOID if scoring == "sigmoid" else SOFTMAX, int(renormalize),
+                    group_count, k_group, group_select_mode, logits_dtype, float(rsf))
+
+
+def route(logits, top_k, scoring="softmax", renormalize=False, group_count=1, k_group=1,
+          group_select_mode=0, routed_scaling_factor=1.0):
+    """Returns (topk_ids int32 [M, k], topk_weights float64 [M, k])."""
+    lib = load()
+    lg = _np(logits)
+    M, E = lg.shape
+    R = _routing(E, top_k, scoring, renormalize, group_count, k_group, group_select_mode,
+                 routed_scaling_factor, _dtype_code(lg))
+    ids = np.empty((M, top_k), np.int32)
+    w = np.empty((M, top_k), np.float64)
+    rc = lib.oracle_route(ctypes.byref(R), lg.ctypes.data, M, ids.ctypes.data, w.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_route rejected the routing parameters")
+    return ids, w
+
+
+def group_keys(logits, group_count, group_select_mode, scoring="softmax"):
+    lib = load()
+    lg = _np(logits)
+    M, E = lg.shape
+    R = _routing(E, 1, scoring, 0, group_count, 1, group_select_mode, 1.0, _dtype_code(lg))
+    keys = np.empty((M, group_count), np.float32)
+    lib.oracle_group_keys(ctypes.byref(R), lg.ctypes.data, M, keys.ctypes.data)
+    return keys
+
+
+def align(topk_ids, E, block_m):
+    """Returns (counts [E], sorted_ids [num_post_padded], expert_ids [npp/BM], npp)."""
+    lib = load()
+    ids = _np(topk_ids, np.int32).ravel()
+    Mk = ids.size
+    cap = Mk + E * (block_m - 1)
+    counts = np.empty(E, np.int32)
+    sorted_ids = np.empty(max(cap, 1), np.int32)
+    expert_ids = np.empty(max(cap // block_m + 1, 1), np.int32)
+    npp = np.zeros(1, np.int32)
+    rc = lib.oracle_align(ids.ctypes.data, Mk, E, block_m, counts.ctypes.data,
+                          sorted_ids.ctypes.data, cap, expert_ids.ctypes.data,
+                          expert_ids.size, npp.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_align: id out of range")
+    n = int(npp[0])
+    return counts, sorted_ids[:n].copy(), expert_ids[: n // block_m].copy(), n
+
+
+# ---------------------------------------------------------------- expert FFN
+
+class Experts:
+    """Keeps the numpy views alive while the C side holds raw pointers."""
+
+    def __init__(self, w13, w2, w13_scale=None, w2_scale=None, w13_bias=None, w2_bias=None,
+                 requant_z=False):
+        self.w13, self.w2 = _np(w13), _np(w2)
+        E, H, N = self.w13.shape
+        I = N // 2
+        assert self.w2.shape == (E, I, H), (self.w2.shape, (E, I, H))
+        self.w13_scale = None if w13_scale is None else _np(w13_scale, np.float32)
+        self.w2_scale = None if w2_scale is None else _np(w2_scale, np.float32)
+        self.b13 = None if w13_bias is None else _np(w13_bias)
+        self.b2 = None if w2_bias is None else _np(w2_bias)
+        bias_dt = F32
+        for b in (self.b13, self.b2):
+            if b is not None:
+                bias_dt = _dtype_code(b)
+        wd = _dtype_code(self.w13)
+        if wd == FP8:
+            assert self.w13_scale is not None and self.w2_scale is not None
+        self.s = _Experts(H, I, E, wd, _ptr(self.w13), _ptr(self.w2), _ptr(self.w13_scale),
+                          _ptr(self.w2_scale), bias_dt, _ptr(self.b13), _ptr(self.b2),
+                          int(requant_z))
+        self.H, self.I, self.E = H, I, E
+
+
+class Acts:
+    def __init__(self, data, scale=None, quantize=False):
+        self.data = _np(data)
+        self.H = self.data.shape[-1]
+        self.data = self.data.reshape(-1, self.H)
+        self.scale = None if scale is None else _np(scale, np.float32).ravel()
+        dt = _dtype_code(self.data)
+        if dt == FP8:
+            assert self.scale is not None
+        self.s = _Acts(dt, _ptr(self.data), _ptr(self.scale), int(quantize))
+
+
+def forward_tokens(experts: Experts, acts: Acts, topk_ids, topk_w, tokens=None, nthreads=0):
+    """y[n] = sum_j w[t,j] f_{id[t,j]}(x_t) for t = tokens[n]; float64 [n, H].
+    Returns (y, threads_used)."""
+    lib = load()
+    ids = _np(topk_ids, np.int32)
+    w = _np(topk_w, np.float64)
+    M, K = ids.shape
+    tok = np.arange(M, dtype=np.int64) if tokens is None else _np(tokens, np.int64).ravel()
+    y = np.empty((tok.size, experts.H), np.float64)
+    used = lib.oracle_forward_tokens(ctypes.byref(experts.s), ctypes.byref(acts.s), K,
+                                     ids.ctypes.data, w.ctypes.data, tok.ctypes.data, tok.size,
+                                     y.ctypes.data, int(nthreads))
+    return y, used
+
+
+def expert_rows(experts: Experts, acts: Acts, rows, expert_of_row, nthreads=0):
+    """out[n] = f_{expert_of_row[n]}(activation row rows[n]); float64 [n, H]."""
+    lib = load()
+    r = _np(rows, np.int64).ravel()
+    e = _np(expert_of_row, np.int32).ravel()
+    assert r.size == e.size
+    out = np.empty((r.size, experts.H), np.float64)
+    used = lib.oracle_expert_rows(ctypes.byref(experts.s), ctypes.byref(acts.s), r.ctypes.data,
+                                  e.ctypes.data, r.size, out.ctypes.data, int(nthreads))
+    return out, used

@@ -1,0 +1,585 @@
+/*
+ * moe_oracle.c -- plain, slow CPU definition of the fused mixture-of-experts
+ * FFN forward.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or helper with the HIP library; it is the yardstick the HIP
+ * path is measured against, never a fallback for it.
+ *
+ * What it computes (sources are the five pages on fused MoE):
+ *   - routed-item form, FlagGems "fused_moe.py" walkthrough, sec. 1.2
+ *     (h_r = W1^T x + b1, z_r = phi(h_r), o_r = W2^T z_r + b2,
+ *      y_t = sum_{r: t(r)=t} a(r) o_r), with the gated SiLU phi that the
+ *     fused gate/up weight of the MindIE-SD "Fused MoE" page (parameter
+ *     table, w13_weight [E, H, 2I]) implies: phi(h) = SiLU(h[:I]) * h[I:];
+ *   - routing: MindIE-SD "Fused MoE" page, "routing selection" section and
+ *     parameter table (softmax | sigmoid, grouped selection by group max or
+ *     top-2 sum, renormalize, routed_scaling_factor); its custom routing
+ *     example (softmax -> top-k -> optional divide by the sum);
+ *   - align: FlagGems walkthrough, "moe_align_block_size" section (sort
+ *     routed items by expert, pad each expert to BLOCK_SIZE_M), stable in
+ *     the sense of the MoonEP page's build_permutation (a stable argsort);
+ *   - fp8: FlagGems walkthrough, "FP8 W8A8" section (per-channel weight
+ *     scales, per-token and block-wise activation scales).
+ *
+ * Precision: every value-path sum and product is taken in double from the
+ * exactly-upcast inputs (bf16 and fp8 codes convert to double exactly).
+ * Where a float decides an integer (an fp8 code, the grouped-routing key),
+ * the decision is made in float32, the precision the device kernels use.
+ * Expert selection compares logits, which is exact because softmax and the
+ * sigmoid are strictly increasing.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2 };
+enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
+
+/* ------------------------------------------------------------------ */
+/* scalar formats                                                      */
+/* ------------------------------------------------------------------ */
+
+static double bf16_bits_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16; /* bf16 is the top half of a float32 */
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* OCP 8-bit float E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits,
+ * no infinities, S.1111.111 is NaN, largest finite magnitude 448. */
+double oracle_fp8_decode(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);          /* (m/8) * 2^-6          */
+    else
+        v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7)   */
+    return s ? -v : v;
+}
+
+/* Round-to-nearest-even onto E4M3FN, saturating at +-448.  Done the plain
+ * way: scan the 127 non-negative finite codes for the nearest value; on an
+ * exact tie take the code with an even mantissa (its lowest bit clear). */
+uint8_t oracle_fp8_encode(float x)
+{
+    uint8_t sign, best = 0;
+    double a, bestd = INFINITY;
+    if (isnan(x))
+        return 0x7F;
+    sign = signbit(x) ? 0x80 : 0x00;
+    a = fabs((double)x);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double d = fabs(oracle_fp8_decode((uint8_t)c) - a);
+        if (d < bestd || (d == bestd && (c & 1) == 0 && (best & 1) == 1)) {
+            bestd = d;
+            best = (uint8_t)c;
+        }
+    }
+    return sign | best;
+}
+
+static double fp8_table[256];
+static int fp8_table_ready = 0;
+
+static void fp8_table_init(void)
+{
+    if (fp8_table_ready)
+        return;
+    for (int c = 0; c < 256; ++c)
+        fp8_table[c] = oracle_fp8_decode((uint8_t)c);
+    fp8_table_ready = 1;
+}
+
+/* Dynamic per-row fp8 quantisation (FlagGems walkthrough, "FP8 W8A8":
+ * activations are quantised before each expert GEMM).  Decision precision
+ * float32: scale = amax / 448 (1 when the row is all zero), code =
+ * RNE(x / scale). */
+void oracle_quant_row_fp8(const float* x, int64_t n, uint8_t* q, float* scale_out)
+{
+    float amax = 0.0f, scale;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(x[i]);
+        if (a > amax)
+            amax = a;
+    }
+    scale = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+    for (int64_t i = 0; i < n; ++i)
+        q[i] = oracle_fp8_encode(x[i] / scale);
+    *scale_out = scale;
+}
+
+/* ------------------------------------------------------------------ */
+/* routing                                                             */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    int32_t E, top_k;
+    int32_t scoring;           /* OR_SOFTMAX or OR_SIGMOID               */
+    int32_t renormalize;       /* softmax only; sigmoid always normalises */
+    int32_t group_count;       /* 1 = no grouped selection               */
+    int32_t k_group;
+    int32_t group_select_mode; /* 0 group max, 1 sum of the group top-2  */
+    int32_t logits_dtype;      /* OR_F32 or OR_BF16                      */
+    double routed_scaling_factor;
+} oracle_routing;
+
+static double logit_at(const oracle_routing* R, const void* logits, int64_t t, int e)
+{
+    int64_t idx = t * (int64_t)R->E + e;
+    if (R->logits_dtype == OR_BF16)
+        return bf16_bits_to_double(((const uint16_t*)logits)[idx]);
+    return (double)((const float*)logits)[idx];
+}
+
+/* Grouped-routing key of mode 1 for one expert logit v: the expert's score
+ * up to a positive factor shared by the whole token (softmax: exp(v - max),
+ * sigmoid: 1/(1+exp(-v))), evaluated in double and rounded to float32. */
+static float group_score_f32(int scoring, double v, double vmax)
+{
+    if (scoring == OR_SIGMOID)
+        return (float)(1.0 / (1.0 + exp(-v)));
+    return (float)exp(v - vmax);
+}
+
+/* Routes one token.  ids[k] in selection order, w[k] in double. */
+static void route_token(const oracle_routing* R, const double* s, int32_t* ids, double* w,
+                        unsigned char* cand, unsigned char* taken, double* p)
+{
+    const int E = R->E, K = R->top_k;
+    double vmax = s[0], sum;
+
+    for (int e = 1; e < E; ++e)
+        if (s[e] > vmax)
+            vmax = s[e];
+
+    /* scores p_t (FlagGems sec. 1.1 softmax; MindIE routing: sigmoid) */
+    if (R->scoring == OR_SOFTMAX) {
+        sum = 0.0;
+        for (int e = 0; e < E; ++e) {
+            p[e] = exp(s[e] - vmax);
+            sum += p[e];
+        }
+        for (int e = 0; e < E; ++e)
+            p[e] /= sum;
+    } else {
+        for (int e = 0; e < E; ++e)
+            p[e] = 1.0 / (1.0 + exp(-s[e]));
+    }
+
+    /* candidate experts: all, or those of the k_group best groups */
+    if (R->group_count > 1) {
+        const int G = R->group_count, per = E / G;
+        double key[1024];
+        unsigned char gtaken[1024];
+        for (int g = 0; g < G; ++g) {
+            const double* sg = s + g * per;
+            gtaken[g] = 0;
+            if (R->group_select_mode == 0) {
+                double m = sg[0];
+                for (int i = 1; i < per; ++i)
+                    if (sg[i] > m)
+                        m = sg[i];
+                key[g] = m; /* the group max score, compared through its logit */
+            } else {
+                /* the two largest logits of the group */
+                int a = 0;
+                for (int i = 1; i < per; ++i)
+                    if (sg[i] > sg[a])
+                        a = i;
+                int b = (a == 0) ? 1 : 0;
+                for (int i = 0; i < per; ++i)
+                    if (i != a && sg[i] > sg[b])
+                        b = i;
+                float ka = group_score_f32(R->scoring, sg[a], vmax);
+                float kb = group_score_f32(R->scoring, sg[b], vmax);
+                float k2 = ka + kb; /* float32 addition */
+                key[g] = (double)k2;
+            }
+        }
+        for (int e = 0; e < E; ++e)
+            cand[e] = 0;
+        for (int round = 0; round < R->k_group; ++round) {
+            int best = -1;
+            for (int g = 0; g < G; ++g)
+                if (!gtaken[g] && (best < 0 || key[g] > key[best]))
+                    best = g; /* strict '>' keeps the lower index on ties */
+            gtaken[best] = 1;
+            for (int i = 0; i < per; ++i)
+                cand[best * per + i] = 1;
+        }
+    } else {
+        for (int e = 0; e < E; ++e)
+            cand[e] = 1;
+    }
+
+    /* top-k over the candidates by (logit desc, index asc) */
+    for (int e = 0; e < E; ++e)
+        taken[e] = 0;
+    for (int j = 0; j < K; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e)
+            if (cand[e] && !taken[e] && (best < 0 || s[e] > s[best]))
+                best = e;
+        taken[best] = 1;
+        ids[j] = best;
+        w[j] = p[best];
+    }
+
+    /* renormalise (softmax when asked; sigmoid always), then scale */
+    if ((R->scoring == OR_SOFTMAX && R->renormalize) || R->scoring == OR_SIGMOID) {
+        double tot = 0.0;
+        for (int j = 0; j < K; ++j)
+            tot += w[j];
+        for (int j = 0; j < K; ++j)
+            w[j] /= tot;
+    }
+    for (int j = 0; j < K; ++j)
+        w[j] *= R->routed_scaling_factor;
+}
+
+/* Routes tokens [0, M).  topk_ids [M, top_k], topk_w [M, top_k] (double). */
+int oracle_route(const oracle_routing* R, const void* logits, int64_t M, int32_t* topk_ids,
+                 double* topk_w)
+{
+    const int E = R->E, K = R->top_k;
+    if (E < 1 || E > 1024 || K < 1 || K > E)
+        return -1;
+    if (R->group_count > 1) {
+        if (E % R->group_count || R->k_group < 1 || R->k_group > R->group_count)
+            return -1;
+        if (K > R->k_group * (E / R->group_count))
+            return -1;
+        if (R->group_select_mode == 1 && E / R->group_count < 2)
+            return -1;
+    }
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * E);
+        double* p = (double*)malloc(sizeof(double) * E);
+        unsigned char* cand = (unsigned char*)malloc(E);
+        unsigned char* taken = (unsigned char*)malloc(E);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < M; ++t) {
+            for (int e = 0; e < E; ++e)
+                s[e] = logit_at(R, logits, t, e);
+            route_token(R, s, topk_ids + t * K, topk_w + t * K, cand, taken, p);
+        }
+        free(s);
+        free(p);
+        free(cand);
+        free(taken);
+    }
+    return 0;
+}
+
+/* Group keys as float32 for tests that inspect near-ties: keys[M, G].
+ * Mode 0 keys are the group's largest logit. */
+int oracle_group_keys(const oracle_routing* R, const void* logits, int64_t M, float* keys)
+{
+    const int E = R->E, G = R->group_count, per = E / G;
+    for (int64_t t = 0; t < M; ++t) {
+        double vmax = logit_at(R, logits, t, 0);
+        for (int e = 1; e < E; ++e) {
+            double v = logit_at(R, logits, t, e);
+            if (v > vmax)
+                vmax = v;
+        }
+        for (int g = 0; g < G; ++g) {
+            double a = -INFINITY, b = -INFINITY;
+            for (int i = 0; i < per; ++i) {
+                double v = logit_at(R, logits, t, g * per + i);
+                if (v > a) {
+                    b = a;
+                    a = v;
+                } else if (v > b) {
+                    b = v;
+                }
+            }
+            if (R->group_select_mode == 0)
+                keys[t * G + g] = (float)a;
+            else
+                keys[t * G + g] = group_score_f32(R->scoring, a, vmax) +
+                                  group_score_f32(R->scoring, b, vmax);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* align (permute metadata)                                            */
+/* ------------------------------------------------------------------ */
+
+/* Stable sort of the Mk routed items r = t*top_k + j by expert, each
+ * expert's run padded up to a multiple of BM with the sentinel Mk.
+ *   counts[E], sorted_ids[>= num_post_padded], expert_ids[num_post_padded/BM],
+ *   *num_post_padded.  Returns 0, or -1 when an id is out of [0, E) or the
+ *   output capacity is too small. */
+int oracle_align(const int32_t* ids, int64_t Mk, int32_t E, int32_t BM, int32_t* counts,
+                 int32_t* sorted_ids, int64_t sorted_cap, int32_t* expert_ids, int64_t blocks_cap,
+                 int32_t* num_post_padded)
+{
+    int64_t pos = 0;
+    for (int e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (int64_t r = 0; r < Mk; ++r) {
+        if (ids[r] < 0 || ids[r] >= E)
+            return -1;
+        counts[ids[r]]++;
+    }
+    for (int e = 0; e < E; ++e) {
+        int64_t start = pos, padded = ((int64_t)counts[e] + BM - 1) / BM * BM;
+        if (start + padded > sorted_cap || (start + padded) / BM > blocks_cap)
+            return -1;
+        for (int64_t r = 0; r < Mk; ++r)
+            if (ids[r] == e)
+                sorted_ids[pos++] = (int32_t)r;
+        while (pos < start + padded)
+            sorted_ids[pos++] = (int32_t)Mk;
+        for (int64_t b = start / BM; b < (start + padded) / BM; ++b)
+            expert_ids[b] = e;
+    }
+    *num_post_padded = (int32_t)pos;
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* expert FFN                                                          */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    int32_t H, I, E;
+    int32_t w_dtype;          /* OR_F32, OR_BF16, OR_FP8                      */
+    const void* w13;          /* [E][H][2I]; gate = columns [0,I), up = [I,2I) */
+    const void* w2;           /* [E][I][H]                                     */
+    const float* w13_scale;   /* OR_FP8: per output channel [E][2I]           */
+    const float* w2_scale;    /* OR_FP8: per output channel [E][H]            */
+    int32_t bias_dtype;       /* OR_F32 or OR_BF16                             */
+    const void* w13_bias;     /* [E][2I] or NULL                               */
+    const void* w2_bias;      /* [E][H] or NULL                                */
+    int32_t requant_z;        /* 1: z is requantised to fp8 per (row, 128 cols) */
+} oracle_experts;
+
+typedef struct {
+    int32_t dtype;            /* OR_F32, OR_BF16, OR_FP8 (codes + per-row scale) */
+    const void* data;         /* [rows][H]                                       */
+    const float* scale;       /* OR_FP8: [rows]                                  */
+    int32_t quantize;         /* 1: quantise the f32/bf16 row to fp8 first      */
+} oracle_acts;
+
+static double bias_at(const oracle_experts* W, const void* b, int64_t idx)
+{
+    if (W->bias_dtype == OR_BF16)
+        return bf16_bits_to_double(((const uint16_t*)b)[idx]);
+    return (double)((const float*)b)[idx];
+}
+
+/* x = one activation row as double (dequantised where it is fp8). */
+static void load_row(const oracle_acts* A, int64_t H, int64_t row, double* x, float* xf,
+                     uint8_t* q)
+{
+    if (A->dtype == OR_FP8) {
+        const uint8_t* c = (const uint8_t*)A->data + row * H;
+        double sc = (double)A->scale[row];
+        for (int64_t k = 0; k < H; ++k)
+            x[k] = fp8_table[c[k]] * sc;
+        return;
+    }
+    for (int64_t k = 0; k < H; ++k)
+        x[k] = (A->dtype == OR_BF16) ? bf16_bits_to_double(((const uint16_t*)A->data)[row * H + k])
+                                     : (double)((const float*)A->data)[row * H + k];
+    if (A->quantize) {
+        float sc;
+        for (int64_t k = 0; k < H; ++k)
+            xf[k] = (float)x[k];
+        oracle_quant_row_fp8(xf, H, q, &sc);
+        for (int64_t k = 0; k < H; ++k)
+            x[k] = fp8_table[q[k]] * (double)sc;
+    }
+}
+
+/* z requantisation for the fp8 path: each 128-column group of a row gets
+ * its own scale (the block-wise granularity of the "FP8 W8A8" section);
+ * codes are decided in float32 as the device does. */
+static void requant_z(double* z, int64_t I)
+{
+    for (int64_t g0 = 0; g0 < I; g0 += 128) {
+        int64_t n = (I - g0 < 128) ? I - g0 : 128;
+        float zf[128], amax = 0.0f, sc;
+        for (int64_t i = 0; i < n; ++i) {
+            zf[i] = (float)z[g0 + i];
+            if (fabsf(zf[i]) > amax)
+                amax = fabsf(zf[i]);
+        }
+        sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+        for (int64_t i = 0; i < n; ++i)
+            z[g0 + i] = fp8_table[oracle_fp8_encode(zf[i] / sc)] * (double)sc;
+    }
+}
+
+/* o = f_e(x): h = W13_e^T x + b13_e; z = SiLU(h[:I]) * h[I:]; o = W2_e^T z + b2_e.
+ * scratch: h[2I], z[I]. */
+static void expert_ffn(const oracle_experts* W, int e, const double* x, double* h, double* z,
+                       double* o)
+{
+    const int64_t H = W->H, I = W->I, N = 2 * (int64_t)W->I;
+
+    for (int64_t n = 0; n < N; ++n)
+        h[n] = 0.0;
+    for (int64_t k = 0; k < H; ++k) {
+        const double xk = x[k];
+        const int64_t base = ((int64_t)e * H + k) * N;
+        if (W->w_dtype == OR_F32) {
+            const float* w = (const float*)W->w13 + base;
+            for (int64_t n = 0; n < N; ++n)
+                h[n] += xk * (double)w[n];
+        } else if (W->w_dtype == OR_BF16) {
+            const uint16_t* w = (const uint16_t*)W->w13 + base;
+            for (int64_t n = 0; n < N; ++n)
+                h[n] += xk * bf16_bits_to_double(w[n]);
+        } else {
+            const uint8_t* w = (const uint8_t*)W->w13 + base;
+            const float* sc = W->w13_scale + (int64_t)e * N;
+            for (int64_t n = 0; n < N; ++n)
+                h[n] += xk * (fp8_table[w[n]] * (double)sc[n]);
+        }
+    }
+    if (W->w13_bias)
+        for (int64_t n = 0; n < N; ++n)
+            h[n] += bias_at(W, W->w13_bias, (int64_t)e * N + n);
+
+    for (int64_t i = 0; i < I; ++i) {
+        const double g = h[i], u = h[I + i];
+        z[i] = g / (1.0 + exp(-g)) * u; /* SiLU(g) = g * sigmoid(g) */
+    }
+    if (W->requant_z)
+        requant_z(z, I);
+
+    for (int64_t c = 0; c < H; ++c)
+        o[c] = 0.0;
+    for (int64_t i = 0; i < I; ++i) {
+        const double zi = z[i];
+        const int64_t base = ((int64_t)e * I + i) * H;
+        if (W->w_dtype == OR_F32) {
+            const float* w = (const float*)W->w2 + base;
+            for (int64_t c = 0; c < H; ++c)
+                o[c] += zi * (double)w[c];
+        } else if (W->w_dtype == OR_BF16) {
+            const uint16_t* w = (const uint16_t*)W->w2 + base;
+            for (int64_t c = 0; c < H; ++c)
+                o[c] += zi * bf16_bits_to_double(w[c]);
+        } else {
+            const uint8_t* w = (const uint8_t*)W->w2 + base;
+            const float* sc = W->w2_scale + (int64_t)e * H;
+            for (int64_t c = 0; c < H; ++c)
+                o[c] += zi * (fp8_table[w[c]] * (double)sc[c]);
+        }
+    }
+    if (W->w2_bias)
+        for (int64_t c = 0; c < H; ++c)
+            o[c] += bias_at(W, W->w2_bias, (int64_t)e * H + c);
+}
+
+/* Contiguous format.  For each listed token t: y[t] = sum_j w[t,j] f_{id[t,j]}(x_t),
+ * j ascending, with (ids, weights) from oracle_route (or given).
+ * tokens[n_tokens] index rows of the activations; y is [n_tokens][H] double.
+ * nthreads <= 0 keeps the OpenMP default.  Returns the thread count used. */
+int oracle_forward_tokens(const oracle_experts* W, const oracle_acts* A, int32_t top_k,
+                          const int32_t* topk_ids, const double* topk_w, const int64_t* tokens,
+                          int64_t n_tokens, double* y, int32_t nthreads)
+{
+    int used = 1;
+    fp8_table_init();
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel
+    {
+        const int64_t H = W->H, I = W->I;
+        double* x = (double*)malloc(sizeof(double) * H);
+        float* xf = (float*)malloc(sizeof(float) * H);
+        uint8_t* q = (uint8_t*)malloc(H);
+        double* h = (double*)malloc(sizeof(double) * 2 * I);
+        double* z = (double*)malloc(sizeof(double) * I);
+        double* o = (double*)malloc(sizeof(double) * H);
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < n_tokens; ++n) {
+            const int64_t t = tokens[n];
+            double* yt = y + n * H;
+            load_row(A, H, t, x, xf, q);
+            for (int64_t c = 0; c < H; ++c)
+                yt[c] = 0.0;
+            for (int j = 0; j < top_k; ++j) {
+                const int e = topk_ids[t * top_k + j];
+                const double wj = topk_w[t * top_k + j];
+                expert_ffn(W, e, x, h, z, o);
+                for (int64_t c = 0; c < H; ++c)
+                    yt[c] += wj * o[c];
+            }
+        }
+        free(x);
+        free(xf);
+        free(q);
+        free(h);
+        free(z);
+        free(o);
+    }
+    return used;
+}
+
+/* Any list of (activation row, expert) pairs: out[n][H] = f_{experts[n]}(row rows[n]).
+ * Serves the batched format, where row = e * max_tokens + i for i < count_e. */
+int oracle_expert_rows(const oracle_experts* W, const oracle_acts* A, const int64_t* rows,
+                       const int32_t* experts, int64_t n_rows, double* out, int32_t nthreads)
+{
+    int used = 1;
+    fp8_table_init();
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel
+    {
+        const int64_t H = W->H, I = W->I;
+        double* x = (double*)malloc(sizeof(double) * H);
+        float* xf = (float*)malloc(sizeof(float) * H);
+        uint8_t* q = (uint8_t*)malloc(H);
+        double* h = (double*)malloc(sizeof(double) * 2 * I);
+        double* z = (double*)malloc(sizeof(double) * I);
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < n_rows; ++n) {
+            load_row(A, H, rows[n], x, xf, q);
+            expert_ffn(W, experts[n], x, h, z, out + n * H);
+        }
+        free(x);
+        free(xf);
+        free(q);
+        free(h);
+        free(z);
+    }
+    return used;
+}

@@ -1,0 +1,475 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test checks the oracle against what the pages or the mathematics fix:
+library routines on special cases (torch float64 matmul, torch's
+float8_e4m3fn cast, numpy's stable argsort), closed forms, invariants, and
+brute force over every routing of tiny inputs.  Each is chosen so that a
+plausible slip in the oracle (a dropped bias, a swapped gate/up half, a
+transposed weight, a wrong tie-break, a missing renormalisation) fails.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- fp8 codec
+
+def test_fp8_decode_matches_torch_all_codes():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = oracle.fp8_decode(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(ref, got, equal_nan=True)
+    assert got[0x7E] == 448.0 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    assert got[0x01] == 2.0 ** -9          # smallest subnormal
+
+
+def test_fp8_encode_matches_torch_on_every_bf16_in_range():
+    bits = np.arange(65536, dtype=np.uint32) << 16
+    vals = bits.view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 448.0)]
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = oracle.fp8_encode(vals)
+    # +-0 both decode to zero; everything else must be the identical code
+    same = (ref == got) | ((ref & 0x7F) == 0) & ((got & 0x7F) == 0)
+    assert same.all(), vals[~same][:10]
+
+
+def test_fp8_encode_random_f32_ties_and_saturation():
+    rng = np.random.default_rng(7)
+    vals = (rng.standard_normal(20000) * rng.choice([1e-3, 0.1, 3.0, 100.0], 20000)).astype(
+        np.float32)
+    vals = vals[np.abs(vals) <= 448.0]
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ref, oracle.fp8_encode(vals))
+    # exact midpoints round to the even mantissa
+    assert oracle.fp8_decode(oracle.fp8_encode(np.float32([1.0625])))[0] == 1.0
+    assert oracle.fp8_decode(oracle.fp8_encode(np.float32([1.1875])))[0] == 1.25
+    # saturation instead of NaN
+    sat = oracle.fp8_decode(oracle.fp8_encode(np.float32([500.0, -1e30, np.inf])))
+    assert list(sat) == [448.0, -448.0, 448.0]
+
+
+def test_row_quant_scale_and_codes():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 300)).astype(np.float32)
+    x[2] = 0.0
+    q, s = oracle.quant_rows_fp8(x)
+    amax = np.abs(x).max(1)
+    assert s[2] == 1.0 and (q[2] & 0x7F == 0).all()
+    for r in (0, 1, 3, 4):
+        assert s[r] == np.float32(amax[r]) / np.float32(448.0)
+        # the largest element lands on the largest code
+        assert (q[r][np.argmax(np.abs(x[r]))] & 0x7F) == 0x7E
+        ref = torch.from_numpy(x[r] / s[r]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(ref, q[r])
+
+
+# ----------------------------------------------------------------- routing
+
+def _dominant_subset(values, cand, k):
+    """Brute force: the unique k-subset S of cand with (v_e, -e) > (v_f, -f)
+    for every e in S, f in cand \\ S."""
+    found = []
+    for S in itertools.combinations(cand, k):
+        rest = [f for f in cand if f not in S]
+        if all((values[e], -e) > (values[f], -f) for e in S for f in rest):
+            found.append(set(S))
+    assert len(found) == 1
+    return found[0]
+
+
+def _sig(v):
+    return 1.0 / (1.0 + np.exp(-np.float64(v)))
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("E,k,G,kg,mode,scoring", [
+    (4, 1, 1, 1, 0, "softmax"), (6, 3, 1, 1, 0, "softmax"), (8, 4, 1, 1, 0, "sigmoid"),
+    (8, 2, 4, 2, 0, "softmax"), (8, 3, 4, 2, 1, "sigmoid"), (8, 2, 2, 1, 1, "softmax"),
+    (6, 4, 3, 2, 1, "sigmoid"), (8, 8, 4, 4, 0, "sigmoid"),
+])
+def test_route_brute_force(seed, E, k, G, kg, mode, scoring):
+    rng = np.random.default_rng(100 + seed)
+    M = 40
+    if seed % 2:   # integer-valued logits: many exact ties
+        logits = rng.integers(-2, 3, size=(M, E)).astype(np.float32)
+    else:
+        logits = rng.standard_normal((M, E)).astype(np.float32)
+    ids, w = oracle.route(logits, k, scoring=scoring, renormalize=True, group_count=G,
+                          k_group=kg, group_select_mode=mode, routed_scaling_factor=1.0)
+    per = E // G
+    for t in range(M):
+        s = logits[t].astype(np.float64)
+        if G > 1:
+            keys = []
+            for g in range(G):
+                grp = np.sort(s[g * per:(g + 1) * per])[::-1]
+                if mode == 0:
+                    keys.append(grp[0])
+                else:
+                    f = (lambda v: _sig(v)) if scoring == "sigmoid" else (
+                        lambda v: np.exp(v - s.max()))
+                    keys.append(float(np.float32(f(grp[0])) + np.float32(f(grp[1]))))
+            groups = _dominant_subset(keys, list(range(G)), kg)
+            cand = [e for e in range(E) if e // per in groups]
+        else:
+            cand = list(range(E))
+        chosen = _dominant_subset(s, cand, k)
+        assert set(ids[t]) == chosen
+        # selection order: descending logit, lower index first on ties
+        order = sorted(chosen, key=lambda e: (-s[e], e))
+        assert list(ids[t]) == order
+        # weights: scores of the chosen experts, renormalised
+        p = _sig(s) if scoring == "sigmoid" else np.exp(s - s.max()) / np.exp(s - s.max()).sum()
+        ref = p[order] / p[order].sum()
+        assert np.allclose(w[t], ref, rtol=1e-13, atol=0)
+
+
+def test_route_matches_pages_custom_routing_example():
+    """MindIE-SD 'Fused MoE' page, custom routing function example:
+    softmax over the logits, top-k, optional division by the sum."""
+    g = torch.Generator().manual_seed(5)
+    logits = torch.randn(64, 16, generator=g, dtype=torch.float64).float()
+    for renorm in (False, True):
+        res = logits.double().softmax(-1).topk(4, dim=-1)
+        w_ref = res.values
+        if renorm:
+            w_ref = w_ref / w_ref.sum(-1, keepdim=True)
+        ids, w = oracle.route(logits, 4, renormalize=renorm)
+        assert np.array_equal(ids, res.indices.numpy())
+        assert np.allclose(w, w_ref.numpy(), rtol=1e-13)
+
+
+@pytest.mark.parametrize("scoring,renorm,rsf", [("softmax", True, 1.0), ("softmax", True, 2.5),
+                                                ("sigmoid", False, 2.5), ("sigmoid", True, 0.5)])
+def test_route_weight_sum_and_scaling(scoring, renorm, rsf):
+    rng = np.random.default_rng(11)
+    logits = rng.standard_normal((200, 32)).astype(np.float32)
+    ids, w = oracle.route(logits, 6, scoring=scoring, renormalize=renorm, group_count=4,
+                          k_group=2, group_select_mode=1, routed_scaling_factor=rsf)
+    # sigmoid is always normalised; softmax when renormalize is set
+    assert np.allclose(w.sum(1), rsf, rtol=1e-12)
+    ids1, w1 = oracle.route(logits, 6, scoring=scoring, renormalize=renorm, group_count=4,
+                            k_group=2, group_select_mode=1, routed_scaling_factor=1.0)
+    assert np.array_equal(ids, ids1) and np.allclose(w, rsf * w1, rtol=1e-14)
+
+
+def test_route_softmax_without_renorm_keeps_probabilities():
+    logits = np.zeros((3, 8), np.float32)
+    ids, w = oracle.route(logits, 3, renormalize=False)
+    assert (ids == np.arange(3)).all() and np.allclose(w, 1 / 8)
+    ids, w = oracle.route(logits, 3, renormalize=True)
+    assert np.allclose(w, 1 / 3)
+    ids, w = oracle.route(logits, 3, scoring="sigmoid", routed_scaling_factor=2.0)
+    assert (ids == np.arange(3)).all() and np.allclose(w, 2 / 3)
+
+
+def test_grouping_special_cases_reduce_to_plain_topk():
+    rng = np.random.default_rng(12)
+    logits = rng.standard_normal((100, 16)).astype(np.float32)
+    ref = oracle.route(logits, 4, renormalize=True)
+    for mode in (0, 1):
+        # every group selected -> no restriction
+        got = oracle.route(logits, 4, renormalize=True, group_count=4, k_group=4,
+                           group_select_mode=mode)
+        assert np.array_equal(ref[0], got[0]) and np.allclose(ref[1], got[1])
+    # one expert per group with mode 0: choosing groups == choosing experts
+    got = oracle.route(logits, 4, renormalize=True, group_count=16, k_group=4)
+    assert np.array_equal(ref[0], got[0])
+
+
+def test_route_rejects_pages_constraints():
+    lg = np.zeros((2, 8), np.float32)
+    for kw in [dict(top_k=9), dict(top_k=0), dict(top_k=2, group_count=3),
+               dict(top_k=2, group_count=4, k_group=5), dict(top_k=5, group_count=4, k_group=2),
+               dict(top_k=2, group_count=8, k_group=2, group_select_mode=1)]:
+        k = kw.pop("top_k")
+        with pytest.raises(ValueError):
+            oracle.route(lg, k, **kw)
+
+
+# ----------------------------------------------------------------- align
+
+@pytest.mark.parametrize("Mk,E,BM", [(1, 1, 16), (37, 5, 16), (1024, 8, 64), (4096, 64, 32),
+                                     (3000, 256, 16), (200, 8, 1)])
+def test_align_against_stable_argsort(Mk, E, BM):
+    rng = np.random.default_rng(Mk + E)
+    ids = rng.integers(0, E, size=Mk).astype(np.int32)
+    if E > 3:
+        ids[ids == 3] = 2          # an expert with no rows
+    counts, sorted_ids, expert_ids, npp = oracle.align(ids, E, BM)
+    assert np.array_equal(counts, np.bincount(ids, minlength=E))
+    assert counts.sum() == Mk
+    padded = -(-counts // BM) * BM
+    assert npp == padded.sum() and npp % BM == 0
+    real = sorted_ids[sorted_ids < Mk]
+    assert np.array_equal(real, np.argsort(ids, kind="stable"))      # bijection, stable
+    assert (sorted_ids[sorted_ids >= Mk] == Mk).all()
+    start = 0
+    for e in range(E):
+        seg = sorted_ids[start:start + padded[e]]
+        assert (ids[seg[:counts[e]]] == e).all() and (seg[counts[e]:] == Mk).all()
+        assert (expert_ids[start // BM:(start + padded[e]) // BM] == e).all()
+        start += padded[e]
+
+
+# ----------------------------------------------------------------- expert FFN
+
+def _dense_ffn(x, W13, W2, b13=None, b2=None):
+    """Gated SiLU FFN in torch float64: (SiLU(x Wg + bg) * (x Wu + bu)) W2 + b2."""
+    h = x @ W13
+    if b13 is not None:
+        h = h + b13
+    I = W2.shape[0]
+    z = torch.nn.functional.silu(h[:, :I]) * h[:, I:]
+    o = z @ W2
+    return o if b2 is None else o + b2
+
+
+def _bf(t):
+    return t.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("scoring,rsf,bias", [("softmax", 1.0, False), ("softmax", 1.0, True),
+                                              ("sigmoid", 2.5, True)])
+def test_dense_equivalence_topk_equals_E(scoring, rsf, bias):
+    """top_k = E, identical experts, normalised weights: y = rsf * dense FFN."""
+    g = torch.Generator().manual_seed(21)
+    M, H, I, E = 7, 48, 80, 4
+    x = _bf(torch.randn(M, H, generator=g))
+    W13 = _bf(torch.randn(H, 2 * I, generator=g) / math.sqrt(H))
+    W2 = _bf(torch.randn(I, H, generator=g) / math.sqrt(I))
+    b13 = _bf(0.1 * torch.randn(2 * I, generator=g)) if bias else None
+    b2 = _bf(0.1 * torch.randn(H, generator=g)) if bias else None
+    logits = _bf(torch.randn(M, E, generator=g))
+    ids, w = oracle.route(logits, E, scoring=scoring, renormalize=True,
+                          routed_scaling_factor=rsf)
+    ex = oracle.Experts(W13[None].expand(E, -1, -1), W2[None].expand(E, -1, -1),
+                        w13_bias=None if b13 is None else b13[None].expand(E, -1),
+                        w2_bias=None if b2 is None else b2[None].expand(E, -1))
+    y, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w)
+    ref = rsf * _dense_ffn(x.double(), W13.double(), W2.double(),
+                           None if b13 is None else b13.double(),
+                           None if b2 is None else b2.double())
+    assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_single_expert_is_the_dense_ffn_f32():
+    g = torch.Generator().manual_seed(22)
+    x = torch.randn(5, 16, generator=g)
+    W13 = torch.randn(1, 16, 24, generator=g)
+    W2 = torch.randn(1, 12, 16, generator=g)
+    ids, w = oracle.route(torch.zeros(5, 1), 1)
+    y, _ = oracle.forward_tokens(oracle.Experts(W13, W2), oracle.Acts(x), ids, w)
+    assert np.allclose(y, _dense_ffn(x.double(), W13[0].double(), W2[0].double()).numpy(),
+                       rtol=1e-13, atol=1e-13)
+
+
+def test_random_experts_weighted_sum_matches_torch():
+    """E = 6 distinct experts, top-2 softmax: y_t = sum_j w_tj FFN_{e_tj}(x_t)."""
+    g = torch.Generator().manual_seed(23)
+    M, H, I, E, K = 9, 32, 40, 6, 2
+    x = torch.randn(M, H, generator=g)
+    W13 = torch.randn(E, H, 2 * I, generator=g) / math.sqrt(H)
+    W2 = torch.randn(E, I, H, generator=g) / math.sqrt(I)
+    b13 = 0.1 * torch.randn(E, 2 * I, generator=g)
+    b2 = 0.1 * torch.randn(E, H, generator=g)
+    logits = torch.randn(M, E, generator=g)
+    res = logits.double().softmax(-1).topk(K, dim=-1)
+    ids_ref = res.indices
+    w_ref = res.values / res.values.sum(-1, keepdim=True)
+    ids, w = oracle.route(logits, K, renormalize=True)
+    assert np.array_equal(ids, ids_ref.numpy())
+    ex = oracle.Experts(W13, W2, w13_bias=b13, w2_bias=b2)
+    y, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w)
+    ref = torch.zeros(M, H, dtype=torch.float64)
+    for t in range(M):
+        for j in range(K):
+            e = int(ids_ref[t, j])
+            ref[t] += w_ref[t, j] * _dense_ffn(x[t:t + 1].double(), W13[e].double(),
+                                               W2[e].double(), b13[e].double(),
+                                               b2[e].double())[0]
+    assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12)
+    # the token subset path gives the same rows
+    ys, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w, tokens=[8, 0, 3])
+    assert np.array_equal(ys, y[[8, 0, 3]])
+
+
+def test_bias_closed_forms():
+    """w13 = 0: h = b13 so z = SiLU(b_gate) * b_up; with w2 = 0 too: y = sum_j w_j b2[e_j]."""
+    g = torch.Generator().manual_seed(24)
+    M, H, I, E, K = 6, 16, 8, 4, 2
+    x = torch.randn(M, H, generator=g)
+    b13 = torch.randn(E, 2 * I, generator=g)
+    b2 = torch.randn(E, H, generator=g)
+    W2 = torch.randn(E, I, H, generator=g)
+    ids, w = oracle.route(torch.randn(M, E, generator=g), K, renormalize=True)
+    y, _ = oracle.forward_tokens(oracle.Experts(torch.zeros(E, H, 2 * I), W2, w13_bias=b13,
+                                                w2_bias=b2), oracle.Acts(x), ids, w)
+    for t in range(M):
+        ref = 0
+        for j in range(K):
+            e = ids[t, j]
+            bg, bu = b13[e, :I].double(), b13[e, I:].double()
+            z = bg / (1 + torch.exp(-bg)) * bu
+            ref = ref + w[t, j] * (z @ W2[e].double() + b2[e].double()).numpy()
+        assert np.allclose(y[t], ref, rtol=1e-12, atol=1e-12)
+    y0, _ = oracle.forward_tokens(oracle.Experts(torch.zeros(E, H, 2 * I), torch.zeros(E, I, H),
+                                                 w13_bias=b13, w2_bias=b2),
+                                  oracle.Acts(x), ids, w)
+    ref0 = (w[:, :, None] * b2.double().numpy()[ids]).sum(1)
+    assert np.allclose(y0, ref0, rtol=1e-13, atol=1e-14)
+
+
+def test_gate_up_order_matters():
+    """Gate = columns [0, I), up = [I, 2I): swapping the halves changes y."""
+    g = torch.Generator().manual_seed(25)
+    M, H, I, E = 4, 16, 8, 2
+    x = torch.randn(M, H, generator=g)
+    W13 = torch.randn(E, H, 2 * I, generator=g)
+    W2 = torch.randn(E, I, H, generator=g)
+    ids, w = oracle.route(torch.randn(M, E, generator=g), 1)
+    y, _ = oracle.forward_tokens(oracle.Experts(W13, W2), oracle.Acts(x), ids, w)
+    sw = torch.cat([W13[:, :, I:], W13[:, :, :I]], dim=2)
+    ys, _ = oracle.forward_tokens(oracle.Experts(sw, W2), oracle.Acts(x), ids, w)
+    assert not np.allclose(y, ys, rtol=1e-3)
+    ref = w[:, :1] * _dense_ffn(x.double(), W13[0].double(), W2[0].double()).numpy()
+    mask = ids[:, 0] == 0
+    assert np.allclose(y[mask], ref[mask], rtol=1e-12, atol=1e-12)
+
+
+def _fp8(t):
+    return t.to(torch.float8_e4m3fn)
+
+
+def test_fp8_weights_equal_dequantised_weights():
+    g = torch.Generator().manual_seed(26)
+    M, H, I, E = 5, 32, 128, 3
+    x = torch.randn(M, H, generator=g)
+    q13 = _fp8(torch.randn(E, H, 2 * I, generator=g) * 8)
+    q2 = _fp8(torch.randn(E, I, H, generator=g) * 8)
+    s13 = torch.rand(E, 2 * I, generator=g) + 0.01
+    s2 = torch.rand(E, H, generator=g) + 0.01
+    ids, w = oracle.route(torch.randn(M, E, generator=g), 2, renormalize=True)
+    y, _ = oracle.forward_tokens(oracle.Experts(q13, q2, s13, s2), oracle.Acts(x), ids, w)
+    d13 = q13.double() * s13.double()[:, None, :]
+    d2 = q2.double() * s2.double()[:, None, :]
+    ref = np.zeros((M, H))
+    for t in range(M):
+        for j in range(2):
+            e = ids[t, j]
+            ref[t] += w[t, j] * _dense_ffn(x[t:t + 1].double(), d13[e], d2[e]).numpy()[0]
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_fp8_activation_quant_and_z_requant_match_torch_cast():
+    """A3: per-token quantisation of x; F3: z requantised per (row, 128 columns),
+    both decided in float32 -- checked against torch's float8_e4m3fn cast."""
+    g = torch.Generator().manual_seed(27)
+    M, H, I, E = 3, 64, 256, 2
+    x = _bf(torch.randn(M, H, generator=g))
+    W13 = torch.randn(E, H, 2 * I, generator=g) / 8
+    W2 = torch.randn(E, I, H, generator=g) / 16
+    ids = np.zeros((M, 1), np.int32)
+    ids[1, 0] = 1
+    w = np.ones((M, 1))
+    y, _ = oracle.forward_tokens(oracle.Experts(W13, W2, requant_z=True),
+                                 oracle.Acts(x, quantize=True), ids, w)
+    for t in range(M):
+        e = ids[t, 0]
+        xf = x[t].float()
+        sx = xf.abs().max() / 448.0
+        xq = (xf / sx).to(torch.float8_e4m3fn).double() * sx.double()
+        h = xq @ W13[e].double()
+        z = (torch.nn.functional.silu(h[:I]) * h[I:]).float()
+        zq = torch.empty(I, dtype=torch.float64)
+        for g0 in range(0, I, 128):
+            blk = z[g0:g0 + 128]
+            sz = blk.abs().max() / 448.0
+            zq[g0:g0 + 128] = (blk / sz).to(torch.float8_e4m3fn).double() * sz.double()
+        ref = zq @ W2[e].double()
+        assert np.allclose(y[t], ref.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_batched_rows_reduce_equals_contiguous():
+    """Batched format: per-slab expert rows, weighted and reduced through the
+    token map, equal the contiguous forward on the same routing."""
+    g = torch.Generator().manual_seed(28)
+    M, H, I, E, K = 12, 16, 24, 4, 2
+    x = _bf(torch.randn(M, H, generator=g))
+    W13 = _bf(torch.randn(E, H, 2 * I, generator=g) / 4)
+    W2 = _bf(torch.randn(E, I, H, generator=g) / 5)
+    ids, w = oracle.route(torch.randn(M, E, generator=g), K, renormalize=True)
+    ex = oracle.Experts(W13, W2)
+    y, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w)
+    T = M
+    xb = torch.full((E, T, H), float("nan"), dtype=torch.bfloat16)
+    fill = [0] * E
+    tmap = np.zeros((M, K), np.int64)
+    for t in range(M):
+        for j in range(K):
+            e = ids[t, j]
+            xb[e, fill[e]] = x[t]
+            tmap[t, j] = e * T + fill[e]
+            fill[e] += 1
+    rows = tmap.ravel()
+    o, _ = oracle.expert_rows(ex, oracle.Acts(xb), rows, rows // T)
+    yb = (w.reshape(-1, 1) * o).reshape(M, K, H).sum(1)
+    assert np.allclose(y, yb, rtol=1e-13, atol=1e-14)
+
+
+def test_hand_worked_closed_form():
+    """x = [1, 2], H = 2, I = 1, E = 2.  Expert 0: W13 = [[1,0],[0,1]] gives
+    gate 1, up 2, z = 2 SiLU(1); W2 = [[3,-1]] gives o0 = z [3, -1].
+    Expert 1: W13 = [[0,1],[1,0]] gives gate 2, up 1, z = SiLU(2); W2 = [[1,1]]
+    gives o1 = z [1, 1].  Logits [0.5, 0]: top-1 picks expert 0 with
+    softmax weight 1/(1+e^-0.5), or 1 after renormalisation; top-2 renormalised
+    mixes both with weights p0 and 1 - p0."""
+    w13 = np.float32([[[1, 0], [0, 1]], [[0, 1], [1, 0]]])
+    w2 = np.float32([[[3, -1]], [[1, 1]]])
+    x = np.float32([[1, 2]])
+    silu = lambda v: v / (1 + math.exp(-v))
+    o0 = np.array([3.0, -1.0]) * 2 * silu(1.0)
+    o1 = np.array([1.0, 1.0]) * silu(2.0)
+    p0 = 1 / (1 + math.exp(-0.5))
+    ex = oracle.Experts(w13, w2)
+    for k, renorm, ids_ref, w_ref, y_ref in [
+            (1, True, [0], [1.0], o0), (1, False, [0], [p0], p0 * o0),
+            (2, True, [0, 1], [p0, 1 - p0], p0 * o0 + (1 - p0) * o1)]:
+        ids, w = oracle.route(np.float32([[0.5, 0.0]]), k, renormalize=renorm)
+        assert list(ids[0]) == ids_ref
+        assert np.allclose(w[0], w_ref, rtol=1e-15)
+        y, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w)
+        assert np.allclose(y[0], y_ref, rtol=1e-14, atol=1e-15)
+
+
+def test_pages_example_shapes_run_through_brute_force():
+    """The MindIE-SD page's grouped-routing example (E 16, top-2, 4 groups,
+    k_group 1, mode 1, sigmoid, scaling 0.5), fixture in tests/golden."""
+    with open(os.path.join(GOLDEN, "pages_examples.json")) as f:
+        ex = json.load(f)["grouped_routing_example"]
+    rng = np.random.default_rng(31)
+    logits = rng.standard_normal((ex["num_tokens"], ex["num_experts"])).astype(np.float32)
+    ids, w = oracle.route(logits, ex["top_k"], scoring=ex["routing_method"],
+                          group_count=ex["group_count"], k_group=ex["k_group"],
+                          group_select_mode=ex["group_select_mode"],
+                          routed_scaling_factor=ex["routed_scaling_factor"])
+    per = ex["num_experts"] // ex["group_count"]
+    for t in range(ex["num_tokens"]):
+        s = logits[t].astype(np.float64)
+        keys = []
+        for g in range(ex["group_count"]):
+            top2 = np.sort(s[g * per:(g + 1) * per])[::-1][:2]
+            keys.append(float(np.float32(_sig(top2[0])) + np.float32(_sig(top2[1]))))
+        grp = _dominant_subset(keys, list(range(ex["group_count"])), ex["k_group"])
+        cand = [e for e in range(ex["num_experts"]) if e // per in grp]
+        assert set(ids[t]) == _dominant_subset(s, cand, ex["top_k"])
+        assert np.isclose(w[t].sum(), ex["routed_scaling_factor"], rtol=1e-13)
