@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE forward on one MI355X (gfx950).
+
+One step = one moe_forward over the whole batch: router -> align ->
+[fp8 quant] -> grouped GEMM W13 + SiLU*up -> grouped GEMM W2 -> top-k
+weight-and-reduce, on seeded synthetic inputs already resident in HBM.
+Prints one JSON line.  Default workload: the Mixtral-shaped prefill
+(M 512, H 4096, I 14336, E 8, top-2, bf16).
+
+The `roofline` object covers the dominant kernel (the W13 GEMM): its
+algorithmic bytes per launch (active experts' w13 + activation rows read
+once + z written once) over its average duration, timed with HIP events
+recorded on the launch stream around that kernel in every timed step.
+`cpu_baseline` times the CPU oracle (test infrastructure, untuned) on a
+bounded token sample of the same workload on this host.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused-MoE fwd tokens/s + active TFLOP/s (or HBM GB/s), % of roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill_bf16")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="tokens (or batched rows) the CPU oracle leg computes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7", mode=ctypes.RTLD_GLOBAL)
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        self.handles.append(e.value)
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                          ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for h in self.handles:
+            self.hip.hipEventDestroy(ctypes.c_void_p(h))
+        self.handles = []
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE {world}) is not "
+              "supported: the fused MoE forward here runs on a single device and no multi-GPU "
+              "path exists to time.", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mixture_experts_ffn_router_amd import binding as B
+    from mixture_experts_ffn_router_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    dev = torch.device("cuda:0")
+    cfg = W.BY_NAME[args.workload]
+    seed = args.seed if args.seed is not None else 1000 + W.CONFIGS.index(cfg)
+    print(f"[bench] {cfg.name}: generating inputs (seed {seed})", file=sys.stderr, flush=True)
+    inp = W.make_inputs(cfg, seed, device=dev)
+    batched = cfg.fmt == "batched"
+
+    # ---- problem and arguments (marshalling only)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    out_dt = tdt[cfg.out_dtype]
+    if batched:
+        hidden = inp["hidden"]
+        prob = B.Problem(M=cfg.M, H=cfg.H, I=cfg.I, E=cfg.E, top_k=cfg.top_k,
+                         fmt=B.MOE_FMT_BATCHED, max_tokens=inp["max_tokens"],
+                         act_dtype=B._dtype_code(hidden), w_dtype=B._dtype_code(inp["w13"]),
+                         out_dtype=B._dtype_code(torch.empty(0, dtype=out_dt)),
+                         routing=B.MOE_ROUTE_PRECOMPUTED)
+        out = torch.empty(cfg.E, inp["max_tokens"], cfg.H, dtype=out_dt, device=dev)
+        cargs = B.make_args(hidden, inp["w13"], inp["w2"], out,
+                            expert_num_tokens=inp["expert_num_tokens"],
+                            w13_scale=inp.get("w13_scale"), w2_scale=inp.get("w2_scale"))
+    else:
+        hidden = inp["hidden"]
+        prob = B.Problem(M=cfg.M, H=cfg.H, I=cfg.I, E=cfg.E, top_k=cfg.top_k,
+                         act_dtype=B._dtype_code(hidden), w_dtype=B._dtype_code(inp["w13"]),
+                         out_dtype=B._dtype_code(torch.empty(0, dtype=out_dt)),
+                         logits_dtype=B._dtype_code(inp["logits"]),
+                         routing=B.MOE_ROUTE_SIGMOID if cfg.scoring == "sigmoid"
+                         else B.MOE_ROUTE_SOFTMAX,
+                         renormalize=cfg.renormalize, group_count=cfg.group_count,
+                         k_group=cfg.k_group, group_select_mode=cfg.group_select_mode,
+                         routed_scaling_factor=cfg.routed_scaling_factor,
+                         has_w13_bias=inp["w13_bias"] is not None,
+                         has_w2_bias=inp["w2_bias"] is not None)
+        out = torch.empty(cfg.M, cfg.H, dtype=out_dt, device=dev)
+        cargs = B.make_args(hidden, inp["w13"], inp["w2"], out, router_logits=inp["logits"],
+                            w13_bias=inp["w13_bias"], w2_bias=inp["w2_bias"],
+                            w13_scale=inp.get("w13_scale"), w2_scale=inp.get("w2_scale"))
+    ws, info = B.allocate_workspace(prob, dev)
+    cprob = prob.c()
+    stream = B.current_stream_handle(dev)
+    hip = HipEvents()
+    nst = len(B.STAGES)
+
+    # ---- warmup
+    for _ in range(args.warmup):
+        B.moe_forward(cprob, cargs, ws.data_ptr(), ws.numel(), stream)
+    torch.cuda.synchronize()
+
+    # ---- timed steps: whole-step events plus per-stage events on the same stream
+    step_ev = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    stage_ev = [[hip.create() for _ in range(2 * nst)] for _ in range(args.steps)]
+    rec = hip.hip.hipEventRecord
+    rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        rec(ctypes.c_void_p(step_ev[k][0]), ctypes.c_void_p(stream))
+        B.moe_forward_timed(cprob, cargs, ws.data_ptr(), ws.numel(), stream, stage_ev[k])
+        rec(ctypes.c_void_p(step_ev[k][1]), ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [hip.elapsed_ms(a, b) for a, b in step_ev]
+    stage_ms = {}
+    ran = []
+    for s, name in enumerate(B.STAGES):
+        try:
+            vals = [hip.elapsed_ms(ev[2 * s], ev[2 * s + 1]) for ev in stage_ev]
+        except RuntimeError:
+            continue            # stage not run for this problem
+        stage_ms[name] = float(np.mean(vals))
+        ran.append(name)
+    hip.close()
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ---- accounting
+    if batched:
+        counts = inp["expert_num_tokens"].cpu().numpy()
+        valid_rows = int(counts.sum())
+    else:
+        off = info.off_expert_counts
+        counts = ws[off:off + 4 * cfg.E].view(torch.int32).cpu().numpy()
+        valid_rows = cfg.M * cfg.top_k
+    active = int((counts > 0).sum())
+    wes = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight]
+    aes = {"f32": 4, "bf16": 2}[cfg.act]
+    oes = {"f32": 4, "bf16": 2}[cfg.out_dtype]
+    zes = 1 if cfg.weight == "fp8" else aes
+    w13_b = active * cfg.H * 2 * cfg.I * wes
+    w2_b = active * cfg.I * cfg.H * wes
+    scale_b = active * (2 * cfg.I + cfg.H) * 4 if cfg.weight == "fp8" else 0
+    bias_b = active * (2 * cfg.I + cfg.H) * aes if cfg.bias else 0
+    x_rows = valid_rows if batched else cfg.M
+    x_b = x_rows * cfg.H * aes
+    out_rows = valid_rows if batched else cfg.M
+    out_b = out_rows * cfg.H * oes
+    logit_b = 0 if batched else cfg.M * cfg.E * aes
+    z_b = valid_rows * cfg.I * zes
+    flops = cfg.flops(valid_rows)
+    path_bytes = w13_b + w2_b + scale_b + bias_b + x_b + out_b + logit_b
+    dt_key = "fp8" if cfg.weight == "fp8" else cfg.weight
+    t_hbm = path_bytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[dt_key] * 1e12)
+    t_step = float(np.median(step_ms)) * 1e-3
+
+    # dominant kernel: W13 GEMM
+    g1_bytes = w13_b + (scale_b // 2 if scale_b else 0) + x_b + z_b
+    g1_ms = stage_ms.get("gemm1", float("nan"))
+    g1_flops = 2.0 * valid_rows * cfg.H * 2 * cfg.I
+    g1_gbs = g1_bytes / (g1_ms * 1e-3) / 1e9
+    g1_bound = "hbm" if g1_flops / g1_bytes < (MFMA_PEAK_TFLOPS[dt_key] * 1e12) / (
+        HBM_PEAK_GBS * 1e9) else "mfma"
+    if g1_bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        tf = g1_flops / (g1_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_PEAK_TFLOPS[dt_key],
+                "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS[dt_key], 4)}
+    roof.update({"kernel": "k_gemm1 (grouped W13 GEMM + SiLU*up)",
+                 "algorithmic_bytes_per_launch": int(g1_bytes),
+                 "avg_launch_ms": round(g1_ms, 4), "traffic": None})
+
+    tokens = cfg.M
+    value = tokens / (ms_per_step * 1e-3)
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3"}[cfg.weight],
+        "data": "synthetic (seeded; see DESIGN.md input recipe)",
+        "config": {"workload": cfg.name, "format": cfg.fmt, "M": cfg.M, "H": cfg.H, "I": cfg.I,
+                   "E": cfg.E, "top_k": cfg.top_k, "routing": cfg.scoring,
+                   "renormalize": cfg.renormalize, "group_count": cfg.group_count,
+                   "k_group": cfg.k_group, "group_select_mode": cfg.group_select_mode,
+                   "routed_scaling_factor": cfg.routed_scaling_factor, "bias": cfg.bias,
+                   "block_m": info.block_m, "active_experts": active,
+                   "valid_rows": valid_rows},
+        "active_tflops": round(flops / t_step / 1e12, 2),
+        "hbm_gbs_path": round(path_bytes / t_step / 1e9, 1),
+        "path_roofline": {"bytes": int(path_bytes), "flops": flops,
+                          "t_hbm_us": round(t_hbm * 1e6, 1), "t_mfma_us": round(t_mfma * 1e6, 1),
+                          "t_step_us_median_events": round(t_step * 1e6, 1),
+                          "frac": round(max(t_hbm, t_mfma) / t_step, 4)},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "roofline": roof,
+    }
+
+    # ---- CPU oracle leg (rank 0, N = 1 only)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, info, args.cpu_sample)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, inp, info, sample):
+    import numpy as np
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    print(f"[bench] cpu oracle leg on {threads} threads", file=sys.stderr, flush=True)
+    ex = oracle.Experts(inp["w13"].cpu(), inp["w2"].cpu(),
+                        None if inp.get("w13_scale") is None else inp["w13_scale"].cpu(),
+                        None if inp.get("w2_scale") is None else inp["w2_scale"].cpu(),
+                        None if inp.get("w13_bias") is None else inp["w13_bias"].cpu(),
+                        None if inp.get("w2_bias") is None else inp["w2_bias"].cpu(),
+                        requant_z=cfg.weight == "fp8")
+    acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8")
+    if cfg.fmt == "batched":
+        T = inp["max_tokens"]
+        counts = inp["expert_num_tokens"].cpu().numpy()
+        rows = np.concatenate([e * T + np.arange(c) for e, c in enumerate(counts)])
+        n = min(sample or 1536, rows.size)
+        rows = rows[:: max(1, rows.size // n)][:n].astype(np.int64)
+        t0 = time.perf_counter()
+        _, used = oracle.expert_rows(ex, acts, rows, (rows // T).astype(np.int32),
+                                     nthreads=threads)
+        dt = time.perf_counter() - t0
+        # tokens/s equivalent: each token is top_k routed rows
+        return {"value": round(n / cfg.top_k / dt, 2), "unit": "tokens/s", "cores": used,
+                "kind": "oracle",
+                "sample": f"{n} of {int(counts.sum())} valid batched rows (every "
+                          f"{max(1, rows.size // n)}th), {dt:.1f}s; tokens = rows / top_k"}
+    n = min(sample or 256, cfg.M)
+    logits = inp["logits"].cpu()
+    t0 = time.perf_counter()
+    ids, w = oracle.route(logits, cfg.top_k, scoring=cfg.scoring, renormalize=cfg.renormalize,
+                          group_count=cfg.group_count, k_group=cfg.k_group,
+                          group_select_mode=cfg.group_select_mode,
+                          routed_scaling_factor=cfg.routed_scaling_factor)
+    oracle.align(ids, cfg.E, info.block_m)
+    _, used = oracle.forward_tokens(ex, acts, ids, w, tokens=np.arange(n), nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"routing + align of all {cfg.M} tokens, expert FFN of the first {n} "
+                      f"tokens, {dt:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

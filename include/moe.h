@@ -1,0 +1,227 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused mixture-of-experts FFN forward.
+ *
+ *   y_t = sum_{e in TopK(t)} alpha_{t,e} * ( W2_e^T ( SiLU(x_t W13_e[:, :I] + b13_e[:I])
+ *                                                  * (x_t W13_e[:, I:] + b13_e[I:]) ) + b2_e )
+ *
+ * Sources (the pages on fused MoE):
+ *   - the math: FlagGems "fused_moe.py" walkthrough, sec. 1.1 (MoE definition)
+ *     and sec. 1.2 (routed-item form h_r, z_r, o_r, y_t);
+ *   - the argument list and its constraints: MindIE-SD "Fused MoE" page,
+ *     function signature, parameter table and routing-selection section;
+ *   - the two activation formats (contiguous (M, K) + topk ids/weights, and
+ *     batched (E, max_tokens, K) + expert_num_tokens) and the
+ *     workspace_shapes / apply split: vLLM "Fused MoE Modular Kernel" page,
+ *     introduction and the workspace_shapes() section;
+ *   - the align metadata (sorted_token_ids, expert_ids, num_tokens_post_padded):
+ *     FlagGems walkthrough, "moe_align_block_size" section;
+ *   - fp8 W8A8 scales: FlagGems walkthrough, "FP8 W8A8" section.
+ *
+ * Conventions shared by every entry point:
+ *   - Every buffer is caller-owned device memory (except the two structs,
+ *     which are host memory read during the call).  The library allocates
+ *     nothing, keeps no pointer after returning, and enqueues all work on the
+ *     caller's stream; it never synchronises the host.  A call can therefore
+ *     be captured into a HIP graph.
+ *   - Row-major, contiguous tensors with a stride-1 last dimension.  Leading
+ *     dims of a [..., H] activation are flattened into M by the caller.
+ *   - Expert ids are int32, routing weights float32.
+ *   - All argument checks run on the host before anything is enqueued; on
+ *     error nothing is enqueued.  Device-side preconditions (precomputed
+ *     topk ids in [0, E), expert_num_tokens[e] <= max_tokens) are not checked
+ *     on the device: violating them is undefined behaviour.
+ *   - Thread safety: concurrent calls are safe when they use distinct
+ *     workspaces and outputs.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1, /* shape / range / null-pointer violation            */
+    MOE_ERR_UNSUPPORTED = -2, /* valid request this build does not implement        */
+    MOE_ERR_WORKSPACE = -3,   /* workspace null, misaligned (256 B) or too small    */
+    MOE_ERR_LAUNCH = -4       /* a kernel launch failed (hipGetLastError)           */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3FN = 2 } moe_dtype;
+
+typedef enum {
+    MOE_ROUTE_SOFTMAX = 0,    /* scores = softmax(logits) over all E              */
+    MOE_ROUTE_SIGMOID = 1,    /* scores = sigmoid(logits); weights always normalised */
+    MOE_ROUTE_PRECOMPUTED = 2 /* caller passes topk_ids / topk_weights (the pages'
+                                 custom_routing_function output)                   */
+} moe_routing;
+
+typedef enum {
+    MOE_FMT_CONTIGUOUS = 0,   /* hidden [M, H], one routed item per (token, slot)  */
+    MOE_FMT_BATCHED = 1       /* hidden [E, max_tokens, H] + expert_num_tokens[E]  */
+} moe_format;
+
+/* Problem description (host struct).
+ *
+ *   format       MOE_FMT_CONTIGUOUS or MOE_FMT_BATCHED.
+ *   M            tokens.  Contiguous: rows of hidden/out.  Batched: rows of the
+ *                token map and of out when batched_reduce is set (else unused).
+ *   H, I         hidden and intermediate sizes; w13 is [E, H, 2I], w2 [E, I, H].
+ *                Both must be multiples of 16; the fp8 path needs I % 128 == 0.
+ *   E, top_k     experts (1..1024) and experts per token (1..E, <= 32).
+ *   max_tokens   batched: rows per expert slab.
+ *   act_dtype    hidden: MOE_F32 or MOE_BF16 (MOE_FP8_E4M3FN: batched only,
+ *                pre-quantised codes with a_scale).
+ *   w_dtype      weights: same as act_dtype for f32/bf16, or MOE_FP8_E4M3FN
+ *                (per-output-channel float scales; activations are then
+ *                quantised per token on the fly unless already fp8).
+ *   out_dtype    MOE_F32 or MOE_BF16.  f32 activations need f32 out.
+ *   logits_dtype MOE_F32 or MOE_BF16 (contiguous, routing != PRECOMPUTED).
+ *   routing, renormalize, group_count, k_group, group_select_mode,
+ *   routed_scaling_factor
+ *                the routing parameters of the MindIE-SD page: grouped
+ *                selection picks k_group of group_count contiguous expert
+ *                groups by their largest score (mode 0) or the sum of their
+ *                two largest scores (mode 1), then top_k experts inside them;
+ *                renormalize divides softmax weights by their sum (sigmoid
+ *                weights are always divided by their sum); the final weights
+ *                are multiplied by routed_scaling_factor.
+ *                Constraints: E % group_count == 0, 1 <= k_group <= group_count,
+ *                top_k <= k_group * E / group_count, mode 1 needs >= 2 experts
+ *                per group.  Ties break toward the lower expert (group) index.
+ *   has_w13_bias, has_w2_bias
+ *                biases [E, 2I] / [E, H], same dtype as the activations (bf16
+ *                for fp8 weights).  b13 is added before the activation; b2 is
+ *                added to each expert output, so it is scaled by the weight.
+ *   batched_reduce
+ *                batched only: also reduce the expert rows into out [M, H] with
+ *                token_map / token_map_w (the pages' naive batched
+ *                weight-and-reduce); 0 writes the expert rows to out
+ *                [E, max_tokens, H] instead.
+ */
+typedef struct {
+    int32_t format;
+    int32_t M, H, I, E, top_k;
+    int32_t max_tokens;
+    int32_t act_dtype, w_dtype, out_dtype, logits_dtype;
+    int32_t routing, renormalize, group_count, k_group, group_select_mode;
+    float routed_scaling_factor;
+    int32_t has_w13_bias, has_w2_bias;
+    int32_t batched_reduce;
+} moe_problem;
+
+/* Workspace layout chosen by the library for one problem.  All offsets are
+ * in bytes from the workspace base and 256-byte aligned.  The regions hold
+ * the path's intermediates and stay readable after the stream work is done
+ * (tests compare them with the CPU definition):
+ *   topk_ids [M, top_k] int32, topk_weights [M, top_k] float  (contiguous)
+ *   expert_counts [E] int32
+ *   expert_offsets [E + 1] int32: start of each expert's padded run in
+ *       sorted_ids (entry E = num_post_padded)
+ *   sorted_ids [max_sorted_len] int32: positions [0, num_post_padded) hold
+ *       the routed items grouped by expert, ascending within an expert, each
+ *       expert's run padded to a multiple of block_m with a sentinel
+ *       (contiguous: r = t*top_k + j, sentinel M*top_k; batched:
+ *       r = e*max_tokens + i, sentinel E*max_tokens)
+ *   expert_ids [max_blocks] int32: the expert of each block_m-row block
+ *   num_post_padded [1] int32
+ *   aq / aq_scale: fp8 activation codes and per-row scales (fp8 weights)
+ *   z [max_sorted_len, I]: SiLU(gate)*up per padded row (bf16 or f32; fp8
+ *       codes + per-(row, 128-column) float scales z_scale on the fp8 path)
+ *   o [M*top_k, H] (contiguous): each routed item's expert output, float.  */
+typedef struct {
+    size_t bytes;
+    int32_t block_m;
+    int32_t max_blocks;
+    int64_t max_sorted_len;
+    size_t off_topk_ids, off_topk_weights, off_expert_counts, off_expert_offsets, off_sorted_ids,
+        off_expert_ids, off_num_post_padded, off_aq, off_aq_scale, off_z, off_z_scale, off_o;
+} moe_workspace_info;
+
+/* Fills *info for problem *p (host only, no device work).  The caller then
+ * provides a device buffer of info->bytes, 256-byte aligned.  Returns MOE_OK,
+ * MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED (same checks as moe_forward). */
+int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* info);
+
+/* Device pointers of one forward (host struct; NULL where unused).
+ *   hidden            contiguous [M, H]; batched [E, max_tokens, H]
+ *                     (rows past expert_num_tokens[e] are never read).
+ *   a_scale           batched fp8 activations: [E, max_tokens] per-row scales.
+ *   router_logits     [M, E] (routing SOFTMAX / SIGMOID).
+ *   topk_ids, topk_weights
+ *                     [M, top_k] int32 / float (routing PRECOMPUTED).
+ *   expert_num_tokens batched: [E] int32 valid rows per slab.
+ *   token_map, token_map_w
+ *                     batched_reduce: [M, top_k] flat slab row e*max_tokens+i
+ *                     holding token t's j-th routed copy, and its weight.
+ *   w13, w2           [E, H, 2I] (gate = columns [0, I), up = [I, 2I)), [E, I, H].
+ *   w13_bias, w2_bias [E, 2I], [E, H] when has_*_bias.
+ *   w13_scale, w2_scale
+ *                     fp8 weights: float per output channel, [E, 2I] and [E, H].
+ *   out               contiguous / batched_reduce: [M, H]; batched: [E, max_tokens, H]
+ *                     (only valid rows written).  out may alias hidden in the
+ *                     contiguous format (in-place): every read of hidden
+ *                     precedes the first write of out on the stream. */
+typedef struct {
+    const void* hidden;
+    const float* a_scale;
+    const void* router_logits;
+    const int32_t* topk_ids;
+    const float* topk_weights;
+    const int32_t* expert_num_tokens;
+    const int32_t* token_map;
+    const float* token_map_w;
+    const void* w13;
+    const void* w2;
+    const void* w13_bias;
+    const void* w2_bias;
+    const float* w13_scale;
+    const float* w2_scale;
+    void* out;
+} moe_args;
+
+/* Enqueues one fused MoE forward on `stream` (a hipStream_t; NULL = the
+ * default stream): router -> align -> [fp8 activation quant] -> grouped
+ * GEMM W13 + bias + SiLU*up [+ fp8 requant] -> grouped GEMM W2 + bias ->
+ * top-k weight-and-reduce (unpermute).  `workspace` is a device buffer of at
+ * least moe_workspace_shapes(p)->bytes, 256-byte aligned.  Returns MOE_OK
+ * after enqueueing, or an error code with nothing enqueued (MOE_ERR_LAUNCH:
+ * a launch failed after earlier kernels of the call were enqueued). */
+int moe_forward(const moe_problem* p, const moe_args* a, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Kernel stages of one forward, in launch order (for moe_forward_timed). */
+typedef enum {
+    MOE_STAGE_ROUTER = 0,  /* top-k routing (skipped for PRECOMPUTED and batched) */
+    MOE_STAGE_ALIGN = 1,   /* align (contiguous) or tile list (batched)           */
+    MOE_STAGE_QUANT = 2,   /* per-row fp8 activation quantisation (fp8 weights)   */
+    MOE_STAGE_GEMM1 = 3,   /* grouped W13 GEMM + bias + SiLU*up (+ fp8 requant)   */
+    MOE_STAGE_GEMM2 = 4,   /* grouped W2 GEMM + bias                              */
+    MOE_STAGE_REDUCE = 5,  /* top-k weight-and-reduce (unpermute)                 */
+    MOE_NUM_STAGES = 6
+} moe_stage;
+
+/* moe_forward with instrumentation for kernel timing: events[2*s] and
+ * events[2*s + 1] (hipEvent_t handles created by the caller, may be NULL)
+ * are recorded on `stream` immediately before and after the launch of stage
+ * s; stages a problem does not run leave their events unrecorded.  `events`
+ * points at 2 * MOE_NUM_STAGES handles.  Same work, arguments and errors as
+ * moe_forward. */
+int moe_forward_timed(const moe_problem* p, const moe_args* a, void* workspace,
+                      size_t workspace_bytes, void* stream, void** events);
+
+/* Static English description of a status code. */
+const char* moe_status_string(int status);
+
+/* Library version, "major.minor.patch". */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

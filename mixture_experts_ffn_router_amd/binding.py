@@ -1,0 +1,291 @@
+"""Thin ctypes binding of libmoe's C ABI (include/moe.h).
+
+Argument marshalling only: every step of the forward runs in the HIP
+kernels behind ``moe_forward``.  PyTorch supplies device memory and the
+stream.  There is no fallback: if libmoe.so is missing or a call fails,
+this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+# enums of moe.h
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16, MOE_FP8_E4M3FN = 0, 1, 2
+MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID, MOE_ROUTE_PRECOMPUTED = 0, 1, 2
+MOE_FMT_CONTIGUOUS, MOE_FMT_BATCHED = 0, 1
+
+EXPORTED = ("moe_workspace_shapes", "moe_forward", "moe_forward_timed", "moe_status_string",
+            "moe_version")
+STAGES = ("router", "align", "quant", "gemm1", "gemm2", "reduce")
+
+
+class moe_problem(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("M", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("I", ctypes.c_int32), ("E", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
+                ("w_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("logits_dtype", ctypes.c_int32), ("routing", ctypes.c_int32),
+                ("renormalize", ctypes.c_int32), ("group_count", ctypes.c_int32),
+                ("k_group", ctypes.c_int32), ("group_select_mode", ctypes.c_int32),
+                ("routed_scaling_factor", ctypes.c_float), ("has_w13_bias", ctypes.c_int32),
+                ("has_w2_bias", ctypes.c_int32), ("batched_reduce", ctypes.c_int32)]
+
+
+class moe_workspace_info(ctypes.Structure):
+    _fields_ = [("bytes", ctypes.c_size_t), ("block_m", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("max_sorted_len", ctypes.c_int64)] + [
+        (n, ctypes.c_size_t) for n in (
+            "off_topk_ids", "off_topk_weights", "off_expert_counts", "off_expert_offsets",
+            "off_sorted_ids", "off_expert_ids", "off_num_post_padded", "off_aq", "off_aq_scale",
+            "off_z", "off_z_scale", "off_o")]
+
+
+class moe_args(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "hidden", "a_scale", "router_logits", "topk_ids", "topk_weights", "expert_num_tokens",
+        "token_map", "token_map_w", "w13", "w2", "w13_bias", "w2_bias", "w13_scale", "w2_scale",
+        "out")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {moe_status_string(status)} ({status})")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads the in-tree libmoe.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        try:   # share torch's HIP runtime (same SONAME) when torch is present
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m mixture_experts_ffn_router_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.moe_workspace_shapes.argtypes = [ctypes.POINTER(moe_problem),
+                                             ctypes.POINTER(moe_workspace_info)]
+        lib.moe_workspace_shapes.restype = ctypes.c_int
+        lib.moe_forward.argtypes = [ctypes.POINTER(moe_problem), ctypes.POINTER(moe_args),
+                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        lib.moe_forward.restype = ctypes.c_int
+        lib.moe_forward_timed.argtypes = [ctypes.POINTER(moe_problem), ctypes.POINTER(moe_args),
+                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.POINTER(ctypes.c_void_p)]
+        lib.moe_forward_timed.restype = ctypes.c_int
+        lib.moe_status_string.argtypes = [ctypes.c_int]
+        lib.moe_status_string.restype = ctypes.c_char_p
+        lib.moe_version.argtypes = []
+        lib.moe_version.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def moe_status_string(status: int) -> str:
+    return load().moe_status_string(int(status)).decode()
+
+
+def moe_version() -> str:
+    return load().moe_version().decode()
+
+
+def moe_workspace_shapes(problem: moe_problem) -> moe_workspace_info:
+    info = moe_workspace_info()
+    rc = load().moe_workspace_shapes(ctypes.byref(problem), ctypes.byref(info))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_workspace_shapes")
+    return info
+
+
+def moe_forward(problem: moe_problem, args: moe_args, workspace: int, workspace_bytes: int,
+                stream: int) -> None:
+    rc = load().moe_forward(ctypes.byref(problem), ctypes.byref(args), ctypes.c_void_p(workspace),
+                            workspace_bytes, ctypes.c_void_p(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_forward")
+
+
+def moe_forward_timed(problem: moe_problem, args: moe_args, workspace: int,
+                      workspace_bytes: int, stream: int, events) -> None:
+    """events: sequence of 2 * len(STAGES) hipEvent_t handles (ints or None)."""
+    arr = (ctypes.c_void_p * (2 * len(STAGES)))(*[e or None for e in events])
+    rc = load().moe_forward_timed(ctypes.byref(problem), ctypes.byref(args),
+                                  ctypes.c_void_p(workspace), workspace_bytes,
+                                  ctypes.c_void_p(stream), arr)
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_forward_timed")
+
+
+def moe_forward_status(problem: moe_problem, args: moe_args, workspace: int,
+                       workspace_bytes: int, stream: int) -> int:
+    """moe_forward returning the raw status (for argument-validation tests)."""
+    return load().moe_forward(ctypes.byref(problem), ctypes.byref(args),
+                              ctypes.c_void_p(workspace), workspace_bytes,
+                              ctypes.c_void_p(stream))
+
+
+# ------------------------------------------------------------ torch marshalling
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return MOE_FP8_E4M3FN
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return t.data_ptr()
+
+
+@dataclass
+class Problem:
+    """Python view of moe_problem."""
+    M: int
+    H: int
+    I: int
+    E: int
+    top_k: int
+    fmt: int = MOE_FMT_CONTIGUOUS
+    max_tokens: int = 0
+    act_dtype: int = MOE_BF16
+    w_dtype: int = MOE_BF16
+    out_dtype: int = MOE_BF16
+    logits_dtype: int = MOE_BF16
+    routing: int = MOE_ROUTE_SOFTMAX
+    renormalize: bool = False
+    group_count: int = 1
+    k_group: int = 1
+    group_select_mode: int = 0
+    routed_scaling_factor: float = 1.0
+    has_w13_bias: bool = False
+    has_w2_bias: bool = False
+    batched_reduce: bool = False
+
+    def c(self) -> moe_problem:
+        return moe_problem(self.fmt, self.M, self.H, self.I, self.E, self.top_k, self.max_tokens,
+                           self.act_dtype, self.w_dtype, self.out_dtype, self.logits_dtype,
+                           self.routing, int(self.renormalize), self.group_count, self.k_group,
+                           self.group_select_mode, float(self.routed_scaling_factor),
+                           int(self.has_w13_bias), int(self.has_w2_bias),
+                           int(self.batched_reduce))
+
+
+def make_args(hidden, w13, w2, out, router_logits=None, topk_ids=None, topk_weights=None,
+              w13_bias=None, w2_bias=None, w13_scale=None, w2_scale=None, a_scale=None,
+              expert_num_tokens=None, token_map=None, token_map_w=None) -> moe_args:
+    return moe_args(_ptr(hidden), _ptr(a_scale), _ptr(router_logits), _ptr(topk_ids),
+                    _ptr(topk_weights), _ptr(expert_num_tokens), _ptr(token_map),
+                    _ptr(token_map_w), _ptr(w13), _ptr(w2), _ptr(w13_bias), _ptr(w2_bias),
+                    _ptr(w13_scale), _ptr(w2_scale), _ptr(out))
+
+
+def allocate_workspace(problem: Problem, device):
+    """A device buffer of the size moe_workspace_shapes asks for (torch
+    allocations are 256-byte aligned)."""
+    import torch
+    info = moe_workspace_shapes(problem.c())
+    ws = torch.empty(max(int(info.bytes), 256), dtype=torch.uint8, device=device)
+    assert ws.data_ptr() % 256 == 0
+    return ws, info
+
+
+def current_stream_handle(device=None) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: bool = False,
+              routing: str = "softmax", group_count: int = 1, k_group: int = 1,
+              group_select_mode: int = 0, routed_scaling_factor: float = 1.0, w13_bias=None,
+              w2_bias=None, topk_ids=None, topk_weights=None, w13_scale=None, w2_scale=None,
+              out_dtype=None, out=None, workspace=None):
+    """Contiguous-format forward on torch device tensors (the MindIE-SD
+    page's fused_moe argument list, single device).  Returns (out, workspace
+    tensor, workspace info)."""
+    import torch
+    M, H = hidden.shape
+    E, _, N = w13.shape
+    I = N // 2
+    if topk_ids is not None:
+        route = MOE_ROUTE_PRECOMPUTED
+        top_k = topk_ids.shape[1]
+    else:
+        route = {"softmax": MOE_ROUTE_SOFTMAX, "sigmoid": MOE_ROUTE_SIGMOID}[routing]
+    act = _dtype_code(hidden)
+    odt = out_dtype or (torch.float32 if act == MOE_F32 else torch.bfloat16)
+    prob = Problem(M=M, H=H, I=I, E=E, top_k=top_k, act_dtype=act, w_dtype=_dtype_code(w13),
+                   out_dtype=_dtype_code(torch.empty(0, dtype=odt)),
+                   logits_dtype=_dtype_code(router_logits) if router_logits is not None else 0,
+                   routing=route, renormalize=renormalize, group_count=group_count,
+                   k_group=k_group, group_select_mode=group_select_mode,
+                   routed_scaling_factor=routed_scaling_factor,
+                   has_w13_bias=w13_bias is not None, has_w2_bias=w2_bias is not None)
+    if out is None:
+        out = torch.empty(M, H, dtype=odt, device=hidden.device)
+    if workspace is None:
+        workspace, info = allocate_workspace(prob, hidden.device)
+    else:
+        info = moe_workspace_shapes(prob.c())
+    args = make_args(hidden, w13, w2, out, router_logits=router_logits, topk_ids=topk_ids,
+                     topk_weights=topk_weights, w13_bias=w13_bias, w2_bias=w2_bias,
+                     w13_scale=w13_scale, w2_scale=w2_scale)
+    moe_forward(prob.c(), args, workspace.data_ptr(), workspace.numel(),
+                current_stream_handle(hidden.device))
+    return out, workspace, info
+
+
+def fused_moe_batched(hidden, expert_num_tokens, w13, w2, *, M: int = 0, top_k: int = 1,
+                      a_scale=None, w13_scale=None, w2_scale=None, w13_bias=None, w2_bias=None,
+                      token_map=None, token_map_w=None, out_dtype=None, out=None,
+                      workspace=None):
+    """Batched-format forward: hidden [E, max_tokens, H] + expert_num_tokens [E].
+    M, top_k (when M > 0) promise that the slabs hold at most M * top_k valid
+    rows, which bounds the workspace.  With token_map / token_map_w
+    ([M, top_k]) the rows are also weighted and reduced into out [M, H];
+    otherwise out is [E, max_tokens, H]."""
+    import torch
+    E, T, H = hidden.shape
+    N = w13.shape[2]
+    I = N // 2
+    reduce = token_map is not None
+    if reduce:
+        M, top_k = token_map.shape
+    odt = out_dtype or torch.bfloat16
+    prob = Problem(M=M, H=H, I=I, E=E, top_k=top_k, fmt=MOE_FMT_BATCHED,
+                   max_tokens=T, act_dtype=_dtype_code(hidden), w_dtype=_dtype_code(w13),
+                   out_dtype=_dtype_code(torch.empty(0, dtype=odt)),
+                   routing=MOE_ROUTE_PRECOMPUTED, has_w13_bias=w13_bias is not None,
+                   has_w2_bias=w2_bias is not None, batched_reduce=reduce)
+    if out is None:
+        shape = (M, H) if reduce else (E, T, H)
+        out = torch.empty(shape, dtype=odt, device=hidden.device)
+    if workspace is None:
+        workspace, info = allocate_workspace(prob, hidden.device)
+    else:
+        info = moe_workspace_shapes(prob.c())
+    args = make_args(hidden, w13, w2, out, a_scale=a_scale, expert_num_tokens=expert_num_tokens,
+                     token_map=token_map, token_map_w=token_map_w, w13_bias=w13_bias,
+                     w2_bias=w2_bias, w13_scale=w13_scale, w2_scale=w2_scale)
+    moe_forward(prob.c(), args, workspace.data_ptr(), workspace.numel(),
+                current_stream_handle(hidden.device))
+    return out, workspace, info

@@ -1,0 +1,329 @@
+// C ABI of libmoe: argument validation, workspace layout, kernel sequence.
+//
+// Entry points and their constraints follow the MindIE-SD "Fused MoE" page
+// (signature, parameter table, grouped-routing constraints) and the
+// FlagGems walkthrough's parameter checks (fused_experts_impl, "parameter
+// validation"); the workspace_shapes / apply split follows the vLLM
+// "Fused MoE Modular Kernel" page.  All checks run on the host before
+// anything is enqueued.
+#include <cmath>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static constexpr size_t ALIGN = 256;
+
+static size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+static int validate(const moe_problem* p)
+{
+    if (!p)
+        return MOE_ERR_INVALID_ARG;
+    if (p->format != MOE_FMT_CONTIGUOUS && p->format != MOE_FMT_BATCHED)
+        return MOE_ERR_INVALID_ARG;
+    if (p->M < 0 || p->H <= 0 || p->I <= 0 || p->E < 1 || p->top_k < 1)
+        return MOE_ERR_INVALID_ARG;
+    if (p->E > 1024)
+        return MOE_ERR_UNSUPPORTED;
+    if (p->top_k > p->E)
+        return MOE_ERR_INVALID_ARG;          // top_k in [1, num_experts]
+    if (p->top_k > 32)
+        return MOE_ERR_UNSUPPORTED;
+    if (p->H % 16 || p->I % 16)
+        return MOE_ERR_UNSUPPORTED;
+    if ((int64_t)p->M * p->top_k >= (1ll << 30) || (int64_t)p->H * p->I >= (1ll << 40))
+        return MOE_ERR_UNSUPPORTED;
+
+    // dtype combinations built here
+    const int act = p->act_dtype, w = p->w_dtype, out = p->out_dtype;
+    if (out != MOE_F32 && out != MOE_BF16)
+        return MOE_ERR_UNSUPPORTED;
+    if (act == MOE_F32) {
+        if (w != MOE_F32 || out != MOE_F32)
+            return MOE_ERR_UNSUPPORTED;
+    } else if (act == MOE_BF16) {
+        if (w != MOE_BF16 && w != MOE_FP8_E4M3FN)
+            return MOE_ERR_UNSUPPORTED;
+    } else if (act == MOE_FP8_E4M3FN) {
+        if (w != MOE_FP8_E4M3FN || p->format != MOE_FMT_BATCHED)
+            return MOE_ERR_UNSUPPORTED;
+    } else {
+        return MOE_ERR_UNSUPPORTED;
+    }
+    if (w == MOE_FP8_E4M3FN && p->I % 128)
+        return MOE_ERR_UNSUPPORTED;
+
+    if (p->format == MOE_FMT_BATCHED) {
+        if (p->max_tokens < 1)
+            return MOE_ERR_INVALID_ARG;
+        if ((int64_t)p->E * p->max_tokens >= (1ll << 30))
+            return MOE_ERR_UNSUPPORTED;
+        if (p->batched_reduce != 0 && p->batched_reduce != 1)
+            return MOE_ERR_INVALID_ARG;
+        return MOE_OK;                        // routing happened upstream
+    }
+
+    if (p->routing != MOE_ROUTE_SOFTMAX && p->routing != MOE_ROUTE_SIGMOID &&
+        p->routing != MOE_ROUTE_PRECOMPUTED)
+        return MOE_ERR_INVALID_ARG;
+    if (p->routing == MOE_ROUTE_PRECOMPUTED)
+        return MOE_OK;
+    if (p->logits_dtype != MOE_F32 && p->logits_dtype != MOE_BF16)
+        return MOE_ERR_UNSUPPORTED;
+    if (!std::isfinite(p->routed_scaling_factor))
+        return MOE_ERR_INVALID_ARG;
+    // grouped routing constraints (MindIE-SD page, routing-selection section)
+    const int G = p->group_count, kg = p->k_group;
+    if (G < 1 || kg < 1 || kg > G)
+        return MOE_ERR_INVALID_ARG;
+    if (p->E % G)
+        return MOE_ERR_INVALID_ARG;
+    if (p->group_select_mode != 0 && p->group_select_mode != 1)
+        return MOE_ERR_INVALID_ARG;
+    if (G > 1) {
+        if (G > 64)
+            return MOE_ERR_UNSUPPORTED;
+        if (p->top_k > kg * (p->E / G))
+            return MOE_ERR_INVALID_ARG;
+        if (p->group_select_mode == 1 && p->E / G < 2)
+            return MOE_ERR_INVALID_ARG;
+    }
+    return MOE_OK;
+}
+
+// Rows per M-block: the smallest MFMA-friendly block that holds the average
+// expert load, so decode-sized batches do not pad to 128 rows.
+static int choose_block_m(const moe_problem* p, int64_t rows_cap)
+{
+    if (p->w_dtype == MOE_FP8_E4M3FN)
+        return 128;
+    const double avg = (double)rows_cap / p->E;
+    if (avg <= 16)
+        return 16;
+    if (avg <= 32)
+        return 32;
+    if (avg <= 64)
+        return 64;
+    return 128;
+}
+
+static int layout(const moe_problem* p, moe_workspace_info* info)
+{
+    const int rc = validate(p);
+    if (rc != MOE_OK)
+        return rc;
+    moe_workspace_info w{};
+    const bool batched = p->format == MOE_FMT_BATCHED;
+    const int64_t MK = (int64_t)p->M * p->top_k;
+    int64_t rows_cap = MK;
+    if (batched) {
+        rows_cap = (int64_t)p->E * p->max_tokens;
+        if (p->M > 0 && MK < rows_cap)
+            rows_cap = MK;   // every valid slab row is one routed copy of a token
+    }
+    const int BM = choose_block_m(p, rows_cap);
+    const int64_t max_sorted = rows_cap + (int64_t)p->E * (BM - 1);
+    const bool fp8 = p->w_dtype == MOE_FP8_E4M3FN;
+    const int zes = fp8 ? 1 : (p->act_dtype == MOE_F32 ? 4 : 2);
+
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes);
+        return o;
+    };
+    w.block_m = BM;
+    w.max_sorted_len = max_sorted;
+    w.max_blocks = (int32_t)(max_sorted / BM);
+    w.off_topk_ids = take(batched ? 0 : MK * 4);
+    w.off_topk_weights = take(batched ? 0 : MK * 4);
+    w.off_expert_counts = take((size_t)p->E * 4);
+    w.off_expert_offsets = take((size_t)(p->E + 1) * 4);
+    w.off_sorted_ids = take((size_t)max_sorted * 4);
+    w.off_expert_ids = take((size_t)w.max_blocks * 4);
+    w.off_num_post_padded = take(4);
+    const bool quant = fp8 && p->act_dtype != MOE_FP8_E4M3FN;
+    const int64_t qrows = batched ? max_sorted : p->M;
+    w.off_aq = take(quant ? (size_t)qrows * p->H : 0);
+    w.off_aq_scale = take(quant ? (size_t)qrows * 4 : 0);
+    w.off_z = take((size_t)max_sorted * p->I * zes);
+    w.off_z_scale = take(fp8 ? (size_t)max_sorted * (p->I / 128) * 4 : 0);
+    const int64_t orows = batched ? (p->batched_reduce ? max_sorted : 0) : MK;
+    w.off_o = take((size_t)orows * p->H * 4);
+    w.bytes = off;
+    *info = w;
+    return MOE_OK;
+}
+
+static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* ws)
+{
+    Plan P{};
+    P.fmt = p->format;
+    P.M = p->M;
+    P.H = p->H;
+    P.I = p->I;
+    P.E = p->E;
+    P.K = p->top_k;
+    P.T = p->max_tokens;
+    P.act = p->act_dtype;
+    P.wdt = p->w_dtype;
+    P.outdt = p->out_dtype;
+    P.lgdt = p->logits_dtype;
+    P.routing = p->routing;
+    P.renorm = p->renormalize ? 1 : 0;
+    P.G = p->group_count < 1 ? 1 : p->group_count;
+    P.kg = p->k_group;
+    P.gmode = p->group_select_mode;
+    P.rsf = p->routed_scaling_factor;
+    P.has_b13 = p->has_w13_bias ? 1 : 0;
+    P.has_b2 = p->has_w2_bias ? 1 : 0;
+    P.breduce = p->batched_reduce ? 1 : 0;
+    P.BM = w.block_m;
+    P.max_sorted = w.max_sorted_len;
+    P.max_blocks = w.max_blocks;
+    P.rows_cap = w.max_sorted_len - (int64_t)p->E * (w.block_m - 1);
+    P.sentinel = (p->format == MOE_FMT_BATCHED) ? (int64_t)p->E * p->max_tokens
+                                                 : (int64_t)p->M * p->top_k;
+    P.topk_ids = (int32_t*)(ws + w.off_topk_ids);
+    P.topk_w = (float*)(ws + w.off_topk_weights);
+    P.counts = (int32_t*)(ws + w.off_expert_counts);
+    P.offsets = (int32_t*)(ws + w.off_expert_offsets);
+    P.sorted_ids = (int32_t*)(ws + w.off_sorted_ids);
+    P.expert_ids = (int32_t*)(ws + w.off_expert_ids);
+    P.npp = (int32_t*)(ws + w.off_num_post_padded);
+    P.aq = (uint8_t*)(ws + w.off_aq);
+    P.aq_scale = (float*)(ws + w.off_aq_scale);
+    P.z = ws + w.off_z;
+    P.z_scale = (float*)(ws + w.off_z_scale);
+    P.o = (float*)(ws + w.off_o);
+    return P;
+}
+
+static int check_args(const moe_problem* p, const moe_args* a)
+{
+    if (!a || !a->w13 || !a->w2 || !a->out)
+        return MOE_ERR_INVALID_ARG;
+    if (!a->hidden)
+        return MOE_ERR_INVALID_ARG;
+    if ((p->has_w13_bias && !a->w13_bias) || (p->has_w2_bias && !a->w2_bias))
+        return MOE_ERR_INVALID_ARG;
+    if (p->w_dtype == MOE_FP8_E4M3FN && (!a->w13_scale || !a->w2_scale))
+        return MOE_ERR_INVALID_ARG;
+    if (p->act_dtype == MOE_FP8_E4M3FN && !a->a_scale)
+        return MOE_ERR_INVALID_ARG;
+    if (p->format == MOE_FMT_BATCHED) {
+        if (!a->expert_num_tokens)
+            return MOE_ERR_INVALID_ARG;
+        if (p->batched_reduce && (!a->token_map || !a->token_map_w))
+            return MOE_ERR_INVALID_ARG;
+        return MOE_OK;
+    }
+    if (p->routing == MOE_ROUTE_PRECOMPUTED) {
+        if (!a->topk_ids || !a->topk_weights)
+            return MOE_ERR_INVALID_ARG;
+    } else if (!a->router_logits) {
+        return MOE_ERR_INVALID_ARG;
+    }
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* info)
+{
+    if (!info)
+        return MOE_ERR_INVALID_ARG;
+    return layout(p, info);
+}
+
+static int forward(const moe_problem* p, const moe_args* a, void* workspace,
+                   size_t workspace_bytes, void* stream, void** events)
+{
+    moe_workspace_info w;
+    int rc = layout(p, &w);
+    if (rc != MOE_OK)
+        return rc;
+    rc = check_args(p, a);
+    if (rc != MOE_OK)
+        return rc;
+    if (!workspace || ((uintptr_t)workspace % ALIGN) || workspace_bytes < w.bytes)
+        return MOE_ERR_WORKSPACE;
+
+    const hipStream_t s = (hipStream_t)stream;
+    const Plan P = make_plan(p, w, (char*)workspace);
+    const bool batched = p->format == MOE_FMT_BATCHED;
+    if (!batched && p->M == 0)
+        return MOE_OK;                                   // nothing routed
+    if (batched && p->batched_reduce && p->M == 0)
+        return MOE_OK;
+
+    hipError_t err;
+    int stage = 0;
+    auto mark = [&](int st, int end) {
+        if (events && events[2 * st + end])
+            (void)hipEventRecord((hipEvent_t)events[2 * st + end], s);
+    };
+#define MOE_TRY(st, call)              \
+    do {                               \
+        stage = (st);                  \
+        mark(stage, 0);                \
+        err = (call);                  \
+        mark(stage, 1);                \
+        if (err != hipSuccess)         \
+            return MOE_ERR_LAUNCH;     \
+    } while (0)
+
+    const float* weights = nullptr;
+    if (!batched) {
+        const int32_t* ids;
+        if (p->routing == MOE_ROUTE_PRECOMPUTED) {
+            ids = a->topk_ids;
+            weights = a->topk_weights;
+        } else {
+            MOE_TRY(MOE_STAGE_ROUTER, launch_router(P, a->router_logits, s));
+            ids = P.topk_ids;
+            weights = P.topk_w;
+        }
+        MOE_TRY(MOE_STAGE_ALIGN, launch_align(P, ids, s));
+    } else {
+        MOE_TRY(MOE_STAGE_ALIGN, launch_tilelist(P, a->expert_num_tokens, s));
+    }
+    if (p->w_dtype == MOE_FP8_E4M3FN && p->act_dtype != MOE_FP8_E4M3FN)
+        MOE_TRY(MOE_STAGE_QUANT, launch_quant_rows(P, a->hidden, s));
+    MOE_TRY(MOE_STAGE_GEMM1, launch_gemm1(P, *a, s));
+    MOE_TRY(MOE_STAGE_GEMM2, launch_gemm2(P, *a, s));
+    if (!batched || p->batched_reduce)
+        MOE_TRY(MOE_STAGE_REDUCE, launch_reduce(P, *a, weights, s));
+#undef MOE_TRY
+    (void)stage;
+    return MOE_OK;
+}
+
+extern "C" int moe_forward(const moe_problem* p, const moe_args* a, void* workspace,
+                           size_t workspace_bytes, void* stream)
+{
+    return forward(p, a, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int moe_forward_timed(const moe_problem* p, const moe_args* a, void* workspace,
+                                 size_t workspace_bytes, void* stream, void** events)
+{
+    return forward(p, a, workspace, workspace_bytes, stream, events);
+}
+
+extern "C" const char* moe_status_string(int status)
+{
+    switch (status) {
+    case MOE_OK: return "success";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+extern "C" const char* moe_version(void) { return "0.1.0"; }

@@ -1,0 +1,146 @@
+// Internal declarations shared by the HIP sources of libmoe (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ vector types
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16;
+
+// ------------------------------------------------------------------ scalar formats
+__device__ __forceinline__ float bf16_to_f32(u16 b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even float -> bf16 (NaN stays NaN).
+__device__ __forceinline__ u16 f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (u16)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (u16)(u >> 16);
+}
+
+// E4M3FN code -> float (exact).
+__device__ __forceinline__ float fp8_to_f32(uint8_t c)
+{
+    const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    float v;
+    if (e == 15 && m == 7)
+        return __uint_as_float(0x7fc00000u);
+    v = (e == 0) ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+    return s ? -v : v;
+}
+
+// float -> E4M3FN, round to nearest even, saturating at +-448.  Integer
+// arithmetic on the float's bits, so the result does not depend on any
+// hardware conversion mode.
+__device__ __forceinline__ uint8_t f32_to_fp8(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u)
+        return 0x7f;                                    // NaN
+    if (a >= 0x43e00000u)                               // |x| >= 448 (incl. inf)
+        return (uint8_t)(sign | 0x7e);
+    const int exp = (int)(a >> 23) - 127;               // unbiased exponent of |x|
+    uint32_t code;
+    if (exp < -6) {
+        // subnormal range: value = m * 2^-9, m = round(|x| * 2^9)
+        // |x| * 2^9 as a fixed-point number with 23+... fractional bits:
+        // mantissa with hidden bit, shifted so that the unit is 2^-9.
+        if (exp < -10)                                  // below half the smallest step
+            return (uint8_t)sign;                       // |x| < 2^-10 rounds to 0
+        const uint32_t mant = (a & 0x7fffffu) | 0x800000u;   // |x| = mant * 2^(exp-23)
+        const int shift = 23 - 9 - exp;                 // mant >> shift = |x| * 2^9
+        const uint32_t q = mant >> shift;
+        const uint32_t rem = mant & ((1u << shift) - 1u);
+        const uint32_t half = 1u << (shift - 1);
+        code = q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u);   // may carry to 8 = 2^-6
+    } else {
+        // normal: keep 3 mantissa bits, round the dropped 20 bits to nearest even
+        const uint32_t mant = a & 0x7fffffu;
+        const uint32_t q = ((uint32_t)(exp + 7) << 3) | (mant >> 20);
+        const uint32_t rem = mant & 0xfffffu;
+        code = q + ((rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u);
+        if (code > 0x7eu)
+            code = 0x7eu;
+    }
+    return (uint8_t)(sign | code);
+}
+
+// ------------------------------------------------------------------ wave helpers
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        unsigned long long w = __shfl_xor(v, o, 64);
+        v = (w > v) ? w : v;
+    }
+    return v;
+}
+
+// ------------------------------------------------------------------ execution plan
+// Host-computed description of one call: problem, tile choice, device pointers.
+struct Plan {
+    int fmt, M, H, I, E, K, T;      // K = top_k, T = max_tokens
+    int act, wdt, outdt, lgdt, routing;
+    int renorm, G, kg, gmode;
+    float rsf;
+    int has_b13, has_b2, breduce;
+    int BM;                         // rows per M-block (align granularity)
+    int64_t rows_cap;               // upper bound of valid routed rows
+    int64_t max_sorted;             // rows_cap + E * (BM - 1)
+    int max_blocks;                 // max_sorted / BM
+    int64_t sentinel;               // sorted-id value of padding rows
+    // workspace
+    int32_t* topk_ids;
+    float* topk_w;
+    int32_t* counts;
+    int32_t* offsets;               // [E + 1] padded prefix (P_e)
+    int32_t* sorted_ids;
+    int32_t* expert_ids;
+    int32_t* npp;
+    uint8_t* aq;
+    float* aq_scale;
+    void* z;
+    float* z_scale;
+    float* o;
+};
+
+// launchers (each returns hipGetLastError() of its launch)
+hipError_t launch_router(const Plan& P, const void* logits, hipStream_t s);
+hipError_t launch_align(const Plan& P, const int32_t* ids, hipStream_t s);
+hipError_t launch_tilelist(const Plan& P, const int32_t* expert_num_tokens, hipStream_t s);
+hipError_t launch_quant_rows(const Plan& P, const void* hidden, hipStream_t s);
+hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s);
+hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s);
+hipError_t launch_reduce(const Plan& P, const moe_args& A, const float* topk_w, hipStream_t s);
+
+}  // namespace moe

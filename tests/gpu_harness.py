@@ -1,0 +1,176 @@
+"""Shared helpers of the GPU tests: run the HIP path through the C ABI on
+seeded inputs, read its intermediates back from the workspace, and check
+them and the output against the CPU oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from mixture_experts_ffn_router_amd import binding as B
+from mixture_experts_ffn_router_amd import workloads as W
+
+# Output tolerances: max |gpu - oracle| over the checked outputs, against the
+# oracle's unrounded (double) result.  float32 absolute; bf16 and fp8
+# relative to the RMS of the oracle output.  The bound applies to the
+# computed result, which the path can hand out in float32; its bf16 output is
+# that float32 result rounded once to nearest-even (checked bit for bit), so a
+# bf16 output may differ from the oracle by the bound plus half a bf16 ulp --
+# storage rounding that on its own exceeds 2e-2 x RMS wherever |y| > 5.12 RMS.
+TOL_F32_ABS = 1e-4
+TOL_BF16_RMS = 2e-2
+TOL_FP8_RMS = 6e-2
+TOL_WEIGHT = 1e-5          # routing weights, relative to max(1, routed_scaling_factor)
+
+
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    return torch.device("cuda:0")
+
+
+def region(ws: torch.Tensor, off: int, dtype, count: int) -> np.ndarray:
+    nbytes = count * torch.empty(0, dtype=dtype).element_size()
+    return ws[off:off + nbytes].view(dtype).cpu().numpy()
+
+
+def run_contiguous(inp: dict, dev, precomputed=None, out=None, inplace=False, out_dtype=None):
+    """One forward of a contiguous workload; returns (out, ws, info).
+    out_dtype=None keeps the workload's own output type."""
+    cfg: W.MoeConfig = inp["cfg"]
+    hidden = inp["hidden"].to(dev)
+    kw = dict(out_dtype=out_dtype, top_k=cfg.top_k, renormalize=cfg.renormalize, routing=cfg.scoring,
+              group_count=cfg.group_count, k_group=cfg.k_group,
+              group_select_mode=cfg.group_select_mode,
+              routed_scaling_factor=cfg.routed_scaling_factor)
+    w13, w2 = inp["w13"].to(dev), inp["w2"].to(dev)
+    for name in ("w13_bias", "w2_bias", "w13_scale", "w2_scale"):
+        if inp.get(name) is not None:
+            kw[name] = inp[name].to(dev)
+    logits = None
+    if precomputed is not None:
+        kw["topk_ids"] = torch.as_tensor(precomputed[0], dtype=torch.int32).to(dev)
+        kw["topk_weights"] = torch.as_tensor(precomputed[1], dtype=torch.float32).to(dev)
+    else:
+        logits = inp["logits"].to(dev)
+    if inplace:
+        out = hidden
+    res = B.fused_moe(hidden, w13, w2, logits, out=out, **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle_route(inp: dict):
+    cfg = inp["cfg"]
+    return oracle.route(inp["logits"].cpu(), cfg.top_k, scoring=cfg.scoring,
+                        renormalize=cfg.renormalize, group_count=cfg.group_count,
+                        k_group=cfg.k_group, group_select_mode=cfg.group_select_mode,
+                        routed_scaling_factor=cfg.routed_scaling_factor)
+
+
+def check_routing_and_align(inp: dict, ws, info, ids_o=None, w_o=None, check_weights=True):
+    """Bit-exact topk ids, counts, sorted ids, expert ids, num_post_padded;
+    routing weights within TOL_WEIGHT.  Returns the oracle (ids, weights)."""
+    cfg = inp["cfg"]
+    M, K, E = cfg.M, cfg.top_k, cfg.E
+    if ids_o is None:
+        ids_o, w_o = oracle_route(inp)
+        ids_g = region(ws, info.off_topk_ids, torch.int32, M * K).reshape(M, K)
+        w_g = region(ws, info.off_topk_weights, torch.float32, M * K).reshape(M, K)
+        bad = np.argwhere(ids_g != ids_o)
+        assert bad.size == 0, f"topk ids differ at {bad[:5].tolist()}"
+        if check_weights:
+            err = np.abs(w_g - w_o).max()
+            assert err <= TOL_WEIGHT * max(1.0, cfg.routed_scaling_factor), err
+    BM = info.block_m
+    counts_o, sorted_o, eids_o, npp_o = oracle.align(ids_o, E, BM)
+    npp = int(region(ws, info.off_num_post_padded, torch.int32, 1)[0])
+    assert npp == npp_o
+    assert np.array_equal(region(ws, info.off_expert_counts, torch.int32, E), counts_o)
+    assert np.array_equal(region(ws, info.off_sorted_ids, torch.int32, npp), sorted_o)
+    assert np.array_equal(region(ws, info.off_expert_ids, torch.int32, npp // BM), eids_o)
+    return ids_o, w_o
+
+
+def oracle_experts(inp: dict) -> oracle.Experts:
+    cfg = inp["cfg"]
+    return oracle.Experts(inp["w13"].cpu(), inp["w2"].cpu(),
+                          None if inp.get("w13_scale") is None else inp["w13_scale"].cpu(),
+                          None if inp.get("w2_scale") is None else inp["w2_scale"].cpu(),
+                          None if inp.get("w13_bias") is None else inp["w13_bias"].cpu(),
+                          None if inp.get("w2_bias") is None else inp["w2_bias"].cpu(),
+                          requant_z=cfg.weight == "fp8")
+
+
+def compare(cfg: W.MoeConfig, got: np.ndarray, ref: np.ndarray, what: str = "") -> float:
+    """Applies the dtype's tolerance; returns the error in tolerance units."""
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = float(np.abs(got.astype(np.float64) - ref).max()) if ref.size else 0.0
+    if cfg.weight == "f32":
+        bound = TOL_F32_ABS
+    else:
+        rms = float(np.sqrt(np.mean(ref ** 2)))
+        bound = (TOL_FP8_RMS if cfg.weight == "fp8" else TOL_BF16_RMS) * rms
+    print(f"[parity] {cfg.name} {what} max_abs_err={err:.3e} bound={bound:.3e} "
+          f"ratio={err / bound if bound else 0:.3f}", flush=True)
+    assert err <= bound, f"{what}: max abs err {err} > {bound}"
+    return err / bound
+
+
+def check_output(inp: dict, out: torch.Tensor, ids_o, w_o, tokens=None, what=""):
+    cfg = inp["cfg"]
+    acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8")
+    y, _ = oracle.forward_tokens(oracle_experts(inp), acts, ids_o, w_o, tokens=tokens)
+    got = out.float().cpu().numpy()
+    if tokens is not None:
+        got = got[np.asarray(tokens)]
+    return compare(cfg, got, y, what)
+
+
+def run_batched(inp: dict, dev, reduce=False, out_dtype=None):
+    cfg = inp["cfg"]
+    kw = {"out_dtype": out_dtype}
+    for name in ("w13_scale", "w2_scale", "w13_bias", "w2_bias"):
+        if inp.get(name) is not None:
+            kw[name] = inp[name].to(dev)
+    if reduce:
+        kw["token_map"] = inp["token_map"].to(dev)
+        kw["token_map_w"] = inp["token_map_w"].to(dev)
+    res = B.fused_moe_batched(inp["hidden"].to(dev), inp["expert_num_tokens"].to(dev),
+                              inp["w13"].to(dev), inp["w2"].to(dev), M=cfg.M, top_k=cfg.top_k,
+                              **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+def check_batched_tilelist(inp, ws, info):
+    cfg = inp["cfg"]
+    T, BM = inp["max_tokens"], info.block_m
+    counts = inp["expert_num_tokens"].cpu().numpy()
+    npp = int(region(ws, info.off_num_post_padded, torch.int32, 1)[0])
+    padded = -(-counts // BM) * BM
+    assert npp == padded.sum()
+    sorted_g = region(ws, info.off_sorted_ids, torch.int32, npp)
+    ref = np.concatenate([np.concatenate([e * T + np.arange(c), np.full(p - c, cfg.E * T)])
+                          for e, (c, p) in enumerate(zip(counts, padded))]).astype(np.int32)
+    assert np.array_equal(sorted_g, ref)
+    eids = region(ws, info.off_expert_ids, torch.int32, npp // BM)
+    assert np.array_equal(eids, np.repeat(np.arange(cfg.E), padded // BM))
+
+
+def batched_rows(inp, sample=None):
+    """(flat slab rows, expert of each row) of the valid rows, optionally a sample."""
+    T = inp["max_tokens"]
+    counts = inp["expert_num_tokens"].cpu().numpy()
+    rows = np.concatenate([e * T + np.arange(c) for e, c in enumerate(counts)])
+    if sample is not None and sample < rows.size:
+        rng = np.random.default_rng(0)
+        rows = np.sort(rng.choice(rows, size=sample, replace=False))
+    return rows.astype(np.int64), (rows // T).astype(np.int32)
+
+
+def check_rounded(out16: torch.Tensor, out32: torch.Tensor):
+    """The bf16 output is the float32 result rounded to nearest-even, bit for bit."""
+    assert out16.dtype == torch.bfloat16 and out32.dtype == torch.float32
+    ref = out32.to(torch.bfloat16)
+    same = out16.view(torch.int16) == ref.view(torch.int16)
+    assert bool(same.all()), f"{int((~same).sum())} bf16 outputs are not RNE(float32 result)"

@@ -1,0 +1,152 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/moe.h declares, the ctypes mirrors match the header's struct layout,
+and host-side validation returns the documented status codes before any
+device work (so fake device pointers are never touched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mixture_experts_ffn_router_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load()
+    decl = re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(moe_\w+)\s*\(", open(HEADER).read(), re.M)
+    assert set(decl) == set(B.EXPORTED)
+    for name in decl:
+        assert hasattr(lib, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    for name in decl:
+        assert re.search(rf"\bT {name}$", nm, re.M), name
+    assert B.moe_version().count(".") == 2
+
+
+def test_struct_layout_matches_header(tmp_path):
+    fields = {"moe_problem": B.moe_problem, "moe_workspace_info": B.moe_workspace_info,
+              "moe_args": B.moe_args}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void){"]
+    for st, cls in fields.items():
+        lines.append(f'printf("{st} size %zu\\n", sizeof({st}));')
+        for f, _ in cls._fields_:
+            lines.append(f'printf("{st}.{f} %zu\\n", offsetof({st}, {f}));')
+    lines.append("return 0;}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    got = dict(l.rsplit(" ", 1) for l in out.strip().splitlines())
+    for st, cls in fields.items():
+        assert int(got[f"{st} size"]) == ctypes.sizeof(cls), st
+        for f, _ in cls._fields_:
+            assert int(got[f"{st}.{f}"]) == getattr(cls, f).offset, (st, f)
+
+
+def _prob(**kw):
+    base = dict(M=16, H=64, I=128, E=8, top_k=2, act_dtype=B.MOE_BF16, w_dtype=B.MOE_BF16,
+                out_dtype=B.MOE_BF16, logits_dtype=B.MOE_BF16, renormalize=True)
+    base.update(kw)
+    return B.Problem(**base)
+
+
+def _status(prob):
+    info = B.moe_workspace_info()
+    return B.load().moe_workspace_shapes(ctypes.byref(prob.c()), ctypes.byref(info))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), B.MOE_OK),
+    (dict(top_k=9), B.MOE_ERR_INVALID_ARG),                 # top_k in [1, E]
+    (dict(top_k=0), B.MOE_ERR_INVALID_ARG),
+    (dict(E=0), B.MOE_ERR_INVALID_ARG),
+    (dict(M=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(group_count=3), B.MOE_ERR_INVALID_ARG),           # E % group_count
+    (dict(group_count=4, k_group=5), B.MOE_ERR_INVALID_ARG),  # k_group in [1, G]
+    (dict(group_count=4, k_group=0), B.MOE_ERR_INVALID_ARG),
+    (dict(group_count=1, k_group=2), B.MOE_ERR_INVALID_ARG),
+    (dict(group_count=4, k_group=1, top_k=3), B.MOE_ERR_INVALID_ARG),  # top_k > k_group*E/G
+    (dict(group_count=8, k_group=2, group_select_mode=1), B.MOE_ERR_INVALID_ARG),  # 1 expert/group
+    (dict(group_count=4, k_group=2, group_select_mode=2), B.MOE_ERR_INVALID_ARG),
+    (dict(routing=7), B.MOE_ERR_INVALID_ARG),
+    (dict(routed_scaling_factor=float("nan")), B.MOE_ERR_INVALID_ARG),
+    (dict(H=72), B.MOE_ERR_UNSUPPORTED),                     # H % 16
+    (dict(I=40), B.MOE_ERR_UNSUPPORTED),
+    (dict(E=2048, top_k=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=B.MOE_F32), B.MOE_ERR_UNSUPPORTED),      # f32 act needs f32 weights/out
+    (dict(act_dtype=B.MOE_F32, w_dtype=B.MOE_F32, out_dtype=B.MOE_F32), B.MOE_OK),
+    (dict(w_dtype=B.MOE_FP8_E4M3FN), B.MOE_OK),
+    (dict(w_dtype=B.MOE_FP8_E4M3FN, I=144), B.MOE_ERR_UNSUPPORTED),   # fp8 groups of 128
+    (dict(act_dtype=B.MOE_FP8_E4M3FN, w_dtype=B.MOE_FP8_E4M3FN), B.MOE_ERR_UNSUPPORTED),
+    (dict(routing=B.MOE_ROUTE_PRECOMPUTED, group_count=3), B.MOE_OK),  # routing params unused
+    (dict(fmt=B.MOE_FMT_BATCHED, max_tokens=0), B.MOE_ERR_INVALID_ARG),
+    (dict(fmt=B.MOE_FMT_BATCHED, max_tokens=32, act_dtype=B.MOE_FP8_E4M3FN,
+          w_dtype=B.MOE_FP8_E4M3FN), B.MOE_OK),
+])
+def test_problem_validation(kw, status):
+    assert _status(_prob(**kw)) == status
+
+
+def test_workspace_layout_is_aligned_and_sized():
+    for kw in [dict(), dict(M=4096, H=7168, I=2048, E=256, top_k=8),
+               dict(w_dtype=B.MOE_FP8_E4M3FN, I=256),
+               dict(fmt=B.MOE_FMT_BATCHED, max_tokens=64, w_dtype=B.MOE_FP8_E4M3FN, I=256,
+                    batched_reduce=True)]:
+        p = _prob(**kw)
+        info = B.moe_workspace_shapes(p.c())
+        offs = [getattr(info, f) for f, _ in B.moe_workspace_info._fields_ if f.startswith("off_")]
+        assert all(o % 256 == 0 for o in offs)
+        assert info.bytes >= max(offs)
+        assert info.max_sorted_len >= min(p.M * p.top_k, p.E * max(p.max_tokens, 1)) + \
+            p.E * (info.block_m - 1) or p.fmt == B.MOE_FMT_BATCHED
+        assert info.max_blocks == info.max_sorted_len // info.block_m
+        assert info.block_m in (16, 32, 64, 128)
+
+
+def test_block_m_follows_expert_load():
+    assert B.moe_workspace_shapes(_prob(M=32, H=2048, I=768, E=128, top_k=8).c()).block_m == 16
+    assert B.moe_workspace_shapes(_prob(M=512, H=4096, I=14336, E=8, top_k=2).c()).block_m == 128
+
+
+def _args(**kw):
+    fake = 4096   # never dereferenced: every case below fails validation on the host
+    base = dict(hidden=fake, w13=fake, w2=fake, out=fake, router_logits=fake)
+    base.update(kw)
+    a = B.moe_args()
+    for k, v in base.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,pkw,status", [
+    (dict(router_logits=None), dict(), B.MOE_ERR_INVALID_ARG),
+    (dict(hidden=None), dict(), B.MOE_ERR_INVALID_ARG),
+    (dict(out=None), dict(), B.MOE_ERR_INVALID_ARG),
+    (dict(), dict(has_w13_bias=True), B.MOE_ERR_INVALID_ARG),
+    (dict(), dict(has_w2_bias=True), B.MOE_ERR_INVALID_ARG),
+    (dict(), dict(routing=B.MOE_ROUTE_PRECOMPUTED), B.MOE_ERR_INVALID_ARG),
+    (dict(), dict(w_dtype=B.MOE_FP8_E4M3FN), B.MOE_ERR_INVALID_ARG),      # scales missing
+    (dict(), dict(fmt=B.MOE_FMT_BATCHED, max_tokens=8), B.MOE_ERR_INVALID_ARG),
+])
+def test_forward_rejects_missing_pointers(kw, pkw, status):
+    p = _prob(**pkw).c()
+    rc = B.moe_forward_status(p, _args(**kw), 1 << 20, 1 << 40, 0)
+    assert rc == status
+
+
+def test_forward_rejects_bad_workspace():
+    p = _prob()
+    info = B.moe_workspace_shapes(p.c())
+    assert B.moe_forward_status(p.c(), _args(), 0, info.bytes, 0) == B.MOE_ERR_WORKSPACE
+    assert B.moe_forward_status(p.c(), _args(), 256 * 1024 + 8, info.bytes, 0) == \
+        B.MOE_ERR_WORKSPACE
+    assert B.moe_forward_status(p.c(), _args(), 256 * 1024, info.bytes - 1, 0) == \
+        B.MOE_ERR_WORKSPACE
+    assert B.moe_status_string(B.MOE_ERR_WORKSPACE).startswith("workspace")

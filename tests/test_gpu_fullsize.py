@@ -1,0 +1,63 @@
+"""Parity at the full workload sizes, in the launch configuration the
+benchmark times.  Every routing / align result is compared bit for bit; the
+oracle computes a sample of output rows one by one (first, last and random
+tokens), which keeps each case within a minute."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as GH
+import oracle
+from mixture_experts_ffn_router_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+FULL = [W.TINY_F32, W.MIXTRAL_PREFILL, W.DECODE_SMALL_EXPERTS, W.DEEPSEEK_GROUPED]
+
+
+def _sample_tokens(M, n=16, seed=0):
+    rng = np.random.default_rng(seed)
+    extra = rng.choice(np.arange(1, max(M - 1, 1)), size=min(n, max(M - 2, 0)), replace=False)
+    return np.unique(np.concatenate([[0, M - 1], extra])).astype(np.int64)
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
+def test_full_size_contiguous(cfg):
+    dev = GH.device()
+    seed = 1000 + W.CONFIGS.index(cfg)
+    print(f"[case] {cfg.name} seed={seed} generating", flush=True)
+    inp = W.make_inputs(cfg, seed, device=dev)
+    out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+    print(f"[case] {cfg.name} ran; block_m={info.block_m}", flush=True)
+    ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    counts = np.bincount(ids_o.ravel(), minlength=cfg.E)
+    print(f"[case] {cfg.name} active experts={int((counts > 0).sum())} "
+          f"rows/expert max={counts.max()} min={counts.min()}", flush=True)
+    tokens = None if cfg.M <= 64 else _sample_tokens(cfg.M)
+    GH.check_output(inp, out, ids_o, w_o, tokens=tokens, what="full")
+    if cfg.out_dtype == "bf16":
+        out16, _, _ = GH.run_contiguous(inp, dev)
+        GH.check_rounded(out16, out)
+
+
+def test_full_size_batched_fp8():
+    cfg = W.BATCHED_FP8
+    dev = GH.device()
+    seed = 1000 + W.CONFIGS.index(cfg)
+    print(f"[case] {cfg.name} seed={seed} generating", flush=True)
+    inp = W.make_inputs(cfg, seed, device=dev)
+    counts = inp["expert_num_tokens"].cpu().numpy()
+    print(f"[case] {cfg.name} rows/expert max={counts.max()} min={counts.min()} "
+          f"total={counts.sum()}", flush=True)
+    out, ws, info = GH.run_batched(inp, dev, out_dtype=torch.float32)
+    GH.check_batched_tilelist(inp, ws, info)
+    rows, experts = GH.batched_rows(inp, sample=48)
+    acts = oracle.Acts(inp["hidden"].cpu(), quantize=True)
+    o_ref, _ = oracle.expert_rows(GH.oracle_experts(inp), acts, rows, experts)
+    got = out.reshape(-1, cfg.H)[torch.as_tensor(rows, device=dev)].cpu().numpy()
+    GH.compare(cfg, got, o_ref, "full batched rows")
+    out16, _, _ = GH.run_batched(inp, dev)
+    idx = torch.as_tensor(rows, device=dev)
+    GH.check_rounded(out16.reshape(-1, cfg.H)[idx], out.reshape(-1, cfg.H)[idx])
+    # invalid (NaN-filled) rows never leak into valid outputs
+    assert torch.isfinite(out.reshape(-1, cfg.H)[idx]).all()

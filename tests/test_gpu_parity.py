@@ -1,0 +1,165 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact: topk ids, per-expert counts, sorted ids, expert ids and
+num_post_padded.  Within tolerance: routing weights and outputs (float32
+max-abs 1e-4; bf16 2e-2 x RMS; fp8 6e-2 x RMS of the oracle output).
+Small shapes compare every output; the full workload shapes compare every
+routing/align result and a sample of output rows."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as GH
+from mixture_experts_ffn_router_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    W.TINY_F32,
+    W.MIXTRAL_PREFILL.scaled(name="mixtral_small", M=96, H=256, I=512),
+    W.MIXTRAL_PREFILL.scaled(name="mixtral_bm128", M=384, H=128, I=256, E=4),
+    W.DECODE_SMALL_EXPERTS.scaled(name="decode_small", M=8, H=256, I=128, E=32, top_k=4),
+    W.DEEPSEEK_GROUPED.scaled(name="deepseek_small", M=64, H=256, I=128, E=64),
+    W.DEEPSEEK_GROUPED.scaled(name="grouped_softmax_small", M=48, H=128, I=64, E=32,
+                              scoring="softmax", renormalize=True, group_count=4, k_group=2,
+                              group_select_mode=1, top_k=4, routed_scaling_factor=1.0),
+    W.MIXTRAL_PREFILL.scaled(name="contig_fp8_small", M=64, H=256, I=256, weight="fp8"),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+@pytest.mark.parametrize("seed_off", [0, 1000, 1001])
+def test_small_parity(cfg, seed_off):
+    dev = GH.device()
+    seed = 1000 + SMALL.index(cfg) + seed_off
+    print(f"[case] {cfg.name} seed={seed}", flush=True)
+    inp = W.make_inputs(cfg, seed)
+    out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+    ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    GH.check_output(inp, out, ids_o, w_o, what=f"seed{seed}")
+    if cfg.out_dtype == "bf16":
+        out16, _, _ = GH.run_contiguous(inp, dev)
+        GH.check_rounded(out16, out)
+
+
+def test_tied_integer_logits_route_bit_exact():
+    """Integer-valued logits: many exact ties, broken toward the lower index."""
+    dev = GH.device()
+    for cfg in (W.DEEPSEEK_GROUPED.scaled(name="ties_grouped", M=128, H=64, I=64, E=64),
+                W.DECODE_SMALL_EXPERTS.scaled(name="ties_plain", M=128, H=64, I=64, E=128)):
+        inp = W.make_inputs(cfg, 77)
+        g = torch.Generator().manual_seed(5)
+        inp["logits"] = torch.randint(-2, 3, (cfg.M, cfg.E), generator=g).to(torch.bfloat16)
+        out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+        ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+        GH.check_output(inp, out, ids_o, w_o, what="ties")
+
+
+@pytest.mark.parametrize("case", ["one_token", "topk_equals_E", "all_to_one_expert",
+                                  "precomputed"])
+def test_edge_cases(case):
+    dev = GH.device()
+    base = W.MIXTRAL_PREFILL.scaled(name=case, M=40, H=128, I=256, E=8)
+    if case == "one_token":
+        cfg = base.scaled(M=1)
+    elif case == "topk_equals_E":
+        cfg = base.scaled(E=4, top_k=4)
+    else:
+        cfg = base
+    inp = W.make_inputs(cfg, 31)
+    if case in ("all_to_one_expert", "precomputed"):
+        rng = np.random.default_rng(3)
+        if case == "all_to_one_expert":   # expert 5 takes every first slot, 6 the second
+            ids = np.stack([np.full(cfg.M, 5), np.full(cfg.M, 6)], 1).astype(np.int32)
+        else:
+            ids = np.stack([rng.permutation(cfg.E)[:cfg.top_k] for _ in range(cfg.M)]).astype(
+                np.int32)
+        w = rng.random((cfg.M, cfg.top_k)).astype(np.float32)
+        out, ws, info = GH.run_contiguous(inp, dev, precomputed=(ids, w),
+                                          out_dtype=torch.float32)
+        GH.check_routing_and_align(inp, ws, info, ids_o=ids, w_o=w.astype(np.float64))
+        GH.check_output(inp, out, ids, w.astype(np.float64), what=case)
+    else:
+        out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+        ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+        GH.check_output(inp, out, ids_o, w_o, what=case)
+
+
+def test_inplace_and_deterministic():
+    dev = GH.device()
+    cfg = W.DEEPSEEK_GROUPED.scaled(name="inplace", M=64, H=256, I=128, E=64)
+    inp = W.make_inputs(cfg, 41)
+    out1, _, _ = GH.run_contiguous(inp, dev)
+    out2, _, _ = GH.run_contiguous(inp, dev)
+    assert torch.equal(out1, out2), "two runs differ"
+    out3, ws, info = GH.run_contiguous(inp, dev, inplace=True)
+    assert torch.equal(out1, out3), "in-place result differs"
+
+
+def test_precomputed_matches_router_path():
+    dev = GH.device()
+    cfg = W.DEEPSEEK_GROUPED.scaled(name="pre_vs_router", M=64, H=128, I=128, E=64)
+    inp = W.make_inputs(cfg, 43)
+    out1, ws, info = GH.run_contiguous(inp, dev)
+    K, M = cfg.top_k, cfg.M
+    ids = GH.region(ws, info.off_topk_ids, torch.int32, M * K).reshape(M, K)
+    w = GH.region(ws, info.off_topk_weights, torch.float32, M * K).reshape(M, K)
+    out2, _, _ = GH.run_contiguous(inp, dev, precomputed=(ids, w))
+    assert torch.equal(out1, out2)
+
+
+BATCHED_SMALL = W.BATCHED_FP8.scaled(name="batched_fp8_small", M=96, H=256, I=256, E=8,
+                                     top_k=2)
+
+
+@pytest.mark.parametrize("reduce", [False, True])
+def test_batched_fp8_small(reduce):
+    dev = GH.device()
+    inp = W.make_inputs(BATCHED_SMALL, 1005)
+    out, ws, info = GH.run_batched(inp, dev, reduce=reduce, out_dtype=torch.float32)
+    out16, _, _ = GH.run_batched(inp, dev, reduce=reduce)
+    rows, experts = GH.batched_rows(inp)
+    if reduce:
+        GH.check_rounded(out16, out)
+    else:
+        flat32 = out.reshape(-1, BATCHED_SMALL.H)[torch.as_tensor(rows, device=out.device)]
+        flat16 = out16.reshape(-1, BATCHED_SMALL.H)[torch.as_tensor(rows, device=out.device)]
+        GH.check_rounded(flat16, flat32)
+    GH.check_batched_tilelist(inp, ws, info)
+    ex = GH.oracle_experts(inp)
+    import oracle
+    acts = oracle.Acts(inp["hidden"].cpu(), quantize=True)
+    o_ref, _ = oracle.expert_rows(ex, acts, rows, experts)
+    if not reduce:
+        got = out.float().cpu().numpy().reshape(-1, BATCHED_SMALL.H)[rows]
+        GH.compare(BATCHED_SMALL, got, o_ref, "batched rows")
+    else:
+        T = inp["max_tokens"]
+        tmap = inp["token_map"].cpu().numpy().astype(np.int64)
+        pos = {r: i for i, r in enumerate(rows)}
+        wts = inp["token_map_w"].cpu().numpy().astype(np.float64)
+        y = np.zeros((BATCHED_SMALL.M, BATCHED_SMALL.H))
+        for t in range(BATCHED_SMALL.M):
+            for j in range(BATCHED_SMALL.top_k):
+                y[t] += wts[t, j] * o_ref[pos[tmap[t, j]]]
+        GH.compare(BATCHED_SMALL, out.float().cpu().numpy(), y, "batched reduce")
+        del T
+
+
+def test_batched_bf16_matches_contiguous():
+    """bf16 batched rows equal the contiguous path's expert rows."""
+    dev = GH.device()
+    cfg = BATCHED_SMALL.scaled(name="batched_bf16", weight="bf16")
+    inp = W.make_inputs(cfg, 1006)
+    out, ws, info = GH.run_batched(inp, dev, reduce=True, out_dtype=torch.float32)
+    GH.check_batched_tilelist(inp, ws, info)
+    import oracle
+    rows, experts = GH.batched_rows(inp)
+    o_ref, _ = oracle.expert_rows(GH.oracle_experts(inp), oracle.Acts(inp["hidden"].cpu()),
+                                  rows, experts)
+    pos = {r: i for i, r in enumerate(rows)}
+    tmap = inp["token_map"].cpu().numpy()
+    wts = inp["token_map_w"].cpu().numpy().astype(np.float64)
+    y = np.stack([sum(wts[t, j] * o_ref[pos[tmap[t, j]]] for j in range(cfg.top_k))
+                  for t in range(cfg.M)])
+    GH.compare(cfg, out.float().cpu().numpy(), y, "batched bf16 reduce")
