@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="tokens (or batched rows) the CPU oracle leg computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB, 5 times (the "
+                         "reference point for scaling HBM byte counters), then exit")
     return ap.parse_args()
 
 
@@ -91,6 +94,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     dev = torch.device("cuda:0")
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": src.numel(), "launches": 5}), flush=True)
+        return
     cfg = W.BY_NAME[args.workload]
     seed = args.seed if args.seed is not None else 1000 + W.CONFIGS.index(cfg)
     print(f"[bench] {cfg.name}: generating inputs (seed {seed})", file=sys.stderr, flush=True)

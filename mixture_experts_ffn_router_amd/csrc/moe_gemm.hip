@@ -135,6 +135,7 @@ struct Gemm1Args {
     int a_div;
     const int32_t* sorted;
     const int32_t* expert_ids;
+    const int32_t* offsets;     // [E + 1] padded run starts
     const int32_t* npp;
     int sentinel;
     const void* w13;            // [E, H, 2I]
@@ -152,6 +153,7 @@ struct Gemm2Args {
     const float* z_scale;
     const int32_t* sorted;
     const int32_t* expert_ids;
+    const int32_t* offsets;
     const int32_t* npp;
     int sentinel;
     const void* w2;             // [E, I, H]
@@ -164,6 +166,29 @@ struct Gemm2Args {
     int out_dt;
     void* out;
 };
+
+// ---------------------------------------------------------------- tile schedule
+// Persistent, XCD-aware schedule.  Logical tiles are ordered by expert, then
+// column tile, then the expert's row blocks, so the row blocks of one expert
+// that share a weight tile are neighbours, and one expert's activation rows
+// are reused across its column tiles.  Workgroups are dealt round-robin over
+// the 8 XCDs (workgroup b runs on XCD b % 8), so XCD x is given the contiguous
+// chunk [x R/8, (x+1) R/8) of the R real tiles and walks it with its own
+// workgroups: neighbouring tiles run together on one XCD and share its L2.
+template <typename F>
+__device__ __forceinline__ void for_each_tile(const int32_t* npp, const int32_t* expert_ids,
+                                              const int32_t* offsets, int BM, int nt, F&& f)
+{
+    const int R = (*npp / BM) * nt;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = gridDim.x >> 3;
+    const int lo = (int)(((int64_t)R * xcd) >> 3), hi = (int)(((int64_t)R * (xcd + 1)) >> 3);
+    for (int L = lo + slot; L < hi; L += per) {
+        const int e = expert_ids[L / nt];
+        const int b0 = offsets[e] / BM, nb = offsets[e + 1] / BM - b0;
+        const int local = L - b0 * nt;
+        f(b0 + local % nb, local / nb);
+    }
+}
 
 // ---------------------------------------------------------------- GEMM1
 template <int DT, int BM, int BNZ, int WAVES_M>
@@ -189,18 +214,14 @@ struct G1Cfg {
 };
 
 template <int DT, int BM, int BNZ, int WAVES_M>
-__global__ void __launch_bounds__(256) k_gemm1(Gemm1Args g)
+__device__ __forceinline__ void gemm1_tile(const Gemm1Args& g, char* smem, int mblk, int ntile)
 {
     typedef G1Cfg<DT, BM, BNZ, WAVES_M> C;
     constexpr int ES = C::ES, BK = C::BK, KM = C::KM;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
     float* a_rowscale = (float*)(smem + 2 * C::STAGE_BYTES);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wave_m = wave / C::WAVES_N, wave_n = wave % C::WAVES_N;
-    const int mblk = blockIdx.x % g.max_blocks, ntile = blockIdx.x / g.max_blocks;
-    if (mblk * BM >= *g.npp)
-        return;
     const int e = g.expert_ids[mblk];
     const int H = g.H, I = g.I, N = 2 * I;
     const int n0 = ntile * BNZ;
@@ -418,6 +439,16 @@ __global__ void __launch_bounds__(256) k_gemm1(Gemm1Args g)
     }
 }
 
+template <int DT, int BM, int BNZ, int WAVES_M>
+__global__ void __launch_bounds__(256) k_gemm1(Gemm1Args g)
+{
+    __shared__ __attribute__((aligned(16))) char smem[G1Cfg<DT, BM, BNZ, WAVES_M>::LDS_BYTES];
+    for_each_tile(g.npp, g.expert_ids, g.offsets, BM, g.n_tiles, [&](int mblk, int ntile) {
+        gemm1_tile<DT, BM, BNZ, WAVES_M>(g, smem, mblk, ntile);
+        __syncthreads();   // the next tile's prologue reuses the LDS
+    });
+}
+
 // ---------------------------------------------------------------- GEMM2
 template <int DT, int BM, int BN, int WAVES_M>
 struct G2Cfg {
@@ -441,17 +472,13 @@ struct G2Cfg {
 };
 
 template <int DT, int BM, int BN, int WAVES_M>
-__global__ void __launch_bounds__(256) k_gemm2(Gemm2Args g)
+__device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int mblk, int ntile)
 {
     typedef G2Cfg<DT, BM, BN, WAVES_M> C;
     constexpr int ES = C::ES, BK = C::BK, KM = C::KM;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wave_m = wave / C::WAVES_N, wave_n = wave % C::WAVES_N;
-    const int mblk = blockIdx.x % g.max_blocks, ntile = blockIdx.x / g.max_blocks;
-    if (mblk * BM >= *g.npp)
-        return;
     const int e = g.expert_ids[mblk];
     const int H = g.H, I = g.I;
     const int c0 = ntile * BN;
@@ -614,26 +641,59 @@ __global__ void __launch_bounds__(256) k_gemm2(Gemm2Args g)
     }
 }
 
+template <int DT, int BM, int BN, int WAVES_M>
+__global__ void __launch_bounds__(256) k_gemm2(Gemm2Args g)
+{
+    __shared__ __attribute__((aligned(16))) char smem[G2Cfg<DT, BM, BN, WAVES_M>::LDS_BYTES];
+    for_each_tile(g.npp, g.expert_ids, g.offsets, BM, g.n_tiles, [&](int mblk, int ntile) {
+        gemm2_tile<DT, BM, BN, WAVES_M>(g, smem, mblk, ntile);
+        __syncthreads();
+    });
+}
+
 // ---------------------------------------------------------------- launchers
+// Persistent grid: every workgroup the device holds at once (a multiple of
+// the 8 XCDs), capped by the largest possible tile count.  Each kernel
+// instance queries its occupancy once; `cached` is that instance's slot.
+template <typename K>
+static unsigned persistent_grid(K kernel, int64_t max_tiles, int& cached)
+{
+    if (cached == 0) {
+        int dev = 0, cus = 0, occ = 0;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, 0);
+        cached = (cus > 0 ? cus : 256) * (occ > 0 ? occ : 1);
+    }
+    int64_t g = cached;
+    const int64_t cap = (max_tiles + 7) / 8 * 8;
+    if (g > cap)
+        g = cap;
+    g = (g + 7) / 8 * 8;
+    return (unsigned)(g < 8 ? 8 : g);
+}
+
 template <int DT, int BM, int BNZ, int WAVES_M>
 static hipError_t run_gemm1(const Gemm1Args& a, hipStream_t s)
 {
-    const int n_tiles = (a.I + BNZ - 1) / BNZ;
     Gemm1Args g = a;
-    g.n_tiles = n_tiles;
-    const dim3 grid((unsigned)(g.max_blocks * n_tiles)), block(256);
-    hipLaunchKernelGGL((k_gemm1<DT, BM, BNZ, WAVES_M>), grid, block, 0, s, g);
+    g.n_tiles = (a.I + BNZ - 1) / BNZ;
+    auto kern = k_gemm1<DT, BM, BNZ, WAVES_M>;
+    static int cached = 0;
+    const dim3 grid(persistent_grid(kern, (int64_t)g.max_blocks * g.n_tiles, cached)), block(256);
+    hipLaunchKernelGGL(kern, grid, block, 0, s, g);
     return hipGetLastError();
 }
 
 template <int DT, int BM, int BN, int WAVES_M>
 static hipError_t run_gemm2(const Gemm2Args& a, hipStream_t s)
 {
-    const int n_tiles = (a.H + BN - 1) / BN;
     Gemm2Args g = a;
-    g.n_tiles = n_tiles;
-    const dim3 grid((unsigned)(g.max_blocks * n_tiles)), block(256);
-    hipLaunchKernelGGL((k_gemm2<DT, BM, BN, WAVES_M>), grid, block, 0, s, g);
+    g.n_tiles = (a.H + BN - 1) / BN;
+    auto kern = k_gemm2<DT, BM, BN, WAVES_M>;
+    static int cached = 0;
+    const dim3 grid(persistent_grid(kern, (int64_t)g.max_blocks * g.n_tiles, cached)), block(256);
+    hipLaunchKernelGGL(kern, grid, block, 0, s, g);
     return hipGetLastError();
 }
 
@@ -660,6 +720,7 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s)
     }
     g.sorted = P.sorted_ids;
     g.expert_ids = P.expert_ids;
+    g.offsets = P.offsets;
     g.npp = P.npp;
     g.sentinel = (int)P.sentinel;
     g.w13 = A.w13;
@@ -696,6 +757,7 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
     g.z_scale = P.z_scale;
     g.sorted = P.sorted_ids;
     g.expert_ids = P.expert_ids;
+    g.offsets = P.offsets;
     g.npp = P.npp;
     g.sentinel = (int)P.sentinel;
     g.w2 = A.w2;
