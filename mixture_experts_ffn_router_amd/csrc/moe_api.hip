@@ -7,6 +7,7 @@
 // "Fused MoE Modular Kernel" page.  All checks run on the host before
 // anything is enqueued.
 #include <cmath>
+#include <cstdlib>
 
 #include "moe_internal.h"
 
@@ -92,24 +93,33 @@ static int validate(const moe_problem* p)
     return MOE_OK;
 }
 
-// Rows per M-block: the smallest MFMA-friendly block that holds the average
-// expert load, so decode-sized batches do not pad to 128 rows.
-static int choose_block_m(const moe_problem* p, int64_t rows_cap)
+// GEMM tile family from the average rows per expert: decode-sized loads use
+// 16-row tiles with the waves split across columns; prefill-sized loads use
+// 256-row tiles so one tile holds a whole expert.
+static int choose_tile(const moe_problem* p, int64_t rows_cap)
 {
     if (p->w_dtype == MOE_FP8_E4M3FN)
-        return 128;
+        return TILE_FP8;
+    if (p->w_dtype == MOE_F32)
+        return TILE_DECODE;
+    // tuning override: MOE_TILE_CFG = 0 (prefill) | 1 (mid) | 2 (decode), read on every call
+    if (const char* env = std::getenv("MOE_TILE_CFG")) {
+        const int v = std::atoi(env);
+        if (v == TILE_PREFILL || v == TILE_MID || v == TILE_DECODE)
+            return v;
+    }
     const double avg = (double)rows_cap / p->E;
-    if (avg <= 16)
-        return 16;
-    if (avg <= 32)
-        return 32;
-    if (avg <= 64)
-        return 64;
-    return 128;
+    if (avg <= 12)
+        return TILE_DECODE;
+    if (avg <= 48)
+        return TILE_MID;
+    return TILE_PREFILL;
 }
 
-static int layout(const moe_problem* p, moe_workspace_info* info)
+static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_offs = nullptr,
+                  int* cfg_out = nullptr)
 {
+    size_t off_chunk_off = 0, off_chunk_expert = 0;
     const int rc = validate(p);
     if (rc != MOE_OK)
         return rc;
@@ -122,7 +132,7 @@ static int layout(const moe_problem* p, moe_workspace_info* info)
         if (p->M > 0 && MK < rows_cap)
             rows_cap = MK;   // every valid slab row is one routed copy of a token
     }
-    const int BM = choose_block_m(p, rows_cap);
+    const int BM = ALIGN_BM;
     const int64_t max_sorted = rows_cap + (int64_t)p->E * (BM - 1);
     const bool fp8 = p->w_dtype == MOE_FP8_E4M3FN;
     const int zes = fp8 ? 1 : (p->act_dtype == MOE_F32 ? 4 : 2);
@@ -143,6 +153,8 @@ static int layout(const moe_problem* p, moe_workspace_info* info)
     w.off_sorted_ids = take((size_t)max_sorted * 4);
     w.off_expert_ids = take((size_t)w.max_blocks * 4);
     w.off_num_post_padded = take(4);
+    off_chunk_off = take((size_t)(p->E + 1) * 4);
+    off_chunk_expert = take((size_t)w.max_blocks * 4);
     const bool quant = fp8 && p->act_dtype != MOE_FP8_E4M3FN;
     const int64_t qrows = batched ? max_sorted : p->M;
     w.off_aq = take(quant ? (size_t)qrows * p->H : 0);
@@ -153,10 +165,17 @@ static int layout(const moe_problem* p, moe_workspace_info* info)
     w.off_o = take((size_t)orows * p->H * 4);
     w.bytes = off;
     *info = w;
+    if (chunk_offs) {
+        chunk_offs[0] = off_chunk_off;
+        chunk_offs[1] = off_chunk_expert;
+    }
+    if (cfg_out)
+        *cfg_out = choose_tile(p, rows_cap);
     return MOE_OK;
 }
 
-static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* ws)
+static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* ws,
+                      const size_t* chunk_offs, int cfg)
 {
     Plan P{};
     P.fmt = p->format;
@@ -180,6 +199,10 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
     P.has_b2 = p->has_w2_bias ? 1 : 0;
     P.breduce = p->batched_reduce ? 1 : 0;
     P.BM = w.block_m;
+    P.cfg = cfg;
+    P.CH = tile_rows(cfg);
+    P.chunk_off = (int32_t*)(ws + chunk_offs[0]);
+    P.chunk_expert = (int32_t*)(ws + chunk_offs[1]);
     P.max_sorted = w.max_sorted_len;
     P.max_blocks = w.max_blocks;
     P.rows_cap = w.max_sorted_len - (int64_t)p->E * (w.block_m - 1);
@@ -243,7 +266,9 @@ static int forward(const moe_problem* p, const moe_args* a, void* workspace,
                    size_t workspace_bytes, void* stream, void** events)
 {
     moe_workspace_info w;
-    int rc = layout(p, &w);
+    size_t chunk_offs[2];
+    int cfg = 0;
+    int rc = layout(p, &w, chunk_offs, &cfg);
     if (rc != MOE_OK)
         return rc;
     rc = check_args(p, a);
@@ -253,7 +278,7 @@ static int forward(const moe_problem* p, const moe_args* a, void* workspace,
         return MOE_ERR_WORKSPACE;
 
     const hipStream_t s = (hipStream_t)stream;
-    const Plan P = make_plan(p, w, (char*)workspace);
+    const Plan P = make_plan(p, w, (char*)workspace, chunk_offs, cfg);
     const bool batched = p->format == MOE_FMT_BATCHED;
     if (!batched && p->M == 0)
         return MOE_OK;                                   // nothing routed

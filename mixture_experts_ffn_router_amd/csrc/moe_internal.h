@@ -107,6 +107,14 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 }
 
 // ------------------------------------------------------------------ execution plan
+// GEMM tile families; each fixes the rows per tile (chunk height).
+enum { TILE_PREFILL = 0, TILE_MID = 1, TILE_DECODE = 2, TILE_FP8 = 3 };
+constexpr int ALIGN_BM = 16;                 // expert runs are padded to 16 rows
+inline int tile_rows(int cfg)
+{
+    return cfg == TILE_PREFILL ? 160 : cfg == TILE_MID ? 64 : cfg == TILE_FP8 ? 128 : 16;
+}
+
 // Host-computed description of one call: problem, tile choice, device pointers.
 struct Plan {
     int fmt, M, H, I, E, K, T;      // K = top_k, T = max_tokens
@@ -114,7 +122,9 @@ struct Plan {
     int renorm, G, kg, gmode;
     float rsf;
     int has_b13, has_b2, breduce;
-    int BM;                         // rows per M-block (align granularity)
+    int BM;                         // align granularity: each expert run padded to BM rows
+    int CH;                         // rows per GEMM tile (a multiple of BM)
+    int cfg;                        // GEMM tile family (see moe_gemm.hip)
     int64_t rows_cap;               // upper bound of valid routed rows
     int64_t max_sorted;             // rows_cap + E * (BM - 1)
     int max_blocks;                 // max_sorted / BM
@@ -127,6 +137,8 @@ struct Plan {
     int32_t* sorted_ids;
     int32_t* expert_ids;
     int32_t* npp;
+    int32_t* chunk_off;             // [E + 1] GEMM row-chunk prefix per expert
+    int32_t* chunk_expert;          // [max_blocks] expert of each chunk
     uint8_t* aq;
     float* aq_scale;
     void* z;

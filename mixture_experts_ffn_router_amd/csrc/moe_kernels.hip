@@ -236,13 +236,37 @@ __device__ int block_exclusive_scan_1024(int v, int* sh_tot, int* out_prefix)
     return total;
 }
 
+
+// GEMM work unit lists: expert e's padded run is cut into chunks of CH rows
+// (the row height of one GEMM tile).  chunk_off[e] = chunks of experts < e,
+// chunk_off[E] = all chunks, chunk_expert[c] = expert of chunk c.  Called by
+// all 1024 threads; `padded` is this thread's expert run (0 for e >= E).
+__device__ void write_chunks(int padded, int CH, int E, int* sh_tot, int32_t* chunk_off,
+                             int32_t* chunk_expert)
+{
+    const int e = threadIdx.x;
+    __syncthreads();   // sh_tot is reused from the previous scan
+    const int nch = (e < E) ? (padded + CH - 1) / CH : 0;
+    int cstart;
+    const int ctotal = block_exclusive_scan_1024(nch, sh_tot, &cstart);
+    if (e < E) {
+        chunk_off[e] = cstart;
+        for (int j = 0; j < nch; ++j)
+            chunk_expert[cstart + j] = e;
+    }
+    if (e == 0)
+        chunk_off[E] = ctotal;
+}
+
 __global__ void __launch_bounds__(1024) k_align(const int32_t* __restrict__ ids, int Mk, int E,
                                                 int BM, int32_t* __restrict__ counts,
                                                 int32_t* __restrict__ offsets,
                                                 int32_t* __restrict__ sorted,
                                                 int32_t* __restrict__ expert_ids,
                                                 int32_t* __restrict__ npp, int sentinel,
-                                                int64_t max_sorted, int max_blocks)
+                                                int64_t max_sorted, int max_blocks, int CH,
+                                                int32_t* __restrict__ chunk_off,
+                                                int32_t* __restrict__ chunk_expert)
 {
     extern __shared__ int sh[];
     int* cnt = sh;                               // [ALIGN_WAVES][E]
@@ -303,6 +327,7 @@ __global__ void __launch_bounds__(1024) k_align(const int32_t* __restrict__ ids,
         offsets[E] = total;
         *npp = total;
     }
+    write_chunks(padded, CH, E, tot, chunk_off, chunk_expert);
     __syncthreads();
 
     // pass 2: stable scatter
@@ -340,7 +365,7 @@ hipError_t launch_align(const Plan& P, const int32_t* ids, hipStream_t s)
     const size_t lds = sizeof(int) * ((size_t)ALIGN_WAVES * P.E + P.E + ALIGN_WAVES);
     hipLaunchKernelGGL(k_align, dim3(1), dim3(1024), lds, s, ids, P.M * P.K, P.E, P.BM, P.counts,
                        P.offsets, P.sorted_ids, P.expert_ids, P.npp, (int)P.sentinel, P.max_sorted,
-                       P.max_blocks);
+                       P.max_blocks, P.CH, P.chunk_off, P.chunk_expert);
     return hipGetLastError();
 }
 
@@ -356,7 +381,9 @@ __global__ void __launch_bounds__(1024) k_tilelist(const int32_t* __restrict__ e
                                                    int32_t* __restrict__ sorted,
                                                    int32_t* __restrict__ expert_ids,
                                                    int32_t* __restrict__ npp, int sentinel,
-                                                   int64_t max_sorted, int max_blocks)
+                                                   int64_t max_sorted, int max_blocks, int CH,
+                                                   int32_t* __restrict__ chunk_off,
+                                                   int32_t* __restrict__ chunk_expert)
 {
     __shared__ int tot[ALIGN_WAVES];
     __shared__ int sh_start[1024], sh_cnt[1024];
@@ -383,6 +410,7 @@ __global__ void __launch_bounds__(1024) k_tilelist(const int32_t* __restrict__ e
         offsets[E] = fits ? total : 0;
         *npp = fits ? total : 0;
     }
+    write_chunks(fits ? padded : 0, CH, E, tot, chunk_off, chunk_expert);
     if (!fits)
         return;
     __syncthreads();
@@ -399,7 +427,7 @@ hipError_t launch_tilelist(const Plan& P, const int32_t* ent, hipStream_t s)
 {
     hipLaunchKernelGGL(k_tilelist, dim3(1), dim3(1024), 0, s, ent, P.E, P.T, P.BM, P.counts,
                        P.offsets, P.sorted_ids, P.expert_ids, P.npp, (int)P.sentinel,
-                       P.max_sorted, P.max_blocks);
+                       P.max_sorted, P.max_blocks, P.CH, P.chunk_off, P.chunk_expert);
     return hipGetLastError();
 }
 

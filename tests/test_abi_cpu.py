@@ -107,12 +107,16 @@ def test_workspace_layout_is_aligned_and_sized():
         assert info.max_sorted_len >= min(p.M * p.top_k, p.E * max(p.max_tokens, 1)) + \
             p.E * (info.block_m - 1) or p.fmt == B.MOE_FMT_BATCHED
         assert info.max_blocks == info.max_sorted_len // info.block_m
-        assert info.block_m in (16, 32, 64, 128)
+        assert info.block_m == 16
 
 
-def test_block_m_follows_expert_load():
-    assert B.moe_workspace_shapes(_prob(M=32, H=2048, I=768, E=128, top_k=8).c()).block_m == 16
-    assert B.moe_workspace_shapes(_prob(M=512, H=4096, I=14336, E=8, top_k=2).c()).block_m == 128
+def test_expert_runs_are_padded_to_16_rows():
+    for kw in [dict(M=32, H=2048, I=768, E=128, top_k=8), dict(M=512, H=4096, I=14336, E=8),
+               dict(w_dtype=B.MOE_FP8_E4M3FN, I=256)]:
+        info = B.moe_workspace_shapes(_prob(**kw).c())
+        assert info.block_m == 16
+        p = _prob(**kw)
+        assert info.max_sorted_len == p.M * p.top_k + p.E * 15
 
 
 def _args(**kw):
