@@ -642,6 +642,433 @@ __global__ void __launch_bounds__(256) k_gemm2(Gemm2Args g)
     });
 }
 
+// ================================================================ LDS-DMA bf16 tiles
+// The large-tile bf16 path moves A and weight tiles with LDS DMA
+// (global_load_lds_dwordx4): each lane names one 16-byte global chunk and the
+// 64 chunks of a wave land at M0 + 16 * lane, so the loads need no staging
+// registers and a ring of NS stages keeps up to NS - 1 K stages in flight.
+// The loads come from inline asm, outside the compiler's wait-count
+// bookkeeping: the ring waits on them itself with s_waitcnt vmcnt(N).  Vector
+// memory loads complete in issue order, so "at most N outstanding" means
+// every load older than the last N has landed in LDS; the compiler's own
+// waits on its loads only ever see a lower count and so stay correct.
+//
+// Tile: CH = 32 * FMW rows x 128 weight columns, one K stage = 64 rows of K.
+// The four waves form a 2 x 2 grid: wave (rg, cg) owns FMW 16-row strips
+// (rows rg * 16 FMW ..) and four 16-column fragments.  Per K stage the LDS
+// reads are CH*128*2 bytes of A plus 2 * 16 KiB of weights, against
+// 4 * CH * 128 + 16 KiB when the four waves share all rows.
+//
+// LDS layout of a stage (no padding: a DMA fills 1024 contiguous bytes):
+//   A  [CH rows][128 B]: 16-byte slot s of row r holds K chunk s ^ ((r>>1)&7),
+//      so the 16 rows of a fragment read hit 16 distinct bank groups.
+//   B  [64 rows][256 B]: slot s of row k holds column chunk s ^ fB(k), with
+//      fB(k) = 2 * ((k & 3) | ((k >> 1) & 4)); a transposing read touches 16
+//      rows x 32 bytes and fB sends the 8 rows of each half-wave to 8
+//      distinct 32-byte bank groups.
+// Out-of-range chunks (K tail, columns past N) are DMA'd from a zero page;
+// rows past the tile's real rows repeat its first row (their results are
+// never stored).
+__device__ __attribute__((aligned(16))) int32_t g_zero16[4] = {0, 0, 0, 0};
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p)
+{
+    return (uint32_t)(uintptr_t)LDS_PTR(const char, p);
+}
+
+// M0 is a reserved register: the compiler never allocates it, and in these
+// kernels no other instruction reads it, so it needs no clobber.
+__device__ __forceinline__ void dma16(const char* g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(g)
+                 : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    // vmcnt[3:0], expcnt[6:4] (7: no wait), lgkmcnt[11:8] (15: no wait), vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int FMW_, int FN_, int NS_>
+struct DS {
+    static constexpr int FMW = FMW_, FN = FN_, NS = NS_;
+    static constexpr int CH = 32 * FMW;                  // rows per tile
+    static constexpr int BN = 32 * FN;                   // weight columns per tile
+    static constexpr int RB = BN * 2;                    // bytes per weight row in LDS
+    static constexpr int SLOTS = RB / 16;                // 16-byte slots per weight row
+    static constexpr int A_BYTES = CH * 128, B_BYTES = 64 * RB;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int A_PW = A_BYTES / 1024 / 4, B_PW = B_BYTES / 1024 / 4;   // DMAs per wave
+    static constexpr int D = A_PW + B_PW;
+    static constexpr int RING = NS * STAGE;
+    static_assert(NS >= 2 && NS <= 4, "ring depth");
+    static_assert(FN == 4 || FN == 8, "128 or 256 weight columns");
+    static_assert((NS - 2) * D < 64, "vmcnt range");
+};
+
+// Per-lane DMA sources of one tile.  Wave w issues the A DMAs i = w + 4j
+// (tile rows 8i .. 8i+7) and the B DMAs i = w + 4j (1024 / RB K rows each).
+template <typename S>
+struct DmaSrc {
+    const char* a[S::A_PW];     // source row + chunk byte offset (K stage 0)
+    int a_k[S::A_PW];           // K element of the chunk within a stage
+    const char* b[S::B_PW];     // weight row (K stage 0) + column byte, or null
+    int b_k[S::B_PW];           // K row within a stage
+    int64_t b_step;             // bytes per K stage of the weights
+
+    __device__ __forceinline__ void issue(int kt, int K, uint32_t lds, int wave) const
+    {
+        const char* zero = (const char*)g_zero16;
+#pragma unroll
+        for (int j = 0; j < S::A_PW; ++j) {
+            const char* p = (kt * 64 + a_k[j] < K) ? a[j] + kt * 128 : zero;
+            dma16(p, lds + (wave + 4 * j) * 1024);
+        }
+#pragma unroll
+        for (int j = 0; j < S::B_PW; ++j) {
+            const char* p = (b[j] && kt * 64 + b_k[j] < K) ? b[j] + kt * b_step : zero;
+            dma16(p, lds + S::A_BYTES + (wave + 4 * j) * 1024);
+        }
+    }
+};
+
+__device__ __forceinline__ int swz_b(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
+
+// Tile row and K chunk of this lane's j-th A DMA.
+template <typename S>
+__device__ __forceinline__ void dma_a_slot(int j, int wave, int lane, int& row, int& chunk)
+{
+    const int i = wave + 4 * j;
+    row = 8 * i + (lane >> 3);
+    chunk = (lane & 7) ^ ((row >> 1) & 7);
+}
+
+// Weight K row and 8-column chunk of this lane's j-th B DMA.
+template <typename S>
+__device__ __forceinline__ void dma_b_slot(int j, int wave, int lane, int& k, int& chunk)
+{
+    const int i = wave + 4 * j;
+    k = i * (1024 / S::RB) + lane / S::SLOTS;
+    chunk = (lane % S::SLOTS) ^ swz_b(k);
+}
+
+// The DMA ring over all K stages; compute(stage pointer) consumes one stage.
+template <typename S, typename F>
+__device__ __forceinline__ void dma_mainloop(const DmaSrc<S>& src, char* ring, int K, int wave,
+                                             F&& compute)
+{
+    const int nk = (K + 63) / 64;
+    const uint32_t ring_lds = lds_u32(ring);
+#pragma unroll
+    for (int st = 0; st < S::NS - 1; ++st)
+        if (st < nk)
+            src.issue(st, K, ring_lds + st * S::STAGE, wave);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int after = min(nk - 1 - kt, S::NS - 2);   // stages issued after stage kt
+        if constexpr (S::NS >= 4) {
+            if (after >= 2)
+                wait_vmcnt<2 * S::D>();
+            else if (after == 1)
+                wait_vmcnt<S::D>();
+            else
+                wait_vmcnt<0>();
+        } else if constexpr (S::NS == 3) {
+            if (after >= 1)
+                wait_vmcnt<S::D>();
+            else
+                wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+        // the slot refilled here was last read in iteration kt - 1, which every
+        // wave finished before the barrier
+        const int nx = kt + S::NS - 1;
+        if (nx < nk)
+            src.issue(nx, K, ring_lds + (nx % S::NS) * S::STAGE, wave);
+        compute(ring + (kt % S::NS) * S::STAGE);
+    }
+}
+
+// Fragment reads and MFMAs of one stage for wave (rg, cg).  bchunk[fn] is the
+// first 8-column chunk of fragment fn within the tile's weight columns.
+template <typename S>
+struct DmaFrag {
+    int a_off[2];               // A fragment byte offset within a strip, per MFMA step
+    int b_off[S::FN];           // B fragment byte offset (MFMA step 0, low half)
+
+    __device__ __forceinline__ void init(int lane, const int (&bchunk)[S::FN])
+    {
+        const int s = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            a_off[ks] = s * 128 + (((ks * 4 + g) ^ (s >> 1)) * 16);
+        // this lane's K rows are 32 ks + 8 g + s/4 (+4): the swizzle depends on g and s only
+        const int x = ((s & 3) >> 1) ^ swz_b(8 * g + (s >> 2));
+#pragma unroll
+        for (int fn = 0; fn < S::FN; ++fn)
+            b_off[fn] = (8 * g + (s >> 2)) * S::RB + ((bchunk[fn] ^ x) * 16) + 8 * (s & 1);
+    }
+
+    __device__ __forceinline__ void stage(const char* st, int rg, f32x4 (&acc)[S::FMW][S::FN]) const
+    {
+        const char* As = st + rg * S::FMW * 2048;
+        const char* Bs = st + S::A_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 a[S::FMW], b[S::FN];
+#pragma unroll
+            for (int fn = 0; fn < S::FN; ++fn) {
+                const char* p = Bs + b_off[fn] + ks * 32 * S::RB;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4, p + 4 * S::RB));
+                const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                b[fn] = __builtin_bit_cast(bf16x8, v);
+            }
+#pragma unroll
+            for (int fm = 0; fm < S::FMW; ++fm)
+                a[fm] = __builtin_bit_cast(bf16x8, *(const i32x4*)(As + fm * 2048 + a_off[ks]));
+#pragma unroll
+            for (int fm = 0; fm < S::FMW; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < S::FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(SCHED_DS_READ, S::FMW + 2 * S::FN, 0);
+            __builtin_amdgcn_sched_group_barrier(SCHED_MFMA, S::FMW * S::FN, 0);
+        }
+    }
+};
+
+// Source row of tile row `row` for GEMM1's A (activations): the routed token's
+// row, the padded position itself (a_ident), or - for padding - the tile's
+// first row.
+__device__ __forceinline__ int64_t gemm1_src_row(const Gemm1Args& g, int r0, int row, int rows)
+{
+    const int64_t p = (int64_t)r0 + (row < rows ? row : 0);
+    if (g.a_ident)
+        return p;
+    int sid = g.s.sorted[p];
+    if (sid >= g.s.sentinel)
+        sid = g.s.sorted[r0];
+    return sid / g.a_div;
+}
+
+// GEMM1 tile: BN/2 gate columns n0.. and the matching BN/2 up columns I + n0..
+template <int FMW, int FN, int NS>
+__device__ __forceinline__ void gemm1_tile_dma(const Gemm1Args& g, char* ring, int e, int r0,
+                                               int rows, int ntile)
+{
+    typedef DS<FMW, FN, NS> S;
+    constexpr int BNZ = S::BN / 2, HC = BNZ / 8;      // z columns per tile, chunks per half
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = wave >> 1, cg = wave & 1;
+    const int H = g.H, I = g.I, N = 2 * I;
+    const int n0 = ntile * BNZ;
+    const int strips = (rows + 15) >> 4;
+
+    DmaSrc<S> src;
+    const char* abase = (const char*)g.a;
+#pragma unroll
+    for (int j = 0; j < S::A_PW; ++j) {
+        int row, c;
+        dma_a_slot<S>(j, wave, lane, row, c);
+        src.a[j] = abase + gemm1_src_row(g, r0, row, rows) * H * 2 + c * 16;
+        src.a_k[j] = c * 8;
+    }
+    const char* wbase = (const char*)g.w13 + (int64_t)e * H * N * 2;
+#pragma unroll
+    for (int j = 0; j < S::B_PW; ++j) {
+        int k, c;
+        dma_b_slot<S>(j, wave, lane, k, c);
+        const int zc = n0 + 8 * (c % HC);                // chunks [0, HC) gate, [HC, 2HC) up
+        const int col = (c < HC) ? zc : I + zc;
+        src.b[j] = (zc < I) ? wbase + (int64_t)k * N * 2 + (int64_t)col * 2 : nullptr;
+        src.b_k[j] = k;
+    }
+    src.b_step = (int64_t)64 * N * 2;
+
+    // wave (rg, cg): gate fragments fn < FN/2 at columns cg*BNZ/2 + 16 fn, up
+    // fragments fn >= FN/2 at the same z columns of the up half
+    constexpr int FH = FN / 2;
+    int bchunk[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        bchunk[fn] = (fn < FH) ? (cg * FH + fn) * 2 : HC + (cg * FH + fn - FH) * 2;
+    DmaFrag<S> fr;
+    fr.init(lane, bchunk);
+
+    f32x4 acc[FMW][FN];
+#pragma unroll
+    for (int fm = 0; fm < FMW; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    dma_mainloop<S>(src, ring, H, wave, [&](const char* st) { fr.stage(st, rg, acc); });
+    __syncthreads();   // the ring becomes the output staging area
+
+    constexpr int O_STRIDE = BNZ + 4;
+    static_assert(32 * FMW * O_STRIDE * 4 <= S::RING, "z staging fits in the ring");
+    float* Zs = (float*)ring;
+    const int g4 = lane >> 4, s16 = lane & 15;
+#pragma unroll
+    for (int fn = 0; fn < FH; ++fn) {
+        const int zc = (cg * FH + fn) * 16 + s16;
+        const int n = n0 + zc;
+        float bg = 0.0f, bu = 0.0f;
+        if (g.b13 && n < I) {
+            bg = load_bias(g.b13, g.bias_dt, (int64_t)e * N + n);
+            bu = load_bias(g.b13, g.bias_dt, (int64_t)e * N + I + n);
+        }
+#pragma unroll
+        for (int fm = 0; fm < FMW; ++fm) {
+            const int strip = rg * FMW + fm;
+            if (strip >= strips)
+                continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = strip * 16 + g4 * 4 + r;
+                Zs[row * O_STRIDE + zc] = silu_mul(acc[fm][fn][r] + bg, acc[fm][fn + FH][r] + bu);
+            }
+        }
+    }
+    __syncthreads();
+
+    constexpr int CPR = BNZ / 8;    // 16-byte bf16 chunks per z row
+    const int nrows = strips * 16;
+    for (int q = tid; q < nrows * CPR; q += 256) {
+        const int row = q / CPR, c0 = (q % CPR) * 8;
+        if (n0 + c0 >= I)
+            continue;
+        const int64_t p = (int64_t)r0 + row;
+        const float* sp = Zs + row * O_STRIDE + c0;
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            w[k] = f32_to_bf16(sp[2 * k]) | ((uint32_t)f32_to_bf16(sp[2 * k + 1]) << 16);
+        *(i32x4*)((u16*)g.z + p * I + n0 + c0) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    }
+}
+
+// GEMM2 tile: BN output columns c0.. of the routed rows.
+template <int FMW, int FN, int NS>
+__device__ __forceinline__ void gemm2_tile_dma(const Gemm2Args& g, char* ring, int e, int r0,
+                                               int rows, int ntile)
+{
+    typedef DS<FMW, FN, NS> S;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rg = wave >> 1, cg = wave & 1;
+    const int H = g.H, I = g.I;
+    const int c0 = ntile * S::BN;
+    const int strips = (rows + 15) >> 4;
+
+    // z rows are the padded positions; rows past the tile's strips repeat row r0
+    DmaSrc<S> src;
+    const char* zbase = (const char*)g.z;
+#pragma unroll
+    for (int j = 0; j < S::A_PW; ++j) {
+        int row, c;
+        dma_a_slot<S>(j, wave, lane, row, c);
+        const int64_t p = (int64_t)r0 + (row < strips * 16 ? row : 0);
+        src.a[j] = zbase + p * I * 2 + c * 16;
+        src.a_k[j] = c * 8;
+    }
+    const char* wbase = (const char*)g.w2 + (int64_t)e * I * H * 2;
+#pragma unroll
+    for (int j = 0; j < S::B_PW; ++j) {
+        int k, c;
+        dma_b_slot<S>(j, wave, lane, k, c);
+        const int col = c0 + 8 * c;
+        src.b[j] = (col < H) ? wbase + (int64_t)k * H * 2 + (int64_t)col * 2 : nullptr;
+        src.b_k[j] = k;
+    }
+    src.b_step = (int64_t)64 * H * 2;
+
+    int bchunk[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+        bchunk[fn] = (cg * FN + fn) * 2;
+    DmaFrag<S> fr;
+    fr.init(lane, bchunk);
+
+    f32x4 acc[FMW][FN];
+#pragma unroll
+    for (int fm = 0; fm < FMW; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    dma_mainloop<S>(src, ring, I, wave, [&](const char* st) { fr.stage(st, rg, acc); });
+
+    // epilogue straight from the accumulators: 16 lanes store 16 consecutive columns of a row
+    const int g4 = lane >> 4, s16 = lane & 15;
+    float bias[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+        const int c = c0 + (cg * FN + fn) * 16 + s16;
+        bias[fn] = (g.b2 && c < H) ? load_bias(g.b2, g.bias_dt, (int64_t)e * H + c) : 0.0f;
+    }
+#pragma unroll
+    for (int fm = 0; fm < FMW; ++fm) {
+        const int strip = rg * FMW + fm;
+        if (strip >= strips)
+            continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = strip * 16 + g4 * 4 + r;
+            if (row >= rows)
+                continue;
+            const int64_t p = (int64_t)r0 + row;
+            const int sid = g.s.sorted[p];
+            if (sid >= g.s.sentinel)
+                continue;
+            const int64_t dst = (g.out_mode == 2) ? p : (int64_t)sid;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int c = c0 + (cg * FN + fn) * 16 + s16;
+                if (c >= H)
+                    continue;
+                const float v = acc[fm][fn][r] + bias[fn];
+                if (g.out_mode == 1 && g.out_dt == MOE_BF16)
+                    ((u16*)g.out)[dst * H + c] = f32_to_bf16(v);
+                else
+                    ((float*)g.out)[dst * H + c] = v;
+            }
+        }
+    }
+}
+
+template <int FMW, int FN, int NS>
+__global__ void __launch_bounds__(256, (DS<FMW, FN, NS>::RING <= 80 * 1024 ? 2 : 1))
+    k_gemm1_dma(Gemm1Args g)
+{
+    typedef DS<FMW, FN, NS> S;
+    __shared__ __attribute__((aligned(16))) char ring[S::RING];
+    for_each_tile<S::CH>(g.s, [&](int e, int r0, int rows, int ntile) {
+        gemm1_tile_dma<FMW, FN, NS>(g, ring, e, r0, rows, ntile);
+        __syncthreads();   // the next tile's DMAs overwrite the staging area
+    });
+}
+
+template <int FMW, int FN, int NS>
+__global__ void __launch_bounds__(256, (DS<FMW, FN, NS>::RING <= 80 * 1024 ? 2 : 1))
+    k_gemm2_dma(Gemm2Args g)
+{
+    typedef DS<FMW, FN, NS> S;
+    __shared__ __attribute__((aligned(16))) char ring[S::RING];
+    for_each_tile<S::CH>(g.s, [&](int e, int r0, int rows, int ntile) {
+        gemm2_tile_dma<FMW, FN, NS>(g, ring, e, r0, rows, ntile);
+        __syncthreads();   // every wave is done with the ring before the next tile's DMAs
+    });
+}
+
 // ---------------------------------------------------------------- launchers
 // Persistent grid: every workgroup the device holds at once (a multiple of
 // the 8 XCDs), capped by the largest possible tile count.  Each kernel
@@ -690,6 +1117,57 @@ static hipError_t run_gemm2(const Gemm2Args& a, const Plan& P, hipStream_t s)
         block(256);
     hipLaunchKernelGGL(kern, grid, block, 0, s, g);
     return hipGetLastError();
+}
+
+template <int FMW, int FN, int NS>
+static hipError_t run_gemm1_dma(const Gemm1Args& a, const Plan& P, hipStream_t s)
+{
+    constexpr int BNZ = DS<FMW, FN, NS>::BN / 2;
+    Gemm1Args g = a;
+    g.s.n_tiles = (a.I + BNZ - 1) / BNZ;
+    auto kern = k_gemm1_dma<FMW, FN, NS>;
+    static int cached = 0;
+    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached)),
+        block(256);
+    hipLaunchKernelGGL(kern, grid, block, 0, s, g);
+    return hipGetLastError();
+}
+
+template <int FMW, int FN, int NS>
+static hipError_t run_gemm2_dma(const Gemm2Args& a, const Plan& P, hipStream_t s)
+{
+    constexpr int BN = DS<FMW, FN, NS>::BN;
+    Gemm2Args g = a;
+    g.s.n_tiles = (a.H + BN - 1) / BN;
+    auto kern = k_gemm2_dma<FMW, FN, NS>;
+    static int cached = 0;
+    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached)),
+        block(256);
+    hipLaunchKernelGGL(kern, grid, block, 0, s, g);
+    return hipGetLastError();
+}
+
+// Expected number of GEMM row chunks: every active expert has at least one,
+// and the routed rows fill at least rows / CH of them.
+static int64_t expected_chunks(const Plan& P)
+{
+    const int64_t rows = (P.fmt == MOE_FMT_BATCHED) ? (int64_t)P.E * P.T : (int64_t)P.M * P.K;
+    const int64_t active = rows < P.E ? rows : P.E;
+    const int64_t fill = (rows + P.CH - 1) / P.CH;
+    return active > fill ? active : fill;
+}
+
+static int device_cus()
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (cus <= 0)
+            cus = 256;
+    }
+    return cus;
 }
 
 static Sched make_sched(const Plan& P)
@@ -745,7 +1223,8 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s)
     if (P.wdt == MOE_F32)
         return run_gemm1<MOE_F32, 1, 16>(g, P, s);
     switch (P.cfg) {
-    case TILE_PREFILL: return run_gemm1<MOE_BF16, 10, 16>(g, P, s);
+    case TILE_PREFILL:
+        return run_gemm1_dma<5, 4, 2>(g, P, s);
     case TILE_MID: return run_gemm1<MOE_BF16, 4, 16>(g, P, s);
     default: return run_gemm1<MOE_BF16, 1, 16>(g, P, s);
     }
@@ -781,7 +1260,13 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
     if (P.wdt == MOE_F32)
         return run_gemm2<MOE_F32, 1, 16>(g, P, s);
     switch (P.cfg) {
-    case TILE_PREFILL: return run_gemm2<MOE_BF16, 10, 32>(g, P, s);
+    case TILE_PREFILL:
+        // about one tile per CU: one workgroup per CU with a 4-stage ring keeps
+        // three K stages in flight; otherwise two workgroups per CU overlap
+        // each other's prologues and epilogues
+        if (expected_chunks(P) * ((P.H + 127) / 128) <= device_cus() * 5 / 4)
+            return run_gemm2_dma<5, 4, 4>(g, P, s);
+        return run_gemm2_dma<5, 4, 2>(g, P, s);
     case TILE_MID: return run_gemm2<MOE_BF16, 4, 32>(g, P, s);
     default: return run_gemm2<MOE_BF16, 1, 32>(g, P, s);
     }

@@ -163,3 +163,28 @@ def test_batched_bf16_matches_contiguous():
     y = np.stack([sum(wts[t, j] * o_ref[pos[tmap[t, j]]] for j in range(cfg.top_k))
                   for t in range(cfg.M)])
     GH.compare(cfg, out.float().cpu().numpy(), y, "batched bf16 reduce")
+
+
+@pytest.mark.parametrize("tile_cfg", ["0", "1", "2"])
+@pytest.mark.parametrize("skew", [False, True])
+def test_tile_families_ragged(tile_cfg, skew, monkeypatch):
+    """Every bf16 tile family on K and column tails (H % 64 = 16, I % 64 = 48)
+    and, with skew, on experts of 200 rows: several row chunks per expert and
+    a partial last strip."""
+    dev = GH.device()
+    monkeypatch.setenv("MOE_TILE_CFG", tile_cfg)
+    cfg = W.MIXTRAL_PREFILL.scaled(name=f"ragged_t{tile_cfg}", M=200, H=208, I=176, E=4)
+    inp = W.make_inputs(cfg, 51)
+    print(f"[case] ragged tile_cfg={tile_cfg} skew={skew}", flush=True)
+    if skew:
+        ids = np.stack([np.full(cfg.M, 1), np.full(cfg.M, 2)], 1).astype(np.int32)
+        w = np.random.default_rng(4).random((cfg.M, cfg.top_k)).astype(np.float32)
+        out, ws, info = GH.run_contiguous(inp, dev, precomputed=(ids, w), out_dtype=torch.float32)
+        GH.check_routing_and_align(inp, ws, info, ids_o=ids, w_o=w.astype(np.float64))
+        GH.check_output(inp, out, ids, w.astype(np.float64), what="ragged skew")
+    else:
+        out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+        ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+        GH.check_output(inp, out, ids_o, w_o, what="ragged")
+    out16, _, _ = GH.run_contiguous(inp, dev, precomputed=(ids, w) if skew else None)
+    GH.check_rounded(out16, out)
