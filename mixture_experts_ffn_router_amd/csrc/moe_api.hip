@@ -94,8 +94,8 @@ static int validate(const moe_problem* p)
 }
 
 // GEMM tile family from the average rows per expert: decode-sized loads use
-// 16-row tiles with the waves split across columns; prefill-sized loads use
-// 256-row tiles so one tile holds a whole expert.
+// 16-row tiles, mid-sized loads 64-row tiles, prefill-sized loads 160-row
+// tiles so that one tile holds a whole expert of about 128 rows.
 static int choose_tile(const moe_problem* p, int64_t rows_cap)
 {
     if (p->w_dtype == MOE_FP8_E4M3FN)
