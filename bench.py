@@ -220,9 +220,11 @@ def main():
         tf = g1_flops / (g1_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_PEAK_TFLOPS[dt_key],
                 "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS[dt_key], 4)}
-    roof.update({"kernel": "k_gemm1 (grouped W13 GEMM + SiLU*up)",
+    traffic, kname, tsrc = profile_traffic(cfg.name)
+    roof.update({"kernel": kname or "GEMM1 (grouped W13 GEMM + SiLU*up)",
                  "algorithmic_bytes_per_launch": int(g1_bytes),
-                 "avg_launch_ms": round(g1_ms, 4), "traffic": None})
+                 "avg_launch_ms": round(g1_ms, 4), "traffic": traffic,
+                 "traffic_source": tsrc})
 
     tokens = cfg.M
     value = tokens / (ms_per_step * 1e-3)
@@ -253,6 +255,27 @@ def main():
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, info, args.cpu_sample)
     print(json.dumps(res), flush=True)
+
+
+def profile_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size),
+    or (None, None, None) when no summary was taken on the current GEMM source."""
+    import glob
+    import hashlib
+    import re
+    src = os.path.join(ROOT, "mixture_experts_ffn_router_amd", "csrc", "moe_gemm.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}.md"))):
+        with open(path) as f:
+            text = f.read()
+        h = re.search(r"^source_sha256: ([0-9a-f]{64})", text, re.M)
+        t = re.search(r"^traffic_bytes_per_launch: (\d+)", text, re.M)
+        k = re.search(r"^dominant_kernel: (.+)$", text, re.M)
+        if h and t and k and h.group(1) == sha:
+            return int(t.group(1)), k.group(1).strip(), os.path.relpath(path, ROOT)
+    return None, None, None
 
 
 def cpu_baseline(cfg, inp, info, sample):
