@@ -69,6 +69,7 @@ class HipEvents:
         rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
                                           ctypes.c_void_p(b))
         if rc != 0:
+            self.hip.hipGetLastError()      # do not leave the error pending for later calls
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return ms.value
 
@@ -140,41 +141,72 @@ def main():
                             w13_bias=inp["w13_bias"], w2_bias=inp["w2_bias"],
                             w13_scale=inp.get("w13_scale"), w2_scale=inp.get("w2_scale"))
     ws, info = B.allocate_workspace(prob, dev)
-    cprob = prob.c()
     stream = B.current_stream_handle(dev)
     hip = HipEvents()
-    nst = len(B.STAGES)
-
-    # ---- warmup
-    for _ in range(args.warmup):
-        B.moe_forward(cprob, cargs, ws.data_ptr(), ws.numel(), stream)
-    torch.cuda.synchronize()
-
-    # ---- timed steps: whole-step events plus per-stage events on the same stream
-    step_ev = [(hip.create(), hip.create()) for _ in range(args.steps)]
-    stage_ev = [[hip.create() for _ in range(2 * nst)] for _ in range(args.steps)]
     rec = hip.hip.hipEventRecord
     rec.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    nst = len(B.STAGES)
+
+    # ---- weights: bf16 expert weights are re-laid out once, as at model load
+    # (moe_pack_weights); the plain layout is timed too, for reference
+    plain_prob, plain_args = prob.c(), cargs
+    pack_ms = None
+    if cfg.weight == "bf16":
+        ev0, ev1 = hip.create(), hip.create()
+        rec(ctypes.c_void_p(ev0), ctypes.c_void_p(stream))
+        pw = B.pack_weights(inp["w13"], inp["w2"])
+        rec(ctypes.c_void_p(ev1), ctypes.c_void_p(stream))
+        torch.cuda.synchronize()
+        pack_ms = hip.elapsed_ms(ev0, ev1)
+        prob.w_layout = B.MOE_W_PACKED
+        cargs = B.moe_args.from_buffer_copy(cargs)
+        cargs.w13, cargs.w2 = pw.w13.data_ptr(), pw.w2.data_ptr()
+    cprob = prob.c()
+
+    def run_steps(p, a, n):
+        for _ in range(n):
+            B.moe_forward(p, a, ws.data_ptr(), ws.numel(), stream)
+
+    # ---- warmup
+    run_steps(cprob, cargs, args.warmup)
+    torch.cuda.synchronize()
+
+    # ---- timed steps: K back-to-back forwards between two synchronisations
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    run_steps(cprob, cargs, args.steps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # ---- the same steps again with HIP events on the launch stream around
+    # every step and every kernel stage (per-kernel durations, roofline)
+    step_ev = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    stage_ev = [[hip.create() for _ in range(2 * nst)] for _ in range(args.steps)]
     for k in range(args.steps):
         rec(ctypes.c_void_p(step_ev[k][0]), ctypes.c_void_p(stream))
         B.moe_forward_timed(cprob, cargs, ws.data_ptr(), ws.numel(), stream, stage_ev[k])
         rec(ctypes.c_void_p(step_ev[k][1]), ctypes.c_void_p(stream))
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     step_ms = [hip.elapsed_ms(a, b) for a, b in step_ev]
     stage_ms = {}
-    ran = []
     for s, name in enumerate(B.STAGES):
         try:
             vals = [hip.elapsed_ms(ev[2 * s], ev[2 * s + 1]) for ev in stage_ev]
         except RuntimeError:
             continue            # stage not run for this problem
         stage_ms[name] = float(np.mean(vals))
-        ran.append(name)
+
+    # ---- plain weight layout, for reference (same steps, same clock)
+    plain_ms = None
+    if pack_ms is not None:
+        run_steps(plain_prob, plain_args, 2)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_steps(plain_prob, plain_args, args.steps)
+        torch.cuda.synchronize()
+        plain_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     hip.close()
-    ms_per_step = wall * 1e3 / args.steps
 
     # ---- accounting
     if batched:
@@ -248,6 +280,9 @@ def main():
                           "t_step_us_median_events": round(t_step * 1e6, 1),
                           "frac": round(max(t_hbm, t_mfma) / t_step, 4)},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "weight_layout": "packed" if pack_ms is not None else "plain",
+        "pack_ms_once": None if pack_ms is None else round(pack_ms, 3),
+        "plain_layout_ms_per_step": None if plain_ms is None else round(plain_ms, 4),
         "roofline": roof,
     }
 

@@ -65,6 +65,12 @@ typedef enum {
     MOE_FMT_BATCHED = 1       /* hidden [E, max_tokens, H] + expert_num_tokens[E]  */
 } moe_format;
 
+/* Memory layout of w13 / w2 (see moe_pack_weights). */
+typedef enum {
+    MOE_W_PLAIN = 0,          /* w13 [E, H, 2I], w2 [E, I, H], row-major          */
+    MOE_W_PACKED = 1          /* bf16 only: the blocked layout of moe_pack_weights */
+} moe_weight_layout;
+
 /* Problem description (host struct).
  *
  *   format       MOE_FMT_CONTIGUOUS or MOE_FMT_BATCHED.
@@ -102,6 +108,8 @@ typedef enum {
  *                token_map / token_map_w (the pages' naive batched
  *                weight-and-reduce); 0 writes the expert rows to out
  *                [E, max_tokens, H] instead.
+ *   w_layout     MOE_W_PLAIN, or MOE_W_PACKED when w13 / w2 hold the output of
+ *                moe_pack_weights (bf16 weights only; else MOE_ERR_UNSUPPORTED).
  */
 typedef struct {
     int32_t format;
@@ -112,6 +120,7 @@ typedef struct {
     float routed_scaling_factor;
     int32_t has_w13_bias, has_w2_bias;
     int32_t batched_reduce;
+    int32_t w_layout;
 } moe_problem;
 
 /* Workspace layout chosen by the library for one problem.  All offsets are
@@ -213,6 +222,34 @@ typedef enum {
  * moe_forward. */
 int moe_forward_timed(const moe_problem* p, const moe_args* a, void* workspace,
                       size_t workspace_bytes, void* stream, void** events);
+
+/* Packed weights.  The expert weights are constant across calls, so a caller
+ * can re-lay them out once, at load time, into the order in which the grouped
+ * GEMMs stream them (the walkthrough's "fused_moe_kernel" section reads each
+ * weight tile as a K x BLOCK_SIZE_N block; packing makes every such block of
+ * one K stage contiguous in memory).  The packed layout is a sequence of
+ * 16 KiB blocks, each 64 weight rows (K) x 128 weight columns (N) of bf16:
+ *   row k of a block is 256 bytes = 16 slots of 16 bytes; slot s holds the
+ *   8-column chunk c = s ^ (2 * ((k & 3) | ((k >> 1) & 4))) of that row.
+ *   w13: block (e, j, kt), j < ceil(I / 64), kt < ceil(H / 64), in that order;
+ *        chunks 0-7 are gate columns 64 j + 8 c .., chunks 8-15 the up
+ *        columns I + 64 j + 8 (c - 8) .., of weight rows 64 kt + k.
+ *   w2:  block (e, j, kt), j < ceil(H / 128), kt < ceil(I / 64); chunk c holds
+ *        columns 128 j + 8 c .. of weight rows 64 kt + k.
+ *   Rows past H (w13) / I (w2) and columns past I (w13) / H (w2) are zero.
+ *
+ * moe_packed_weight_bytes: sizes of the two packed buffers for *p (host
+ * only).  Returns MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED (the
+ * weights are not bf16).
+ * moe_pack_weights: enqueues the re-layout of w13 / w2 (plain layout, device
+ * pointers) into w13_packed / w2_packed (device buffers of the sizes above,
+ * caller-owned, must not overlap the inputs) on `stream`.  The forward then
+ * takes w13_packed / w2_packed as w13 / w2 with p->w_layout = MOE_W_PACKED.
+ * Errors as moe_packed_weight_bytes, MOE_ERR_INVALID_ARG for null pointers,
+ * MOE_ERR_LAUNCH if a launch failed. */
+int moe_packed_weight_bytes(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes);
+int moe_pack_weights(const moe_problem* p, const void* w13, const void* w2, void* w13_packed,
+                     void* w2_packed, void* stream);
 
 /* Static English description of a status code. */
 const char* moe_status_string(int status);

@@ -20,9 +20,10 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAU
 MOE_F32, MOE_BF16, MOE_FP8_E4M3FN = 0, 1, 2
 MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID, MOE_ROUTE_PRECOMPUTED = 0, 1, 2
 MOE_FMT_CONTIGUOUS, MOE_FMT_BATCHED = 0, 1
+MOE_W_PLAIN, MOE_W_PACKED = 0, 1
 
-EXPORTED = ("moe_workspace_shapes", "moe_forward", "moe_forward_timed", "moe_status_string",
-            "moe_version")
+EXPORTED = ("moe_workspace_shapes", "moe_forward", "moe_forward_timed", "moe_packed_weight_bytes",
+            "moe_pack_weights", "moe_status_string", "moe_version")
 STAGES = ("router", "align", "quant", "gemm1", "gemm2", "reduce")
 
 
@@ -35,7 +36,8 @@ class moe_problem(ctypes.Structure):
                 ("renormalize", ctypes.c_int32), ("group_count", ctypes.c_int32),
                 ("k_group", ctypes.c_int32), ("group_select_mode", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float), ("has_w13_bias", ctypes.c_int32),
-                ("has_w2_bias", ctypes.c_int32), ("batched_reduce", ctypes.c_int32)]
+                ("has_w2_bias", ctypes.c_int32), ("batched_reduce", ctypes.c_int32),
+                ("w_layout", ctypes.c_int32)]
 
 
 class moe_workspace_info(ctypes.Structure):
@@ -85,6 +87,12 @@ def load() -> ctypes.CDLL:
                                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                           ctypes.POINTER(ctypes.c_void_p)]
         lib.moe_forward_timed.restype = ctypes.c_int
+        lib.moe_packed_weight_bytes.argtypes = [ctypes.POINTER(moe_problem),
+                                                ctypes.POINTER(ctypes.c_size_t),
+                                                ctypes.POINTER(ctypes.c_size_t)]
+        lib.moe_packed_weight_bytes.restype = ctypes.c_int
+        lib.moe_pack_weights.argtypes = [ctypes.POINTER(moe_problem)] + [ctypes.c_void_p] * 5
+        lib.moe_pack_weights.restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         lib.moe_version.argtypes = []
@@ -115,6 +123,23 @@ def moe_forward(problem: moe_problem, args: moe_args, workspace: int, workspace_
                             workspace_bytes, ctypes.c_void_p(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_forward")
+
+
+def moe_packed_weight_bytes(problem: moe_problem):
+    b13, b2 = ctypes.c_size_t(), ctypes.c_size_t()
+    rc = load().moe_packed_weight_bytes(ctypes.byref(problem), ctypes.byref(b13), ctypes.byref(b2))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_packed_weight_bytes")
+    return int(b13.value), int(b2.value)
+
+
+def moe_pack_weights(problem: moe_problem, w13: int, w2: int, w13_packed: int, w2_packed: int,
+                     stream: int) -> None:
+    rc = load().moe_pack_weights(ctypes.byref(problem), ctypes.c_void_p(w13), ctypes.c_void_p(w2),
+                                 ctypes.c_void_p(w13_packed), ctypes.c_void_p(w2_packed),
+                                 ctypes.c_void_p(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_pack_weights")
 
 
 def moe_forward_timed(problem: moe_problem, args: moe_args, workspace: int,
@@ -180,6 +205,7 @@ class Problem:
     has_w13_bias: bool = False
     has_w2_bias: bool = False
     batched_reduce: bool = False
+    w_layout: int = MOE_W_PLAIN
 
     def c(self) -> moe_problem:
         return moe_problem(self.fmt, self.M, self.H, self.I, self.E, self.top_k, self.max_tokens,
@@ -187,7 +213,44 @@ class Problem:
                            self.routing, int(self.renormalize), self.group_count, self.k_group,
                            self.group_select_mode, float(self.routed_scaling_factor),
                            int(self.has_w13_bias), int(self.has_w2_bias),
-                           int(self.batched_reduce))
+                           int(self.batched_reduce), int(self.w_layout))
+
+
+@dataclass
+class PackedWeights:
+    """bf16 expert weights re-laid out once by moe_pack_weights (uint8 device
+    buffers) with the plain shapes they came from."""
+    w13: object
+    w2: object
+    E: int
+    H: int
+    I: int
+
+
+def pack_weights(w13, w2) -> PackedWeights:
+    """Packs plain bf16 w13 [E, H, 2I] / w2 [E, I, H] on their device (one
+    launch pair on the current stream)."""
+    import torch
+    E, H, N = w13.shape
+    I = N // 2
+    if tuple(w2.shape) != (E, I, H):
+        raise ValueError(f"w2 shape {tuple(w2.shape)} does not match w13 {tuple(w13.shape)}")
+    prob = Problem(M=0, H=H, I=I, E=E, top_k=1, act_dtype=MOE_BF16, w_dtype=_dtype_code(w13),
+                   out_dtype=MOE_BF16).c()
+    b13, b2 = moe_packed_weight_bytes(prob)
+    p13 = torch.empty(b13, dtype=torch.uint8, device=w13.device)
+    p2 = torch.empty(b2, dtype=torch.uint8, device=w13.device)
+    moe_pack_weights(prob, _ptr(w13), _ptr(w2), p13.data_ptr(), p2.data_ptr(),
+                     current_stream_handle(w13.device))
+    return PackedWeights(p13, p2, E, H, I)
+
+
+def _weights(w13, w2):
+    """(w13 tensor, w2 tensor, E, H, I, w_dtype code, layout) of plain or packed weights."""
+    if isinstance(w13, PackedWeights):
+        return w13.w13, w13.w2, w13.E, w13.H, w13.I, MOE_BF16, MOE_W_PACKED
+    E, H, N = w13.shape
+    return w13, w2, E, H, N // 2, _dtype_code(w13), MOE_W_PLAIN
 
 
 def make_args(hidden, w13, w2, out, router_logits=None, topk_ids=None, topk_weights=None,
@@ -220,12 +283,12 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
               w2_bias=None, topk_ids=None, topk_weights=None, w13_scale=None, w2_scale=None,
               out_dtype=None, out=None, workspace=None):
     """Contiguous-format forward on torch device tensors (the MindIE-SD
-    page's fused_moe argument list, single device).  Returns (out, workspace
-    tensor, workspace info)."""
+    page's fused_moe argument list, single device).  w13 may be a
+    PackedWeights (then w2 is ignored).  Returns (out, workspace tensor,
+    workspace info)."""
     import torch
-    M, H = hidden.shape
-    E, _, N = w13.shape
-    I = N // 2
+    M = hidden.shape[0]
+    w13, w2, E, H, I, wdt, layout = _weights(w13, w2)
     if topk_ids is not None:
         route = MOE_ROUTE_PRECOMPUTED
         top_k = topk_ids.shape[1]
@@ -233,13 +296,14 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
         route = {"softmax": MOE_ROUTE_SOFTMAX, "sigmoid": MOE_ROUTE_SIGMOID}[routing]
     act = _dtype_code(hidden)
     odt = out_dtype or (torch.float32 if act == MOE_F32 else torch.bfloat16)
-    prob = Problem(M=M, H=H, I=I, E=E, top_k=top_k, act_dtype=act, w_dtype=_dtype_code(w13),
+    prob = Problem(M=M, H=H, I=I, E=E, top_k=top_k, act_dtype=act, w_dtype=wdt,
                    out_dtype=_dtype_code(torch.empty(0, dtype=odt)),
                    logits_dtype=_dtype_code(router_logits) if router_logits is not None else 0,
                    routing=route, renormalize=renormalize, group_count=group_count,
                    k_group=k_group, group_select_mode=group_select_mode,
                    routed_scaling_factor=routed_scaling_factor,
-                   has_w13_bias=w13_bias is not None, has_w2_bias=w2_bias is not None)
+                   has_w13_bias=w13_bias is not None, has_w2_bias=w2_bias is not None,
+                   w_layout=layout)
     if out is None:
         out = torch.empty(M, H, dtype=odt, device=hidden.device)
     if workspace is None:
@@ -265,17 +329,16 @@ def fused_moe_batched(hidden, expert_num_tokens, w13, w2, *, M: int = 0, top_k: 
     otherwise out is [E, max_tokens, H]."""
     import torch
     E, T, H = hidden.shape
-    N = w13.shape[2]
-    I = N // 2
+    w13, w2, _, _, I, wdt, layout = _weights(w13, w2)
     reduce = token_map is not None
     if reduce:
         M, top_k = token_map.shape
     odt = out_dtype or torch.bfloat16
     prob = Problem(M=M, H=H, I=I, E=E, top_k=top_k, fmt=MOE_FMT_BATCHED,
-                   max_tokens=T, act_dtype=_dtype_code(hidden), w_dtype=_dtype_code(w13),
+                   max_tokens=T, act_dtype=_dtype_code(hidden), w_dtype=wdt,
                    out_dtype=_dtype_code(torch.empty(0, dtype=odt)),
                    routing=MOE_ROUTE_PRECOMPUTED, has_w13_bias=w13_bias is not None,
-                   has_w2_bias=w2_bias is not None, batched_reduce=reduce)
+                   has_w2_bias=w2_bias is not None, batched_reduce=reduce, w_layout=layout)
     if out is None:
         shape = (M, H) if reduce else (E, T, H)
         out = torch.empty(shape, dtype=odt, device=hidden.device)

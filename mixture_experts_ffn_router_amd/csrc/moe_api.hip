@@ -54,6 +54,10 @@ static int validate(const moe_problem* p)
     }
     if (w == MOE_FP8_E4M3FN && p->I % 128)
         return MOE_ERR_UNSUPPORTED;
+    if (p->w_layout != MOE_W_PLAIN && p->w_layout != MOE_W_PACKED)
+        return MOE_ERR_INVALID_ARG;
+    if (p->w_layout == MOE_W_PACKED && w != MOE_BF16)
+        return MOE_ERR_UNSUPPORTED;
 
     if (p->format == MOE_FMT_BATCHED) {
         if (p->max_tokens < 1)
@@ -198,6 +202,7 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
     P.has_b13 = p->has_w13_bias ? 1 : 0;
     P.has_b2 = p->has_w2_bias ? 1 : 0;
     P.breduce = p->batched_reduce ? 1 : 0;
+    P.wpacked = p->w_layout == MOE_W_PACKED ? 1 : 0;
     P.BM = w.block_m;
     P.cfg = cfg;
     P.CH = tile_rows(cfg);
@@ -285,6 +290,10 @@ static int forward(const moe_problem* p, const moe_args* a, void* workspace,
     if (batched && p->batched_reduce && p->M == 0)
         return MOE_OK;
 
+    // hipGetLastError reports the calling thread's last runtime error, which
+    // may come from an unrelated earlier call of the caller; clear it so the
+    // checks below see only this call's launches
+    (void)hipGetLastError();
     hipError_t err;
     int stage = 0;
     auto mark = [&](int st, int end) {
@@ -337,6 +346,43 @@ extern "C" int moe_forward_timed(const moe_problem* p, const moe_args* a, void* 
                                  size_t workspace_bytes, void* stream, void** events)
 {
     return forward(p, a, workspace, workspace_bytes, stream, events);
+}
+
+// Packed weight sizes: 16 KiB blocks of 64 weight rows x 128 weight columns
+// (w13: 64 gate + 64 up columns per block).
+static int packed_sizes(const moe_problem* p, size_t* b13, size_t* b2)
+{
+    const int rc = validate(p);
+    if (rc != MOE_OK)
+        return rc;
+    if (p->w_dtype != MOE_BF16)
+        return MOE_ERR_UNSUPPORTED;
+    const size_t blk = 64 * 256;
+    *b13 = (size_t)p->E * ((p->I + 63) / 64) * ((p->H + 63) / 64) * blk;
+    *b2 = (size_t)p->E * ((p->H + 127) / 128) * ((p->I + 63) / 64) * blk;
+    return MOE_OK;
+}
+
+extern "C" int moe_packed_weight_bytes(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes)
+{
+    if (!w13_bytes || !w2_bytes)
+        return MOE_ERR_INVALID_ARG;
+    return packed_sizes(p, w13_bytes, w2_bytes);
+}
+
+extern "C" int moe_pack_weights(const moe_problem* p, const void* w13, const void* w2,
+                                void* w13_packed, void* w2_packed, void* stream)
+{
+    size_t b13 = 0, b2 = 0;
+    const int rc = packed_sizes(p, &b13, &b2);
+    if (rc != MOE_OK)
+        return rc;
+    if (!w13 || !w2 || !w13_packed || !w2_packed)
+        return MOE_ERR_INVALID_ARG;
+    (void)hipGetLastError();   // a stale error of an earlier, unrelated call
+    const hipError_t err =
+        launch_pack_weights(p->E, p->H, p->I, w13, w2, w13_packed, w2_packed, (hipStream_t)stream);
+    return err == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
 extern "C" const char* moe_status_string(int status)

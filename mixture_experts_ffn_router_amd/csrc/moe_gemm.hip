@@ -88,6 +88,15 @@ __device__ __forceinline__ typename GT<DT>::Frag load_b_frag(const char* Bs, int
     }
 }
 
+// Weight-row swizzle of the packed weight layout and of the LDS weight tiles
+// of the DMA path: slot s of weight row k (within a 64-row K stage, 16 slots
+// of 16 bytes per 256-byte row) holds 8-column chunk s ^ swz_b(k).  A
+// transposing fragment read touches 16 rows x 32 bytes; swz_b sends the 8
+// rows each half-wave reads to 8 distinct 32-byte bank groups.
+__device__ __forceinline__ int swz_b(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
+
+constexpr int PACK_BLOCK = 64 * 256;     // bytes of one packed weight block
+
 // sched_group_barrier instruction classes
 constexpr int SCHED_MFMA = 0x008, SCHED_DS_READ = 0x100;
 
@@ -126,7 +135,8 @@ struct Gemm1Args {
     const float* a_scale;       // fp8: per activation row
     int a_ident;                // 1: A row = padded position p; 0: sorted[p] / a_div
     int a_div;
-    const void* w13;            // [E, H, 2I]
+    const void* w13;            // [E, H, 2I], or packed blocks [E][ceil(I/64)][ceil(H/64)]
+    int w_packed;               // 1: w13 is in the packed block layout (bf16)
     const float* w13_scale;     // fp8: [E, 2I]
     const void* b13;            // [E, 2I] or null
     int bias_dt;
@@ -139,7 +149,8 @@ struct Gemm2Args {
     Sched s;
     const void* z;
     const float* z_scale;
-    const void* w2;             // [E, I, H]
+    const void* w2;             // [E, I, H], or packed blocks [E][ceil(H/128)][ceil(I/64)]
+    int w_packed;               // 1: w2 is in the packed block layout (bf16)
     const float* w2_scale;      // fp8: [E, H]
     const void* b2;             // [E, H] or null
     int bias_dt;
@@ -312,10 +323,22 @@ __device__ __forceinline__ void gemm1_tile(const Gemm1Args& g, char* smem, int e
         const int gcol = (col < BNZ) ? n0 + zc : I + n0 + zc;
         st.b_kk[i] = kk;
         st.b_lds[i] = kk * S::B_STRIDE + cc * 16;
-        st.b_off[i] = (n0 + zc < I) ? (int64_t)gcol * ES : -1;
+        if (g.w_packed)   // one packed block per tile: chunk cc sits in slot cc ^ swz_b(kk)
+            st.b_off[i] = (n0 + zc < I) ? (int64_t)((cc ^ swz_b(kk)) * 16) : -1;
+        else
+            st.b_off[i] = (n0 + zc < I) ? (int64_t)gcol * ES : -1;
     }
     const char* abase = (const char*)g.a;
     const char* wbase = (const char*)g.w13 + (int64_t)e * H * N * ES;
+    int64_t w_ld = (int64_t)N * ES;
+    if constexpr (DT == MOE_BF16) {
+        static_assert(DT != MOE_BF16 || BNZ == 64, "packed w13 blocks pair 64 gate and 64 up columns");
+        if (g.w_packed) {   // rows of the (e, ntile) block run: 256 bytes each, 64 per K stage
+            const int64_t nblk = (I + 63) / 64, nks = (H + 63) / 64;
+            wbase = (const char*)g.w13 + ((int64_t)e * nblk + ntile) * nks * PACK_BLOCK;
+            w_ld = 256;
+        }
+    }
 
     f32x4 acc[2][FM][FN];
 #pragma unroll
@@ -325,13 +348,13 @@ __device__ __forceinline__ void gemm1_tile(const Gemm1Args& g, char* smem, int e
             acc[0][fm][fn] = acc[1][fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int nk = (H + S::BK - 1) / S::BK;
-    st.load(0, abase, (int64_t)H * ES, wbase, (int64_t)N * ES, H);
+    st.load(0, abase, (int64_t)H * ES, wbase, w_ld, H);
     st.store(smem);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const bool more = kt + 1 < nk;
         if (more)
-            st.load(kt + 1, abase, (int64_t)H * ES, wbase, (int64_t)N * ES, H);
+            st.load(kt + 1, abase, (int64_t)H * ES, wbase, w_ld, H);
         const char* As = smem + (kt & 1) * S::STAGE_BYTES;
         const char* Bs = As + S::A_BYTES;
 #pragma unroll
@@ -498,12 +521,24 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int e
         const int col = c0 + cc * 16 / ES;
         st.b_kk[i] = kk;
         st.b_lds[i] = kk * S::B_STRIDE + cc * 16;
-        st.b_off[i] = (col < H) ? (int64_t)col * ES : -1;
+        if (g.w_packed)   // one packed block per tile: chunk cc sits in slot cc ^ swz_b(kk)
+            st.b_off[i] = (col < H) ? (int64_t)((cc ^ swz_b(kk)) * 16) : -1;
+        else
+            st.b_off[i] = (col < H) ? (int64_t)col * ES : -1;
     }
     const char* zbase = (const char*)g.z;
     const char* wbase = (const char*)g.w2 + (int64_t)e * I * H * ES;
+    int64_t w_ld = (int64_t)H * ES;
+    if constexpr (DT == MOE_BF16) {
+        static_assert(DT != MOE_BF16 || BN == 128, "packed w2 blocks are 128 columns");
+        if (g.w_packed) {
+            const int64_t nblk = (H + 127) / 128, nks = (I + 63) / 64;
+            wbase = (const char*)g.w2 + ((int64_t)e * nblk + ntile) * nks * PACK_BLOCK;
+            w_ld = 256;
+        }
+    }
     auto load = [&](int kt) {
-        st.load(kt, zbase, (int64_t)I * ES, wbase, (int64_t)H * ES, I);
+        st.load(kt, zbase, (int64_t)I * ES, wbase, w_ld, I);
         if constexpr (FP8)
             st.rs = (tid < strips * 16) ? g.z_scale[((int64_t)r0 + tid) * ngrp + kt] : 0.0f;
     };
@@ -699,9 +734,9 @@ struct DS {
     static constexpr int FMW = FMW_, FN = FN_, NS = NS_;
     static constexpr int CH = 32 * FMW;                  // rows per tile
     static constexpr int BN = 32 * FN;                   // weight columns per tile
-    static constexpr int RB = BN * 2;                    // bytes per weight row in LDS
-    static constexpr int SLOTS = RB / 16;                // 16-byte slots per weight row
-    static constexpr int A_BYTES = CH * 128, B_BYTES = 64 * RB;
+    static constexpr int NB = FN / 4;                    // 128-column weight blocks per tile
+    static constexpr int RB = 256;                       // bytes per weight row of a block
+    static constexpr int A_BYTES = CH * 128, B_BYTES = NB * PACK_BLOCK;
     static constexpr int STAGE = A_BYTES + B_BYTES;
     static constexpr int A_PW = A_BYTES / 1024 / 4, B_PW = B_BYTES / 1024 / 4;   // DMAs per wave
     static constexpr int D = A_PW + B_PW;
@@ -712,7 +747,8 @@ struct DS {
 };
 
 // Per-lane DMA sources of one tile.  Wave w issues the A DMAs i = w + 4j
-// (tile rows 8i .. 8i+7) and the B DMAs i = w + 4j (1024 / RB K rows each).
+// (tile rows 8i .. 8i+7) and the B DMAs i = w + 4j (block i / 16, K rows
+// 4 (i % 16) .. +3).
 template <typename S>
 struct DmaSrc {
     const char* a[S::A_PW];     // source row + chunk byte offset (K stage 0)
@@ -721,23 +757,23 @@ struct DmaSrc {
     int b_k[S::B_PW];           // K row within a stage
     int64_t b_step;             // bytes per K stage of the weights
 
-    __device__ __forceinline__ void issue(int kt, int K, uint32_t lds, int wave) const
+    // stage kt into the LDS stage at `lds`; live = false sends every lane
+    // to the zero page (a filler stage past the last one)
+    __device__ __forceinline__ void issue(int kt, int K, uint32_t lds, int wave, bool live) const
     {
         const char* zero = (const char*)g_zero16;
 #pragma unroll
         for (int j = 0; j < S::A_PW; ++j) {
-            const char* p = (kt * 64 + a_k[j] < K) ? a[j] + kt * 128 : zero;
+            const char* p = (live && kt * 64 + a_k[j] < K) ? a[j] + kt * 128 : zero;
             dma16(p, lds + (wave + 4 * j) * 1024);
         }
 #pragma unroll
         for (int j = 0; j < S::B_PW; ++j) {
-            const char* p = (b[j] && kt * 64 + b_k[j] < K) ? b[j] + kt * b_step : zero;
+            const char* p = (live && b[j] && kt * 64 + b_k[j] < K) ? b[j] + kt * b_step : zero;
             dma16(p, lds + S::A_BYTES + (wave + 4 * j) * 1024);
         }
     }
 };
-
-__device__ __forceinline__ int swz_b(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
 
 // Tile row and K chunk of this lane's j-th A DMA.
 template <typename S>
@@ -748,16 +784,24 @@ __device__ __forceinline__ void dma_a_slot(int j, int wave, int lane, int& row, 
     chunk = (lane & 7) ^ ((row >> 1) & 7);
 }
 
-// Weight K row and 8-column chunk of this lane's j-th B DMA.
+// Weight block, K row, LDS slot and 8-column chunk of this lane's j-th B DMA.
 template <typename S>
-__device__ __forceinline__ void dma_b_slot(int j, int wave, int lane, int& k, int& chunk)
+__device__ __forceinline__ void dma_b_slot(int j, int wave, int lane, int& blk, int& k, int& slot,
+                                           int& chunk)
 {
     const int i = wave + 4 * j;
-    k = i * (1024 / S::RB) + lane / S::SLOTS;
-    chunk = (lane % S::SLOTS) ^ swz_b(k);
+    blk = i >> 4;
+    k = 4 * (i & 15) + (lane >> 4);
+    slot = lane & 15;
+    chunk = slot ^ swz_b(k);
 }
 
 // The DMA ring over all K stages; compute(stage pointer) consumes one stage.
+// Every iteration issues exactly one stage (a zero-page filler once the real
+// stages run out), so when stage kt is awaited exactly NS - 2 stages of D
+// DMAs per wave were issued after it, one constant wait serves every
+// iteration and the loop body stays one basic block (branches in it make the
+// register allocator copy the accumulators between VGPRs and AGPRs).
 template <typename S, typename F>
 __device__ __forceinline__ void dma_mainloop(const DmaSrc<S>& src, char* ring, int K, int wave,
                                              F&& compute)
@@ -766,43 +810,31 @@ __device__ __forceinline__ void dma_mainloop(const DmaSrc<S>& src, char* ring, i
     const uint32_t ring_lds = lds_u32(ring);
 #pragma unroll
     for (int st = 0; st < S::NS - 1; ++st)
-        if (st < nk)
-            src.issue(st, K, ring_lds + st * S::STAGE, wave);
+        src.issue(st, K, ring_lds + st * S::STAGE, wave, st < nk);
+    int slot = 0;                                   // kt % NS
     for (int kt = 0; kt < nk; ++kt) {
-        const int after = min(nk - 1 - kt, S::NS - 2);   // stages issued after stage kt
-        if constexpr (S::NS >= 4) {
-            if (after >= 2)
-                wait_vmcnt<2 * S::D>();
-            else if (after == 1)
-                wait_vmcnt<S::D>();
-            else
-                wait_vmcnt<0>();
-        } else if constexpr (S::NS == 3) {
-            if (after >= 1)
-                wait_vmcnt<S::D>();
-            else
-                wait_vmcnt<0>();
-        } else {
-            wait_vmcnt<0>();
-        }
+        wait_vmcnt<(S::NS - 2) * S::D>();
         __syncthreads();
         // the slot refilled here was last read in iteration kt - 1, which every
         // wave finished before the barrier
         const int nx = kt + S::NS - 1;
-        if (nx < nk)
-            src.issue(nx, K, ring_lds + (nx % S::NS) * S::STAGE, wave);
-        compute(ring + (kt % S::NS) * S::STAGE);
+        const int nslot = (slot == 0) ? S::NS - 1 : slot - 1;   // nx % NS
+        src.issue(nx, K, ring_lds + nslot * S::STAGE, wave, nx < nk);
+        compute(ring + slot * S::STAGE);
+        slot = (slot == S::NS - 1) ? 0 : slot + 1;
     }
+    wait_vmcnt<0>();                                // the fillers land before the ring is reused
+    __syncthreads();
 }
 
-// Fragment reads and MFMAs of one stage for wave (rg, cg).  bchunk[fn] is the
-// first 8-column chunk of fragment fn within the tile's weight columns.
+// Fragment reads and MFMAs of one stage for wave (rg, cg).  Fragment fn's
+// columns start at 8-column chunk bchunk[fn] of weight block bblk[fn].
 template <typename S>
 struct DmaFrag {
     int a_off[2];               // A fragment byte offset within a strip, per MFMA step
     int b_off[S::FN];           // B fragment byte offset (MFMA step 0, low half)
 
-    __device__ __forceinline__ void init(int lane, const int (&bchunk)[S::FN])
+    __device__ __forceinline__ void init(int lane, const int (&bblk)[S::FN], const int (&bchunk)[S::FN])
     {
         const int s = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -812,7 +844,8 @@ struct DmaFrag {
         const int x = ((s & 3) >> 1) ^ swz_b(8 * g + (s >> 2));
 #pragma unroll
         for (int fn = 0; fn < S::FN; ++fn)
-            b_off[fn] = (8 * g + (s >> 2)) * S::RB + ((bchunk[fn] ^ x) * 16) + 8 * (s & 1);
+            b_off[fn] = bblk[fn] * PACK_BLOCK + (8 * g + (s >> 2)) * S::RB + ((bchunk[fn] ^ x) * 16) +
+                        8 * (s & 1);
     }
 
     __device__ __forceinline__ void stage(const char* st, int rg, f32x4 (&acc)[S::FMW][S::FN]) const
@@ -864,7 +897,7 @@ __device__ __forceinline__ void gemm1_tile_dma(const Gemm1Args& g, char* ring, i
                                                int rows, int ntile)
 {
     typedef DS<FMW, FN, NS> S;
-    constexpr int BNZ = S::BN / 2, HC = BNZ / 8;      // z columns per tile, chunks per half
+    constexpr int BNZ = S::BN / 2;                    // z columns per tile
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rg = wave >> 1, cg = wave & 1;
@@ -881,27 +914,41 @@ __device__ __forceinline__ void gemm1_tile_dma(const Gemm1Args& g, char* ring, i
         src.a[j] = abase + gemm1_src_row(g, r0, row, rows) * H * 2 + c * 16;
         src.a_k[j] = c * 8;
     }
-    const char* wbase = (const char*)g.w13 + (int64_t)e * H * N * 2;
+    // weight block bb of the tile: z columns n0 + 64 bb .. +63 (chunks 0-7
+    // gate, 8-15 up); packed, it is block (e, n0 / 64 + bb) of the layout
+    const int64_t nblk = (I + 63) / 64, nks = (H + 63) / 64;
 #pragma unroll
     for (int j = 0; j < S::B_PW; ++j) {
-        int k, c;
-        dma_b_slot<S>(j, wave, lane, k, c);
-        const int zc = n0 + 8 * (c % HC);                // chunks [0, HC) gate, [HC, 2HC) up
-        const int col = (c < HC) ? zc : I + zc;
-        src.b[j] = (zc < I) ? wbase + (int64_t)k * N * 2 + (int64_t)col * 2 : nullptr;
+        int bb, k, sl, c;
+        dma_b_slot<S>(j, wave, lane, bb, k, sl, c);
+        const int zc = n0 + 64 * bb + 8 * (c & 7);
+        if (g.w_packed) {
+            const int64_t jb = n0 / 64 + bb;
+            src.b[j] = (jb < nblk) ? (const char*)g.w13 + ((e * nblk + jb) * nks) * PACK_BLOCK +
+                                         k * S::RB + sl * 16
+                                   : nullptr;
+        } else {
+            const int col = (c < 8) ? zc : I + zc;
+            src.b[j] = (zc < I) ? (const char*)g.w13 + (int64_t)e * H * N * 2 + (int64_t)k * N * 2 +
+                                      (int64_t)col * 2
+                                : nullptr;
+        }
         src.b_k[j] = k;
     }
-    src.b_step = (int64_t)64 * N * 2;
+    src.b_step = g.w_packed ? PACK_BLOCK : (int64_t)64 * N * 2;
 
-    // wave (rg, cg): gate fragments fn < FN/2 at columns cg*BNZ/2 + 16 fn, up
-    // fragments fn >= FN/2 at the same z columns of the up half
+    // wave (rg, cg): gate fragments fn < FN/2 at z columns (cg FN/2 + fn) 16,
+    // up fragments fn >= FN/2 at the same z columns of the up half
     constexpr int FH = FN / 2;
-    int bchunk[FN];
+    int bblk[FN], bchunk[FN];
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-        bchunk[fn] = (fn < FH) ? (cg * FH + fn) * 2 : HC + (cg * FH + fn - FH) * 2;
+    for (int fn = 0; fn < FN; ++fn) {
+        const int zc = (cg * FH + (fn < FH ? fn : fn - FH)) * 16;
+        bblk[fn] = zc / 64;
+        bchunk[fn] = (fn < FH ? 0 : 8) + (zc % 64) / 8;
+    }
     DmaFrag<S> fr;
-    fr.init(lane, bchunk);
+    fr.init(lane, bblk, bchunk);
 
     f32x4 acc[FMW][FN];
 #pragma unroll
@@ -910,8 +957,8 @@ __device__ __forceinline__ void gemm1_tile_dma(const Gemm1Args& g, char* ring, i
         for (int fn = 0; fn < FN; ++fn)
             acc[fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // (the mainloop ends with a barrier: the ring becomes the output staging area)
     dma_mainloop<S>(src, ring, H, wave, [&](const char* st) { fr.stage(st, rg, acc); });
-    __syncthreads();   // the ring becomes the output staging area
 
     constexpr int O_STRIDE = BNZ + 4;
     static_assert(32 * FMW * O_STRIDE * 4 <= S::RING, "z staging fits in the ring");
@@ -980,23 +1027,37 @@ __device__ __forceinline__ void gemm2_tile_dma(const Gemm2Args& g, char* ring, i
         src.a[j] = zbase + p * I * 2 + c * 16;
         src.a_k[j] = c * 8;
     }
-    const char* wbase = (const char*)g.w2 + (int64_t)e * I * H * 2;
+    // weight block bb of the tile: output columns c0 + 128 bb .. +127;
+    // packed, it is block (e, c0 / 128 + bb) of the layout
+    const int64_t nblk = (H + 127) / 128, nks = (I + 63) / 64;
 #pragma unroll
     for (int j = 0; j < S::B_PW; ++j) {
-        int k, c;
-        dma_b_slot<S>(j, wave, lane, k, c);
-        const int col = c0 + 8 * c;
-        src.b[j] = (col < H) ? wbase + (int64_t)k * H * 2 + (int64_t)col * 2 : nullptr;
+        int bb, k, sl, c;
+        dma_b_slot<S>(j, wave, lane, bb, k, sl, c);
+        if (g.w_packed) {
+            const int64_t jb = c0 / 128 + bb;
+            src.b[j] = (jb < nblk) ? (const char*)g.w2 + ((e * nblk + jb) * nks) * PACK_BLOCK +
+                                         k * S::RB + sl * 16
+                                   : nullptr;
+        } else {
+            const int col = c0 + 128 * bb + 8 * c;
+            src.b[j] = (col < H) ? (const char*)g.w2 + (int64_t)e * I * H * 2 + (int64_t)k * H * 2 +
+                                       (int64_t)col * 2
+                                 : nullptr;
+        }
         src.b_k[j] = k;
     }
-    src.b_step = (int64_t)64 * H * 2;
+    src.b_step = g.w_packed ? PACK_BLOCK : (int64_t)64 * H * 2;
 
-    int bchunk[FN];
+    int bblk[FN], bchunk[FN];
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-        bchunk[fn] = (cg * FN + fn) * 2;
+    for (int fn = 0; fn < FN; ++fn) {
+        const int cl = (cg * FN + fn) * 16;
+        bblk[fn] = cl / 128;
+        bchunk[fn] = (cl % 128) / 8;
+    }
     DmaFrag<S> fr;
-    fr.init(lane, bchunk);
+    fr.init(lane, bblk, bchunk);
 
     f32x4 acc[FMW][FN];
 #pragma unroll
@@ -1067,6 +1128,72 @@ __global__ void __launch_bounds__(256, (DS<FMW, FN, NS>::RING <= 80 * 1024 ? 2 :
         gemm2_tile_dma<FMW, FN, NS>(g, ring, e, r0, rows, ntile);
         __syncthreads();   // every wave is done with the ring before the next tile's DMAs
     });
+}
+
+// ================================================================ weight packing
+// One-time re-layout of bf16 expert weights into 16 KiB blocks of 64 weight
+// rows x 128 weight columns, each row's 16-byte chunks swizzled by swz_b, so
+// that one K stage of a GEMM tile is one contiguous block and a DMA of it is
+// a linear copy (the layout is spelled out next to moe_pack_weights in
+// moe.h).  One thread per 16-byte slot of the output; out-of-range rows and
+// columns are written as zeros.
+__global__ void __launch_bounds__(256) k_pack_w13(const u16* __restrict__ w, int H, int I,
+                                                  i32x4* __restrict__ out, int64_t slots)
+{
+    const int64_t nblk = (I + 63) / 64, nks = (H + 63) / 64;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < slots;
+         q += (int64_t)gridDim.x * 256) {
+        const int sl = (int)(q & 15), k = (int)((q >> 4) & 63);
+        const int64_t b = q >> 10;                      // block (e, j, kt)
+        const int kt = (int)(b % nks);
+        const int j = (int)((b / nks) % nblk);
+        const int64_t e = b / nks / nblk;
+        const int c = sl ^ swz_b(k);
+        const int row = kt * 64 + k, zc = 64 * j + 8 * (c & 7);
+        i32x4 v = {0, 0, 0, 0};
+        if (row < H && zc < I)
+            v = *(const i32x4*)(w + (e * H + row) * 2 * I + (c < 8 ? zc : I + zc));
+        out[q] = v;
+    }
+}
+
+__global__ void __launch_bounds__(256) k_pack_w2(const u16* __restrict__ w, int H, int I,
+                                                 i32x4* __restrict__ out, int64_t slots)
+{
+    const int64_t nblk = (H + 127) / 128, nks = (I + 63) / 64;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < slots;
+         q += (int64_t)gridDim.x * 256) {
+        const int sl = (int)(q & 15), k = (int)((q >> 4) & 63);
+        const int64_t b = q >> 10;
+        const int kt = (int)(b % nks);
+        const int j = (int)((b / nks) % nblk);
+        const int64_t e = b / nks / nblk;
+        const int c = sl ^ swz_b(k);
+        const int row = kt * 64 + k, col = 128 * j + 8 * c;
+        i32x4 v = {0, 0, 0, 0};
+        if (row < I && col < H)
+            v = *(const i32x4*)(w + (e * I + row) * H + col);
+        out[q] = v;
+    }
+}
+
+hipError_t launch_pack_weights(int E, int H, int I, const void* w13, const void* w2, void* p13,
+                               void* p2, hipStream_t s)
+{
+    const int64_t s13 = (int64_t)E * ((I + 63) / 64) * ((H + 63) / 64) * (PACK_BLOCK / 16);
+    const int64_t s2 = (int64_t)E * ((H + 127) / 128) * ((I + 63) / 64) * (PACK_BLOCK / 16);
+    auto grid = [](int64_t slots) {
+        const int64_t b = (slots + 255) / 256;
+        return (unsigned)(b < 16384 ? b : 16384);
+    };
+    hipLaunchKernelGGL(k_pack_w13, dim3(grid(s13)), dim3(256), 0, s, (const u16*)w13, H, I,
+                       (i32x4*)p13, s13);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    hipLaunchKernelGGL(k_pack_w2, dim3(grid(s2)), dim3(256), 0, s, (const u16*)w2, H, I,
+                       (i32x4*)p2, s2);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- launchers
@@ -1211,6 +1338,7 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s)
         g.a_div = (P.fmt == MOE_FMT_BATCHED) ? 1 : P.K;
     }
     g.w13 = A.w13;
+    g.w_packed = P.wpacked;
     g.w13_scale = A.w13_scale;
     g.b13 = P.has_b13 ? A.w13_bias : nullptr;
     g.bias_dt = (P.act == MOE_F32) ? MOE_F32 : MOE_BF16;
@@ -1224,6 +1352,10 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s)
         return run_gemm1<MOE_F32, 1, 16>(g, P, s);
     switch (P.cfg) {
     case TILE_PREFILL:
+        if (getenv("MOE_G1") && atoi(getenv("MOE_G1")) == 3)
+            return run_gemm1_dma<5, 8, 3>(g, P, s);
+        if (getenv("MOE_G1") && atoi(getenv("MOE_G1")) == 2)
+            return run_gemm1_dma<5, 8, 2>(g, P, s);
         return run_gemm1_dma<5, 4, 2>(g, P, s);
     case TILE_MID: return run_gemm1<MOE_BF16, 4, 16>(g, P, s);
     default: return run_gemm1<MOE_BF16, 1, 16>(g, P, s);
@@ -1237,6 +1369,7 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
     g.z = P.z;
     g.z_scale = P.z_scale;
     g.w2 = A.w2;
+    g.w_packed = P.wpacked;
     g.w2_scale = A.w2_scale;
     g.b2 = P.has_b2 ? A.w2_bias : nullptr;
     g.bias_dt = (P.act == MOE_F32) ? MOE_F32 : MOE_BF16;

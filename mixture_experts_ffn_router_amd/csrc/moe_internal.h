@@ -122,6 +122,7 @@ struct Plan {
     int renorm, G, kg, gmode;
     float rsf;
     int has_b13, has_b2, breduce;
+    int wpacked;                    // weights in the packed block layout (bf16)
     int BM;                         // align granularity: each expert run padded to BM rows
     int CH;                         // rows per GEMM tile (a multiple of BM)
     int cfg;                        // GEMM tile family (see moe_gemm.hip)
@@ -154,5 +155,7 @@ hipError_t launch_quant_rows(const Plan& P, const void* hidden, hipStream_t s);
 hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s);
 hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s);
 hipError_t launch_reduce(const Plan& P, const moe_args& A, const float* topk_w, hipStream_t s);
+hipError_t launch_pack_weights(int E, int H, int I, const void* w13, const void* w2, void* p13,
+                               void* p2, hipStream_t s);
 
 }  // namespace moe

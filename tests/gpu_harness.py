@@ -33,9 +33,11 @@ def region(ws: torch.Tensor, off: int, dtype, count: int) -> np.ndarray:
     return ws[off:off + nbytes].view(dtype).cpu().numpy()
 
 
-def run_contiguous(inp: dict, dev, precomputed=None, out=None, inplace=False, out_dtype=None):
+def run_contiguous(inp: dict, dev, precomputed=None, out=None, inplace=False, out_dtype=None,
+                   packed=False):
     """One forward of a contiguous workload; returns (out, ws, info).
-    out_dtype=None keeps the workload's own output type."""
+    out_dtype=None keeps the workload's own output type; packed=True re-lays
+    the weights out with moe_pack_weights first."""
     cfg: W.MoeConfig = inp["cfg"]
     hidden = inp["hidden"].to(dev)
     kw = dict(out_dtype=out_dtype, top_k=cfg.top_k, renormalize=cfg.renormalize, routing=cfg.scoring,
@@ -43,6 +45,8 @@ def run_contiguous(inp: dict, dev, precomputed=None, out=None, inplace=False, ou
               group_select_mode=cfg.group_select_mode,
               routed_scaling_factor=cfg.routed_scaling_factor)
     w13, w2 = inp["w13"].to(dev), inp["w2"].to(dev)
+    if packed:
+        w13, w2 = B.pack_weights(w13, w2), None
     for name in ("w13_bias", "w2_bias", "w13_scale", "w2_scale"):
         if inp.get(name) is not None:
             kw[name] = inp[name].to(dev)
@@ -126,9 +130,12 @@ def check_output(inp: dict, out: torch.Tensor, ids_o, w_o, tokens=None, what="")
     return compare(cfg, got, y, what)
 
 
-def run_batched(inp: dict, dev, reduce=False, out_dtype=None):
+def run_batched(inp: dict, dev, reduce=False, out_dtype=None, packed=False):
     cfg = inp["cfg"]
     kw = {"out_dtype": out_dtype}
+    w13, w2 = inp["w13"].to(dev), inp["w2"].to(dev)
+    if packed:
+        w13, w2 = B.pack_weights(w13, w2), None
     for name in ("w13_scale", "w2_scale", "w13_bias", "w2_bias"):
         if inp.get(name) is not None:
             kw[name] = inp[name].to(dev)
@@ -136,7 +143,7 @@ def run_batched(inp: dict, dev, reduce=False, out_dtype=None):
         kw["token_map"] = inp["token_map"].to(dev)
         kw["token_map_w"] = inp["token_map_w"].to(dev)
     res = B.fused_moe_batched(inp["hidden"].to(dev), inp["expert_num_tokens"].to(dev),
-                              inp["w13"].to(dev), inp["w2"].to(dev), M=cfg.M, top_k=cfg.top_k,
+                              w13, w2, M=cfg.M, top_k=cfg.top_k,
                               **kw)
     torch.cuda.synchronize()
     return res

@@ -89,6 +89,11 @@ def _status(prob):
     (dict(fmt=B.MOE_FMT_BATCHED, max_tokens=0), B.MOE_ERR_INVALID_ARG),
     (dict(fmt=B.MOE_FMT_BATCHED, max_tokens=32, act_dtype=B.MOE_FP8_E4M3FN,
           w_dtype=B.MOE_FP8_E4M3FN), B.MOE_OK),
+    (dict(w_layout=B.MOE_W_PACKED), B.MOE_OK),
+    (dict(w_layout=2), B.MOE_ERR_INVALID_ARG),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_FP8_E4M3FN), B.MOE_ERR_UNSUPPORTED),
+    (dict(w_layout=B.MOE_W_PACKED, act_dtype=B.MOE_F32, w_dtype=B.MOE_F32, out_dtype=B.MOE_F32),
+     B.MOE_ERR_UNSUPPORTED),
 ])
 def test_problem_validation(kw, status):
     assert _status(_prob(**kw)) == status
@@ -154,3 +159,31 @@ def test_forward_rejects_bad_workspace():
     assert B.moe_forward_status(p.c(), _args(), 256 * 1024, info.bytes - 1, 0) == \
         B.MOE_ERR_WORKSPACE
     assert B.moe_status_string(B.MOE_ERR_WORKSPACE).startswith("workspace")
+
+
+def test_packed_weight_sizes():
+    """16 KiB blocks of 64 rows x 128 columns: w13 ceil(I/64) x ceil(H/64) per
+    expert (64 gate + 64 up columns a block), w2 ceil(H/128) x ceil(I/64)."""
+    for E, H, I in [(8, 4096, 14336), (2, 208, 176), (256, 7168, 2048), (1, 16, 16)]:
+        b13, b2 = B.moe_packed_weight_bytes(_prob(E=E, H=H, I=I, top_k=1).c())
+        blk = 64 * 128 * 2
+        assert b13 == E * -(-I // 64) * -(-H // 64) * blk
+        assert b2 == E * -(-H // 128) * -(-I // 64) * blk
+    for kw, status in [(dict(w_dtype=B.MOE_FP8_E4M3FN, I=256), B.MOE_ERR_UNSUPPORTED),
+                       (dict(act_dtype=B.MOE_F32, w_dtype=B.MOE_F32, out_dtype=B.MOE_F32),
+                        B.MOE_ERR_UNSUPPORTED),
+                       (dict(H=72), B.MOE_ERR_UNSUPPORTED)]:
+        b13, b2 = ctypes.c_size_t(), ctypes.c_size_t()
+        rc = B.load().moe_packed_weight_bytes(ctypes.byref(_prob(**kw).c()), ctypes.byref(b13),
+                                              ctypes.byref(b2))
+        assert rc == status
+
+
+def test_pack_rejects_null_pointers():
+    fake = 4096   # never dereferenced: the null check fails first
+    p = _prob().c()
+    lib = B.load()
+    assert lib.moe_pack_weights(ctypes.byref(p), None, fake, fake, fake, None) == \
+        B.MOE_ERR_INVALID_ARG
+    assert lib.moe_pack_weights(ctypes.byref(p), fake, fake, fake, None, None) == \
+        B.MOE_ERR_INVALID_ARG

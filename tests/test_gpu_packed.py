@@ -1,0 +1,117 @@
+"""Packed weight layout (moe_pack_weights): the packed bytes follow the
+layout moe.h documents, and a forward on packed weights equals the forward
+on the plain weights bit for bit (same products, same summation order) and
+so meets the oracle bar wherever the plain path does."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as GH
+from mixture_experts_ffn_router_amd import binding as B
+from mixture_experts_ffn_router_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _swz(k):
+    return 2 * ((k & 3) | ((k >> 1) & 4))
+
+
+def _ref_pack(w, gate_up):
+    """The documented layout, written out with numpy: 16 KiB blocks of 64 rows
+    x 16 slots of 8 columns; slot s of row k holds chunk s ^ swz(k)."""
+    E, K, N = w.shape
+    ncols = N // 2 if gate_up else N          # columns per half (w13) / all (w2)
+    bw = 64 if gate_up else 128               # columns of one half-block / block
+    nblk, nks = -(-ncols // bw), -(-K // 64)
+    out = np.zeros((E, nblk, nks, 64, 16, 8), dtype=np.uint16)
+    for j in range(nblk):
+        for kt in range(nks):
+            for k in range(64):
+                row = kt * 64 + k
+                if row >= K:
+                    continue
+                for s in range(16):
+                    c = s ^ _swz(k)
+                    if gate_up:
+                        col = bw * j + 8 * (c % 8)
+                        if col >= ncols:
+                            continue
+                        src = col if c < 8 else ncols + col
+                    else:
+                        src = bw * j + 8 * c
+                        if src >= ncols:
+                            continue
+                    out[:, j, kt, k, s, :] = w[:, row, src:src + 8]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("E,H,I", [(2, 208, 176), (3, 128, 256)])
+def test_pack_layout_bytes(E, H, I):
+    dev = GH.device()
+    g = torch.Generator().manual_seed(7)
+    w13 = torch.randn(E, H, 2 * I, generator=g).to(torch.bfloat16)
+    w2 = torch.randn(E, I, H, generator=g).to(torch.bfloat16)
+    print(f"[case] pack E={E} H={H} I={I}", flush=True)
+    pw = B.pack_weights(w13.to(dev), w2.to(dev))
+    torch.cuda.synchronize()
+    got13 = pw.w13.cpu().view(torch.int16).numpy().view(np.uint16)
+    got2 = pw.w2.cpu().view(torch.int16).numpy().view(np.uint16)
+    ref13 = _ref_pack(w13.view(torch.int16).numpy().view(np.uint16), True)
+    ref2 = _ref_pack(w2.view(torch.int16).numpy().view(np.uint16), False)
+    assert got13.shape == ref13.shape and got2.shape == ref2.shape
+    assert np.array_equal(got13, ref13)
+    assert np.array_equal(got2, ref2)
+
+
+SMALL_BF16 = [
+    W.MIXTRAL_PREFILL.scaled(name="mixtral_small", M=96, H=256, I=512),
+    W.MIXTRAL_PREFILL.scaled(name="mixtral_bm128", M=384, H=128, I=256, E=4),
+    W.DECODE_SMALL_EXPERTS.scaled(name="decode_small", M=8, H=256, I=128, E=32, top_k=4),
+    W.DEEPSEEK_GROUPED.scaled(name="deepseek_small", M=64, H=256, I=128, E=64),
+    W.MIXTRAL_PREFILL.scaled(name="ragged", M=200, H=208, I=176, E=4),
+]
+
+
+@pytest.mark.parametrize("tile_cfg", ["auto", "0", "1", "2"])
+@pytest.mark.parametrize("cfg", SMALL_BF16, ids=[c.name for c in SMALL_BF16])
+def test_packed_equals_plain_small(cfg, tile_cfg, monkeypatch):
+    dev = GH.device()
+    if tile_cfg != "auto":
+        monkeypatch.setenv("MOE_TILE_CFG", tile_cfg)
+    inp = W.make_inputs(cfg, 61)
+    print(f"[case] packed {cfg.name} tile_cfg={tile_cfg}", flush=True)
+    plain, _, _ = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+    packed, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, packed=True)
+    assert torch.equal(plain, packed)
+    ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    GH.check_output(inp, packed, ids_o, w_o, what="packed")
+
+
+@pytest.mark.parametrize("cfg", [W.MIXTRAL_PREFILL, W.DEEPSEEK_GROUPED],
+                         ids=["mixtral_prefill_bf16", "deepseek_grouped_sigmoid_bf16"])
+def test_packed_equals_plain_full_size(cfg):
+    dev = GH.device()
+    inp = W.make_inputs(cfg, 1000 + W.CONFIGS.index(cfg), device=dev)
+    print(f"[case] packed full {cfg.name}", flush=True)
+    plain, _, _ = GH.run_contiguous(inp, dev)
+    packed, _, _ = GH.run_contiguous(inp, dev, packed=True)
+    assert torch.equal(plain, packed)
+
+
+def test_packed_batched_bf16():
+    dev = GH.device()
+    cfg = W.BATCHED_FP8.scaled(name="batched_bf16_packed", M=96, H=256, I=256, E=8,
+                               weight="bf16")
+    inp = W.make_inputs(cfg, 1006)
+    for reduce in (False, True):
+        plain, _, _ = GH.run_batched(inp, dev, reduce=reduce, out_dtype=torch.float32)
+        packed, _, _ = GH.run_batched(inp, dev, reduce=reduce, out_dtype=torch.float32,
+                                      packed=True)
+        rows, _ = GH.batched_rows(inp) if not reduce else (None, None)
+        if reduce:
+            assert torch.equal(plain, packed)
+        else:
+            idx = torch.as_tensor(rows, device=dev)
+            flat_p, flat_k = plain.reshape(-1, cfg.H)[idx], packed.reshape(-1, cfg.H)[idx]
+            assert torch.equal(flat_p, flat_k)
