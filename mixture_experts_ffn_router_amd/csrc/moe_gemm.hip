@@ -701,9 +701,9 @@ __global__ void __launch_bounds__(256) k_gemm2(Gemm2Args g)
 //      fB(k) = 2 * ((k & 3) | ((k >> 1) & 4)); a transposing read touches 16
 //      rows x 32 bytes and fB sends the 8 rows of each half-wave to 8
 //      distinct 32-byte bank groups.
-// Out-of-range chunks (K tail, columns past N) are DMA'd from a zero page;
-// rows past the tile's real rows repeat its first row (their results are
-// never stored).
+// Out-of-range chunks (K tail, columns past N) and rows past the tile's real
+// rows are DMA'd from a zero page; strips that hold only padding skip their
+// fragment reads and MFMAs.
 __device__ __attribute__((aligned(16))) int32_t g_zero16[4] = {0, 0, 0, 0};
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p)
@@ -751,7 +751,7 @@ struct DS {
 // 4 (i % 16) .. +3).
 template <typename S>
 struct DmaSrc {
-    const char* a[S::A_PW];     // source row + chunk byte offset (K stage 0)
+    const char* a[S::A_PW];     // source row + chunk byte offset (K stage 0), null: padding row
     int a_k[S::A_PW];           // K element of the chunk within a stage
     const char* b[S::B_PW];     // weight row (K stage 0) + column byte, or null
     int b_k[S::B_PW];           // K row within a stage
@@ -764,7 +764,7 @@ struct DmaSrc {
         const char* zero = (const char*)g_zero16;
 #pragma unroll
         for (int j = 0; j < S::A_PW; ++j) {
-            const char* p = (live && kt * 64 + a_k[j] < K) ? a[j] + kt * 128 : zero;
+            const char* p = (live && a[j] && kt * 64 + a_k[j] < K) ? a[j] + kt * 128 : zero;
             dma16(p, lds + (wave + 4 * j) * 1024);
         }
 #pragma unroll
@@ -848,13 +848,15 @@ struct DmaFrag {
                         8 * (s & 1);
     }
 
+    // the MFMAs of the wave's first NM strips (the others hold only padding)
+    template <int NM>
     __device__ __forceinline__ void stage(const char* st, int rg, f32x4 (&acc)[S::FMW][S::FN]) const
     {
         const char* As = st + rg * S::FMW * 2048;
         const char* Bs = st + S::A_BYTES;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 a[S::FMW], b[S::FN];
+            bf16x8 a[NM], b[S::FN];
 #pragma unroll
             for (int fn = 0; fn < S::FN; ++fn) {
                 const char* p = Bs + b_off[fn] + ks * 32 * S::RB;
@@ -864,31 +866,44 @@ struct DmaFrag {
                 b[fn] = __builtin_bit_cast(bf16x8, v);
             }
 #pragma unroll
-            for (int fm = 0; fm < S::FMW; ++fm)
+            for (int fm = 0; fm < NM; ++fm)
                 a[fm] = __builtin_bit_cast(bf16x8, *(const i32x4*)(As + fm * 2048 + a_off[ks]));
 #pragma unroll
-            for (int fm = 0; fm < S::FMW; ++fm)
+            for (int fm = 0; fm < NM; ++fm)
 #pragma unroll
                 for (int fn = 0; fn < S::FN; ++fn)
                     acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(SCHED_DS_READ, S::FMW + 2 * S::FN, 0);
-            __builtin_amdgcn_sched_group_barrier(SCHED_MFMA, S::FMW * S::FN, 0);
+            __builtin_amdgcn_sched_group_barrier(SCHED_DS_READ, NM + 2 * S::FN, 0);
+            __builtin_amdgcn_sched_group_barrier(SCHED_MFMA, NM * S::FN, 0);
         }
     }
 };
 
-// Source row of tile row `row` for GEMM1's A (activations): the routed token's
-// row, the padded position itself (a_ident), or - for padding - the tile's
-// first row.
-__device__ __forceinline__ int64_t gemm1_src_row(const Gemm1Args& g, int r0, int row, int rows)
+// The mainloop with the MFMAs of the wave's first `live` strips (wave
+// uniform): one instantiation per count, so the loop body stays branch free;
+// every wave still issues its DMAs and meets every barrier.
+template <typename S, int NM = S::FMW>
+__device__ __forceinline__ void dma_run(const DmaSrc<S>& src, char* ring, int K, int wave, int rg,
+                                        const DmaFrag<S>& fr, f32x4 (&acc)[S::FMW][S::FN], int live)
 {
-    const int64_t p = (int64_t)r0 + (row < rows ? row : 0);
-    if (g.a_ident)
-        return p;
-    int sid = g.s.sorted[p];
-    if (sid >= g.s.sentinel)
-        sid = g.s.sorted[r0];
-    return sid / g.a_div;
+    if constexpr (NM == 0) {
+        dma_mainloop<S>(src, ring, K, wave, [](const char*) {});
+    } else {
+        if (live >= NM) {
+            dma_mainloop<S>(src, ring, K, wave,
+                            [&](const char* st) { fr.template stage<NM>(st, rg, acc); });
+            return;
+        }
+        dma_run<S, NM - 1>(src, ring, K, wave, rg, fr, acc, live);
+    }
+}
+
+// Source row of real tile row `row` (< rows) for GEMM1's A (activations):
+// the routed token's row, or the padded position itself (a_ident).
+__device__ __forceinline__ int64_t gemm1_src_row(const Gemm1Args& g, int r0, int row)
+{
+    const int64_t p = (int64_t)r0 + row;
+    return g.a_ident ? p : (int64_t)(g.s.sorted[p] / g.a_div);
 }
 
 // GEMM1 tile: BN/2 gate columns n0.. and the matching BN/2 up columns I + n0..
@@ -911,7 +926,7 @@ __device__ __forceinline__ void gemm1_tile_dma(const Gemm1Args& g, char* ring, i
     for (int j = 0; j < S::A_PW; ++j) {
         int row, c;
         dma_a_slot<S>(j, wave, lane, row, c);
-        src.a[j] = abase + gemm1_src_row(g, r0, row, rows) * H * 2 + c * 16;
+        src.a[j] = (row < rows) ? abase + gemm1_src_row(g, r0, row) * H * 2 + c * 16 : nullptr;
         src.a_k[j] = c * 8;
     }
     // weight block bb of the tile: z columns n0 + 64 bb .. +63 (chunks 0-7
@@ -958,7 +973,7 @@ __device__ __forceinline__ void gemm1_tile_dma(const Gemm1Args& g, char* ring, i
             acc[fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // (the mainloop ends with a barrier: the ring becomes the output staging area)
-    dma_mainloop<S>(src, ring, H, wave, [&](const char* st) { fr.stage(st, rg, acc); });
+    dma_run<S>(src, ring, H, wave, rg, fr, acc, min(max(strips - rg * FMW, 0), FMW));
 
     constexpr int O_STRIDE = BNZ + 4;
     static_assert(32 * FMW * O_STRIDE * 4 <= S::RING, "z staging fits in the ring");
@@ -1016,15 +1031,14 @@ __device__ __forceinline__ void gemm2_tile_dma(const Gemm2Args& g, char* ring, i
     const int c0 = ntile * S::BN;
     const int strips = (rows + 15) >> 4;
 
-    // z rows are the padded positions; rows past the tile's strips repeat row r0
+    // z rows are the padded positions; rows past the real ones read the zero page
     DmaSrc<S> src;
     const char* zbase = (const char*)g.z;
 #pragma unroll
     for (int j = 0; j < S::A_PW; ++j) {
         int row, c;
         dma_a_slot<S>(j, wave, lane, row, c);
-        const int64_t p = (int64_t)r0 + (row < strips * 16 ? row : 0);
-        src.a[j] = zbase + p * I * 2 + c * 16;
+        src.a[j] = (row < rows) ? zbase + ((int64_t)r0 + row) * I * 2 + c * 16 : nullptr;
         src.a_k[j] = c * 8;
     }
     // weight block bb of the tile: output columns c0 + 128 bb .. +127;
@@ -1066,7 +1080,7 @@ __device__ __forceinline__ void gemm2_tile_dma(const Gemm2Args& g, char* ring, i
         for (int fn = 0; fn < FN; ++fn)
             acc[fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    dma_mainloop<S>(src, ring, I, wave, [&](const char* st) { fr.stage(st, rg, acc); });
+    dma_run<S>(src, ring, I, wave, rg, fr, acc, min(max(strips - rg * FMW, 0), FMW));
 
     // epilogue straight from the accumulators: 16 lanes store 16 consecutive columns of a row
     const int g4 = lane >> 4, s16 = lane & 15;
@@ -1352,10 +1366,6 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s)
         return run_gemm1<MOE_F32, 1, 16>(g, P, s);
     switch (P.cfg) {
     case TILE_PREFILL:
-        if (getenv("MOE_G1") && atoi(getenv("MOE_G1")) == 3)
-            return run_gemm1_dma<5, 8, 3>(g, P, s);
-        if (getenv("MOE_G1") && atoi(getenv("MOE_G1")) == 2)
-            return run_gemm1_dma<5, 8, 2>(g, P, s);
         return run_gemm1_dma<5, 4, 2>(g, P, s);
     case TILE_MID: return run_gemm1<MOE_BF16, 4, 16>(g, P, s);
     default: return run_gemm1<MOE_BF16, 1, 16>(g, P, s);
