@@ -231,10 +231,11 @@ int moe_forward_timed(const moe_problem* p, const moe_args* a, void* workspace,
  * 16 KiB blocks, each 64 weight rows (K) x 128 weight columns (N) of bf16:
  *   row k of a block is 256 bytes = 16 slots of 16 bytes; slot s holds the
  *   8-column chunk c = s ^ (2 * ((k & 3) | ((k >> 1) & 4))) of that row.
- *   w13: block (e, j, kt), j < ceil(I / 64), kt < ceil(H / 64), in that order;
- *        chunks 0-7 are gate columns 64 j + 8 c .., chunks 8-15 the up
- *        columns I + 64 j + 8 (c - 8) .., of weight rows 64 kt + k.
- *   w2:  block (e, j, kt), j < ceil(H / 128), kt < ceil(I / 64); chunk c holds
+ *   w13: block (e, kt, j), kt < ceil(H / 64), j < ceil(I / 64), in that order
+ *        (j fastest: the blocks of one K stage are adjacent); chunks 0-7 are
+ *        gate columns 64 j + 8 c .., chunks 8-15 the up columns
+ *        I + 64 j + 8 (c - 8) .., of weight rows 64 kt + k.
+ *   w2:  block (e, kt, j), kt < ceil(I / 64), j < ceil(H / 128); chunk c holds
  *        columns 128 j + 8 c .. of weight rows 64 kt + k.
  *   Rows past H (w13) / I (w2) and columns past I (w13) / H (w2) are zero.
  *

@@ -120,10 +120,14 @@ static int choose_tile(const moe_problem* p, int64_t rows_cap)
     return TILE_PREFILL;
 }
 
+// Internal workspace regions beyond moe_workspace_info: chunk tables and the
+// position of every routed item in the sorted order.
+enum { INT_CHUNK_OFF = 0, INT_CHUNK_EXPERT = 1, INT_INV = 2, INT_REGIONS = 3 };
+
 static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_offs = nullptr,
                   int* cfg_out = nullptr)
 {
-    size_t off_chunk_off = 0, off_chunk_expert = 0;
+    size_t off_chunk_off = 0, off_chunk_expert = 0, off_inv = 0;
     const int rc = validate(p);
     if (rc != MOE_OK)
         return rc;
@@ -159,19 +163,21 @@ static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_
     w.off_num_post_padded = take(4);
     off_chunk_off = take((size_t)(p->E + 1) * 4);
     off_chunk_expert = take((size_t)w.max_blocks * 4);
+    off_inv = take(batched ? 0 : (size_t)MK * 4);
     const bool quant = fp8 && p->act_dtype != MOE_FP8_E4M3FN;
     const int64_t qrows = batched ? max_sorted : p->M;
     w.off_aq = take(quant ? (size_t)qrows * p->H : 0);
     w.off_aq_scale = take(quant ? (size_t)qrows * 4 : 0);
     w.off_z = take((size_t)max_sorted * p->I * zes);
     w.off_z_scale = take(fp8 ? (size_t)max_sorted * (p->I / 128) * 4 : 0);
-    const int64_t orows = batched ? (p->batched_reduce ? max_sorted : 0) : MK;
+    const int64_t orows = (batched && !p->batched_reduce) ? 0 : max_sorted;
     w.off_o = take((size_t)orows * p->H * 4);
     w.bytes = off;
     *info = w;
     if (chunk_offs) {
-        chunk_offs[0] = off_chunk_off;
-        chunk_offs[1] = off_chunk_expert;
+        chunk_offs[INT_CHUNK_OFF] = off_chunk_off;
+        chunk_offs[INT_CHUNK_EXPERT] = off_chunk_expert;
+        chunk_offs[INT_INV] = off_inv;
     }
     if (cfg_out)
         *cfg_out = choose_tile(p, rows_cap);
@@ -206,8 +212,9 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
     P.BM = w.block_m;
     P.cfg = cfg;
     P.CH = tile_rows(cfg);
-    P.chunk_off = (int32_t*)(ws + chunk_offs[0]);
-    P.chunk_expert = (int32_t*)(ws + chunk_offs[1]);
+    P.chunk_off = (int32_t*)(ws + chunk_offs[INT_CHUNK_OFF]);
+    P.chunk_expert = (int32_t*)(ws + chunk_offs[INT_CHUNK_EXPERT]);
+    P.inv = (int32_t*)(ws + chunk_offs[INT_INV]);
     P.max_sorted = w.max_sorted_len;
     P.max_blocks = w.max_blocks;
     P.rows_cap = w.max_sorted_len - (int64_t)p->E * (w.block_m - 1);
@@ -271,7 +278,7 @@ static int forward(const moe_problem* p, const moe_args* a, void* workspace,
                    size_t workspace_bytes, void* stream, void** events)
 {
     moe_workspace_info w;
-    size_t chunk_offs[2];
+    size_t chunk_offs[INT_REGIONS];
     int cfg = 0;
     int rc = layout(p, &w, chunk_offs, &cfg);
     if (rc != MOE_OK)

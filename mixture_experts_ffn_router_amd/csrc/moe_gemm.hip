@@ -155,8 +155,9 @@ struct Gemm2Args {
     const void* b2;             // [E, H] or null
     int bias_dt;
     int H, I;
-    int out_mode;               // 0: float o[sorted[p]]; 1: out[sorted[p]] (out_dt); 2: float o[p]
+    int out_mode;               // 1: out[sorted[p]] (out_dt, batched slabs); 2: float o[p]
     int out_dt;
+    int T;                      // batched: rows per expert slab
     void* out;
 };
 
@@ -167,21 +168,49 @@ struct Gemm2Args {
 // over the 8 XCDs (workgroup b runs on XCD b % 8), so XCD x is given the
 // contiguous range [x R/8, (x+1) R/8) of the R tiles and walks it with its own
 // workgroups: neighbouring tiles run together on one XCD and share its L2.
-// f(e, row0, rows, ntile): rows = real rows of the chunk (>= 1).
-template <int CH, typename F>
-__device__ __forceinline__ void for_each_tile(const Sched& s, F&& f)
-{
-    const int nt = s.n_tiles;
-    const int R = s.chunk_off[s.E] * nt;
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = gridDim.x >> 3;
-    const int lo = (int)(((int64_t)R * xcd) >> 3), hi = (int)(((int64_t)R * (xcd + 1)) >> 3);
-    for (int L = lo + slot; L < hi; L += per) {
+struct TileRef {
+    int e, r0, rows, ntile;     // expert, first padded row, real rows (>= 1), column block
+    int base;                   // first padded row of the expert's run
+};
+
+template <int CH>
+struct TileIter {
+    int L, hi, per, nt;
+
+    __device__ __forceinline__ explicit TileIter(const Sched& s)
+    {
+        nt = s.n_tiles;
+        const int R = s.chunk_off[s.E] * nt;
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        per = gridDim.x >> 3;
+        const int lo = (int)(((int64_t)R * xcd) >> 3);
+        hi = (int)(((int64_t)R * (xcd + 1)) >> 3);
+        L = lo + slot;
+    }
+
+    __device__ __forceinline__ bool next(const Sched& s, TileRef& t)
+    {
+        if (L >= hi)
+            return false;
         const int e = s.chunk_expert[L / nt];
         const int c0 = s.chunk_off[e], nch = s.chunk_off[e + 1] - c0;
         const int local = L - c0 * nt;
         const int j = local % nch;
-        f(e, s.offsets[e] + j * CH, min(CH, s.counts[e] - j * CH), local / nch);
+        const int base = s.offsets[e];
+        t = TileRef{e, base + j * CH, min(CH, s.counts[e] - j * CH), local / nch, base};
+        L += per;
+        return true;
     }
+};
+
+// f(e, row0, rows, ntile) for every tile of this workgroup.
+template <int CH, typename F>
+__device__ __forceinline__ void for_each_tile(const Sched& s, F&& f)
+{
+    TileIter<CH> it(s);
+    TileRef t;
+    while (it.next(s, t))
+        f(t.e, t.r0, t.rows, t.ntile);
 }
 
 // ---------------------------------------------------------------- tile shapes
@@ -246,8 +275,9 @@ struct Stager {
     i32x4 ra[S::A_PER_T], rb[S::B_PER_T];
     float rs;                           // fp8 z: this thread's row scale (tid < CH)
 
+    // weights: row kk of K stage kt at wbase + kt * w_stage + kk * w_ld + column byte
     __device__ __forceinline__ void load(int kt, const char* abase, int64_t a_k_bytes,
-                                         const char* wbase, int64_t w_ld_bytes, int K)
+                                         const char* wbase, int64_t w_ld, int64_t w_stage, int K)
     {
         const int k0 = kt * S::BK;
 #pragma unroll
@@ -262,7 +292,7 @@ struct Stager {
             rb[i] = i32x4{0, 0, 0, 0};
             const int k = k0 + b_kk[i];
             if (b_off[i] >= 0 && k < K)
-                rb[i] = *(const i32x4*)(wbase + (int64_t)k * w_ld_bytes + b_off[i]);
+                rb[i] = *(const i32x4*)(wbase + kt * w_stage + (int64_t)b_kk[i] * w_ld + b_off[i]);
         }
     }
     __device__ __forceinline__ void store(char* stage) const
@@ -330,13 +360,14 @@ __device__ __forceinline__ void gemm1_tile(const Gemm1Args& g, char* smem, int e
     }
     const char* abase = (const char*)g.a;
     const char* wbase = (const char*)g.w13 + (int64_t)e * H * N * ES;
-    int64_t w_ld = (int64_t)N * ES;
+    int64_t w_ld = (int64_t)N * ES, w_stage = S::BK * w_ld;
     if constexpr (DT == MOE_BF16) {
         static_assert(DT != MOE_BF16 || BNZ == 64, "packed w13 blocks pair 64 gate and 64 up columns");
-        if (g.w_packed) {   // rows of the (e, ntile) block run: 256 bytes each, 64 per K stage
+        if (g.w_packed) {   // block (e, kt, ntile): 64 rows of 256 bytes
             const int64_t nblk = (I + 63) / 64, nks = (H + 63) / 64;
-            wbase = (const char*)g.w13 + ((int64_t)e * nblk + ntile) * nks * PACK_BLOCK;
+            wbase = (const char*)g.w13 + ((int64_t)e * nks * nblk + ntile) * PACK_BLOCK;
             w_ld = 256;
+            w_stage = nblk * PACK_BLOCK;
         }
     }
 
@@ -348,13 +379,13 @@ __device__ __forceinline__ void gemm1_tile(const Gemm1Args& g, char* smem, int e
             acc[0][fm][fn] = acc[1][fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int nk = (H + S::BK - 1) / S::BK;
-    st.load(0, abase, (int64_t)H * ES, wbase, w_ld, H);
+    st.load(0, abase, (int64_t)H * ES, wbase, w_ld, w_stage, H);
     st.store(smem);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         const bool more = kt + 1 < nk;
         if (more)
-            st.load(kt + 1, abase, (int64_t)H * ES, wbase, w_ld, H);
+            st.load(kt + 1, abase, (int64_t)H * ES, wbase, w_ld, w_stage, H);
         const char* As = smem + (kt & 1) * S::STAGE_BYTES;
         const char* Bs = As + S::A_BYTES;
 #pragma unroll
@@ -528,17 +559,18 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int e
     }
     const char* zbase = (const char*)g.z;
     const char* wbase = (const char*)g.w2 + (int64_t)e * I * H * ES;
-    int64_t w_ld = (int64_t)H * ES;
+    int64_t w_ld = (int64_t)H * ES, w_stage = S::BK * w_ld;
     if constexpr (DT == MOE_BF16) {
         static_assert(DT != MOE_BF16 || BN == 128, "packed w2 blocks are 128 columns");
-        if (g.w_packed) {
+        if (g.w_packed) {   // block (e, kt, ntile)
             const int64_t nblk = (H + 127) / 128, nks = (I + 63) / 64;
-            wbase = (const char*)g.w2 + ((int64_t)e * nblk + ntile) * nks * PACK_BLOCK;
+            wbase = (const char*)g.w2 + ((int64_t)e * nks * nblk + ntile) * PACK_BLOCK;
             w_ld = 256;
+            w_stage = nblk * PACK_BLOCK;
         }
     }
     auto load = [&](int kt) {
-        st.load(kt, zbase, (int64_t)I * ES, wbase, w_ld, I);
+        st.load(kt, zbase, (int64_t)I * ES, wbase, w_ld, w_stage, I);
         if constexpr (FP8)
             st.rs = (tid < strips * 16) ? g.z_scale[((int64_t)r0 + tid) * ngrp + kt] : 0.0f;
     };
@@ -742,35 +774,67 @@ struct DS {
     static constexpr int D = A_PW + B_PW;
     static constexpr int RING = NS * STAGE;
     static_assert(NS >= 2 && NS <= 4, "ring depth");
-    static_assert(FN == 4 || FN == 8, "128 or 256 weight columns");
+    static_assert(FN == 4 || FN == 8, "128 or 256 weight columns (one or two weight blocks)");
     static_assert((NS - 2) * D < 64, "vmcnt range");
 };
 
-// Per-lane DMA sources of one tile.  Wave w issues the A DMAs i = w + 4j
-// (tile rows 8i .. 8i+7) and the B DMAs i = w + 4j (block i / 16, K rows
-// 4 (i % 16) .. +3).
-template <typename S>
-struct DmaSrc {
-    const char* a[S::A_PW];     // source row + chunk byte offset (K stage 0), null: padding row
-    int a_k[S::A_PW];           // K element of the chunk within a stage
-    const char* b[S::B_PW];     // weight row (K stage 0) + column byte, or null
-    int b_k[S::B_PW];           // K row within a stage
-    int64_t b_step;             // bytes per K stage of the weights
+// DMA sources of one tile.  Wave w issues the A DMAs i = w + 4j (tile rows
+// 8i .. 8i+7; lane l: row 8i + l/8, 16-byte K chunk (l%8) ^ ((row>>1)&7)) and
+// the B DMAs i = w + 4j (weight block i/16, K rows 4(i%16) + l/16, slot l%16).
+// A lane keeps a pointer per A DMA; weight addresses are recomputed per issue
+// from uniform bases.  PACKED: each weight block of a K stage is one
+// contiguous 16 KiB block of the packed layout; plain: the weights are read
+// in place (W13: [H, 2I] gate | up; else [I, H]).
+template <typename S, bool PACKED, bool W13>
+struct DmaTile {
+    const char* wb[S::NB];      // PACKED: block (stage 0) per tile block, null past N;
+                                //   plain: wb[0] = the expert's weight matrix
+    int64_t w_ld;               // plain: bytes per weight row
+    int64_t w_stage;            // PACKED: bytes from one K stage's blocks to the next
+    int n0;                     // plain: first column of the tile (z column for W13)
+    int ncols;                  // plain: columns (I for W13, H otherwise)
+    int K;                      // contraction length
+    const char* ap[S::A_PW];    // this lane's A chunk (K stage 0), null: padding row
 
-    // stage kt into the LDS stage at `lds`; live = false sends every lane
-    // to the zero page (a filler stage past the last one)
-    __device__ __forceinline__ void issue(int kt, int K, uint32_t lds, int wave, bool live) const
+    __device__ __forceinline__ void issue(int kt, uint32_t lds, int wave, bool live) const
     {
+        const int lane = threadIdx.x & 63;
         const char* zero = (const char*)g_zero16;
 #pragma unroll
         for (int j = 0; j < S::A_PW; ++j) {
-            const char* p = (live && a[j] && kt * 64 + a_k[j] < K) ? a[j] + kt * 128 : zero;
-            dma16(p, lds + (wave + 4 * j) * 1024);
+            const int i = wave + 4 * j;
+            const int row = 8 * i + (lane >> 3);
+            const int c = (lane & 7) ^ ((row >> 1) & 7);
+            const bool ok = live && ap[j] && kt * 64 + c * 8 < K;
+            const char* p = ok ? ap[j] + kt * 128 : zero;
+            dma16(p, lds + i * 1024);
         }
 #pragma unroll
         for (int j = 0; j < S::B_PW; ++j) {
-            const char* p = (live && b[j] && kt * 64 + b_k[j] < K) ? b[j] + kt * b_step : zero;
-            dma16(p, lds + S::A_BYTES + (wave + 4 * j) * 1024);
+            const int i = wave + 4 * j;
+            const int bb = i >> 4, k = 4 * (i & 15) + (lane >> 4);
+            const char* p = zero;
+            if constexpr (PACKED) {
+                // a select, not wb[bb]: bb depends on the wave index, and a
+                // runtime index would put wb in scratch memory
+                const char* w = (S::NB == 1 || bb == 0) ? wb[0] : wb[S::NB - 1];
+                if (live && w)
+                    p = w + kt * w_stage + (i & 15) * 1024 + lane * 16;
+            } else {
+                const int c = (lane & 15) ^ swz_b(k);
+                int col, valid;
+                if constexpr (W13) {
+                    const int zc = n0 + 64 * bb + 8 * (c & 7);
+                    valid = zc < ncols;
+                    col = (c < 8) ? zc : ncols + zc;
+                } else {
+                    col = n0 + 128 * bb + 8 * c;
+                    valid = col < ncols;
+                }
+                if (live && valid && kt * 64 + k < K)
+                    p = wb[0] + (int64_t)(kt * 64 + k) * w_ld + (int64_t)col * 2;
+            }
+            dma16(p, lds + S::A_BYTES + i * 1024);
         }
     }
 };
@@ -784,33 +848,32 @@ __device__ __forceinline__ void dma_a_slot(int j, int wave, int lane, int& row, 
     chunk = (lane & 7) ^ ((row >> 1) & 7);
 }
 
-// Weight block, K row, LDS slot and 8-column chunk of this lane's j-th B DMA.
-template <typename S>
-__device__ __forceinline__ void dma_b_slot(int j, int wave, int lane, int& blk, int& k, int& slot,
-                                           int& chunk)
-{
-    const int i = wave + 4 * j;
-    blk = i >> 4;
-    k = 4 * (i & 15) + (lane >> 4);
-    slot = lane & 15;
-    chunk = slot ^ swz_b(k);
-}
-
-// The DMA ring over all K stages; compute(stage pointer) consumes one stage.
-// Every iteration issues exactly one stage (a zero-page filler once the real
-// stages run out), so when stage kt is awaited exactly NS - 2 stages of D
-// DMAs per wave were issued after it, one constant wait serves every
-// iteration and the loop body stays one basic block (branches in it make the
-// register allocator copy the accumulators between VGPRs and AGPRs).
-template <typename S, typename F>
-__device__ __forceinline__ void dma_mainloop(const DmaSrc<S>& src, char* ring, int K, int wave,
-                                             F&& compute)
+// The DMA ring over the K stages of one tile.  dma_prologue issues stages
+// 0 .. NS-2; dma_mainloop then, per stage, waits for it, refills the slot
+// freed one iteration earlier and hands the stage to compute().  Every
+// iteration issues exactly one stage (a zero-page filler once the real stages
+// run out), so when stage kt is awaited exactly NS - 2 stages of D DMAs per
+// wave were issued after it: one constant wait serves every iteration and the
+// loop body stays one basic block (branches in it make the register
+// allocator copy the accumulators between VGPRs and AGPRs).  The loop ends
+// drained, with every wave past its last LDS read, so the next tile's
+// prologue may refill the ring at once.
+template <typename S, typename Src>
+__device__ __forceinline__ void dma_prologue(const Src& src, char* ring, int K, int wave)
 {
     const int nk = (K + 63) / 64;
     const uint32_t ring_lds = lds_u32(ring);
 #pragma unroll
     for (int st = 0; st < S::NS - 1; ++st)
-        src.issue(st, K, ring_lds + st * S::STAGE, wave, st < nk);
+        src.issue(st, ring_lds + st * S::STAGE, wave, st < nk);
+}
+
+template <typename S, typename Src, typename F>
+__device__ __forceinline__ void dma_mainloop(const Src& src, char* ring, int K, int wave,
+                                             F&& compute)
+{
+    const int nk = (K + 63) / 64;
+    const uint32_t ring_lds = lds_u32(ring);
     int slot = 0;                                   // kt % NS
     for (int kt = 0; kt < nk; ++kt) {
         wait_vmcnt<(S::NS - 2) * S::D>();
@@ -819,7 +882,7 @@ __device__ __forceinline__ void dma_mainloop(const DmaSrc<S>& src, char* ring, i
         // wave finished before the barrier
         const int nx = kt + S::NS - 1;
         const int nslot = (slot == 0) ? S::NS - 1 : slot - 1;   // nx % NS
-        src.issue(nx, K, ring_lds + nslot * S::STAGE, wave, nx < nk);
+        src.issue(nx, ring_lds + nslot * S::STAGE, wave, nx < nk);
         compute(ring + slot * S::STAGE);
         slot = (slot == S::NS - 1) ? 0 : slot + 1;
     }
@@ -882,8 +945,8 @@ struct DmaFrag {
 // The mainloop with the MFMAs of the wave's first `live` strips (wave
 // uniform): one instantiation per count, so the loop body stays branch free;
 // every wave still issues its DMAs and meets every barrier.
-template <typename S, int NM = S::FMW>
-__device__ __forceinline__ void dma_run(const DmaSrc<S>& src, char* ring, int K, int wave, int rg,
+template <typename S, int NM = S::FMW, typename Src>
+__device__ __forceinline__ void dma_run(const Src& src, char* ring, int K, int wave, int rg,
                                         const DmaFrag<S>& fr, f32x4 (&acc)[S::FMW][S::FN], int live)
 {
     if constexpr (NM == 0) {
@@ -906,55 +969,143 @@ __device__ __forceinline__ int64_t gemm1_src_row(const Gemm1Args& g, int r0, int
     return g.a_ident ? p : (int64_t)(g.s.sorted[p] / g.a_div);
 }
 
-// GEMM1 tile: BN/2 gate columns n0.. and the matching BN/2 up columns I + n0..
-template <int FMW, int FN, int NS>
-__device__ __forceinline__ void gemm1_tile_dma(const Gemm1Args& g, char* ring, int e, int r0,
-                                               int rows, int ntile)
+// Makes the compiler hold v in a register here.  Values loaded from global
+// memory ahead of time are pinned this way right after the ring has drained,
+// so that the compiler's wait for them (it does not see the DMAs) costs
+// nothing instead of stalling behind the next tile's DMAs.
+template <typename T>
+__device__ __forceinline__ void pin(const T& v)
 {
-    typedef DS<FMW, FN, NS> S;
-    constexpr int BNZ = S::BN / 2;                    // z columns per tile
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rg = wave >> 1, cg = wave & 1;
-    const int H = g.H, I = g.I, N = 2 * I;
-    const int n0 = ntile * BNZ;
-    const int strips = (rows + 15) >> 4;
+    asm volatile("" : : "v"(v));
+}
 
-    DmaSrc<S> src;
-    const char* abase = (const char*)g.a;
+// Per-lane source rows of one GEMM1 tile's A DMAs (-1: padding row); loaded
+// one tile ahead.
+template <typename S>
+__device__ __forceinline__ void gemm1_rows(const Gemm1Args& g, const TileRef& t, int wave, int lane,
+                                           int (&src)[S::A_PW])
+{
 #pragma unroll
     for (int j = 0; j < S::A_PW; ++j) {
         int row, c;
         dma_a_slot<S>(j, wave, lane, row, c);
-        src.a[j] = (row < rows) ? abase + gemm1_src_row(g, r0, row) * H * 2 + c * 16 : nullptr;
-        src.a_k[j] = c * 8;
+        src[j] = (row < t.rows) ? (int)gemm1_src_row(g, t.r0, row) : -1;
     }
-    // weight block bb of the tile: z columns n0 + 64 bb .. +63 (chunks 0-7
-    // gate, 8-15 up); packed, it is block (e, n0 / 64 + bb) of the layout
-    const int64_t nblk = (I + 63) / 64, nks = (H + 63) / 64;
+}
+
+// DMA sources of a GEMM1 tile: BN/2 gate columns n0.. and the matching BN/2
+// up columns I + n0..; weight block bb holds z columns n0 + 64 bb .. +63
+// (chunks 0-7 gate, 8-15 up), packed it is block (e, kt, n0 / 64 + bb).
+template <typename S, bool PACKED>
+__device__ __forceinline__ void gemm1_src(const Gemm1Args& g, const TileRef& t,
+                                          const int (&srow)[S::A_PW], DmaTile<S, PACKED, true>& d)
+{
+    const int H = g.H, I = g.I, N = 2 * I;
+    const int n0 = t.ntile * (S::BN / 2);
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    d.n0 = n0;
+    d.ncols = I;
+    d.K = H;
+    d.w_ld = (int64_t)N * 2;
+    if constexpr (PACKED) {
+        const int64_t nblk = (I + 63) / 64, nks = (H + 63) / 64;
+        d.w_stage = nblk * PACK_BLOCK;
 #pragma unroll
-    for (int j = 0; j < S::B_PW; ++j) {
-        int bb, k, sl, c;
-        dma_b_slot<S>(j, wave, lane, bb, k, sl, c);
-        const int zc = n0 + 64 * bb + 8 * (c & 7);
-        if (g.w_packed) {
+        for (int bb = 0; bb < S::NB; ++bb) {
             const int64_t jb = n0 / 64 + bb;
-            src.b[j] = (jb < nblk) ? (const char*)g.w13 + ((e * nblk + jb) * nks) * PACK_BLOCK +
-                                         k * S::RB + sl * 16
+            d.wb[bb] = (jb < nblk) ? (const char*)g.w13 + (t.e * nks * nblk + jb) * PACK_BLOCK
                                    : nullptr;
-        } else {
-            const int col = (c < 8) ? zc : I + zc;
-            src.b[j] = (zc < I) ? (const char*)g.w13 + (int64_t)e * H * N * 2 + (int64_t)k * N * 2 +
-                                      (int64_t)col * 2
-                                : nullptr;
         }
-        src.b_k[j] = k;
+    } else {
+        d.wb[0] = (const char*)g.w13 + (int64_t)t.e * H * N * 2;
     }
-    src.b_step = g.w_packed ? PACK_BLOCK : (int64_t)64 * N * 2;
+#pragma unroll
+    for (int j = 0; j < S::A_PW; ++j) {
+        const int row = 8 * (wave + 4 * j) + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        d.ap[j] = (srow[j] >= 0) ? (const char*)g.a + (int64_t)srow[j] * H * 2 + c * 16 : nullptr;
+    }
+}
+
+// DMA sources of a GEMM2 tile: BN output columns c0..; A rows are the padded
+// positions (z written by GEMM1); weight block bb holds columns c0 + 128 bb ..,
+// packed it is block (e, kt, c0 / 128 + bb).
+template <typename S, bool PACKED>
+__device__ __forceinline__ void gemm2_src(const Gemm2Args& g, const TileRef& t, int wave,
+                                          DmaTile<S, PACKED, false>& d)
+{
+    const int H = g.H, I = g.I;
+    const int c0 = t.ntile * S::BN;
+    const int lane = threadIdx.x & 63;
+    d.n0 = c0;
+    d.ncols = H;
+    d.K = I;
+    d.w_ld = (int64_t)H * 2;
+    if constexpr (PACKED) {
+        const int64_t nblk = (H + 127) / 128, nks = (I + 63) / 64;
+        d.w_stage = nblk * PACK_BLOCK;
+#pragma unroll
+        for (int bb = 0; bb < S::NB; ++bb) {
+            const int64_t jb = c0 / 128 + bb;
+            d.wb[bb] = (jb < nblk) ? (const char*)g.w2 + (t.e * nks * nblk + jb) * PACK_BLOCK
+                                   : nullptr;
+        }
+    } else {
+        d.wb[0] = (const char*)g.w2 + (int64_t)t.e * I * H * 2;
+    }
+#pragma unroll
+    for (int j = 0; j < S::A_PW; ++j) {
+        const int row = 8 * (wave + 4 * j) + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        d.ap[j] = (row < t.rows) ? (const char*)g.z + ((int64_t)t.r0 + row) * I * 2 + c * 16
+                                 : nullptr;
+    }
+}
+
+template <typename S>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[S::FMW][S::FN])
+{
+#pragma unroll
+    for (int fm = 0; fm < S::FMW; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < S::FN; ++fn)
+            acc[fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// The DMA kernels are compiled for two waves per SIMD (at most 256 registers
+// a lane) even where the ring's LDS allows one workgroup per CU: with a
+// larger budget the compiler moves the accumulators into AGPRs and copies
+// them back and forth around the loops.
+//
+// Persistent GEMM1 over this workgroup's tiles.  The next tile's A source
+// rows are loaded while the current tile streams; once its ring has drained
+// the next tile's first stages are issued and the current tile's epilogue
+// (bias, SiLU(gate) * up, bf16 z stores straight from the accumulators) runs
+// while they are in flight.
+template <int FMW, int FN, int NS, bool PACKED>
+__global__ void __launch_bounds__(256, 2)
+    k_gemm1_dma(Gemm1Args g)
+{
+    typedef DS<FMW, FN, NS> S;
+    constexpr int FH = FN / 2;
+    __shared__ __attribute__((aligned(16))) char ring[S::RING];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rg = wave >> 1, cg = wave & 1;
+    const int I = g.I, N = 2 * I;
+
+    TileIter<S::CH> it(g.s);
+    TileRef cur;
+    if (!it.next(g.s, cur))
+        return;
+    int srow[S::A_PW];
+    gemm1_rows<S>(g, cur, wave, lane, srow);
+    DmaTile<S, PACKED, true> src;
+    gemm1_src<S, PACKED>(g, cur, srow, src);
+    dma_prologue<S>(src, ring, g.H, wave);
 
     // wave (rg, cg): gate fragments fn < FN/2 at z columns (cg FN/2 + fn) 16,
     // up fragments fn >= FN/2 at the same z columns of the up half
-    constexpr int FH = FN / 2;
     int bblk[FN], bchunk[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
@@ -964,104 +1115,95 @@ __device__ __forceinline__ void gemm1_tile_dma(const Gemm1Args& g, char* ring, i
     }
     DmaFrag<S> fr;
     fr.init(lane, bblk, bchunk);
-
-    f32x4 acc[FMW][FN];
-#pragma unroll
-    for (int fm = 0; fm < FMW; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            acc[fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    // (the mainloop ends with a barrier: the ring becomes the output staging area)
-    dma_run<S>(src, ring, H, wave, rg, fr, acc, min(max(strips - rg * FMW, 0), FMW));
-
-    constexpr int O_STRIDE = BNZ + 4;
-    static_assert(32 * FMW * O_STRIDE * 4 <= S::RING, "z staging fits in the ring");
-    float* Zs = (float*)ring;
     const int g4 = lane >> 4, s16 = lane & 15;
+
+    for (;;) {
+        TileRef nxt;
+        const bool more = it.next(g.s, nxt);
+        if (more)
+            gemm1_rows<S>(g, nxt, wave, lane, srow);
+        const int n0 = cur.ntile * (S::BN / 2);
+        float bg[FH], bu[FH];
 #pragma unroll
-    for (int fn = 0; fn < FH; ++fn) {
-        const int zc = (cg * FH + fn) * 16 + s16;
-        const int n = n0 + zc;
-        float bg = 0.0f, bu = 0.0f;
-        if (g.b13 && n < I) {
-            bg = load_bias(g.b13, g.bias_dt, (int64_t)e * N + n);
-            bu = load_bias(g.b13, g.bias_dt, (int64_t)e * N + I + n);
-        }
-#pragma unroll
-        for (int fm = 0; fm < FMW; ++fm) {
-            const int strip = rg * FMW + fm;
-            if (strip >= strips)
-                continue;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = strip * 16 + g4 * 4 + r;
-                Zs[row * O_STRIDE + zc] = silu_mul(acc[fm][fn][r] + bg, acc[fm][fn + FH][r] + bu);
+        for (int fn = 0; fn < FH; ++fn) {
+            const int n = n0 + (cg * FH + fn) * 16 + s16;
+            bg[fn] = bu[fn] = 0.0f;
+            if (g.b13 && n < I) {
+                bg[fn] = load_bias(g.b13, g.bias_dt, (int64_t)cur.e * N + n);
+                bu[fn] = load_bias(g.b13, g.bias_dt, (int64_t)cur.e * N + I + n);
             }
         }
-    }
-    __syncthreads();
-
-    constexpr int CPR = BNZ / 8;    // 16-byte bf16 chunks per z row
-    const int nrows = strips * 16;
-    for (int q = tid; q < nrows * CPR; q += 256) {
-        const int row = q / CPR, c0 = (q % CPR) * 8;
-        if (n0 + c0 >= I)
-            continue;
-        const int64_t p = (int64_t)r0 + row;
-        const float* sp = Zs + row * O_STRIDE + c0;
-        uint32_t w[4];
+        f32x4 acc[FMW][FN];
+        zero_acc<S>(acc);
+        const int strips = (cur.rows + 15) >> 4;
+        dma_run<S>(src, ring, g.H, wave, rg, fr, acc, min(max(strips - rg * FMW, 0), FMW));
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            w[k] = f32_to_bf16(sp[2 * k]) | ((uint32_t)f32_to_bf16(sp[2 * k + 1]) << 16);
-        *(i32x4*)((u16*)g.z + p * I + n0 + c0) = i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+        for (int fn = 0; fn < FH; ++fn) {
+            pin(bg[fn]);
+            pin(bu[fn]);
+        }
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < S::A_PW; ++j)
+                pin(srow[j]);
+            gemm1_src<S, PACKED>(g, nxt, srow, src);
+            dma_prologue<S>(src, ring, g.H, wave);
+        }
+        // epilogue: bf16 z of the real rows, staged in the ring slot that no
+        // DMA touches before the next tile's first barrier (the prologue
+        // above fills slots 0 .. NS-2), then written as 16-byte row chunks
+        constexpr int ZS = S::BN / 2 + 8;               // staged row, bf16 elements
+        static_assert(S::CH * ZS * 2 <= S::STAGE, "z staging fits in one ring slot");
+        u16* Zs = (u16*)(ring + (S::NS - 1) * S::STAGE);
+#pragma unroll
+        for (int fn = 0; fn < FH; ++fn) {
+            const int zc = (cg * FH + fn) * 16 + s16;
+#pragma unroll
+            for (int fm = 0; fm < FMW; ++fm) {
+                if (rg * FMW + fm >= strips)
+                    continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = (rg * FMW + fm) * 16 + g4 * 4 + r;
+                    Zs[row * ZS + zc] =
+                        f32_to_bf16(silu_mul(acc[fm][fn][r] + bg[fn], acc[fm][fn + FH][r] + bu[fn]));
+                }
+            }
+        }
+        __syncthreads();
+        constexpr int CPR = S::BN / 16;                 // 16-byte chunks per z row
+        for (int q = threadIdx.x; q < cur.rows * CPR; q += 256) {
+            const int row = q / CPR, c8 = (q % CPR) * 8;
+            if (n0 + c8 < I)
+                *(i32x4*)((u16*)g.z + ((int64_t)cur.r0 + row) * I + n0 + c8) =
+                    *(const i32x4*)(Zs + row * ZS + c8);
+        }
+        if (!more)
+            break;
+        cur = nxt;
     }
 }
 
-// GEMM2 tile: BN output columns c0.. of the routed rows.
-template <int FMW, int FN, int NS>
-__device__ __forceinline__ void gemm2_tile_dma(const Gemm2Args& g, char* ring, int e, int r0,
-                                               int rows, int ntile)
+// Persistent GEMM2 over this workgroup's tiles, pipelined across tiles like
+// GEMM1; the epilogue (bias, output rows) runs straight from the accumulators.
+template <int FMW, int FN, int NS, bool PACKED>
+__global__ void __launch_bounds__(256, 2)
+    k_gemm2_dma(Gemm2Args g)
 {
     typedef DS<FMW, FN, NS> S;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    __shared__ __attribute__((aligned(16))) char ring[S::RING];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rg = wave >> 1, cg = wave & 1;
-    const int H = g.H, I = g.I;
-    const int c0 = ntile * S::BN;
-    const int strips = (rows + 15) >> 4;
+    const int H = g.H;
 
-    // z rows are the padded positions; rows past the real ones read the zero page
-    DmaSrc<S> src;
-    const char* zbase = (const char*)g.z;
-#pragma unroll
-    for (int j = 0; j < S::A_PW; ++j) {
-        int row, c;
-        dma_a_slot<S>(j, wave, lane, row, c);
-        src.a[j] = (row < rows) ? zbase + ((int64_t)r0 + row) * I * 2 + c * 16 : nullptr;
-        src.a_k[j] = c * 8;
-    }
-    // weight block bb of the tile: output columns c0 + 128 bb .. +127;
-    // packed, it is block (e, c0 / 128 + bb) of the layout
-    const int64_t nblk = (H + 127) / 128, nks = (I + 63) / 64;
-#pragma unroll
-    for (int j = 0; j < S::B_PW; ++j) {
-        int bb, k, sl, c;
-        dma_b_slot<S>(j, wave, lane, bb, k, sl, c);
-        if (g.w_packed) {
-            const int64_t jb = c0 / 128 + bb;
-            src.b[j] = (jb < nblk) ? (const char*)g.w2 + ((e * nblk + jb) * nks) * PACK_BLOCK +
-                                         k * S::RB + sl * 16
-                                   : nullptr;
-        } else {
-            const int col = c0 + 128 * bb + 8 * c;
-            src.b[j] = (col < H) ? (const char*)g.w2 + (int64_t)e * I * H * 2 + (int64_t)k * H * 2 +
-                                       (int64_t)col * 2
-                                 : nullptr;
-        }
-        src.b_k[j] = k;
-    }
-    src.b_step = g.w_packed ? PACK_BLOCK : (int64_t)64 * H * 2;
+    TileIter<S::CH> it(g.s);
+    TileRef cur;
+    if (!it.next(g.s, cur))
+        return;
+    DmaTile<S, PACKED, false> src;
+    gemm2_src<S, PACKED>(g, cur, wave, src);
+    dma_prologue<S>(src, ring, g.I, wave);
 
     int bblk[FN], bchunk[FN];
 #pragma unroll
@@ -1072,76 +1214,64 @@ __device__ __forceinline__ void gemm2_tile_dma(const Gemm2Args& g, char* ring, i
     }
     DmaFrag<S> fr;
     fr.init(lane, bblk, bchunk);
+    const int g4 = lane >> 4, s16 = lane & 15;
 
-    f32x4 acc[FMW][FN];
+    for (;;) {
+        TileRef nxt;
+        const bool more = it.next(g.s, nxt);
+        const int c0 = cur.ntile * S::BN;
+        const int strips = (cur.rows + 15) >> 4;
+        // output row r0 + row goes to o[r0 + row] (padded position) or, for the
+        // batched slabs, to out[e * T + (r0 - base) + row]
+        const int64_t dst0 = (g.out_mode == 2) ? (int64_t)cur.r0
+                                               : (int64_t)cur.e * g.T + (cur.r0 - cur.base);
+        float bias[FN];
 #pragma unroll
-    for (int fm = 0; fm < FMW; ++fm)
+        for (int fn = 0; fn < FN; ++fn) {
+            const int c = c0 + (cg * FN + fn) * 16 + s16;
+            bias[fn] = (g.b2 && c < H) ? load_bias(g.b2, g.bias_dt, (int64_t)cur.e * H + c) : 0.0f;
+        }
+        f32x4 acc[FMW][FN];
+        zero_acc<S>(acc);
+        dma_run<S>(src, ring, g.I, wave, rg, fr, acc, min(max(strips - rg * FMW, 0), FMW));
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
-            acc[fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    dma_run<S>(src, ring, I, wave, rg, fr, acc, min(max(strips - rg * FMW, 0), FMW));
-
-    // epilogue straight from the accumulators: 16 lanes store 16 consecutive columns of a row
-    const int g4 = lane >> 4, s16 = lane & 15;
-    float bias[FN];
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-        const int c = c0 + (cg * FN + fn) * 16 + s16;
-        bias[fn] = (g.b2 && c < H) ? load_bias(g.b2, g.bias_dt, (int64_t)e * H + c) : 0.0f;
-    }
-#pragma unroll
-    for (int fm = 0; fm < FMW; ++fm) {
-        const int strip = rg * FMW + fm;
-        if (strip >= strips)
-            continue;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = strip * 16 + g4 * 4 + r;
-            if (row >= rows)
-                continue;
-            const int64_t p = (int64_t)r0 + row;
-            const int sid = g.s.sorted[p];
-            if (sid >= g.s.sentinel)
-                continue;
-            const int64_t dst = (g.out_mode == 2) ? p : (int64_t)sid;
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int c = c0 + (cg * FN + fn) * 16 + s16;
-                if (c >= H)
-                    continue;
-                const float v = acc[fm][fn][r] + bias[fn];
-                if (g.out_mode == 1 && g.out_dt == MOE_BF16)
-                    ((u16*)g.out)[dst * H + c] = f32_to_bf16(v);
-                else
-                    ((float*)g.out)[dst * H + c] = v;
-            }
+            pin(bias[fn]);
+        if (more) {
+            gemm2_src<S, PACKED>(g, nxt, wave, src);
+            dma_prologue<S>(src, ring, g.I, wave);
         }
+        // row (strip, g4*4 + r): uniform base of the strip's 16 rows plus this
+        // lane's offset, one strip at a time (keeps the addresses out of registers)
+        const int lane_off = g4 * 4 * H + c0 + cg * FN * 16 + s16;
+#pragma unroll
+        for (int fm = 0; fm < FMW; ++fm) {
+            const int strip = rg * FMW + fm;
+            if (strip >= strips)
+                continue;
+            const int64_t base = (dst0 + strip * 16) * H;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (strip * 16 + g4 * 4 + r >= cur.rows)
+                    continue;
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    if (c0 + (cg * FN + fn) * 16 + s16 >= H)
+                        continue;
+                    const float v = acc[fm][fn][r] + bias[fn];
+                    const int64_t o = base + lane_off + r * H + fn * 16;
+                    if (g.out_mode == 1 && g.out_dt == MOE_BF16)
+                        ((u16*)g.out)[o] = f32_to_bf16(v);
+                    else
+                        ((float*)g.out)[o] = v;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (!more)
+            break;
+        cur = nxt;
     }
-}
-
-template <int FMW, int FN, int NS>
-__global__ void __launch_bounds__(256, (DS<FMW, FN, NS>::RING <= 80 * 1024 ? 2 : 1))
-    k_gemm1_dma(Gemm1Args g)
-{
-    typedef DS<FMW, FN, NS> S;
-    __shared__ __attribute__((aligned(16))) char ring[S::RING];
-    for_each_tile<S::CH>(g.s, [&](int e, int r0, int rows, int ntile) {
-        gemm1_tile_dma<FMW, FN, NS>(g, ring, e, r0, rows, ntile);
-        __syncthreads();   // the next tile's DMAs overwrite the staging area
-    });
-}
-
-template <int FMW, int FN, int NS>
-__global__ void __launch_bounds__(256, (DS<FMW, FN, NS>::RING <= 80 * 1024 ? 2 : 1))
-    k_gemm2_dma(Gemm2Args g)
-{
-    typedef DS<FMW, FN, NS> S;
-    __shared__ __attribute__((aligned(16))) char ring[S::RING];
-    for_each_tile<S::CH>(g.s, [&](int e, int r0, int rows, int ntile) {
-        gemm2_tile_dma<FMW, FN, NS>(g, ring, e, r0, rows, ntile);
-        __syncthreads();   // every wave is done with the ring before the next tile's DMAs
-    });
 }
 
 // ================================================================ weight packing
@@ -1158,10 +1288,10 @@ __global__ void __launch_bounds__(256) k_pack_w13(const u16* __restrict__ w, int
     for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < slots;
          q += (int64_t)gridDim.x * 256) {
         const int sl = (int)(q & 15), k = (int)((q >> 4) & 63);
-        const int64_t b = q >> 10;                      // block (e, j, kt)
-        const int kt = (int)(b % nks);
-        const int j = (int)((b / nks) % nblk);
-        const int64_t e = b / nks / nblk;
+        const int64_t b = q >> 10;                      // block (e, kt, j)
+        const int j = (int)(b % nblk);
+        const int kt = (int)((b / nblk) % nks);
+        const int64_t e = b / nblk / nks;
         const int c = sl ^ swz_b(k);
         const int row = kt * 64 + k, zc = 64 * j + 8 * (c & 7);
         i32x4 v = {0, 0, 0, 0};
@@ -1178,10 +1308,10 @@ __global__ void __launch_bounds__(256) k_pack_w2(const u16* __restrict__ w, int 
     for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < slots;
          q += (int64_t)gridDim.x * 256) {
         const int sl = (int)(q & 15), k = (int)((q >> 4) & 63);
-        const int64_t b = q >> 10;
-        const int kt = (int)(b % nks);
-        const int j = (int)((b / nks) % nblk);
-        const int64_t e = b / nks / nblk;
+        const int64_t b = q >> 10;                      // block (e, kt, j)
+        const int j = (int)(b % nblk);
+        const int kt = (int)((b / nblk) % nks);
+        const int64_t e = b / nblk / nks;
         const int c = sl ^ swz_b(k);
         const int row = kt * 64 + k, col = 128 * j + 8 * c;
         i32x4 v = {0, 0, 0, 0};
@@ -1260,13 +1390,13 @@ static hipError_t run_gemm2(const Gemm2Args& a, const Plan& P, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int FMW, int FN, int NS>
+template <int FMW, int FN, int NS, bool PACKED>
 static hipError_t run_gemm1_dma(const Gemm1Args& a, const Plan& P, hipStream_t s)
 {
     constexpr int BNZ = DS<FMW, FN, NS>::BN / 2;
     Gemm1Args g = a;
     g.s.n_tiles = (a.I + BNZ - 1) / BNZ;
-    auto kern = k_gemm1_dma<FMW, FN, NS>;
+    auto kern = k_gemm1_dma<FMW, FN, NS, PACKED>;
     static int cached = 0;
     const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached)),
         block(256);
@@ -1274,13 +1404,13 @@ static hipError_t run_gemm1_dma(const Gemm1Args& a, const Plan& P, hipStream_t s
     return hipGetLastError();
 }
 
-template <int FMW, int FN, int NS>
+template <int FMW, int FN, int NS, bool PACKED>
 static hipError_t run_gemm2_dma(const Gemm2Args& a, const Plan& P, hipStream_t s)
 {
     constexpr int BN = DS<FMW, FN, NS>::BN;
     Gemm2Args g = a;
     g.s.n_tiles = (a.H + BN - 1) / BN;
-    auto kern = k_gemm2_dma<FMW, FN, NS>;
+    auto kern = k_gemm2_dma<FMW, FN, NS, PACKED>;
     static int cached = 0;
     const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached)),
         block(256);
@@ -1366,7 +1496,8 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s)
         return run_gemm1<MOE_F32, 1, 16>(g, P, s);
     switch (P.cfg) {
     case TILE_PREFILL:
-        return run_gemm1_dma<5, 4, 2>(g, P, s);
+        return P.wpacked ? run_gemm1_dma<5, 4, 2, true>(g, P, s)
+                         : run_gemm1_dma<5, 4, 2, false>(g, P, s);
     case TILE_MID: return run_gemm1<MOE_BF16, 4, 16>(g, P, s);
     default: return run_gemm1<MOE_BF16, 1, 16>(g, P, s);
     }
@@ -1385,8 +1516,9 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
     g.bias_dt = (P.act == MOE_F32) ? MOE_F32 : MOE_BF16;
     g.H = P.H;
     g.I = P.I;
+    g.T = P.T;
     if (P.fmt == MOE_FMT_CONTIGUOUS) {
-        g.out_mode = 0;
+        g.out_mode = 2;
         g.out = P.o;
         g.out_dt = MOE_F32;
     } else if (P.breduce) {
@@ -1408,8 +1540,10 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
         // three K stages in flight; otherwise two workgroups per CU overlap
         // each other's prologues and epilogues
         if (expected_chunks(P) * ((P.H + 127) / 128) <= device_cus() * 5 / 4)
-            return run_gemm2_dma<5, 4, 4>(g, P, s);
-        return run_gemm2_dma<5, 4, 2>(g, P, s);
+            return P.wpacked ? run_gemm2_dma<5, 4, 4, true>(g, P, s)
+                             : run_gemm2_dma<5, 4, 4, false>(g, P, s);
+        return P.wpacked ? run_gemm2_dma<5, 4, 2, true>(g, P, s)
+                         : run_gemm2_dma<5, 4, 2, false>(g, P, s);
     case TILE_MID: return run_gemm2<MOE_BF16, 4, 32>(g, P, s);
     default: return run_gemm2<MOE_BF16, 1, 32>(g, P, s);
     }

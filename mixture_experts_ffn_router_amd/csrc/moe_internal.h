@@ -140,6 +140,7 @@ struct Plan {
     int32_t* npp;
     int32_t* chunk_off;             // [E + 1] GEMM row-chunk prefix per expert
     int32_t* chunk_expert;          // [max_blocks] expert of each chunk
+    int32_t* inv;                   // contiguous: [M*K] padded position of routed item r (-1: none)
     uint8_t* aq;
     float* aq_scale;
     void* z;

@@ -266,7 +266,8 @@ __global__ void __launch_bounds__(1024) k_align(const int32_t* __restrict__ ids,
                                                 int32_t* __restrict__ npp, int sentinel,
                                                 int64_t max_sorted, int max_blocks, int CH,
                                                 int32_t* __restrict__ chunk_off,
-                                                int32_t* __restrict__ chunk_expert)
+                                                int32_t* __restrict__ chunk_expert,
+                                                int32_t* __restrict__ inv)
 {
     extern __shared__ int sh[];
     int* cnt = sh;                               // [ALIGN_WAVES][E]
@@ -344,12 +345,16 @@ __global__ void __launch_bounds__(1024) k_align(const int32_t* __restrict__ ids,
         for (int u = 0; u < ALIGN_UNROLL; ++u) {
             const bool valid = ev[u] >= 0;
             const unsigned long long m = match_mask(ev[u], valid, nbits);
+            const int r = b0 + u * 64 + lane;
             if (valid) {
                 const int rank = __popcll(m & ((1ull << lane) - 1ull));
                 const int base = offs[ev[u]] + cnt[wave * E + ev[u]];
                 const int64_t pos = (int64_t)base + rank;
                 if (pos < max_sorted)
-                    sorted[pos] = b0 + u * 64 + lane;
+                    sorted[pos] = r;
+                inv[r] = (pos < max_sorted) ? (int)pos : -1;
+            } else if (r < end) {
+                inv[r] = -1;                        // expert id out of range: no row
             }
             // every lane has read its base before the leader moves it on
             __builtin_amdgcn_wave_barrier();
@@ -365,7 +370,7 @@ hipError_t launch_align(const Plan& P, const int32_t* ids, hipStream_t s)
     const size_t lds = sizeof(int) * ((size_t)ALIGN_WAVES * P.E + P.E + ALIGN_WAVES);
     hipLaunchKernelGGL(k_align, dim3(1), dim3(1024), lds, s, ids, P.M * P.K, P.E, P.BM, P.counts,
                        P.offsets, P.sorted_ids, P.expert_ids, P.npp, (int)P.sentinel, P.max_sorted,
-                       P.max_blocks, P.CH, P.chunk_off, P.chunk_expert);
+                       P.max_blocks, P.CH, P.chunk_off, P.chunk_expert, P.inv);
     return hipGetLastError();
 }
 
@@ -509,7 +514,9 @@ hipError_t launch_quant_rows(const Plan& P, const void* hidden, hipStream_t s)
 // ============================================================ weight-and-reduce
 // Unpermute + top-k weight-and-reduce (vLLM page, TopKWeightAndReduce;
 // FlagGems moe_sum): y[t] = sum_{j ascending} w[t,j] * o[row(t,j)] in float32,
-// rounded once to the output type.  Contiguous: row = t*top_k + j.  Batched:
+// rounded once to the output type.  o holds each routed item's expert output
+// at its padded position: contiguous, row = inv[t*top_k + j] (the align
+// kernel's inverse permutation; -1 contributes nothing); batched,
 // row = offsets[e] + i for the slab row e*T + i named by token_map.
 // One thread per 4 consecutive columns of one token; no atomics.
 template <typename TOut>
@@ -517,6 +524,7 @@ __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int
                                                 const float* __restrict__ w,
                                                 const int32_t* __restrict__ tmap, int T,
                                                 const int32_t* __restrict__ offsets,
+                                                const int32_t* __restrict__ inv,
                                                 TOut* __restrict__ out)
 {
     const int cpr = H / 4;
@@ -526,10 +534,14 @@ __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int
     const int t = (int)(gid / cpr), c = (int)(gid % cpr) * 4;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int j = 0; j < K; ++j) {
-        int64_t row = (int64_t)t * K + j;
+        int64_t row;
         if (tmap) {
             const int flat = tmap[(int64_t)t * K + j];
             row = (int64_t)offsets[flat / T] + flat % T;
+        } else {
+            row = inv[(int64_t)t * K + j];
+            if (row < 0)
+                continue;
         }
         const float wj = w[(int64_t)t * K + j];
         const f32x4 v = *(const f32x4*)(o + row * H + c);
@@ -556,10 +568,10 @@ hipError_t launch_reduce(const Plan& P, const moe_args& A, const float* topk_w, 
     const dim3 grid((unsigned)((n + 255) / 256)), block(256);
     if (P.outdt == MOE_BF16)
         hipLaunchKernelGGL(k_reduce<u16>, grid, block, 0, s, P.o, P.M, P.H, P.K, w, tmap, P.T,
-                           P.offsets, (u16*)A.out);
+                           P.offsets, P.inv, (u16*)A.out);
     else
         hipLaunchKernelGGL(k_reduce<float>, grid, block, 0, s, P.o, P.M, P.H, P.K, w, tmap, P.T,
-                           P.offsets, (float*)A.out);
+                           P.offsets, P.inv, (float*)A.out);
     return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ def _ref_pack(w, gate_up):
     ncols = N // 2 if gate_up else N          # columns per half (w13) / all (w2)
     bw = 64 if gate_up else 128               # columns of one half-block / block
     nblk, nks = -(-ncols // bw), -(-K // 64)
-    out = np.zeros((E, nblk, nks, 64, 16, 8), dtype=np.uint16)
+    out = np.zeros((E, nks, nblk, 64, 16, 8), dtype=np.uint16)
     for j in range(nblk):
         for kt in range(nks):
             for k in range(64):
@@ -42,7 +42,7 @@ def _ref_pack(w, gate_up):
                         src = bw * j + 8 * c
                         if src >= ncols:
                             continue
-                    out[:, j, kt, k, s, :] = w[:, row, src:src + 8]
+                    out[:, kt, j, k, s, :] = w[:, row, src:src + 8]
     return out.reshape(-1)
 
 
