@@ -720,11 +720,13 @@ __global__ void __launch_bounds__(256) k_gemm2(Gemm2Args g)
 // every load older than the last N has landed in LDS; the compiler's own
 // waits on its loads only ever see a lower count and so stay correct.
 //
-// Tile: CH = 32 * FMW rows x 128 weight columns, one K stage = 64 rows of K.
-// The four waves form a 2 x 2 grid: wave (rg, cg) owns FMW 16-row strips
-// (rows rg * 16 FMW ..) and four 16-column fragments.  Per K stage the LDS
-// reads are CH*128*2 bytes of A plus 2 * 16 KiB of weights, against
-// 4 * CH * 128 + 16 KiB when the four waves share all rows.
+// Tile: CH = 32 * FMW rows x BN = 64 * WC weight columns, one K stage = 64
+// rows of K.  The 2 * WC waves form a 2 x WC grid: wave (rg, cg) owns FMW
+// 16-row strips (rows rg * 16 FMW ..) and four 16-column fragments (64
+// weight columns).  Each A fragment is read from LDS by WC waves and each
+// weight fragment by two.  WC = 2: 128 columns, 4 waves, two workgroups per
+// CU; WC = 4: 256 columns, 8 waves, one workgroup per CU with a deeper ring
+// and half the activation traffic per weight byte.
 //
 // LDS layout of a stage (no padding: a DMA fills 1024 contiguous bytes):
 //   A  [CH rows][128 B]: 16-byte slot s of row r holds K chunk s ^ ((r>>1)&7),
@@ -761,26 +763,34 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int FMW_, int FN_, int NS_>
+template <int FMW_, int WC_, int NS_>
 struct DS {
-    static constexpr int FMW = FMW_, FN = FN_, NS = NS_;
+    static constexpr int FMW = FMW_, WC = WC_, NS = NS_;
+    static constexpr int NW = 2 * WC, NT = 64 * NW;      // waves, threads
+    static constexpr int FN = 4;                         // 16-column fragments per wave
     static constexpr int CH = 32 * FMW;                  // rows per tile
-    static constexpr int BN = 32 * FN;                   // weight columns per tile
-    static constexpr int NB = FN / 4;                    // 128-column weight blocks per tile
+    static constexpr int BN = 64 * WC;                   // weight columns per tile
+    static constexpr int NB = BN / 128;                  // 128-column weight blocks per tile
     static constexpr int RB = 256;                       // bytes per weight row of a block
     static constexpr int A_BYTES = CH * 128, B_BYTES = NB * PACK_BLOCK;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int A_PW = A_BYTES / 1024 / 4, B_PW = B_BYTES / 1024 / 4;   // DMAs per wave
-    static constexpr int D = A_PW + B_PW;
-    static constexpr int RING = NS * STAGE;
+    static constexpr int A_INS = A_BYTES / 1024, B_INS = B_BYTES / 1024;   // 1 KiB DMAs a stage
+    static constexpr int A_PW = (A_INS + NW - 1) / NW;   // A DMA slots per wave
+    static constexpr int B_PW = B_INS / NW;
+    static constexpr int D = A_PW + B_PW;                // DMAs per wave per stage
+    // when NW does not divide A_INS, the spare A slots DMA the zero page into
+    // a scratch KiB past the ring, so every wave issues D DMAs a stage
+    static constexpr bool A_SPARE = A_PW * NW > A_INS;
+    static constexpr int RING = NS * STAGE + (A_SPARE ? 1024 : 0);
+    static_assert(WC == 2 || WC == 4, "2 x 2 or 2 x 4 waves");
+    static_assert(B_INS % NW == 0, "weight DMAs split evenly");
     static_assert(NS >= 2 && NS <= 4, "ring depth");
-    static_assert(FN == 4 || FN == 8, "128 or 256 weight columns (one or two weight blocks)");
     static_assert((NS - 2) * D < 64, "vmcnt range");
 };
 
-// DMA sources of one tile.  Wave w issues the A DMAs i = w + 4j (tile rows
+// DMA sources of one tile.  Wave w issues the A DMAs i = w + NW j (tile rows
 // 8i .. 8i+7; lane l: row 8i + l/8, 16-byte K chunk (l%8) ^ ((row>>1)&7)) and
-// the B DMAs i = w + 4j (weight block i/16, K rows 4(i%16) + l/16, slot l%16).
+// the B DMAs i = w + NW j (weight block i/16, K rows 4(i%16) + l/16, slot l%16).
 // A lane keeps a pointer per A DMA; weight addresses are recomputed per issue
 // from uniform bases.  PACKED: each weight block of a K stage is one
 // contiguous 16 KiB block of the packed layout; plain: the weights are read
@@ -796,22 +806,24 @@ struct DmaTile {
     int K;                      // contraction length
     const char* ap[S::A_PW];    // this lane's A chunk (K stage 0), null: padding row
 
-    __device__ __forceinline__ void issue(int kt, uint32_t lds, int wave, bool live) const
+    // spare: LDS address of the scratch KiB for spare A slots
+    __device__ __forceinline__ void issue(int kt, uint32_t lds, uint32_t spare, int wave,
+                                          bool live) const
     {
         const int lane = threadIdx.x & 63;
         const char* zero = (const char*)g_zero16;
 #pragma unroll
         for (int j = 0; j < S::A_PW; ++j) {
-            const int i = wave + 4 * j;
+            const int i = wave + S::NW * j;
             const int row = 8 * i + (lane >> 3);
             const int c = (lane & 7) ^ ((row >> 1) & 7);
             const bool ok = live && ap[j] && kt * 64 + c * 8 < K;
             const char* p = ok ? ap[j] + kt * 128 : zero;
-            dma16(p, lds + i * 1024);
+            dma16(p, (!S::A_SPARE || i < S::A_INS) ? lds + i * 1024 : spare);
         }
 #pragma unroll
         for (int j = 0; j < S::B_PW; ++j) {
-            const int i = wave + 4 * j;
+            const int i = wave + S::NW * j;
             const int bb = i >> 4, k = 4 * (i & 15) + (lane >> 4);
             const char* p = zero;
             if constexpr (PACKED) {
@@ -839,11 +851,11 @@ struct DmaTile {
     }
 };
 
-// Tile row and K chunk of this lane's j-th A DMA.
+// Tile row and K chunk of this lane's j-th A DMA (row >= CH: a spare slot).
 template <typename S>
 __device__ __forceinline__ void dma_a_slot(int j, int wave, int lane, int& row, int& chunk)
 {
-    const int i = wave + 4 * j;
+    const int i = wave + S::NW * j;
     row = 8 * i + (lane >> 3);
     chunk = (lane & 7) ^ ((row >> 1) & 7);
 }
@@ -865,7 +877,7 @@ __device__ __forceinline__ void dma_prologue(const Src& src, char* ring, int K, 
     const uint32_t ring_lds = lds_u32(ring);
 #pragma unroll
     for (int st = 0; st < S::NS - 1; ++st)
-        src.issue(st, ring_lds + st * S::STAGE, wave, st < nk);
+        src.issue(st, ring_lds + st * S::STAGE, ring_lds + S::NS * S::STAGE, wave, st < nk);
 }
 
 template <typename S, typename Src, typename F>
@@ -882,7 +894,7 @@ __device__ __forceinline__ void dma_mainloop(const Src& src, char* ring, int K, 
         // wave finished before the barrier
         const int nx = kt + S::NS - 1;
         const int nslot = (slot == 0) ? S::NS - 1 : slot - 1;   // nx % NS
-        src.issue(nx, ring_lds + nslot * S::STAGE, wave, nx < nk);
+        src.issue(nx, ring_lds + nslot * S::STAGE, ring_lds + S::NS * S::STAGE, wave, nx < nk);
         compute(ring + slot * S::STAGE);
         slot = (slot == S::NS - 1) ? 0 : slot + 1;
     }
@@ -1021,7 +1033,7 @@ __device__ __forceinline__ void gemm1_src(const Gemm1Args& g, const TileRef& t,
     }
 #pragma unroll
     for (int j = 0; j < S::A_PW; ++j) {
-        const int row = 8 * (wave + 4 * j) + (lane >> 3);
+        const int row = 8 * (wave + S::NW * j) + (lane >> 3);
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         d.ap[j] = (srow[j] >= 0) ? (const char*)g.a + (int64_t)srow[j] * H * 2 + c * 16 : nullptr;
     }
@@ -1055,7 +1067,7 @@ __device__ __forceinline__ void gemm2_src(const Gemm2Args& g, const TileRef& t, 
     }
 #pragma unroll
     for (int j = 0; j < S::A_PW; ++j) {
-        const int row = 8 * (wave + 4 * j) + (lane >> 3);
+        const int row = 8 * (wave + S::NW * j) + (lane >> 3);
         const int c = (lane & 7) ^ ((row >> 1) & 7);
         d.ap[j] = (row < t.rows) ? (const char*)g.z + ((int64_t)t.r0 + row) * I * 2 + c * 16
                                  : nullptr;
@@ -1073,25 +1085,27 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[S::FMW][S::FN])
 }
 
 // The DMA kernels are compiled for two waves per SIMD (at most 256 registers
-// a lane) even where the ring's LDS allows one workgroup per CU: with a
-// larger budget the compiler moves the accumulators into AGPRs and copies
-// them back and forth around the loops.
+// a lane): two 4-wave workgroups or one 8-wave workgroup per CU, or one
+// 4-wave workgroup where the ring's LDS allows no more; with a larger budget
+// the compiler moves the accumulators into AGPRs and copies them back and
+// forth around the loops.
 //
 // Persistent GEMM1 over this workgroup's tiles.  The next tile's A source
 // rows are loaded while the current tile streams; once its ring has drained
 // the next tile's first stages are issued and the current tile's epilogue
 // (bias, SiLU(gate) * up, bf16 z stores straight from the accumulators) runs
 // while they are in flight.
-template <int FMW, int FN, int NS, bool PACKED>
-__global__ void __launch_bounds__(256, 2)
+template <int FMW, int WC, int NS, bool PACKED>
+__global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
     k_gemm1_dma(Gemm1Args g)
 {
-    typedef DS<FMW, FN, NS> S;
+    typedef DS<FMW, WC, NS> S;
+    constexpr int FN = S::FN;
     constexpr int FH = FN / 2;
     __shared__ __attribute__((aligned(16))) char ring[S::RING];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int rg = wave >> 1, cg = wave & 1;
+    const int rg = wave / S::WC, cg = wave % S::WC;
     const int I = g.I, N = 2 * I;
 
     TileIter<S::CH> it(g.s);
@@ -1172,7 +1186,7 @@ __global__ void __launch_bounds__(256, 2)
         }
         __syncthreads();
         constexpr int CPR = S::BN / 16;                 // 16-byte chunks per z row
-        for (int q = threadIdx.x; q < cur.rows * CPR; q += 256) {
+        for (int q = threadIdx.x; q < cur.rows * CPR; q += S::NT) {
             const int row = q / CPR, c8 = (q % CPR) * 8;
             if (n0 + c8 < I)
                 *(i32x4*)((u16*)g.z + ((int64_t)cur.r0 + row) * I + n0 + c8) =
@@ -1186,15 +1200,16 @@ __global__ void __launch_bounds__(256, 2)
 
 // Persistent GEMM2 over this workgroup's tiles, pipelined across tiles like
 // GEMM1; the epilogue (bias, output rows) runs straight from the accumulators.
-template <int FMW, int FN, int NS, bool PACKED>
-__global__ void __launch_bounds__(256, 2)
+template <int FMW, int WC, int NS, bool PACKED>
+__global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
     k_gemm2_dma(Gemm2Args g)
 {
-    typedef DS<FMW, FN, NS> S;
+    typedef DS<FMW, WC, NS> S;
+    constexpr int FN = S::FN;
     __shared__ __attribute__((aligned(16))) char ring[S::RING];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int rg = wave >> 1, cg = wave & 1;
+    const int rg = wave / S::WC, cg = wave % S::WC;
     const int H = g.H;
 
     TileIter<S::CH> it(g.s);
@@ -1345,13 +1360,13 @@ hipError_t launch_pack_weights(int E, int H, int I, const void* w13, const void*
 // the 8 XCDs), capped by the largest possible tile count.  Each kernel
 // instance queries its occupancy once; `cached` is that instance's slot.
 template <typename K>
-static unsigned persistent_grid(K kernel, int64_t max_tiles, int& cached)
+static unsigned persistent_grid(K kernel, int64_t max_tiles, int& cached, int threads = 256)
 {
     if (cached == 0) {
         int dev = 0, cus = 0, occ = 0;
         (void)hipGetDevice(&dev);
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 256, 0);
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0);
         cached = (cus > 0 ? cus : 256) * (occ > 0 ? occ : 1);
     }
     int64_t g = cached;
@@ -1390,30 +1405,31 @@ static hipError_t run_gemm2(const Gemm2Args& a, const Plan& P, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int FMW, int FN, int NS, bool PACKED>
+template <int FMW, int WC, int NS, bool PACKED>
 static hipError_t run_gemm1_dma(const Gemm1Args& a, const Plan& P, hipStream_t s)
 {
-    constexpr int BNZ = DS<FMW, FN, NS>::BN / 2;
+    typedef DS<FMW, WC, NS> S;
+    constexpr int BNZ = S::BN / 2;
     Gemm1Args g = a;
     g.s.n_tiles = (a.I + BNZ - 1) / BNZ;
-    auto kern = k_gemm1_dma<FMW, FN, NS, PACKED>;
+    auto kern = k_gemm1_dma<FMW, WC, NS, PACKED>;
     static int cached = 0;
-    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached)),
-        block(256);
+    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, S::NT)),
+        block(S::NT);
     hipLaunchKernelGGL(kern, grid, block, 0, s, g);
     return hipGetLastError();
 }
 
-template <int FMW, int FN, int NS, bool PACKED>
+template <int FMW, int WC, int NS, bool PACKED>
 static hipError_t run_gemm2_dma(const Gemm2Args& a, const Plan& P, hipStream_t s)
 {
-    constexpr int BN = DS<FMW, FN, NS>::BN;
+    typedef DS<FMW, WC, NS> S;
     Gemm2Args g = a;
-    g.s.n_tiles = (a.H + BN - 1) / BN;
-    auto kern = k_gemm2_dma<FMW, FN, NS, PACKED>;
+    g.s.n_tiles = (a.H + S::BN - 1) / S::BN;
+    auto kern = k_gemm2_dma<FMW, WC, NS, PACKED>;
     static int cached = 0;
-    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached)),
-        block(256);
+    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, S::NT)),
+        block(S::NT);
     hipLaunchKernelGGL(kern, grid, block, 0, s, g);
     return hipGetLastError();
 }
@@ -1426,6 +1442,21 @@ static int64_t expected_chunks(const Plan& P)
     const int64_t active = rows < P.E ? rows : P.E;
     const int64_t fill = (rows + P.CH - 1) / P.CH;
     return active > fill ? active : fill;
+}
+
+static int device_cus();
+
+// Wave columns of the large bf16 GEMM1 tile: 4 (256 columns, 8 waves) when
+// there are a few tiles per CU, else 2.  Tuning override: MOE_GEMM1_WC = 2 | 4,
+// read on every call.
+static int gemm1_wave_cols(const Plan& P)
+{
+    if (const char* env = getenv("MOE_GEMM1_WC")) {
+        const int v = atoi(env);
+        if (v == 2 || v == 4)
+            return v;
+    }
+    return expected_chunks(P) * ((P.I + 127) / 128) <= 8 * device_cus() ? 4 : 2;
 }
 
 static int device_cus()
@@ -1496,8 +1527,15 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s)
         return run_gemm1<MOE_F32, 1, 16>(g, P, s);
     switch (P.cfg) {
     case TILE_PREFILL:
-        return P.wpacked ? run_gemm1_dma<5, 4, 2, true>(g, P, s)
-                         : run_gemm1_dma<5, 4, 2, false>(g, P, s);
+        // a few tiles per CU (few experts, wide I): 256-column tiles, 8 waves and
+        // a 3-stage ring at one workgroup per CU stream the weights fastest;
+        // with many tiles per CU two 4-wave workgroups per CU hide the tile
+        // transitions better
+        if (gemm1_wave_cols(P) == 4)
+            return P.wpacked ? run_gemm1_dma<5, 4, 3, true>(g, P, s)
+                             : run_gemm1_dma<5, 4, 3, false>(g, P, s);
+        return P.wpacked ? run_gemm1_dma<5, 2, 2, true>(g, P, s)
+                         : run_gemm1_dma<5, 2, 2, false>(g, P, s);
     case TILE_MID: return run_gemm1<MOE_BF16, 4, 16>(g, P, s);
     default: return run_gemm1<MOE_BF16, 1, 16>(g, P, s);
     }
@@ -1540,10 +1578,10 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
         // three K stages in flight; otherwise two workgroups per CU overlap
         // each other's prologues and epilogues
         if (expected_chunks(P) * ((P.H + 127) / 128) <= device_cus() * 5 / 4)
-            return P.wpacked ? run_gemm2_dma<5, 4, 4, true>(g, P, s)
-                             : run_gemm2_dma<5, 4, 4, false>(g, P, s);
-        return P.wpacked ? run_gemm2_dma<5, 4, 2, true>(g, P, s)
-                         : run_gemm2_dma<5, 4, 2, false>(g, P, s);
+            return P.wpacked ? run_gemm2_dma<5, 2, 4, true>(g, P, s)
+                             : run_gemm2_dma<5, 2, 4, false>(g, P, s);
+        return P.wpacked ? run_gemm2_dma<5, 2, 2, true>(g, P, s)
+                         : run_gemm2_dma<5, 2, 2, false>(g, P, s);
     case TILE_MID: return run_gemm2<MOE_BF16, 4, 32>(g, P, s);
     default: return run_gemm2<MOE_BF16, 1, 32>(g, P, s);
     }

@@ -73,10 +73,13 @@ SMALL_BF16 = [
 ]
 
 
-@pytest.mark.parametrize("tile_cfg", ["auto", "0", "1", "2"])
+@pytest.mark.parametrize("tile_cfg", ["auto", "0", "0/wc2", "1", "2"])
 @pytest.mark.parametrize("cfg", SMALL_BF16, ids=[c.name for c in SMALL_BF16])
 def test_packed_equals_plain_small(cfg, tile_cfg, monkeypatch):
     dev = GH.device()
+    if tile_cfg == "0/wc2":
+        tile_cfg = "0"
+        monkeypatch.setenv("MOE_GEMM1_WC", "2")
     if tile_cfg != "auto":
         monkeypatch.setenv("MOE_TILE_CFG", tile_cfg)
     inp = W.make_inputs(cfg, 61)

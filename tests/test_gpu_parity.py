@@ -165,13 +165,17 @@ def test_batched_bf16_matches_contiguous():
     GH.compare(cfg, out.float().cpu().numpy(), y, "batched bf16 reduce")
 
 
-@pytest.mark.parametrize("tile_cfg", ["0", "1", "2"])
+@pytest.mark.parametrize("tile_cfg", ["0", "0/wc2", "1", "2"])
 @pytest.mark.parametrize("skew", [False, True])
 def test_tile_families_ragged(tile_cfg, skew, monkeypatch):
     """Every bf16 tile family on K and column tails (H % 64 = 16, I % 64 = 48)
     and, with skew, on experts of 200 rows: several row chunks per expert and
-    a partial last strip."""
+    a partial last strip.  "0/wc2": the 160-row family with the 4-wave,
+    128-column GEMM1 tile instead of the 8-wave one small problems get."""
     dev = GH.device()
+    if tile_cfg == "0/wc2":
+        tile_cfg = "0"
+        monkeypatch.setenv("MOE_GEMM1_WC", "2")
     monkeypatch.setenv("MOE_TILE_CFG", tile_cfg)
     cfg = W.MIXTRAL_PREFILL.scaled(name=f"ragged_t{tile_cfg}", M=200, H=208, I=176, E=4)
     inp = W.make_inputs(cfg, 51)
