@@ -122,12 +122,12 @@ static int choose_tile(const moe_problem* p, int64_t rows_cap)
 
 // Internal workspace regions beyond moe_workspace_info: chunk tables and the
 // position of every routed item in the sorted order.
-enum { INT_CHUNK_OFF = 0, INT_CHUNK_EXPERT = 1, INT_INV = 2, INT_REGIONS = 3 };
+enum { INT_CHUNK_OFF = 0, INT_CHUNK_EXPERT = 1, INT_INV = 2, INT_O2 = 3, INT_REGIONS = 4 };
 
 static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_offs = nullptr,
                   int* cfg_out = nullptr)
 {
-    size_t off_chunk_off = 0, off_chunk_expert = 0, off_inv = 0;
+    size_t off_chunk_off = 0, off_chunk_expert = 0, off_inv = 0, off_o2 = 0;
     const int rc = validate(p);
     if (rc != MOE_OK)
         return rc;
@@ -172,15 +172,22 @@ static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_
     w.off_z_scale = take(fp8 ? (size_t)max_sorted * (p->I / 128) * 4 : 0);
     const int64_t orows = (batched && !p->batched_reduce) ? 0 : max_sorted;
     w.off_o = take((size_t)orows * p->H * 4);
+    const int cfg = choose_tile(p, rows_cap);
+    const bool split = gemm2_k_split(
+        cfg, p->format, p->batched_reduce,
+        expected_chunks(p->format, p->M, p->top_k, p->E, p->max_tokens, tile_rows(cfg)), p->H,
+        p->I, device_cus());
+    off_o2 = take(split ? (size_t)orows * p->H * 4 : 0);
     w.bytes = off;
     *info = w;
     if (chunk_offs) {
         chunk_offs[INT_CHUNK_OFF] = off_chunk_off;
         chunk_offs[INT_CHUNK_EXPERT] = off_chunk_expert;
         chunk_offs[INT_INV] = off_inv;
+        chunk_offs[INT_O2] = split ? off_o2 : 0;
     }
     if (cfg_out)
-        *cfg_out = choose_tile(p, rows_cap);
+        *cfg_out = cfg;
     return MOE_OK;
 }
 
@@ -232,6 +239,8 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
     P.z = ws + w.off_z;
     P.z_scale = (float*)(ws + w.off_z_scale);
     P.o = (float*)(ws + w.off_o);
+    P.g2split = chunk_offs[INT_O2] != 0;
+    P.o2 = P.g2split ? (float*)(ws + chunk_offs[INT_O2]) : nullptr;
     return P;
 }
 

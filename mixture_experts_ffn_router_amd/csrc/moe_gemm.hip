@@ -159,6 +159,8 @@ struct Gemm2Args {
     int out_dt;
     int T;                      // batched: rows per expert slab
     void* out;
+    int ksplit;                 // 2: column block ntile = 2 c + h covers K half h;
+    float* out2;                //    half 1 writes its float partials here, without bias
 };
 
 // ---------------------------------------------------------------- tile schedule
@@ -870,31 +872,31 @@ __device__ __forceinline__ void dma_a_slot(int j, int wave, int lane, int& row, 
 // allocator copy the accumulators between VGPRs and AGPRs).  The loop ends
 // drained, with every wave past its last LDS read, so the next tile's
 // prologue may refill the ring at once.
+// The stages run over [kb, ke) (K / 64 rounded up; a K-split half covers part).
 template <typename S, typename Src>
-__device__ __forceinline__ void dma_prologue(const Src& src, char* ring, int K, int wave)
+__device__ __forceinline__ void dma_prologue(const Src& src, char* ring, int kb, int ke, int wave)
 {
-    const int nk = (K + 63) / 64;
     const uint32_t ring_lds = lds_u32(ring);
 #pragma unroll
     for (int st = 0; st < S::NS - 1; ++st)
-        src.issue(st, ring_lds + st * S::STAGE, ring_lds + S::NS * S::STAGE, wave, st < nk);
+        src.issue(kb + st, ring_lds + st * S::STAGE, ring_lds + S::NS * S::STAGE, wave,
+                  kb + st < ke);
 }
 
 template <typename S, typename Src, typename F>
-__device__ __forceinline__ void dma_mainloop(const Src& src, char* ring, int K, int wave,
+__device__ __forceinline__ void dma_mainloop(const Src& src, char* ring, int kb, int ke, int wave,
                                              F&& compute)
 {
-    const int nk = (K + 63) / 64;
     const uint32_t ring_lds = lds_u32(ring);
-    int slot = 0;                                   // kt % NS
-    for (int kt = 0; kt < nk; ++kt) {
+    int slot = 0;                                   // (kt - kb) % NS
+    for (int kt = kb; kt < ke; ++kt) {
         wait_vmcnt<(S::NS - 2) * S::D>();
         __syncthreads();
         // the slot refilled here was last read in iteration kt - 1, which every
         // wave finished before the barrier
         const int nx = kt + S::NS - 1;
-        const int nslot = (slot == 0) ? S::NS - 1 : slot - 1;   // nx % NS
-        src.issue(nx, ring_lds + nslot * S::STAGE, ring_lds + S::NS * S::STAGE, wave, nx < nk);
+        const int nslot = (slot == 0) ? S::NS - 1 : slot - 1;   // (nx - kb) % NS
+        src.issue(nx, ring_lds + nslot * S::STAGE, ring_lds + S::NS * S::STAGE, wave, nx < ke);
         compute(ring + slot * S::STAGE);
         slot = (slot == S::NS - 1) ? 0 : slot + 1;
     }
@@ -958,18 +960,19 @@ struct DmaFrag {
 // uniform): one instantiation per count, so the loop body stays branch free;
 // every wave still issues its DMAs and meets every barrier.
 template <typename S, int NM = S::FMW, typename Src>
-__device__ __forceinline__ void dma_run(const Src& src, char* ring, int K, int wave, int rg,
-                                        const DmaFrag<S>& fr, f32x4 (&acc)[S::FMW][S::FN], int live)
+__device__ __forceinline__ void dma_run(const Src& src, char* ring, int kb, int ke, int wave,
+                                        int rg, const DmaFrag<S>& fr,
+                                        f32x4 (&acc)[S::FMW][S::FN], int live)
 {
     if constexpr (NM == 0) {
-        dma_mainloop<S>(src, ring, K, wave, [](const char*) {});
+        dma_mainloop<S>(src, ring, kb, ke, wave, [](const char*) {});
     } else {
         if (live >= NM) {
-            dma_mainloop<S>(src, ring, K, wave,
+            dma_mainloop<S>(src, ring, kb, ke, wave,
                             [&](const char* st) { fr.template stage<NM>(st, rg, acc); });
             return;
         }
-        dma_run<S, NM - 1>(src, ring, K, wave, rg, fr, acc, live);
+        dma_run<S, NM - 1>(src, ring, kb, ke, wave, rg, fr, acc, live);
     }
 }
 
@@ -1115,8 +1118,9 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
     int srow[S::A_PW];
     gemm1_rows<S>(g, cur, wave, lane, srow);
     DmaTile<S, PACKED, true> src;
+    const int nk1 = (g.H + 63) / 64;
     gemm1_src<S, PACKED>(g, cur, srow, src);
-    dma_prologue<S>(src, ring, g.H, wave);
+    dma_prologue<S>(src, ring, 0, nk1, wave);
 
     // wave (rg, cg): gate fragments fn < FN/2 at z columns (cg FN/2 + fn) 16,
     // up fragments fn >= FN/2 at the same z columns of the up half
@@ -1150,7 +1154,7 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
         f32x4 acc[FMW][FN];
         zero_acc<S>(acc);
         const int strips = (cur.rows + 15) >> 4;
-        dma_run<S>(src, ring, g.H, wave, rg, fr, acc, min(max(strips - rg * FMW, 0), FMW));
+        dma_run<S>(src, ring, 0, nk1, wave, rg, fr, acc, min(max(strips - rg * FMW, 0), FMW));
 #pragma unroll
         for (int fn = 0; fn < FH; ++fn) {
             pin(bg[fn]);
@@ -1161,7 +1165,7 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
             for (int j = 0; j < S::A_PW; ++j)
                 pin(srow[j]);
             gemm1_src<S, PACKED>(g, nxt, srow, src);
-            dma_prologue<S>(src, ring, g.H, wave);
+            dma_prologue<S>(src, ring, 0, nk1, wave);
         }
         // epilogue: bf16 z of the real rows, staged in the ring slot that no
         // DMA touches before the next tile's first barrier (the prologue
@@ -1212,13 +1216,26 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
     const int rg = wave / S::WC, cg = wave % S::WC;
     const int H = g.H;
 
+    // with a K split, logical column block ntile = 2 c + h is block c over the
+    // K half h; unit() splits it
+    const int nk2 = (g.I + 63) / 64, kmid = nk2 / 2;
+    auto unit = [&](TileRef t, int& kb, int& ke, int& part) {
+        part = (g.ksplit == 2) ? (t.ntile & 1) : 0;
+        if (g.ksplit == 2)
+            t.ntile >>= 1;
+        kb = (g.ksplit == 2 && part) ? kmid : 0;
+        ke = (g.ksplit == 2 && !part) ? kmid : nk2;
+        return t;
+    };
     TileIter<S::CH> it(g.s);
     TileRef cur;
     if (!it.next(g.s, cur))
         return;
+    int kb, ke, part;
+    cur = unit(cur, kb, ke, part);
     DmaTile<S, PACKED, false> src;
     gemm2_src<S, PACKED>(g, cur, wave, src);
-    dma_prologue<S>(src, ring, g.I, wave);
+    dma_prologue<S>(src, ring, kb, ke, wave);
 
     int bblk[FN], bchunk[FN];
 #pragma unroll
@@ -1234,27 +1251,33 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
     for (;;) {
         TileRef nxt;
         const bool more = it.next(g.s, nxt);
+        int nkb = 0, nke = 0, npart = 0;
+        if (more)
+            nxt = unit(nxt, nkb, nke, npart);
         const int c0 = cur.ntile * S::BN;
         const int strips = (cur.rows + 15) >> 4;
         // output row r0 + row goes to o[r0 + row] (padded position) or, for the
         // batched slabs, to out[e * T + (r0 - base) + row]
         const int64_t dst0 = (g.out_mode == 2) ? (int64_t)cur.r0
                                                : (int64_t)cur.e * g.T + (cur.r0 - cur.base);
-        float bias[FN];
+        float bias[FN];   // the bias belongs to the first K half only
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int c = c0 + (cg * FN + fn) * 16 + s16;
-            bias[fn] = (g.b2 && c < H) ? load_bias(g.b2, g.bias_dt, (int64_t)cur.e * H + c) : 0.0f;
+            bias[fn] = (g.b2 && c < H && part == 0)
+                           ? load_bias(g.b2, g.bias_dt, (int64_t)cur.e * H + c)
+                           : 0.0f;
         }
         f32x4 acc[FMW][FN];
         zero_acc<S>(acc);
-        dma_run<S>(src, ring, g.I, wave, rg, fr, acc, min(max(strips - rg * FMW, 0), FMW));
+        dma_run<S>(src, ring, kb, ke, wave, rg, fr, acc, min(max(strips - rg * FMW, 0), FMW));
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
             pin(bias[fn]);
+        float* const outf = part ? g.out2 : (float*)g.out;
         if (more) {
             gemm2_src<S, PACKED>(g, nxt, wave, src);
-            dma_prologue<S>(src, ring, g.I, wave);
+            dma_prologue<S>(src, ring, nkb, nke, wave);
         }
         // row (strip, g4*4 + r): uniform base of the strip's 16 rows plus this
         // lane's offset, one strip at a time (keeps the addresses out of registers)
@@ -1278,7 +1301,7 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
                     if (g.out_mode == 1 && g.out_dt == MOE_BF16)
                         ((u16*)g.out)[o] = f32_to_bf16(v);
                     else
-                        ((float*)g.out)[o] = v;
+                        outf[o] = v;
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -1286,6 +1309,9 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
         if (!more)
             break;
         cur = nxt;
+        kb = nkb;
+        ke = nke;
+        part = npart;
     }
 }
 
@@ -1425,7 +1451,7 @@ static hipError_t run_gemm2_dma(const Gemm2Args& a, const Plan& P, hipStream_t s
 {
     typedef DS<FMW, WC, NS> S;
     Gemm2Args g = a;
-    g.s.n_tiles = (a.H + S::BN - 1) / S::BN;
+    g.s.n_tiles = (a.H + S::BN - 1) / S::BN * g.ksplit;
     auto kern = k_gemm2_dma<FMW, WC, NS, PACKED>;
     static int cached = 0;
     const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, S::NT)),
@@ -1438,13 +1464,8 @@ static hipError_t run_gemm2_dma(const Gemm2Args& a, const Plan& P, hipStream_t s
 // and the routed rows fill at least rows / CH of them.
 static int64_t expected_chunks(const Plan& P)
 {
-    const int64_t rows = (P.fmt == MOE_FMT_BATCHED) ? (int64_t)P.E * P.T : (int64_t)P.M * P.K;
-    const int64_t active = rows < P.E ? rows : P.E;
-    const int64_t fill = (rows + P.CH - 1) / P.CH;
-    return active > fill ? active : fill;
+    return expected_chunks(P.fmt, P.M, P.K, P.E, P.T, P.CH);
 }
-
-static int device_cus();
 
 // Wave columns of the large bf16 GEMM1 tile: 4 (256 columns, 8 waves) when
 // there are a few tiles per CU, else 2.  Tuning override: MOE_GEMM1_WC = 2 | 4,
@@ -1459,15 +1480,14 @@ static int gemm1_wave_cols(const Plan& P)
     return expected_chunks(P) * ((P.I + 127) / 128) <= 8 * device_cus() ? 4 : 2;
 }
 
-static int device_cus()
+int device_cus()
 {
     static int cus = 0;
     if (cus == 0) {
-        int dev = 0;
+        int dev = 0, n = 0;
         (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (cus <= 0)
-            cus = 256;
+        (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        cus = n > 0 ? n : 256;
     }
     return cus;
 }
@@ -1555,6 +1575,8 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
     g.H = P.H;
     g.I = P.I;
     g.T = P.T;
+    g.ksplit = 1;
+    g.out2 = P.o2;
     if (P.fmt == MOE_FMT_CONTIGUOUS) {
         g.out_mode = 2;
         g.out = P.o;
@@ -1574,6 +1596,11 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
         return run_gemm2<MOE_F32, 1, 16>(g, P, s);
     switch (P.cfg) {
     case TILE_PREFILL:
+        if (P.g2split) {   // 256-column tiles over two K halves
+            g.ksplit = 2;
+            return P.wpacked ? run_gemm2_dma<5, 4, 3, true>(g, P, s)
+                             : run_gemm2_dma<5, 4, 3, false>(g, P, s);
+        }
         // about one tile per CU: one workgroup per CU with a 4-stage ring keeps
         // three K stages in flight; otherwise two workgroups per CU overlap
         // each other's prologues and epilogues

@@ -146,7 +146,33 @@ struct Plan {
     void* z;
     float* z_scale;
     float* o;
+    float* o2;                      // GEMM2 split in K: the second half's partial outputs
+    int g2split;                    // GEMM2 runs as two K halves (o + o2)
 };
+
+// Host-side helpers shared by the workspace layout and the GEMM launchers.
+// Expected number of GEMM row chunks: every active expert has at least one,
+// and the routed rows fill at least rows / CH of them.
+inline int64_t expected_chunks(int fmt, int64_t M, int K, int E, int T, int CH)
+{
+    const int64_t rows = (fmt == MOE_FMT_BATCHED) ? (int64_t)E * T : M * K;
+    const int64_t active = rows < E ? rows : E;
+    const int64_t fill = (rows + CH - 1) / CH;
+    return active > fill ? active : fill;
+}
+
+// Compute units of the current device (cached after the first query).
+int device_cus();
+
+// GEMM2 of the 160-row bf16 family runs with 256-column tiles split in two K
+// halves when whole tiles would not cover the CUs and K is long: the halves
+// write separate float partials that the reduce kernel adds.
+inline bool gemm2_k_split(int cfg, int fmt, int breduce, int64_t chunks, int H, int I, int cus)
+{
+    if (cfg != TILE_PREFILL || (fmt == MOE_FMT_BATCHED && !breduce))
+        return false;
+    return chunks * ((H + 255) / 256) < cus && I >= 1024;
+}
 
 // launchers (each returns hipGetLastError() of its launch)
 hipError_t launch_router(const Plan& P, const void* logits, hipStream_t s);

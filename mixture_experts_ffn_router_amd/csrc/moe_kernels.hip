@@ -517,14 +517,16 @@ hipError_t launch_quant_rows(const Plan& P, const void* hidden, hipStream_t s)
 // rounded once to the output type.  o holds each routed item's expert output
 // at its padded position: contiguous, row = inv[t*top_k + j] (the align
 // kernel's inverse permutation; -1 contributes nothing); batched,
-// row = offsets[e] + i for the slab row e*T + i named by token_map.
-// One thread per 4 consecutive columns of one token; no atomics.
+// row = offsets[e] + i for the slab row e*T + i named by token_map.  When
+// GEMM2 ran as two K halves, an item's output is o[row] + o2[row] (that
+// order).  One thread per 4 consecutive columns of one token; no atomics.
 template <typename TOut>
 __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int M, int H, int K,
                                                 const float* __restrict__ w,
                                                 const int32_t* __restrict__ tmap, int T,
                                                 const int32_t* __restrict__ offsets,
                                                 const int32_t* __restrict__ inv,
+                                                const float* __restrict__ o2,
                                                 TOut* __restrict__ out)
 {
     const int cpr = H / 4;
@@ -544,7 +546,11 @@ __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int
                 continue;
         }
         const float wj = w[(int64_t)t * K + j];
-        const f32x4 v = *(const f32x4*)(o + row * H + c);
+        f32x4 v = *(const f32x4*)(o + row * H + c);
+        if (o2) {
+            const f32x4 v2 = *(const f32x4*)(o2 + row * H + c);
+            v = f32x4{v[0] + v2[0], v[1] + v2[1], v[2] + v2[2], v[3] + v2[3]};
+        }
         acc[0] += wj * v[0];
         acc[1] += wj * v[1];
         acc[2] += wj * v[2];
@@ -568,10 +574,10 @@ hipError_t launch_reduce(const Plan& P, const moe_args& A, const float* topk_w, 
     const dim3 grid((unsigned)((n + 255) / 256)), block(256);
     if (P.outdt == MOE_BF16)
         hipLaunchKernelGGL(k_reduce<u16>, grid, block, 0, s, P.o, P.M, P.H, P.K, w, tmap, P.T,
-                           P.offsets, P.inv, (u16*)A.out);
+                           P.offsets, P.inv, P.o2, (u16*)A.out);
     else
         hipLaunchKernelGGL(k_reduce<float>, grid, block, 0, s, P.o, P.M, P.H, P.K, w, tmap, P.T,
-                           P.offsets, P.inv, (float*)A.out);
+                           P.offsets, P.inv, P.o2, (float*)A.out);
     return hipGetLastError();
 }
 

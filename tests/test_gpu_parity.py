@@ -192,3 +192,18 @@ def test_tile_families_ragged(tile_cfg, skew, monkeypatch):
         GH.check_output(inp, out, ids_o, w_o, what="ragged")
     out16, _, _ = GH.run_contiguous(inp, dev, precomputed=(ids, w) if skew else None)
     GH.check_rounded(out16, out)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm2_k_split(packed, monkeypatch):
+    """The 160-row family on a problem whose GEMM2 runs as two K halves
+    (I >= 1024, few tiles): I = 1040 also leaves a K tail in the second half,
+    and biases check that b2 enters once."""
+    dev = GH.device()
+    monkeypatch.setenv("MOE_TILE_CFG", "0")
+    cfg = W.MIXTRAL_PREFILL.scaled(name="k_split", M=96, H=256, I=1040, E=4, bias=True)
+    inp = W.make_inputs(cfg, 71)
+    print(f"[case] gemm2 k split packed={packed}", flush=True)
+    out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, packed=packed)
+    ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    GH.check_output(inp, out, ids_o, w_o, what="k split")
