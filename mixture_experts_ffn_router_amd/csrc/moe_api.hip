@@ -106,15 +106,17 @@ static int choose_tile(const moe_problem* p, int64_t rows_cap)
         return TILE_FP8;
     if (p->w_dtype == MOE_F32)
         return TILE_DECODE;
-    // tuning override: MOE_TILE_CFG = 0 (prefill) | 1 (mid) | 2 (decode), read on every call
+    // tuning override: MOE_TILE_CFG = 0 (prefill) | 1 (mid) | 2 (decode) | 4 (decode, DMA)
+    // | 5 (mid, DMA), read on every call
     if (const char* env = std::getenv("MOE_TILE_CFG")) {
         const int v = std::atoi(env);
-        if (v == TILE_PREFILL || v == TILE_MID || v == TILE_DECODE)
+        if (v == TILE_PREFILL || v == TILE_MID || v == TILE_DECODE || v == TILE_DECODE_DMA ||
+            v == TILE_MID_DMA)
             return v;
     }
     const double avg = (double)rows_cap / p->E;
     if (avg <= 12)
-        return TILE_DECODE;
+        return TILE_DECODE_DMA;
     if (avg <= 48)
         return TILE_MID;
     return TILE_PREFILL;
@@ -332,12 +334,13 @@ static int forward(const moe_problem* p, const moe_args* a, void* workspace,
         if (p->routing == MOE_ROUTE_PRECOMPUTED) {
             ids = a->topk_ids;
             weights = a->topk_weights;
+            MOE_TRY(MOE_STAGE_ALIGN, launch_align(P, ids, s));
         } else {
             MOE_TRY(MOE_STAGE_ROUTER, launch_router(P, a->router_logits, s));
             ids = P.topk_ids;
             weights = P.topk_w;
+            MOE_TRY(MOE_STAGE_ALIGN, launch_align(P, ids, s));
         }
-        MOE_TRY(MOE_STAGE_ALIGN, launch_align(P, ids, s));
     } else {
         MOE_TRY(MOE_STAGE_ALIGN, launch_tilelist(P, a->expert_num_tokens, s));
     }

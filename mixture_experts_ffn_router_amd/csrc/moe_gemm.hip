@@ -1557,6 +1557,12 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s)
         return P.wpacked ? run_gemm1_dma<5, 2, 2, true>(g, P, s)
                          : run_gemm1_dma<5, 2, 2, false>(g, P, s);
     case TILE_MID: return run_gemm1<MOE_BF16, 4, 16>(g, P, s);
+    case TILE_DECODE_DMA:
+        return P.wpacked ? run_gemm1_dma<1, 2, 4, true>(g, P, s)
+                         : run_gemm1_dma<1, 2, 4, false>(g, P, s);
+    case TILE_MID_DMA:
+        return P.wpacked ? run_gemm1_dma<2, 2, 3, true>(g, P, s)
+                         : run_gemm1_dma<2, 2, 3, false>(g, P, s);
     default: return run_gemm1<MOE_BF16, 1, 16>(g, P, s);
     }
 }
@@ -1610,6 +1616,12 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
         return P.wpacked ? run_gemm2_dma<5, 2, 2, true>(g, P, s)
                          : run_gemm2_dma<5, 2, 2, false>(g, P, s);
     case TILE_MID: return run_gemm2<MOE_BF16, 4, 32>(g, P, s);
+    case TILE_DECODE_DMA:
+        return P.wpacked ? run_gemm2_dma<1, 2, 4, true>(g, P, s)
+                         : run_gemm2_dma<1, 2, 4, false>(g, P, s);
+    case TILE_MID_DMA:
+        return P.wpacked ? run_gemm2_dma<2, 2, 3, true>(g, P, s)
+                         : run_gemm2_dma<2, 2, 3, false>(g, P, s);
     default: return run_gemm2<MOE_BF16, 1, 32>(g, P, s);
     }
 }

@@ -108,11 +108,25 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 
 // ------------------------------------------------------------------ execution plan
 // GEMM tile families; each fixes the rows per tile (chunk height).
-enum { TILE_PREFILL = 0, TILE_MID = 1, TILE_DECODE = 2, TILE_FP8 = 3 };
+enum {
+    TILE_PREFILL = 0,      // LDS-DMA ring, 160 rows
+    TILE_MID = 1,          // register-staged, 64 rows
+    TILE_DECODE = 2,       // register-staged, 16 rows
+    TILE_FP8 = 3,          // fp8 register-staged, 128 rows
+    TILE_DECODE_DMA = 4,   // LDS-DMA ring, 32 rows
+    TILE_MID_DMA = 5       // LDS-DMA ring, 64 rows
+};
 constexpr int ALIGN_BM = 16;                 // expert runs are padded to 16 rows
 inline int tile_rows(int cfg)
 {
-    return cfg == TILE_PREFILL ? 160 : cfg == TILE_MID ? 64 : cfg == TILE_FP8 ? 128 : 16;
+    switch (cfg) {
+    case TILE_PREFILL: return 160;
+    case TILE_MID: return 64;
+    case TILE_FP8: return 128;
+    case TILE_DECODE_DMA: return 32;
+    case TILE_MID_DMA: return 64;
+    default: return 16;
+    }
 }
 
 // Host-computed description of one call: problem, tile choice, device pointers.

@@ -16,7 +16,10 @@ namespace moe {
 // and it is formed as float32(score_a) + float32(score_b) with each score
 // evaluated in double and rounded once.
 //
-// One wavefront per token; lane l holds experts [l*EPL, (l+1)*EPL).
+// A token is routed by a group of LPT lanes of one wave (LPT = 64, or the
+// power of two >= E when E is small, so that several tokens share a wave);
+// lane `sub` of the group holds experts [sub*EPL, (sub+1)*EPL).  Grouped
+// selection always uses whole waves (LPT = 64).
 
 // Orders float bit patterns as unsigned integers (monotone for non-NaN).
 __device__ __forceinline__ uint32_t ord_f32(float f)
@@ -25,47 +28,122 @@ __device__ __forceinline__ uint32_t ord_f32(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int EPL>
-__global__ void __launch_bounds__(256) k_router(const void* __restrict__ logits, int lgdt, int M,
-                                                int E, int K, int scoring, int renorm, int G,
-                                                int kg, int gmode, float rsf,
-                                                int32_t* __restrict__ topk_ids,
-                                                float* __restrict__ topk_w)
+// Reductions over aligned groups of LPT lanes; every lane of a group gets
+// the same result.  Inside a row of 16 lanes the partners are reached with
+// DPP (lane i reads lane i^1, i^2 (quad_perm), 7-i within its 8, 15-i within
+// its 16), which costs a few cycles where a shuffle through the LDS crossbar
+// costs about a hundred; rows are then combined from v_readlane values.
+// Each step combines a lane's value with its partner's and the partner
+// combines the same two values, so with a commutative op every lane of the
+// group ends with identical bits.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_MIRROR8 = 0x141, DPP_MIRROR16 = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
 {
-    __shared__ float sh_logit[4][EPL * 64];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + wave;
-    if (t >= M)
-        return;
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
 
-    float s[EPL];
-    bool valid[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-        const int e = lane * EPL + i;
-        valid[i] = e < E;
-        float v = -INFINITY;
-        if (valid[i])
-            v = (lgdt == MOE_BF16) ? bf16_to_f32(((const u16*)logits)[(int64_t)t * E + e])
-                                   : ((const float*)logits)[(int64_t)t * E + e];
-        s[i] = v;
+// (key, value) pair: the largest key wins and carries its value along
+struct KeyVal {
+    uint32_t hi, lo;
+    float val;
+};
+
+__device__ __forceinline__ KeyVal kv_max(const KeyVal& a, const KeyVal& b)
+{
+    const bool take = b.hi > a.hi || (b.hi == a.hi && b.lo > a.lo);
+    return take ? b : a;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float xchg(float v)
+{
+    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ KeyVal xchg(const KeyVal& v)
+{
+    return KeyVal{dpp_u32<CTRL>(v.hi), dpp_u32<CTRL>(v.lo), xchg<CTRL>(v.val)};
+}
+__device__ __forceinline__ float rdlane(float v, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ KeyVal rdlane(const KeyVal& v, int l)
+{
+    return KeyVal{(uint32_t)__builtin_amdgcn_readlane((int)v.hi, l),
+                  (uint32_t)__builtin_amdgcn_readlane((int)v.lo, l), rdlane(v.val, l)};
+}
+
+template <int LPT, typename T, typename Op>
+__device__ __forceinline__ T grp_reduce(T v, Op op)
+{
+    static_assert(LPT == 8 || LPT == 16 || LPT == 32 || LPT == 64, "group width");
+    v = op(v, xchg<DPP_XOR1>(v));
+    v = op(v, xchg<DPP_XOR2>(v));
+    v = op(v, xchg<DPP_MIRROR8>(v));
+    if constexpr (LPT >= 16)
+        v = op(v, xchg<DPP_MIRROR16>(v));
+    if constexpr (LPT == 32) {
+        const T a = op(rdlane(v, 0), rdlane(v, 16)), b = op(rdlane(v, 32), rdlane(v, 48));
+        v = (threadIdx.x & 32) ? b : a;
+    } else if constexpr (LPT == 64) {
+        v = op(op(rdlane(v, 0), rdlane(v, 16)), op(rdlane(v, 32), rdlane(v, 48)));
     }
+    return v;
+}
 
+template <int LPT>
+__device__ __forceinline__ float grp_max(float v)
+{
+    return grp_reduce<LPT>(v, [](float a, float b) { return fmaxf(a, b); });
+}
+
+template <int LPT>
+__device__ __forceinline__ float grp_sum(float v)
+{
+    return grp_reduce<LPT>(v, [](float a, float b) { return a + b; });
+}
+
+template <int LPT>
+__device__ __forceinline__ KeyVal grp_max_kv(const KeyVal& v)
+{
+    return grp_reduce<LPT>(v, kv_max);
+}
+
+struct RouteArgs {
+    int E, K, scoring, renorm, G, kg, gmode;
+    float rsf;
+};
+
+// Routes one token.  s: this lane's EPL logits (-inf past E).  grow: the
+// token's E logits as floats in LDS (read by the grouped selection only).
+// Lanes sub < K return pick `sub` (expert id, final weight).
+template <int EPL, int LPT>
+__device__ __forceinline__ void route_token(const RouteArgs& R, const float (&s)[EPL], int sub,
+                                            const float* grow, int& id_out, float& w_out)
+{
+    const int lane = threadIdx.x & 63;
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
         mx = fmaxf(mx, s[i]);
-    mx = wave_max(mx);
+    mx = grp_max<LPT>(mx);
 
     float p[EPL];
-    if (scoring == MOE_ROUTE_SOFTMAX) {
+    bool cand[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+        cand[i] = sub * EPL + i < R.E;
+    if (R.scoring == MOE_ROUTE_SOFTMAX) {
         float sum = 0.0f;
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
-            p[i] = valid[i] ? expf(s[i] - mx) : 0.0f;
+            p[i] = cand[i] ? expf(s[i] - mx) : 0.0f;
             sum += p[i];
         }
-        sum = wave_sum(sum);
+        sum = grp_sum<LPT>(sum);
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
             p[i] = p[i] / sum;
@@ -75,117 +153,157 @@ __global__ void __launch_bounds__(256) k_router(const void* __restrict__ logits,
             p[i] = 1.0f / (1.0f + expf(-s[i]));
     }
 
-    bool cand[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-        cand[i] = valid[i];
-
-    if (G > 1) {
-        const int per = E / G;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            if (valid[i])
-                sh_logit[wave][lane * EPL + i] = s[i];
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        // lane g < G forms the key of group g
-        unsigned long long gkey = 0;
-        if (lane < G) {
-            const float* sg = &sh_logit[wave][lane * per];
-            float a = -INFINITY, b = -INFINITY;
-            for (int i = 0; i < per; ++i) {
-                const float v = sg[i];
-                if (v > a) {
-                    b = a;
-                    a = v;
-                } else if (v > b) {
-                    b = v;
+    if constexpr (LPT == 64) {
+        if (R.G > 1) {
+            const int per = R.E / R.G;
+            // lane g < G forms the key of group g
+            KeyVal gkey{0u, 0u, 0.0f};
+            if (lane < R.G) {
+                const float* sg = grow + lane * per;
+                float a = -INFINITY, b = -INFINITY;
+                for (int i = 0; i < per; ++i) {
+                    const float v = sg[i];
+                    if (v > a) {
+                        b = a;
+                        a = v;
+                    } else if (v > b) {
+                        b = v;
+                    }
                 }
+                float key;
+                if (R.gmode == 0) {
+                    key = a;
+                } else if (R.scoring == MOE_ROUTE_SIGMOID) {
+                    key = (float)(1.0 / (1.0 + exp(-(double)a))) +
+                          (float)(1.0 / (1.0 + exp(-(double)b)));
+                } else {
+                    key = (float)exp((double)a - (double)mx) + (float)exp((double)b - (double)mx);
+                }
+                gkey = KeyVal{ord_f32(key), 0xffffffffu - lane, 0.0f};
             }
-            float key;
-            if (gmode == 0) {
-                key = a;
-            } else if (scoring == MOE_ROUTE_SIGMOID) {
-                key = (float)(1.0 / (1.0 + exp(-(double)a))) + (float)(1.0 / (1.0 + exp(-(double)b)));
-            } else {
-                key = (float)exp((double)a - (double)mx) + (float)exp((double)b - (double)mx);
+            unsigned long long chosen = 0;
+            for (int r = 0; r < R.kg; ++r) {
+                const KeyVal best = grp_max_kv<64>(gkey);
+                const int g = (int)(0xffffffffu - best.lo);
+                chosen |= 1ull << g;
+                if (lane == g)
+                    gkey = KeyVal{0u, 0u, 0.0f};
             }
-            gkey = ((unsigned long long)ord_f32(key) << 32) | (uint32_t)(0xffffffffu - lane);
-        }
-        unsigned long long chosen = 0;
-        for (int r = 0; r < kg; ++r) {
-            const unsigned long long best = wave_max_u64(gkey);
-            const int g = (int)(0xffffffffu - (uint32_t)best);
-            chosen |= 1ull << g;
-            if (lane == g)
-                gkey = 0;
-        }
 #pragma unroll
-        for (int i = 0; i < EPL; ++i)
-            cand[i] = valid[i] && ((chosen >> ((lane * EPL + i) / per)) & 1ull);
+            for (int i = 0; i < EPL; ++i)
+                cand[i] = cand[i] && ((chosen >> ((sub * EPL + i) / per)) & 1ull);
+        }
     }
 
-    // top-k by (logit desc, index asc)
-    float wsel = 0.0f;   // lane j keeps the score of the j-th pick
+    // top-k by (logit desc, index asc); the winner's score travels with its key
+    float wsel = 0.0f;
     int idsel = 0;
-    for (int j = 0; j < K; ++j) {
-        unsigned long long mine = 0;
-        float pmine = 0.0f;
+    for (int j = 0; j < R.K; ++j) {
+        KeyVal mine{0u, 0u, 0.0f};
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
             if (cand[i]) {
-                const unsigned long long k = ((unsigned long long)ord_f32(s[i]) << 32) |
-                                             (uint32_t)(0xffffffffu - (lane * EPL + i));
-                if (k > mine) {
-                    mine = k;
-                    pmine = p[i];
-                }
+                const KeyVal k{ord_f32(s[i]), 0xffffffffu - (uint32_t)(sub * EPL + i), p[i]};
+                mine = kv_max(mine, k);
             }
         }
-        const unsigned long long best = wave_max_u64(mine);
-        const int e = (int)(0xffffffffu - (uint32_t)best);
-        const int owner = e / EPL;
-        const float pe = __shfl(pmine, owner, 64);
-        if (lane == owner) {
+        const KeyVal best = grp_max_kv<LPT>(mine);
+        const int e = (int)(0xffffffffu - best.lo);
+        if (sub == e / EPL) {
 #pragma unroll
             for (int i = 0; i < EPL; ++i)
-                if (lane * EPL + i == e)
+                if (sub * EPL + i == e)
                     cand[i] = false;
         }
-        if (lane == j) {
-            wsel = pe;
+        if (sub == j) {
+            wsel = best.val;
             idsel = e;
         }
     }
-    if ((scoring == MOE_ROUTE_SOFTMAX && renorm) || scoring == MOE_ROUTE_SIGMOID) {
-        const float tot = wave_sum(lane < K ? wsel : 0.0f);
+    if ((R.scoring == MOE_ROUTE_SOFTMAX && R.renorm) || R.scoring == MOE_ROUTE_SIGMOID) {
+        const float tot = grp_sum<LPT>(sub < R.K ? wsel : 0.0f);
         wsel = wsel / tot;
     }
-    if (lane < K) {
-        topk_ids[(int64_t)t * K + lane] = idsel;
-        topk_w[(int64_t)t * K + lane] = wsel * rsf;
+    id_out = idsel;
+    w_out = wsel * R.rsf;
+}
+
+__device__ __forceinline__ float load_logit(const void* lg, int lgdt, int64_t i)
+{
+    return (lgdt == MOE_BF16) ? bf16_to_f32(((const u16*)lg)[i]) : ((const float*)lg)[i];
+}
+
+// Router for many tokens: 4 waves of 64 / LPT tokens each per workgroup.
+template <int EPL, int LPT>
+__global__ void __launch_bounds__(256) k_router(const void* __restrict__ logits, int lgdt, int M,
+                                                RouteArgs R, int32_t* __restrict__ topk_ids,
+                                                float* __restrict__ topk_w)
+{
+    constexpr int TPW = 64 / LPT;
+    __shared__ float sh_logit[4][EPL * 64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, sub = lane & (LPT - 1);
+    const int t = (blockIdx.x * 4 + wave) * TPW + lane / LPT;
+    if (t >= M)
+        return;                                 // whole groups leave together
+    float s[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = sub * EPL + i;
+        s[i] = (e < R.E) ? load_logit(logits, lgdt, (int64_t)t * R.E + e) : -INFINITY;
+    }
+    if constexpr (LPT == 64) {
+        if (R.G > 1) {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (sub * EPL + i < R.E)
+                    sh_logit[wave][sub * EPL + i] = s[i];
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        }
+    }
+    int id;
+    float w;
+    route_token<EPL, LPT>(R, s, sub, sh_logit[wave], id, w);
+    if (sub < R.K) {
+        topk_ids[(int64_t)t * R.K + sub] = id;
+        topk_w[(int64_t)t * R.K + sub] = w;
     }
 }
 
+static RouteArgs route_args(const Plan& P)
+{
+    return RouteArgs{P.E, P.K, P.routing, P.renorm, P.G, P.kg, P.gmode, P.rsf};
+}
+
+// Lanes per token and experts per lane for E experts (grouped: whole waves).
+static void route_shape(int E, int G, int& epl, int& lpt)
+{
+    epl = E <= 64 ? 1 : (E + 63) / 64;
+    epl = epl <= 1 ? 1 : epl <= 2 ? 2 : epl <= 4 ? 4 : epl <= 8 ? 8 : 16;
+    lpt = 64;
+    if (G <= 1 && E <= 32)
+        lpt = E <= 8 ? 8 : E <= 16 ? 16 : 32;
+}
+
+#define MOE_ROUTE_SHAPES(X) \
+    X(1, 8) X(1, 16) X(1, 32) X(1, 64) X(2, 64) X(4, 64) X(8, 64) X(16, 64)
+
 hipError_t launch_router(const Plan& P, const void* logits, hipStream_t s)
 {
-    const dim3 grid((P.M + 3) / 4), block(256);
-    const int scoring = P.routing;
-#define MOE_ROUTER(EPL)                                                                          \
-    hipLaunchKernelGGL(k_router<EPL>, grid, block, 0, s, logits, P.lgdt, P.M, P.E, P.K, scoring, \
-                       P.renorm, P.G, P.kg, P.gmode, P.rsf, P.topk_ids, P.topk_w)
-    if (P.E <= 64)
-        MOE_ROUTER(1);
-    else if (P.E <= 128)
-        MOE_ROUTER(2);
-    else if (P.E <= 256)
-        MOE_ROUTER(4);
-    else if (P.E <= 512)
-        MOE_ROUTER(8);
-    else
-        MOE_ROUTER(16);
+    int epl, lpt;
+    route_shape(P.E, P.G, epl, lpt);
+    const int tpb = 4 * (64 / lpt);
+    const dim3 grid((P.M + tpb - 1) / tpb), block(256);
+    const RouteArgs R = route_args(P);
+#define MOE_ROUTER(EPL, LPT)                                                                  \
+    if (epl == EPL && lpt == LPT) {                                                           \
+        hipLaunchKernelGGL((k_router<EPL, LPT>), grid, block, 0, s, logits, P.lgdt, P.M, R,   \
+                           P.topk_ids, P.topk_w);                                             \
+        return hipGetLastError();                                                             \
+    }
+    MOE_ROUTE_SHAPES(MOE_ROUTER)
 #undef MOE_ROUTER
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 // ============================================================ align
@@ -193,12 +311,14 @@ hipError_t launch_router(const Plan& P, const void* logits, hipStream_t s)
 // section): group the M*top_k routed items by expert, pad each expert's run
 // to a multiple of BM.  Items keep ascending order inside an expert (a stable
 // sort, as the MoonEP page's build_permutation), so the result is unique and
-// independent of scheduling.  One workgroup of 16 waves; each wave owns a
-// contiguous chunk of items.  Equal-expert lanes of a wave are matched with
-// ballots over the id bits, which gives each item its rank without atomics.
+// independent of scheduling.  One workgroup of 16 waves.  The items sit in
+// LDS (in batches of ALIGN_CAP when there are more); each wave owns a
+// contiguous range of a batch.  Counting uses LDS atomics; the scatter ranks
+// equal-expert lanes of a wave with ballots over the id bits, so every item's
+// position is fixed without global atomics.
 
 constexpr int ALIGN_WAVES = 16;
-constexpr int ALIGN_UNROLL = 16;   // 64-item steps loaded per batch
+constexpr int ALIGN_CAP = 8192;        // items per LDS batch of the standalone align
 
 __device__ __forceinline__ unsigned long long match_mask(int e, bool valid, int nbits)
 {
@@ -226,6 +346,7 @@ __device__ int block_exclusive_scan_1024(int v, int* sh_tot, int* out_prefix)
         sh_tot[wave] = incl;
     __syncthreads();
     int base = 0, total = 0;
+#pragma unroll
     for (int w = 0; w < ALIGN_WAVES; ++w) {
         const int tw = sh_tot[w];
         if (w < wave)
@@ -236,13 +357,27 @@ __device__ int block_exclusive_scan_1024(int v, int* sh_tot, int* out_prefix)
     return total;
 }
 
+// Largest e in [0, n) with a[e] <= x (a non-decreasing, a[0] <= x).
+__device__ __forceinline__ int upper_index(const int* a, int n, int x)
+{
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a[mid] <= x)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
 
 // GEMM work unit lists: expert e's padded run is cut into chunks of CH rows
 // (the row height of one GEMM tile).  chunk_off[e] = chunks of experts < e,
 // chunk_off[E] = all chunks, chunk_expert[c] = expert of chunk c.  Called by
-// all 1024 threads; `padded` is this thread's expert run (0 for e >= E).
-__device__ void write_chunks(int padded, int CH, int E, int* sh_tot, int32_t* chunk_off,
-                             int32_t* chunk_expert)
+// all 1024 threads; `padded` is this thread's expert run (0 for e >= E);
+// choff: E + 1 ints of LDS scratch.
+__device__ void write_chunks(int padded, int CH, int E, int* sh_tot, int* choff,
+                             int32_t* chunk_off, int32_t* chunk_expert)
 {
     const int e = threadIdx.x;
     __syncthreads();   // sh_tot is reused from the previous scan
@@ -251,126 +386,202 @@ __device__ void write_chunks(int padded, int CH, int E, int* sh_tot, int32_t* ch
     const int ctotal = block_exclusive_scan_1024(nch, sh_tot, &cstart);
     if (e < E) {
         chunk_off[e] = cstart;
-        for (int j = 0; j < nch; ++j)
-            chunk_expert[cstart + j] = e;
+        choff[e] = cstart;
     }
     if (e == 0)
         chunk_off[E] = ctotal;
+    __syncthreads();
+    for (int c = threadIdx.x; c < ctotal; c += 1024)
+        chunk_expert[c] = upper_index(choff, E, c);
 }
 
-__global__ void __launch_bounds__(1024) k_align(const int32_t* __restrict__ ids, int Mk, int E,
-                                                int BM, int32_t* __restrict__ counts,
-                                                int32_t* __restrict__ offsets,
-                                                int32_t* __restrict__ sorted,
-                                                int32_t* __restrict__ expert_ids,
-                                                int32_t* __restrict__ npp, int sentinel,
-                                                int64_t max_sorted, int max_blocks, int CH,
-                                                int32_t* __restrict__ chunk_off,
-                                                int32_t* __restrict__ chunk_expert,
-                                                int32_t* __restrict__ inv)
+struct AlignOut {
+    int32_t *counts, *offsets, *sorted, *expert_ids, *npp, *chunk_off, *chunk_expert, *inv;
+    int E, BM, CH, sentinel, max_blocks;
+    int64_t max_sorted;
+};
+
+// LDS scratch of align_items (ints), after the item batch.
+__host__ __device__ constexpr int align_scratch_ints(int E)
 {
-    extern __shared__ int sh[];
-    int* cnt = sh;                               // [ALIGN_WAVES][E]
-    int* offs = sh + ALIGN_WAVES * E;            // [E]
-    int* tot = offs + E;                         // [ALIGN_WAVES]
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    return ALIGN_WAVES * E + 3 * (E + 1) + ALIGN_WAVES;
+}
+
+// The align proper over the n routed items.  ids_s: LDS batch of up to cap
+// items; if ids_g is non-null the batches are loaded from it, otherwise
+// ids_s already holds all n <= cap items.  Called by all 1024 threads.
+__device__ void align_items(const int32_t* __restrict__ ids_g, int n, int* ids_s, int cap,
+                           int* scratch, const AlignOut& O)
+{
+    const int E = O.E, BM = O.BM;
+    int* cnt = scratch;                         // [ALIGN_WAVES][E]
+    int* offs = cnt + ALIGN_WAVES * E;          // [E + 1] padded start per expert
+    int* run = offs + (E + 1);                  // [E + 1] next free position (pass 2)
+    int* choff = run + (E + 1);                 // [E + 1] chunk prefix
+    int* tot = choff + (E + 1);                 // [ALIGN_WAVES]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
-    const int chunk = ((Mk + ALIGN_WAVES - 1) / ALIGN_WAVES + 63) / 64 * 64;
-    const int beg = wave * chunk, end = min(Mk, beg + chunk);
+    const int nb = (n + cap - 1) / cap;
 
-    for (int i = threadIdx.x; i < ALIGN_WAVES * E; i += blockDim.x)
-        cnt[i] = 0;
-    __syncthreads();
-
-    // pass 1: per-wave, per-expert counts
-    for (int b0 = beg; b0 < end; b0 += 64 * ALIGN_UNROLL) {
-        int ev[ALIGN_UNROLL];
+    // item i of the current batch -> LDS (ids outside [0, E) become -1)
+    auto load_batch = [&](int b0, int len) {
+        for (int i0 = 0; i0 < len; i0 += 1024 * 8) {
+            int v[8];
 #pragma unroll
-        for (int u = 0; u < ALIGN_UNROLL; ++u) {
-            const int r = b0 + u * 64 + lane;
-            ev[u] = (r < end) ? ids[r] : -1;
-            if (ev[u] >= E)
-                ev[u] = -1;
-        }
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * 1024 + tid;
+                v[u] = (i < len) ? ids_g[b0 + i] : -1;
+            }
 #pragma unroll
-        for (int u = 0; u < ALIGN_UNROLL; ++u) {
-            const bool valid = ev[u] >= 0;
-            const unsigned long long m = match_mask(ev[u], valid, nbits);
-            if (valid && lane == (int)__builtin_ctzll(m))
-                cnt[wave * E + ev[u]] += __popcll(m);
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * 1024 + tid;
+                if (i < len)
+                    ids_s[i] = (v[u] >= 0 && v[u] < E) ? v[u] : -1;
+            }
         }
-    }
-    __syncthreads();
+    };
+    // per-wave counts of a batch of len items: wave w owns [w*ch, (w+1)*ch)
+    auto count_waves = [&](int len) {
+        for (int i = tid; i < ALIGN_WAVES * E; i += 1024)
+            cnt[i] = 0;
+        __syncthreads();
+        const int ch = (len + ALIGN_WAVES - 1) / ALIGN_WAVES;
+        const int end = min(len, (wave + 1) * ch);
+        for (int i = wave * ch + lane; i < end; i += 64) {
+            const int e = ids_s[i];
+            if (e >= 0)
+                atomicAdd(&cnt[wave * E + e], 1);
+        }
+        __syncthreads();
+    };
 
-    // per-expert totals, wave prefixes, padded offsets
-    int run = 0, padded = 0;
-    const int e = threadIdx.x;
-    if (e < E) {
-        for (int w = 0; w < ALIGN_WAVES; ++w) {
-            const int c = cnt[w * E + e];
-            cnt[w * E + e] = run;
-            run += c;
+    // pass 1: per-expert totals
+    int total_e = 0;
+    if (nb <= 1) {
+        if (ids_g)
+            load_batch(0, n);
+        __syncthreads();
+        count_waves(n);
+        if (tid < E)
+            for (int w = 0; w < ALIGN_WAVES; ++w)
+                total_e += cnt[w * E + tid];
+    } else {
+        for (int i = tid; i < E; i += 1024)
+            run[i] = 0;
+        for (int b = 0; b < nb; ++b) {
+            const int b0 = b * cap, len = min(cap, n - b0);
+            __syncthreads();
+            load_batch(b0, len);
+            __syncthreads();
+            for (int i = tid; i < len; i += 1024) {
+                const int e = ids_s[i];
+                if (e >= 0)
+                    atomicAdd(&run[e], 1);
+            }
         }
-        padded = (run + BM - 1) / BM * BM;
+        __syncthreads();
+        if (tid < E)
+            total_e = run[tid];
     }
+
+    // padded offsets, counts, expert ids, sentinel padding
+    const int e = tid;
+    const int padded = (e < E) ? (total_e + BM - 1) / BM * BM : 0;
     int start;
     const int total = block_exclusive_scan_1024(padded, tot, &start);
     if (e < E) {
-        counts[e] = run;
-        offsets[e] = start;
+        O.counts[e] = total_e;
+        O.offsets[e] = start;
         offs[e] = start;
-        for (int b = start / BM; b < (start + padded) / BM && b < max_blocks; ++b)
-            expert_ids[b] = e;
-        for (int q = start + run; q < start + padded && q < max_sorted; ++q)
-            sorted[q] = sentinel;
+        run[e] = start;
+        for (int q = start + total_e; q < start + padded && q < O.max_sorted; ++q)
+            O.sorted[q] = O.sentinel;
     }
-    if (threadIdx.x == 0) {
-        offsets[E] = total;
-        *npp = total;
+    if (tid == 0) {
+        O.offsets[E] = total;
+        offs[E] = total;
+        *O.npp = total;
     }
-    write_chunks(padded, CH, E, tot, chunk_off, chunk_expert);
-    __syncthreads();
+    write_chunks(padded, O.CH, E, tot, choff, O.chunk_off, O.chunk_expert);
+    for (int b = tid; b < total / BM && b < O.max_blocks; b += 1024)
+        O.expert_ids[b] = upper_index(offs, E, b * BM);
 
-    // pass 2: stable scatter
-    for (int b0 = beg; b0 < end; b0 += 64 * ALIGN_UNROLL) {
-        int ev[ALIGN_UNROLL];
-#pragma unroll
-        for (int u = 0; u < ALIGN_UNROLL; ++u) {
-            const int r = b0 + u * 64 + lane;
-            ev[u] = (r < end) ? ids[r] : -1;
-            if (ev[u] >= E)
-                ev[u] = -1;
+    // pass 2: stable scatter, batch by batch
+    for (int b = 0; b < nb; ++b) {
+        const int b0 = b * cap, len = min(cap, n - b0);
+        if (nb > 1) {
+            __syncthreads();
+            load_batch(b0, len);
+            __syncthreads();
+            count_waves(len);
         }
-#pragma unroll
-        for (int u = 0; u < ALIGN_UNROLL; ++u) {
-            const bool valid = ev[u] >= 0;
-            const unsigned long long m = match_mask(ev[u], valid, nbits);
-            const int r = b0 + u * 64 + lane;
+        // cnt[w][e] <- first position of wave w's items of expert e
+        if (tid < E) {
+            int base = run[tid];
+            for (int w = 0; w < ALIGN_WAVES; ++w) {
+                const int c = cnt[w * E + tid];
+                cnt[w * E + tid] = base;
+                base += c;
+            }
+            run[tid] = base;
+        }
+        __syncthreads();
+        const int ch = (len + ALIGN_WAVES - 1) / ALIGN_WAVES;
+        const int end = min(len, (wave + 1) * ch);
+        for (int i0 = wave * ch; i0 < end; i0 += 64) {
+            const int i = i0 + lane;
+            const int ev = (i < end) ? ids_s[i] : -1;
+            const bool valid = ev >= 0;
+            const unsigned long long m = match_mask(ev, valid, nbits);
+            const int r = b0 + i;
             if (valid) {
                 const int rank = __popcll(m & ((1ull << lane) - 1ull));
-                const int base = offs[ev[u]] + cnt[wave * E + ev[u]];
-                const int64_t pos = (int64_t)base + rank;
-                if (pos < max_sorted)
-                    sorted[pos] = r;
-                inv[r] = (pos < max_sorted) ? (int)pos : -1;
-            } else if (r < end) {
-                inv[r] = -1;                        // expert id out of range: no row
+                const int64_t pos = (int64_t)cnt[wave * E + ev] + rank;
+                if (pos < O.max_sorted)
+                    O.sorted[pos] = r;
+                O.inv[r] = (pos < O.max_sorted) ? (int)pos : -1;
+            } else if (i < end) {
+                O.inv[r] = -1;                      // expert id out of range: no row
             }
             // every lane has read its base before the leader moves it on
             __builtin_amdgcn_wave_barrier();
             if (valid && lane == (int)__builtin_ctzll(m))
-                cnt[wave * E + ev[u]] += __popcll(m);
+                cnt[wave * E + ev] += __popcll(m);
             __builtin_amdgcn_wave_barrier();
         }
     }
 }
 
+static AlignOut align_out(const Plan& P)
+{
+    return AlignOut{P.counts,     P.offsets,      P.sorted_ids, P.expert_ids, P.npp,
+                    P.chunk_off,  P.chunk_expert, P.inv,        P.E,          P.BM,
+                    P.CH,         (int)P.sentinel, P.max_blocks, P.max_sorted};
+}
+
+__global__ void __launch_bounds__(1024) k_align(const int32_t* __restrict__ ids, int Mk, int cap,
+                                                AlignOut O)
+{
+    extern __shared__ int sh[];
+    align_items(ids, Mk, sh, cap, sh + cap, O);
+}
+
+static hipError_t set_lds(const void* kernel, size_t bytes)
+{
+    if (bytes <= 65536)
+        return hipSuccess;
+    return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 hipError_t launch_align(const Plan& P, const int32_t* ids, hipStream_t s)
 {
-    const size_t lds = sizeof(int) * ((size_t)ALIGN_WAVES * P.E + P.E + ALIGN_WAVES);
-    hipLaunchKernelGGL(k_align, dim3(1), dim3(1024), lds, s, ids, P.M * P.K, P.E, P.BM, P.counts,
-                       P.offsets, P.sorted_ids, P.expert_ids, P.npp, (int)P.sentinel, P.max_sorted,
-                       P.max_blocks, P.CH, P.chunk_off, P.chunk_expert, P.inv);
+    const int Mk = P.M * P.K;
+    const int cap = Mk < ALIGN_CAP ? (Mk > 0 ? Mk : 1) : ALIGN_CAP;
+    const size_t lds = sizeof(int) * ((size_t)cap + align_scratch_ints(P.E));
+    const hipError_t e = set_lds((const void*)k_align, lds);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_align, dim3(1), dim3(1024), lds, s, ids, Mk, cap, align_out(P));
     return hipGetLastError();
 }
 
@@ -391,7 +602,7 @@ __global__ void __launch_bounds__(1024) k_tilelist(const int32_t* __restrict__ e
                                                    int32_t* __restrict__ chunk_expert)
 {
     __shared__ int tot[ALIGN_WAVES];
-    __shared__ int sh_start[1024], sh_cnt[1024];
+    __shared__ int sh_start[1025], sh_cnt[1024], choff[1025];
     const int e = threadIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int c = 0, padded = 0;
     if (e < E) {
@@ -407,18 +618,17 @@ __global__ void __launch_bounds__(1024) k_tilelist(const int32_t* __restrict__ e
         offsets[e] = fits ? start : 0;
         sh_start[e] = start;
         sh_cnt[e] = c;
-        if (fits)
-            for (int b = start / BM; b < (start + padded) / BM; ++b)
-                expert_ids[b] = e;
     }
     if (threadIdx.x == 0) {
         offsets[E] = fits ? total : 0;
+        sh_start[E] = total;
         *npp = fits ? total : 0;
     }
-    write_chunks(fits ? padded : 0, CH, E, tot, chunk_off, chunk_expert);
+    write_chunks(fits ? padded : 0, CH, E, tot, choff, chunk_off, chunk_expert);
     if (!fits)
         return;
-    __syncthreads();
+    for (int b = threadIdx.x; b < total / BM; b += 1024)
+        expert_ids[b] = upper_index(sh_start, E, b * BM);
     // each wave fills the runs of experts wave, wave+16, ...
     for (int x = wave; x < E; x += ALIGN_WAVES) {
         const int st = sh_start[x], cx = sh_cnt[x];
@@ -535,26 +745,47 @@ __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int
         return;
     const int t = (int)(gid / cpr), c = (int)(gid % cpr) * 4;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j = 0; j < K; ++j) {
-        int64_t row;
-        if (tmap) {
-            const int flat = tmap[(int64_t)t * K + j];
-            row = (int64_t)offsets[flat / T] + flat % T;
-        } else {
-            row = inv[(int64_t)t * K + j];
-            if (row < 0)
-                continue;
+    // eight routed items at a time: their rows and weights, then their
+    // output chunks, are all in flight before the (ordered) accumulation
+    for (int j0 = 0; j0 < K; j0 += 8) {
+        int64_t row[8];
+        float wj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u;
+            row[u] = -1;
+            wj[u] = 0.0f;
+            if (j < K) {
+                if (tmap) {
+                    const int flat = tmap[(int64_t)t * K + j];
+                    row[u] = (int64_t)offsets[flat / T] + flat % T;
+                } else {
+                    row[u] = inv[(int64_t)t * K + j];
+                }
+                wj[u] = w[(int64_t)t * K + j];
+            }
         }
-        const float wj = w[(int64_t)t * K + j];
-        f32x4 v = *(const f32x4*)(o + row * H + c);
-        if (o2) {
-            const f32x4 v2 = *(const f32x4*)(o2 + row * H + c);
-            v = f32x4{v[0] + v2[0], v[1] + v2[1], v[2] + v2[2], v[3] + v2[3]};
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            v[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (row[u] >= 0) {
+                v[u] = *(const f32x4*)(o + row[u] * H + c);
+                if (o2) {
+                    const f32x4 v2 = *(const f32x4*)(o2 + row[u] * H + c);
+                    v[u] = f32x4{v[u][0] + v2[0], v[u][1] + v2[1], v[u][2] + v2[2], v[u][3] + v2[3]};
+                }
+            }
         }
-        acc[0] += wj * v[0];
-        acc[1] += wj * v[1];
-        acc[2] += wj * v[2];
-        acc[3] += wj * v[3];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (row[u] < 0)
+                continue;                           // no row: contributes nothing
+            acc[0] += wj[u] * v[u][0];
+            acc[1] += wj[u] * v[u][1];
+            acc[2] += wj[u] * v[u][2];
+            acc[3] += wj[u] * v[u][3];
+        }
     }
     if constexpr (sizeof(TOut) == 2) {
         const uint32_t lo = f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);

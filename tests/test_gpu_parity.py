@@ -165,12 +165,13 @@ def test_batched_bf16_matches_contiguous():
     GH.compare(cfg, out.float().cpu().numpy(), y, "batched bf16 reduce")
 
 
-@pytest.mark.parametrize("tile_cfg", ["0", "0/wc2", "1", "2"])
+@pytest.mark.parametrize("tile_cfg", ["0", "0/wc2", "1", "2", "4", "5"])
 @pytest.mark.parametrize("skew", [False, True])
 def test_tile_families_ragged(tile_cfg, skew, monkeypatch):
-    """Every bf16 tile family on K and column tails (H % 64 = 16, I % 64 = 48)
-    and, with skew, on experts of 200 rows: several row chunks per expert and
-    a partial last strip.  "0/wc2": the 160-row family with the 4-wave,
+    """Every bf16 tile family (0: 160-row DMA ring, 1 / 2: 64 / 16-row
+    register-staged, 4 / 5: 32 / 64-row DMA ring) on K and column tails
+    (H % 64 = 16, I % 64 = 48) and, with skew, on experts of 200 rows: several
+    row chunks per expert and a partial last strip.  "0/wc2": the 160-row family with the 4-wave,
     128-column GEMM1 tile instead of the 8-wave one small problems get."""
     dev = GH.device()
     if tile_cfg == "0/wc2":
@@ -207,3 +208,36 @@ def test_gemm2_k_split(packed, monkeypatch):
     out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, packed=packed)
     ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
     GH.check_output(inp, out, ids_o, w_o, what="k split")
+
+
+# Routing / align launch shapes, with tiny expert FFNs so the oracle stays
+# fast: (M, E, top_k, scoring, groups).  Lanes per token: 8, 16, 32 or 64
+# (E <= 64), several experts per lane above 64.  Past 8192 routed items the
+# align streams its items through LDS in batches; at E = 1024 its LDS passes
+# 64 KiB.
+ROUTE_PATHS = [
+    ("lpt8", 200, 8, 2, "softmax", 1),
+    ("lpt16", 96, 16, 3, "sigmoid", 1),
+    ("lpt32_tail", 70, 24, 5, "softmax", 1),
+    ("e1024_lds_over_64k", 6, 1024, 8, "softmax", 1),
+    ("lpt8_many_tokens", 1500, 8, 2, "softmax", 1),
+    ("lpt16_multibatch", 3000, 16, 4, "softmax", 1),
+    ("e256_grouped_multibatch", 1300, 256, 8, "sigmoid", 8),
+    ("e512", 300, 512, 6, "softmax", 1),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_PATHS, ids=[c[0] for c in ROUTE_PATHS])
+def test_route_align_paths(case):
+    name, M, E, K, scoring, G = case
+    dev = GH.device()
+    cfg = W.MIXTRAL_PREFILL.scaled(name=name, M=M, H=32, I=32, E=E, top_k=K, scoring=scoring,
+                                   renormalize=scoring == "softmax", group_count=G,
+                                   k_group=min(G, 4), group_select_mode=1 if G > 1 else 0,
+                                   routed_scaling_factor=1.5 if G > 1 else 1.0)
+    print(f"[case] route/align {name} M={M} E={E} k={K}", flush=True)
+    inp = W.make_inputs(cfg, 2000 + ROUTE_PATHS.index(case))
+    out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+    ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    tokens = None if M <= 64 else np.arange(0, M, max(1, M // 48))
+    GH.check_output(inp, out, ids_o, w_o, tokens=tokens, what=name)
