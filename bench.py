@@ -151,7 +151,7 @@ def main():
     # (moe_pack_weights); the plain layout is timed too, for reference
     plain_prob, plain_args = prob.c(), cargs
     pack_ms = None
-    if cfg.weight == "bf16":
+    if cfg.weight in ("bf16", "fp8"):
         ev0, ev1 = hip.create(), hip.create()
         rec(ctypes.c_void_p(ev0), ctypes.c_void_p(stream))
         pw = B.pack_weights(inp["w13"], inp["w2"])

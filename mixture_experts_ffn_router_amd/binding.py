@@ -218,18 +218,19 @@ class Problem:
 
 @dataclass
 class PackedWeights:
-    """bf16 expert weights re-laid out once by moe_pack_weights (uint8 device
-    buffers) with the plain shapes they came from."""
+    """bf16 or fp8 expert weights re-laid out once by moe_pack_weights (uint8
+    device buffers) with the plain shapes and the dtype they came from."""
     w13: object
     w2: object
     E: int
     H: int
     I: int
+    w_dtype: int = MOE_BF16
 
 
 def pack_weights(w13, w2) -> PackedWeights:
-    """Packs plain bf16 w13 [E, H, 2I] / w2 [E, I, H] on their device (one
-    launch pair on the current stream)."""
+    """Packs plain bf16 or fp8 w13 [E, H, 2I] / w2 [E, I, H] on their device
+    (one launch pair on the current stream)."""
     import torch
     E, H, N = w13.shape
     I = N // 2
@@ -242,13 +243,13 @@ def pack_weights(w13, w2) -> PackedWeights:
     p2 = torch.empty(b2, dtype=torch.uint8, device=w13.device)
     moe_pack_weights(prob, _ptr(w13), _ptr(w2), p13.data_ptr(), p2.data_ptr(),
                      current_stream_handle(w13.device))
-    return PackedWeights(p13, p2, E, H, I)
+    return PackedWeights(p13, p2, E, H, I, _dtype_code(w13))
 
 
 def _weights(w13, w2):
     """(w13 tensor, w2 tensor, E, H, I, w_dtype code, layout) of plain or packed weights."""
     if isinstance(w13, PackedWeights):
-        return w13.w13, w13.w2, w13.E, w13.H, w13.I, MOE_BF16, MOE_W_PACKED
+        return w13.w13, w13.w2, w13.E, w13.H, w13.I, w13.w_dtype, MOE_W_PACKED
     E, H, N = w13.shape
     return w13, w2, E, H, N // 2, _dtype_code(w13), MOE_W_PLAIN
 

@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["moe_api.hip", "moe_kernels.hip", "moe_gemm.hip"]
+SOURCES = ["moe_api.hip", "moe_kernels.hip", "moe_gemm.hip", "moe_gemm_fp8.hip"]
 ARCH = "gfx950"
 
 

@@ -56,7 +56,7 @@ static int validate(const moe_problem* p)
         return MOE_ERR_UNSUPPORTED;
     if (p->w_layout != MOE_W_PLAIN && p->w_layout != MOE_W_PACKED)
         return MOE_ERR_INVALID_ARG;
-    if (p->w_layout == MOE_W_PACKED && w != MOE_BF16)
+    if (p->w_layout == MOE_W_PACKED && w != MOE_BF16 && w != MOE_FP8_E4M3FN)
         return MOE_ERR_UNSUPPORTED;
 
     if (p->format == MOE_FMT_BATCHED) {
@@ -103,7 +103,7 @@ static int validate(const moe_problem* p)
 static int choose_tile(const moe_problem* p, int64_t rows_cap)
 {
     if (p->w_dtype == MOE_FP8_E4M3FN)
-        return TILE_FP8;
+        return p->w_layout == MOE_W_PACKED ? TILE_FP8_DMA : TILE_FP8;
     if (p->w_dtype == MOE_F32)
         return TILE_DECODE;
     // tuning override: MOE_TILE_CFG = 0 (prefill) | 1 (mid) | 2 (decode) | 4 (decode, DMA)
@@ -171,7 +171,9 @@ static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_
     w.off_aq = take(quant ? (size_t)qrows * p->H : 0);
     w.off_aq_scale = take(quant ? (size_t)qrows * 4 : 0);
     w.off_z = take((size_t)max_sorted * p->I * zes);
-    w.off_z_scale = take(fp8 ? (size_t)max_sorted * (p->I / 128) * 4 : 0);
+    // fp8 z scales, group-major: [I/128][zs_ld]; the row padding lets a GEMM
+    // tile read the scales of all its rows as one block
+    w.off_z_scale = take(fp8 ? (size_t)zs_ld(max_sorted) * (p->I / 128) * 4 : 0);
     const int64_t orows = (batched && !p->batched_reduce) ? 0 : max_sorted;
     w.off_o = take((size_t)orows * p->H * 4);
     const int cfg = choose_tile(p, rows_cap);
@@ -240,6 +242,7 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
     P.aq_scale = (float*)(ws + w.off_aq_scale);
     P.z = ws + w.off_z;
     P.z_scale = (float*)(ws + w.off_z_scale);
+    P.zs_ld = zs_ld(w.max_sorted_len);
     P.o = (float*)(ws + w.off_o);
     P.g2split = chunk_offs[INT_O2] != 0;
     P.o2 = P.g2split ? (float*)(ws + chunk_offs[INT_O2]) : nullptr;
@@ -367,19 +370,26 @@ extern "C" int moe_forward_timed(const moe_problem* p, const moe_args* a, void* 
     return forward(p, a, workspace, workspace_bytes, stream, events);
 }
 
-// Packed weight sizes: 16 KiB blocks of 64 weight rows x 128 weight columns
-// (w13: 64 gate + 64 up columns per block).
+// Packed weight sizes: 16 KiB blocks.  bf16: 64 weight rows x 128 weight
+// columns (w13: 64 gate + 64 up columns per block); fp8: 128 weight columns x
+// 128 K values (w13: 64 gate + 64 up columns).
 static int packed_sizes(const moe_problem* p, size_t* b13, size_t* b2)
 {
     const int rc = validate(p);
     if (rc != MOE_OK)
         return rc;
-    if (p->w_dtype != MOE_BF16)
-        return MOE_ERR_UNSUPPORTED;
     const size_t blk = 64 * 256;
-    *b13 = (size_t)p->E * ((p->I + 63) / 64) * ((p->H + 63) / 64) * blk;
-    *b2 = (size_t)p->E * ((p->H + 127) / 128) * ((p->I + 63) / 64) * blk;
-    return MOE_OK;
+    if (p->w_dtype == MOE_BF16) {
+        *b13 = (size_t)p->E * ((p->I + 63) / 64) * ((p->H + 63) / 64) * blk;
+        *b2 = (size_t)p->E * ((p->H + 127) / 128) * ((p->I + 63) / 64) * blk;
+        return MOE_OK;
+    }
+    if (p->w_dtype == MOE_FP8_E4M3FN) {          // I is a multiple of 128 (validated)
+        *b13 = (size_t)p->E * (p->I / 64) * ((p->H + 127) / 128) * blk;
+        *b2 = (size_t)p->E * ((p->H + 127) / 128) * (p->I / 128) * blk;
+        return MOE_OK;
+    }
+    return MOE_ERR_UNSUPPORTED;
 }
 
 extern "C" int moe_packed_weight_bytes(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes)
@@ -400,7 +410,11 @@ extern "C" int moe_pack_weights(const moe_problem* p, const void* w13, const voi
         return MOE_ERR_INVALID_ARG;
     (void)hipGetLastError();   // a stale error of an earlier, unrelated call
     const hipError_t err =
-        launch_pack_weights(p->E, p->H, p->I, w13, w2, w13_packed, w2_packed, (hipStream_t)stream);
+        (p->w_dtype == MOE_FP8_E4M3FN)
+            ? launch_pack_weights_fp8(p->E, p->H, p->I, w13, w2, w13_packed, w2_packed,
+                                      (hipStream_t)stream)
+            : launch_pack_weights(p->E, p->H, p->I, w13, w2, w13_packed, w2_packed,
+                                  (hipStream_t)stream);
     return err == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 

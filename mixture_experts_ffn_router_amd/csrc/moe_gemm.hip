@@ -32,12 +32,10 @@
 //     one column.  Row strides are padded by 16 bytes against bank conflicts.
 //   * A K stage is 128 bytes of each A row (64 bf16 / 128 fp8 / 32 f32);
 //     outputs are staged through LDS so global stores are 16-byte vectors.
-#include "moe_internal.h"
+#include "moe_gemm_common.h"
 
 namespace moe {
 
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 // element size, K per MFMA, K elements per lane per MFMA, K per LDS stage
 template <int DT>
@@ -95,10 +93,6 @@ __device__ __forceinline__ typename GT<DT>::Frag load_b_frag(const char* Bs, int
 // rows each half-wave reads to 8 distinct 32-byte bank groups.
 __device__ __forceinline__ int swz_b(int k) { return 2 * ((k & 3) | ((k >> 1) & 4)); }
 
-constexpr int PACK_BLOCK = 64 * 256;     // bytes of one packed weight block
-
-// sched_group_barrier instruction classes
-constexpr int SCHED_MFMA = 0x008, SCHED_DS_READ = 0x100;
 
 template <int DT>
 __device__ __forceinline__ f32x4 mma(typename GT<DT>::Frag a, typename GT<DT>::Frag b, f32x4 c)
@@ -109,110 +103,6 @@ __device__ __forceinline__ f32x4 mma(typename GT<DT>::Frag a, typename GT<DT>::F
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
     else   // e4m3 x e4m3, unit block scales (E8M0 127 = 2^0)
         return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
-
-__device__ __forceinline__ float load_bias(const void* b, int dt, int64_t idx)
-{
-    return (dt == MOE_BF16) ? bf16_to_f32(((const u16*)b)[idx]) : ((const float*)b)[idx];
-}
-
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
-
-// ---------------------------------------------------------------- arguments
-struct Sched {
-    const int32_t* counts;      // [E] real rows per expert
-    const int32_t* offsets;     // [E + 1] start of each expert's padded run
-    const int32_t* chunk_off;   // [E + 1] chunk prefix per expert
-    const int32_t* chunk_expert;
-    const int32_t* sorted;
-    int sentinel;
-    int E, n_tiles;
-};
-
-struct Gemm1Args {
-    Sched s;
-    const void* a;              // activation rows [*, H] (f32 / bf16 / fp8 codes)
-    const float* a_scale;       // fp8: per activation row
-    int a_ident;                // 1: A row = padded position p; 0: sorted[p] / a_div
-    int a_div;
-    const void* w13;            // [E, H, 2I], or packed blocks [E][ceil(I/64)][ceil(H/64)]
-    int w_packed;               // 1: w13 is in the packed block layout (bf16)
-    const float* w13_scale;     // fp8: [E, 2I]
-    const void* b13;            // [E, 2I] or null
-    int bias_dt;
-    int H, I;
-    void* z;                    // [max_sorted, I]
-    float* z_scale;             // fp8: [max_sorted, I/128]
-};
-
-struct Gemm2Args {
-    Sched s;
-    const void* z;
-    const float* z_scale;
-    const void* w2;             // [E, I, H], or packed blocks [E][ceil(H/128)][ceil(I/64)]
-    int w_packed;               // 1: w2 is in the packed block layout (bf16)
-    const float* w2_scale;      // fp8: [E, H]
-    const void* b2;             // [E, H] or null
-    int bias_dt;
-    int H, I;
-    int out_mode;               // 1: out[sorted[p]] (out_dt, batched slabs); 2: float o[p]
-    int out_dt;
-    int T;                      // batched: rows per expert slab
-    void* out;
-    int ksplit;                 // 2: column block ntile = 2 c + h covers K half h;
-    float* out2;                //    half 1 writes its float partials here, without bias
-};
-
-// ---------------------------------------------------------------- tile schedule
-// Persistent, XCD-aware schedule.  Logical tiles are ordered by expert, then
-// column block, then the expert's row chunks, so the chunks of one expert
-// that share a weight tile are neighbours.  Workgroups are dealt round-robin
-// over the 8 XCDs (workgroup b runs on XCD b % 8), so XCD x is given the
-// contiguous range [x R/8, (x+1) R/8) of the R tiles and walks it with its own
-// workgroups: neighbouring tiles run together on one XCD and share its L2.
-struct TileRef {
-    int e, r0, rows, ntile;     // expert, first padded row, real rows (>= 1), column block
-    int base;                   // first padded row of the expert's run
-};
-
-template <int CH>
-struct TileIter {
-    int L, hi, per, nt;
-
-    __device__ __forceinline__ explicit TileIter(const Sched& s)
-    {
-        nt = s.n_tiles;
-        const int R = s.chunk_off[s.E] * nt;
-        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-        per = gridDim.x >> 3;
-        const int lo = (int)(((int64_t)R * xcd) >> 3);
-        hi = (int)(((int64_t)R * (xcd + 1)) >> 3);
-        L = lo + slot;
-    }
-
-    __device__ __forceinline__ bool next(const Sched& s, TileRef& t)
-    {
-        if (L >= hi)
-            return false;
-        const int e = s.chunk_expert[L / nt];
-        const int c0 = s.chunk_off[e], nch = s.chunk_off[e + 1] - c0;
-        const int local = L - c0 * nt;
-        const int j = local % nch;
-        const int base = s.offsets[e];
-        t = TileRef{e, base + j * CH, min(CH, s.counts[e] - j * CH), local / nch, base};
-        L += per;
-        return true;
-    }
-};
-
-// f(e, row0, rows, ntile) for every tile of this workgroup.
-template <int CH, typename F>
-__device__ __forceinline__ void for_each_tile(const Sched& s, F&& f)
-{
-    TileIter<CH> it(s);
-    TileRef t;
-    while (it.next(s, t))
-        f(t.e, t.r0, t.rows, t.ntile);
 }
 
 // ---------------------------------------------------------------- tile shapes
@@ -469,7 +359,6 @@ __device__ __forceinline__ void gemm1_tile(const Gemm1Args& g, char* smem, int e
     if constexpr (DT == MOE_FP8_E4M3FN) {
         // requantise per (row, 128 columns): 8 threads per row, 16 columns each
         static_assert(BNZ == 128, "fp8 z groups are 128 columns");
-        const int ngrp = I / 128;
         for (int rb = 0; rb < nrows; rb += 32) {
             const int row = rb + tid / 8, c0 = (tid % 8) * 16;
             if (row >= nrows)
@@ -495,7 +384,7 @@ __device__ __forceinline__ void gemm1_tile(const Gemm1Args& g, char* smem, int e
             *(i32x4*)((uint8_t*)g.z + p * I + n0 + c0) =
                 i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
             if ((tid % 8) == 0)
-                g.z_scale[p * ngrp + n0 / 128] = sc;
+                g.z_scale[(int64_t)(n0 / 128) * g.zs_ld + p] = sc;
         }
     } else {
         constexpr int VE = 16 / ES;                 // z elements per 16-B store
@@ -535,7 +424,6 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int e
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int H = g.H, I = g.I;
     const int c0 = ntile * BN;
-    const int ngrp = I / 128;
     const int strips = (rows + 15) >> 4;
 
     // z rows are the padded positions themselves (written by GEMM1)
@@ -574,7 +462,7 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int e
     auto load = [&](int kt) {
         st.load(kt, zbase, (int64_t)I * ES, wbase, w_ld, w_stage, I);
         if constexpr (FP8)
-            st.rs = (tid < strips * 16) ? g.z_scale[((int64_t)r0 + tid) * ngrp + kt] : 0.0f;
+            st.rs = (tid < strips * 16) ? g.z_scale[(int64_t)kt * g.zs_ld + r0 + tid] : 0.0f;
     };
     auto store = [&](int stage) {
         char* base = smem + stage * S::STAGE_BYTES;
@@ -740,31 +628,6 @@ __global__ void __launch_bounds__(256) k_gemm2(Gemm2Args g)
 // Out-of-range chunks (K tail, columns past N) and rows past the tile's real
 // rows are DMA'd from a zero page; strips that hold only padding skip their
 // fragment reads and MFMAs.
-__device__ __attribute__((aligned(16))) int32_t g_zero16[4] = {0, 0, 0, 0};
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p)
-{
-    return (uint32_t)(uintptr_t)LDS_PTR(const char, p);
-}
-
-// M0 is a reserved register: the compiler never allocates it, and in these
-// kernels no other instruction reads it, so it needs no clobber.
-__device__ __forceinline__ void dma16(const char* g, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(lds), "v"(g)
-                 : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
-    // vmcnt[3:0], expcnt[6:4] (7: no wait), lgkmcnt[11:8] (15: no wait), vmcnt[5:4] at [15:14]
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 template <int FMW_, int WC_, int NS_>
 struct DS {
     static constexpr int FMW = FMW_, WC = WC_, NS = NS_;
@@ -862,48 +725,6 @@ __device__ __forceinline__ void dma_a_slot(int j, int wave, int lane, int& row, 
     chunk = (lane & 7) ^ ((row >> 1) & 7);
 }
 
-// The DMA ring over the K stages of one tile.  dma_prologue issues stages
-// 0 .. NS-2; dma_mainloop then, per stage, waits for it, refills the slot
-// freed one iteration earlier and hands the stage to compute().  Every
-// iteration issues exactly one stage (a zero-page filler once the real stages
-// run out), so when stage kt is awaited exactly NS - 2 stages of D DMAs per
-// wave were issued after it: one constant wait serves every iteration and the
-// loop body stays one basic block (branches in it make the register
-// allocator copy the accumulators between VGPRs and AGPRs).  The loop ends
-// drained, with every wave past its last LDS read, so the next tile's
-// prologue may refill the ring at once.
-// The stages run over [kb, ke) (K / 64 rounded up; a K-split half covers part).
-template <typename S, typename Src>
-__device__ __forceinline__ void dma_prologue(const Src& src, char* ring, int kb, int ke, int wave)
-{
-    const uint32_t ring_lds = lds_u32(ring);
-#pragma unroll
-    for (int st = 0; st < S::NS - 1; ++st)
-        src.issue(kb + st, ring_lds + st * S::STAGE, ring_lds + S::NS * S::STAGE, wave,
-                  kb + st < ke);
-}
-
-template <typename S, typename Src, typename F>
-__device__ __forceinline__ void dma_mainloop(const Src& src, char* ring, int kb, int ke, int wave,
-                                             F&& compute)
-{
-    const uint32_t ring_lds = lds_u32(ring);
-    int slot = 0;                                   // (kt - kb) % NS
-    for (int kt = kb; kt < ke; ++kt) {
-        wait_vmcnt<(S::NS - 2) * S::D>();
-        __syncthreads();
-        // the slot refilled here was last read in iteration kt - 1, which every
-        // wave finished before the barrier
-        const int nx = kt + S::NS - 1;
-        const int nslot = (slot == 0) ? S::NS - 1 : slot - 1;   // (nx - kb) % NS
-        src.issue(nx, ring_lds + nslot * S::STAGE, ring_lds + S::NS * S::STAGE, wave, nx < ke);
-        compute(ring + slot * S::STAGE);
-        slot = (slot == S::NS - 1) ? 0 : slot + 1;
-    }
-    wait_vmcnt<0>();                                // the fillers land before the ring is reused
-    __syncthreads();
-}
-
 // Fragment reads and MFMAs of one stage for wave (rg, cg).  Fragment fn's
 // columns start at 8-column chunk bchunk[fn] of weight block bblk[fn].
 template <typename S>
@@ -974,24 +795,6 @@ __device__ __forceinline__ void dma_run(const Src& src, char* ring, int kb, int 
         }
         dma_run<S, NM - 1>(src, ring, kb, ke, wave, rg, fr, acc, live);
     }
-}
-
-// Source row of real tile row `row` (< rows) for GEMM1's A (activations):
-// the routed token's row, or the padded position itself (a_ident).
-__device__ __forceinline__ int64_t gemm1_src_row(const Gemm1Args& g, int r0, int row)
-{
-    const int64_t p = (int64_t)r0 + row;
-    return g.a_ident ? p : (int64_t)(g.s.sorted[p] / g.a_div);
-}
-
-// Makes the compiler hold v in a register here.  Values loaded from global
-// memory ahead of time are pinned this way right after the ring has drained,
-// so that the compiler's wait for them (it does not see the DMAs) costs
-// nothing instead of stalling behind the next tile's DMAs.
-template <typename T>
-__device__ __forceinline__ void pin(const T& v)
-{
-    asm volatile("" : : "v"(v));
 }
 
 // Per-lane source rows of one GEMM1 tile's A DMAs (-1: padding row); loaded
@@ -1382,27 +1185,6 @@ hipError_t launch_pack_weights(int E, int H, int I, const void* w13, const void*
 }
 
 // ---------------------------------------------------------------- launchers
-// Persistent grid: every workgroup the device holds at once (a multiple of
-// the 8 XCDs), capped by the largest possible tile count.  Each kernel
-// instance queries its occupancy once; `cached` is that instance's slot.
-template <typename K>
-static unsigned persistent_grid(K kernel, int64_t max_tiles, int& cached, int threads = 256)
-{
-    if (cached == 0) {
-        int dev = 0, cus = 0, occ = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0);
-        cached = (cus > 0 ? cus : 256) * (occ > 0 ? occ : 1);
-    }
-    int64_t g = cached;
-    const int64_t cap = (max_tiles + 7) / 8 * 8;
-    if (g > cap)
-        g = cap;
-    g = (g + 7) / 8 * 8;
-    return (unsigned)(g < 8 ? 8 : g);
-}
-
 template <int DT, int FM, int WN>
 static hipError_t run_gemm1(const Gemm1Args& a, const Plan& P, hipStream_t s)
 {
@@ -1541,8 +1323,9 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s)
     g.I = P.I;
     g.z = P.z;
     g.z_scale = P.z_scale;
+    g.zs_ld = P.zs_ld;
     if (fp8)
-        return run_gemm1<MOE_FP8_E4M3FN, 8, 32>(g, P, s);
+        return P.wpacked ? launch_gemm1_fp8(g, P, s) : run_gemm1<MOE_FP8_E4M3FN, 8, 32>(g, P, s);
     if (P.wdt == MOE_F32)
         return run_gemm1<MOE_F32, 1, 16>(g, P, s);
     switch (P.cfg) {
@@ -1573,6 +1356,7 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
     g.s = make_sched(P);
     g.z = P.z;
     g.z_scale = P.z_scale;
+    g.zs_ld = P.zs_ld;
     g.w2 = A.w2;
     g.w_packed = P.wpacked;
     g.w2_scale = A.w2_scale;
@@ -1597,7 +1381,7 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
         g.out_dt = P.outdt;
     }
     if (P.wdt == MOE_FP8_E4M3FN)
-        return run_gemm2<MOE_FP8_E4M3FN, 8, 32>(g, P, s);
+        return P.wpacked ? launch_gemm2_fp8(g, P, s) : run_gemm2<MOE_FP8_E4M3FN, 8, 32>(g, P, s);
     if (P.wdt == MOE_F32)
         return run_gemm2<MOE_F32, 1, 16>(g, P, s);
     switch (P.cfg) {

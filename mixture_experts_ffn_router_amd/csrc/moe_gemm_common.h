@@ -1,0 +1,239 @@
+// Shared pieces of the grouped expert GEMMs (bf16 / f32 in moe_gemm.hip,
+// fp8 in moe_gemm_fp8.hip): launch arguments, the persistent tile schedule,
+// LDS-DMA helpers and the DMA ring loop.  gfx950 only.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr int PACK_BLOCK = 64 * 256;     // bytes of one packed weight block
+
+// sched_group_barrier instruction classes
+constexpr int SCHED_MFMA = 0x008, SCHED_DS_READ = 0x100;
+
+__device__ __forceinline__ float load_bias(const void* b, int dt, int64_t idx)
+{
+    return (dt == MOE_BF16) ? bf16_to_f32(((const u16*)b)[idx]) : ((const float*)b)[idx];
+}
+
+// SiLU(g) * u with the hardware exponential (v_exp_f32 on a prescaled
+// argument, a few ulp): the epilogue's cost matters where the MFMAs are fast.
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// ---------------------------------------------------------------- arguments
+struct Sched {
+    const int32_t* counts;      // [E] real rows per expert
+    const int32_t* offsets;     // [E + 1] start of each expert's padded run
+    const int32_t* chunk_off;   // [E + 1] chunk prefix per expert
+    const int32_t* chunk_expert;
+    const int32_t* sorted;
+    int sentinel;
+    int E, n_tiles;
+};
+
+struct Gemm1Args {
+    Sched s;
+    const void* a;              // activation rows [*, H] (f32 / bf16 / fp8 codes)
+    const float* a_scale;       // fp8: per activation row
+    int a_ident;                // 1: A row = padded position p; 0: sorted[p] / a_div
+    int a_div;
+    const void* w13;            // [E, H, 2I], or packed blocks (bf16 / fp8 block layouts)
+    int w_packed;               // 1: w13 is in the packed block layout
+    const float* w13_scale;     // fp8: [E, 2I]
+    const void* b13;            // [E, 2I] or null
+    int bias_dt;
+    int H, I;
+    void* z;                    // [max_sorted, I]
+    float* z_scale;             // fp8: [I/128][zs_ld] (group-major)
+    int64_t zs_ld;              // fp8: floats from one z scale group to the next
+};
+
+struct Gemm2Args {
+    Sched s;
+    const void* z;
+    const float* z_scale;       // fp8: [I/128][zs_ld] (group-major)
+    int64_t zs_ld;
+    const void* w2;             // [E, I, H], or packed blocks (bf16 / fp8 block layouts)
+    int w_packed;               // 1: w2 is in the packed block layout
+    const float* w2_scale;      // fp8: [E, H]
+    const void* b2;             // [E, H] or null
+    int bias_dt;
+    int H, I;
+    int out_mode;               // 1: out[sorted[p]] (out_dt, batched slabs); 2: float o[p]
+    int out_dt;
+    int T;                      // batched: rows per expert slab
+    void* out;
+    int ksplit;                 // 2: column block ntile = 2 c + h covers K half h;
+    float* out2;                //    half 1 writes its float partials here, without bias
+};
+
+// ---------------------------------------------------------------- tile schedule
+// Persistent, XCD-aware schedule.  Logical tiles are ordered by expert, then
+// column block, then the expert's row chunks, so the chunks of one expert
+// that share a weight tile are neighbours.  Workgroups are dealt round-robin
+// over the 8 XCDs (workgroup b runs on XCD b % 8), so XCD x is given the
+// contiguous range [x R/8, (x+1) R/8) of the R tiles and walks it with its own
+// workgroups: neighbouring tiles run together on one XCD and share its L2.
+struct TileRef {
+    int e, r0, rows, ntile;     // expert, first padded row, real rows (>= 1), column block
+    int base;                   // first padded row of the expert's run
+};
+
+template <int CH>
+struct TileIter {
+    int L, hi, per, nt;
+
+    __device__ __forceinline__ explicit TileIter(const Sched& s)
+    {
+        nt = s.n_tiles;
+        const int R = s.chunk_off[s.E] * nt;
+        const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+        per = gridDim.x >> 3;
+        const int lo = (int)(((int64_t)R * xcd) >> 3);
+        hi = (int)(((int64_t)R * (xcd + 1)) >> 3);
+        L = lo + slot;
+    }
+
+    __device__ __forceinline__ bool next(const Sched& s, TileRef& t)
+    {
+        if (L >= hi)
+            return false;
+        const int e = s.chunk_expert[L / nt];
+        const int c0 = s.chunk_off[e], nch = s.chunk_off[e + 1] - c0;
+        const int local = L - c0 * nt;
+        const int j = local % nch;
+        const int base = s.offsets[e];
+        t = TileRef{e, base + j * CH, min(CH, s.counts[e] - j * CH), local / nch, base};
+        L += per;
+        return true;
+    }
+};
+
+// f(e, row0, rows, ntile) for every tile of this workgroup.
+template <int CH, typename F>
+__device__ __forceinline__ void for_each_tile(const Sched& s, F&& f)
+{
+    TileIter<CH> it(s);
+    TileRef t;
+    while (it.next(s, t))
+        f(t.e, t.r0, t.rows, t.ntile);
+}
+
+// ---------------------------------------------------------------- LDS DMA
+// 16 zero bytes: the DMA source of padding rows and out-of-range chunks
+static __device__ __attribute__((aligned(16))) int32_t g_zero16[4] = {0, 0, 0, 0};
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p)
+{
+    return (uint32_t)(uintptr_t)LDS_PTR(const char, p);
+}
+
+// M0 is a reserved register: the compiler never allocates it, and in these
+// kernels no other instruction reads it, so it needs no clobber.
+__device__ __forceinline__ void dma16(const char* g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(g)
+                 : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    // vmcnt[3:0], expcnt[6:4] (7: no wait), lgkmcnt[11:8] (15: no wait), vmcnt[5:4] at [15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The DMA ring over the K stages of one tile.  dma_prologue issues stages
+// 0 .. NS-2; dma_mainloop then, per stage, waits for it, refills the slot
+// freed one iteration earlier and hands the stage to compute().  Every
+// iteration issues exactly one stage (a zero-page filler once the real stages
+// run out), so when stage kt is awaited exactly NS - 2 stages of D DMAs per
+// wave were issued after it: one constant wait serves every iteration and the
+// loop body stays one basic block (branches in it make the register
+// allocator copy the accumulators between VGPRs and AGPRs).  The loop ends
+// drained, with every wave past its last LDS read, so the next tile's
+// prologue may refill the ring at once.
+// The stages run over [kb, ke) (K / 64 rounded up; a K-split half covers part).
+template <typename S, typename Src>
+__device__ __forceinline__ void dma_prologue(const Src& src, char* ring, int kb, int ke, int wave)
+{
+    const uint32_t ring_lds = lds_u32(ring);
+#pragma unroll
+    for (int st = 0; st < S::NS - 1; ++st)
+        src.issue(kb + st, ring_lds + st * S::STAGE, ring_lds + S::NS * S::STAGE, wave,
+                  kb + st < ke);
+}
+
+template <typename S, typename Src, typename F>
+__device__ __forceinline__ void dma_mainloop(const Src& src, char* ring, int kb, int ke, int wave,
+                                             F&& compute)
+{
+    const uint32_t ring_lds = lds_u32(ring);
+    int slot = 0;                                   // (kt - kb) % NS
+    for (int kt = kb; kt < ke; ++kt) {
+        wait_vmcnt<(S::NS - 2) * S::D>();
+        __syncthreads();
+        // the slot refilled here was last read in iteration kt - 1, which every
+        // wave finished before the barrier
+        const int nx = kt + S::NS - 1;
+        const int nslot = (slot == 0) ? S::NS - 1 : slot - 1;   // (nx - kb) % NS
+        src.issue(nx, ring_lds + nslot * S::STAGE, ring_lds + S::NS * S::STAGE, wave, nx < ke);
+        compute(ring + slot * S::STAGE);
+        slot = (slot == S::NS - 1) ? 0 : slot + 1;
+    }
+    wait_vmcnt<0>();                                // the fillers land before the ring is reused
+    __syncthreads();
+}
+
+// Source row of real tile row `row` (< rows) for GEMM1's A (activations):
+// the routed token's row, or the padded position itself (a_ident).
+__device__ __forceinline__ int64_t gemm1_src_row(const Gemm1Args& g, int r0, int row)
+{
+    const int64_t p = (int64_t)r0 + row;
+    return g.a_ident ? p : (int64_t)(g.s.sorted[p] / g.a_div);
+}
+
+// Makes the compiler hold v in a register here.  Values loaded from global
+// memory ahead of time are pinned this way right after the ring has drained,
+// so that the compiler's wait for them (it does not see the DMAs) costs
+// nothing instead of stalling behind the next tile's DMAs.
+template <typename T>
+__device__ __forceinline__ void pin(const T& v)
+{
+    asm volatile("" : : "v"(v));
+}
+
+// Persistent grid: every workgroup the device holds at once (a multiple of
+// the 8 XCDs), capped by the largest possible tile count.  Each kernel
+// instance queries its occupancy once; `cached` is that instance's slot.
+template <typename K>
+static unsigned persistent_grid(K kernel, int64_t max_tiles, int& cached, int threads = 256)
+{
+    if (cached == 0) {
+        int dev = 0, cus = 0, occ = 0;
+        (void)hipGetDevice(&dev);
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0);
+        cached = (cus > 0 ? cus : 256) * (occ > 0 ? occ : 1);
+    }
+    int64_t g = cached;
+    const int64_t cap = (max_tiles + 7) / 8 * 8;
+    if (g > cap)
+        g = cap;
+    g = (g + 7) / 8 * 8;
+    return (unsigned)(g < 8 ? 8 : g);
+}
+
+
+// fp8 GEMMs on packed fp8 weights (moe_gemm_fp8.hip)
+hipError_t launch_gemm1_fp8(const Gemm1Args& a, const Plan& P, hipStream_t s);
+hipError_t launch_gemm2_fp8(const Gemm2Args& a, const Plan& P, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,565 @@
+// fp8 (OCP E4M3FN) grouped expert GEMMs on packed fp8 weights, gfx950.
+//
+// Same organisation as the bf16 path (FlagGems walkthrough, "fused_moe_kernel"
+// section; its "FP8 W8A8" section for the scales): one workgroup computes one
+// tile of one expert's sorted rows x a block of output columns, float32
+// accumulation, dequant / bias / activation / requant in the epilogue.
+//
+//   GEMM1: h = (sum_k qa[row, k] qw13[e, k, n]) * sa[row] * sw13[e, n] + b13[e, n]
+//          z = SiLU(h_gate) * h_up, requantised per (row, 128 z columns)
+//   GEMM2: o = (sum_g sz[row, g] sum_{k in g} qz[row, k] qw2[e, k, c]) * sw2[e, c] + b2
+//
+// With about 770 rows per expert these contractions are MFMA-bound.  A tile is
+// F8_ROWS rows x 256 weight columns on 8 waves (2 x 4), each wave F8_ROWS / 2
+// rows x 64 columns: (F8_ROWS / 32) x 4 MFMA tiles of
+// v_mfma_scale_f32_16x16x128_f8f6f4 (unit block scales) sharing their A and B
+// fragments within a 128-deep K stage.  One workgroup per CU; the ring holds
+// as many stages as fit in LDS.
+//
+// Both operands are K-contiguous in LDS (128 bytes = one K stage per row or
+// column), so A and B fragments are read the same way: lane l takes row /
+// column l % 16 and the 32 K bytes (l / 16) * 32 .. as two 16-byte reads.
+// The 16-byte chunk q of row / column r sits in slot q ^ ((r >> 1) & 7), which
+// spreads every fragment read over all banks.  Activations arrive that way by
+// DMA of their natural [rows, K] layout; the weights are packed once into
+// blocks that hold them that way (moe_pack_weights).
+#include "moe_gemm_common.h"
+
+namespace moe {
+
+// Packed fp8 weight block: 128 weight columns x 128 K values (16 KiB); column
+// c is 128 contiguous K bytes whose 16-byte chunk q sits in slot q ^ ((c >> 1) & 7).
+constexpr int F8_BLOCK = 128 * 128;
+
+__device__ __forceinline__ int f8_slot(int chunk, int r) { return chunk ^ ((r >> 1) & 7); }
+
+template <bool ZS>
+struct F8S {
+    static constexpr int NW = 8, NT = 64 * NW;   // 2 x 4 waves
+    static constexpr int CG = 4;                  // column groups of waves
+    static constexpr int FMW = F8_ROWS / 32;      // 16-row strips per wave
+    static constexpr int FN = 4;                  // 16-column fragments per wave
+    static constexpr int CH = 2 * FMW * 16;       // rows per tile
+    static constexpr int BN = CG * FN * 16;       // 256 weight columns
+    static constexpr int NB = BN / 128;           // weight blocks per K stage
+    static constexpr int A_BYTES = CH * 128, B_BYTES = NB * F8_BLOCK;
+    // GEMM2: the z scales of the stage's rows, one 1 KiB DMA (256 rows' worth;
+    // the scale rows are padded so that the read stays in bounds)
+    static constexpr int S_BYTES = ZS ? 1024 : 0;
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int NS = (3 * STAGE <= 150 * 1024) ? 3 : 2;   // ring stages
+    static constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / NW;
+    // DMAs per wave per stage; wave 0 also issues the z-scale DMA of GEMM2,
+    // so with 3 stages GEMM2 waits on a count that covers wave 0's extra one
+    static constexpr int D = A_PW + B_PW;
+    static constexpr int RING = NS * STAGE;
+    static_assert(A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES, "DMA split");
+    static_assert(CH * 4 <= 1024, "z scales of a stage are one DMA");
+};
+
+// DMA sources of one fp8 tile.  Wave w issues A DMAs i = w + 8 j (tile rows
+// 8i .. 8i+7, lane l: row 8i + l/8, K chunk f8_slot(l % 8, row)), weight DMAs
+// i = w + 8 j (block i / 16, its KiB i % 16, linear) and, for GEMM2, wave 0
+// one DMA of the stage's z scales.
+template <bool ZS>
+struct F8Src {
+    typedef F8S<ZS> S;
+    const char* ap[S::A_PW];    // this lane's A chunk at K stage 0, null: padding row
+    const char* wb[S::NB];      // packed block of K stage 0 per tile block, null past N
+    int64_t w_stage;            // bytes from one K stage's blocks to the next
+    const char* zs;             // GEMM2: this lane's 16 bytes of the stage-0 z scales
+    int64_t zs_stage;           // bytes from one z scale group to the next
+    int K;                      // contraction length
+
+    __device__ __forceinline__ void issue(int kt, uint32_t lds, uint32_t, int wave,
+                                          bool live) const
+    {
+        const int lane = threadIdx.x & 63;
+        const char* zero = (const char*)g_zero16;
+#pragma unroll
+        for (int j = 0; j < S::A_PW; ++j) {
+            const int i = wave + S::NW * j;
+            const int row = 8 * i + (lane >> 3);
+            const int c = f8_slot(lane & 7, row);
+            const bool ok = live && ap[j] && kt * 128 + c * 16 < K;
+            dma16(ok ? ap[j] + kt * 128 : zero, lds + i * 1024);
+        }
+#pragma unroll
+        for (int j = 0; j < S::B_PW; ++j) {
+            const int i = wave + S::NW * j;          // block i >> 4 == j >> 1 (wave < 8)
+            const char* w = wb[(j * S::NW) >> 4];
+            const char* p = (live && w) ? w + kt * w_stage + (i & 15) * 1024 + lane * 16 : zero;
+            dma16(p, lds + S::A_BYTES + i * 1024);
+        }
+        if constexpr (ZS) {
+            if (wave == 0)
+                dma16(live ? zs + kt * zs_stage : zero, lds + S::A_BYTES + S::B_BYTES);
+        }
+    }
+};
+
+// 32 K bytes of row / column r (l % 16 of a fragment) for lane group g = l / 16.
+__device__ __forceinline__ i32x8 f8_frag(const char* base, int r, int g)
+{
+    const char* p = base + r * 128;
+    const i32x4 lo = *(const i32x4*)(p + 16 * f8_slot(2 * g, r));
+    const i32x4 hi = *(const i32x4*)(p + 16 * f8_slot(2 * g + 1, r));
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ f32x4 mma_f8(const i32x8& a, const i32x8& b, const f32x4& c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// One K stage for wave (rg, cg): B fragment fn is column bcol[fn] (a multiple
+// of 16) of the stage's weight tile; the first NM strips of the wave's eight
+// hold real rows.  ZS: every product is scaled by its row's z scale before
+// it is accumulated (one MFMA spans exactly one 128-column z group).
+template <bool ZS, int NM>
+__device__ __forceinline__ void f8_stage(const char* st, int rg, const int (&bcol)[4], int lane,
+                                         f32x4 (&acc)[F8_ROWS / 32][4])
+{
+    typedef F8S<ZS> S;
+    const int s16 = lane & 15, g = lane >> 4;
+    const char* As = st + rg * (S::FMW * 16 * 128);
+    const char* Bs = st + S::A_BYTES;
+    i32x8 b[S::FN];
+#pragma unroll
+    for (int fn = 0; fn < S::FN; ++fn)
+        b[fn] = f8_frag(Bs + bcol[fn] * 128, s16, g);
+#pragma unroll
+    for (int fm = 0; fm < NM; ++fm) {
+        const i32x8 a = f8_frag(As + fm * 2048, s16, g);
+        if constexpr (ZS) {
+            const f32x4 sz = *(const f32x4*)(st + S::A_BYTES + S::B_BYTES +
+                                             (rg * S::FMW * 16 + fm * 16 + g * 4) * 4);
+#pragma unroll
+            for (int fn = 0; fn < S::FN; ++fn) {
+                const f32x4 t = mma_f8(a, b[fn], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[fm][fn][r] += t[r] * sz[r];
+            }
+        } else {
+#pragma unroll
+            for (int fn = 0; fn < S::FN; ++fn)
+                acc[fm][fn] = mma_f8(a, b[fn], acc[fm][fn]);
+        }
+    }
+}
+
+// The ring over [0, nk) with the MFMAs of the wave's first `live` strips;
+// one instantiation per count keeps the loop body branch free.
+template <bool ZS, int NM = F8_ROWS / 32>
+__device__ __forceinline__ void f8_run(const F8Src<ZS>& src, char* ring, int nk, int wave, int rg,
+                                       const int (&bcol)[4], int lane, f32x4 (&acc)[F8_ROWS / 32][4],
+                                       int live)
+{
+    typedef F8S<ZS> S;
+    if constexpr (NM == 0) {
+        dma_mainloop<S>(src, ring, 0, nk, wave, [](const char*) {});
+    } else {
+        if (live >= NM) {
+            dma_mainloop<S>(src, ring, 0, nk, wave, [&](const char* st) {
+                f8_stage<ZS, NM>(st, rg, bcol, lane, acc);
+            });
+            return;
+        }
+        f8_run<ZS, NM - 1>(src, ring, nk, wave, rg, bcol, lane, acc, live);
+    }
+}
+
+__device__ __forceinline__ void f8_zero(f32x4 (&acc)[F8_ROWS / 32][4])
+{
+#pragma unroll
+    for (int fm = 0; fm < F8_ROWS / 32; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn)
+            acc[fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// ---------------------------------------------------------------- GEMM1
+// Tile (expert, row chunk, ntile): z columns 128 ntile .. +127, i.e. the
+// gate and up columns of packed blocks 2 ntile and 2 ntile + 1 (each 64 gate
+// + 64 up columns).  Wave (rg, cg) owns z columns 32 cg .. +31: gate
+// fragments fn = 0, 1 and the matching up fragments fn = 2, 3.
+struct F8G1Src {
+    int srow[F8S<false>::A_PW];     // per-lane A source rows, -1: padding
+    int sa_row;                     // thread t < CH: source row of tile row t, -1: none
+};
+
+__device__ __forceinline__ void f8_gemm1_rows(const Gemm1Args& g, const TileRef& t, int wave,
+                                              int lane, F8G1Src& r)
+{
+    typedef F8S<false> S;
+#pragma unroll
+    for (int j = 0; j < S::A_PW; ++j) {
+        const int row = 8 * (wave + S::NW * j) + (lane >> 3);
+        r.srow[j] = (row < t.rows) ? (int)gemm1_src_row(g, t.r0, row) : -1;
+    }
+    const int tr = threadIdx.x;
+    r.sa_row = (tr < S::CH && tr < t.rows) ? (int)gemm1_src_row(g, t.r0, tr) : -1;
+}
+
+__device__ __forceinline__ void f8_gemm1_src(const Gemm1Args& g, const TileRef& t,
+                                             const F8G1Src& r, F8Src<false>& d)
+{
+    typedef F8S<false> S;
+    const int H = g.H, I = g.I;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nblk = I / 64, nks = (H + 127) / 128;
+    d.K = H;
+    d.w_stage = nblk * F8_BLOCK;
+    d.zs = nullptr;
+    d.zs_stage = 0;
+#pragma unroll
+    for (int bb = 0; bb < S::NB; ++bb)
+        d.wb[bb] = (const char*)g.w13 +
+                   ((int64_t)t.e * nks * nblk + (int64_t)t.ntile * S::NB + bb) * F8_BLOCK;
+#pragma unroll
+    for (int j = 0; j < S::A_PW; ++j) {
+        const int row = 8 * (wave + S::NW * j) + (lane >> 3);
+        const int c = f8_slot(lane & 7, row);
+        d.ap[j] = (r.srow[j] >= 0) ? (const char*)g.a + (int64_t)r.srow[j] * H + c * 16
+                                   : nullptr;
+    }
+}
+
+__global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
+{
+    typedef F8S<false> S;
+    __shared__ __attribute__((aligned(16))) char ring[S::RING];
+    __shared__ float rs[2][S::CH];                  // activation row scales, by tile parity
+    const int lane = threadIdx.x & 63, tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rg = wave / S::CG, cg = wave % S::CG;
+    const int I = g.I, N = 2 * I;
+    const int s16 = lane & 15, g4 = lane >> 4;
+    const int nk = (g.H + 127) / 128;
+
+    TileIter<S::CH> it(g.s);
+    TileRef cur;
+    if (!it.next(g.s, cur))
+        return;
+    F8G1Src rows;
+    f8_gemm1_rows(g, cur, wave, lane, rows);
+    F8Src<false> src;
+    f8_gemm1_src(g, cur, rows, src);
+    if (tid < S::CH)
+        rs[0][tid] = rows.sa_row >= 0 ? g.a_scale[rows.sa_row] : 0.0f;
+    dma_prologue<S>(src, ring, 0, nk, wave);
+
+    // B fragment columns within the stage's 256-column weight tile
+    int bcol[4];
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn) {
+        const int zl = cg * 32 + (fn & 1) * 16;             // z column within the tile
+        bcol[fn] = (zl / 64) * 128 + (fn >= 2 ? 64 : 0) + zl % 64;
+    }
+
+    int parity = 0;
+    for (;;) {
+        TileRef nxt;
+        const bool more = it.next(g.s, nxt);
+        if (more)
+            f8_gemm1_rows(g, nxt, wave, lane, rows);
+        float sn = 0.0f;                            // the next tile's row scale (tid < CH)
+        if (more && tid < S::CH && rows.sa_row >= 0)
+            sn = g.a_scale[rows.sa_row];
+        const int z0 = cur.ntile * 128;
+        float sg[2], su[2], bg[2], bu[2];
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) {
+            const int n = z0 + cg * 32 + fn * 16 + s16;
+            sg[fn] = g.w13_scale[(int64_t)cur.e * N + n];
+            su[fn] = g.w13_scale[(int64_t)cur.e * N + I + n];
+            bg[fn] = bu[fn] = 0.0f;
+            if (g.b13) {
+                bg[fn] = load_bias(g.b13, g.bias_dt, (int64_t)cur.e * N + n);
+                bu[fn] = load_bias(g.b13, g.bias_dt, (int64_t)cur.e * N + I + n);
+            }
+        }
+        f32x4 acc[F8_ROWS / 32][4];
+        f8_zero(acc);
+        const int strips = (cur.rows + 15) >> 4;
+        f8_run<false>(src, ring, nk, wave, rg, bcol, lane, acc,
+                      min(max(strips - rg * S::FMW, 0), S::FMW));
+        pin(sn);
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) {
+            pin(sg[fn]);
+            pin(su[fn]);
+            pin(bg[fn]);
+            pin(bu[fn]);
+        }
+        if (more) {
+#pragma unroll
+            for (int j = 0; j < S::A_PW; ++j)
+                pin(rows.srow[j]);
+            f8_gemm1_src(g, nxt, rows, src);
+            dma_prologue<S>(src, ring, 0, nk, wave);
+            if (tid < S::CH)
+                rs[parity ^ 1][tid] = sn;
+        }
+
+        // epilogue: z in registers, row amax across the 4 column waves through
+        // LDS, fp8 codes staged in the ring slot no DMA touches before the next
+        // tile's first barrier, then 16-byte row stores
+        uint8_t* zst = (uint8_t*)(ring + (S::NS - 1) * S::STAGE);           // [CH][128]
+        float* amx = (float*)(ring + (S::NS - 1) * S::STAGE + S::CH * 128);  // [4][CH]
+        // pass 1: z of (strip fm, fragment fn < 2, row r) replaces the gate
+        // accumulator; row amax over this wave's 32 z columns
+#pragma unroll
+        for (int fm = 0; fm < S::FMW; ++fm) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = rg * S::FMW * 16 + fm * 16 + g4 * 4 + r;
+                const float sa = rs[parity][row];
+                float m = 0.0f;
+#pragma unroll
+                for (int fn = 0; fn < 2; ++fn) {
+                    const float hg = acc[fm][fn][r] * sa * sg[fn];
+                    const float hu = acc[fm][fn + 2][r] * sa * su[fn];
+                    acc[fm][fn][r] = silu_mul(hg + bg[fn], hu + bu[fn]);
+                    m = fmaxf(m, fabsf(acc[fm][fn][r]));
+                }
+                m = grp_max<16>(m);
+                if (s16 == 0)
+                    amx[cg * S::CH + row] = m;
+            }
+        }
+        __syncthreads();
+        // pass 2: the row scale over all 128 z columns, the codes
+#pragma unroll
+        for (int fm = 0; fm < S::FMW; ++fm) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = rg * S::FMW * 16 + fm * 16 + g4 * 4 + r;
+                const float amax = fmaxf(fmaxf(amx[row], amx[S::CH + row]),
+                                         fmaxf(amx[2 * S::CH + row], amx[3 * S::CH + row]));
+                const float sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+                const uint32_t q = cvt_fp8x2(acc[fm][0][r] / sc, acc[fm][1][r] / sc);
+                zst[row * 128 + cg * 32 + s16] = (uint8_t)q;
+                zst[row * 128 + cg * 32 + 16 + s16] = (uint8_t)(q >> 8);
+                if (cg == 0 && s16 == 0 && row < cur.rows)
+                    g.z_scale[(int64_t)cur.ntile * g.zs_ld + cur.r0 + row] = sc;
+            }
+        }
+        __syncthreads();
+        for (int q = tid; q < cur.rows * 8; q += S::NT) {
+            const int row = q >> 3, c = q & 7;
+            *(i32x4*)((uint8_t*)g.z + ((int64_t)cur.r0 + row) * I + z0 + c * 16) =
+                *(const i32x4*)(zst + row * 128 + c * 16);
+        }
+        if (!more)
+            break;
+        cur = nxt;
+        parity ^= 1;
+    }
+}
+
+// ---------------------------------------------------------------- GEMM2
+// Tile (expert, row chunk, ntile): output columns 256 ntile .. +255 =
+// packed blocks 2 ntile, 2 ntile + 1; wave (rg, cg) owns columns 64 cg .. +63.
+// A rows are the padded positions (z written by GEMM1); the stage's z scales
+// (group kt of the tile's rows) arrive with it.
+__device__ __forceinline__ void f8_gemm2_src(const Gemm2Args& g, const TileRef& t, int wave,
+                                             F8Src<true>& d)
+{
+    typedef F8S<true> S;
+    const int H = g.H, I = g.I;
+    const int lane = threadIdx.x & 63;
+    const int64_t nblk = (H + 127) / 128, nks = I / 128;
+    d.K = I;
+    d.w_stage = nblk * F8_BLOCK;
+    d.zs = (const char*)(g.z_scale + t.r0) + lane * 16;
+    d.zs_stage = g.zs_ld * 4;
+#pragma unroll
+    for (int bb = 0; bb < S::NB; ++bb) {
+        const int64_t jb = (int64_t)t.ntile * S::NB + bb;
+        d.wb[bb] = (jb < nblk) ? (const char*)g.w2 + ((int64_t)t.e * nks * nblk + jb) * F8_BLOCK
+                               : nullptr;
+    }
+#pragma unroll
+    for (int j = 0; j < S::A_PW; ++j) {
+        const int row = 8 * (wave + S::NW * j) + (lane >> 3);
+        const int c = f8_slot(lane & 7, row);
+        d.ap[j] = (row < t.rows) ? (const char*)g.z + ((int64_t)t.r0 + row) * I + c * 16
+                                 : nullptr;
+    }
+}
+
+__global__ void __launch_bounds__(512, 1) k_gemm2_f8(Gemm2Args g)
+{
+    typedef F8S<true> S;
+    __shared__ __attribute__((aligned(16))) char ring[S::RING];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rg = wave / S::CG, cg = wave % S::CG;
+    const int H = g.H;
+    const int s16 = lane & 15, g4 = lane >> 4;
+    const int nk = g.I / 128;
+
+    TileIter<S::CH> it(g.s);
+    TileRef cur;
+    if (!it.next(g.s, cur))
+        return;
+    F8Src<true> src;
+    f8_gemm2_src(g, cur, wave, src);
+    dma_prologue<S>(src, ring, 0, nk, wave);
+    int bcol[4];
+#pragma unroll
+    for (int fn = 0; fn < 4; ++fn)
+        bcol[fn] = cg * 64 + fn * 16;
+
+    for (;;) {
+        TileRef nxt;
+        const bool more = it.next(g.s, nxt);
+        const int c0 = cur.ntile * S::BN;
+        const int strips = (cur.rows + 15) >> 4;
+        const int64_t dst0 = (g.out_mode == 2) ? (int64_t)cur.r0
+                                               : (int64_t)cur.e * g.T + (cur.r0 - cur.base);
+        float sw[4], bias[4];
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn) {
+            const int c = c0 + bcol[fn] + s16;
+            sw[fn] = (c < H) ? g.w2_scale[(int64_t)cur.e * H + c] : 0.0f;
+            bias[fn] = (g.b2 && c < H) ? load_bias(g.b2, g.bias_dt, (int64_t)cur.e * H + c) : 0.0f;
+        }
+        f32x4 acc[F8_ROWS / 32][4];
+        f8_zero(acc);
+        f8_run<true>(src, ring, nk, wave, rg, bcol, lane, acc,
+                     min(max(strips - rg * S::FMW, 0), S::FMW));
+#pragma unroll
+        for (int fn = 0; fn < 4; ++fn) {
+            pin(sw[fn]);
+            pin(bias[fn]);
+        }
+        if (more) {
+            f8_gemm2_src(g, nxt, wave, src);
+            dma_prologue<S>(src, ring, 0, nk, wave);
+        }
+        // epilogue straight from the accumulators: one strip at a time
+#pragma unroll
+        for (int fm = 0; fm < S::FMW; ++fm) {
+            const int strip = rg * S::FMW + fm;
+            if (strip >= strips)
+                continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = strip * 16 + g4 * 4 + r;
+                if (row >= cur.rows)
+                    continue;
+                const int64_t base = (dst0 + row) * H;
+#pragma unroll
+                for (int fn = 0; fn < 4; ++fn) {
+                    const int c = c0 + bcol[fn] + s16;
+                    if (c >= H)
+                        continue;
+                    const float v = acc[fm][fn][r] * sw[fn] + bias[fn];
+                    if (g.out_mode == 1 && g.out_dt == MOE_BF16)
+                        ((u16*)g.out)[base + c] = f32_to_bf16(v);
+                    else
+                        ((float*)g.out)[base + c] = v;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (!more)
+            break;
+        cur = nxt;
+    }
+}
+
+// ---------------------------------------------------------------- packing
+// One-time re-layout of fp8 expert weights into the K-contiguous blocks
+// above.  One thread per 16-byte slot of the output: it gathers 16 K values
+// of one weight column; rows past K and columns past N are zeros.
+//   w13 [E, H, 2I]: block (e, kt, j), kt < ceil(H/128), j < I/64: columns
+//     0-63 = gate columns 64 j .., 64-127 = up columns I + 64 j ..
+//   w2 [E, I, H]: block (e, kt, j), kt < I/128, j < ceil(H/128): columns 128 j ..
+template <bool W13>
+__global__ void __launch_bounds__(256) k_pack_f8(const uint8_t* __restrict__ w, int H, int I,
+                                                 i32x4* __restrict__ out, int64_t slots)
+{
+    const int K = W13 ? H : I, ncol = W13 ? 2 * I : H;
+    const int64_t nblk = W13 ? I / 64 : (H + 127) / 128, nks = (K + 127) / 128;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < slots;
+         q += (int64_t)gridDim.x * 256) {
+        const int sl = (int)(q & 7), c = (int)((q >> 3) & 127);
+        const int64_t b = q >> 10;                      // block (e, kt, j)
+        const int j = (int)(b % nblk);
+        const int kt = (int)((b / nblk) % nks);
+        const int64_t e = b / nblk / nks;
+        const int chunk = f8_slot(sl, c);              // slot sl holds K chunk sl ^ swz(c)
+        int col;
+        bool valid;
+        if constexpr (W13) {
+            col = (c < 64) ? 64 * j + c : I + 64 * j + (c - 64);
+            valid = true;
+        } else {
+            col = 128 * j + c;
+            valid = col < H;
+        }
+        uint32_t v[4] = {0u, 0u, 0u, 0u};
+        if (valid) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int row = kt * 128 + chunk * 16 + k;
+                const uint32_t byte =
+                    (row < K) ? w[((int64_t)e * K + row) * ncol + col] : 0u;
+                v[k >> 2] |= byte << (8 * (k & 3));
+            }
+        }
+        out[q] = i32x4{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+    }
+}
+
+hipError_t launch_pack_weights_fp8(int E, int H, int I, const void* w13, const void* w2,
+                                   void* p13, void* p2, hipStream_t s)
+{
+    const int64_t s13 = (int64_t)E * ((H + 127) / 128) * (I / 64) * (F8_BLOCK / 16);
+    const int64_t s2 = (int64_t)E * (I / 128) * ((H + 127) / 128) * (F8_BLOCK / 16);
+    auto grid = [](int64_t slots) {
+        const int64_t b = (slots + 255) / 256;
+        return (unsigned)(b < 16384 ? b : 16384);
+    };
+    hipLaunchKernelGGL(k_pack_f8<true>, dim3(grid(s13)), dim3(256), 0, s, (const uint8_t*)w13, H,
+                       I, (i32x4*)p13, s13);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    hipLaunchKernelGGL(k_pack_f8<false>, dim3(grid(s2)), dim3(256), 0, s, (const uint8_t*)w2, H,
+                       I, (i32x4*)p2, s2);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_gemm1_fp8(const Gemm1Args& a, const Plan& P, hipStream_t s)
+{
+    typedef F8S<false> S;
+    Gemm1Args g = a;
+    g.s.n_tiles = a.I / 128;
+    static int cached = 0;
+    const dim3 grid(persistent_grid(k_gemm1_f8, (int64_t)P.max_blocks * g.s.n_tiles, cached,
+                                    S::NT)),
+        block(S::NT);
+    hipLaunchKernelGGL(k_gemm1_f8, grid, block, 0, s, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm2_fp8(const Gemm2Args& a, const Plan& P, hipStream_t s)
+{
+    typedef F8S<true> S;
+    Gemm2Args g = a;
+    g.s.n_tiles = (a.H + S::BN - 1) / S::BN;
+    static int cached = 0;
+    const dim3 grid(persistent_grid(k_gemm2_f8, (int64_t)P.max_blocks * g.s.n_tiles, cached,
+                                    S::NT)),
+        block(S::NT);
+    hipLaunchKernelGGL(k_gemm2_f8, grid, block, 0, s, g);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -79,6 +79,15 @@ __device__ __forceinline__ uint8_t f32_to_fp8(float x)
     return (uint8_t)(sign | code);
 }
 
+// Two floats -> E4M3FN codes (a in bits 0-7, b in bits 8-15) by the hardware
+// conversion, which rounds to nearest even and equals f32_to_fp8 wherever
+// |x| <= 464 (the midpoint between 448 and the next binade step).  Callers
+// pass x / scale with scale = amax / 448, so |x| <= 448 up to one rounding.
+__device__ __forceinline__ uint32_t cvt_fp8x2(float a, float b)
+{
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+
 // ------------------------------------------------------------------ wave helpers
 __device__ __forceinline__ float wave_max(float v)
 {
@@ -106,6 +115,61 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
     return v;
 }
 
+// Reductions over aligned groups of LPT lanes; every lane of a group gets
+// the same result.  Inside a row of 16 lanes the partners are reached with
+// DPP (lane i reads lane i^1, i^2 (quad_perm), 7-i within its 8, 15-i within
+// its 16), which costs a few cycles where a shuffle through the LDS crossbar
+// costs about a hundred; rows are then combined from v_readlane values.
+// Each step combines a lane's value with its partner's and the partner
+// combines the same two values, so with a commutative op every lane of the
+// group ends with identical bits.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_MIRROR8 = 0x141, DPP_MIRROR16 = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float xchg(float v)
+{
+    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+__device__ __forceinline__ float rdlane(float v, int l)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+template <int LPT, typename T, typename Op>
+__device__ __forceinline__ T grp_reduce(T v, Op op)
+{
+    static_assert(LPT == 8 || LPT == 16 || LPT == 32 || LPT == 64, "group width");
+    v = op(v, xchg<DPP_XOR1>(v));
+    v = op(v, xchg<DPP_XOR2>(v));
+    v = op(v, xchg<DPP_MIRROR8>(v));
+    if constexpr (LPT >= 16)
+        v = op(v, xchg<DPP_MIRROR16>(v));
+    if constexpr (LPT == 32) {
+        const T a = op(rdlane(v, 0), rdlane(v, 16)), b = op(rdlane(v, 32), rdlane(v, 48));
+        v = (threadIdx.x & 32) ? b : a;
+    } else if constexpr (LPT == 64) {
+        v = op(op(rdlane(v, 0), rdlane(v, 16)), op(rdlane(v, 32), rdlane(v, 48)));
+    }
+    return v;
+}
+
+template <int LPT>
+__device__ __forceinline__ float grp_max(float v)
+{
+    return grp_reduce<LPT>(v, [](float a, float b) { return fmaxf(a, b); });
+}
+
+template <int LPT>
+__device__ __forceinline__ float grp_sum(float v)
+{
+    return grp_reduce<LPT>(v, [](float a, float b) { return a + b; });
+}
+
 // ------------------------------------------------------------------ execution plan
 // GEMM tile families; each fixes the rows per tile (chunk height).
 enum {
@@ -114,9 +178,11 @@ enum {
     TILE_DECODE = 2,       // register-staged, 16 rows
     TILE_FP8 = 3,          // fp8 register-staged, 128 rows
     TILE_DECODE_DMA = 4,   // LDS-DMA ring, 32 rows
-    TILE_MID_DMA = 5       // LDS-DMA ring, 64 rows
+    TILE_MID_DMA = 5,      // LDS-DMA ring, 64 rows
+    TILE_FP8_DMA = 6       // fp8 LDS-DMA ring on packed fp8 weights, F8_ROWS rows
 };
 constexpr int ALIGN_BM = 16;                 // expert runs are padded to 16 rows
+constexpr int F8_ROWS = 128;                 // rows per tile of the fp8 LDS-DMA GEMMs
 inline int tile_rows(int cfg)
 {
     switch (cfg) {
@@ -125,6 +191,7 @@ inline int tile_rows(int cfg)
     case TILE_FP8: return 128;
     case TILE_DECODE_DMA: return 32;
     case TILE_MID_DMA: return 64;
+    case TILE_FP8_DMA: return F8_ROWS;
     default: return 16;
     }
 }
@@ -158,11 +225,20 @@ struct Plan {
     uint8_t* aq;
     float* aq_scale;
     void* z;
-    float* z_scale;
+    float* z_scale;                 // fp8: [I/128][zs_ld], group-major
+    int64_t zs_ld;
     float* o;
     float* o2;                      // GEMM2 split in K: the second half's partial outputs
     int g2split;                    // GEMM2 runs as two K halves (o + o2)
 };
+
+// Row stride of the group-major fp8 z scales: every padded position plus one
+// GEMM tile of rows, so a tile may read its rows' scales as one block.
+inline int64_t zs_ld(int64_t max_sorted) { return max_sorted + 256; }
+
+// fp8 packed weights (moe_gemm_fp8.hip)
+hipError_t launch_pack_weights_fp8(int E, int H, int I, const void* w13, const void* w2,
+                                   void* p13, void* p2, hipStream_t s);
 
 // Host-side helpers shared by the workspace layout and the GEMM launchers.
 // Expected number of GEMM row chunks: every active expert has at least one,

@@ -28,22 +28,6 @@ __device__ __forceinline__ uint32_t ord_f32(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Reductions over aligned groups of LPT lanes; every lane of a group gets
-// the same result.  Inside a row of 16 lanes the partners are reached with
-// DPP (lane i reads lane i^1, i^2 (quad_perm), 7-i within its 8, 15-i within
-// its 16), which costs a few cycles where a shuffle through the LDS crossbar
-// costs about a hundred; rows are then combined from v_readlane values.
-// Each step combines a lane's value with its partner's and the partner
-// combines the same two values, so with a commutative op every lane of the
-// group ends with identical bits.
-constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_MIRROR8 = 0x141, DPP_MIRROR16 = 0x140;
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
-{
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
-}
-
 // (key, value) pair: the largest key wins and carries its value along
 struct KeyVal {
     uint32_t hi, lo;
@@ -57,53 +41,14 @@ __device__ __forceinline__ KeyVal kv_max(const KeyVal& a, const KeyVal& b)
 }
 
 template <int CTRL>
-__device__ __forceinline__ float xchg(float v)
-{
-    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
-}
-template <int CTRL>
 __device__ __forceinline__ KeyVal xchg(const KeyVal& v)
 {
     return KeyVal{dpp_u32<CTRL>(v.hi), dpp_u32<CTRL>(v.lo), xchg<CTRL>(v.val)};
-}
-__device__ __forceinline__ float rdlane(float v, int l)
-{
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 __device__ __forceinline__ KeyVal rdlane(const KeyVal& v, int l)
 {
     return KeyVal{(uint32_t)__builtin_amdgcn_readlane((int)v.hi, l),
                   (uint32_t)__builtin_amdgcn_readlane((int)v.lo, l), rdlane(v.val, l)};
-}
-
-template <int LPT, typename T, typename Op>
-__device__ __forceinline__ T grp_reduce(T v, Op op)
-{
-    static_assert(LPT == 8 || LPT == 16 || LPT == 32 || LPT == 64, "group width");
-    v = op(v, xchg<DPP_XOR1>(v));
-    v = op(v, xchg<DPP_XOR2>(v));
-    v = op(v, xchg<DPP_MIRROR8>(v));
-    if constexpr (LPT >= 16)
-        v = op(v, xchg<DPP_MIRROR16>(v));
-    if constexpr (LPT == 32) {
-        const T a = op(rdlane(v, 0), rdlane(v, 16)), b = op(rdlane(v, 32), rdlane(v, 48));
-        v = (threadIdx.x & 32) ? b : a;
-    } else if constexpr (LPT == 64) {
-        v = op(op(rdlane(v, 0), rdlane(v, 16)), op(rdlane(v, 32), rdlane(v, 48)));
-    }
-    return v;
-}
-
-template <int LPT>
-__device__ __forceinline__ float grp_max(float v)
-{
-    return grp_reduce<LPT>(v, [](float a, float b) { return fmaxf(a, b); });
-}
-
-template <int LPT>
-__device__ __forceinline__ float grp_sum(float v)
-{
-    return grp_reduce<LPT>(v, [](float a, float b) { return a + b; });
 }
 
 template <int LPT>
@@ -650,7 +595,8 @@ hipError_t launch_tilelist(const Plan& P, const int32_t* ent, hipStream_t s)
 // Dynamic per-row quantisation before the first expert GEMM (FlagGems
 // walkthrough, "FP8 W8A8": activations are quantised before each GEMM):
 // scale = amax / 448 (1 for an all-zero row), code = RNE(x / scale),
-// all in float32 with IEEE division.  One wave per row.
+// all in float32 with IEEE division.  One wave per row, 16-byte loads: a
+// first pass forms the amax, a second (from L2) writes the codes.
 //   ident == 0: rows t in [0, M) of hidden -> aq[t]         (contiguous)
 //   ident == 1: padded positions p < npp, source row sorted[p] -> aq[p] (batched)
 template <typename TIn>
@@ -660,8 +606,10 @@ __global__ void __launch_bounds__(256) k_quant_rows(const TIn* __restrict__ x, i
                                                     uint8_t* __restrict__ aq,
                                                     float* __restrict__ aq_scale)
 {
+    constexpr int VE = 16 / sizeof(TIn);            // elements per 16-byte chunk
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    const int nch = H / VE;                          // H is a multiple of 16
     int64_t src = r;
     if (ident) {
         if (r >= *npp)
@@ -678,30 +626,40 @@ __global__ void __launch_bounds__(256) k_quant_rows(const TIn* __restrict__ x, i
     } else if (r >= rows) {
         return;
     }
-    const TIn* row = x + src * (int64_t)H;
-    float amax = 0.0f;
-    for (int k = lane; k < H; k += 64) {
-        float v;
+    const i32x4* row = (const i32x4*)(x + src * (int64_t)H);
+    auto val = [&](const i32x4& c, int i) {
         if constexpr (sizeof(TIn) == 2)
-            v = bf16_to_f32(row[k]);
+            return bf16_to_f32((u16)((uint32_t)c[i >> 1] >> (16 * (i & 1))));
         else
-            v = row[k];
-        amax = fmaxf(amax, fabsf(v));
+            return __int_as_float(c[i]);
+    };
+    float amax = 0.0f;
+    for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
+        i32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = c0 + u * 64 + lane;
+            v[u] = (c < nch) ? row[c] : i32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < VE; ++i)
+                amax = fmaxf(amax, fabsf(val(v[u], i)));
     }
     amax = wave_max(amax);
     const float scale = (amax > 0.0f) ? amax / 448.0f : 1.0f;
-    for (int k = lane * 4; k < H; k += 64 * 4) {
-        uint32_t packed = 0;
+    for (int c = lane; c < nch; c += 64) {
+        const i32x4 v = row[c];
+        uint32_t w[VE / 4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float v;
-            if constexpr (sizeof(TIn) == 2)
-                v = bf16_to_f32(row[k + i]);
-            else
-                v = row[k + i];
-            packed |= (uint32_t)f32_to_fp8(v / scale) << (8 * i);
-        }
-        *(uint32_t*)(aq + r * H + k) = packed;
+        for (int q = 0; q < VE / 4; ++q)
+            w[q] = cvt_fp8x2(val(v, 4 * q) / scale, val(v, 4 * q + 1) / scale) |
+                   (cvt_fp8x2(val(v, 4 * q + 2) / scale, val(v, 4 * q + 3) / scale) << 16);
+        if constexpr (VE == 8)
+            *(i32x2*)(aq + r * H + c * 8) = i32x2{(int)w[0], (int)w[1]};
+        else
+            *(uint32_t*)(aq + r * H + c * 4) = w[0];
     }
     if (lane == 0)
         aq_scale[r] = scale;

@@ -91,7 +91,8 @@ def _status(prob):
           w_dtype=B.MOE_FP8_E4M3FN), B.MOE_OK),
     (dict(w_layout=B.MOE_W_PACKED), B.MOE_OK),
     (dict(w_layout=2), B.MOE_ERR_INVALID_ARG),
-    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_FP8_E4M3FN), B.MOE_ERR_UNSUPPORTED),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_FP8_E4M3FN), B.MOE_OK),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_FP8_E4M3FN, I=144), B.MOE_ERR_UNSUPPORTED),
     (dict(w_layout=B.MOE_W_PACKED, act_dtype=B.MOE_F32, w_dtype=B.MOE_F32, out_dtype=B.MOE_F32),
      B.MOE_ERR_UNSUPPORTED),
 ])
@@ -162,14 +163,22 @@ def test_forward_rejects_bad_workspace():
 
 
 def test_packed_weight_sizes():
-    """16 KiB blocks of 64 rows x 128 columns: w13 ceil(I/64) x ceil(H/64) per
-    expert (64 gate + 64 up columns a block), w2 ceil(H/128) x ceil(I/64)."""
+    """bf16: 16 KiB blocks of 64 rows x 128 columns: w13 ceil(I/64) x ceil(H/64)
+    per expert (64 gate + 64 up columns a block), w2 ceil(H/128) x ceil(I/64).
+    fp8: 16 KiB blocks of 128 columns x 128 K: w13 I/64 x ceil(H/128), w2
+    ceil(H/128) x I/128."""
     for E, H, I in [(8, 4096, 14336), (2, 208, 176), (256, 7168, 2048), (1, 16, 16)]:
         b13, b2 = B.moe_packed_weight_bytes(_prob(E=E, H=H, I=I, top_k=1).c())
         blk = 64 * 128 * 2
         assert b13 == E * -(-I // 64) * -(-H // 64) * blk
         assert b2 == E * -(-H // 128) * -(-I // 64) * blk
-    for kw, status in [(dict(w_dtype=B.MOE_FP8_E4M3FN, I=256), B.MOE_ERR_UNSUPPORTED),
+    for E, H, I in [(64, 2048, 1408), (2, 208, 384), (1, 16, 128)]:
+        b13, b2 = B.moe_packed_weight_bytes(
+            _prob(E=E, H=H, I=I, top_k=1, w_dtype=B.MOE_FP8_E4M3FN).c())
+        blk = 128 * 128
+        assert b13 == E * (I // 64) * -(-H // 128) * blk
+        assert b2 == E * -(-H // 128) * (I // 128) * blk
+    for kw, status in [(dict(w_dtype=B.MOE_FP8_E4M3FN, I=144), B.MOE_ERR_UNSUPPORTED),
                        (dict(act_dtype=B.MOE_F32, w_dtype=B.MOE_F32, out_dtype=B.MOE_F32),
                         B.MOE_ERR_UNSUPPORTED),
                        (dict(H=72), B.MOE_ERR_UNSUPPORTED)]:

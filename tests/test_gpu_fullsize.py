@@ -40,23 +40,24 @@ def test_full_size_contiguous(cfg):
         GH.check_rounded(out16, out)
 
 
-def test_full_size_batched_fp8():
+@pytest.mark.parametrize("packed", [False, True], ids=["plain", "packed"])
+def test_full_size_batched_fp8(packed):
     cfg = W.BATCHED_FP8
     dev = GH.device()
     seed = 1000 + W.CONFIGS.index(cfg)
-    print(f"[case] {cfg.name} seed={seed} generating", flush=True)
+    print(f"[case] {cfg.name} seed={seed} packed={packed} generating", flush=True)
     inp = W.make_inputs(cfg, seed, device=dev)
     counts = inp["expert_num_tokens"].cpu().numpy()
     print(f"[case] {cfg.name} rows/expert max={counts.max()} min={counts.min()} "
           f"total={counts.sum()}", flush=True)
-    out, ws, info = GH.run_batched(inp, dev, out_dtype=torch.float32)
+    out, ws, info = GH.run_batched(inp, dev, out_dtype=torch.float32, packed=packed)
     GH.check_batched_tilelist(inp, ws, info)
     rows, experts = GH.batched_rows(inp, sample=48)
     acts = oracle.Acts(inp["hidden"].cpu(), quantize=True)
     o_ref, _ = oracle.expert_rows(GH.oracle_experts(inp), acts, rows, experts)
     got = out.reshape(-1, cfg.H)[torch.as_tensor(rows, device=dev)].cpu().numpy()
     GH.compare(cfg, got, o_ref, "full batched rows")
-    out16, _, _ = GH.run_batched(inp, dev)
+    out16, _, _ = GH.run_batched(inp, dev, packed=packed)
     idx = torch.as_tensor(rows, device=dev)
     GH.check_rounded(out16.reshape(-1, cfg.H)[idx], out.reshape(-1, cfg.H)[idx])
     # invalid (NaN-filled) rows never leak into valid outputs

@@ -1,7 +1,7 @@
-"""Packed weight layout (moe_pack_weights): the packed bytes follow the
-layout moe.h documents, and a forward on packed weights equals the forward
-on the plain weights bit for bit (same products, same summation order) and
-so meets the oracle bar wherever the plain path does."""
+"""Packed weight layouts (moe_pack_weights, bf16 and fp8): the packed bytes
+follow the layouts moe.h documents, and a forward on packed weights equals
+the forward on the plain weights bit for bit (same products, same summation
+order) and so meets the oracle bar wherever the plain path does."""
 import numpy as np
 import pytest
 import torch
@@ -118,3 +118,93 @@ def test_packed_batched_bf16():
             idx = torch.as_tensor(rows, device=dev)
             flat_p, flat_k = plain.reshape(-1, cfg.H)[idx], packed.reshape(-1, cfg.H)[idx]
             assert torch.equal(flat_p, flat_k)
+
+
+def _ref_pack_f8(w, gate_up):
+    """The documented fp8 layout, written out with numpy: 16 KiB blocks of 128
+    columns x 128 K bytes; column c's 16-byte slot s holds K chunk s ^ ((c >> 1) & 7)."""
+    E, K, N = w.shape
+    half = N // 2
+    nblk = half // 64 if gate_up else -(-N // 128)
+    nks = -(-K // 128)
+    out = np.zeros((E, nks, nblk, 128, 8, 16), dtype=np.uint8)
+    for j in range(nblk):
+        for c in range(128):
+            if gate_up:
+                col = 64 * j + c if c < 64 else half + 64 * j + (c - 64)
+            else:
+                col = 128 * j + c
+                if col >= N:
+                    continue
+            for kt in range(nks):
+                for sl in range(8):
+                    chunk = sl ^ ((c >> 1) & 7)
+                    rows = kt * 128 + chunk * 16 + np.arange(16)
+                    ok = rows < K
+                    out[:, kt, j, c, sl, :ok.sum()] = w[:, rows[ok], col]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("E,H,I", [(2, 208, 256), (3, 128, 384)])
+def test_pack_layout_bytes_fp8(E, H, I):
+    dev = GH.device()
+    g = torch.Generator().manual_seed(9)
+    w13 = (torch.randn(E, H, 2 * I, generator=g) * 8).to(torch.float8_e4m3fn)
+    w2 = (torch.randn(E, I, H, generator=g) * 8).to(torch.float8_e4m3fn)
+    print(f"[case] pack fp8 E={E} H={H} I={I}", flush=True)
+    pw = B.pack_weights(w13.to(dev), w2.to(dev))
+    torch.cuda.synchronize()
+    got13, got2 = pw.w13.cpu().numpy(), pw.w2.cpu().numpy()
+    ref13 = _ref_pack_f8(w13.view(torch.uint8).numpy(), True)
+    ref2 = _ref_pack_f8(w2.view(torch.uint8).numpy(), False)
+    assert got13.shape == ref13.shape and got2.shape == ref2.shape
+    assert np.array_equal(got13, ref13)
+    assert np.array_equal(got2, ref2)
+
+
+# fp8: packed weights run the 256-row LDS-DMA kernels, plain weights the
+# register-staged ones; both sum the same products in the same order.
+FP8_CASES = [
+    W.MIXTRAL_PREFILL.scaled(name="contig_fp8_small", M=64, H=256, I=256, weight="fp8"),
+    W.MIXTRAL_PREFILL.scaled(name="contig_fp8_ragged_bias", M=300, H=208, I=384, E=4,
+                             weight="fp8", bias=True),
+]
+
+
+@pytest.mark.parametrize("cfg", FP8_CASES, ids=[c.name for c in FP8_CASES])
+def test_packed_fp8_equals_plain_contiguous(cfg):
+    dev = GH.device()
+    inp = W.make_inputs(cfg, 63)
+    print(f"[case] packed fp8 {cfg.name}", flush=True)
+    plain, _, _ = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+    packed, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, packed=True)
+    assert torch.equal(plain, packed)
+    ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    GH.check_output(inp, packed, ids_o, w_o, what="packed fp8")
+
+
+@pytest.mark.parametrize("reduce", [False, True])
+def test_packed_fp8_batched_skewed(reduce):
+    """Batched fp8 with expert runs past one 256-row tile, a K tail in GEMM1
+    (H % 128 = 80) and a column tail in GEMM2 (H < 256)."""
+    dev = GH.device()
+    cfg = W.BATCHED_FP8.scaled(name="batched_fp8_skew_packed", M=400, H=208, I=384, E=4,
+                               top_k=2)
+    inp = W.make_inputs(cfg, 1007)
+    counts = inp["expert_num_tokens"].cpu().numpy()
+    print(f"[case] packed fp8 batched reduce={reduce} counts={counts.tolist()}", flush=True)
+    assert counts.max() > 256
+    plain, _, _ = GH.run_batched(inp, dev, reduce=reduce, out_dtype=torch.float32)
+    packed, ws, info = GH.run_batched(inp, dev, reduce=reduce, out_dtype=torch.float32,
+                                      packed=True)
+    rows, experts = GH.batched_rows(inp)
+    if reduce:
+        assert torch.equal(plain, packed)
+    else:
+        idx = torch.as_tensor(rows, device=dev)
+        assert torch.equal(plain.reshape(-1, cfg.H)[idx], packed.reshape(-1, cfg.H)[idx])
+        import oracle
+        acts = oracle.Acts(inp["hidden"].cpu(), quantize=True)
+        o_ref, _ = oracle.expert_rows(GH.oracle_experts(inp), acts, rows, experts)
+        got = packed.reshape(-1, cfg.H)[idx].cpu().numpy()
+        GH.compare(cfg, got, o_ref, "packed fp8 batched rows")

@@ -241,3 +241,36 @@ def test_route_align_paths(case):
     ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
     tokens = None if M <= 64 else np.arange(0, M, max(1, M // 48))
     GH.check_output(inp, out, ids_o, w_o, tokens=tokens, what=name)
+
+
+def test_fp8_activation_codes_bit_exact():
+    """The in-path per-token fp8 quantisation (scale = amax / 448, RNE,
+    saturating) produces the oracle's codes and scales bit for bit: contiguous
+    rows by token, batched rows at their padded positions."""
+    import oracle
+    dev = GH.device()
+    cfg = W.MIXTRAL_PREFILL.scaled(name="contig_fp8_codes", M=96, H=208, I=256, weight="fp8")
+    inp = W.make_inputs(cfg, 81)
+    inp["hidden"][3] = 0.0                         # an all-zero row: scale 1, codes 0
+    _, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+    q_ref, s_ref = oracle.quant_rows_fp8(inp["hidden"].float().numpy())
+    q = GH.region(ws, info.off_aq, torch.uint8, cfg.M * cfg.H).reshape(cfg.M, cfg.H)
+    s = GH.region(ws, info.off_aq_scale, torch.float32, cfg.M)
+    assert np.array_equal(q, q_ref.reshape(cfg.M, cfg.H))
+    assert np.array_equal(s.view(np.uint32), np.asarray(s_ref, np.float32).view(np.uint32))
+
+    inp = W.make_inputs(BATCHED_SMALL, 1008)
+    _, ws, info = GH.run_batched(inp, dev, out_dtype=torch.float32)
+    T, H, BM = inp["max_tokens"], BATCHED_SMALL.H, info.block_m
+    counts = inp["expert_num_tokens"].cpu().numpy()
+    npp = int(GH.region(ws, info.off_num_post_padded, torch.int32, 1)[0])
+    q = GH.region(ws, info.off_aq, torch.uint8, npp * H).reshape(npp, H)
+    s = GH.region(ws, info.off_aq_scale, torch.float32, npp)
+    xb = inp["hidden"].float().numpy().reshape(-1, H)
+    p = 0
+    for e, c in enumerate(counts):
+        if c:
+            q_ref, s_ref = oracle.quant_rows_fp8(xb[e * T:e * T + c])
+            assert np.array_equal(q[p:p + c], q_ref.reshape(c, H)), e
+            assert np.array_equal(s[p:p + c], np.asarray(s_ref, np.float32)), e
+        p += -(-c // BM) * BM
