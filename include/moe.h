@@ -27,9 +27,10 @@
  *     dims of a [..., H] activation are flattened into M by the caller.
  *   - Expert ids are int32, routing weights float32.
  *   - All argument checks run on the host before anything is enqueued; on
- *     error nothing is enqueued.  Device-side preconditions (precomputed
- *     topk ids in [0, E), expert_num_tokens[e] <= max_tokens) are not checked
- *     on the device: violating them is undefined behaviour.
+ *     error nothing is enqueued.  Device-side data is not validated:
+ *     precomputed topk ids outside [0, E) (or [0, global_experts)) and
+ *     expert_map values outside [-1, E) contribute nothing; counts past
+ *     max_tokens are clamped.
  *   - Thread safety: concurrent calls are safe when they use distinct
  *     workspaces and outputs.
  */
@@ -68,7 +69,7 @@ typedef enum {
 /* Memory layout of w13 / w2 (see moe_pack_weights). */
 typedef enum {
     MOE_W_PLAIN = 0,          /* w13 [E, H, 2I], w2 [E, I, H], row-major          */
-    MOE_W_PACKED = 1          /* bf16 only: the blocked layout of moe_pack_weights */
+    MOE_W_PACKED = 1          /* bf16 / fp8: the blocked layouts of moe_pack_weights */
 } moe_weight_layout;
 
 /* Problem description (host struct).
@@ -109,7 +110,33 @@ typedef enum {
  *                weight-and-reduce); 0 writes the expert rows to out
  *                [E, max_tokens, H] instead.
  *   w_layout     MOE_W_PLAIN, or MOE_W_PACKED when w13 / w2 hold the output of
- *                moe_pack_weights (bf16 weights only; else MOE_ERR_UNSUPPORTED).
+ *                moe_pack_weights (bf16 or fp8 weights; else MOE_ERR_UNSUPPORTED).
+ *   global_experts
+ *                contiguous only.  0: the E experts of w13 / w2 are all the
+ *                experts.  > 0: routing runs over global_experts experts
+ *                (logits [M, global_experts], topk ids in [0, global_experts))
+ *                of which this device holds the E of w13 / w2, named by
+ *                args->expert_map [global_experts]: the local index of each
+ *                global expert, or -1 for an expert held elsewhere (the
+ *                expert-parallel shard of the FlagGems walkthrough, whose
+ *                kernel writes zeros for an expert id of -1, and of the vLLM
+ *                page's expert map).  Routed items of unmapped experts add
+ *                nothing to out, which then holds this shard's partial sum;
+ *                the workspace topk ids stay global, align counts, sorted ids
+ *                and expert ids are local.  Needs global_experts >= E; the
+ *                routing constraints apply to global_experts.
+ *   apply_weight_on_input
+ *                contiguous only.  0: the routing weight scales each expert
+ *                output o_r (b2 included).  1: it scales the expert's
+ *                intermediate z_r = SiLU(gate) * up before the second GEMM
+ *                and the outputs are summed unweighted (the walkthrough's
+ *                apply_router_weight_on_input switch, sec. 1.2; equal to 0
+ *                when there is no b2, since W2^T (a z) = a W2^T z).
+ *   chunk_tokens contiguous only.  0: one pass over all M tokens.  > 0: the
+ *                tokens are processed in chunks of chunk_tokens rows, one
+ *                after another on the stream (the walkthrough's CHUNK_SIZE
+ *                execution), and the workspace is sized for one chunk; its
+ *                regions then hold the last chunk's intermediates.
  */
 typedef struct {
     int32_t format;
@@ -121,6 +148,9 @@ typedef struct {
     int32_t has_w13_bias, has_w2_bias;
     int32_t batched_reduce;
     int32_t w_layout;
+    int32_t global_experts;
+    int32_t apply_weight_on_input;
+    int32_t chunk_tokens;
 } moe_problem;
 
 /* Workspace layout chosen by the library for one problem.  All offsets are
@@ -174,7 +204,10 @@ int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* info);
  *   out               contiguous / batched_reduce: [M, H]; batched: [E, max_tokens, H]
  *                     (only valid rows written).  out may alias hidden in the
  *                     contiguous format (in-place): every read of hidden
- *                     precedes the first write of out on the stream. */
+ *                     precedes the first write of out on the stream (per
+ *                     chunk, when chunk_tokens is set).
+ *   expert_map        global_experts > 0: [global_experts] int32, each value
+ *                     in [-1, E). */
 typedef struct {
     const void* hidden;
     const float* a_scale;
@@ -191,6 +224,7 @@ typedef struct {
     const float* w13_scale;
     const float* w2_scale;
     void* out;
+    const int32_t* expert_map;
 } moe_args;
 
 /* Enqueues one fused MoE forward on `stream` (a hipStream_t; NULL = the

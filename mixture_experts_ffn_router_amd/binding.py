@@ -37,7 +37,8 @@ class moe_problem(ctypes.Structure):
                 ("k_group", ctypes.c_int32), ("group_select_mode", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float), ("has_w13_bias", ctypes.c_int32),
                 ("has_w2_bias", ctypes.c_int32), ("batched_reduce", ctypes.c_int32),
-                ("w_layout", ctypes.c_int32)]
+                ("w_layout", ctypes.c_int32), ("global_experts", ctypes.c_int32),
+                ("apply_weight_on_input", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32)]
 
 
 class moe_workspace_info(ctypes.Structure):
@@ -53,7 +54,7 @@ class moe_args(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "hidden", "a_scale", "router_logits", "topk_ids", "topk_weights", "expert_num_tokens",
         "token_map", "token_map_w", "w13", "w2", "w13_bias", "w2_bias", "w13_scale", "w2_scale",
-        "out")]
+        "out", "expert_map")]
 
 
 class MoeError(RuntimeError):
@@ -206,6 +207,9 @@ class Problem:
     has_w2_bias: bool = False
     batched_reduce: bool = False
     w_layout: int = MOE_W_PLAIN
+    global_experts: int = 0
+    apply_weight_on_input: bool = False
+    chunk_tokens: int = 0
 
     def c(self) -> moe_problem:
         return moe_problem(self.fmt, self.M, self.H, self.I, self.E, self.top_k, self.max_tokens,
@@ -213,7 +217,8 @@ class Problem:
                            self.routing, int(self.renormalize), self.group_count, self.k_group,
                            self.group_select_mode, float(self.routed_scaling_factor),
                            int(self.has_w13_bias), int(self.has_w2_bias),
-                           int(self.batched_reduce), int(self.w_layout))
+                           int(self.batched_reduce), int(self.w_layout), int(self.global_experts),
+                           int(self.apply_weight_on_input), int(self.chunk_tokens))
 
 
 @dataclass
@@ -256,11 +261,12 @@ def _weights(w13, w2):
 
 def make_args(hidden, w13, w2, out, router_logits=None, topk_ids=None, topk_weights=None,
               w13_bias=None, w2_bias=None, w13_scale=None, w2_scale=None, a_scale=None,
-              expert_num_tokens=None, token_map=None, token_map_w=None) -> moe_args:
+              expert_num_tokens=None, token_map=None, token_map_w=None,
+              expert_map=None) -> moe_args:
     return moe_args(_ptr(hidden), _ptr(a_scale), _ptr(router_logits), _ptr(topk_ids),
                     _ptr(topk_weights), _ptr(expert_num_tokens), _ptr(token_map),
                     _ptr(token_map_w), _ptr(w13), _ptr(w2), _ptr(w13_bias), _ptr(w2_bias),
-                    _ptr(w13_scale), _ptr(w2_scale), _ptr(out))
+                    _ptr(w13_scale), _ptr(w2_scale), _ptr(out), _ptr(expert_map))
 
 
 def allocate_workspace(problem: Problem, device):
@@ -282,10 +288,13 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
               routing: str = "softmax", group_count: int = 1, k_group: int = 1,
               group_select_mode: int = 0, routed_scaling_factor: float = 1.0, w13_bias=None,
               w2_bias=None, topk_ids=None, topk_weights=None, w13_scale=None, w2_scale=None,
-              out_dtype=None, out=None, workspace=None):
+              out_dtype=None, out=None, workspace=None, expert_map=None,
+              apply_weight_on_input=False, chunk_tokens=0):
     """Contiguous-format forward on torch device tensors (the MindIE-SD
     page's fused_moe argument list, single device).  w13 may be a
-    PackedWeights (then w2 is ignored).  Returns (out, workspace tensor,
+    PackedWeights (then w2 is ignored).  expert_map [global experts] int32
+    makes this device an expert-parallel shard holding the E experts of w13
+    (routing over len(expert_map) experts).  Returns (out, workspace tensor,
     workspace info)."""
     import torch
     M = hidden.shape[0]
@@ -304,7 +313,9 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
                    k_group=k_group, group_select_mode=group_select_mode,
                    routed_scaling_factor=routed_scaling_factor,
                    has_w13_bias=w13_bias is not None, has_w2_bias=w2_bias is not None,
-                   w_layout=layout)
+                   w_layout=layout,
+                   global_experts=0 if expert_map is None else int(expert_map.numel()),
+                   apply_weight_on_input=apply_weight_on_input, chunk_tokens=chunk_tokens)
     if out is None:
         out = torch.empty(M, H, dtype=odt, device=hidden.device)
     if workspace is None:
@@ -313,7 +324,7 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
         info = moe_workspace_shapes(prob.c())
     args = make_args(hidden, w13, w2, out, router_logits=router_logits, topk_ids=topk_ids,
                      topk_weights=topk_weights, w13_bias=w13_bias, w2_bias=w2_bias,
-                     w13_scale=w13_scale, w2_scale=w2_scale)
+                     w13_scale=w13_scale, w2_scale=w2_scale, expert_map=expert_map)
     moe_forward(prob.c(), args, workspace.data_ptr(), workspace.numel(),
                 current_stream_handle(hidden.device))
     return out, workspace, info

@@ -17,6 +17,12 @@ static constexpr size_t ALIGN = 256;
 
 static size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
+// Tokens per pass of the contiguous forward (all M unless chunked).
+static int chunk_rows(const moe_problem* p)
+{
+    return (p->chunk_tokens > 0 && p->chunk_tokens < p->M) ? p->chunk_tokens : p->M;
+}
+
 static int validate(const moe_problem* p)
 {
     if (!p)
@@ -27,7 +33,7 @@ static int validate(const moe_problem* p)
         return MOE_ERR_INVALID_ARG;
     if (p->E > 1024)
         return MOE_ERR_UNSUPPORTED;
-    if (p->top_k > p->E)
+    if (p->top_k > (p->global_experts > p->E ? p->global_experts : p->E))
         return MOE_ERR_INVALID_ARG;          // top_k in [1, num_experts]
     if (p->top_k > 32)
         return MOE_ERR_UNSUPPORTED;
@@ -35,6 +41,7 @@ static int validate(const moe_problem* p)
         return MOE_ERR_UNSUPPORTED;
     if ((int64_t)p->M * p->top_k >= (1ll << 30) || (int64_t)p->H * p->I >= (1ll << 40))
         return MOE_ERR_UNSUPPORTED;
+    const int Er = p->global_experts > 0 ? p->global_experts : p->E;   // experts routed over
 
     // dtype combinations built here
     const int act = p->act_dtype, w = p->w_dtype, out = p->out_dtype;
@@ -59,7 +66,19 @@ static int validate(const moe_problem* p)
     if (p->w_layout == MOE_W_PACKED && w != MOE_BF16 && w != MOE_FP8_E4M3FN)
         return MOE_ERR_UNSUPPORTED;
 
+    if (p->global_experts < 0 || p->chunk_tokens < 0 || p->apply_weight_on_input < 0 ||
+        p->apply_weight_on_input > 1)
+        return MOE_ERR_INVALID_ARG;
+    if (p->global_experts > 0) {
+        if (p->global_experts < p->E)
+            return MOE_ERR_INVALID_ARG;
+        if (p->global_experts > 1024)
+            return MOE_ERR_UNSUPPORTED;
+    }
     if (p->format == MOE_FMT_BATCHED) {
+        // expert maps, input-side routing weights and chunking are contiguous-format features
+        if (p->global_experts || p->apply_weight_on_input || p->chunk_tokens)
+            return MOE_ERR_UNSUPPORTED;
         if (p->max_tokens < 1)
             return MOE_ERR_INVALID_ARG;
         if ((int64_t)p->E * p->max_tokens >= (1ll << 30))
@@ -82,16 +101,16 @@ static int validate(const moe_problem* p)
     const int G = p->group_count, kg = p->k_group;
     if (G < 1 || kg < 1 || kg > G)
         return MOE_ERR_INVALID_ARG;
-    if (p->E % G)
+    if (Er % G)
         return MOE_ERR_INVALID_ARG;
     if (p->group_select_mode != 0 && p->group_select_mode != 1)
         return MOE_ERR_INVALID_ARG;
     if (G > 1) {
         if (G > 64)
             return MOE_ERR_UNSUPPORTED;
-        if (p->top_k > kg * (p->E / G))
+        if (p->top_k > kg * (Er / G))
             return MOE_ERR_INVALID_ARG;
-        if (p->group_select_mode == 1 && p->E / G < 2)
+        if (p->group_select_mode == 1 && Er / G < 2)
             return MOE_ERR_INVALID_ARG;
     }
     return MOE_OK;
@@ -135,7 +154,7 @@ static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_
         return rc;
     moe_workspace_info w{};
     const bool batched = p->format == MOE_FMT_BATCHED;
-    const int64_t MK = (int64_t)p->M * p->top_k;
+    const int64_t MK = (int64_t)chunk_rows(p) * p->top_k;
     int64_t rows_cap = MK;
     if (batched) {
         rows_cap = (int64_t)p->E * p->max_tokens;
@@ -179,8 +198,8 @@ static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_
     const int cfg = choose_tile(p, rows_cap);
     const bool split = gemm2_k_split(
         cfg, p->format, p->batched_reduce,
-        expected_chunks(p->format, p->M, p->top_k, p->E, p->max_tokens, tile_rows(cfg)), p->H,
-        p->I, device_cus());
+        expected_chunks(p->format, chunk_rows(p), p->top_k, p->E, p->max_tokens, tile_rows(cfg)),
+        p->H, p->I, device_cus());
     off_o2 = take(split ? (size_t)orows * p->H * 4 : 0);
     w.bytes = off;
     *info = w;
@@ -200,7 +219,9 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
 {
     Plan P{};
     P.fmt = p->format;
-    P.M = p->M;
+    P.M = chunk_rows(p);
+    P.Er = p->global_experts > 0 ? p->global_experts : p->E;
+    P.w_on_input = p->apply_weight_on_input ? 1 : 0;
     P.H = p->H;
     P.I = p->I;
     P.E = p->E;
@@ -230,7 +251,7 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
     P.max_blocks = w.max_blocks;
     P.rows_cap = w.max_sorted_len - (int64_t)p->E * (w.block_m - 1);
     P.sentinel = (p->format == MOE_FMT_BATCHED) ? (int64_t)p->E * p->max_tokens
-                                                 : (int64_t)p->M * p->top_k;
+                                                 : (int64_t)P.M * p->top_k;
     P.topk_ids = (int32_t*)(ws + w.off_topk_ids);
     P.topk_w = (float*)(ws + w.off_topk_weights);
     P.counts = (int32_t*)(ws + w.off_expert_counts);
@@ -268,6 +289,8 @@ static int check_args(const moe_problem* p, const moe_args* a)
             return MOE_ERR_INVALID_ARG;
         return MOE_OK;
     }
+    if (p->global_experts > 0 && !a->expert_map)
+        return MOE_ERR_INVALID_ARG;
     if (p->routing == MOE_ROUTE_PRECOMPUTED) {
         if (!a->topk_ids || !a->topk_weights)
             return MOE_ERR_INVALID_ARG;
@@ -288,6 +311,9 @@ extern "C" int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* in
     return layout(p, info);
 }
 
+static int run_path(const moe_problem* p, const Plan& P, const moe_args& A, hipStream_t s,
+                    void** events);
+
 static int forward(const moe_problem* p, const moe_args* a, void* workspace,
                    size_t workspace_bytes, void* stream, void** events)
 {
@@ -304,7 +330,8 @@ static int forward(const moe_problem* p, const moe_args* a, void* workspace,
         return MOE_ERR_WORKSPACE;
 
     const hipStream_t s = (hipStream_t)stream;
-    const Plan P = make_plan(p, w, (char*)workspace, chunk_offs, cfg);
+    Plan P = make_plan(p, w, (char*)workspace, chunk_offs, cfg);
+    P.emap = a->expert_map;
     const bool batched = p->format == MOE_FMT_BATCHED;
     if (!batched && p->M == 0)
         return MOE_OK;                                   // nothing routed
@@ -315,6 +342,38 @@ static int forward(const moe_problem* p, const moe_args* a, void* workspace,
     // may come from an unrelated earlier call of the caller; clear it so the
     // checks below see only this call's launches
     (void)hipGetLastError();
+    if (batched || P.M == p->M)
+        return run_path(p, P, *a, s, events);
+    // chunked contiguous forward: the same path over token rows [c0, c0 + n)
+    const size_t aes = p->act_dtype == MOE_F32 ? 4 : 2;
+    const size_t oes = p->out_dtype == MOE_F32 ? 4 : 2;
+    const size_t les = p->logits_dtype == MOE_F32 ? 4 : 2;
+    for (int c0 = 0; c0 < p->M; c0 += P.M) {
+        Plan Pc = P;
+        Pc.M = (p->M - c0 < P.M) ? p->M - c0 : P.M;
+        moe_args ac = *a;
+        ac.hidden = (const char*)a->hidden + (size_t)c0 * p->H * aes;
+        ac.out = (char*)a->out + (size_t)c0 * p->H * oes;
+        if (p->routing == MOE_ROUTE_PRECOMPUTED) {
+            ac.topk_ids = a->topk_ids + (size_t)c0 * p->top_k;
+            ac.topk_weights = a->topk_weights + (size_t)c0 * p->top_k;
+        } else {
+            ac.router_logits = (const char*)a->router_logits + (size_t)c0 * P.Er * les;
+        }
+        const int rc2 = run_path(p, Pc, ac, s, events);
+        if (rc2 != MOE_OK)
+            return rc2;
+    }
+    return MOE_OK;
+}
+
+// The kernel sequence of one pass (P.M tokens of the contiguous format, or
+// the batched slabs).
+static int run_path(const moe_problem* p, const Plan& P, const moe_args& A, hipStream_t s,
+                    void** events)
+{
+    const moe_args* a = &A;
+    const bool batched = p->format == MOE_FMT_BATCHED;
     hipError_t err;
     int stage = 0;
     auto mark = [&](int st, int end) {
@@ -349,10 +408,10 @@ static int forward(const moe_problem* p, const moe_args* a, void* workspace,
     }
     if (p->w_dtype == MOE_FP8_E4M3FN && p->act_dtype != MOE_FP8_E4M3FN)
         MOE_TRY(MOE_STAGE_QUANT, launch_quant_rows(P, a->hidden, s));
-    MOE_TRY(MOE_STAGE_GEMM1, launch_gemm1(P, *a, s));
+    MOE_TRY(MOE_STAGE_GEMM1, launch_gemm1(P, *a, P.w_on_input ? weights : nullptr, s));
     MOE_TRY(MOE_STAGE_GEMM2, launch_gemm2(P, *a, s));
     if (!batched || p->batched_reduce)
-        MOE_TRY(MOE_STAGE_REDUCE, launch_reduce(P, *a, weights, s));
+        MOE_TRY(MOE_STAGE_REDUCE, launch_reduce(P, *a, P.w_on_input ? nullptr : weights, s));
 #undef MOE_TRY
     (void)stage;
     return MOE_OK;

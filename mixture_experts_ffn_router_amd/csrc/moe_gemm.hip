@@ -363,23 +363,22 @@ __device__ __forceinline__ void gemm1_tile(const Gemm1Args& g, char* smem, int e
             const int row = rb + tid / 8, c0 = (tid % 8) * 16;
             if (row >= nrows)
                 continue;                                // whole 8-lane groups skip together
+            const float rw = (row < rows) ? gemm1_row_w(g, (int64_t)r0 + row) : 1.0f;
             float v[16], amax = 0.0f;
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
-                v[c] = Zs[row * S::O_STRIDE + c0 + c];
+                v[c] = Zs[row * S::O_STRIDE + c0 + c] * rw;
                 amax = fmaxf(amax, fabsf(v[c]));
             }
             amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
             amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
             amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
-            const float sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+            const float sc = zq_scale(amax), rc = __builtin_amdgcn_rcpf(sc);
             uint32_t w[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                w[q] = (uint32_t)f32_to_fp8(v[4 * q] / sc) |
-                       ((uint32_t)f32_to_fp8(v[4 * q + 1] / sc) << 8) |
-                       ((uint32_t)f32_to_fp8(v[4 * q + 2] / sc) << 16) |
-                       ((uint32_t)f32_to_fp8(v[4 * q + 3] / sc) << 24);
+                w[q] = cvt_fp8x2(v[4 * q] * rc, v[4 * q + 1] * rc) |
+                       (cvt_fp8x2(v[4 * q + 2] * rc, v[4 * q + 3] * rc) << 16);
             const int64_t p = (int64_t)r0 + row;
             *(i32x4*)((uint8_t*)g.z + p * I + n0 + c0) =
                 i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
@@ -395,15 +394,18 @@ __device__ __forceinline__ void gemm1_tile(const Gemm1Args& g, char* smem, int e
                 continue;
             const int64_t p = (int64_t)r0 + row;
             const float* src = Zs + row * S::O_STRIDE + c0;
+            const float rw = (row < rows) ? gemm1_row_w(g, p) : 1.0f;
             if constexpr (DT == MOE_BF16) {
                 uint32_t w[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
-                    w[k] = f32_to_bf16(src[2 * k]) | ((uint32_t)f32_to_bf16(src[2 * k + 1]) << 16);
+                    w[k] = f32_to_bf16(src[2 * k] * rw) |
+                           ((uint32_t)f32_to_bf16(src[2 * k + 1] * rw) << 16);
                 *(i32x4*)((u16*)g.z + p * I + n0 + c0) =
                     i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
             } else {
-                *(f32x4*)((float*)g.z + p * I + n0 + c0) = f32x4{src[0], src[1], src[2], src[3]};
+                *(f32x4*)((float*)g.z + p * I + n0 + c0) =
+                    f32x4{src[0] * rw, src[1] * rw, src[2] * rw, src[3] * rw};
             }
         }
     }
@@ -974,8 +976,14 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
         // DMA touches before the next tile's first barrier (the prologue
         // above fills slots 0 .. NS-2), then written as 16-byte row chunks
         constexpr int ZS = S::BN / 2 + 8;               // staged row, bf16 elements
-        static_assert(S::CH * ZS * 2 <= S::STAGE, "z staging fits in one ring slot");
+        static_assert(S::CH * ZS * 2 + S::CH * 4 <= S::STAGE, "z staging fits in one ring slot");
         u16* Zs = (u16*)(ring + (S::NS - 1) * S::STAGE);
+        float* rws = (float*)(ring + (S::NS - 1) * S::STAGE + S::CH * ZS * 2);
+        if (g.row_w) {          // routing weights of the tile's rows, applied to z
+            for (int t = threadIdx.x; t < S::CH; t += S::NT)
+                rws[t] = (t < cur.rows) ? gemm1_row_w(g, (int64_t)cur.r0 + t) : 0.0f;
+            __syncthreads();
+        }
 #pragma unroll
         for (int fn = 0; fn < FH; ++fn) {
             const int zc = (cg * FH + fn) * 16 + s16;
@@ -986,8 +994,10 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int row = (rg * FMW + fm) * 16 + g4 * 4 + r;
-                    Zs[row * ZS + zc] =
-                        f32_to_bf16(silu_mul(acc[fm][fn][r] + bg[fn], acc[fm][fn + FH][r] + bu[fn]));
+                    float zv = silu_mul(acc[fm][fn][r] + bg[fn], acc[fm][fn + FH][r] + bu[fn]);
+                    if (g.row_w)
+                        zv *= rws[row];
+                    Zs[row * ZS + zc] = f32_to_bf16(zv);
                 }
             }
         }
@@ -1292,10 +1302,11 @@ static Sched make_sched(const Plan& P)
 //   TILE_MID       4 strips, CH 64
 //   TILE_DECODE    1 strip,  CH 16: a few rows per expert
 //   TILE_FP8       8 strips, CH 128, 128-column z groups
-hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s)
+hipError_t launch_gemm1(const Plan& P, const moe_args& A, const float* row_w, hipStream_t s)
 {
     Gemm1Args g{};
     g.s = make_sched(P);
+    g.row_w = row_w;
     const bool fp8 = P.wdt == MOE_FP8_E4M3FN;
     if (fp8) {
         if (P.act == MOE_FP8_E4M3FN) {           // batched, pre-quantised codes

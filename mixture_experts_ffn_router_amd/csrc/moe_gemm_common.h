@@ -20,9 +20,19 @@ __device__ __forceinline__ float load_bias(const void* b, int dt, int64_t idx)
     return (dt == MOE_BF16) ? bf16_to_f32(((const u16*)b)[idx]) : ((const float*)b)[idx];
 }
 
-// SiLU(g) * u with the hardware exponential (v_exp_f32 on a prescaled
-// argument, a few ulp): the epilogue's cost matters where the MFMAs are fast.
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// SiLU(g) * u = g / (1 + e^-g) * u with the hardware exponential and
+// reciprocal (v_exp_f32 on a prescaled argument, v_rcp_f32; a few ulp): the
+// epilogue's cost matters where the MFMAs are fast.
+__device__ __forceinline__ float silu_mul(float g, float u)
+{
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+// fp8 requantisation of z per (row, 128 columns): scale = amax / 448 (1 for
+// an all-zero group); the codes are RNE(z * rcp(scale)) with the hardware
+// reciprocal (1 ulp), one per group: against an exact division this can move
+// a code by one step only where z / scale lies within an ulp of a rounding tie.
+__device__ __forceinline__ float zq_scale(float amax) { return (amax > 0.0f) ? amax / 448.0f : 1.0f; }
 
 // ---------------------------------------------------------------- arguments
 struct Sched {
@@ -50,7 +60,17 @@ struct Gemm1Args {
     void* z;                    // [max_sorted, I]
     float* z_scale;             // fp8: [I/128][zs_ld] (group-major)
     int64_t zs_ld;              // fp8: floats from one z scale group to the next
+    const float* row_w;         // routing weight per routed item r (scales z), or null
 };
+
+// Routing weight of padded row p (1 without row weights; padding rows 0).
+__device__ __forceinline__ float gemm1_row_w(const Gemm1Args& g, int64_t p)
+{
+    if (!g.row_w)
+        return 1.0f;
+    const int sid = g.s.sorted[p];
+    return sid < g.s.sentinel ? g.row_w[sid] : 0.0f;
+}
 
 struct Gemm2Args {
     Sched s;

@@ -187,6 +187,7 @@ __device__ __forceinline__ void f8_zero(f32x4 (&acc)[F8_ROWS / 32][4])
 struct F8G1Src {
     int srow[F8S<false>::A_PW];     // per-lane A source rows, -1: padding
     int sa_row;                     // thread t < CH: source row of tile row t, -1: none
+    float rw;                       // thread t < CH: routing weight of tile row t (z scale)
 };
 
 __device__ __forceinline__ void f8_gemm1_rows(const Gemm1Args& g, const TileRef& t, int wave,
@@ -200,6 +201,7 @@ __device__ __forceinline__ void f8_gemm1_rows(const Gemm1Args& g, const TileRef&
     }
     const int tr = threadIdx.x;
     r.sa_row = (tr < S::CH && tr < t.rows) ? (int)gemm1_src_row(g, t.r0, tr) : -1;
+    r.rw = (tr < S::CH && tr < t.rows) ? gemm1_row_w(g, (int64_t)t.r0 + tr) : 0.0f;
 }
 
 __device__ __forceinline__ void f8_gemm1_src(const Gemm1Args& g, const TileRef& t,
@@ -231,6 +233,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
     typedef F8S<false> S;
     __shared__ __attribute__((aligned(16))) char ring[S::RING];
     __shared__ float rs[2][S::CH];                  // activation row scales, by tile parity
+    __shared__ float rws[2][S::CH];                 // routing weights of the rows (z scale)
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rg = wave / S::CG, cg = wave % S::CG;
@@ -246,8 +249,10 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
     f8_gemm1_rows(g, cur, wave, lane, rows);
     F8Src<false> src;
     f8_gemm1_src(g, cur, rows, src);
-    if (tid < S::CH)
+    if (tid < S::CH) {
         rs[0][tid] = rows.sa_row >= 0 ? g.a_scale[rows.sa_row] : 0.0f;
+        rws[0][tid] = rows.rw;
+    }
     dma_prologue<S>(src, ring, 0, nk, wave);
 
     // B fragment columns within the stage's 256-column weight tile
@@ -286,6 +291,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
         f8_run<false>(src, ring, nk, wave, rg, bcol, lane, acc,
                       min(max(strips - rg * S::FMW, 0), S::FMW));
         pin(sn);
+        pin(rows.rw);
 #pragma unroll
         for (int fn = 0; fn < 2; ++fn) {
             pin(sg[fn]);
@@ -299,8 +305,10 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
                 pin(rows.srow[j]);
             f8_gemm1_src(g, nxt, rows, src);
             dma_prologue<S>(src, ring, 0, nk, wave);
-            if (tid < S::CH)
+            if (tid < S::CH) {
                 rs[parity ^ 1][tid] = sn;
+                rws[parity ^ 1][tid] = rows.rw;
+            }
         }
 
         // epilogue: z in registers, row amax across the 4 column waves through
@@ -315,13 +323,15 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = rg * S::FMW * 16 + fm * 16 + g4 * 4 + r;
-                const float sa = rs[parity][row];
+                const float sa = rs[parity][row], rw = rws[parity][row];
                 float m = 0.0f;
 #pragma unroll
                 for (int fn = 0; fn < 2; ++fn) {
                     const float hg = acc[fm][fn][r] * sa * sg[fn];
                     const float hu = acc[fm][fn + 2][r] * sa * su[fn];
                     acc[fm][fn][r] = silu_mul(hg + bg[fn], hu + bu[fn]);
+                    if (g.row_w)
+                        acc[fm][fn][r] *= rw;
                     m = fmaxf(m, fabsf(acc[fm][fn][r]));
                 }
                 m = grp_max<16>(m);
@@ -338,8 +348,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
                 const int row = rg * S::FMW * 16 + fm * 16 + g4 * 4 + r;
                 const float amax = fmaxf(fmaxf(amx[row], amx[S::CH + row]),
                                          fmaxf(amx[2 * S::CH + row], amx[3 * S::CH + row]));
-                const float sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
-                const uint32_t q = cvt_fp8x2(acc[fm][0][r] / sc, acc[fm][1][r] / sc);
+                const float sc = zq_scale(amax), rc = __builtin_amdgcn_rcpf(sc);
+                const uint32_t q = cvt_fp8x2(acc[fm][0][r] * rc, acc[fm][1][r] * rc);
                 zst[row * 128 + cg * 32 + s16] = (uint8_t)q;
                 zst[row * 128 + cg * 32 + 16 + s16] = (uint8_t)(q >> 8);
                 if (cg == 0 && s16 == 0 && row < cur.rows)

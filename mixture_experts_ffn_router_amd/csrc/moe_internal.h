@@ -198,7 +198,10 @@ inline int tile_rows(int cfg)
 
 // Host-computed description of one call: problem, tile choice, device pointers.
 struct Plan {
-    int fmt, M, H, I, E, K, T;      // K = top_k, T = max_tokens
+    int fmt, M, H, I, E, K, T;      // M: tokens of one pass, K = top_k, T = max_tokens
+    int Er;                         // experts routed over (global experts of a shard, else E)
+    const int32_t* emap;            // [Er] global -> local expert, -1: held elsewhere (or null)
+    int w_on_input;                 // routing weight scales z (GEMM1) instead of o (reduce)
     int act, wdt, outdt, lgdt, routing;
     int renorm, G, kg, gmode;
     float rsf;
@@ -269,7 +272,8 @@ hipError_t launch_router(const Plan& P, const void* logits, hipStream_t s);
 hipError_t launch_align(const Plan& P, const int32_t* ids, hipStream_t s);
 hipError_t launch_tilelist(const Plan& P, const int32_t* expert_num_tokens, hipStream_t s);
 hipError_t launch_quant_rows(const Plan& P, const void* hidden, hipStream_t s);
-hipError_t launch_gemm1(const Plan& P, const moe_args& A, hipStream_t s);
+// row_w: routing weight per routed item, applied to z in GEMM1's epilogue (or null)
+hipError_t launch_gemm1(const Plan& P, const moe_args& A, const float* row_w, hipStream_t s);
 hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s);
 hipError_t launch_reduce(const Plan& P, const moe_args& A, const float* topk_w, hipStream_t s);
 hipError_t launch_pack_weights(int E, int H, int I, const void* w13, const void* w2, void* p13,

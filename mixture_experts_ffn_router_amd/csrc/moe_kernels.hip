@@ -217,7 +217,7 @@ __global__ void __launch_bounds__(256) k_router(const void* __restrict__ logits,
 
 static RouteArgs route_args(const Plan& P)
 {
-    return RouteArgs{P.E, P.K, P.routing, P.renorm, P.G, P.kg, P.gmode, P.rsf};
+    return RouteArgs{P.Er, P.K, P.routing, P.renorm, P.G, P.kg, P.gmode, P.rsf};
 }
 
 // Lanes per token and experts per lane for E experts (grouped: whole waves).
@@ -236,7 +236,7 @@ static void route_shape(int E, int G, int& epl, int& lpt)
 hipError_t launch_router(const Plan& P, const void* logits, hipStream_t s)
 {
     int epl, lpt;
-    route_shape(P.E, P.G, epl, lpt);
+    route_shape(P.Er, P.G, epl, lpt);
     const int tpb = 4 * (64 / lpt);
     const dim3 grid((P.M + tpb - 1) / tpb), block(256);
     const RouteArgs R = route_args(P);
@@ -344,6 +344,8 @@ struct AlignOut {
     int32_t *counts, *offsets, *sorted, *expert_ids, *npp, *chunk_off, *chunk_expert, *inv;
     int E, BM, CH, sentinel, max_blocks;
     int64_t max_sorted;
+    const int32_t* emap;        // [Er] global -> local expert (-1: elsewhere), or null
+    int Er;                     // range of the routed ids
 };
 
 // LDS scratch of align_items (ints), after the item batch.
@@ -368,7 +370,9 @@ __device__ void align_items(const int32_t* __restrict__ ids_g, int n, int* ids_s
     const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
     const int nb = (n + cap - 1) / cap;
 
-    // item i of the current batch -> LDS (ids outside [0, E) become -1)
+    // item i of the current batch -> LDS as a local expert id: through the
+    // expert map when there is one; ids outside the routed range, unmapped
+    // experts and map values outside [0, E) become -1 (no row)
     auto load_batch = [&](int b0, int len) {
         for (int i0 = 0; i0 < len; i0 += 1024 * 8) {
             int v[8];
@@ -376,6 +380,11 @@ __device__ void align_items(const int32_t* __restrict__ ids_g, int n, int* ids_s
             for (int u = 0; u < 8; ++u) {
                 const int i = i0 + u * 1024 + tid;
                 v[u] = (i < len) ? ids_g[b0 + i] : -1;
+            }
+            if (O.emap) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    v[u] = (v[u] >= 0 && v[u] < O.Er) ? O.emap[v[u]] : -1;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
@@ -499,9 +508,10 @@ __device__ void align_items(const int32_t* __restrict__ ids_g, int n, int* ids_s
 
 static AlignOut align_out(const Plan& P)
 {
-    return AlignOut{P.counts,     P.offsets,      P.sorted_ids, P.expert_ids, P.npp,
-                    P.chunk_off,  P.chunk_expert, P.inv,        P.E,          P.BM,
-                    P.CH,         (int)P.sentinel, P.max_blocks, P.max_sorted};
+    return AlignOut{P.counts,     P.offsets,       P.sorted_ids,  P.expert_ids, P.npp,
+                    P.chunk_off,  P.chunk_expert,  P.inv,         P.E,          P.BM,
+                    P.CH,         (int)P.sentinel, P.max_blocks,  P.max_sorted, P.emap,
+                    P.Er};
 }
 
 __global__ void __launch_bounds__(1024) k_align(const int32_t* __restrict__ ids, int Mk, int cap,
@@ -681,7 +691,8 @@ hipError_t launch_quant_rows(const Plan& P, const void* hidden, hipStream_t s)
 
 // ============================================================ weight-and-reduce
 // Unpermute + top-k weight-and-reduce (vLLM page, TopKWeightAndReduce;
-// FlagGems moe_sum): y[t] = sum_{j ascending} w[t,j] * o[row(t,j)] in float32,
+// FlagGems moe_sum): y[t] = sum_{j ascending} w[t,j] * o[row(t,j)] in float32
+// (w null: weights of 1, when the routing weight was applied to z),
 // rounded once to the output type.  o holds each routed item's expert output
 // at its padded position: contiguous, row = inv[t*top_k + j] (the align
 // kernel's inverse permutation; -1 contributes nothing); batched,
@@ -720,7 +731,7 @@ __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int
                 } else {
                     row[u] = inv[(int64_t)t * K + j];
                 }
-                wj[u] = w[(int64_t)t * K + j];
+                wj[u] = w ? w[(int64_t)t * K + j] : 1.0f;
             }
         }
         f32x4 v[8];

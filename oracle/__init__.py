@@ -80,7 +80,7 @@ def load() -> ctypes.CDLL:
     lib.oracle_align.argtypes = [P, i64, i32, i32, P, P, i64, P, i64, P]
     lib.oracle_align.restype = ctypes.c_int
     lib.oracle_forward_tokens.argtypes = [ctypes.POINTER(_Experts), ctypes.POINTER(_Acts), i32,
-                                          P, P, P, i64, P, i32]
+                                          P, P, P, i64, P, i32, P, i32]
     lib.oracle_forward_tokens.restype = ctypes.c_int
     lib.oracle_expert_rows.argtypes = [ctypes.POINTER(_Experts), ctypes.POINTER(_Acts), P, P,
                                        i64, P, i32]
@@ -187,10 +187,14 @@ def group_keys(logits, group_count, group_select_mode, scoring="softmax"):
     return keys
 
 
-def align(topk_ids, E, block_m):
-    """Returns (counts [E], sorted_ids [num_post_padded], expert_ids [npp/BM], npp)."""
+def align(topk_ids, E, block_m, expert_map=None):
+    """Returns (counts [E], sorted_ids [num_post_padded], expert_ids [npp/BM], npp).
+    expert_map [global experts]: topk_ids are global ids, mapped to the E
+    local experts; items of experts mapped to -1 get no row."""
     lib = load()
     ids = _np(topk_ids, np.int32).ravel()
+    if expert_map is not None:
+        ids = np.ascontiguousarray(_np(expert_map, np.int32)[ids], dtype=np.int32)
     Mk = ids.size
     cap = Mk + E * (block_m - 1)
     counts = np.empty(E, np.int32)
@@ -246,10 +250,14 @@ class Acts:
         self.s = _Acts(dt, _ptr(self.data), _ptr(self.scale), int(quantize))
 
 
-def forward_tokens(experts: Experts, acts: Acts, topk_ids, topk_w, tokens=None, nthreads=0):
+def forward_tokens(experts: Experts, acts: Acts, topk_ids, topk_w, tokens=None, nthreads=0,
+                   expert_map=None, weight_on_input=False):
     """y[n] = sum_j w[t,j] f_{id[t,j]}(x_t) for t = tokens[n]; float64 [n, H].
-    Returns (y, threads_used)."""
+    expert_map [global experts]: ids are global and map to experts' rows, -1
+    for experts held elsewhere (left out).  weight_on_input: w scales z_r and
+    the expert outputs are summed unweighted.  Returns (y, threads_used)."""
     lib = load()
+    emap = None if expert_map is None else _np(expert_map, np.int32)
     ids = _np(topk_ids, np.int32)
     w = _np(topk_w, np.float64)
     M, K = ids.shape
@@ -257,7 +265,8 @@ def forward_tokens(experts: Experts, acts: Acts, topk_ids, topk_w, tokens=None, 
     y = np.empty((tok.size, experts.H), np.float64)
     used = lib.oracle_forward_tokens(ctypes.byref(experts.s), ctypes.byref(acts.s), K,
                                      ids.ctypes.data, w.ctypes.data, tok.ctypes.data, tok.size,
-                                     y.ctypes.data, int(nthreads))
+                                     y.ctypes.data, int(nthreads), _ptr(emap),
+                                     int(bool(weight_on_input)))
     return y, used
 
 

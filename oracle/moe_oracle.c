@@ -328,8 +328,10 @@ int oracle_group_keys(const oracle_routing* R, const void* logits, int64_t M, fl
 /* Stable sort of the Mk routed items r = t*top_k + j by expert, each
  * expert's run padded up to a multiple of BM with the sentinel Mk.
  *   counts[E], sorted_ids[>= num_post_padded], expert_ids[num_post_padded/BM],
- *   *num_post_padded.  Returns 0, or -1 when an id is out of [0, E) or the
- *   output capacity is too small. */
+ *   *num_post_padded.  An id of -1 marks an item whose expert is held by
+ *   another expert-parallel rank (the walkthrough's expert_id == -1): it gets
+ *   no row.  Returns 0, or -1 when an id is out of [-1, E) or the output
+ *   capacity is too small. */
 int oracle_align(const int32_t* ids, int64_t Mk, int32_t E, int32_t BM, int32_t* counts,
                  int32_t* sorted_ids, int64_t sorted_cap, int32_t* expert_ids, int64_t blocks_cap,
                  int32_t* num_post_padded)
@@ -338,6 +340,8 @@ int oracle_align(const int32_t* ids, int64_t Mk, int32_t E, int32_t BM, int32_t*
     for (int e = 0; e < E; ++e)
         counts[e] = 0;
     for (int64_t r = 0; r < Mk; ++r) {
+        if (ids[r] == -1)
+            continue;
         if (ids[r] < 0 || ids[r] >= E)
             return -1;
         counts[ids[r]]++;
@@ -432,10 +436,12 @@ static void requant_z(double* z, int64_t I)
     }
 }
 
-/* o = f_e(x): h = W13_e^T x + b13_e; z = SiLU(h[:I]) * h[I:]; o = W2_e^T z + b2_e.
+/* o = f_e(x): h = W13_e^T x + b13_e; z = a * SiLU(h[:I]) * h[I:]; o = W2_e^T z + b2_e.
+ * a = zscale: 1, or the routing weight when it is applied to the first
+ * layer's output (the walkthrough's apply_router_weight_on_input, sec. 1.2).
  * scratch: h[2I], z[I]. */
 static void expert_ffn(const oracle_experts* W, int e, const double* x, double* h, double* z,
-                       double* o)
+                       double* o, double zscale)
 {
     const int64_t H = W->H, I = W->I, N = 2 * (int64_t)W->I;
 
@@ -465,7 +471,7 @@ static void expert_ffn(const oracle_experts* W, int e, const double* x, double* 
 
     for (int64_t i = 0; i < I; ++i) {
         const double g = h[i], u = h[I + i];
-        z[i] = g / (1.0 + exp(-g)) * u; /* SiLU(g) = g * sigmoid(g) */
+        z[i] = zscale * (g / (1.0 + exp(-g)) * u); /* SiLU(g) = g * sigmoid(g) */
     }
     if (W->requant_z)
         requant_z(z, I);
@@ -498,10 +504,15 @@ static void expert_ffn(const oracle_experts* W, int e, const double* x, double* 
 /* Contiguous format.  For each listed token t: y[t] = sum_j w[t,j] f_{id[t,j]}(x_t),
  * j ascending, with (ids, weights) from oracle_route (or given).
  * tokens[n_tokens] index rows of the activations; y is [n_tokens][H] double.
+ * expert_map (may be NULL): global expert id -> index into W's experts, -1 for
+ * an expert held by another expert-parallel rank, whose items are left out
+ * (y is then this rank's partial sum).  weight_on_input: the routing weight
+ * scales z_r and the expert outputs are summed unweighted.
  * nthreads <= 0 keeps the OpenMP default.  Returns the thread count used. */
 int oracle_forward_tokens(const oracle_experts* W, const oracle_acts* A, int32_t top_k,
                           const int32_t* topk_ids, const double* topk_w, const int64_t* tokens,
-                          int64_t n_tokens, double* y, int32_t nthreads)
+                          int64_t n_tokens, double* y, int32_t nthreads,
+                          const int32_t* expert_map, int32_t weight_on_input)
 {
     int used = 1;
     fp8_table_init();
@@ -530,11 +541,20 @@ int oracle_forward_tokens(const oracle_experts* W, const oracle_acts* A, int32_t
             for (int64_t c = 0; c < H; ++c)
                 yt[c] = 0.0;
             for (int j = 0; j < top_k; ++j) {
-                const int e = topk_ids[t * top_k + j];
+                const int g = topk_ids[t * top_k + j];
+                const int e = expert_map ? expert_map[g] : g;
                 const double wj = topk_w[t * top_k + j];
-                expert_ffn(W, e, x, h, z, o);
-                for (int64_t c = 0; c < H; ++c)
-                    yt[c] += wj * o[c];
+                if (e < 0)
+                    continue;                       /* held by another rank */
+                if (weight_on_input) {
+                    expert_ffn(W, e, x, h, z, o, wj);
+                    for (int64_t c = 0; c < H; ++c)
+                        yt[c] += o[c];
+                } else {
+                    expert_ffn(W, e, x, h, z, o, 1.0);
+                    for (int64_t c = 0; c < H; ++c)
+                        yt[c] += wj * o[c];
+                }
             }
         }
         free(x);
@@ -573,7 +593,7 @@ int oracle_expert_rows(const oracle_experts* W, const oracle_acts* A, const int6
 #pragma omp for schedule(dynamic, 1)
         for (int64_t n = 0; n < n_rows; ++n) {
             load_row(A, H, rows[n], x, xf, q);
-            expert_ffn(W, experts[n], x, h, z, out + n * H);
+            expert_ffn(W, experts[n], x, h, z, out + n * H, 1.0);
         }
         free(x);
         free(xf);

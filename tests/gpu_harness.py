@@ -34,10 +34,11 @@ def region(ws: torch.Tensor, off: int, dtype, count: int) -> np.ndarray:
 
 
 def run_contiguous(inp: dict, dev, precomputed=None, out=None, inplace=False, out_dtype=None,
-                   packed=False):
+                   packed=False, **extra):
     """One forward of a contiguous workload; returns (out, ws, info).
     out_dtype=None keeps the workload's own output type; packed=True re-lays
-    the weights out with moe_pack_weights first."""
+    the weights out with moe_pack_weights first; extra keyword arguments go
+    to binding.fused_moe (expert_map, apply_weight_on_input, chunk_tokens)."""
     cfg: W.MoeConfig = inp["cfg"]
     hidden = inp["hidden"].to(dev)
     kw = dict(out_dtype=out_dtype, top_k=cfg.top_k, renormalize=cfg.renormalize, routing=cfg.scoring,
@@ -58,6 +59,7 @@ def run_contiguous(inp: dict, dev, precomputed=None, out=None, inplace=False, ou
         logits = inp["logits"].to(dev)
     if inplace:
         out = hidden
+    kw.update(extra)
     res = B.fused_moe(hidden, w13, w2, logits, out=out, **kw)
     torch.cuda.synchronize()
     return res

@@ -95,6 +95,21 @@ def _status(prob):
     (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_FP8_E4M3FN, I=144), B.MOE_ERR_UNSUPPORTED),
     (dict(w_layout=B.MOE_W_PACKED, act_dtype=B.MOE_F32, w_dtype=B.MOE_F32, out_dtype=B.MOE_F32),
      B.MOE_ERR_UNSUPPORTED),
+    # expert-parallel shard: routing over global_experts, E local experts
+    (dict(global_experts=32), B.MOE_OK),
+    (dict(global_experts=4), B.MOE_ERR_INVALID_ARG),              # fewer than E
+    (dict(global_experts=2048), B.MOE_ERR_UNSUPPORTED),
+    (dict(global_experts=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(global_experts=12, top_k=10), B.MOE_OK),                # top_k bound is global
+    (dict(global_experts=12, group_count=3, k_group=2), B.MOE_OK),   # groups split the global set
+    (dict(global_experts=12, group_count=8, k_group=2), B.MOE_ERR_INVALID_ARG),
+    (dict(fmt=B.MOE_FMT_BATCHED, max_tokens=8, global_experts=16), B.MOE_ERR_UNSUPPORTED),
+    (dict(apply_weight_on_input=1), B.MOE_OK),
+    (dict(apply_weight_on_input=2), B.MOE_ERR_INVALID_ARG),
+    (dict(fmt=B.MOE_FMT_BATCHED, max_tokens=8, apply_weight_on_input=1), B.MOE_ERR_UNSUPPORTED),
+    (dict(chunk_tokens=4), B.MOE_OK),
+    (dict(chunk_tokens=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(fmt=B.MOE_FMT_BATCHED, max_tokens=8, chunk_tokens=4), B.MOE_ERR_UNSUPPORTED),
 ])
 def test_problem_validation(kw, status):
     assert _status(_prob(**kw)) == status
@@ -144,6 +159,7 @@ def _args(**kw):
     (dict(), dict(routing=B.MOE_ROUTE_PRECOMPUTED), B.MOE_ERR_INVALID_ARG),
     (dict(), dict(w_dtype=B.MOE_FP8_E4M3FN), B.MOE_ERR_INVALID_ARG),      # scales missing
     (dict(), dict(fmt=B.MOE_FMT_BATCHED, max_tokens=8), B.MOE_ERR_INVALID_ARG),
+    (dict(), dict(global_experts=32), B.MOE_ERR_INVALID_ARG),       # expert_map missing
 ])
 def test_forward_rejects_missing_pointers(kw, pkw, status):
     p = _prob(**pkw).c()
@@ -196,3 +212,14 @@ def test_pack_rejects_null_pointers():
         B.MOE_ERR_INVALID_ARG
     assert lib.moe_pack_weights(ctypes.byref(p), fake, fake, fake, None, None) == \
         B.MOE_ERR_INVALID_ARG
+
+
+def test_chunked_workspace_is_sized_for_one_chunk():
+    full = B.moe_workspace_shapes(_prob(M=4096, H=256, I=512, top_k=2).c())
+    chunk = B.moe_workspace_shapes(_prob(M=4096, H=256, I=512, top_k=2, chunk_tokens=512).c())
+    one = B.moe_workspace_shapes(_prob(M=512, H=256, I=512, top_k=2).c())
+    assert chunk.bytes == one.bytes < full.bytes
+    assert chunk.max_sorted_len == 512 * 2 + 8 * 15
+    # a chunk larger than M is the unchunked problem
+    big = B.moe_workspace_shapes(_prob(M=100, chunk_tokens=4096).c())
+    assert big.bytes == B.moe_workspace_shapes(_prob(M=100).c()).bytes

@@ -473,3 +473,96 @@ def test_pages_example_shapes_run_through_brute_force():
         cand = [e for e in range(ex["num_experts"]) if e // per in grp]
         assert set(ids[t]) == _dominant_subset(s, cand, ex["top_k"])
         assert np.isclose(w[t].sum(), ex["routed_scaling_factor"], rtol=1e-13)
+
+
+# ----------------------------------------------------------------- expert-parallel shards
+
+def _ep_case(seed, M=11, H=24, I=32, E=8, K=3):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(M, H, generator=g)
+    W13 = torch.randn(E, H, 2 * I, generator=g) / math.sqrt(H)
+    W2 = torch.randn(E, I, H, generator=g) / math.sqrt(I)
+    b13 = 0.1 * torch.randn(E, 2 * I, generator=g)
+    b2 = 0.1 * torch.randn(E, H, generator=g)
+    ids, w = oracle.route(torch.randn(M, E, generator=g), K, renormalize=True)
+    return x, W13, W2, b13, b2, ids, w
+
+
+@pytest.mark.parametrize("R", [2, 4])
+def test_expert_shards_sum_to_the_full_layer(R):
+    """Each of R ranks holds E/R experts (expert_map: global -> local, -1
+    elsewhere); the rank outputs are partial sums whose total is the
+    unsharded layer, and each rank's part is the sum over its own experts."""
+    x, W13, W2, b13, b2, ids, w = _ep_case(31 + R)
+    E = W13.shape[0]
+    full, _ = oracle.forward_tokens(oracle.Experts(W13, W2, w13_bias=b13, w2_bias=b2),
+                                    oracle.Acts(x), ids, w)
+    total = np.zeros_like(full)
+    per = E // R
+    for rank in range(R):
+        own = np.arange(rank * per, (rank + 1) * per)
+        emap = np.full(E, -1, np.int32)
+        emap[own] = np.arange(per)
+        ex = oracle.Experts(W13[own], W2[own], w13_bias=b13[own], w2_bias=b2[own])
+        part, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w, expert_map=emap)
+        # the part equals the full layer with the other experts' weights zeroed
+        w_own = np.where(np.isin(ids, own), w, 0.0)
+        ref, _ = oracle.forward_tokens(oracle.Experts(W13, W2, w13_bias=b13, w2_bias=b2),
+                                       oracle.Acts(x), ids, w_own)
+        assert np.allclose(part, ref, rtol=1e-13, atol=1e-14)
+        total += part
+    assert np.allclose(total, full, rtol=1e-12, atol=1e-13)
+
+
+def test_expert_map_identity_and_empty_shard():
+    x, W13, W2, b13, b2, ids, w = _ep_case(41)
+    E = W13.shape[0]
+    ex = oracle.Experts(W13, W2, w13_bias=b13, w2_bias=b2)
+    full, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w)
+    ident, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w,
+                                     expert_map=np.arange(E, dtype=np.int32))
+    assert np.array_equal(full, ident)
+    none, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w,
+                                    expert_map=np.full(E, -1, np.int32))
+    assert not none.any()
+
+
+def test_align_with_expert_map_against_stable_argsort():
+    """Mapped align: items of experts held elsewhere get no row; the rest
+    keep routed-index order within each local expert."""
+    rng = np.random.default_rng(5)
+    Eg, E, BM, Mk = 16, 5, 16, 700
+    ids = rng.integers(0, Eg, size=Mk).astype(np.int32)
+    emap = np.full(Eg, -1, np.int32)
+    emap[[2, 3, 7, 11, 12]] = [4, 0, 1, 2, 3]          # any order of local slots
+    counts, sorted_ids, expert_ids, npp = oracle.align(ids, E, BM, expert_map=emap)
+    loc = emap[ids]
+    assert np.array_equal(counts, np.bincount(loc[loc >= 0], minlength=E))
+    real = sorted_ids[sorted_ids < Mk]
+    keep = np.flatnonzero(loc >= 0)
+    assert np.array_equal(real, keep[np.argsort(loc[keep], kind="stable")])
+    assert npp == (-(-counts // BM) * BM).sum()
+
+
+# ----------------------------------------------------------------- weight on input
+
+def test_weight_on_input_equals_output_weight_without_b2():
+    """The walkthrough (sec. 1.2): W^T (a z) = a W^T z, so scaling z_r instead
+    of o_r gives the same layer when there is no b2."""
+    x, W13, W2, b13, _, ids, w = _ep_case(51)
+    ex = oracle.Experts(W13, W2, w13_bias=b13)
+    y_out, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w)
+    y_in, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w, weight_on_input=True)
+    assert np.allclose(y_in, y_out, rtol=1e-12, atol=1e-13)
+
+
+def test_weight_on_input_with_b2_closed_form():
+    """With b2 the two placements differ by sum_j (1 - w_j) b2[e_j]: the bias
+    is added unweighted when the weight scales z."""
+    x, W13, W2, b13, b2, ids, w = _ep_case(52)
+    ex = oracle.Experts(W13, W2, w13_bias=b13, w2_bias=b2)
+    y_out, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w)
+    y_in, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w, weight_on_input=True)
+    diff = ((1.0 - w)[:, :, None] * b2.double().numpy()[ids]).sum(1)
+    assert np.allclose(y_in - y_out, diff, rtol=1e-10, atol=1e-12)
+    assert np.abs(diff).max() > 1e-3
