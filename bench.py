@@ -104,7 +104,8 @@ def main():
         print(json.dumps({"copy_probe_bytes": src.numel(), "launches": 5}), flush=True)
         return
     cfg = W.BY_NAME[args.workload]
-    seed = args.seed if args.seed is not None else 1000 + W.CONFIGS.index(cfg)
+    seed = args.seed if args.seed is not None else (
+        1000 + W.CONFIGS.index(cfg) if cfg in W.CONFIGS else 1100 + W.EXTRA.index(cfg))
     print(f"[bench] {cfg.name}: generating inputs (seed {seed})", file=sys.stderr, flush=True)
     inp = W.make_inputs(cfg, seed, device=dev)
     batched = cfg.fmt == "batched"
@@ -125,7 +126,10 @@ def main():
                             w13_scale=inp.get("w13_scale"), w2_scale=inp.get("w2_scale"))
     else:
         hidden = inp["hidden"]
-        prob = B.Problem(M=cfg.M, H=cfg.H, I=cfg.I, E=cfg.E, top_k=cfg.top_k,
+        emap = inp.get("expert_map")
+        E_local = inp["w13"].shape[0]
+        prob = B.Problem(M=cfg.M, H=cfg.H, I=cfg.I, E=E_local, top_k=cfg.top_k,
+                         global_experts=0 if emap is None else cfg.E,
                          act_dtype=B._dtype_code(hidden), w_dtype=B._dtype_code(inp["w13"]),
                          out_dtype=B._dtype_code(torch.empty(0, dtype=out_dt)),
                          logits_dtype=B._dtype_code(inp["logits"]),
@@ -139,7 +143,8 @@ def main():
         out = torch.empty(cfg.M, cfg.H, dtype=out_dt, device=dev)
         cargs = B.make_args(hidden, inp["w13"], inp["w2"], out, router_logits=inp["logits"],
                             w13_bias=inp["w13_bias"], w2_bias=inp["w2_bias"],
-                            w13_scale=inp.get("w13_scale"), w2_scale=inp.get("w2_scale"))
+                            w13_scale=inp.get("w13_scale"), w2_scale=inp.get("w2_scale"),
+                            expert_map=emap)
     ws, info = B.allocate_workspace(prob, dev)
     stream = B.current_stream_handle(dev)
     hip = HipEvents()
@@ -214,8 +219,8 @@ def main():
         valid_rows = int(counts.sum())
     else:
         off = info.off_expert_counts
-        counts = ws[off:off + 4 * cfg.E].view(torch.int32).cpu().numpy()
-        valid_rows = cfg.M * cfg.top_k
+        counts = ws[off:off + 4 * prob.E].view(torch.int32).cpu().numpy()
+        valid_rows = int(counts.sum())          # M * top_k, or this shard's routed rows
     active = int((counts > 0).sum())
     wes = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight]
     aes = {"f32": 4, "bf16": 2}[cfg.act]
@@ -272,7 +277,8 @@ def main():
                    "k_group": cfg.k_group, "group_select_mode": cfg.group_select_mode,
                    "routed_scaling_factor": cfg.routed_scaling_factor, "bias": cfg.bias,
                    "block_m": info.block_m, "active_experts": active,
-                   "valid_rows": valid_rows},
+                   "valid_rows": valid_rows,
+                   **({"local_experts": cfg.local_experts} if cfg.local_experts else {})},
         "active_tflops": round(flops / t_step / 1e12, 2),
         "hbm_gbs_path": round(path_bytes / t_step / 1e9, 1),
         "path_roofline": {"bytes": int(path_bytes), "flops": flops,
@@ -347,8 +353,11 @@ def cpu_baseline(cfg, inp, info, sample):
                           group_count=cfg.group_count, k_group=cfg.k_group,
                           group_select_mode=cfg.group_select_mode,
                           routed_scaling_factor=cfg.routed_scaling_factor)
-    oracle.align(ids, cfg.E, info.block_m)
-    _, used = oracle.forward_tokens(ex, acts, ids, w, tokens=np.arange(n), nthreads=threads)
+    emap = inp.get("expert_map")
+    emap = None if emap is None else emap.cpu().numpy()
+    oracle.align(ids, inp["w13"].shape[0], info.block_m, expert_map=emap)
+    _, used = oracle.forward_tokens(ex, acts, ids, w, tokens=np.arange(n), nthreads=threads,
+                                    expert_map=emap)
     dt = time.perf_counter() - t0
     return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": used, "kind": "oracle",
             "sample": f"routing + align of all {cfg.M} tokens, expert FFN of the first {n} "

@@ -46,6 +46,8 @@ class MoeConfig:
     expert_bias_var: float = 0.0     # per-expert logit offset ~ N(0, var)
     zipf_s: float = 0.0              # per-expert logit offset -s*ln(rank+1)
     max_tokens: int = 0              # batched: rows per expert slab (0 = M)
+    local_experts: int = 0           # > 0: an expert-parallel shard holding experts
+                                     # [0, local_experts) of the E routed over
 
     @property
     def logits_dtype(self) -> str:
@@ -81,7 +83,14 @@ BATCHED_FP8 = MoeConfig("batched_fp8_skewed", M=8192, H=2048, I=1408, E=64, top_
                         fmt="batched", weight="fp8", renormalize=False, zipf_s=1.1)
 
 CONFIGS = [TINY_F32, MIXTRAL_PREFILL, DECODE_SMALL_EXPERTS, DEEPSEEK_GROUPED, BATCHED_FP8]
-BY_NAME = {c.name: c for c in CONFIGS}
+
+# One rank of the DeepSeek-like layer under 8-way expert parallelism: the
+# tokens of all 8 ranks (8 x 4096) are routed over the 256 experts and this
+# rank holds 32 of them, about 1024 rows each (the MFMA-bound share).
+EP8_SHARD = DEEPSEEK_GROUPED.scaled(name="ep8_shard_deepseek_bf16", M=32768, local_experts=32)
+
+EXTRA = [EP8_SHARD]
+BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -122,6 +131,11 @@ def make_inputs(cfg: MoeConfig, seed: int, device="cpu") -> dict:
     logits = logits.to(_TORCH_DT[cfg.logits_dtype])
 
     w_dt = torch.float32 if cfg.weight == "fp8" else _TORCH_DT[cfg.weight]
+    if cfg.local_experts:                       # the shard's experts only
+        E = cfg.local_experts
+        emap = torch.full((cfg.E,), -1, dtype=torch.int32, device=device)
+        emap[:E] = torch.arange(E, dtype=torch.int32, device=device)
+        out["expert_map"] = emap
     w13 = _randn((E, H, 2 * I), gen, device, std=1.0 / math.sqrt(H), dtype=w_dt)
     w2 = _randn((E, I, H), gen, device, std=1.0 / math.sqrt(I), dtype=w_dt)
     if cfg.weight == "fp8":

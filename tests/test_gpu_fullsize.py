@@ -62,3 +62,34 @@ def test_full_size_batched_fp8(packed):
     GH.check_rounded(out16.reshape(-1, cfg.H)[idx], out.reshape(-1, cfg.H)[idx])
     # invalid (NaN-filled) rows never leak into valid outputs
     assert torch.isfinite(out.reshape(-1, cfg.H)[idx]).all()
+
+
+def test_full_size_ep8_shard():
+    """One rank of the DeepSeek-like layer under 8-way expert parallelism
+    (32768 tokens routed over 256 experts, 32 held here), in the launch
+    configuration the benchmark times: global ids and local align bit for
+    bit, sampled output rows against the oracle's partial sums."""
+    cfg = W.EP8_SHARD
+    dev = GH.device()
+    seed = 1100 + W.EXTRA.index(cfg)
+    print(f"[case] {cfg.name} seed={seed} generating", flush=True)
+    inp = W.make_inputs(cfg, seed, device=dev)
+    emap = inp["expert_map"]
+    out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, expert_map=emap)
+    ids_o, w_o = GH.oracle_route(inp)
+    M, K, E = cfg.M, cfg.top_k, cfg.local_experts
+    ids_g = GH.region(ws, info.off_topk_ids, torch.int32, M * K).reshape(M, K)
+    assert np.array_equal(ids_g, ids_o)
+    emap_np = emap.cpu().numpy()
+    counts_o, sorted_o, eids_o, npp_o = oracle.align(ids_o, E, info.block_m, expert_map=emap_np)
+    npp = int(GH.region(ws, info.off_num_post_padded, torch.int32, 1)[0])
+    assert npp == npp_o
+    assert np.array_equal(GH.region(ws, info.off_expert_counts, torch.int32, E), counts_o)
+    assert np.array_equal(GH.region(ws, info.off_sorted_ids, torch.int32, npp), sorted_o)
+    print(f"[case] {cfg.name} local rows={int(counts_o.sum())} max/expert={counts_o.max()}",
+          flush=True)
+    tokens = _sample_tokens(M)
+    acts = oracle.Acts(inp["hidden"].cpu())
+    y, _ = oracle.forward_tokens(GH.oracle_experts(inp), acts, ids_o, w_o, tokens=tokens,
+                                 expert_map=emap_np)
+    GH.compare(cfg, out.cpu().numpy()[tokens], y, what="ep8 shard")
