@@ -298,16 +298,27 @@ def main():
     print(json.dumps(res), flush=True)
 
 
+GEMM_SOURCES = ("moe_gemm_common.h", "moe_gemm.hip", "moe_gemm_fp8.hip")
+
+
+def gemm_source_sha():
+    """SHA-256 over the grouped-GEMM sources (in this order), the code the
+    committed counter summaries were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_ffn_router_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def profile_traffic(workload):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size),
     or (None, None, None) when no summary was taken on the current GEMM source."""
     import glob
-    import hashlib
     import re
-    src = os.path.join(ROOT, "mixture_experts_ffn_router_amd", "csrc", "moe_gemm.hip")
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    sha = gemm_source_sha()
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}.md"))):
         with open(path) as f:
             text = f.read()
