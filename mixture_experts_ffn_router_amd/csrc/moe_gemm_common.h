@@ -92,16 +92,30 @@ struct Gemm2Args {
 };
 
 // ---------------------------------------------------------------- tile schedule
-// Persistent, XCD-aware schedule.  Logical tiles are ordered by expert, then
-// column block, then the expert's row chunks, so the chunks of one expert
-// that share a weight tile are neighbours.  Workgroups are dealt round-robin
-// over the 8 XCDs (workgroup b runs on XCD b % 8), so XCD x is given the
-// contiguous range [x R/8, (x+1) R/8) of the R tiles and walks it with its own
+// Persistent, XCD-aware schedule.  Workgroups are dealt round-robin over the
+// 8 XCDs (workgroup b runs on XCD b % 8), so XCD x is given the contiguous
+// range [x R/8, (x+1) R/8) of the R logical tiles and walks it with its own
 // workgroups: neighbouring tiles run together on one XCD and share its L2.
+//
+// Sharing through L2 only works between tiles that stream the same operand
+// within a few K stages of each other (at full HBM rate an XCD's 4 MB L2
+// turns over in a few microseconds).  Two rules keep the tiles that share an
+// operand in step:
+//  - an expert's rows are split into its nch chunks as evenly as 16-row
+//    strips allow (rather than full chunks plus a ragged tail), so the
+//    chunks that share a weight tile have the same work and run at the same
+//    speed;
+//  - within an expert, tiles are ordered by groups of up to 8 chunks, then
+//    column block, then the chunk in the group, so the tiles running at once
+//    on an XCD form a block of about 8 chunks x 8 column blocks: each weight
+//    tile is read by the group's chunks together and each activation chunk by
+//    the neighbouring column blocks together.
 struct TileRef {
     int e, r0, rows, ntile;     // expert, first padded row, real rows (>= 1), column block
     int base;                   // first padded row of the expert's run
 };
+
+constexpr int TILE_GROUP = 8;   // chunks walked together over the column blocks
 
 template <int CH>
 struct TileIter {
@@ -125,9 +139,25 @@ struct TileIter {
         const int e = s.chunk_expert[L / nt];
         const int c0 = s.chunk_off[e], nch = s.chunk_off[e + 1] - c0;
         const int local = L - c0 * nt;
-        const int j = local % nch;
+        // chunk group: full groups of TILE_GROUP chunks, then the remainder
+        const int full = nch / TILE_GROUP;
+        int j, ntile;
+        if (local < full * TILE_GROUP * nt) {
+            const int grp = local / (TILE_GROUP * nt), rem = local - grp * TILE_GROUP * nt;
+            ntile = rem / TILE_GROUP;
+            j = grp * TILE_GROUP + rem % TILE_GROUP;
+        } else {
+            const int rem = local - full * TILE_GROUP * nt, gc = nch - full * TILE_GROUP;
+            ntile = rem / gc;
+            j = full * TILE_GROUP + rem % gc;
+        }
+        // chunk j's rows: U = ceil(count / 16) strips dealt out evenly, the
+        // first U % nch chunks one strip more.  nch = ceil(count / CH) makes
+        // every chunk hold between 1 and CH rows, and starts stay 16-row aligned.
+        const int cnt = s.counts[e], U = (cnt + 15) >> 4, q = U / nch, extra = U - q * nch;
+        const int u0 = j * q + min(j, extra);
         const int base = s.offsets[e];
-        t = TileRef{e, base + j * CH, min(CH, s.counts[e] - j * CH), local / nch, base};
+        t = TileRef{e, base + 16 * u0, min(16 * (q + (j < extra)), cnt - 16 * u0), ntile, base};
         L += per;
         return true;
     }

@@ -316,17 +316,20 @@ __device__ __forceinline__ int upper_index(const int* a, int n, int x)
     return lo;
 }
 
-// GEMM work unit lists: expert e's padded run is cut into chunks of CH rows
-// (the row height of one GEMM tile).  chunk_off[e] = chunks of experts < e,
+// GEMM work unit lists: expert e's rows need ceil(rows / CH) chunks of at
+// most CH rows (the row height of one GEMM tile); how the rows are dealt out
+// to the chunks is the GEMM schedule's business.  Counting the real rows, not
+// the BM-padded run, matters: a chunk made only of padding would still stream
+// the expert's whole weight tile.  chunk_off[e] = chunks of experts < e,
 // chunk_off[E] = all chunks, chunk_expert[c] = expert of chunk c.  Called by
-// all 1024 threads; `padded` is this thread's expert run (0 for e >= E);
+// all 1024 threads; `rows` is this thread's expert's row count (0 for e >= E);
 // choff: E + 1 ints of LDS scratch.
-__device__ void write_chunks(int padded, int CH, int E, int* sh_tot, int* choff,
+__device__ void write_chunks(int rows, int CH, int E, int* sh_tot, int* choff,
                              int32_t* chunk_off, int32_t* chunk_expert)
 {
     const int e = threadIdx.x;
     __syncthreads();   // sh_tot is reused from the previous scan
-    const int nch = (e < E) ? (padded + CH - 1) / CH : 0;
+    const int nch = (e < E) ? (rows + CH - 1) / CH : 0;
     int cstart;
     const int ctotal = block_exclusive_scan_1024(nch, sh_tot, &cstart);
     if (e < E) {
@@ -456,7 +459,7 @@ __device__ void align_items(const int32_t* __restrict__ ids_g, int n, int* ids_s
         offs[E] = total;
         *O.npp = total;
     }
-    write_chunks(padded, O.CH, E, tot, choff, O.chunk_off, O.chunk_expert);
+    write_chunks((e < E) ? total_e : 0, O.CH, E, tot, choff, O.chunk_off, O.chunk_expert);
     for (int b = tid; b < total / BM && b < O.max_blocks; b += 1024)
         O.expert_ids[b] = upper_index(offs, E, b * BM);
 
@@ -579,7 +582,7 @@ __global__ void __launch_bounds__(1024) k_tilelist(const int32_t* __restrict__ e
         sh_start[E] = total;
         *npp = fits ? total : 0;
     }
-    write_chunks(fits ? padded : 0, CH, E, tot, choff, chunk_off, chunk_expert);
+    write_chunks(fits ? c : 0, CH, E, tot, choff, chunk_off, chunk_expert);
     if (!fits)
         return;
     for (int b = threadIdx.x; b < total / BM; b += 1024)
