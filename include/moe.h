@@ -262,7 +262,9 @@ int moe_forward_timed(const moe_problem* p, const moe_args* a, void* workspace,
  * GEMMs stream them (the walkthrough's "fused_moe_kernel" section reads each
  * weight tile as a K x BLOCK_SIZE_N block; packing makes every such block of
  * one K stage contiguous in memory).  The packed layout is a sequence of
- * 16 KiB blocks, each 64 weight rows (K) x 128 weight columns (N) of bf16:
+ * 16 KiB blocks.
+ *
+ * bf16 weights: each block is 64 weight rows (K) x 128 weight columns (N):
  *   row k of a block is 256 bytes = 16 slots of 16 bytes; slot s holds the
  *   8-column chunk c = s ^ (2 * ((k & 3) | ((k >> 1) & 4))) of that row.
  *   w13: block (e, kt, j), kt < ceil(H / 64), j < ceil(I / 64), in that order
@@ -271,11 +273,22 @@ int moe_forward_timed(const moe_problem* p, const moe_args* a, void* workspace,
  *        I + 64 j + 8 (c - 8) .., of weight rows 64 kt + k.
  *   w2:  block (e, kt, j), kt < ceil(I / 64), j < ceil(H / 128); chunk c holds
  *        columns 128 j + 8 c .. of weight rows 64 kt + k.
- *   Rows past H (w13) / I (w2) and columns past I (w13) / H (w2) are zero.
+ * fp8 weights (K-contiguous): each block is 128 weight columns (N) x 128
+ *   weight rows (K) of one-byte codes: column n of a block is 128 bytes =
+ *   8 slots of 16 bytes; slot s holds the codes of weight rows
+ *   128 kt + 16 q .. + 15 with q = s ^ ((n >> 1) & 7).
+ *   w13: block (e, kt, j), kt < ceil(H / 128), j < I / 64, j fastest; block
+ *        columns 0-63 are gate columns 64 j .., 64-127 the up columns
+ *        I + 64 j ...
+ *   w2:  block (e, kt, j), kt < I / 128, j < ceil(H / 128); block column n
+ *        is weight column 128 j + n.
+ *   The per-channel scales are not packed.
+ * In both, rows past H (w13) / I (w2) and columns past I (w13) / H (w2) are
+ * zero.
  *
  * moe_packed_weight_bytes: sizes of the two packed buffers for *p (host
  * only).  Returns MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED (the
- * weights are not bf16).
+ * weights are neither bf16 nor fp8).
  * moe_pack_weights: enqueues the re-layout of w13 / w2 (plain layout, device
  * pointers) into w13_packed / w2_packed (device buffers of the sizes above,
  * caller-owned, must not overlap the inputs) on `stream`.  The forward then
