@@ -48,12 +48,14 @@ class _Experts(ctypes.Structure):
                 ("w_dtype", ctypes.c_int32), ("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
                 ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
                 ("bias_dtype", ctypes.c_int32), ("w13_bias", ctypes.c_void_p),
-                ("w2_bias", ctypes.c_void_p), ("requant_z", ctypes.c_int32)]
+                ("w2_bias", ctypes.c_void_p), ("requant_z", ctypes.c_int32),
+                ("block", ctypes.c_int32)]
 
 
 class _Acts(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("data", ctypes.c_void_p),
-                ("scale", ctypes.c_void_p), ("quantize", ctypes.c_int32)]
+                ("scale", ctypes.c_void_p), ("quantize", ctypes.c_int32),
+                ("block", ctypes.c_int32)]
 
 
 _lib = None
@@ -73,6 +75,8 @@ def load() -> ctypes.CDLL:
     lib.oracle_fp8_encode.restype = ctypes.c_uint8
     lib.oracle_quant_row_fp8.argtypes = [P, i64, P, P]
     lib.oracle_quant_row_fp8.restype = None
+    lib.oracle_quant_row_fp8_groups.argtypes = [P, i64, i64, P, P]
+    lib.oracle_quant_row_fp8_groups.restype = None
     lib.oracle_route.argtypes = [ctypes.POINTER(_Routing), P, i64, P, P]
     lib.oracle_route.restype = ctypes.c_int
     lib.oracle_group_keys.argtypes = [ctypes.POINTER(_Routing), P, i64, P]
@@ -140,12 +144,21 @@ def fp8_encode(x) -> np.ndarray:
                     dtype=np.uint8).reshape(a.shape)
 
 
-def quant_rows_fp8(x):
-    """Per-row dynamic fp8: returns (codes uint8 [R, H], scale float32 [R])."""
+def quant_rows_fp8(x, block=0):
+    """Dynamic fp8 of each row: returns (codes uint8 [R, H], scales float32).
+    block 0: one scale per row, [R]; block B > 0: one per B columns,
+    [R, ceil(H / B)] (the block-wise granularity of "FP8 W8A8")."""
     lib = load()
     a = _np(x, np.float32)
     R, H = a.shape
     q = np.empty((R, H), np.uint8)
+    if block:
+        s = np.empty((R, -(-H // block)), np.float32)
+        for r in range(R):
+            row = np.ascontiguousarray(a[r])
+            lib.oracle_quant_row_fp8_groups(row.ctypes.data, H, block, q[r].ctypes.data,
+                                            s[r].ctypes.data)
+        return q, s
     s = np.empty(R, np.float32)
     for r in range(R):
         row = np.ascontiguousarray(a[r])
@@ -213,10 +226,13 @@ def align(topk_ids, E, block_m, expert_map=None):
 # ---------------------------------------------------------------- expert FFN
 
 class Experts:
-    """Keeps the numpy views alive while the C side holds raw pointers."""
+    """Keeps the numpy views alive while the C side holds raw pointers.
+    fp8 weights: block 0 takes per-output-channel scales w13_scale [E, 2I],
+    w2_scale [E, H]; block B > 0 one scale per B x B block, w13_scale
+    [E, ceil(2I/B), ceil(H/B)], w2_scale [E, ceil(H/B), ceil(I/B)]."""
 
     def __init__(self, w13, w2, w13_scale=None, w2_scale=None, w13_bias=None, w2_bias=None,
-                 requant_z=False):
+                 requant_z=False, block=0):
         self.w13, self.w2 = _np(w13), _np(w2)
         E, H, N = self.w13.shape
         I = N // 2
@@ -232,14 +248,24 @@ class Experts:
         wd = _dtype_code(self.w13)
         if wd == FP8:
             assert self.w13_scale is not None and self.w2_scale is not None
+            if block:
+                nb = lambda n: -(-n // block)
+                assert self.w13_scale.shape == (E, nb(N), nb(H)), self.w13_scale.shape
+                assert self.w2_scale.shape == (E, nb(H), nb(I)), self.w2_scale.shape
+            else:
+                assert self.w13_scale.size == E * N and self.w2_scale.size == E * H
         self.s = _Experts(H, I, E, wd, _ptr(self.w13), _ptr(self.w2), _ptr(self.w13_scale),
                           _ptr(self.w2_scale), bias_dt, _ptr(self.b13), _ptr(self.b2),
-                          int(requant_z))
+                          int(requant_z), int(block))
         self.H, self.I, self.E = H, I, E
 
 
 class Acts:
-    def __init__(self, data, scale=None, quantize=False):
+    """Activation rows.  fp8 codes come with scales [rows] (block 0) or
+    [rows, ceil(H/B)] (block B); quantize=True quantises float rows the same
+    way first."""
+
+    def __init__(self, data, scale=None, quantize=False, block=0):
         self.data = _np(data)
         self.H = self.data.shape[-1]
         self.data = self.data.reshape(-1, self.H)
@@ -247,7 +273,9 @@ class Acts:
         dt = _dtype_code(self.data)
         if dt == FP8:
             assert self.scale is not None
-        self.s = _Acts(dt, _ptr(self.data), _ptr(self.scale), int(quantize))
+            groups = -(-self.H // block) if block else 1
+            assert self.scale.size == self.data.shape[0] * groups, self.scale.size
+        self.s = _Acts(dt, _ptr(self.data), _ptr(self.scale), int(quantize), int(block))
 
 
 def forward_tokens(experts: Experts, acts: Acts, topk_ids, topk_w, tokens=None, nthreads=0,

@@ -20,8 +20,10 @@
  *   - align: FlagGems walkthrough, "moe_align_block_size" section (sort
  *     routed items by expert, pad each expert to BLOCK_SIZE_M), stable in
  *     the sense of the MoonEP page's build_permutation (a stable argsort);
- *   - fp8: FlagGems walkthrough, "FP8 W8A8" section (per-channel weight
- *     scales, per-token and block-wise activation scales).
+ *   - fp8: FlagGems walkthrough, "FP8 W8A8" section (per-channel or
+ *     block-wise weight scales, per-token or block-wise activation scales;
+ *     a block-wise product is the sum over K blocks of dot(qA, qB) times the
+ *     two blocks' scales, which is the product of the dequantised operands).
  *
  * Precision: every value-path sum and product is taken in double from the
  * exactly-upcast inputs (bf16 and fp8 codes convert to double exactly).
@@ -122,6 +124,19 @@ void oracle_quant_row_fp8(const float* x, int64_t n, uint8_t* q, float* scale_ou
     for (int64_t i = 0; i < n; ++i)
         q[i] = oracle_fp8_encode(x[i] / scale);
     *scale_out = scale;
+}
+
+/* Block-wise dynamic quantisation of one row (FlagGems walkthrough, "FP8
+ * W8A8", block-wise granularity): every group of `block` columns (the last
+ * one may be shorter) is quantised on its own, as oracle_quant_row_fp8 does
+ * for a whole row; scale_out[g] is group g's scale. */
+void oracle_quant_row_fp8_groups(const float* x, int64_t n, int64_t block, uint8_t* q,
+                                 float* scale_out)
+{
+    for (int64_t g0 = 0, g = 0; g0 < n; g0 += block, ++g) {
+        const int64_t len = (n - g0 < block) ? n - g0 : block;
+        oracle_quant_row_fp8(x + g0, len, q + g0, scale_out + g);
+    }
 }
 
 /* ------------------------------------------------------------------ */
@@ -371,19 +386,24 @@ typedef struct {
     int32_t w_dtype;          /* OR_F32, OR_BF16, OR_FP8                      */
     const void* w13;          /* [E][H][2I]; gate = columns [0,I), up = [I,2I) */
     const void* w2;           /* [E][I][H]                                     */
-    const float* w13_scale;   /* OR_FP8: per output channel [E][2I]           */
-    const float* w2_scale;    /* OR_FP8: per output channel [E][H]            */
+    const float* w13_scale;   /* OR_FP8: per output channel [E][2I], or with  */
+                              /*   block B: [E][ceil(2I/B)][ceil(H/B)]         */
+    const float* w2_scale;    /* OR_FP8: per output channel [E][H], or with   */
+                              /*   block B: [E][ceil(H/B)][ceil(I/B)]          */
     int32_t bias_dtype;       /* OR_F32 or OR_BF16                             */
     const void* w13_bias;     /* [E][2I] or NULL                               */
     const void* w2_bias;      /* [E][H] or NULL                                */
     int32_t requant_z;        /* 1: z is requantised to fp8 per (row, 128 cols) */
+    int32_t block;            /* OR_FP8: 0 per-channel scales; B > 0: one scale */
+                              /*   per B x B block (output columns x K rows)   */
 } oracle_experts;
 
 typedef struct {
     int32_t dtype;            /* OR_F32, OR_BF16, OR_FP8 (codes + per-row scale) */
     const void* data;         /* [rows][H]                                       */
-    const float* scale;       /* OR_FP8: [rows]                                  */
+    const float* scale;       /* OR_FP8: [rows], or with block B: [rows][ceil(H/B)] */
     int32_t quantize;         /* 1: quantise the f32/bf16 row to fp8 first      */
+    int32_t block;            /* 0: one scale per row; B > 0: per B columns     */
 } oracle_acts;
 
 static double bias_at(const oracle_experts* W, const void* b, int64_t idx)
@@ -399,6 +419,12 @@ static void load_row(const oracle_acts* A, int64_t H, int64_t row, double* x, fl
 {
     if (A->dtype == OR_FP8) {
         const uint8_t* c = (const uint8_t*)A->data + row * H;
+        if (A->block > 0) {
+            const int64_t B = A->block, ng = (H + B - 1) / B;
+            for (int64_t k = 0; k < H; ++k)
+                x[k] = fp8_table[c[k]] * (double)A->scale[row * ng + k / B];
+            return;
+        }
         double sc = (double)A->scale[row];
         for (int64_t k = 0; k < H; ++k)
             x[k] = fp8_table[c[k]] * sc;
@@ -408,12 +434,14 @@ static void load_row(const oracle_acts* A, int64_t H, int64_t row, double* x, fl
         x[k] = (A->dtype == OR_BF16) ? bf16_bits_to_double(((const uint16_t*)A->data)[row * H + k])
                                      : (double)((const float*)A->data)[row * H + k];
     if (A->quantize) {
-        float sc;
+        const int64_t B = (A->block > 0) ? A->block : H;
+        float* sc = (float*)malloc(sizeof(float) * (size_t)((H + B - 1) / B));
         for (int64_t k = 0; k < H; ++k)
             xf[k] = (float)x[k];
-        oracle_quant_row_fp8(xf, H, q, &sc);
+        oracle_quant_row_fp8_groups(xf, H, B, q, sc);
         for (int64_t k = 0; k < H; ++k)
-            x[k] = fp8_table[q[k]] * (double)sc;
+            x[k] = fp8_table[q[k]] * (double)sc[k / B];
+        free(sc);
     }
 }
 
@@ -458,6 +486,13 @@ static void expert_ffn(const oracle_experts* W, int e, const double* x, double* 
             const uint16_t* w = (const uint16_t*)W->w13 + base;
             for (int64_t n = 0; n < N; ++n)
                 h[n] += xk * bf16_bits_to_double(w[n]);
+        } else if (W->block > 0) {
+            /* scale of weight (k, n): block (n / B, k / B) of expert e */
+            const int64_t B = W->block, nbn = (N + B - 1) / B, nbk = (H + B - 1) / B;
+            const uint8_t* w = (const uint8_t*)W->w13 + base;
+            const float* sc = W->w13_scale + (int64_t)e * nbn * nbk + k / B;
+            for (int64_t n = 0; n < N; ++n)
+                h[n] += xk * (fp8_table[w[n]] * (double)sc[(n / B) * nbk]);
         } else {
             const uint8_t* w = (const uint8_t*)W->w13 + base;
             const float* sc = W->w13_scale + (int64_t)e * N;
@@ -489,6 +524,13 @@ static void expert_ffn(const oracle_experts* W, int e, const double* x, double* 
             const uint16_t* w = (const uint16_t*)W->w2 + base;
             for (int64_t c = 0; c < H; ++c)
                 o[c] += zi * bf16_bits_to_double(w[c]);
+        } else if (W->block > 0) {
+            /* scale of weight (i, c): block (c / B, i / B) of expert e */
+            const int64_t B = W->block, nbn = (H + B - 1) / B, nbk = (I + B - 1) / B;
+            const uint8_t* w = (const uint8_t*)W->w2 + base;
+            const float* sc = W->w2_scale + (int64_t)e * nbn * nbk + i / B;
+            for (int64_t c = 0; c < H; ++c)
+                o[c] += zi * (fp8_table[w[c]] * (double)sc[(c / B) * nbk]);
         } else {
             const uint8_t* w = (const uint8_t*)W->w2 + base;
             const float* sc = W->w2_scale + (int64_t)e * H;

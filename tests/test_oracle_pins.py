@@ -399,6 +399,90 @@ def test_fp8_activation_quant_and_z_requant_match_torch_cast():
         assert np.allclose(y[t], ref.numpy(), rtol=1e-10, atol=1e-12)
 
 
+def test_block_row_quant_matches_torch_cast_per_group():
+    """Block-wise activation quant ("FP8 W8A8", block-wise): every 128-column
+    group of a row, the last one short, has its own amax / 448 scale."""
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal((4, 320)).astype(np.float32)
+    x[1, 128:256] = 0.0                     # an all-zero group: scale 1, zero codes
+    x[3, :128] *= 1000.0                    # groups of very different range
+    q, s = oracle.quant_rows_fp8(x, block=128)
+    assert s.shape == (4, 3)
+    assert s[1, 1] == 1.0 and (q[1, 128:256] & 0x7F == 0).all()
+    for r in range(4):
+        for gi, g0 in enumerate(range(0, 320, 128)):
+            blk = torch.from_numpy(x[r, g0:g0 + 128])
+            if blk.abs().max() == 0:
+                continue
+            sc = blk.abs().max() / 448.0
+            assert s[r, gi] == np.float32(sc)
+            ref = (blk / sc).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(ref, q[r, g0:g0 + 128]), (r, gi)
+
+
+def _expand_blocks(sc, rows, cols, B=128):
+    """[.., ceil(rows/B), ceil(cols/B)] block scales -> [.., rows, cols] per element."""
+    t = torch.as_tensor(sc, dtype=torch.float64)
+    t = t.repeat_interleave(B, dim=-2).repeat_interleave(B, dim=-1)
+    return t[..., :rows, :cols]
+
+
+def test_block_fp8_forward_equals_dequantised_product():
+    """Block-wise W8A8: sum over K blocks of dot(qA, qB) * a_scale * b_scale is
+    the product of the dequantised operands; checked against torch float64 on
+    block-dequantised weights and group-quantised activations (H with a short
+    last block, several column blocks, biases)."""
+    g = torch.Generator().manual_seed(32)
+    M, H, I, E, B = 6, 320, 256, 3, 128
+    x = _bf(torch.randn(M, H, generator=g))
+    q13 = _fp8(torch.randn(E, H, 2 * I, generator=g) * 8)
+    q2 = _fp8(torch.randn(E, I, H, generator=g) * 8)
+    s13 = torch.rand(E, 2 * I // B, -(-H // B), generator=g) + 0.01     # [E, N/B, K/B]
+    s2 = torch.rand(E, -(-H // B), I // B, generator=g) + 0.01          # [E, H/B, I/B]
+    b13 = 0.1 * torch.randn(E, 2 * I, generator=g)
+    b2 = 0.1 * torch.randn(E, H, generator=g)
+    ids, w = oracle.route(torch.randn(M, E, generator=g), 2, renormalize=True)
+    ex = oracle.Experts(q13, q2, s13, s2, w13_bias=b13, w2_bias=b2, block=B)
+    y, _ = oracle.forward_tokens(ex, oracle.Acts(x, quantize=True, block=B), ids, w)
+    # weights: element (k, n) of expert e times block (n / B, k / B)
+    d13 = q13.double() * _expand_blocks(s13, 2 * I, H).transpose(1, 2)
+    d2 = q2.double() * _expand_blocks(s2, H, I).transpose(1, 2)
+    ref = np.zeros((M, H))
+    for t in range(M):
+        xf = x[t].float()
+        xq = torch.empty(H, dtype=torch.float64)
+        for g0 in range(0, H, B):
+            blk = xf[g0:g0 + B]
+            sc = blk.abs().max() / 448.0
+            xq[g0:g0 + B] = (blk / sc).to(torch.float8_e4m3fn).double() * sc.double()
+        for j in range(2):
+            e = ids[t, j]
+            ref[t] += w[t, j] * _dense_ffn(xq[None], d13[e], d2[e], b13[e].double(),
+                                           b2[e].double()).numpy()[0]
+    assert np.allclose(y, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
+def test_block_scales_constant_along_k_equal_per_channel_scales():
+    """Block scales that vary only with the column block are per-channel
+    scales repeated over each block's 128 columns: both forms give one result."""
+    g = torch.Generator().manual_seed(33)
+    M, H, I, E, B = 4, 256, 128, 2, 128
+    x = torch.randn(M, H, generator=g)
+    q13 = _fp8(torch.randn(E, H, 2 * I, generator=g) * 8)
+    q2 = _fp8(torch.randn(E, I, H, generator=g) * 8)
+    c13 = torch.rand(E, 2 * I // B, generator=g) + 0.01
+    c2 = torch.rand(E, H // B, generator=g) + 0.01
+    blk13 = c13[:, :, None].expand(E, 2 * I // B, H // B).contiguous()
+    blk2 = c2[:, :, None].expand(E, H // B, I // B).contiguous()
+    ids, w = oracle.route(torch.randn(M, E, generator=g), 2, renormalize=True)
+    y_blk, _ = oracle.forward_tokens(oracle.Experts(q13, q2, blk13, blk2, block=B),
+                                     oracle.Acts(x), ids, w)
+    y_ch, _ = oracle.forward_tokens(
+        oracle.Experts(q13, q2, c13.repeat_interleave(B, 1), c2.repeat_interleave(B, 1)),
+        oracle.Acts(x), ids, w)
+    assert np.allclose(y_blk, y_ch, rtol=1e-13, atol=1e-13 * np.abs(y_ch).max())
+
+
 def test_batched_rows_reduce_equals_contiguous():
     """Batched format: per-slab expert rows, weighted and reduced through the
     token map, equal the contiguous forward on the same routing."""
