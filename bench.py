@@ -119,7 +119,8 @@ def main():
                          fmt=B.MOE_FMT_BATCHED, max_tokens=inp["max_tokens"],
                          act_dtype=B._dtype_code(hidden), w_dtype=B._dtype_code(inp["w13"]),
                          out_dtype=B._dtype_code(torch.empty(0, dtype=out_dt)),
-                         routing=B.MOE_ROUTE_PRECOMPUTED)
+                         routing=B.MOE_ROUTE_PRECOMPUTED, fp8_block=cfg.fp8_block,
+                         w_layout=B.MOE_W_PACKED if cfg.fp8_block else B.MOE_W_PLAIN)
         out = torch.empty(cfg.E, inp["max_tokens"], cfg.H, dtype=out_dt, device=dev)
         cargs = B.make_args(hidden, inp["w13"], inp["w2"], out,
                             expert_num_tokens=inp["expert_num_tokens"],
@@ -139,7 +140,8 @@ def main():
                          k_group=cfg.k_group, group_select_mode=cfg.group_select_mode,
                          routed_scaling_factor=cfg.routed_scaling_factor,
                          has_w13_bias=inp["w13_bias"] is not None,
-                         has_w2_bias=inp["w2_bias"] is not None)
+                         has_w2_bias=inp["w2_bias"] is not None, fp8_block=cfg.fp8_block,
+                         w_layout=B.MOE_W_PACKED if cfg.fp8_block else B.MOE_W_PLAIN)
         out = torch.empty(cfg.M, cfg.H, dtype=out_dt, device=dev)
         cargs = B.make_args(hidden, inp["w13"], inp["w2"], out, router_logits=inp["logits"],
                             w13_bias=inp["w13_bias"], w2_bias=inp["w2_bias"],
@@ -204,7 +206,7 @@ def main():
 
     # ---- plain weight layout, for reference (same steps, same clock)
     plain_ms = None
-    if pack_ms is not None:
+    if pack_ms is not None and not cfg.fp8_block:       # block-wise scales run packed only
         run_steps(plain_prob, plain_args, 2)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -228,7 +230,13 @@ def main():
     zes = 1 if cfg.weight == "fp8" else aes
     w13_b = active * cfg.H * 2 * cfg.I * wes
     w2_b = active * cfg.I * cfg.H * wes
-    scale_b = active * (2 * cfg.I + cfg.H) * 4 if cfg.weight == "fp8" else 0
+    if cfg.weight != "fp8":
+        scale_b = 0
+    elif cfg.fp8_block:                     # one float per 128 x 128 weight block
+        nb = lambda n: -(-n // 128)
+        scale_b = active * (nb(2 * cfg.I) * nb(cfg.H) + nb(cfg.H) * nb(cfg.I)) * 4
+    else:
+        scale_b = active * (2 * cfg.I + cfg.H) * 4
     bias_b = active * (2 * cfg.I + cfg.H) * aes if cfg.bias else 0
     x_rows = valid_rows if batched else cfg.M
     x_b = x_rows * cfg.H * aes
@@ -278,7 +286,8 @@ def main():
                    "routed_scaling_factor": cfg.routed_scaling_factor, "bias": cfg.bias,
                    "block_m": info.block_m, "active_experts": active,
                    "valid_rows": valid_rows,
-                   **({"local_experts": cfg.local_experts} if cfg.local_experts else {})},
+                   **({"local_experts": cfg.local_experts} if cfg.local_experts else {}),
+                   **({"fp8_block": cfg.fp8_block} if cfg.fp8_block else {})},
         "active_tflops": round(flops / t_step / 1e12, 2),
         "hbm_gbs_path": round(path_bytes / t_step / 1e9, 1),
         "path_roofline": {"bytes": int(path_bytes), "flops": flops,
@@ -340,8 +349,8 @@ def cpu_baseline(cfg, inp, info, sample):
                         None if inp.get("w2_scale") is None else inp["w2_scale"].cpu(),
                         None if inp.get("w13_bias") is None else inp["w13_bias"].cpu(),
                         None if inp.get("w2_bias") is None else inp["w2_bias"].cpu(),
-                        requant_z=cfg.weight == "fp8")
-    acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8")
+                        requant_z=cfg.weight == "fp8", block=cfg.fp8_block)
+    acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8", block=cfg.fp8_block)
     if cfg.fmt == "batched":
         T = inp["max_tokens"]
         counts = inp["expert_num_tokens"].cpu().numpy()

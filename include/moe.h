@@ -84,8 +84,9 @@ typedef enum {
  *   act_dtype    hidden: MOE_F32 or MOE_BF16 (MOE_FP8_E4M3FN: batched only,
  *                pre-quantised codes with a_scale).
  *   w_dtype      weights: same as act_dtype for f32/bf16, or MOE_FP8_E4M3FN
- *                (per-output-channel float scales; activations are then
- *                quantised per token on the fly unless already fp8).
+ *                (float scales per output channel, or per block with
+ *                fp8_block; activations are then quantised per token, or per
+ *                token and 128 columns, on the fly unless already fp8).
  *   out_dtype    MOE_F32 or MOE_BF16.  f32 activations need f32 out.
  *   logits_dtype MOE_F32 or MOE_BF16 (contiguous, routing != PRECOMPUTED).
  *   routing, renormalize, group_count, k_group, group_select_mode,
@@ -137,6 +138,14 @@ typedef enum {
  *                after another on the stream (the walkthrough's CHUNK_SIZE
  *                execution), and the workspace is sized for one chunk; its
  *                regions then hold the last chunk's intermediates.
+ *   fp8_block    fp8 weights only.  0: per-output-channel weight scales and
+ *                per-token activation scales.  128: block-wise scales (the
+ *                walkthrough's "FP8 W8A8" block-wise granularity: every
+ *                128-deep K block of a product is scaled by its activation
+ *                block's and weight block's scales): one weight scale per
+ *                128 x 128 block and one activation scale per token and 128
+ *                columns (see moe_args).  Needs w_layout = MOE_W_PACKED.
+ *                Other block sizes: MOE_ERR_UNSUPPORTED.
  */
 typedef struct {
     int32_t format;
@@ -151,6 +160,7 @@ typedef struct {
     int32_t global_experts;
     int32_t apply_weight_on_input;
     int32_t chunk_tokens;
+    int32_t fp8_block;
 } moe_problem;
 
 /* Workspace layout chosen by the library for one problem.  All offsets are
@@ -189,7 +199,8 @@ int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* info);
 /* Device pointers of one forward (host struct; NULL where unused).
  *   hidden            contiguous [M, H]; batched [E, max_tokens, H]
  *                     (rows past expert_num_tokens[e] are never read).
- *   a_scale           batched fp8 activations: [E, max_tokens] per-row scales.
+ *   a_scale           batched fp8 activations: [E, max_tokens] per-row scales,
+ *                     or [E, max_tokens, ceil(H / 128)] with fp8_block = 128.
  *   router_logits     [M, E] (routing SOFTMAX / SIGMOID).
  *   topk_ids, topk_weights
  *                     [M, top_k] int32 / float (routing PRECOMPUTED).
@@ -200,7 +211,12 @@ int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* info);
  *   w13, w2           [E, H, 2I] (gate = columns [0, I), up = [I, 2I)), [E, I, H].
  *   w13_bias, w2_bias [E, 2I], [E, H] when has_*_bias.
  *   w13_scale, w2_scale
- *                     fp8 weights: float per output channel, [E, 2I] and [E, H].
+ *                     fp8 weights: float per output channel, [E, 2I] and [E, H];
+ *                     with fp8_block = 128 one float per 128 x 128 block,
+ *                     [E, 2I / 128, ceil(H / 128)] and [E, ceil(H / 128), I / 128]
+ *                     (output-column block, then K block), the layout of the
+ *                     [N / 128, K / 128] per-expert scale grids of block-wise
+ *                     fp8 checkpoints.
  *   out               contiguous / batched_reduce: [M, H]; batched: [E, max_tokens, H]
  *                     (only valid rows written).  out may alias hidden in the
  *                     contiguous format (in-place): every read of hidden

@@ -38,7 +38,8 @@ class moe_problem(ctypes.Structure):
                 ("routed_scaling_factor", ctypes.c_float), ("has_w13_bias", ctypes.c_int32),
                 ("has_w2_bias", ctypes.c_int32), ("batched_reduce", ctypes.c_int32),
                 ("w_layout", ctypes.c_int32), ("global_experts", ctypes.c_int32),
-                ("apply_weight_on_input", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32)]
+                ("apply_weight_on_input", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
+                ("fp8_block", ctypes.c_int32)]
 
 
 class moe_workspace_info(ctypes.Structure):
@@ -210,6 +211,7 @@ class Problem:
     global_experts: int = 0
     apply_weight_on_input: bool = False
     chunk_tokens: int = 0
+    fp8_block: int = 0
 
     def c(self) -> moe_problem:
         return moe_problem(self.fmt, self.M, self.H, self.I, self.E, self.top_k, self.max_tokens,
@@ -218,7 +220,8 @@ class Problem:
                            self.group_select_mode, float(self.routed_scaling_factor),
                            int(self.has_w13_bias), int(self.has_w2_bias),
                            int(self.batched_reduce), int(self.w_layout), int(self.global_experts),
-                           int(self.apply_weight_on_input), int(self.chunk_tokens))
+                           int(self.apply_weight_on_input), int(self.chunk_tokens),
+                           int(self.fp8_block))
 
 
 @dataclass
@@ -289,13 +292,14 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
               group_select_mode: int = 0, routed_scaling_factor: float = 1.0, w13_bias=None,
               w2_bias=None, topk_ids=None, topk_weights=None, w13_scale=None, w2_scale=None,
               out_dtype=None, out=None, workspace=None, expert_map=None,
-              apply_weight_on_input=False, chunk_tokens=0):
+              apply_weight_on_input=False, chunk_tokens=0, fp8_block=0):
     """Contiguous-format forward on torch device tensors (the MindIE-SD
     page's fused_moe argument list, single device).  w13 may be a
     PackedWeights (then w2 is ignored).  expert_map [global experts] int32
     makes this device an expert-parallel shard holding the E experts of w13
-    (routing over len(expert_map) experts).  Returns (out, workspace tensor,
-    workspace info)."""
+    (routing over len(expert_map) experts).  fp8_block=128: block-wise fp8
+    scales (w13_scale [E, 2I/128, ceil(H/128)], w2_scale [E, ceil(H/128),
+    I/128]).  Returns (out, workspace tensor, workspace info)."""
     import torch
     M = hidden.shape[0]
     w13, w2, E, H, I, wdt, layout = _weights(w13, w2)
@@ -315,7 +319,8 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
                    has_w13_bias=w13_bias is not None, has_w2_bias=w2_bias is not None,
                    w_layout=layout,
                    global_experts=0 if expert_map is None else int(expert_map.numel()),
-                   apply_weight_on_input=apply_weight_on_input, chunk_tokens=chunk_tokens)
+                   apply_weight_on_input=apply_weight_on_input, chunk_tokens=chunk_tokens,
+                   fp8_block=fp8_block)
     if out is None:
         out = torch.empty(M, H, dtype=odt, device=hidden.device)
     if workspace is None:
@@ -333,7 +338,7 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
 def fused_moe_batched(hidden, expert_num_tokens, w13, w2, *, M: int = 0, top_k: int = 1,
                       a_scale=None, w13_scale=None, w2_scale=None, w13_bias=None, w2_bias=None,
                       token_map=None, token_map_w=None, out_dtype=None, out=None,
-                      workspace=None):
+                      workspace=None, fp8_block=0):
     """Batched-format forward: hidden [E, max_tokens, H] + expert_num_tokens [E].
     M, top_k (when M > 0) promise that the slabs hold at most M * top_k valid
     rows, which bounds the workspace.  With token_map / token_map_w
@@ -350,7 +355,8 @@ def fused_moe_batched(hidden, expert_num_tokens, w13, w2, *, M: int = 0, top_k: 
                    max_tokens=T, act_dtype=_dtype_code(hidden), w_dtype=wdt,
                    out_dtype=_dtype_code(torch.empty(0, dtype=odt)),
                    routing=MOE_ROUTE_PRECOMPUTED, has_w13_bias=w13_bias is not None,
-                   has_w2_bias=w2_bias is not None, batched_reduce=reduce, w_layout=layout)
+                   has_w2_bias=w2_bias is not None, batched_reduce=reduce, w_layout=layout,
+                   fp8_block=fp8_block)
     if out is None:
         shape = (M, H) if reduce else (E, T, H)
         out = torch.empty(shape, dtype=odt, device=hidden.device)

@@ -65,6 +65,12 @@ static int validate(const moe_problem* p)
         return MOE_ERR_INVALID_ARG;
     if (p->w_layout == MOE_W_PACKED && w != MOE_BF16 && w != MOE_FP8_E4M3FN)
         return MOE_ERR_UNSUPPORTED;
+    // block-wise fp8 scales: 128 x 128 weight blocks, on the packed fp8 kernels
+    if (p->fp8_block < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (p->fp8_block != 0 &&
+        (p->fp8_block != 128 || w != MOE_FP8_E4M3FN || p->w_layout != MOE_W_PACKED))
+        return MOE_ERR_UNSUPPORTED;
 
     if (p->global_experts < 0 || p->chunk_tokens < 0 || p->apply_weight_on_input < 0 ||
         p->apply_weight_on_input > 1)
@@ -186,9 +192,11 @@ static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_
     off_chunk_expert = take((size_t)w.max_blocks * 4);
     off_inv = take(batched ? 0 : (size_t)MK * 4);
     const bool quant = fp8 && p->act_dtype != MOE_FP8_E4M3FN;
-    const int64_t qrows = batched ? max_sorted : p->M;
+    const int64_t qrows = batched ? max_sorted : chunk_rows(p);
     w.off_aq = take(quant ? (size_t)qrows * p->H : 0);
-    w.off_aq_scale = take(quant ? (size_t)qrows * 4 : 0);
+    // one scale per row, or per row and 128 columns (block-wise)
+    const int64_t qgroups = p->fp8_block ? (p->H + 127) / 128 : 1;
+    w.off_aq_scale = take(quant ? (size_t)qrows * qgroups * 4 : 0);
     w.off_z = take((size_t)max_sorted * p->I * zes);
     // fp8 z scales, group-major: [I/128][zs_ld]; the row padding lets a GEMM
     // tile read the scales of all its rows as one block
@@ -241,6 +249,7 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
     P.has_b2 = p->has_w2_bias ? 1 : 0;
     P.breduce = p->batched_reduce ? 1 : 0;
     P.wpacked = p->w_layout == MOE_W_PACKED ? 1 : 0;
+    P.blk = p->fp8_block ? 1 : 0;
     P.BM = w.block_m;
     P.cfg = cfg;
     P.CH = tile_rows(cfg);

@@ -1328,6 +1328,8 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, const float* row_w, hi
     g.w13 = A.w13;
     g.w_packed = P.wpacked;
     g.w13_scale = A.w13_scale;
+    g.blk = P.blk;
+    g.a_sld = P.blk ? (P.H + 127) / 128 : 1;
     g.b13 = P.has_b13 ? A.w13_bias : nullptr;
     g.bias_dt = (P.act == MOE_F32) ? MOE_F32 : MOE_BF16;
     g.H = P.H;
@@ -1371,6 +1373,7 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
     g.w2 = A.w2;
     g.w_packed = P.wpacked;
     g.w2_scale = A.w2_scale;
+    g.blk = P.blk;
     g.b2 = P.has_b2 ? A.w2_bias : nullptr;
     g.bias_dt = (P.act == MOE_F32) ? MOE_F32 : MOE_BF16;
     g.H = P.H;

@@ -48,12 +48,14 @@ struct Sched {
 struct Gemm1Args {
     Sched s;
     const void* a;              // activation rows [*, H] (f32 / bf16 / fp8 codes)
-    const float* a_scale;       // fp8: per activation row
+    const float* a_scale;       // fp8: per activation row, or [row][a_sld] block scales
+    int a_sld;                  // block-wise: floats per activation scale row (ceil(H / 128))
+    int blk;                    // fp8: block-wise scales (128 x 128 weight blocks)
     int a_ident;                // 1: A row = padded position p; 0: sorted[p] / a_div
     int a_div;
     const void* w13;            // [E, H, 2I], or packed blocks (bf16 / fp8 block layouts)
     int w_packed;               // 1: w13 is in the packed block layout
-    const float* w13_scale;     // fp8: [E, 2I]
+    const float* w13_scale;     // fp8: [E, 2I], or block-wise [E][2I/128][ceil(H/128)]
     const void* b13;            // [E, 2I] or null
     int bias_dt;
     int H, I;
@@ -79,7 +81,8 @@ struct Gemm2Args {
     int64_t zs_ld;
     const void* w2;             // [E, I, H], or packed blocks (bf16 / fp8 block layouts)
     int w_packed;               // 1: w2 is in the packed block layout
-    const float* w2_scale;      // fp8: [E, H]
+    const float* w2_scale;      // fp8: [E, H], or block-wise [E][ceil(H/128)][I/128]
+    int blk;                    // fp8: block-wise scales
     const void* b2;             // [E, H] or null
     int bias_dt;
     int H, I;
@@ -187,6 +190,15 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p)
 __device__ __forceinline__ void dma16(const char* g, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(g)
+                 : "memory");
+}
+
+// 4 bytes a lane: LDS byte lds + 4 l receives lane l's word.
+__device__ __forceinline__ void dma4(const char* g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                  :
                  : "s"(lds), "v"(g)
                  : "memory");

@@ -8,6 +8,12 @@
 //   GEMM1: h = (sum_k qa[row, k] qw13[e, k, n]) * sa[row] * sw13[e, n] + b13[e, n]
 //          z = SiLU(h_gate) * h_up, requantised per (row, 128 z columns)
 //   GEMM2: o = (sum_g sz[row, g] sum_{k in g} qz[row, k] qw2[e, k, c]) * sw2[e, c] + b2
+// Block-wise scales (BW; the same section's block-wise granularity): each
+// 128-deep K block g of a product is scaled by its own activation and weight
+// block scales, h = sum_g sa[row, g] sw13[e, n / 128, g] sum_{k in g} qa qw13,
+// and likewise in GEMM2 with sz[row, g] sw2[e, c / 128, g].  A K stage is one
+// such block, so each stage's MFMA products are scaled before they are
+// accumulated; the scales of the stage arrive by DMA with its operands.
 //
 // With about 770 rows per expert these contractions are MFMA-bound.  A tile is
 // F8_ROWS rows x 256 weight columns on 8 waves (2 x 4), each wave F8_ROWS / 2
@@ -33,7 +39,7 @@ constexpr int F8_BLOCK = 128 * 128;
 
 __device__ __forceinline__ int f8_slot(int chunk, int r) { return chunk ^ ((r >> 1) & 7); }
 
-template <bool ZS>
+template <bool ZS, bool BW = false>
 struct F8S {
     static constexpr int NW = 8, NT = 64 * NW;   // 2 x 4 waves
     static constexpr int CG = 4;                  // column groups of waves
@@ -43,9 +49,14 @@ struct F8S {
     static constexpr int BN = CG * FN * 16;       // 256 weight columns
     static constexpr int NB = BN / 128;           // weight blocks per K stage
     static constexpr int A_BYTES = CH * 128, B_BYTES = NB * F8_BLOCK;
-    // GEMM2: the z scales of the stage's rows, one 1 KiB DMA (256 rows' worth;
-    // the scale rows are padded so that the read stays in bounds)
-    static constexpr int S_BYTES = ZS ? 1024 : 0;
+    // per-stage scales after the operands:
+    //   GEMM2: the z scales of the stage's rows, one 1 KiB DMA (256 rows' worth;
+    //     the scale rows are padded so that the read stays in bounds);
+    //   BW GEMM1: the rows' activation block scales (2 x 256 B, one float per
+    //     lane), then the gate / up weight block scales (256 B);
+    //   BW GEMM2: the two weight block scales of the tile's columns (256 B).
+    static constexpr int SA_OFF = 0, SW_OFF = ZS ? 1024 : 512;
+    static constexpr int S_BYTES = ZS ? (BW ? 1280 : 1024) : (BW ? 768 : 0);
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     static constexpr int NS = (3 * STAGE <= 150 * 1024) ? 3 : 2;   // ring stages
     static constexpr int A_PW = A_BYTES / 1024 / NW, B_PW = B_BYTES / 1024 / NW;
@@ -60,15 +71,23 @@ struct F8S {
 // DMA sources of one fp8 tile.  Wave w issues A DMAs i = w + 8 j (tile rows
 // 8i .. 8i+7, lane l: row 8i + l/8, K chunk f8_slot(l % 8, row)), weight DMAs
 // i = w + 8 j (block i / 16, its KiB i % 16, linear) and, for GEMM2, wave 0
-// one DMA of the stage's z scales.
-template <bool ZS>
+// one DMA of the stage's z scales.  BW: GEMM1 waves 0 and 1 gather the
+// activation block scales of tile rows 64 w + l (4 bytes a lane) and wave 2
+// the gate / up weight block scales (lanes 0, 1); GEMM2 wave 1 the weight
+// block scales of the tile's two 128-column blocks (lanes 0, 1).  Those waves
+// issue one DMA more than the others; each wave waits on its own count, and
+// the shared constant (the others' count) only makes them wait a little
+// longer, never too little.
+template <bool ZS, bool BW = false>
 struct F8Src {
-    typedef F8S<ZS> S;
+    typedef F8S<ZS, BW> S;
     const char* ap[S::A_PW];    // this lane's A chunk at K stage 0, null: padding row
     const char* wb[S::NB];      // packed block of K stage 0 per tile block, null past N
     int64_t w_stage;            // bytes from one K stage's blocks to the next
     const char* zs;             // GEMM2: this lane's 16 bytes of the stage-0 z scales
     int64_t zs_stage;           // bytes from one z scale group to the next
+    const char* as;             // BW GEMM1: this lane's activation scale at stage 0 (null: none)
+    const char* bs;             // BW: this lane's weight block scale at stage 0 (null: none)
     int K;                      // contraction length
 
     __device__ __forceinline__ void issue(int kt, uint32_t lds, uint32_t, int wave,
@@ -95,6 +114,19 @@ struct F8Src {
             if (wave == 0)
                 dma16(live ? zs + kt * zs_stage : zero, lds + S::A_BYTES + S::B_BYTES);
         }
+        if constexpr (BW) {
+            // block scales: consecutive K blocks are consecutive floats
+            const uint32_t sl = lds + S::A_BYTES + S::B_BYTES;
+            if constexpr (!ZS) {
+                if (wave < 2)
+                    dma4((live && as) ? as + kt * 4 : zero, sl + S::SA_OFF + wave * 256);
+                else if (wave == 2)
+                    dma4((live && bs) ? bs + kt * 4 : zero, sl + S::SW_OFF);
+            } else {
+                if (wave == 1)
+                    dma4((live && bs) ? bs + kt * 4 : zero, sl + S::SW_OFF);
+            }
+        }
     }
 };
 
@@ -115,15 +147,19 @@ __device__ __forceinline__ f32x4 mma_f8(const i32x8& a, const i32x8& b, const f3
 // One K stage for wave (rg, cg): B fragment fn is column bcol[fn] (a multiple
 // of 16) of the stage's weight tile; the first NM strips of the wave's eight
 // hold real rows.  ZS: every product is scaled by its row's z scale before
-// it is accumulated (one MFMA spans exactly one 128-column z group).
-template <bool ZS, int NM>
+// it is accumulated (one MFMA spans exactly one 128-column z group).  BW:
+// scaled by the row's activation block scale times the weight block scale
+// of its columns (GEMM1: fragments 0, 1 are gate columns, 2, 3 up columns;
+// GEMM2: the wave's 64 columns lie in block bcol[0] / 128 of the tile).
+template <bool ZS, bool BW, int NM>
 __device__ __forceinline__ void f8_stage(const char* st, int rg, const int (&bcol)[4], int lane,
                                          f32x4 (&acc)[F8_ROWS / 32][4])
 {
-    typedef F8S<ZS> S;
+    typedef F8S<ZS, BW> S;
     const int s16 = lane & 15, g = lane >> 4;
     const char* As = st + rg * (S::FMW * 16 * 128);
     const char* Bs = st + S::A_BYTES;
+    const char* Ss = st + S::A_BYTES + S::B_BYTES;
     i32x8 b[S::FN];
 #pragma unroll
     for (int fn = 0; fn < S::FN; ++fn)
@@ -131,15 +167,37 @@ __device__ __forceinline__ void f8_stage(const char* st, int rg, const int (&bco
 #pragma unroll
     for (int fm = 0; fm < NM; ++fm) {
         const i32x8 a = f8_frag(As + fm * 2048, s16, g);
+        const int row0 = rg * S::FMW * 16 + fm * 16 + g * 4;
         if constexpr (ZS) {
-            const f32x4 sz = *(const f32x4*)(st + S::A_BYTES + S::B_BYTES +
-                                             (rg * S::FMW * 16 + fm * 16 + g * 4) * 4);
+            f32x4 sz = *(const f32x4*)(Ss + row0 * 4);
+            if constexpr (BW) {
+                const float sw = *(const float*)(Ss + S::SW_OFF + (bcol[0] >> 7) * 4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sz[r] *= sw;
+            }
 #pragma unroll
             for (int fn = 0; fn < S::FN; ++fn) {
                 const f32x4 t = mma_f8(a, b[fn], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     acc[fm][fn][r] += t[r] * sz[r];
+            }
+        } else if constexpr (BW) {
+            const f32x4 sa = *(const f32x4*)(Ss + S::SA_OFF + row0 * 4);
+            const float swg = *(const float*)(Ss + S::SW_OFF), swu = *(const float*)(Ss + S::SW_OFF + 4);
+            f32x4 fg, fu;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                fg[r] = sa[r] * swg;
+                fu[r] = sa[r] * swu;
+            }
+#pragma unroll
+            for (int fn = 0; fn < S::FN; ++fn) {
+                const f32x4 t = mma_f8(a, b[fn], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[fm][fn][r] += t[r] * (fn < 2 ? fg[r] : fu[r]);
             }
         } else {
 #pragma unroll
@@ -151,22 +209,22 @@ __device__ __forceinline__ void f8_stage(const char* st, int rg, const int (&bco
 
 // The ring over [0, nk) with the MFMAs of the wave's first `live` strips;
 // one instantiation per count keeps the loop body branch free.
-template <bool ZS, int NM = F8_ROWS / 32>
-__device__ __forceinline__ void f8_run(const F8Src<ZS>& src, char* ring, int nk, int wave, int rg,
-                                       const int (&bcol)[4], int lane, f32x4 (&acc)[F8_ROWS / 32][4],
-                                       int live)
+template <bool ZS, bool BW, int NM = F8_ROWS / 32>
+__device__ __forceinline__ void f8_run(const F8Src<ZS, BW>& src, char* ring, int nk, int wave,
+                                       int rg, const int (&bcol)[4], int lane,
+                                       f32x4 (&acc)[F8_ROWS / 32][4], int live)
 {
-    typedef F8S<ZS> S;
+    typedef F8S<ZS, BW> S;
     if constexpr (NM == 0) {
         dma_mainloop<S>(src, ring, 0, nk, wave, [](const char*) {});
     } else {
         if (live >= NM) {
             dma_mainloop<S>(src, ring, 0, nk, wave, [&](const char* st) {
-                f8_stage<ZS, NM>(st, rg, bcol, lane, acc);
+                f8_stage<ZS, BW, NM>(st, rg, bcol, lane, acc);
             });
             return;
         }
-        f8_run<ZS, NM - 1>(src, ring, nk, wave, rg, bcol, lane, acc, live);
+        f8_run<ZS, BW, NM - 1>(src, ring, nk, wave, rg, bcol, lane, acc, live);
     }
 }
 
@@ -204,10 +262,11 @@ __device__ __forceinline__ void f8_gemm1_rows(const Gemm1Args& g, const TileRef&
     r.rw = (tr < S::CH && tr < t.rows) ? gemm1_row_w(g, (int64_t)t.r0 + tr) : 0.0f;
 }
 
+template <bool BW>
 __device__ __forceinline__ void f8_gemm1_src(const Gemm1Args& g, const TileRef& t,
-                                             const F8G1Src& r, F8Src<false>& d)
+                                             const F8G1Src& r, F8Src<false, BW>& d)
 {
-    typedef F8S<false> S;
+    typedef F8S<false, BW> S;
     const int H = g.H, I = g.I;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nblk = I / 64, nks = (H + 127) / 128;
@@ -215,6 +274,18 @@ __device__ __forceinline__ void f8_gemm1_src(const Gemm1Args& g, const TileRef& 
     d.w_stage = nblk * F8_BLOCK;
     d.zs = nullptr;
     d.zs_stage = 0;
+    d.as = d.bs = nullptr;
+    if constexpr (BW) {
+        // waves 0, 1: activation scales of tile rows 64 wave + lane (thread
+        // index = tile row); wave 2, lanes 0 / 1: the gate / up weight blocks
+        // of z columns 128 ntile .. (2I / 128 column blocks, nks K blocks)
+        if (r.sa_row >= 0)
+            d.as = (const char*)(g.a_scale + (int64_t)r.sa_row * g.a_sld);
+        if (lane < 2) {
+            const int64_t nb = (lane == 0) ? t.ntile : I / 128 + t.ntile;
+            d.bs = (const char*)(g.w13_scale + ((int64_t)t.e * (2 * I / 128) + nb) * nks);
+        }
+    }
 #pragma unroll
     for (int bb = 0; bb < S::NB; ++bb)
         d.wb[bb] = (const char*)g.w13 +
@@ -228,9 +299,10 @@ __device__ __forceinline__ void f8_gemm1_src(const Gemm1Args& g, const TileRef& 
     }
 }
 
+template <bool BW>
 __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
 {
-    typedef F8S<false> S;
+    typedef F8S<false, BW> S;
     __shared__ __attribute__((aligned(16))) char ring[S::RING];
     __shared__ float rs[2][S::CH];                  // activation row scales, by tile parity
     __shared__ float rws[2][S::CH];                 // routing weights of the rows (z scale)
@@ -247,10 +319,11 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
         return;
     F8G1Src rows;
     f8_gemm1_rows(g, cur, wave, lane, rows);
-    F8Src<false> src;
-    f8_gemm1_src(g, cur, rows, src);
+    F8Src<false, BW> src;
+    f8_gemm1_src<BW>(g, cur, rows, src);
+    // per-row activation scale for the epilogue (block-wise: applied per stage)
     if (tid < S::CH) {
-        rs[0][tid] = rows.sa_row >= 0 ? g.a_scale[rows.sa_row] : 0.0f;
+        rs[0][tid] = BW ? 1.0f : (rows.sa_row >= 0 ? g.a_scale[rows.sa_row] : 0.0f);
         rws[0][tid] = rows.rw;
     }
     dma_prologue<S>(src, ring, 0, nk, wave);
@@ -269,16 +342,16 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
         const bool more = it.next(g.s, nxt);
         if (more)
             f8_gemm1_rows(g, nxt, wave, lane, rows);
-        float sn = 0.0f;                            // the next tile's row scale (tid < CH)
-        if (more && tid < S::CH && rows.sa_row >= 0)
+        float sn = BW ? 1.0f : 0.0f;               // the next tile's row scale (tid < CH)
+        if (!BW && more && tid < S::CH && rows.sa_row >= 0)
             sn = g.a_scale[rows.sa_row];
         const int z0 = cur.ntile * 128;
         float sg[2], su[2], bg[2], bu[2];
 #pragma unroll
         for (int fn = 0; fn < 2; ++fn) {
             const int n = z0 + cg * 32 + fn * 16 + s16;
-            sg[fn] = g.w13_scale[(int64_t)cur.e * N + n];
-            su[fn] = g.w13_scale[(int64_t)cur.e * N + I + n];
+            sg[fn] = BW ? 1.0f : g.w13_scale[(int64_t)cur.e * N + n];
+            su[fn] = BW ? 1.0f : g.w13_scale[(int64_t)cur.e * N + I + n];
             bg[fn] = bu[fn] = 0.0f;
             if (g.b13) {
                 bg[fn] = load_bias(g.b13, g.bias_dt, (int64_t)cur.e * N + n);
@@ -288,8 +361,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
         f32x4 acc[F8_ROWS / 32][4];
         f8_zero(acc);
         const int strips = (cur.rows + 15) >> 4;
-        f8_run<false>(src, ring, nk, wave, rg, bcol, lane, acc,
-                      min(max(strips - rg * S::FMW, 0), S::FMW));
+        f8_run<false, BW>(src, ring, nk, wave, rg, bcol, lane, acc,
+                          min(max(strips - rg * S::FMW, 0), S::FMW));
         pin(sn);
         pin(rows.rw);
 #pragma unroll
@@ -303,7 +376,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
 #pragma unroll
             for (int j = 0; j < S::A_PW; ++j)
                 pin(rows.srow[j]);
-            f8_gemm1_src(g, nxt, rows, src);
+            f8_gemm1_src<BW>(g, nxt, rows, src);
             dma_prologue<S>(src, ring, 0, nk, wave);
             if (tid < S::CH) {
                 rs[parity ^ 1][tid] = sn;
@@ -374,10 +447,11 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
 // packed blocks 2 ntile, 2 ntile + 1; wave (rg, cg) owns columns 64 cg .. +63.
 // A rows are the padded positions (z written by GEMM1); the stage's z scales
 // (group kt of the tile's rows) arrive with it.
+template <bool BW>
 __device__ __forceinline__ void f8_gemm2_src(const Gemm2Args& g, const TileRef& t, int wave,
-                                             F8Src<true>& d)
+                                             F8Src<true, BW>& d)
 {
-    typedef F8S<true> S;
+    typedef F8S<true, BW> S;
     const int H = g.H, I = g.I;
     const int lane = threadIdx.x & 63;
     const int64_t nblk = (H + 127) / 128, nks = I / 128;
@@ -385,6 +459,13 @@ __device__ __forceinline__ void f8_gemm2_src(const Gemm2Args& g, const TileRef& 
     d.w_stage = nblk * F8_BLOCK;
     d.zs = (const char*)(g.z_scale + t.r0) + lane * 16;
     d.zs_stage = g.zs_ld * 4;
+    d.as = d.bs = nullptr;
+    if constexpr (BW) {
+        // lanes 0 / 1: weight blocks 2 ntile, 2 ntile + 1 (none past H)
+        const int64_t nb = 2 * (int64_t)t.ntile + lane;
+        if (lane < 2 && nb < nblk)
+            d.bs = (const char*)(g.w2_scale + ((int64_t)t.e * nblk + nb) * nks);
+    }
 #pragma unroll
     for (int bb = 0; bb < S::NB; ++bb) {
         const int64_t jb = (int64_t)t.ntile * S::NB + bb;
@@ -400,9 +481,10 @@ __device__ __forceinline__ void f8_gemm2_src(const Gemm2Args& g, const TileRef& 
     }
 }
 
+template <bool BW>
 __global__ void __launch_bounds__(512, 1) k_gemm2_f8(Gemm2Args g)
 {
-    typedef F8S<true> S;
+    typedef F8S<true, BW> S;
     __shared__ __attribute__((aligned(16))) char ring[S::RING];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -415,8 +497,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm2_f8(Gemm2Args g)
     TileRef cur;
     if (!it.next(g.s, cur))
         return;
-    F8Src<true> src;
-    f8_gemm2_src(g, cur, wave, src);
+    F8Src<true, BW> src;
+    f8_gemm2_src<BW>(g, cur, wave, src);
     dma_prologue<S>(src, ring, 0, nk, wave);
     int bcol[4];
 #pragma unroll
@@ -434,20 +516,20 @@ __global__ void __launch_bounds__(512, 1) k_gemm2_f8(Gemm2Args g)
 #pragma unroll
         for (int fn = 0; fn < 4; ++fn) {
             const int c = c0 + bcol[fn] + s16;
-            sw[fn] = (c < H) ? g.w2_scale[(int64_t)cur.e * H + c] : 0.0f;
+            sw[fn] = (c >= H) ? 0.0f : BW ? 1.0f : g.w2_scale[(int64_t)cur.e * H + c];
             bias[fn] = (g.b2 && c < H) ? load_bias(g.b2, g.bias_dt, (int64_t)cur.e * H + c) : 0.0f;
         }
         f32x4 acc[F8_ROWS / 32][4];
         f8_zero(acc);
-        f8_run<true>(src, ring, nk, wave, rg, bcol, lane, acc,
-                     min(max(strips - rg * S::FMW, 0), S::FMW));
+        f8_run<true, BW>(src, ring, nk, wave, rg, bcol, lane, acc,
+                         min(max(strips - rg * S::FMW, 0), S::FMW));
 #pragma unroll
         for (int fn = 0; fn < 4; ++fn) {
             pin(sw[fn]);
             pin(bias[fn]);
         }
         if (more) {
-            f8_gemm2_src(g, nxt, wave, src);
+            f8_gemm2_src<BW>(g, nxt, wave, src);
             dma_prologue<S>(src, ring, 0, nk, wave);
         }
         // epilogue straight from the accumulators: one strip at a time
@@ -546,30 +628,42 @@ hipError_t launch_pack_weights_fp8(int E, int H, int I, const void* w13, const v
 }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_gemm1_fp8(const Gemm1Args& a, const Plan& P, hipStream_t s)
+template <bool BW>
+static hipError_t run_gemm1_f8(const Gemm1Args& a, const Plan& P, hipStream_t s)
 {
-    typedef F8S<false> S;
+    typedef F8S<false, BW> S;
     Gemm1Args g = a;
     g.s.n_tiles = a.I / 128;
+    auto kern = k_gemm1_f8<BW>;
     static int cached = 0;
-    const dim3 grid(persistent_grid(k_gemm1_f8, (int64_t)P.max_blocks * g.s.n_tiles, cached,
-                                    S::NT)),
+    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, S::NT)),
         block(S::NT);
-    hipLaunchKernelGGL(k_gemm1_f8, grid, block, 0, s, g);
+    hipLaunchKernelGGL(kern, grid, block, 0, s, g);
     return hipGetLastError();
+}
+
+template <bool BW>
+static hipError_t run_gemm2_f8(const Gemm2Args& a, const Plan& P, hipStream_t s)
+{
+    typedef F8S<true, BW> S;
+    Gemm2Args g = a;
+    g.s.n_tiles = (a.H + S::BN - 1) / S::BN;
+    auto kern = k_gemm2_f8<BW>;
+    static int cached = 0;
+    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, S::NT)),
+        block(S::NT);
+    hipLaunchKernelGGL(kern, grid, block, 0, s, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm1_fp8(const Gemm1Args& a, const Plan& P, hipStream_t s)
+{
+    return a.blk ? run_gemm1_f8<true>(a, P, s) : run_gemm1_f8<false>(a, P, s);
 }
 
 hipError_t launch_gemm2_fp8(const Gemm2Args& a, const Plan& P, hipStream_t s)
 {
-    typedef F8S<true> S;
-    Gemm2Args g = a;
-    g.s.n_tiles = (a.H + S::BN - 1) / S::BN;
-    static int cached = 0;
-    const dim3 grid(persistent_grid(k_gemm2_f8, (int64_t)P.max_blocks * g.s.n_tiles, cached,
-                                    S::NT)),
-        block(S::NT);
-    hipLaunchKernelGGL(k_gemm2_f8, grid, block, 0, s, g);
-    return hipGetLastError();
+    return a.blk ? run_gemm2_f8<true>(a, P, s) : run_gemm2_f8<false>(a, P, s);
 }
 
 }  // namespace moe

@@ -206,7 +206,9 @@ struct Plan {
     int renorm, G, kg, gmode;
     float rsf;
     int has_b13, has_b2, breduce;
-    int wpacked;                    // weights in the packed block layout (bf16)
+    int wpacked;                    // weights in the packed block layout (bf16 / fp8)
+    int blk;                        // fp8: block-wise scales (128 x 128 weight blocks,
+                                    // activation scales per row and 128 columns)
     int BM;                         // align granularity: each expert run padded to BM rows
     int CH;                         // rows per GEMM tile (a multiple of BM)
     int cfg;                        // GEMM tile family (see moe_gemm.hip)

@@ -678,11 +678,87 @@ __global__ void __launch_bounds__(256) k_quant_rows(const TIn* __restrict__ x, i
         aq_scale[r] = scale;
 }
 
+// Block-wise variant (the "FP8 W8A8" section's block-wise granularity): one
+// scale per row and 128 columns (amax / 448 over the group, 1 for an all-zero
+// group; a short last group covers the rest of the row), codes as above,
+// scales row-major [rows][ceil(H / 128)].  One wave per row, one pass: the
+// GL lanes that hold one 128-column group's chunks reduce its amax among
+// themselves.
+template <typename TIn>
+__global__ void __launch_bounds__(256) k_quant_groups(const TIn* __restrict__ x, int64_t rows, int H,
+                                                      int ident, const int32_t* __restrict__ sorted,
+                                                      const int32_t* __restrict__ npp, int sentinel,
+                                                      uint8_t* __restrict__ aq,
+                                                      float* __restrict__ aq_scale)
+{
+    constexpr int VE = 16 / sizeof(TIn);            // elements per 16-byte chunk
+    constexpr int GL = 128 / VE;                     // lanes (chunks) per 128-column group
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + wave;
+    const int nch = H / VE, ng = (H + 127) / 128;
+    int64_t src = r;
+    if (ident) {
+        if (r >= *npp)
+            return;
+        const int sid = sorted[r];
+        if (sid >= sentinel) {          // padding row: zeros, unit scales
+            for (int k = lane * 16; k < H; k += 64 * 16)
+                *(i32x4*)(aq + r * H + k) = i32x4{0, 0, 0, 0};
+            for (int gi = lane; gi < ng; gi += 64)
+                aq_scale[r * ng + gi] = 1.0f;
+            return;
+        }
+        src = sid;
+    } else if (r >= rows) {
+        return;
+    }
+    const i32x4* row = (const i32x4*)(x + src * (int64_t)H);
+    auto val = [&](const i32x4& c, int i) {
+        if constexpr (sizeof(TIn) == 2)
+            return bf16_to_f32((u16)((uint32_t)c[i >> 1] >> (16 * (i & 1))));
+        else
+            return __int_as_float(c[i]);
+    };
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+        const int c = c0 + lane;
+        const i32x4 v = (c < nch) ? row[c] : i32x4{0, 0, 0, 0};
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < VE; ++i)
+            amax = fmaxf(amax, fabsf(val(v, i)));
+        amax = grp_max<GL>(amax);                    // the lanes of one group, all active
+        const float scale = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+        if (c < nch) {
+            uint32_t w[VE / 4];
+#pragma unroll
+            for (int q = 0; q < VE / 4; ++q)
+                w[q] = cvt_fp8x2(val(v, 4 * q) / scale, val(v, 4 * q + 1) / scale) |
+                       (cvt_fp8x2(val(v, 4 * q + 2) / scale, val(v, 4 * q + 3) / scale) << 16);
+            if constexpr (VE == 8)
+                *(i32x2*)(aq + r * H + c * 8) = i32x2{(int)w[0], (int)w[1]};
+            else
+                *(uint32_t*)(aq + r * H + c * 4) = w[0];
+            if (lane % GL == 0)
+                aq_scale[r * ng + c / GL] = scale;
+        }
+    }
+}
+
 hipError_t launch_quant_rows(const Plan& P, const void* hidden, hipStream_t s)
 {
     const int ident = (P.fmt == MOE_FMT_BATCHED) ? 1 : 0;
     const int64_t rows = ident ? P.max_sorted : P.M;
     const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    if (P.blk) {
+        if (P.act == MOE_BF16)
+            hipLaunchKernelGGL(k_quant_groups<u16>, grid, block, 0, s, (const u16*)hidden, rows,
+                               P.H, ident, P.sorted_ids, P.npp, (int)P.sentinel, P.aq, P.aq_scale);
+        else
+            hipLaunchKernelGGL(k_quant_groups<float>, grid, block, 0, s, (const float*)hidden,
+                               rows, P.H, ident, P.sorted_ids, P.npp, (int)P.sentinel, P.aq,
+                               P.aq_scale);
+        return hipGetLastError();
+    }
     if (P.act == MOE_BF16)
         hipLaunchKernelGGL(k_quant_rows<u16>, grid, block, 0, s, (const u16*)hidden, rows, P.H,
                            ident, P.sorted_ids, P.npp, (int)P.sentinel, P.aq, P.aq_scale);

@@ -10,8 +10,9 @@ Distribution notation: N(mu, v) takes the second argument as the variance
 
 Two inputs are upstream of the fused MoE rather than part of it and are
 prepared here with library calls only:
-  * fp8 weights: per-output-channel scale amax/448 and a cast through
-    torch.float8_e4m3fn (weights are quantised once, at load time);
+  * fp8 weights: per-output-channel scale amax/448 (or one per 128 x 128
+    block) and a cast through torch.float8_e4m3fn (weights are quantised
+    once, at load time);
   * the batched format's token layout: the dispatcher that produced it ran
     a top-k of (logits + per-expert offset) (torch.topk) and packed each
     expert's tokens in ascending token order.
@@ -36,6 +37,8 @@ class MoeConfig:
     fmt: str = "contiguous"          # "contiguous" (M,K) or "batched" (E,max_tokens,K)
     act: str = "bf16"                # activation storage: f32 | bf16
     weight: str = "bf16"             # f32 | bf16 | fp8 (per-output-channel scales)
+    fp8_block: int = 0               # fp8: 128 = block-wise scales (128 x 128 weight
+                                     # blocks, activations per token and 128 columns)
     scoring: str = "softmax"         # softmax | sigmoid
     renormalize: bool = True
     group_count: int = 1
@@ -89,7 +92,12 @@ CONFIGS = [TINY_F32, MIXTRAL_PREFILL, DECODE_SMALL_EXPERTS, DEEPSEEK_GROUPED, BA
 # rank holds 32 of them, about 1024 rows each (the MFMA-bound share).
 EP8_SHARD = DEEPSEEK_GROUPED.scaled(name="ep8_shard_deepseek_bf16", M=32768, local_experts=32)
 
-EXTRA = [EP8_SHARD]
+# The DeepSeek-like layer with block-wise fp8 weights (one scale per 128 x 128
+# block, activations quantised per token and 128 columns in the path): the
+# form DeepSeek-V3-class checkpoints ship.
+DEEPSEEK_BLOCKFP8 = DEEPSEEK_GROUPED.scaled(name="deepseek_blockfp8", weight="fp8", fp8_block=128)
+
+EXTRA = [EP8_SHARD, DEEPSEEK_BLOCKFP8]
 BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -109,6 +117,25 @@ def quantize_weight_fp8(w: torch.Tensor):
     scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
     codes = (w / scale[:, None, :]).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
     return codes, scale.to(torch.float32)
+
+
+def quantize_weight_fp8_blocks(w: torch.Tensor, B: int = 128):
+    """Block-wise fp8 e4m3fn codes + one float32 scale (amax / 448, 1 for an
+    all-zero block) per B x B block.  w: [E, K, N] float32 -> (codes
+    float8_e4m3fn [E, K, N], scale [E, ceil(N / B), ceil(K / B)]), the scale
+    grid indexed (output-column block, K block).  One expert at a time."""
+    E, K, N = w.shape
+    nk, nn = -(-K // B), -(-N // B)
+    codes = torch.empty(E, K, N, dtype=torch.float8_e4m3fn, device=w.device)
+    scale = torch.empty(E, nn, nk, dtype=torch.float32, device=w.device)
+    for e in range(E):
+        wp = torch.nn.functional.pad(w[e], (0, nn * B - N, 0, nk * B - K))
+        amax = wp.abs().view(nk, B, nn, B).amax(dim=(1, 3))            # [nk, nn]
+        sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (wp.view(nk, B, nn, B) / sc[:, None, :, None]).clamp_(-448.0, 448.0)
+        codes[e] = q.view(nk * B, nn * B)[:K, :N].to(torch.float8_e4m3fn)
+        scale[e] = sc.t()
+    return codes, scale
 
 
 def make_inputs(cfg: MoeConfig, seed: int, device="cpu") -> dict:
@@ -139,9 +166,10 @@ def make_inputs(cfg: MoeConfig, seed: int, device="cpu") -> dict:
     w13 = _randn((E, H, 2 * I), gen, device, std=1.0 / math.sqrt(H), dtype=w_dt)
     w2 = _randn((E, I, H), gen, device, std=1.0 / math.sqrt(I), dtype=w_dt)
     if cfg.weight == "fp8":
-        out["w13"], out["w13_scale"] = quantize_weight_fp8(w13)
+        quant = quantize_weight_fp8_blocks if cfg.fp8_block else quantize_weight_fp8
+        out["w13"], out["w13_scale"] = quant(w13)
         del w13
-        out["w2"], out["w2_scale"] = quantize_weight_fp8(w2)
+        out["w2"], out["w2_scale"] = quant(w2)
         del w2
     else:
         out["w13"], out["w2"] = w13, w2

@@ -46,6 +46,9 @@ def run_contiguous(inp: dict, dev, precomputed=None, out=None, inplace=False, ou
               group_select_mode=cfg.group_select_mode,
               routed_scaling_factor=cfg.routed_scaling_factor)
     w13, w2 = inp["w13"].to(dev), inp["w2"].to(dev)
+    if cfg.fp8_block:
+        packed = True                   # block-wise scales run on the packed fp8 kernels
+        kw["fp8_block"] = cfg.fp8_block
     if packed:
         w13, w2 = B.pack_weights(w13, w2), None
     for name in ("w13_bias", "w2_bias", "w13_scale", "w2_scale"):
@@ -104,7 +107,7 @@ def oracle_experts(inp: dict) -> oracle.Experts:
                           None if inp.get("w2_scale") is None else inp["w2_scale"].cpu(),
                           None if inp.get("w13_bias") is None else inp["w13_bias"].cpu(),
                           None if inp.get("w2_bias") is None else inp["w2_bias"].cpu(),
-                          requant_z=cfg.weight == "fp8")
+                          requant_z=cfg.weight == "fp8", block=cfg.fp8_block)
 
 
 def compare(cfg: W.MoeConfig, got: np.ndarray, ref: np.ndarray, what: str = "") -> float:
@@ -124,7 +127,7 @@ def compare(cfg: W.MoeConfig, got: np.ndarray, ref: np.ndarray, what: str = "") 
 
 def check_output(inp: dict, out: torch.Tensor, ids_o, w_o, tokens=None, what=""):
     cfg = inp["cfg"]
-    acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8")
+    acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8", block=cfg.fp8_block)
     y, _ = oracle.forward_tokens(oracle_experts(inp), acts, ids_o, w_o, tokens=tokens)
     got = out.float().cpu().numpy()
     if tokens is not None:
@@ -136,6 +139,9 @@ def run_batched(inp: dict, dev, reduce=False, out_dtype=None, packed=False):
     cfg = inp["cfg"]
     kw = {"out_dtype": out_dtype}
     w13, w2 = inp["w13"].to(dev), inp["w2"].to(dev)
+    if cfg.fp8_block:
+        packed = True
+        kw["fp8_block"] = cfg.fp8_block
     if packed:
         w13, w2 = B.pack_weights(w13, w2), None
     for name in ("w13_scale", "w2_scale", "w13_bias", "w2_bias"):

@@ -110,6 +110,17 @@ def _status(prob):
     (dict(chunk_tokens=4), B.MOE_OK),
     (dict(chunk_tokens=-1), B.MOE_ERR_INVALID_ARG),
     (dict(fmt=B.MOE_FMT_BATCHED, max_tokens=8, chunk_tokens=4), B.MOE_ERR_UNSUPPORTED),
+    # block-wise fp8 scales: 128 x 128 blocks, packed fp8 weights only
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_FP8_E4M3FN, fp8_block=128), B.MOE_OK),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_FP8_E4M3FN, fp8_block=128, H=80), B.MOE_OK),
+    (dict(fmt=B.MOE_FMT_BATCHED, max_tokens=32, act_dtype=B.MOE_FP8_E4M3FN,
+          w_dtype=B.MOE_FP8_E4M3FN, w_layout=B.MOE_W_PACKED, fp8_block=128), B.MOE_OK),
+    (dict(w_dtype=B.MOE_FP8_E4M3FN, fp8_block=128), B.MOE_ERR_UNSUPPORTED),      # plain layout
+    (dict(w_layout=B.MOE_W_PACKED, fp8_block=128), B.MOE_ERR_UNSUPPORTED),       # bf16 weights
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_FP8_E4M3FN, fp8_block=64),
+     B.MOE_ERR_UNSUPPORTED),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_FP8_E4M3FN, fp8_block=-128),
+     B.MOE_ERR_INVALID_ARG),
 ])
 def test_problem_validation(kw, status):
     assert _status(_prob(**kw)) == status
@@ -223,3 +234,15 @@ def test_chunked_workspace_is_sized_for_one_chunk():
     # a chunk larger than M is the unchunked problem
     big = B.moe_workspace_shapes(_prob(M=100, chunk_tokens=4096).c())
     assert big.bytes == B.moe_workspace_shapes(_prob(M=100).c()).bytes
+
+
+def test_block_fp8_activation_scales_are_sized_per_group():
+    """Block-wise fp8: the in-path activation scales take one float per row
+    and 128 columns (a short last group included) instead of one per row."""
+    kw = dict(M=64, H=320, I=256, w_dtype=B.MOE_FP8_E4M3FN, w_layout=B.MOE_W_PACKED)
+    per_row = B.moe_workspace_shapes(_prob(**kw).c())
+    per_blk = B.moe_workspace_shapes(_prob(fp8_block=128, **kw).c())
+    span = lambda w: w.off_z - w.off_aq_scale          # the scale region (aligned to 256 B)
+    assert span(per_row) >= 64 * 4
+    assert span(per_blk) >= 64 * 3 * 4 > span(per_row)
+    assert per_blk.off_aq_scale == per_row.off_aq_scale

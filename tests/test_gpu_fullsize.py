@@ -93,3 +93,19 @@ def test_full_size_ep8_shard():
     y, _ = oracle.forward_tokens(GH.oracle_experts(inp), acts, ids_o, w_o, tokens=tokens,
                                  expert_map=emap_np)
     GH.compare(cfg, out.cpu().numpy()[tokens], y, what="ep8 shard")
+
+
+def test_full_size_block_fp8():
+    """The DeepSeek-like layer with block-wise fp8 weights (128 x 128 blocks)
+    and in-path per (token, 128 columns) activation quantisation."""
+    cfg = W.DEEPSEEK_BLOCKFP8
+    dev = GH.device()
+    seed = 1100 + W.EXTRA.index(cfg)
+    print(f"[case] {cfg.name} seed={seed} generating", flush=True)
+    inp = W.make_inputs(cfg, seed, device=dev)
+    out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+    print(f"[case] {cfg.name} ran", flush=True)
+    ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    GH.check_output(inp, out, ids_o, w_o, tokens=_sample_tokens(cfg.M), what="full block fp8")
+    out16, _, _ = GH.run_contiguous(inp, dev)
+    GH.check_rounded(out16, out)
