@@ -22,6 +22,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 
 F32, BF16, FP8 = 0, 1, 2
+U8, U4 = 3, 4                    # WNA16 weight codes (8 or 4 bits)
 SOFTMAX, SIGMOID = 0, 1
 _DT = {"f32": F32, "bf16": BF16, "fp8": FP8}
 
@@ -49,7 +50,8 @@ class _Experts(ctypes.Structure):
                 ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
                 ("bias_dtype", ctypes.c_int32), ("w13_bias", ctypes.c_void_p),
                 ("w2_bias", ctypes.c_void_p), ("requant_z", ctypes.c_int32),
-                ("block", ctypes.c_int32)]
+                ("block", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("w13_zero", ctypes.c_void_p), ("w2_zero", ctypes.c_void_p)]
 
 
 class _Acts(ctypes.Structure):
@@ -229,14 +231,23 @@ class Experts:
     """Keeps the numpy views alive while the C side holds raw pointers.
     fp8 weights: block 0 takes per-output-channel scales w13_scale [E, 2I],
     w2_scale [E, H]; block B > 0 one scale per B x B block, w13_scale
-    [E, ceil(2I/B), ceil(H/B)], w2_scale [E, ceil(H/B), ceil(I/B)]."""
+    [E, ceil(2I/B), ceil(H/B)], w2_scale [E, ceil(H/B), ceil(I/B)].
+    WNA16 (bits 8 or 4): unsigned codes, w13 [E, H, 2I] / w2 [E, I, H] bytes
+    (bits 4: two per byte along the last dim, even column in the low nibble,
+    so [E, H, I] / [E, I, H/2]); scales [E, ceil(K/group), N] float; zero
+    points the same shape as uint8, or None for 2^(bits-1)."""
 
     def __init__(self, w13, w2, w13_scale=None, w2_scale=None, w13_bias=None, w2_bias=None,
-                 requant_z=False, block=0):
+                 requant_z=False, block=0, bits=0, group=128, w13_zero=None, w2_zero=None):
         self.w13, self.w2 = _np(w13), _np(w2)
         E, H, N = self.w13.shape
+        if bits == 4:
+            N *= 2
         I = N // 2
-        assert self.w2.shape == (E, I, H), (self.w2.shape, (E, I, H))
+        w2_shape = (E, I, H // 2) if bits == 4 else (E, I, H)
+        assert self.w2.shape == w2_shape, (self.w2.shape, w2_shape)
+        self.z13 = None if w13_zero is None else _np(w13_zero, np.uint8)
+        self.z2 = None if w2_zero is None else _np(w2_zero, np.uint8)
         self.w13_scale = None if w13_scale is None else _np(w13_scale, np.float32)
         self.w2_scale = None if w2_scale is None else _np(w2_scale, np.float32)
         self.b13 = None if w13_bias is None else _np(w13_bias)
@@ -245,8 +256,15 @@ class Experts:
         for b in (self.b13, self.b2):
             if b is not None:
                 bias_dt = _dtype_code(b)
-        wd = _dtype_code(self.w13)
-        if wd == FP8:
+        wd = {8: U8, 4: U4}[bits] if bits else _dtype_code(self.w13)
+        if bits:
+            assert self.w13.dtype == np.uint8 and self.w2.dtype == np.uint8
+            ng = lambda k: -(-k // group)
+            assert self.w13_scale.shape == (E, ng(H), N), self.w13_scale.shape
+            assert self.w2_scale.shape == (E, ng(I), H), self.w2_scale.shape
+            for z, sc in ((self.z13, self.w13_scale), (self.z2, self.w2_scale)):
+                assert z is None or z.shape == sc.shape
+        elif wd == FP8:
             assert self.w13_scale is not None and self.w2_scale is not None
             if block:
                 nb = lambda n: -(-n // block)
@@ -256,7 +274,8 @@ class Experts:
                 assert self.w13_scale.size == E * N and self.w2_scale.size == E * H
         self.s = _Experts(H, I, E, wd, _ptr(self.w13), _ptr(self.w2), _ptr(self.w13_scale),
                           _ptr(self.w2_scale), bias_dt, _ptr(self.b13), _ptr(self.b2),
-                          int(requant_z), int(block))
+                          int(requant_z), int(block), int(group), _ptr(self.z13),
+                          _ptr(self.z2))
         self.H, self.I, self.E = H, I, E
 
 

@@ -20,6 +20,9 @@
  *   - align: FlagGems walkthrough, "moe_align_block_size" section (sort
  *     routed items by expert, pad each expert to BLOCK_SIZE_M), stable in
  *     the sense of the MoonEP page's build_permutation (a stable argsort);
+ *   - WNA16: FlagGems walkthrough, "WNA16" section (int8_w8a16 and
+ *     int4_w4a16 weights with group scales and zero points; activations stay
+ *     16-bit): w = (q - z) * s, one (s, z) per group of K rows and column;
  *   - fp8: FlagGems walkthrough, "FP8 W8A8" section (per-channel or
  *     block-wise weight scales, per-token or block-wise activation scales;
  *     a block-wise product is the sum over K blocks of dot(qA, qB) times the
@@ -43,7 +46,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8 = 2, OR_U8 = 3, OR_U4 = 4 };
 enum { OR_SOFTMAX = 0, OR_SIGMOID = 1 };
 
 /* ------------------------------------------------------------------ */
@@ -396,7 +399,31 @@ typedef struct {
     int32_t requant_z;        /* 1: z is requantised to fp8 per (row, 128 cols) */
     int32_t block;            /* OR_FP8: 0 per-channel scales; B > 0: one scale */
                               /*   per B x B block (output columns x K rows)   */
+    int32_t group;            /* OR_U8 / OR_U4: K rows per scale group          */
+    const uint8_t* w13_zero;  /* OR_U8 / OR_U4: [E][ceil(H/group)][2I] or NULL  */
+    const uint8_t* w2_zero;   /*   [E][ceil(I/group)][H] or NULL (2^(bits-1))   */
 } oracle_experts;
+
+/* WNA16 weight codes: OR_U8 one unsigned byte per weight, [E][K][N];
+ * OR_U4 two per byte along N, [E][K][N/2], the even column in the low
+ * nibble.  The scales are [E][ceil(K/group)][N] floats (w13_scale / w2_scale). */
+static int wq_code(const oracle_experts* W, const void* w, int64_t row, int64_t N, int64_t n)
+{
+    if (W->w_dtype == OR_U8)
+        return ((const uint8_t*)w)[row * N + n];
+    const uint8_t b = ((const uint8_t*)w)[row * (N / 2) + n / 2];
+    return (n & 1) ? (b >> 4) : (b & 15);
+}
+
+/* Dequantised WNA16 weight (k, n) of expert e: (q - z) * s of its K group. */
+static double wq_weight(const oracle_experts* W, const void* w, const float* scale,
+                        const uint8_t* zero, int e, int64_t K, int64_t N, int64_t k, int64_t n)
+{
+    const int64_t G = W->group, ng = (K + G - 1) / G;
+    const int64_t gi = ((int64_t)e * ng + k / G) * N + n;
+    const int z = zero ? zero[gi] : (W->w_dtype == OR_U8 ? 128 : 8);
+    return (double)(wq_code(W, w, (int64_t)e * K + k, N, n) - z) * (double)scale[gi];
+}
 
 typedef struct {
     int32_t dtype;            /* OR_F32, OR_BF16, OR_FP8 (codes + per-row scale) */
@@ -486,6 +513,9 @@ static void expert_ffn(const oracle_experts* W, int e, const double* x, double* 
             const uint16_t* w = (const uint16_t*)W->w13 + base;
             for (int64_t n = 0; n < N; ++n)
                 h[n] += xk * bf16_bits_to_double(w[n]);
+        } else if (W->w_dtype == OR_U8 || W->w_dtype == OR_U4) {
+            for (int64_t n = 0; n < N; ++n)
+                h[n] += xk * wq_weight(W, W->w13, W->w13_scale, W->w13_zero, e, H, N, k, n);
         } else if (W->block > 0) {
             /* scale of weight (k, n): block (n / B, k / B) of expert e */
             const int64_t B = W->block, nbn = (N + B - 1) / B, nbk = (H + B - 1) / B;
@@ -524,6 +554,9 @@ static void expert_ffn(const oracle_experts* W, int e, const double* x, double* 
             const uint16_t* w = (const uint16_t*)W->w2 + base;
             for (int64_t c = 0; c < H; ++c)
                 o[c] += zi * bf16_bits_to_double(w[c]);
+        } else if (W->w_dtype == OR_U8 || W->w_dtype == OR_U4) {
+            for (int64_t c = 0; c < H; ++c)
+                o[c] += zi * wq_weight(W, W->w2, W->w2_scale, W->w2_zero, e, I, H, i, c);
         } else if (W->block > 0) {
             /* scale of weight (i, c): block (c / B, i / B) of expert e */
             const int64_t B = W->block, nbn = (H + B - 1) / B, nbk = (I + B - 1) / B;

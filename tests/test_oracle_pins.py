@@ -483,6 +483,75 @@ def test_block_scales_constant_along_k_equal_per_channel_scales():
     assert np.allclose(y_blk, y_ch, rtol=1e-13, atol=1e-13 * np.abs(y_ch).max())
 
 
+def _wq_dequant(codes, scale, zero, bits, group, K, N):
+    """torch float64 dequantisation of WNA16 codes: unpack (bits 4: two per
+    byte along N, even column in the low nibble), then (q - z) * s by K group."""
+    c = torch.as_tensor(codes).to(torch.int64)
+    if bits == 4:
+        c = torch.stack([c & 15, c >> 4], dim=-1).reshape(*c.shape[:-1], N)
+    z = (torch.full_like(torch.as_tensor(scale, dtype=torch.float64), 2 ** (bits - 1))
+         if zero is None else torch.as_tensor(zero).to(torch.float64))
+    s = torch.as_tensor(scale, dtype=torch.float64)
+    zk = z.repeat_interleave(group, dim=-2)[..., :K, :]
+    sk = s.repeat_interleave(group, dim=-2)[..., :K, :]
+    return (c.double() - zk) * sk
+
+
+@pytest.mark.parametrize("bits,zero", [(8, True), (8, False), (4, True), (4, False)])
+def test_wna16_equals_dequantised_product(bits, zero):
+    """WNA16 (int8_w8a16 / int4_w4a16 with group scales and zero points):
+    against torch float64 on dequantised weights.  H 320 gives a short last
+    K group; biases included."""
+    g = torch.Generator().manual_seed(40 + bits + int(zero))
+    M, H, I, E, G = 6, 320, 256, 3, 128
+    hi = 2 ** bits
+    x = _bf(torch.randn(M, H, generator=g))
+    q13 = torch.randint(0, hi, (E, H, 2 * I), generator=g)
+    q2 = torch.randint(0, hi, (E, I, H), generator=g)
+    s13 = (torch.rand(E, -(-H // G), 2 * I, generator=g) + 0.5) / (hi * 8)
+    s2 = (torch.rand(E, -(-I // G), H, generator=g) + 0.5) / (hi * 8)
+    z13 = torch.randint(0, hi, s13.shape, generator=g).to(torch.uint8) if zero else None
+    z2 = torch.randint(0, hi, s2.shape, generator=g).to(torch.uint8) if zero else None
+    b13 = 0.1 * torch.randn(E, 2 * I, generator=g)
+    b2 = 0.1 * torch.randn(E, H, generator=g)
+
+    def pack(q):
+        q = q.to(torch.uint8)
+        return q if bits == 8 else (q[..., 0::2] | (q[..., 1::2] << 4))
+    ids, w = oracle.route(torch.randn(M, E, generator=g), 2, renormalize=True)
+    ex = oracle.Experts(pack(q13), pack(q2), s13, s2, w13_bias=b13, w2_bias=b2, bits=bits,
+                        group=G, w13_zero=z13, w2_zero=z2)
+    y, _ = oracle.forward_tokens(ex, oracle.Acts(x), ids, w)
+    d13 = _wq_dequant(pack(q13), s13, z13, bits, G, H, 2 * I)
+    d2 = _wq_dequant(pack(q2), s2, z2, bits, G, I, H)
+    ref = np.zeros((M, H))
+    for t in range(M):
+        for j in range(2):
+            e = ids[t, j]
+            ref[t] += w[t, j] * _dense_ffn(x[t:t + 1].double(), d13[e], d2[e], b13[e].double(),
+                                           b2[e].double()).numpy()[0]
+    assert np.allclose(y, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+
+
+def test_wna16_int4_nibble_order_and_default_zero():
+    """A hand-made int4 expert: one K row whose byte 0x5A holds column 0 = 10
+    (low nibble) and column 1 = 5 (high nibble); with the default zero point
+    8 and scale 1 the weights are +2 and -3."""
+    H, I, E = 2, 1, 1
+    w13 = np.zeros((E, H, I), np.uint8)               # [E, H, 2I / 2]
+    w13[0, 0, 0] = 0x5A
+    w13[0, 1, 0] = 0x88                               # both 8: weight 0
+    s13 = np.ones((E, 1, 2 * I), np.float32)
+    s2 = np.ones((E, 1, H), np.float32)
+    # w2 row 0: column 0 = 9 - 8 = 1, column 1 = 8 - 8 = 0, so o = (z, 0)
+    w2 = np.array([[[0x89]]], np.uint8)
+    ex = oracle.Experts(w13, w2, s13, s2, bits=4, group=128)
+    # x = (1, 0): h = (gate, up) = (2, -3), z = SiLU(2) * -3
+    out, _ = oracle.expert_rows(ex, oracle.Acts(np.array([[1.0, 0.0]], np.float32)), [0], [0])
+    silu = 2.0 / (1.0 + math.exp(-2.0))
+    assert np.allclose(out[0], [silu * -3.0, 0.0], rtol=1e-14)
+
+
 def test_batched_rows_reduce_equals_contiguous():
     """Batched format: per-slab expert rows, weighted and reduced through the
     token map, equal the contiguous forward on the same routing."""
