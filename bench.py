@@ -113,25 +113,30 @@ def main():
     # ---- problem and arguments (marshalling only)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
     out_dt = tdt[cfg.out_dtype]
+    wq_bits = {"u8": 8, "u4": 4}.get(cfg.weight, 0)           # WNA16 weight codes
+    w_code = {8: B.MOE_U8, 4: B.MOE_U4}[wq_bits] if wq_bits else B._dtype_code(inp["w13"])
+    # block-wise fp8 scales and WNA16 codes run on packed weights only
+    layout0 = B.MOE_W_PACKED if (cfg.fp8_block or wq_bits) else B.MOE_W_PLAIN
     if batched:
         hidden = inp["hidden"]
         prob = B.Problem(M=cfg.M, H=cfg.H, I=cfg.I, E=cfg.E, top_k=cfg.top_k,
                          fmt=B.MOE_FMT_BATCHED, max_tokens=inp["max_tokens"],
-                         act_dtype=B._dtype_code(hidden), w_dtype=B._dtype_code(inp["w13"]),
+                         act_dtype=B._dtype_code(hidden), w_dtype=w_code,
                          out_dtype=B._dtype_code(torch.empty(0, dtype=out_dt)),
                          routing=B.MOE_ROUTE_PRECOMPUTED, fp8_block=cfg.fp8_block,
-                         w_layout=B.MOE_W_PACKED if cfg.fp8_block else B.MOE_W_PLAIN)
+                         w_layout=layout0)
         out = torch.empty(cfg.E, inp["max_tokens"], cfg.H, dtype=out_dt, device=dev)
         cargs = B.make_args(hidden, inp["w13"], inp["w2"], out,
                             expert_num_tokens=inp["expert_num_tokens"],
-                            w13_scale=inp.get("w13_scale"), w2_scale=inp.get("w2_scale"))
+                            w13_scale=inp.get("w13_scale"), w2_scale=inp.get("w2_scale"),
+                            w13_zero=inp.get("w13_zero"), w2_zero=inp.get("w2_zero"))
     else:
         hidden = inp["hidden"]
         emap = inp.get("expert_map")
         E_local = inp["w13"].shape[0]
         prob = B.Problem(M=cfg.M, H=cfg.H, I=cfg.I, E=E_local, top_k=cfg.top_k,
                          global_experts=0 if emap is None else cfg.E,
-                         act_dtype=B._dtype_code(hidden), w_dtype=B._dtype_code(inp["w13"]),
+                         act_dtype=B._dtype_code(hidden), w_dtype=w_code,
                          out_dtype=B._dtype_code(torch.empty(0, dtype=out_dt)),
                          logits_dtype=B._dtype_code(inp["logits"]),
                          routing=B.MOE_ROUTE_SIGMOID if cfg.scoring == "sigmoid"
@@ -141,12 +146,13 @@ def main():
                          routed_scaling_factor=cfg.routed_scaling_factor,
                          has_w13_bias=inp["w13_bias"] is not None,
                          has_w2_bias=inp["w2_bias"] is not None, fp8_block=cfg.fp8_block,
-                         w_layout=B.MOE_W_PACKED if cfg.fp8_block else B.MOE_W_PLAIN)
+                         w_layout=layout0)
         out = torch.empty(cfg.M, cfg.H, dtype=out_dt, device=dev)
         cargs = B.make_args(hidden, inp["w13"], inp["w2"], out, router_logits=inp["logits"],
                             w13_bias=inp["w13_bias"], w2_bias=inp["w2_bias"],
                             w13_scale=inp.get("w13_scale"), w2_scale=inp.get("w2_scale"),
-                            expert_map=emap)
+                            expert_map=emap, w13_zero=inp.get("w13_zero"),
+                            w2_zero=inp.get("w2_zero"))
     ws, info = B.allocate_workspace(prob, dev)
     stream = B.current_stream_handle(dev)
     hip = HipEvents()
@@ -158,10 +164,10 @@ def main():
     # (moe_pack_weights); the plain layout is timed too, for reference
     plain_prob, plain_args = prob.c(), cargs
     pack_ms = None
-    if cfg.weight in ("bf16", "fp8"):
+    if cfg.weight in ("bf16", "fp8", "u8", "u4"):
         ev0, ev1 = hip.create(), hip.create()
         rec(ctypes.c_void_p(ev0), ctypes.c_void_p(stream))
-        pw = B.pack_weights(inp["w13"], inp["w2"])
+        pw = B.pack_weights(inp["w13"], inp["w2"], wq_bits=wq_bits)
         rec(ctypes.c_void_p(ev1), ctypes.c_void_p(stream))
         torch.cuda.synchronize()
         pack_ms = hip.elapsed_ms(ev0, ev1)
@@ -206,7 +212,7 @@ def main():
 
     # ---- plain weight layout, for reference (same steps, same clock)
     plain_ms = None
-    if pack_ms is not None and not cfg.fp8_block:       # block-wise scales run packed only
+    if pack_ms is not None and layout0 == B.MOE_W_PLAIN:   # some forms run packed only
         run_steps(plain_prob, plain_args, 2)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -224,13 +230,17 @@ def main():
         counts = ws[off:off + 4 * prob.E].view(torch.int32).cpu().numpy()
         valid_rows = int(counts.sum())          # M * top_k, or this shard's routed rows
     active = int((counts > 0).sum())
-    wes = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.weight]
+    wes = {"f32": 4, "bf16": 2, "fp8": 1, "u8": 1, "u4": 0.5}[cfg.weight]
     aes = {"f32": 4, "bf16": 2}[cfg.act]
     oes = {"f32": 4, "bf16": 2}[cfg.out_dtype]
     zes = 1 if cfg.weight == "fp8" else aes
-    w13_b = active * cfg.H * 2 * cfg.I * wes
-    w2_b = active * cfg.I * cfg.H * wes
-    if cfg.weight != "fp8":
+    w13_b = int(active * cfg.H * 2 * cfg.I * wes)
+    w2_b = int(active * cfg.I * cfg.H * wes)
+    if wq_bits:                             # group scales (+ zero points) per 128 K rows
+        ng = lambda k: -(-k // 128)
+        scale_b = active * (ng(cfg.H) * 2 * cfg.I + ng(cfg.I) * cfg.H) * (
+            4 + (1 if cfg.wq_zero else 0))
+    elif cfg.weight != "fp8":
         scale_b = 0
     elif cfg.fp8_block:                     # one float per 128 x 128 weight block
         nb = lambda n: -(-n // 128)
@@ -246,7 +256,8 @@ def main():
     z_b = valid_rows * cfg.I * zes
     flops = cfg.flops(valid_rows)
     path_bytes = w13_b + w2_b + scale_b + bias_b + x_b + out_b + logit_b
-    dt_key = "fp8" if cfg.weight == "fp8" else cfg.weight
+    # WNA16 dequantises to bf16 and runs bf16 MFMAs
+    dt_key = "fp8" if cfg.weight == "fp8" else "bf16" if wq_bits else cfg.weight
     t_hbm = path_bytes / (HBM_PEAK_GBS * 1e9)
     t_mfma = flops / (MFMA_PEAK_TFLOPS[dt_key] * 1e12)
     t_step = float(np.median(step_ms)) * 1e-3
@@ -277,7 +288,8 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3"}[cfg.weight],
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3", "u8": "w8a16_bf16",
+                  "u4": "w4a16_bf16"}[cfg.weight],
         "data": "synthetic (seeded; see DESIGN.md input recipe)",
         "config": {"workload": cfg.name, "format": cfg.fmt, "M": cfg.M, "H": cfg.H, "I": cfg.I,
                    "E": cfg.E, "top_k": cfg.top_k, "routing": cfg.scoring,
@@ -287,7 +299,8 @@ def main():
                    "block_m": info.block_m, "active_experts": active,
                    "valid_rows": valid_rows,
                    **({"local_experts": cfg.local_experts} if cfg.local_experts else {}),
-                   **({"fp8_block": cfg.fp8_block} if cfg.fp8_block else {})},
+                   **({"fp8_block": cfg.fp8_block} if cfg.fp8_block else {}),
+                   **({"weight": cfg.weight, "zero_points": cfg.wq_zero} if wq_bits else {})},
         "active_tflops": round(flops / t_step / 1e12, 2),
         "hbm_gbs_path": round(path_bytes / t_step / 1e9, 1),
         "path_roofline": {"bytes": int(path_bytes), "flops": flops,
@@ -349,7 +362,10 @@ def cpu_baseline(cfg, inp, info, sample):
                         None if inp.get("w2_scale") is None else inp["w2_scale"].cpu(),
                         None if inp.get("w13_bias") is None else inp["w13_bias"].cpu(),
                         None if inp.get("w2_bias") is None else inp["w2_bias"].cpu(),
-                        requant_z=cfg.weight == "fp8", block=cfg.fp8_block)
+                        requant_z=cfg.weight == "fp8", block=cfg.fp8_block,
+                        bits={"u8": 8, "u4": 4}.get(cfg.weight, 0),
+                        w13_zero=None if inp.get("w13_zero") is None else inp["w13_zero"].cpu(),
+                        w2_zero=None if inp.get("w2_zero") is None else inp["w2_zero"].cpu())
     acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8", block=cfg.fp8_block)
     if cfg.fmt == "batched":
         T = inp["max_tokens"]

@@ -52,7 +52,13 @@ typedef enum {
     MOE_ERR_LAUNCH = -4       /* a kernel launch failed (hipGetLastError)           */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3FN = 2 } moe_dtype;
+typedef enum {
+    MOE_F32 = 0,
+    MOE_BF16 = 1,
+    MOE_FP8_E4M3FN = 2,
+    MOE_U8 = 3,               /* weights only: unsigned 8-bit codes (WNA16, int8_w8a16)  */
+    MOE_U4 = 4                /* weights only: unsigned 4-bit codes, two per byte (int4_w4a16) */
+} moe_dtype;
 
 typedef enum {
     MOE_ROUTE_SOFTMAX = 0,    /* scores = softmax(logits) over all E              */
@@ -86,7 +92,14 @@ typedef enum {
  *   w_dtype      weights: same as act_dtype for f32/bf16, or MOE_FP8_E4M3FN
  *                (float scales per output channel, or per block with
  *                fp8_block; activations are then quantised per token, or per
- *                token and 128 columns, on the fly unless already fp8).
+ *                token and 128 columns, on the fly unless already fp8), or
+ *                MOE_U8 / MOE_U4: WNA16 weights (the walkthrough's "WNA16"
+ *                section, int8_w8a16 / int4_w4a16) with bf16 activations:
+ *                weight = (q - z) * s, q the unsigned code, one float scale s
+ *                and one zero point z per group of 128 K rows and output
+ *                column (z = 2^(bits-1) when no zero points are given); the
+ *                weights are dequantised to bf16 inside the GEMMs, which
+ *                accumulate in float32.  Needs w_layout = MOE_W_PACKED.
  *   out_dtype    MOE_F32 or MOE_BF16.  f32 activations need f32 out.
  *   logits_dtype MOE_F32 or MOE_BF16 (contiguous, routing != PRECOMPUTED).
  *   routing, renormalize, group_count, k_group, group_select_mode,
@@ -208,9 +221,13 @@ int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* info);
  *   token_map, token_map_w
  *                     batched_reduce: [M, top_k] flat slab row e*max_tokens+i
  *                     holding token t's j-th routed copy, and its weight.
- *   w13, w2           [E, H, 2I] (gate = columns [0, I), up = [I, 2I)), [E, I, H].
+ *   w13, w2           [E, H, 2I] (gate = columns [0, I), up = [I, 2I)), [E, I, H];
+ *                     MOE_U4 codes two per byte along the last dimension, the
+ *                     even column in the low nibble: [E, H, I], [E, I, H / 2].
  *   w13_bias, w2_bias [E, 2I], [E, H] when has_*_bias.
  *   w13_scale, w2_scale
+ *                     MOE_U8 / MOE_U4 weights: float per 128-row K group and
+ *                     column, [E, ceil(H / 128), 2I] and [E, ceil(I / 128), H].
  *                     fp8 weights: float per output channel, [E, 2I] and [E, H];
  *                     with fp8_block = 128 one float per 128 x 128 block,
  *                     [E, 2I / 128, ceil(H / 128)] and [E, ceil(H / 128), I / 128]
@@ -223,7 +240,10 @@ int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* info);
  *                     precedes the first write of out on the stream (per
  *                     chunk, when chunk_tokens is set).
  *   expert_map        global_experts > 0: [global_experts] int32, each value
- *                     in [-1, E). */
+ *                     in [-1, E).
+ *   w13_zero, w2_zero MOE_U8 / MOE_U4 weights: uint8 zero points, the shapes of
+ *                     w13_scale / w2_scale (one per group and column, values
+ *                     below 2^bits), or NULL for the symmetric 2^(bits-1). */
 typedef struct {
     const void* hidden;
     const float* a_scale;
@@ -241,6 +261,8 @@ typedef struct {
     const float* w2_scale;
     void* out;
     const int32_t* expert_map;
+    const uint8_t* w13_zero;
+    const uint8_t* w2_zero;
 } moe_args;
 
 /* Enqueues one fused MoE forward on `stream` (a hipStream_t; NULL = the
@@ -299,12 +321,25 @@ int moe_forward_timed(const moe_problem* p, const moe_args* a, void* workspace,
  *   w2:  block (e, kt, j), kt < I / 128, j < ceil(H / 128); block column n
  *        is weight column 128 j + n.
  *   The per-channel scales are not packed.
- * In both, rows past H (w13) / I (w2) and columns past I (w13) / H (w2) are
+ * MOE_U8 / MOE_U4 codes: each block is 128 weight columns x 64 weight rows
+ *   (K), 8 KiB of 8-bit or 4 KiB of 4-bit codes, in the order the GEMM's
+ *   bf16 MFMA fragments read them: for column group f (16 columns), K half h
+ *   (32 rows) and lane l = 16 a + c (column 16 f + c, rows 32 h + 8 a ..
+ *   + 7), the lane's 8 codes are one 8-byte (U8) or 4-byte (U4, code i in
+ *   nibble i & 1 of byte i / 2, low nibble first) run at offset
+ *   ((2 f + h) * 64 + l) * 8 or * 4.
+ *   w13: block (e, kt, j), kt < ceil(H / 64), j < ceil(I / 64), j fastest;
+ *        block columns 0-63 are gate columns 64 j .., 64-127 up columns
+ *        I + 64 j ...
+ *   w2:  block (e, kt, j), kt < ceil(I / 64), j < ceil(H / 128); block
+ *        column n is weight column 128 j + n.
+ *   Scales and zero points are not packed.
+ * In all, rows past H (w13) / I (w2) and columns past I (w13) / H (w2) are
  * zero.
  *
  * moe_packed_weight_bytes: sizes of the two packed buffers for *p (host
  * only).  Returns MOE_OK, MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED (the
- * weights are neither bf16 nor fp8).
+ * weights are not bf16, fp8, MOE_U8 or MOE_U4).
  * moe_pack_weights: enqueues the re-layout of w13 / w2 (plain layout, device
  * pointers) into w13_packed / w2_packed (device buffers of the sizes above,
  * caller-owned, must not overlap the inputs) on `stream`.  The forward then

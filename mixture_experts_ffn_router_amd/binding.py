@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 # enums of moe.h
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 0, -1, -2, -3, -4
-MOE_F32, MOE_BF16, MOE_FP8_E4M3FN = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3FN, MOE_U8, MOE_U4 = 0, 1, 2, 3, 4
 MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID, MOE_ROUTE_PRECOMPUTED = 0, 1, 2
 MOE_FMT_CONTIGUOUS, MOE_FMT_BATCHED = 0, 1
 MOE_W_PLAIN, MOE_W_PACKED = 0, 1
@@ -55,7 +55,7 @@ class moe_args(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "hidden", "a_scale", "router_logits", "topk_ids", "topk_weights", "expert_num_tokens",
         "token_map", "token_map_w", "w13", "w2", "w13_bias", "w2_bias", "w13_scale", "w2_scale",
-        "out", "expert_map")]
+        "out", "expert_map", "w13_zero", "w2_zero")]
 
 
 class MoeError(RuntimeError):
@@ -236,22 +236,30 @@ class PackedWeights:
     w_dtype: int = MOE_BF16
 
 
-def pack_weights(w13, w2) -> PackedWeights:
+def pack_weights(w13, w2, wq_bits: int = 0) -> PackedWeights:
     """Packs plain bf16 or fp8 w13 [E, H, 2I] / w2 [E, I, H] on their device
-    (one launch pair on the current stream)."""
+    (one launch pair on the current stream).  wq_bits 8 / 4: WNA16 codes in
+    uint8 tensors, 4-bit codes two per byte along the last dim ([E, H, I] /
+    [E, I, H / 2])."""
     import torch
     E, H, N = w13.shape
+    if wq_bits == 4:
+        N *= 2
     I = N // 2
-    if tuple(w2.shape) != (E, I, H):
+    w2_shape = (E, I, H // 2) if wq_bits == 4 else (E, I, H)
+    if tuple(w2.shape) != w2_shape:
         raise ValueError(f"w2 shape {tuple(w2.shape)} does not match w13 {tuple(w13.shape)}")
-    prob = Problem(M=0, H=H, I=I, E=E, top_k=1, act_dtype=MOE_BF16, w_dtype=_dtype_code(w13),
+    wdt = {8: MOE_U8, 4: MOE_U4}[wq_bits] if wq_bits else _dtype_code(w13)
+    if wq_bits and (w13.dtype != torch.uint8 or w2.dtype != torch.uint8):
+        raise TypeError("WNA16 codes are uint8 tensors")
+    prob = Problem(M=0, H=H, I=I, E=E, top_k=1, act_dtype=MOE_BF16, w_dtype=wdt,
                    out_dtype=MOE_BF16).c()
     b13, b2 = moe_packed_weight_bytes(prob)
     p13 = torch.empty(b13, dtype=torch.uint8, device=w13.device)
     p2 = torch.empty(b2, dtype=torch.uint8, device=w13.device)
     moe_pack_weights(prob, _ptr(w13), _ptr(w2), p13.data_ptr(), p2.data_ptr(),
                      current_stream_handle(w13.device))
-    return PackedWeights(p13, p2, E, H, I, _dtype_code(w13))
+    return PackedWeights(p13, p2, E, H, I, wdt)
 
 
 def _weights(w13, w2):
@@ -265,11 +273,12 @@ def _weights(w13, w2):
 def make_args(hidden, w13, w2, out, router_logits=None, topk_ids=None, topk_weights=None,
               w13_bias=None, w2_bias=None, w13_scale=None, w2_scale=None, a_scale=None,
               expert_num_tokens=None, token_map=None, token_map_w=None,
-              expert_map=None) -> moe_args:
+              expert_map=None, w13_zero=None, w2_zero=None) -> moe_args:
     return moe_args(_ptr(hidden), _ptr(a_scale), _ptr(router_logits), _ptr(topk_ids),
                     _ptr(topk_weights), _ptr(expert_num_tokens), _ptr(token_map),
                     _ptr(token_map_w), _ptr(w13), _ptr(w2), _ptr(w13_bias), _ptr(w2_bias),
-                    _ptr(w13_scale), _ptr(w2_scale), _ptr(out), _ptr(expert_map))
+                    _ptr(w13_scale), _ptr(w2_scale), _ptr(out), _ptr(expert_map),
+                    _ptr(w13_zero), _ptr(w2_zero))
 
 
 def allocate_workspace(problem: Problem, device):
@@ -292,14 +301,18 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
               group_select_mode: int = 0, routed_scaling_factor: float = 1.0, w13_bias=None,
               w2_bias=None, topk_ids=None, topk_weights=None, w13_scale=None, w2_scale=None,
               out_dtype=None, out=None, workspace=None, expert_map=None,
-              apply_weight_on_input=False, chunk_tokens=0, fp8_block=0):
+              apply_weight_on_input=False, chunk_tokens=0, fp8_block=0, w13_zero=None,
+              w2_zero=None):
     """Contiguous-format forward on torch device tensors (the MindIE-SD
     page's fused_moe argument list, single device).  w13 may be a
     PackedWeights (then w2 is ignored).  expert_map [global experts] int32
     makes this device an expert-parallel shard holding the E experts of w13
     (routing over len(expert_map) experts).  fp8_block=128: block-wise fp8
     scales (w13_scale [E, 2I/128, ceil(H/128)], w2_scale [E, ceil(H/128),
-    I/128]).  Returns (out, workspace tensor, workspace info)."""
+    I/128]).  WNA16 weights come packed (pack_weights(..., wq_bits)) with
+    group scales w13_scale [E, ceil(H/128), 2I] / w2_scale [E, ceil(I/128), H]
+    and optional uint8 zero points of the same shapes.  Returns (out,
+    workspace tensor, workspace info)."""
     import torch
     M = hidden.shape[0]
     w13, w2, E, H, I, wdt, layout = _weights(w13, w2)
@@ -329,7 +342,8 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
         info = moe_workspace_shapes(prob.c())
     args = make_args(hidden, w13, w2, out, router_logits=router_logits, topk_ids=topk_ids,
                      topk_weights=topk_weights, w13_bias=w13_bias, w2_bias=w2_bias,
-                     w13_scale=w13_scale, w2_scale=w2_scale, expert_map=expert_map)
+                     w13_scale=w13_scale, w2_scale=w2_scale, expert_map=expert_map,
+                     w13_zero=w13_zero, w2_zero=w2_zero)
     moe_forward(prob.c(), args, workspace.data_ptr(), workspace.numel(),
                 current_stream_handle(hidden.device))
     return out, workspace, info
@@ -338,7 +352,7 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
 def fused_moe_batched(hidden, expert_num_tokens, w13, w2, *, M: int = 0, top_k: int = 1,
                       a_scale=None, w13_scale=None, w2_scale=None, w13_bias=None, w2_bias=None,
                       token_map=None, token_map_w=None, out_dtype=None, out=None,
-                      workspace=None, fp8_block=0):
+                      workspace=None, fp8_block=0, w13_zero=None, w2_zero=None):
     """Batched-format forward: hidden [E, max_tokens, H] + expert_num_tokens [E].
     M, top_k (when M > 0) promise that the slabs hold at most M * top_k valid
     rows, which bounds the workspace.  With token_map / token_map_w
@@ -366,7 +380,8 @@ def fused_moe_batched(hidden, expert_num_tokens, w13, w2, *, M: int = 0, top_k: 
         info = moe_workspace_shapes(prob.c())
     args = make_args(hidden, w13, w2, out, a_scale=a_scale, expert_num_tokens=expert_num_tokens,
                      token_map=token_map, token_map_w=token_map_w, w13_bias=w13_bias,
-                     w2_bias=w2_bias, w13_scale=w13_scale, w2_scale=w2_scale)
+                     w2_bias=w2_bias, w13_scale=w13_scale, w2_scale=w2_scale,
+                     w13_zero=w13_zero, w2_zero=w2_zero)
     moe_forward(prob.c(), args, workspace.data_ptr(), workspace.numel(),
                 current_stream_handle(hidden.device))
     return out, workspace, info

@@ -51,7 +51,7 @@ static int validate(const moe_problem* p)
         if (w != MOE_F32 || out != MOE_F32)
             return MOE_ERR_UNSUPPORTED;
     } else if (act == MOE_BF16) {
-        if (w != MOE_BF16 && w != MOE_FP8_E4M3FN)
+        if (w != MOE_BF16 && w != MOE_FP8_E4M3FN && w != MOE_U8 && w != MOE_U4)
             return MOE_ERR_UNSUPPORTED;
     } else if (act == MOE_FP8_E4M3FN) {
         if (w != MOE_FP8_E4M3FN || p->format != MOE_FMT_BATCHED)
@@ -63,7 +63,11 @@ static int validate(const moe_problem* p)
         return MOE_ERR_UNSUPPORTED;
     if (p->w_layout != MOE_W_PLAIN && p->w_layout != MOE_W_PACKED)
         return MOE_ERR_INVALID_ARG;
-    if (p->w_layout == MOE_W_PACKED && w != MOE_BF16 && w != MOE_FP8_E4M3FN)
+    if (p->w_layout == MOE_W_PACKED && w != MOE_BF16 && w != MOE_FP8_E4M3FN && w != MOE_U8 &&
+        w != MOE_U4)
+        return MOE_ERR_UNSUPPORTED;
+    // WNA16 weights are dequantised inside the packed-layout GEMMs
+    if ((w == MOE_U8 || w == MOE_U4) && p->w_layout != MOE_W_PACKED)
         return MOE_ERR_UNSUPPORTED;
     // block-wise fp8 scales: 128 x 128 weight blocks, on the packed fp8 kernels
     if (p->fp8_block < 0)
@@ -131,6 +135,10 @@ static int choose_tile(const moe_problem* p, int64_t rows_cap)
         return p->w_layout == MOE_W_PACKED ? TILE_FP8_DMA : TILE_FP8;
     if (p->w_dtype == MOE_F32)
         return TILE_DECODE;
+    if (p->w_dtype == MOE_U8 || p->w_dtype == MOE_U4) {   // DMA families only
+        const double avg = (double)rows_cap / p->E;
+        return avg <= 12 ? TILE_DECODE_DMA : avg <= 48 ? TILE_MID_DMA : TILE_PREFILL;
+    }
     // tuning override: MOE_TILE_CFG = 0 (prefill) | 1 (mid) | 2 (decode) | 4 (decode, DMA)
     // | 5 (mid, DMA), read on every call
     if (const char* env = std::getenv("MOE_TILE_CFG")) {
@@ -204,7 +212,8 @@ static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_
     const int64_t orows = (batched && !p->batched_reduce) ? 0 : max_sorted;
     w.off_o = take((size_t)orows * p->H * 4);
     const int cfg = choose_tile(p, rows_cap);
-    const bool split = gemm2_k_split(
+    // (WNA16 GEMM2 runs whole-K tiles)
+    const bool split = p->w_dtype != MOE_U8 && p->w_dtype != MOE_U4 && gemm2_k_split(
         cfg, p->format, p->batched_reduce,
         expected_chunks(p->format, chunk_rows(p), p->top_k, p->E, p->max_tokens, tile_rows(cfg)),
         p->H, p->I, device_cus());
@@ -250,6 +259,7 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
     P.breduce = p->batched_reduce ? 1 : 0;
     P.wpacked = p->w_layout == MOE_W_PACKED ? 1 : 0;
     P.blk = p->fp8_block ? 1 : 0;
+    P.wq = (p->w_dtype == MOE_U8) ? 8 : (p->w_dtype == MOE_U4) ? 4 : 0;
     P.BM = w.block_m;
     P.cfg = cfg;
     P.CH = tile_rows(cfg);
@@ -287,7 +297,11 @@ static int check_args(const moe_problem* p, const moe_args* a)
         return MOE_ERR_INVALID_ARG;
     if ((p->has_w13_bias && !a->w13_bias) || (p->has_w2_bias && !a->w2_bias))
         return MOE_ERR_INVALID_ARG;
-    if (p->w_dtype == MOE_FP8_E4M3FN && (!a->w13_scale || !a->w2_scale))
+    if ((p->w_dtype == MOE_FP8_E4M3FN || p->w_dtype == MOE_U8 || p->w_dtype == MOE_U4) &&
+        (!a->w13_scale || !a->w2_scale))
+        return MOE_ERR_INVALID_ARG;
+    // zero points of WNA16 weights: both or neither
+    if ((p->w_dtype == MOE_U8 || p->w_dtype == MOE_U4) && (!a->w13_zero != !a->w2_zero))
         return MOE_ERR_INVALID_ARG;
     if (p->act_dtype == MOE_FP8_E4M3FN && !a->a_scale)
         return MOE_ERR_INVALID_ARG;
@@ -443,7 +457,13 @@ extern "C" int moe_forward_timed(const moe_problem* p, const moe_args* a, void* 
 // 128 K values (w13: 64 gate + 64 up columns).
 static int packed_sizes(const moe_problem* p, size_t* b13, size_t* b2)
 {
-    const int rc = validate(p);
+    if (!p)
+        return MOE_ERR_INVALID_ARG;
+    // the sizes do not depend on the layout the problem names (a caller may
+    // size the packed buffers from the problem of the plain weights)
+    moe_problem q = *p;
+    q.w_layout = MOE_W_PACKED;
+    const int rc = validate(&q);
     if (rc != MOE_OK)
         return rc;
     const size_t blk = 64 * 256;
@@ -455,6 +475,12 @@ static int packed_sizes(const moe_problem* p, size_t* b13, size_t* b2)
     if (p->w_dtype == MOE_FP8_E4M3FN) {          // I is a multiple of 128 (validated)
         *b13 = (size_t)p->E * (p->I / 64) * ((p->H + 127) / 128) * blk;
         *b2 = (size_t)p->E * ((p->H + 127) / 128) * (p->I / 128) * blk;
+        return MOE_OK;
+    }
+    if (p->w_dtype == MOE_U8 || p->w_dtype == MOE_U4) {   // 128 columns x 64 K codes a block
+        const size_t qb = (p->w_dtype == MOE_U8) ? 8192 : 4096;
+        *b13 = (size_t)p->E * ((p->H + 63) / 64) * ((p->I + 63) / 64) * qb;
+        *b2 = (size_t)p->E * ((p->I + 63) / 64) * ((p->H + 127) / 128) * qb;
         return MOE_OK;
     }
     return MOE_ERR_UNSUPPORTED;
@@ -477,11 +503,15 @@ extern "C" int moe_pack_weights(const moe_problem* p, const void* w13, const voi
     if (!w13 || !w2 || !w13_packed || !w2_packed)
         return MOE_ERR_INVALID_ARG;
     (void)hipGetLastError();   // a stale error of an earlier, unrelated call
-    const hipError_t err =
-        (p->w_dtype == MOE_FP8_E4M3FN)
-            ? launch_pack_weights_fp8(p->E, p->H, p->I, w13, w2, w13_packed, w2_packed,
-                                      (hipStream_t)stream)
-            : launch_pack_weights(p->E, p->H, p->I, w13, w2, w13_packed, w2_packed,
+    hipError_t err;
+    if (p->w_dtype == MOE_FP8_E4M3FN)
+        err = launch_pack_weights_fp8(p->E, p->H, p->I, w13, w2, w13_packed, w2_packed,
+                                      (hipStream_t)stream);
+    else if (p->w_dtype == MOE_U8 || p->w_dtype == MOE_U4)
+        err = launch_pack_weights_wq(p->w_dtype == MOE_U8 ? 8 : 4, p->E, p->H, p->I, w13, w2,
+                                     w13_packed, w2_packed, (hipStream_t)stream);
+    else
+        err = launch_pack_weights(p->E, p->H, p->I, w13, w2, w13_packed, w2_packed,
                                   (hipStream_t)stream);
     return err == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }

@@ -630,17 +630,30 @@ __global__ void __launch_bounds__(256) k_gemm2(Gemm2Args g)
 // Out-of-range chunks (K tail, columns past N) and rows past the tile's real
 // rows are DMA'd from a zero page; strips that hold only padding skip their
 // fragment reads and MFMAs.
-template <int FMW_, int WC_, int NS_>
+//
+// WNA16 (Q = 8 or 4 code bits; the walkthrough's "WNA16" section): the
+// weight block of a stage is 128 columns x 64 K of codes in fragment order
+// (8 or 4 KiB, see the packed layout in moe.h), followed by the stage's
+// group scales (128 floats, 1 KiB slot) and zero points (128 bytes, 1 KiB
+// slot), both DMA'd from the plain [E, K / 128, N] grids.  The B fragments
+// are dequantised to bf16 right after their LDS read: w = (q - z) * s as one
+// FMA q * s + (-z s) on the float code, then a packed RNE conversion.
+template <int FMW_, int WC_, int NS_, int Q_ = 0>
 struct DS {
-    static constexpr int FMW = FMW_, WC = WC_, NS = NS_;
+    static constexpr int FMW = FMW_, WC = WC_, NS = NS_, Q = Q_;
     static constexpr int NW = 2 * WC, NT = 64 * NW;      // waves, threads
     static constexpr int FN = 4;                         // 16-column fragments per wave
     static constexpr int CH = 32 * FMW;                  // rows per tile
     static constexpr int BN = 64 * WC;                   // weight columns per tile
     static constexpr int NB = BN / 128;                  // 128-column weight blocks per tile
     static constexpr int RB = 256;                       // bytes per weight row of a block
-    static constexpr int A_BYTES = CH * 128, B_BYTES = NB * PACK_BLOCK;
-    static constexpr int STAGE = A_BYTES + B_BYTES;
+    // bytes of one 128-column weight block per K stage: bf16 rows, or codes
+    static constexpr int QB = Q ? 128 * 64 * Q / 8 : PACK_BLOCK;
+    static constexpr int IPB = QB / 1024;                // 1 KiB DMAs per weight block
+    static constexpr int A_BYTES = CH * 128, B_BYTES = NB * QB;
+    static constexpr int SZ_OFF = A_BYTES + B_BYTES;     // WNA16: scales, then zero points
+    static constexpr int SZ_BYTES = Q ? 2048 : 0;
+    static constexpr int STAGE = A_BYTES + B_BYTES + SZ_BYTES;
     static constexpr int A_INS = A_BYTES / 1024, B_INS = B_BYTES / 1024;   // 1 KiB DMAs a stage
     static constexpr int A_PW = (A_INS + NW - 1) / NW;   // A DMA slots per wave
     static constexpr int B_PW = B_INS / NW;
@@ -653,11 +666,16 @@ struct DS {
     static_assert(B_INS % NW == 0, "weight DMAs split evenly");
     static_assert(NS >= 2 && NS <= 4, "ring depth");
     static_assert((NS - 2) * D < 64, "vmcnt range");
+    static_assert(Q == 0 || Q == 8 || Q == 4, "code width");
+    static_assert(Q == 0 || NB == 1, "a WNA16 tile holds one weight block");
 };
 
 // DMA sources of one tile.  Wave w issues the A DMAs i = w + NW j (tile rows
 // 8i .. 8i+7; lane l: row 8i + l/8, 16-byte K chunk (l%8) ^ ((row>>1)&7)) and
-// the B DMAs i = w + NW j (weight block i/16, K rows 4(i%16) + l/16, slot l%16).
+// the B DMAs i = w + NW j (weight block i / IPB, its KiB i % IPB; plain bf16:
+// K rows 4(i%16) + l/16, slot l%16).  WNA16: wave 0 also DMAs the stage's
+// group scales, wave 1 its zero points (one group spans two stages); those
+// waves wait on the shared count, which only makes them wait a little longer.
 // A lane keeps a pointer per A DMA; weight addresses are recomputed per issue
 // from uniform bases.  PACKED: each weight block of a K stage is one
 // contiguous 16 KiB block of the packed layout; plain: the weights are read
@@ -672,6 +690,9 @@ struct DmaTile {
     int ncols;                  // plain: columns (I for W13, H otherwise)
     int K;                      // contraction length
     const char* ap[S::A_PW];    // this lane's A chunk (K stage 0), null: padding row
+    const char* qs;             // WNA16: this lane's 16 scale bytes of group 0, or null
+    const char* qz;             //   and its 16 zero-point bytes, or null
+    int64_t qs_g, qz_g;         //   bytes from one K group to the next
 
     // spare: LDS address of the scratch KiB for spare A slots
     __device__ __forceinline__ void issue(int kt, uint32_t lds, uint32_t spare, int wave,
@@ -691,15 +712,16 @@ struct DmaTile {
 #pragma unroll
         for (int j = 0; j < S::B_PW; ++j) {
             const int i = wave + S::NW * j;
-            const int bb = i >> 4, k = 4 * (i & 15) + (lane >> 4);
+            const int bb = i / S::IPB, k = 4 * (i & 15) + (lane >> 4);
             const char* p = zero;
             if constexpr (PACKED) {
                 // a select, not wb[bb]: bb depends on the wave index, and a
                 // runtime index would put wb in scratch memory
                 const char* w = (S::NB == 1 || bb == 0) ? wb[0] : wb[S::NB - 1];
                 if (live && w)
-                    p = w + kt * w_stage + (i & 15) * 1024 + lane * 16;
+                    p = w + kt * w_stage + (i % S::IPB) * 1024 + lane * 16;
             } else {
+                static_assert(S::Q == 0, "WNA16 weights are packed");
                 const int c = (lane & 15) ^ swz_b(k);
                 int col, valid;
                 if constexpr (W13) {
@@ -714,6 +736,13 @@ struct DmaTile {
                     p = wb[0] + (int64_t)(kt * 64 + k) * w_ld + (int64_t)col * 2;
             }
             dma16(p, lds + S::A_BYTES + i * 1024);
+        }
+        if constexpr (S::Q != 0) {
+            const int grp = kt >> 1;            // 128-row K groups, 64-row stages
+            if (wave == 0)
+                dma16((live && qs) ? qs + grp * qs_g : zero, lds + S::SZ_OFF);
+            else if (wave == 1)
+                dma16((live && qz) ? qz + grp * qz_g : zero, lds + S::SZ_OFF + 1024);
         }
     }
 };
@@ -732,7 +761,10 @@ __device__ __forceinline__ void dma_a_slot(int j, int wave, int lane, int& row, 
 template <typename S>
 struct DmaFrag {
     int a_off[2];               // A fragment byte offset within a strip, per MFMA step
-    int b_off[S::FN];           // B fragment byte offset (MFMA step 0, low half)
+    int b_off[S::FN];           // B fragment byte offset (MFMA step 0, low half); WNA16:
+                                //   this lane's codes of MFMA step 0
+    int s_off[S::FN];           // WNA16: this lane's column scale (+ 1024: zero point)
+    int hz;                     // WNA16: zero points given (else 2^(Q-1))
 
     __device__ __forceinline__ void init(int lane, const int (&bblk)[S::FN], const int (&bchunk)[S::FN])
     {
@@ -748,12 +780,85 @@ struct DmaFrag {
                         8 * (s & 1);
     }
 
+    // WNA16: fragment fn is block column group bchunk[fn] / 2 (16 columns);
+    // the lane's 8 codes of MFMA step ks sit at ((2 f + ks) * 64 + lane) * Q bytes
+    __device__ __forceinline__ void init_q(int lane, const int (&bchunk)[S::FN], bool zeros)
+    {
+        const int s = lane & 15, g = lane >> 4;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            a_off[ks] = s * 128 + (((ks * 4 + g) ^ (s >> 1)) * 16);
+#pragma unroll
+        for (int fn = 0; fn < S::FN; ++fn) {
+            const int f = bchunk[fn] >> 1;
+            b_off[fn] = S::A_BYTES + (2 * f * 64 + lane) * S::Q;
+            s_off[fn] = S::SZ_OFF + (16 * f + s) * 4;
+        }
+        hz = zeros ? 1 : 0;
+    }
+
+    // the 8 bf16 weights of a WNA16 fragment: w = q * sc + bz, bz = -z * sc
+    __device__ __forceinline__ static bf16x8 dequant(const char* p, float sc, float bz)
+    {
+        float w[8];
+        if constexpr (S::Q == 8) {
+            const i32x2 c = *(const i32x2*)p;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                w[i] = fmaf((float)(((uint32_t)c[i >> 2] >> (8 * (i & 3))) & 255u), sc, bz);
+        } else {
+            // code i is nibble i & 1 of byte i / 2: even codes from the low
+            // nibbles, odd ones from the high nibbles, byte by byte
+            const uint32_t c = *(const uint32_t*)p;
+            const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                w[2 * b] = fmaf((float)((lo >> (8 * b)) & 255u), sc, bz);
+                w[2 * b + 1] = fmaf((float)((hi >> (8 * b)) & 255u), sc, bz);
+            }
+        }
+        bf16x8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = (__bf16)w[i];
+        return v;
+    }
+
     // the MFMAs of the wave's first NM strips (the others hold only padding)
     template <int NM>
     __device__ __forceinline__ void stage(const char* st, int rg, f32x4 (&acc)[S::FMW][S::FN]) const
     {
         const char* As = st + rg * S::FMW * 2048;
         const char* Bs = st + S::A_BYTES;
+        if constexpr (S::Q != 0) {
+            constexpr float ZDEF = (S::Q == 8) ? 128.0f : 8.0f;
+            float sc[S::FN], bz[S::FN];
+#pragma unroll
+            for (int fn = 0; fn < S::FN; ++fn) {
+                sc[fn] = *(const float*)(st + s_off[fn]);
+                const float z = hz ? (float)*(const uint8_t*)(st + S::SZ_OFF + 1024 +
+                                                              (s_off[fn] - S::SZ_OFF) / 4)
+                                   : ZDEF;
+                bz[fn] = -z * sc[fn];
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 a[NM], b[S::FN];
+#pragma unroll
+                for (int fn = 0; fn < S::FN; ++fn)
+                    b[fn] = dequant(st + b_off[fn] + ks * 64 * S::Q, sc[fn], bz[fn]);
+#pragma unroll
+                for (int fm = 0; fm < NM; ++fm)
+                    a[fm] = __builtin_bit_cast(bf16x8, *(const i32x4*)(As + fm * 2048 + a_off[ks]));
+#pragma unroll
+                for (int fm = 0; fm < NM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < S::FN; ++fn)
+                        acc[fm][fn] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+            }
+            return;
+        }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             bf16x8 a[NM], b[S::FN];
@@ -827,14 +932,34 @@ __device__ __forceinline__ void gemm1_src(const Gemm1Args& g, const TileRef& t,
     d.ncols = I;
     d.K = H;
     d.w_ld = (int64_t)N * 2;
+    d.qs = d.qz = nullptr;
+    d.qs_g = d.qz_g = 0;
     if constexpr (PACKED) {
         const int64_t nblk = (I + 63) / 64, nks = (H + 63) / 64;
-        d.w_stage = nblk * PACK_BLOCK;
+        d.w_stage = nblk * S::QB;
 #pragma unroll
         for (int bb = 0; bb < S::NB; ++bb) {
             const int64_t jb = n0 / 64 + bb;
-            d.wb[bb] = (jb < nblk) ? (const char*)g.w13 + (t.e * nks * nblk + jb) * PACK_BLOCK
+            d.wb[bb] = (jb < nblk) ? (const char*)g.w13 + (t.e * nks * nblk + jb) * S::QB
                                    : nullptr;
+        }
+        if constexpr (S::Q != 0) {
+            // the block's group scales / zero points: gate z columns n0 .. n0 + 63
+            // (block columns 0-63), then the up ones (64-127); lanes 0-31 take 4
+            // scales each, lanes 0-7 16 zero points each
+            const int64_t ngk = (H + 127) / 128, base = (int64_t)t.e * ngk * N;
+            d.qs_g = (int64_t)N * 4;
+            d.qz_g = N;
+            if (lane < 32) {
+                const int c = n0 + 4 * (lane & 15);
+                if (c < I)
+                    d.qs = (const char*)(g.w13_scale + base + (lane < 16 ? c : I + c));
+            }
+            if (lane < 8 && g.w13_zero) {
+                const int c = n0 + 16 * (lane & 3);
+                if (c < I)
+                    d.qz = (const char*)(g.w13_zero + base + (lane < 4 ? c : I + c));
+            }
         }
     } else {
         d.wb[0] = (const char*)g.w13 + (int64_t)t.e * H * N * 2;
@@ -861,14 +986,26 @@ __device__ __forceinline__ void gemm2_src(const Gemm2Args& g, const TileRef& t, 
     d.ncols = H;
     d.K = I;
     d.w_ld = (int64_t)H * 2;
+    d.qs = d.qz = nullptr;
+    d.qs_g = d.qz_g = 0;
     if constexpr (PACKED) {
         const int64_t nblk = (H + 127) / 128, nks = (I + 63) / 64;
-        d.w_stage = nblk * PACK_BLOCK;
+        d.w_stage = nblk * S::QB;
 #pragma unroll
         for (int bb = 0; bb < S::NB; ++bb) {
             const int64_t jb = c0 / 128 + bb;
-            d.wb[bb] = (jb < nblk) ? (const char*)g.w2 + (t.e * nks * nblk + jb) * PACK_BLOCK
+            d.wb[bb] = (jb < nblk) ? (const char*)g.w2 + (t.e * nks * nblk + jb) * S::QB
                                    : nullptr;
+        }
+        if constexpr (S::Q != 0) {
+            // the block's group scales / zero points: columns c0 .. c0 + 127
+            const int64_t ngi = (I + 127) / 128, base = (int64_t)t.e * ngi * H;
+            d.qs_g = (int64_t)H * 4;
+            d.qz_g = H;
+            if (lane < 32 && c0 + 4 * lane < H)
+                d.qs = (const char*)(g.w2_scale + base + c0 + 4 * lane);
+            if (lane < 8 && g.w2_zero && c0 + 16 * lane < H)
+                d.qz = (const char*)(g.w2_zero + base + c0 + 16 * lane);
         }
     } else {
         d.wb[0] = (const char*)g.w2 + (int64_t)t.e * I * H * 2;
@@ -903,11 +1040,11 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[S::FMW][S::FN])
 // the next tile's first stages are issued and the current tile's epilogue
 // (bias, SiLU(gate) * up, bf16 z stores straight from the accumulators) runs
 // while they are in flight.
-template <int FMW, int WC, int NS, bool PACKED>
+template <int FMW, int WC, int NS, bool PACKED, int Q = 0>
 __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
     k_gemm1_dma(Gemm1Args g)
 {
-    typedef DS<FMW, WC, NS> S;
+    typedef DS<FMW, WC, NS, Q> S;
     constexpr int FN = S::FN;
     constexpr int FH = FN / 2;
     __shared__ __attribute__((aligned(16))) char ring[S::RING];
@@ -937,7 +1074,10 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
         bchunk[fn] = (fn < FH ? 0 : 8) + (zc % 64) / 8;
     }
     DmaFrag<S> fr;
-    fr.init(lane, bblk, bchunk);
+    if constexpr (Q != 0)
+        fr.init_q(lane, bchunk, g.w13_zero != nullptr);
+    else
+        fr.init(lane, bblk, bchunk);
     const int g4 = lane >> 4, s16 = lane & 15;
 
     for (;;) {
@@ -1017,11 +1157,11 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
 
 // Persistent GEMM2 over this workgroup's tiles, pipelined across tiles like
 // GEMM1; the epilogue (bias, output rows) runs straight from the accumulators.
-template <int FMW, int WC, int NS, bool PACKED>
+template <int FMW, int WC, int NS, bool PACKED, int Q = 0>
 __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
     k_gemm2_dma(Gemm2Args g)
 {
-    typedef DS<FMW, WC, NS> S;
+    typedef DS<FMW, WC, NS, Q> S;
     constexpr int FN = S::FN;
     __shared__ __attribute__((aligned(16))) char ring[S::RING];
     const int lane = threadIdx.x & 63;
@@ -1058,7 +1198,10 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
         bchunk[fn] = (cl % 128) / 8;
     }
     DmaFrag<S> fr;
-    fr.init(lane, bblk, bchunk);
+    if constexpr (Q != 0)
+        fr.init_q(lane, bchunk, g.w2_zero != nullptr);
+    else
+        fr.init(lane, bblk, bchunk);
     const int g4 = lane >> 4, s16 = lane & 15;
 
     for (;;) {
@@ -1194,6 +1337,92 @@ hipError_t launch_pack_weights(int E, int H, int I, const void* w13, const void*
     return hipGetLastError();
 }
 
+// One-time re-layout of WNA16 weight codes (Q = 8: one byte per weight; Q = 4:
+// two per byte along N, the even column in the low nibble) into blocks of
+// 128 columns x 64 K in MFMA fragment order (the layout in moe.h): one
+// thread per lane group of 8 codes of one column.  Codes past K or N are 0.
+//   w13 [E, H, 2I]: block (e, kt, j), j < ceil(I / 64): block columns 0-63 =
+//     gate columns 64 j .., 64-127 = up columns I + 64 j ..
+//   w2 [E, I, H]: block (e, kt, j), j < ceil(H / 128): columns 128 j ..
+template <bool W13, int Q>
+__global__ void __launch_bounds__(256) k_pack_wq(const uint8_t* __restrict__ w, int H, int I,
+                                                 uint8_t* __restrict__ out, int64_t groups)
+{
+    const int K = W13 ? H : I, N = W13 ? 2 * I : H;
+    const int64_t nblk = W13 ? (I + 63) / 64 : (H + 127) / 128, nks = (K + 63) / 64;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < groups;
+         q += (int64_t)gridDim.x * 256) {
+        const int l = (int)(q & 63), ks = (int)((q >> 6) & 1), f = (int)((q >> 7) & 7);
+        const int64_t b = q >> 10;                      // block (e, kt, j)
+        const int j = (int)(b % nblk);
+        const int kt = (int)((b / nblk) % nks);
+        const int64_t e = b / nblk / nks;
+        const int c = 16 * f + (l & 15);                // block column
+        int col;
+        bool valid;
+        if constexpr (W13) {
+            const int zc = 64 * j + (c & 63);
+            valid = zc < I;
+            col = (c < 64) ? zc : I + zc;
+        } else {
+            col = 128 * j + c;
+            valid = col < H;
+        }
+        const int k0 = 64 * kt + 32 * ks + 8 * (l >> 4);
+        uint32_t code[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = k0 + i;
+            code[i] = 0;
+            if (valid && row < K) {
+                const int64_t r = e * K + row;
+                if constexpr (Q == 8)
+                    code[i] = w[r * N + col];
+                else
+                    code[i] = (w[r * (N / 2) + col / 2] >> (4 * (col & 1))) & 15u;
+            }
+        }
+        if constexpr (Q == 8) {
+            const uint32_t lo = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+            const uint32_t hi = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+            *(i32x2*)(out + q * 8) = i32x2{(int)lo, (int)hi};
+        } else {
+            uint32_t v = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v |= code[i] << (4 * i);                // code i: nibble i & 1 of byte i / 2
+            *(uint32_t*)(out + q * 4) = v;
+        }
+    }
+}
+
+template <int Q>
+static hipError_t pack_wq(int E, int H, int I, const void* w13, const void* w2, void* p13,
+                          void* p2, hipStream_t s)
+{
+    const int64_t g13 = (int64_t)E * ((H + 63) / 64) * ((I + 63) / 64) * 1024;
+    const int64_t g2 = (int64_t)E * ((I + 63) / 64) * ((H + 127) / 128) * 1024;
+    auto grid = [](int64_t n) {
+        const int64_t b = (n + 255) / 256;
+        return (unsigned)(b < 16384 ? b : 16384);
+    };
+    hipLaunchKernelGGL((k_pack_wq<true, Q>), dim3(grid(g13)), dim3(256), 0, s,
+                       (const uint8_t*)w13, H, I, (uint8_t*)p13, g13);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess)
+        return err;
+    hipLaunchKernelGGL((k_pack_wq<false, Q>), dim3(grid(g2)), dim3(256), 0, s,
+                       (const uint8_t*)w2, H, I, (uint8_t*)p2, g2);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_weights_wq(int bits, int E, int H, int I, const void* w13, const void* w2,
+                                  void* p13, void* p2, hipStream_t s)
+{
+    return bits == 8 ? pack_wq<8>(E, H, I, w13, w2, p13, p2, s)
+                     : pack_wq<4>(E, H, I, w13, w2, p13, p2, s);
+}
+
 // ---------------------------------------------------------------- launchers
 template <int DT, int FM, int WN>
 static hipError_t run_gemm1(const Gemm1Args& a, const Plan& P, hipStream_t s)
@@ -1223,14 +1452,14 @@ static hipError_t run_gemm2(const Gemm2Args& a, const Plan& P, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int FMW, int WC, int NS, bool PACKED>
+template <int FMW, int WC, int NS, bool PACKED, int Q = 0>
 static hipError_t run_gemm1_dma(const Gemm1Args& a, const Plan& P, hipStream_t s)
 {
-    typedef DS<FMW, WC, NS> S;
+    typedef DS<FMW, WC, NS, Q> S;
     constexpr int BNZ = S::BN / 2;
     Gemm1Args g = a;
     g.s.n_tiles = (a.I + BNZ - 1) / BNZ;
-    auto kern = k_gemm1_dma<FMW, WC, NS, PACKED>;
+    auto kern = k_gemm1_dma<FMW, WC, NS, PACKED, Q>;
     static int cached = 0;
     const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, S::NT)),
         block(S::NT);
@@ -1238,13 +1467,13 @@ static hipError_t run_gemm1_dma(const Gemm1Args& a, const Plan& P, hipStream_t s
     return hipGetLastError();
 }
 
-template <int FMW, int WC, int NS, bool PACKED>
+template <int FMW, int WC, int NS, bool PACKED, int Q = 0>
 static hipError_t run_gemm2_dma(const Gemm2Args& a, const Plan& P, hipStream_t s)
 {
-    typedef DS<FMW, WC, NS> S;
+    typedef DS<FMW, WC, NS, Q> S;
     Gemm2Args g = a;
     g.s.n_tiles = (a.H + S::BN - 1) / S::BN * g.ksplit;
-    auto kern = k_gemm2_dma<FMW, WC, NS, PACKED>;
+    auto kern = k_gemm2_dma<FMW, WC, NS, PACKED, Q>;
     static int cached = 0;
     const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, S::NT)),
         block(S::NT);
@@ -1302,6 +1531,27 @@ static Sched make_sched(const Plan& P)
 //   TILE_MID       4 strips, CH 64
 //   TILE_DECODE    1 strip,  CH 16: a few rows per expert
 //   TILE_FP8       8 strips, CH 128, 128-column z groups
+// WNA16 (Q code bits) runs the DMA tile families with one weight block a tile.
+template <int Q>
+static hipError_t launch_gemm1_wq(const Gemm1Args& g, const Plan& P, hipStream_t s)
+{
+    switch (P.cfg) {
+    case TILE_DECODE_DMA: return run_gemm1_dma<1, 2, 4, true, Q>(g, P, s);
+    case TILE_MID_DMA: return run_gemm1_dma<2, 2, 3, true, Q>(g, P, s);
+    default: return run_gemm1_dma<5, 2, 2, true, Q>(g, P, s);
+    }
+}
+
+template <int Q>
+static hipError_t launch_gemm2_wq(const Gemm2Args& g, const Plan& P, hipStream_t s)
+{
+    switch (P.cfg) {
+    case TILE_DECODE_DMA: return run_gemm2_dma<1, 2, 4, true, Q>(g, P, s);
+    case TILE_MID_DMA: return run_gemm2_dma<2, 2, 3, true, Q>(g, P, s);
+    default: return run_gemm2_dma<5, 2, 2, true, Q>(g, P, s);
+    }
+}
+
 hipError_t launch_gemm1(const Plan& P, const moe_args& A, const float* row_w, hipStream_t s)
 {
     Gemm1Args g{};
@@ -1328,6 +1578,7 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, const float* row_w, hi
     g.w13 = A.w13;
     g.w_packed = P.wpacked;
     g.w13_scale = A.w13_scale;
+    g.w13_zero = A.w13_zero;
     g.blk = P.blk;
     g.a_sld = P.blk ? (P.H + 127) / 128 : 1;
     g.b13 = P.has_b13 ? A.w13_bias : nullptr;
@@ -1341,6 +1592,10 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, const float* row_w, hi
         return P.wpacked ? launch_gemm1_fp8(g, P, s) : run_gemm1<MOE_FP8_E4M3FN, 8, 32>(g, P, s);
     if (P.wdt == MOE_F32)
         return run_gemm1<MOE_F32, 1, 16>(g, P, s);
+    if (P.wq == 8)
+        return launch_gemm1_wq<8>(g, P, s);
+    if (P.wq == 4)
+        return launch_gemm1_wq<4>(g, P, s);
     switch (P.cfg) {
     case TILE_PREFILL:
         // a few tiles per CU (few experts, wide I): 256-column tiles, 8 waves and
@@ -1373,6 +1628,7 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
     g.w2 = A.w2;
     g.w_packed = P.wpacked;
     g.w2_scale = A.w2_scale;
+    g.w2_zero = A.w2_zero;
     g.blk = P.blk;
     g.b2 = P.has_b2 ? A.w2_bias : nullptr;
     g.bias_dt = (P.act == MOE_F32) ? MOE_F32 : MOE_BF16;
@@ -1398,6 +1654,10 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
         return P.wpacked ? launch_gemm2_fp8(g, P, s) : run_gemm2<MOE_FP8_E4M3FN, 8, 32>(g, P, s);
     if (P.wdt == MOE_F32)
         return run_gemm2<MOE_F32, 1, 16>(g, P, s);
+    if (P.wq == 8)
+        return launch_gemm2_wq<8>(g, P, s);
+    if (P.wq == 4)
+        return launch_gemm2_wq<4>(g, P, s);
     switch (P.cfg) {
     case TILE_PREFILL:
         if (P.g2split) {   // 256-column tiles over two K halves

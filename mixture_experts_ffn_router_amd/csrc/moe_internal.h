@@ -209,6 +209,7 @@ struct Plan {
     int wpacked;                    // weights in the packed block layout (bf16 / fp8)
     int blk;                        // fp8: block-wise scales (128 x 128 weight blocks,
                                     // activation scales per row and 128 columns)
+    int wq;                         // WNA16 weight code bits (8 or 4), 0 otherwise
     int BM;                         // align granularity: each expert run padded to BM rows
     int CH;                         // rows per GEMM tile (a multiple of BM)
     int cfg;                        // GEMM tile family (see moe_gemm.hip)
@@ -240,6 +241,10 @@ struct Plan {
 // Row stride of the group-major fp8 z scales: every padded position plus one
 // GEMM tile of rows, so a tile may read its rows' scales as one block.
 inline int64_t zs_ld(int64_t max_sorted) { return max_sorted + 256; }
+
+// WNA16 packed weight codes (moe_gemm.hip): bits 8 or 4
+hipError_t launch_pack_weights_wq(int bits, int E, int H, int I, const void* w13, const void* w2,
+                                  void* p13, void* p2, hipStream_t s);
 
 // fp8 packed weights (moe_gemm_fp8.hip)
 hipError_t launch_pack_weights_fp8(int E, int H, int I, const void* w13, const void* w2,

@@ -36,9 +36,12 @@ class MoeConfig:
     top_k: int
     fmt: str = "contiguous"          # "contiguous" (M,K) or "batched" (E,max_tokens,K)
     act: str = "bf16"                # activation storage: f32 | bf16
-    weight: str = "bf16"             # f32 | bf16 | fp8 (per-output-channel scales)
+    weight: str = "bf16"             # f32 | bf16 | fp8 (per-output-channel scales) |
+                                     # u8 | u4 (WNA16 codes, group scales per 128 K rows)
     fp8_block: int = 0               # fp8: 128 = block-wise scales (128 x 128 weight
                                      # blocks, activations per token and 128 columns)
+    wq_zero: bool = False            # u8 / u4 (WNA16): per-group zero points (asymmetric);
+                                     # False: symmetric codes around 2^(bits-1)
     scoring: str = "softmax"         # softmax | sigmoid
     renormalize: bool = True
     group_count: int = 1
@@ -97,7 +100,13 @@ EP8_SHARD = DEEPSEEK_GROUPED.scaled(name="ep8_shard_deepseek_bf16", M=32768, loc
 # form DeepSeek-V3-class checkpoints ship.
 DEEPSEEK_BLOCKFP8 = DEEPSEEK_GROUPED.scaled(name="deepseek_blockfp8", weight="fp8", fp8_block=128)
 
-EXTRA = [EP8_SHARD, DEEPSEEK_BLOCKFP8]
+# Decode with WNA16 weights (the decode-sized layer of C3): 4-bit codes with
+# symmetric groups (GPTQ-style default zero point 8), and 8-bit codes with
+# per-group zero points.
+DECODE_W4A16 = DECODE_SMALL_EXPERTS.scaled(name="decode_e128_w4a16", weight="u4")
+DECODE_W8A16 = DECODE_SMALL_EXPERTS.scaled(name="decode_e128_w8a16", weight="u8", wq_zero=True)
+
+EXTRA = [EP8_SHARD, DEEPSEEK_BLOCKFP8, DECODE_W4A16, DECODE_W8A16]
 BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -138,6 +147,32 @@ def quantize_weight_fp8_blocks(w: torch.Tensor, B: int = 128):
     return codes, scale
 
 
+def quantize_weight_wna16(w: torch.Tensor, bits: int, zero: bool, G: int = 128):
+    """WNA16 codes of w [E, K, N] float32, one scale (and zero point) per G
+    K rows and column: symmetric s = amax / (2^(bits-1) - 1) around the
+    default zero point 2^(bits-1), or asymmetric s = (max - min) / (2^bits - 1)
+    with z = round(-min / s).  Returns (codes uint8 [E, K, N], or two per byte
+    along N for 4 bits [E, K, N / 2]; scale float32 [E, ceil(K/G), N]; zero
+    uint8 of the same shape, or None)."""
+    E, K, N = w.shape
+    ng = -(-K // G)
+    qmax = 2 ** bits - 1
+    wp = torch.nn.functional.pad(w, (0, 0, 0, ng * G - K)).view(E, ng, G, N)
+    if zero:
+        lo, hi = wp.amin(dim=2), wp.amax(dim=2)
+        s = torch.where(hi > lo, (hi - lo) / qmax, torch.ones_like(hi))
+        z = torch.round(-lo / s).clamp_(0, qmax)
+    else:
+        amax = wp.abs().amax(dim=2)
+        s = torch.where(amax > 0, amax / (2 ** (bits - 1) - 1), torch.ones_like(amax))
+        z = torch.full_like(s, 2 ** (bits - 1))
+    q = torch.round(wp / s[:, :, None, :] + z[:, :, None, :]).clamp_(0, qmax)
+    q = q.view(E, ng * G, N)[:, :K].to(torch.uint8)
+    if bits == 4:
+        q = q[..., 0::2] | (q[..., 1::2] << 4)
+    return q.contiguous(), s.to(torch.float32), (z.to(torch.uint8) if zero else None)
+
+
 def make_inputs(cfg: MoeConfig, seed: int, device="cpu") -> dict:
     """Draws every input of one forward.  Order of draws: hidden, logits
     (+ offsets), w13, w2, w13_bias, w2_bias."""
@@ -157,7 +192,7 @@ def make_inputs(cfg: MoeConfig, seed: int, device="cpu") -> dict:
         logits += offset[None, :]
     logits = logits.to(_TORCH_DT[cfg.logits_dtype])
 
-    w_dt = torch.float32 if cfg.weight == "fp8" else _TORCH_DT[cfg.weight]
+    w_dt = torch.float32 if cfg.weight in ("fp8", "u8", "u4") else _TORCH_DT[cfg.weight]
     if cfg.local_experts:                       # the shard's experts only
         E = cfg.local_experts
         emap = torch.full((cfg.E,), -1, dtype=torch.int32, device=device)
@@ -165,7 +200,14 @@ def make_inputs(cfg: MoeConfig, seed: int, device="cpu") -> dict:
         out["expert_map"] = emap
     w13 = _randn((E, H, 2 * I), gen, device, std=1.0 / math.sqrt(H), dtype=w_dt)
     w2 = _randn((E, I, H), gen, device, std=1.0 / math.sqrt(I), dtype=w_dt)
-    if cfg.weight == "fp8":
+    if cfg.weight in ("u8", "u4"):
+        bits = 8 if cfg.weight == "u8" else 4
+        out["w13"], out["w13_scale"], out["w13_zero"] = quantize_weight_wna16(w13, bits,
+                                                                               cfg.wq_zero)
+        del w13
+        out["w2"], out["w2_scale"], out["w2_zero"] = quantize_weight_wna16(w2, bits, cfg.wq_zero)
+        del w2
+    elif cfg.weight == "fp8":
         quant = quantize_weight_fp8_blocks if cfg.fp8_block else quantize_weight_fp8
         out["w13"], out["w13_scale"] = quant(w13)
         del w13

@@ -21,6 +21,8 @@ TOL_F32_ABS = 1e-4
 TOL_BF16_RMS = 2e-2
 TOL_FP8_RMS = 6e-2
 TOL_WEIGHT = 1e-5          # routing weights, relative to max(1, routed_scaling_factor)
+# WNA16 (u8 / u4 codes, bf16 activations) is held to the bf16 bound
+WQ_BITS = {"u8": 8, "u4": 4}
 
 
 def device():
@@ -49,9 +51,12 @@ def run_contiguous(inp: dict, dev, precomputed=None, out=None, inplace=False, ou
     if cfg.fp8_block:
         packed = True                   # block-wise scales run on the packed fp8 kernels
         kw["fp8_block"] = cfg.fp8_block
+    bits = WQ_BITS.get(cfg.weight, 0)
+    if bits:
+        packed = True                   # WNA16 codes run packed
     if packed:
-        w13, w2 = B.pack_weights(w13, w2), None
-    for name in ("w13_bias", "w2_bias", "w13_scale", "w2_scale"):
+        w13, w2 = B.pack_weights(w13, w2, wq_bits=bits), None
+    for name in ("w13_bias", "w2_bias", "w13_scale", "w2_scale", "w13_zero", "w2_zero"):
         if inp.get(name) is not None:
             kw[name] = inp[name].to(dev)
     logits = None
@@ -100,14 +105,17 @@ def check_routing_and_align(inp: dict, ws, info, ids_o=None, w_o=None, check_wei
     return ids_o, w_o
 
 
+def _cpu(t):
+    return None if t is None else t.cpu()
+
+
 def oracle_experts(inp: dict) -> oracle.Experts:
     cfg = inp["cfg"]
-    return oracle.Experts(inp["w13"].cpu(), inp["w2"].cpu(),
-                          None if inp.get("w13_scale") is None else inp["w13_scale"].cpu(),
-                          None if inp.get("w2_scale") is None else inp["w2_scale"].cpu(),
-                          None if inp.get("w13_bias") is None else inp["w13_bias"].cpu(),
-                          None if inp.get("w2_bias") is None else inp["w2_bias"].cpu(),
-                          requant_z=cfg.weight == "fp8", block=cfg.fp8_block)
+    return oracle.Experts(inp["w13"].cpu(), inp["w2"].cpu(), _cpu(inp.get("w13_scale")),
+                          _cpu(inp.get("w2_scale")), _cpu(inp.get("w13_bias")),
+                          _cpu(inp.get("w2_bias")), requant_z=cfg.weight == "fp8",
+                          block=cfg.fp8_block, bits=WQ_BITS.get(cfg.weight, 0),
+                          w13_zero=_cpu(inp.get("w13_zero")), w2_zero=_cpu(inp.get("w2_zero")))
 
 
 def compare(cfg: W.MoeConfig, got: np.ndarray, ref: np.ndarray, what: str = "") -> float:
@@ -142,9 +150,12 @@ def run_batched(inp: dict, dev, reduce=False, out_dtype=None, packed=False):
     if cfg.fp8_block:
         packed = True
         kw["fp8_block"] = cfg.fp8_block
+    bits = WQ_BITS.get(cfg.weight, 0)
+    if bits:
+        packed = True
     if packed:
-        w13, w2 = B.pack_weights(w13, w2), None
-    for name in ("w13_scale", "w2_scale", "w13_bias", "w2_bias"):
+        w13, w2 = B.pack_weights(w13, w2, wq_bits=bits), None
+    for name in ("w13_scale", "w2_scale", "w13_bias", "w2_bias", "w13_zero", "w2_zero"):
         if inp.get(name) is not None:
             kw[name] = inp[name].to(dev)
     if reduce:

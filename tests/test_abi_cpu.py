@@ -121,6 +121,15 @@ def _status(prob):
      B.MOE_ERR_UNSUPPORTED),
     (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_FP8_E4M3FN, fp8_block=-128),
      B.MOE_ERR_INVALID_ARG),
+    # WNA16: 8- / 4-bit codes with bf16 activations, packed only
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U8), B.MOE_OK),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U4, H=80, I=48), B.MOE_OK),
+    (dict(fmt=B.MOE_FMT_BATCHED, max_tokens=8, w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U4),
+     B.MOE_OK),
+    (dict(w_dtype=B.MOE_U4), B.MOE_ERR_UNSUPPORTED),                       # plain layout
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U8, act_dtype=B.MOE_F32, out_dtype=B.MOE_F32),
+     B.MOE_ERR_UNSUPPORTED),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U8, fp8_block=128), B.MOE_ERR_UNSUPPORTED),
 ])
 def test_problem_validation(kw, status):
     assert _status(_prob(**kw)) == status
@@ -171,6 +180,9 @@ def _args(**kw):
     (dict(), dict(w_dtype=B.MOE_FP8_E4M3FN), B.MOE_ERR_INVALID_ARG),      # scales missing
     (dict(), dict(fmt=B.MOE_FMT_BATCHED, max_tokens=8), B.MOE_ERR_INVALID_ARG),
     (dict(), dict(global_experts=32), B.MOE_ERR_INVALID_ARG),       # expert_map missing
+    (dict(), dict(w_dtype=B.MOE_U4, w_layout=B.MOE_W_PACKED), B.MOE_ERR_INVALID_ARG),  # scales
+    (dict(w13_scale=4096, w2_scale=4096, w13_zero=4096), dict(w_dtype=B.MOE_U8,
+     w_layout=B.MOE_W_PACKED), B.MOE_ERR_INVALID_ARG),              # one zero-point grid only
 ])
 def test_forward_rejects_missing_pointers(kw, pkw, status):
     p = _prob(**pkw).c()
@@ -205,6 +217,15 @@ def test_packed_weight_sizes():
         blk = 128 * 128
         assert b13 == E * (I // 64) * -(-H // 128) * blk
         assert b2 == E * -(-H // 128) * (I // 128) * blk
+    # WNA16: blocks of 128 columns x 64 K codes (8 or 4 KiB): w13 ceil(I/64) x
+    # ceil(H/64), w2 ceil(H/128) x ceil(I/64); the plain problem sizes them too
+    for E, H, I in [(128, 2048, 768), (2, 80, 48), (1, 16, 16)]:
+        for dt, blk in [(B.MOE_U8, 8192), (B.MOE_U4, 4096)]:
+            for layout in (B.MOE_W_PLAIN, B.MOE_W_PACKED):
+                b13, b2 = B.moe_packed_weight_bytes(
+                    _prob(E=E, H=H, I=I, top_k=1, w_dtype=dt, w_layout=layout).c())
+                assert b13 == E * -(-I // 64) * -(-H // 64) * blk
+                assert b2 == E * -(-H // 128) * -(-I // 64) * blk
     for kw, status in [(dict(w_dtype=B.MOE_FP8_E4M3FN, I=144), B.MOE_ERR_UNSUPPORTED),
                        (dict(act_dtype=B.MOE_F32, w_dtype=B.MOE_F32, out_dtype=B.MOE_F32),
                         B.MOE_ERR_UNSUPPORTED),

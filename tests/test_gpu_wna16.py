@@ -1,0 +1,127 @@
+"""WNA16 (8- and 4-bit weight codes with group scales and zero points, bf16
+activations) against the CPU oracle, and the packed code layout bit for bit.
+
+Outputs within the bf16 bound (2e-2 x RMS of the oracle's double result):
+the GEMMs dequantise each weight to bf16, which is the precision of the bf16
+path's weights; routing and align bit for bit as everywhere else."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as GH
+from mixture_experts_ffn_router_amd import binding as B
+from mixture_experts_ffn_router_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+WQ_SMALL = [
+    # a few rows per expert (32-row tiles), short last K group (H 320)
+    W.DECODE_SMALL_EXPERTS.scaled(name="w4_decode", M=8, H=320, I=256, E=32, top_k=4,
+                                  weight="u4"),
+    W.DECODE_SMALL_EXPERTS.scaled(name="w8z_decode", M=8, H=320, I=256, E=32, top_k=4,
+                                  weight="u8", wq_zero=True),
+    # about 16 rows per expert (64-row tiles), zero points, biases
+    W.MIXTRAL_PREFILL.scaled(name="w4z_mid", M=64, H=256, I=384, E=8, weight="u4",
+                             wq_zero=True, bias=True),
+    # 256 rows per expert (160-row tiles, two chunks), grouped sigmoid routing
+    W.DEEPSEEK_GROUPED.scaled(name="w8_prefill", M=512, H=256, I=256, E=8, top_k=4,
+                              group_count=4, k_group=2, weight="u8"),
+]
+
+
+@pytest.mark.parametrize("cfg", WQ_SMALL, ids=[c.name for c in WQ_SMALL])
+@pytest.mark.parametrize("seed_off", [0, 1000])
+def test_wna16_small_parity(cfg, seed_off):
+    dev = GH.device()
+    seed = 4000 + WQ_SMALL.index(cfg) + seed_off
+    print(f"[case] {cfg.name} seed={seed}", flush=True)
+    inp = W.make_inputs(cfg, seed)
+    out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+    ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    GH.check_output(inp, out, ids_o, w_o, what=f"seed{seed}")
+    out16, _, _ = GH.run_contiguous(inp, dev)
+    GH.check_rounded(out16, out)
+
+
+def test_wna16_batched():
+    """Batched slabs with 4-bit codes and zero points (rows past the counts
+    are NaN and never reach valid rows)."""
+    import oracle
+    dev = GH.device()
+    cfg = W.BATCHED_FP8.scaled(name="w4_batched", M=96, H=256, I=256, E=8, top_k=2, weight="u4",
+                               wq_zero=True)
+    inp = W.make_inputs(cfg, 4100)
+    out, ws, info = GH.run_batched(inp, dev, out_dtype=torch.float32)
+    GH.check_batched_tilelist(inp, ws, info)
+    rows, experts = GH.batched_rows(inp)
+    ref, _ = oracle.expert_rows(GH.oracle_experts(inp), oracle.Acts(inp["hidden"].cpu()), rows,
+                                experts)
+    got = out.reshape(-1, cfg.H)[torch.as_tensor(rows, device=out.device)]
+    GH.compare(cfg, got.cpu().numpy(), ref, "batched w4")
+
+
+def _fragment_order(codes, bits, w13, H, I):
+    """numpy reference of the documented packed order: blocks (e, kt, j) of
+    128 columns x 64 K rows; lane group ((2 f + h) * 64 + l) holds column
+    16 f + l % 16 and K rows 64 kt + 32 h + 8 (l // 16) + 0..7."""
+    c = codes.astype(np.int64)
+    if bits == 4:
+        c = np.stack([c & 15, c >> 4], -1).reshape(*c.shape[:-1], -1)
+    E, K, N = c.shape
+    nks = -(-K // 64)
+    nblk = -(-I // 64) if w13 else -(-H // 128)
+    out = []
+    for e in range(E):
+        for kt in range(nks):
+            for j in range(nblk):
+                blk = np.zeros((8, 2, 64, 8), np.int64)
+                for f in range(8):
+                    for h in range(2):
+                        for l in range(64):
+                            bc = 16 * f + l % 16
+                            if w13:
+                                zc = 64 * j + bc % 64
+                                col, ok = (zc if bc < 64 else I + zc), zc < I
+                            else:
+                                col = 128 * j + bc
+                                ok = col < H
+                            for i in range(8):
+                                k = 64 * kt + 32 * h + 8 * (l // 16) + i
+                                if ok and k < K:
+                                    blk[f, h, l, i] = c[e, k, col]
+                out.append(blk.reshape(-1, 8))
+    v = np.concatenate(out)
+    if bits == 8:
+        return v.astype(np.uint8).ravel()
+    return (v[:, 0::2] | (v[:, 1::2] << 4)).astype(np.uint8).ravel()
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_wna16_pack_layout(bits):
+    dev = GH.device()
+    E, H, I = 2, 80, 96                 # partial blocks in K and N
+    g = torch.Generator().manual_seed(bits)
+    hi = 256 if bits == 8 else 16
+    q13 = torch.randint(0, hi, (E, H, 2 * I), generator=g, dtype=torch.int64)
+    q2 = torch.randint(0, hi, (E, I, H), generator=g, dtype=torch.int64)
+
+    def store(q):
+        q = q.to(torch.uint8)
+        return q if bits == 8 else (q[..., 0::2] | (q[..., 1::2] << 4)).contiguous()
+    w13, w2 = store(q13), store(q2)
+    pw = B.pack_weights(w13.to(dev), w2.to(dev), wq_bits=bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(pw.w13.cpu().numpy(), _fragment_order(w13.numpy(), bits, True, H, I))
+    assert np.array_equal(pw.w2.cpu().numpy(), _fragment_order(w2.numpy(), bits, False, H, I))
+
+
+@pytest.mark.parametrize("name", ["decode_e128_w4a16", "decode_e128_w8a16"])
+def test_wna16_full_size_decode(name):
+    cfg = W.BY_NAME[name]
+    dev = GH.device()
+    seed = 1100 + W.EXTRA.index(cfg)
+    print(f"[case] {cfg.name} seed={seed}", flush=True)
+    inp = W.make_inputs(cfg, seed, device=dev)
+    out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+    ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    GH.check_output(inp, out, ids_o, w_o, what="full wna16")
