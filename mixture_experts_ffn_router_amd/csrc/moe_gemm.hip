@@ -635,9 +635,11 @@ __global__ void __launch_bounds__(256) k_gemm2(Gemm2Args g)
 // weight block of a stage is 128 columns x 64 K of codes in fragment order
 // (8 or 4 KiB, see the packed layout in moe.h), followed by the stage's
 // group scales (128 floats, 1 KiB slot) and zero points (128 bytes, 1 KiB
-// slot), both DMA'd from the plain [E, K / 128, N] grids.  The B fragments
-// are dequantised to bf16 right after their LDS read: w = (q - z) * s as one
-// FMA q * s + (-z s) on the float code, then a packed RNE conversion.
+// slot), both DMA'd from the plain [E, K / 128, N] grids.  The 160-row tile
+// dequantises its B fragments to bf16 right after their LDS read (w =
+// (q - z) * s as one FMA q * s + (-z s) on the float code, then a packed RNE
+// conversion); the small-row tiles feed the raw codes to the MFMAs and
+// apply s and z per stage (DmaFrag::raw_codes).
 template <int FMW_, int WC_, int NS_, int Q_ = 0>
 struct DS {
     static constexpr int FMW = FMW_, WC = WC_, NS = NS_, Q = Q_;
@@ -797,6 +799,39 @@ struct DmaFrag {
         hz = zeros ? 1 : 0;
     }
 
+    // Raw form of a WNA16 fragment for the small-row tiles: the 8 codes as
+    // exact bf16 integers, 4-bit ones offset by 128 (bf16 bits 0x4300 | q are
+    // 128 + q, built two at a time with one byte permute and one OR), 8-bit
+    // ones converted through float.  A 64-row K stage lies inside one
+    // 128-row scale group, so the stage's products are exactly
+    // s (A Q - (z + offset) A 1): P = A Q and the row sums R = A 1 run on the
+    // MFMAs and the scale / zero point are applied per stage to the
+    // accumulators, instead of to every weight.
+    static constexpr float RAW_OFF = (S::Q == 4) ? 128.0f : 0.0f;
+    __device__ __forceinline__ static bf16x8 raw_codes(const char* p)
+    {
+        if constexpr (S::Q == 4) {
+            const uint32_t c = *(const uint32_t*)p;
+            const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+            i32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                // bytes (lo_q, 0, hi_q, 0): codes 2q and 2q + 1 in the two halves
+                const uint32_t sel = (uint32_t)q | (0x0Cu << 8) | ((uint32_t)(4 + q) << 16) |
+                                     (0x0Cu << 24);
+                v[q] = (int)(__builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u);
+            }
+            return __builtin_bit_cast(bf16x8, v);
+        } else {
+            const i32x2 c = *(const i32x2*)p;
+            bf16x8 v;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = (__bf16)(float)(((uint32_t)c[i >> 2] >> (8 * (i & 3))) & 255u);
+            return v;
+        }
+    }
+
     // the 8 bf16 weights of a WNA16 fragment: w = q * sc + bz, bz = -z * sc
     __device__ __forceinline__ static bf16x8 dequant(const char* p, float sc, float bz)
     {
@@ -830,7 +865,54 @@ struct DmaFrag {
     {
         const char* As = st + rg * S::FMW * 2048;
         const char* Bs = st + S::A_BYTES;
-        if constexpr (S::Q != 0) {
+        if constexpr (S::Q != 0 && S::FMW <= 2) {
+            constexpr float ZDEF = (S::Q == 8) ? 128.0f : 8.0f;
+            float sc[S::FN], szn[S::FN];
+#pragma unroll
+            for (int fn = 0; fn < S::FN; ++fn) {
+                sc[fn] = *(const float*)(st + s_off[fn]);
+                const float z = hz ? (float)*(const uint8_t*)(st + S::SZ_OFF + 1024 +
+                                                              (s_off[fn] - S::SZ_OFF) / 4)
+                                   : ZDEF;
+                szn[fn] = -(z + RAW_OFF) * sc[fn];
+            }
+            const i32x4 ones_bits = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};
+            const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_bits);
+            f32x4 pq[NM][S::FN], rs[NM];
+#pragma unroll
+            for (int fm = 0; fm < NM; ++fm) {
+                rs[fm] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int fn = 0; fn < S::FN; ++fn)
+                    pq[fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                bf16x8 a[NM], b[S::FN];
+#pragma unroll
+                for (int fn = 0; fn < S::FN; ++fn)
+                    b[fn] = raw_codes(st + b_off[fn] + ks * 64 * S::Q);
+#pragma unroll
+                for (int fm = 0; fm < NM; ++fm)
+                    a[fm] = __builtin_bit_cast(bf16x8, *(const i32x4*)(As + fm * 2048 + a_off[ks]));
+#pragma unroll
+                for (int fm = 0; fm < NM; ++fm) {
+                    rs[fm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], ones, rs[fm], 0, 0, 0);
+#pragma unroll
+                    for (int fn = 0; fn < S::FN; ++fn)
+                        pq[fm][fn] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[fn], pq[fm][fn], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int fm = 0; fm < NM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < S::FN; ++fn)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[fm][fn][r] += sc[fn] * pq[fm][fn][r] + szn[fn] * rs[fm][r];
+            return;
+        } else if constexpr (S::Q != 0) {
             constexpr float ZDEF = (S::Q == 8) ? 128.0f : 8.0f;
             float sc[S::FN], bz[S::FN];
 #pragma unroll
