@@ -777,9 +777,14 @@ hipError_t launch_quant_rows(const Plan& P, const void* hidden, hipStream_t s)
 // kernel's inverse permutation; -1 contributes nothing); batched,
 // row = offsets[e] + i for the slab row e*T + i named by token_map.  When
 // GEMM2 ran as two K halves, an item's output is o[row] + o2[row] (that
-// order).  One thread per 4 consecutive columns of one token; no atomics.
-template <typename TOut>
-__global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int M, int H, int K,
+// order).  One workgroup per token: the token's item rows and weights are
+// the same for every thread (scalar loads), items without a row are skipped
+// by a uniform branch.  A thread holds CPT 4-column chunks (256 apart) of
+// the row and loads them for 8 / CPT items at once before accumulating, so
+// eight loads are in flight whatever H; every output element still sums its
+// items in ascending j.  No atomics.
+template <typename TOut, int CPT>
+__global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int H, int K,
                                                 const float* __restrict__ w,
                                                 const int32_t* __restrict__ tmap, int T,
                                                 const int32_t* __restrict__ offsets,
@@ -787,61 +792,97 @@ __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int
                                                 const float* __restrict__ o2,
                                                 TOut* __restrict__ out)
 {
+    constexpr int IU = 8 / CPT;             // items in flight together: IU x CPT loads a thread
+    const int64_t t = blockIdx.x;
     const int cpr = H / 4;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= (int64_t)M * cpr)
-        return;
-    const int t = (int)(gid / cpr), c = (int)(gid % cpr) * 4;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    // eight routed items at a time: their rows and weights, then their
-    // output chunks, are all in flight before the (ordered) accumulation
-    for (int j0 = 0; j0 < K; j0 += 8) {
-        int64_t row[8];
-        float wj[8];
+    for (int c0 = 0; c0 < cpr; c0 += 256 * CPT) {
+        f32x4 acc[CPT];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int j = j0 + u;
-            row[u] = -1;
-            wj[u] = 0.0f;
-            if (j < K) {
-                if (tmap) {
-                    const int flat = tmap[(int64_t)t * K + j];
-                    row[u] = (int64_t)offsets[flat / T] + flat % T;
-                } else {
-                    row[u] = inv[(int64_t)t * K + j];
-                }
-                wj[u] = w ? w[(int64_t)t * K + j] : 1.0f;
-            }
-        }
-        f32x4 v[8];
+        for (int i = 0; i < CPT; ++i)
+            acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int j0 = 0; j0 < K; j0 += IU) {
+            int64_t row[IU];
+            float wj[IU];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            v[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (row[u] >= 0) {
-                v[u] = *(const f32x4*)(o + row[u] * H + c);
-                if (o2) {
-                    const f32x4 v2 = *(const f32x4*)(o2 + row[u] * H + c);
-                    v[u] = f32x4{v[u][0] + v2[0], v[u][1] + v2[1], v[u][2] + v2[2], v[u][3] + v2[3]};
+            for (int u = 0; u < IU; ++u) {
+                const int j = j0 + u;
+                row[u] = -1;
+                wj[u] = 0.0f;
+                if (j < K) {
+                    if (tmap) {
+                        const int flat = tmap[t * K + j];
+                        row[u] = (int64_t)offsets[flat / T] + flat % T;
+                    } else {
+                        row[u] = inv[t * K + j];
+                    }
+                    wj[u] = w ? w[t * K + j] : 1.0f;
                 }
             }
+            f32x4 v[IU][CPT];
+#pragma unroll
+            for (int u = 0; u < IU; ++u) {
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) {
+                    const int q = c0 + threadIdx.x + 256 * i;
+                    v[u][i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    if (row[u] >= 0 && q < cpr) {   // no row: nothing loaded
+                        v[u][i] = *(const f32x4*)(o + row[u] * H + 4 * q);
+                        if (o2) {
+                            const f32x4 v2 = *(const f32x4*)(o2 + row[u] * H + 4 * q);
+                            v[u][i] = f32x4{v[u][i][0] + v2[0], v[u][i][1] + v2[1],
+                                            v[u][i][2] + v2[2], v[u][i][3] + v2[3]};
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < IU; ++u) {
+                if (row[u] < 0)
+                    continue;                       // contributes nothing
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) {
+                    acc[i][0] += wj[u] * v[u][i][0];
+                    acc[i][1] += wj[u] * v[u][i][1];
+                    acc[i][2] += wj[u] * v[u][i][2];
+                    acc[i][3] += wj[u] * v[u][i][3];
+                }
+            }
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (row[u] < 0)
-                continue;                           // no row: contributes nothing
-            acc[0] += wj[u] * v[u][0];
-            acc[1] += wj[u] * v[u][1];
-            acc[2] += wj[u] * v[u][2];
-            acc[3] += wj[u] * v[u][3];
+        for (int i = 0; i < CPT; ++i) {
+            const int q = c0 + threadIdx.x + 256 * i;
+            if (q >= cpr)
+                continue;
+            if constexpr (sizeof(TOut) == 2) {
+                const uint32_t lo = f32_to_bf16(acc[i][0]) | ((uint32_t)f32_to_bf16(acc[i][1]) << 16);
+                const uint32_t hi = f32_to_bf16(acc[i][2]) | ((uint32_t)f32_to_bf16(acc[i][3]) << 16);
+                *(i32x2*)(out + t * H + 4 * q) = i32x2{(int)lo, (int)hi};
+            } else {
+                *(f32x4*)(out + t * H + 4 * q) = acc[i];
+            }
         }
     }
-    if constexpr (sizeof(TOut) == 2) {
-        const uint32_t lo = f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-        const uint32_t hi = f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-        *(i32x2*)(out + (int64_t)t * H + c) = i32x2{(int)lo, (int)hi};
-    } else {
-        *(f32x4*)(out + (int64_t)t * H + c) = acc;
-    }
+}
+
+template <typename TOut>
+static void reduce_launch(const Plan& P, const float* w, const int32_t* tmap, void* out,
+                          hipStream_t s)
+{
+    // chunks a thread holds: enough to cover the row in one pass, at most 8
+    const int per = (P.H / 4 + 255) / 256;
+    const dim3 grid((unsigned)P.M), block(256);
+#define MOE_REDUCE(C)                                                                           \
+    hipLaunchKernelGGL((k_reduce<TOut, C>), grid, block, 0, s, P.o, P.H, P.K, w, tmap, P.T,    \
+                       P.offsets, P.inv, P.o2, (TOut*)out)
+    if (per <= 1)
+        MOE_REDUCE(1);
+    else if (per <= 2)
+        MOE_REDUCE(2);
+    else if (per <= 4)
+        MOE_REDUCE(4);
+    else
+        MOE_REDUCE(8);
+#undef MOE_REDUCE
 }
 
 hipError_t launch_reduce(const Plan& P, const moe_args& A, const float* topk_w, hipStream_t s)
@@ -849,14 +890,10 @@ hipError_t launch_reduce(const Plan& P, const moe_args& A, const float* topk_w, 
     const bool batched = P.fmt == MOE_FMT_BATCHED;
     const float* w = batched ? A.token_map_w : topk_w;
     const int32_t* tmap = batched ? A.token_map : nullptr;
-    const int64_t n = (int64_t)P.M * (P.H / 4);
-    const dim3 grid((unsigned)((n + 255) / 256)), block(256);
     if (P.outdt == MOE_BF16)
-        hipLaunchKernelGGL(k_reduce<u16>, grid, block, 0, s, P.o, P.M, P.H, P.K, w, tmap, P.T,
-                           P.offsets, P.inv, P.o2, (u16*)A.out);
+        reduce_launch<u16>(P, w, tmap, A.out, s);
     else
-        hipLaunchKernelGGL(k_reduce<float>, grid, block, 0, s, P.o, P.M, P.H, P.K, w, tmap, P.T,
-                           P.offsets, P.inv, P.o2, (float*)A.out);
+        reduce_launch<float>(P, w, tmap, A.out, s);
     return hipGetLastError();
 }
 
