@@ -357,91 +357,59 @@ __host__ __device__ constexpr int align_scratch_ints(int E)
     return ALIGN_WAVES * E + 3 * (E + 1) + ALIGN_WAVES;
 }
 
-// The align proper over the n routed items.  ids_s: LDS batch of up to cap
-// items; if ids_g is non-null the batches are loaded from it, otherwise
-// ids_s already holds all n <= cap items.  Called by all 1024 threads.
-__device__ void align_items(const int32_t* __restrict__ ids_g, int n, int* ids_s, int cap,
-                           int* scratch, const AlignOut& O)
+// Item i of ids_g[b0 ..) -> ids_s[i] as a local expert id: through the
+// expert map when there is one; ids outside the routed range, unmapped
+// experts and map values outside [0, E) become -1 (no row).  All threads.
+__device__ void align_load(const int32_t* __restrict__ ids_g, int b0, int len, int* ids_s,
+                           const AlignOut& O)
 {
-    const int E = O.E, BM = O.BM;
-    int* cnt = scratch;                         // [ALIGN_WAVES][E]
-    int* offs = cnt + ALIGN_WAVES * E;          // [E + 1] padded start per expert
-    int* run = offs + (E + 1);                  // [E + 1] next free position (pass 2)
-    int* choff = run + (E + 1);                 // [E + 1] chunk prefix
-    int* tot = choff + (E + 1);                 // [ALIGN_WAVES]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
-    const int nb = (n + cap - 1) / cap;
-
-    // item i of the current batch -> LDS as a local expert id: through the
-    // expert map when there is one; ids outside the routed range, unmapped
-    // experts and map values outside [0, E) become -1 (no row)
-    auto load_batch = [&](int b0, int len) {
-        for (int i0 = 0; i0 < len; i0 += 1024 * 8) {
-            int v[8];
+    const int tid = threadIdx.x, E = O.E;
+    for (int i0 = 0; i0 < len; i0 += 1024 * 8) {
+        int v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * 1024 + tid;
-                v[u] = (i < len) ? ids_g[b0 + i] : -1;
-            }
-            if (O.emap) {
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * 1024 + tid;
+            v[u] = (i < len) ? ids_g[b0 + i] : -1;
+        }
+        if (O.emap) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    v[u] = (v[u] >= 0 && v[u] < O.Er) ? O.emap[v[u]] : -1;
-            }
+            for (int u = 0; u < 8; ++u)
+                v[u] = (v[u] >= 0 && v[u] < O.Er) ? O.emap[v[u]] : -1;
+        }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * 1024 + tid;
-                if (i < len)
-                    ids_s[i] = (v[u] >= 0 && v[u] < E) ? v[u] : -1;
-            }
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * 1024 + tid;
+            if (i < len)
+                ids_s[i] = (v[u] >= 0 && v[u] < E) ? v[u] : -1;
         }
-    };
-    // per-wave counts of a batch of len items: wave w owns [w*ch, (w+1)*ch)
-    auto count_waves = [&](int len) {
-        for (int i = tid; i < ALIGN_WAVES * E; i += 1024)
-            cnt[i] = 0;
-        __syncthreads();
-        const int ch = (len + ALIGN_WAVES - 1) / ALIGN_WAVES;
-        const int end = min(len, (wave + 1) * ch);
-        for (int i = wave * ch + lane; i < end; i += 64) {
-            const int e = ids_s[i];
-            if (e >= 0)
-                atomicAdd(&cnt[wave * E + e], 1);
-        }
-        __syncthreads();
-    };
-
-    // pass 1: per-expert totals
-    int total_e = 0;
-    if (nb <= 1) {
-        if (ids_g)
-            load_batch(0, n);
-        __syncthreads();
-        count_waves(n);
-        if (tid < E)
-            for (int w = 0; w < ALIGN_WAVES; ++w)
-                total_e += cnt[w * E + tid];
-    } else {
-        for (int i = tid; i < E; i += 1024)
-            run[i] = 0;
-        for (int b = 0; b < nb; ++b) {
-            const int b0 = b * cap, len = min(cap, n - b0);
-            __syncthreads();
-            load_batch(b0, len);
-            __syncthreads();
-            for (int i = tid; i < len; i += 1024) {
-                const int e = ids_s[i];
-                if (e >= 0)
-                    atomicAdd(&run[e], 1);
-            }
-        }
-        __syncthreads();
-        if (tid < E)
-            total_e = run[tid];
     }
+}
 
-    // padded offsets, counts, expert ids, sentinel padding
+// Per-wave counts of ids_s[0, len): wave w owns [w ch, (w+1) ch) and
+// cnt[w][e] counts its items of expert e.  Starts and ends with a barrier.
+__device__ void align_count_waves(const int* ids_s, int len, int* cnt, int E)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < ALIGN_WAVES * E; i += 1024)
+        cnt[i] = 0;
+    __syncthreads();
+    const int ch = (len + ALIGN_WAVES - 1) / ALIGN_WAVES;
+    const int end = min(len, (wave + 1) * ch);
+    for (int i = wave * ch + lane; i < end; i += 64) {
+        const int e = ids_s[i];
+        if (e >= 0)
+            atomicAdd(&cnt[wave * E + e], 1);
+    }
+    __syncthreads();
+}
+
+// From per-expert totals (thread e < E holds total_e): counts, padded
+// offsets, sentinel padding, num_post_padded, GEMM row chunks and block
+// expert ids; offs[e] = run[e] = the expert's first padded position.
+__device__ void align_layout(int total_e, int* offs, int* run, int* choff, int* tot,
+                             const AlignOut& O)
+{
+    const int tid = threadIdx.x, E = O.E, BM = O.BM;
     const int e = tid;
     const int padded = (e < E) ? (total_e + BM - 1) / BM * BM : 0;
     int start;
@@ -462,51 +430,183 @@ __device__ void align_items(const int32_t* __restrict__ ids_g, int n, int* ids_s
     write_chunks((e < E) ? total_e : 0, O.CH, E, tot, choff, O.chunk_off, O.chunk_expert);
     for (int b = tid; b < total / BM && b < O.max_blocks; b += 1024)
         O.expert_ids[b] = upper_index(offs, E, b * BM);
+}
+
+// Stable scatter of ids_s[0, len) (routed items b0 ..): with cnt holding
+// the per-wave counts and run[e] the next free position of expert e, wave
+// w's items of expert e go to run[e] + (items of e in waves < w) + their
+// rank; run advances past the batch.  Writes sorted ids and inv.
+__device__ void align_scatter(const int* ids_s, int b0, int len, int* cnt, int* run,
+                              const AlignOut& O)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, E = O.E;
+    const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
+    // cnt[w][e] <- first position of wave w's items of expert e
+    if (tid < E) {
+        int base = run[tid];
+        for (int w = 0; w < ALIGN_WAVES; ++w) {
+            const int c = cnt[w * E + tid];
+            cnt[w * E + tid] = base;
+            base += c;
+        }
+        run[tid] = base;
+    }
+    __syncthreads();
+    const int ch = (len + ALIGN_WAVES - 1) / ALIGN_WAVES;
+    const int end = min(len, (wave + 1) * ch);
+    for (int i0 = wave * ch; i0 < end; i0 += 64) {
+        const int i = i0 + lane;
+        const int ev = (i < end) ? ids_s[i] : -1;
+        const bool valid = ev >= 0;
+        const unsigned long long m = match_mask(ev, valid, nbits);
+        const int r = b0 + i;
+        if (valid) {
+            const int rank = __popcll(m & ((1ull << lane) - 1ull));
+            const int64_t pos = (int64_t)cnt[wave * E + ev] + rank;
+            if (pos < O.max_sorted)
+                O.sorted[pos] = r;
+            O.inv[r] = (pos < O.max_sorted) ? (int)pos : -1;
+        } else if (i < end) {
+            O.inv[r] = -1;                          // expert id out of range: no row
+        }
+        // every lane has read its base before the leader moves it on
+        __builtin_amdgcn_wave_barrier();
+        if (valid && lane == (int)__builtin_ctzll(m))
+            cnt[wave * E + ev] += __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// The align proper over the n routed items, in one workgroup.  ids_s: LDS
+// batch of up to cap items; if ids_g is non-null the batches are loaded from
+// it, otherwise ids_s already holds all n <= cap items.  All 1024 threads.
+__device__ void align_items(const int32_t* __restrict__ ids_g, int n, int* ids_s, int cap,
+                           int* scratch, const AlignOut& O)
+{
+    const int E = O.E;
+    int* cnt = scratch;                         // [ALIGN_WAVES][E]
+    int* offs = cnt + ALIGN_WAVES * E;          // [E + 1] padded start per expert
+    int* run = offs + (E + 1);                  // [E + 1] next free position (pass 2)
+    int* choff = run + (E + 1);                 // [E + 1] chunk prefix
+    int* tot = choff + (E + 1);                 // [ALIGN_WAVES]
+    const int tid = threadIdx.x;
+    const int nb = (n + cap - 1) / cap;
+
+    // pass 1: per-expert totals
+    int total_e = 0;
+    if (nb <= 1) {
+        if (ids_g)
+            align_load(ids_g, 0, n, ids_s, O);
+        __syncthreads();
+        align_count_waves(ids_s, n, cnt, E);
+        if (tid < E)
+            for (int w = 0; w < ALIGN_WAVES; ++w)
+                total_e += cnt[w * E + tid];
+    } else {
+        for (int i = tid; i < E; i += 1024)
+            run[i] = 0;
+        for (int b = 0; b < nb; ++b) {
+            const int b0 = b * cap, len = min(cap, n - b0);
+            __syncthreads();
+            align_load(ids_g, b0, len, ids_s, O);
+            __syncthreads();
+            for (int i = tid; i < len; i += 1024) {
+                const int e = ids_s[i];
+                if (e >= 0)
+                    atomicAdd(&run[e], 1);
+            }
+        }
+        __syncthreads();
+        if (tid < E)
+            total_e = run[tid];
+    }
+
+    align_layout(total_e, offs, run, choff, tot, O);
 
     // pass 2: stable scatter, batch by batch
     for (int b = 0; b < nb; ++b) {
         const int b0 = b * cap, len = min(cap, n - b0);
         if (nb > 1) {
             __syncthreads();
-            load_batch(b0, len);
+            align_load(ids_g, b0, len, ids_s, O);
             __syncthreads();
-            count_waves(len);
+            align_count_waves(ids_s, len, cnt, E);
         }
-        // cnt[w][e] <- first position of wave w's items of expert e
-        if (tid < E) {
-            int base = run[tid];
-            for (int w = 0; w < ALIGN_WAVES; ++w) {
-                const int c = cnt[w * E + tid];
-                cnt[w * E + tid] = base;
-                base += c;
-            }
-            run[tid] = base;
-        }
-        __syncthreads();
-        const int ch = (len + ALIGN_WAVES - 1) / ALIGN_WAVES;
-        const int end = min(len, (wave + 1) * ch);
-        for (int i0 = wave * ch; i0 < end; i0 += 64) {
-            const int i = i0 + lane;
-            const int ev = (i < end) ? ids_s[i] : -1;
-            const bool valid = ev >= 0;
-            const unsigned long long m = match_mask(ev, valid, nbits);
-            const int r = b0 + i;
-            if (valid) {
-                const int rank = __popcll(m & ((1ull << lane) - 1ull));
-                const int64_t pos = (int64_t)cnt[wave * E + ev] + rank;
-                if (pos < O.max_sorted)
-                    O.sorted[pos] = r;
-                O.inv[r] = (pos < O.max_sorted) ? (int)pos : -1;
-            } else if (i < end) {
-                O.inv[r] = -1;                      // expert id out of range: no row
-            }
-            // every lane has read its base before the leader moves it on
-            __builtin_amdgcn_wave_barrier();
-            if (valid && lane == (int)__builtin_ctzll(m))
-                cnt[wave * E + ev] += __popcll(m);
-            __builtin_amdgcn_wave_barrier();
+        align_scatter(ids_s, b0, len, cnt, run, O);
+    }
+}
+
+// ---- the same align over many workgroups, for large batches of routed
+// items: block b of the grid owns items [b ALIGN_BLOCK, (b+1) ALIGN_BLOCK).
+// (1) k_align_count: hist[b][e] = block b's items of expert e; (2)
+// k_align_layout (one workgroup): totals, the padded layout, and hist[b][e]
+// <- first position of block b's items of expert e (blocks in order); (3)
+// k_align_scatter: each block's stable scatter from those bases.  Blocks are
+// consecutive ranges and the layout takes them in order, so the result is
+// the one-workgroup align's, bit for bit.
+constexpr int ALIGN_BLOCK = 8192;
+
+__global__ void __launch_bounds__(1024) k_align_count(const int32_t* __restrict__ ids, int Mk,
+                                                      AlignOut O, int32_t* __restrict__ hist)
+{
+    extern __shared__ int sh[];
+    int* ids_s = sh;                            // [ALIGN_BLOCK]
+    int* cnt = sh + ALIGN_BLOCK;                // [E]
+    const int b0 = blockIdx.x * ALIGN_BLOCK, len = min(ALIGN_BLOCK, Mk - b0);
+    for (int i = threadIdx.x; i < O.E; i += 1024)
+        cnt[i] = 0;
+    align_load(ids, b0, len, ids_s, O);
+    __syncthreads();
+    for (int i = threadIdx.x; i < len; i += 1024) {
+        const int e = ids_s[i];
+        if (e >= 0)
+            atomicAdd(&cnt[e], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < O.E; e += 1024)
+        hist[(int64_t)blockIdx.x * O.E + e] = cnt[e];
+}
+
+__global__ void __launch_bounds__(1024) k_align_layout(int nblk, AlignOut O,
+                                                       int32_t* __restrict__ hist)
+{
+    extern __shared__ int sh[];
+    const int E = O.E, e = threadIdx.x;
+    int* offs = sh;                             // [E + 1]
+    int* run = offs + (E + 1);                  // [E + 1]
+    int* choff = run + (E + 1);                 // [E + 1]
+    int* tot = choff + (E + 1);                 // [ALIGN_WAVES]
+    int total_e = 0;
+    if (e < E)
+        for (int b = 0; b < nblk; ++b)
+            total_e += hist[(int64_t)b * E + e];
+    align_layout(total_e, offs, run, choff, tot, O);
+    if (e < E) {
+        int base = run[e];
+        for (int b = 0; b < nblk; ++b) {
+            const int c = hist[(int64_t)b * E + e];
+            hist[(int64_t)b * E + e] = base;
+            base += c;
         }
     }
+}
+
+__global__ void __launch_bounds__(1024) k_align_scatter(const int32_t* __restrict__ ids, int Mk,
+                                                        AlignOut O,
+                                                        const int32_t* __restrict__ hist)
+{
+    extern __shared__ int sh[];
+    const int E = O.E;
+    int* ids_s = sh;                            // [ALIGN_BLOCK]
+    int* cnt = sh + ALIGN_BLOCK;                // [ALIGN_WAVES][E]
+    int* run = cnt + ALIGN_WAVES * E;           // [E]
+    const int b0 = blockIdx.x * ALIGN_BLOCK, len = min(ALIGN_BLOCK, Mk - b0);
+    for (int e = threadIdx.x; e < E; e += 1024)
+        run[e] = hist[(int64_t)blockIdx.x * E + e];
+    align_load(ids, b0, len, ids_s, O);
+    __syncthreads();
+    align_count_waves(ids_s, len, cnt, E);
+    align_scatter(ids_s, b0, len, cnt, run, O);
 }
 
 static AlignOut align_out(const Plan& P)
@@ -534,6 +634,26 @@ static hipError_t set_lds(const void* kernel, size_t bytes)
 hipError_t launch_align(const Plan& P, const int32_t* ids, hipStream_t s)
 {
     const int Mk = P.M * P.K;
+    if (Mk > 2 * ALIGN_BLOCK) {
+        // many workgroups; block histograms in the o region, which only GEMM2 writes
+        const int nblk = (Mk + ALIGN_BLOCK - 1) / ALIGN_BLOCK;
+        int32_t* hist = (int32_t*)P.o;
+        const AlignOut O = align_out(P);
+        const size_t l1 = sizeof(int) * ((size_t)ALIGN_BLOCK + P.E);
+        const size_t l2 = sizeof(int) * (3 * ((size_t)P.E + 1) + ALIGN_WAVES);
+        const size_t l3 = sizeof(int) * ((size_t)ALIGN_BLOCK + (size_t)(ALIGN_WAVES + 1) * P.E);
+        hipError_t e = set_lds((const void*)k_align_count, l1);
+        if (e == hipSuccess)
+            e = set_lds((const void*)k_align_layout, l2);
+        if (e == hipSuccess)
+            e = set_lds((const void*)k_align_scatter, l3);
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(k_align_count, dim3(nblk), dim3(1024), l1, s, ids, Mk, O, hist);
+        hipLaunchKernelGGL(k_align_layout, dim3(1), dim3(1024), l2, s, nblk, O, hist);
+        hipLaunchKernelGGL(k_align_scatter, dim3(nblk), dim3(1024), l3, s, ids, Mk, O, hist);
+        return hipGetLastError();
+    }
     const int cap = Mk < ALIGN_CAP ? (Mk > 0 ? Mk : 1) : ALIGN_CAP;
     const size_t lds = sizeof(int) * ((size_t)cap + align_scratch_ints(P.E));
     const hipError_t e = set_lds((const void*)k_align, lds);
