@@ -15,6 +15,7 @@ recorded on the launch stream around that kernel in every timed step.
 bounded token sample of the same workload on this host.
 """
 import argparse
+import dataclasses
 import ctypes
 import json
 import os
@@ -153,7 +154,13 @@ def main():
                             w13_scale=inp.get("w13_scale"), w2_scale=inp.get("w2_scale"),
                             expert_map=emap, w13_zero=inp.get("w13_zero"),
                             w2_zero=inp.get("w2_zero"))
+    # one workspace for both weight layouts (their tile choices, and so their
+    # workspace layouts, may differ); `info` describes the packed (timed) one
     ws, info = B.allocate_workspace(prob, dev)
+    if cfg.weight in ("bf16", "fp8", "u8", "u4") and layout0 == B.MOE_W_PLAIN:
+        info = B.moe_workspace_shapes(dataclasses.replace(prob, w_layout=B.MOE_W_PACKED).c())
+        if int(info.bytes) > ws.numel():
+            ws = torch.empty(int(info.bytes), dtype=torch.uint8, device=dev)
     stream = B.current_stream_handle(dev)
     hip = HipEvents()
     rec = hip.hip.hipEventRecord
