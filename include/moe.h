@@ -314,7 +314,8 @@ int moe_forward_timed(const moe_problem* p, const moe_args* a, void* workspace,
  * fp8 weights (K-contiguous): each block is 128 weight columns (N) x 128
  *   weight rows (K) of one-byte codes: column n of a block is 128 bytes =
  *   8 slots of 16 bytes; slot s holds the codes of weight rows
- *   128 kt + 16 q .. + 15 with q = s ^ ((n >> 1) & 7).
+ *   128 kt + 16 q .. + 15 with p = s ^ ((n >> 1) & 7), q = 2 (p & 3) + (p >> 2)
+ *   (the even 16-row chunks before the odd ones, then the column's XOR).
  *   w13: block (e, kt, j), kt < ceil(H / 128), j < I / 64, j fastest; block
  *        columns 0-63 are gate columns 64 j .., 64-127 the up columns
  *        I + 64 j ...

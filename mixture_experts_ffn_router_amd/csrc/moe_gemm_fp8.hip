@@ -25,19 +25,32 @@
 // Both operands are K-contiguous in LDS (128 bytes = one K stage per row or
 // column), so A and B fragments are read the same way: lane l takes row /
 // column l % 16 and the 32 K bytes (l / 16) * 32 .. as two 16-byte reads.
-// The 16-byte chunk q of row / column r sits in slot q ^ ((r >> 1) & 7), which
-// spreads every fragment read over all banks.  Activations arrive that way by
-// DMA of their natural [rows, K] layout; the weights are packed once into
-// blocks that hold them that way (moe_pack_weights).
+// The 16-byte chunk q of row / column r sits in slot
+// (q / 2 + 4 (q % 2)) ^ ((r >> 1) & 7): the even chunks (the first reads of
+// the four lane groups) fill slots 0-3 and the odd ones slots 4-7 before the
+// row's XOR.  Measured with the LDS bank-conflict counter on gfx950, each of
+// the two fragment reads is then conflict free (q ^ ((r >> 1) & 7) costs 4
+// extra cycles per read).  Activations arrive that way by DMA of their
+// natural [rows, K] layout; the weights are packed once into blocks that
+// hold them that way (moe_pack_weights).
 #include "moe_gemm_common.h"
 
 namespace moe {
 
 // Packed fp8 weight block: 128 weight columns x 128 K values (16 KiB); column
-// c is 128 contiguous K bytes whose 16-byte chunk q sits in slot q ^ ((c >> 1) & 7).
+// c is 128 contiguous K bytes whose 16-byte chunk q sits in slot f8_slot(q, c).
 constexpr int F8_BLOCK = 128 * 128;
 
-__device__ __forceinline__ int f8_slot(int chunk, int r) { return chunk ^ ((r >> 1) & 7); }
+// Slot of 16-byte K chunk q of row / column r, and its inverse: the chunk in slot sl.
+__device__ __forceinline__ int f8_slot(int q, int r)
+{
+    return ((q >> 1) | ((q & 1) << 2)) ^ ((r >> 1) & 7);
+}
+__device__ __forceinline__ int f8_chunk(int sl, int r)
+{
+    const int p = sl ^ ((r >> 1) & 7);
+    return ((p & 3) << 1) | (p >> 2);
+}
 
 template <bool ZS, bool BW = false>
 struct F8S {
@@ -69,7 +82,7 @@ struct F8S {
 };
 
 // DMA sources of one fp8 tile.  Wave w issues A DMAs i = w + 8 j (tile rows
-// 8i .. 8i+7, lane l: row 8i + l/8, K chunk f8_slot(l % 8, row)), weight DMAs
+// 8i .. 8i+7, lane l: row 8i + l/8, K chunk f8_chunk(l % 8, row)), weight DMAs
 // i = w + 8 j (block i / 16, its KiB i % 16, linear) and, for GEMM2, wave 0
 // one DMA of the stage's z scales.  BW: GEMM1 waves 0 and 1 gather the
 // activation block scales of tile rows 64 w + l (4 bytes a lane) and wave 2
@@ -99,7 +112,7 @@ struct F8Src {
         for (int j = 0; j < S::A_PW; ++j) {
             const int i = wave + S::NW * j;
             const int row = 8 * i + (lane >> 3);
-            const int c = f8_slot(lane & 7, row);
+            const int c = f8_chunk(lane & 7, row);
             const bool ok = live && ap[j] && kt * 128 + c * 16 < K;
             dma16(ok ? ap[j] + kt * 128 : zero, lds + i * 1024);
         }
@@ -293,7 +306,7 @@ __device__ __forceinline__ void f8_gemm1_src(const Gemm1Args& g, const TileRef& 
 #pragma unroll
     for (int j = 0; j < S::A_PW; ++j) {
         const int row = 8 * (wave + S::NW * j) + (lane >> 3);
-        const int c = f8_slot(lane & 7, row);
+        const int c = f8_chunk(lane & 7, row);
         d.ap[j] = (r.srow[j] >= 0) ? (const char*)g.a + (int64_t)r.srow[j] * H + c * 16
                                    : nullptr;
     }
@@ -475,7 +488,7 @@ __device__ __forceinline__ void f8_gemm2_src(const Gemm2Args& g, const TileRef& 
 #pragma unroll
     for (int j = 0; j < S::A_PW; ++j) {
         const int row = 8 * (wave + S::NW * j) + (lane >> 3);
-        const int c = f8_slot(lane & 7, row);
+        const int c = f8_chunk(lane & 7, row);
         d.ap[j] = (row < t.rows) ? (const char*)g.z + ((int64_t)t.r0 + row) * I + c * 16
                                  : nullptr;
     }
@@ -584,7 +597,7 @@ __global__ void __launch_bounds__(256) k_pack_f8(const uint8_t* __restrict__ w, 
         const int j = (int)(b % nblk);
         const int kt = (int)((b / nblk) % nks);
         const int64_t e = b / nblk / nks;
-        const int chunk = f8_slot(sl, c);              // slot sl holds K chunk sl ^ swz(c)
+        const int chunk = f8_chunk(sl, c);             // the K chunk slot sl holds
         int col;
         bool valid;
         if constexpr (W13) {

@@ -122,7 +122,8 @@ def test_packed_batched_bf16():
 
 def _ref_pack_f8(w, gate_up):
     """The documented fp8 layout, written out with numpy: 16 KiB blocks of 128
-    columns x 128 K bytes; column c's 16-byte slot s holds K chunk s ^ ((c >> 1) & 7)."""
+    columns x 128 K bytes; column c's 16-byte slot s holds K chunk 2 (p & 3) + (p >> 2),
+    p = s ^ ((c >> 1) & 7)."""
     E, K, N = w.shape
     half = N // 2
     nblk = half // 64 if gate_up else -(-N // 128)
@@ -138,7 +139,8 @@ def _ref_pack_f8(w, gate_up):
                     continue
             for kt in range(nks):
                 for sl in range(8):
-                    chunk = sl ^ ((c >> 1) & 7)
+                    p = sl ^ ((c >> 1) & 7)
+                    chunk = 2 * (p & 3) + (p >> 2)
                     rows = kt * 128 + chunk * 16 + np.arange(16)
                     ok = rows < K
                     out[:, kt, j, c, sl, :ok.sum()] = w[:, rows[ok], col]
