@@ -729,7 +729,8 @@ hipError_t launch_tilelist(const Plan& P, const int32_t* ent, hipStream_t s)
 // walkthrough, "FP8 W8A8": activations are quantised before each GEMM):
 // scale = amax / 448 (1 for an all-zero row), code = RNE(x / scale),
 // all in float32 with IEEE division.  One wave per row, 16-byte loads: a
-// first pass forms the amax, a second (from L2) writes the codes.
+// first pass forms the amax, then the codes are written from the registers
+// (rows of up to 256 chunks) or from a second pass over the row (from L2).
 //   ident == 0: rows t in [0, M) of hidden -> aq[t]         (contiguous)
 //   ident == 1: padded positions p < npp, source row sorted[p] -> aq[p] (batched)
 template <typename TIn>
@@ -767,8 +768,8 @@ __global__ void __launch_bounds__(256) k_quant_rows(const TIn* __restrict__ x, i
             return __int_as_float(c[i]);
     };
     float amax = 0.0f;
+    i32x4 v[4];                                      // the last 256 chunks read
     for (int c0 = 0; c0 < nch; c0 += 64 * 4) {
-        i32x4 v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int c = c0 + u * 64 + lane;
@@ -782,17 +783,28 @@ __global__ void __launch_bounds__(256) k_quant_rows(const TIn* __restrict__ x, i
     }
     amax = wave_max(amax);
     const float scale = (amax > 0.0f) ? amax / 448.0f : 1.0f;
-    for (int c = lane; c < nch; c += 64) {
-        const i32x4 v = row[c];
+    auto emit = [&](int c, const i32x4& cv) {
         uint32_t w[VE / 4];
 #pragma unroll
         for (int q = 0; q < VE / 4; ++q)
-            w[q] = cvt_fp8x2(val(v, 4 * q) / scale, val(v, 4 * q + 1) / scale) |
-                   (cvt_fp8x2(val(v, 4 * q + 2) / scale, val(v, 4 * q + 3) / scale) << 16);
+            w[q] = cvt_fp8x2(val(cv, 4 * q) / scale, val(cv, 4 * q + 1) / scale) |
+                   (cvt_fp8x2(val(cv, 4 * q + 2) / scale, val(cv, 4 * q + 3) / scale) << 16);
         if constexpr (VE == 8)
             *(i32x2*)(aq + r * H + c * 8) = i32x2{(int)w[0], (int)w[1]};
         else
             *(uint32_t*)(aq + r * H + c * 4) = w[0];
+    };
+    if (nch <= 64 * 4) {
+        // the whole row is still in registers (up to 2048 bf16 / 1024 f32 columns)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = u * 64 + lane;
+            if (c < nch)
+                emit(c, v[u]);
+        }
+    } else {
+        for (int c = lane; c < nch; c += 64)        // second pass, from L2
+            emit(c, row[c]);
     }
     if (lane == 0)
         aq_scale[r] = scale;

@@ -224,6 +224,10 @@ ROUTE_PATHS = [
     ("lpt16_multibatch", 3000, 16, 4, "softmax", 1),
     ("e256_grouped_multibatch", 1300, 256, 8, "sigmoid", 8),
     ("e512", 300, 512, 6, "softmax", 1),
+    # grouped keys from LDS: 12 experts a group over 6 lanes (not a power of two)
+    ("e96_groups_of_12", 400, 96, 6, "sigmoid", 8),
+    # grouped keys by shuffles over 8-lane groups, softmax top-2 sums, 4 of 6 groups
+    ("e192_six_groups", 400, 192, 6, "softmax", 6),
 ]
 
 
@@ -243,13 +247,15 @@ def test_route_align_paths(case):
     GH.check_output(inp, out, ids_o, w_o, tokens=tokens, what=name)
 
 
-def test_fp8_activation_codes_bit_exact():
+@pytest.mark.parametrize("H", [208, 2304])
+def test_fp8_activation_codes_bit_exact(H):
     """The in-path per-token fp8 quantisation (scale = amax / 448, RNE,
     saturating) produces the oracle's codes and scales bit for bit: contiguous
-    rows by token, batched rows at their padded positions."""
+    rows by token, batched rows at their padded positions.  Rows of up to 2048
+    bf16 columns are coded from registers, longer ones in a second pass."""
     import oracle
     dev = GH.device()
-    cfg = W.MIXTRAL_PREFILL.scaled(name="contig_fp8_codes", M=96, H=208, I=256, weight="fp8")
+    cfg = W.MIXTRAL_PREFILL.scaled(name="contig_fp8_codes", M=96, H=H, I=256, weight="fp8")
     inp = W.make_inputs(cfg, 81)
     inp["hidden"][3] = 0.0                         # an all-zero row: scale 1, codes 0
     _, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
