@@ -389,7 +389,7 @@ def cpu_baseline(cfg, inp, info, sample):
                 "kind": "oracle",
                 "sample": f"{n} of {int(counts.sum())} valid batched rows (every "
                           f"{max(1, rows.size // n)}th), {dt:.1f}s; tokens = rows / top_k"}
-    n = min(sample or 256, cfg.M)
+    n = min(sample or 512, cfg.M)
     logits = inp["logits"].cpu()
     t0 = time.perf_counter()
     ids, w = oracle.route(logits, cfg.top_k, scoring=cfg.scoring, renormalize=cfg.renormalize,
