@@ -696,9 +696,19 @@ struct DmaTile {
     const char* qz;             //   and its 16 zero-point bytes, or null
     int64_t qs_g, qz_g;         //   bytes from one K group to the next
 
+    bool nt;                    // the weights are read by this tile alone: non-temporal DMAs
+
     // spare: LDS address of the scratch KiB for spare A slots
     __device__ __forceinline__ void issue(int kt, uint32_t lds, uint32_t spare, int wave,
                                           bool live) const
+    {
+        issue_p<false>(kt, lds, spare, wave, live);
+    }
+
+    // NT: the weight DMAs with the non-temporal policy
+    template <bool NT>
+    __device__ __forceinline__ void issue_p(int kt, uint32_t lds, uint32_t spare, int wave,
+                                            bool live) const
     {
         const int lane = threadIdx.x & 63;
         const char* zero = (const char*)g_zero16;
@@ -737,7 +747,10 @@ struct DmaTile {
                 if (live && valid && kt * 64 + k < K)
                     p = wb[0] + (int64_t)(kt * 64 + k) * w_ld + (int64_t)col * 2;
             }
-            dma16(p, lds + S::A_BYTES + i * 1024);
+            if constexpr (NT)
+                dma16_nt(p, lds + S::A_BYTES + i * 1024);
+            else
+                dma16(p, lds + S::A_BYTES + i * 1024);
         }
         if constexpr (S::Q != 0) {
             const int grp = kt >> 1;            // 128-row K groups, 64-row stages
@@ -966,24 +979,53 @@ struct DmaFrag {
     }
 };
 
+// A tile's DMA source with its weight DMAs non-temporal.
+template <typename Src>
+struct NtSrc {
+    const Src& s;
+    __device__ __forceinline__ void issue(int kt, uint32_t lds, uint32_t spare, int wave,
+                                          bool live) const
+    {
+        s.template issue_p<true>(kt, lds, spare, wave, live);
+    }
+};
+
+// The first stages of a tile's ring, with the tile's weight cache policy.
+template <typename S, typename Src>
+__device__ __forceinline__ void dma_prologue_p(const Src& src, char* ring, int kb, int ke, int wave)
+{
+    if (__builtin_amdgcn_readfirstlane(src.nt))
+        dma_prologue<S>(NtSrc<Src>{src}, ring, kb, ke, wave);
+    else
+        dma_prologue<S>(src, ring, kb, ke, wave);
+}
+
 // The mainloop with the MFMAs of the wave's first `live` strips (wave
-// uniform): one instantiation per count, so the loop body stays branch free;
-// every wave still issues its DMAs and meets every barrier.
+// uniform): one instantiation per count and weight cache policy, so the loop
+// body stays branch free; every wave still issues its DMAs and meets every
+// barrier.
 template <typename S, int NM = S::FMW, typename Src>
 __device__ __forceinline__ void dma_run(const Src& src, char* ring, int kb, int ke, int wave,
                                         int rg, const DmaFrag<S>& fr,
                                         f32x4 (&acc)[S::FMW][S::FN], int live)
 {
-    if constexpr (NM == 0) {
-        dma_mainloop<S>(src, ring, kb, ke, wave, [](const char*) {});
-    } else {
-        if (live >= NM) {
-            dma_mainloop<S>(src, ring, kb, ke, wave,
+    auto loop = [&](const auto& ss) {
+        if constexpr (NM == 0)
+            dma_mainloop<S>(ss, ring, kb, ke, wave, [](const char*) {});
+        else
+            dma_mainloop<S>(ss, ring, kb, ke, wave,
                             [&](const char* st) { fr.template stage<NM>(st, rg, acc); });
+    };
+    if constexpr (NM > 0) {
+        if (live < NM) {
+            dma_run<S, NM - 1>(src, ring, kb, ke, wave, rg, fr, acc, live);
             return;
         }
-        dma_run<S, NM - 1>(src, ring, kb, ke, wave, rg, fr, acc, live);
     }
+    if (__builtin_amdgcn_readfirstlane(src.nt))
+        loop(NtSrc<Src>{src});
+    else
+        loop(src);
 }
 
 // Per-lane source rows of one GEMM1 tile's A DMAs (-1: padding row); loaded
@@ -1016,6 +1058,7 @@ __device__ __forceinline__ void gemm1_src(const Gemm1Args& g, const TileRef& t,
     d.w_ld = (int64_t)N * 2;
     d.qs = d.qz = nullptr;
     d.qs_g = d.qz_g = 0;
+    d.nt = __builtin_amdgcn_readfirstlane(t.nch) == 1;
     if constexpr (PACKED) {
         const int64_t nblk = (I + 63) / 64, nks = (H + 63) / 64;
         d.w_stage = nblk * S::QB;
@@ -1070,6 +1113,7 @@ __device__ __forceinline__ void gemm2_src(const Gemm2Args& g, const TileRef& t, 
     d.w_ld = (int64_t)H * 2;
     d.qs = d.qz = nullptr;
     d.qs_g = d.qz_g = 0;
+    d.nt = __builtin_amdgcn_readfirstlane(t.nch) == 1;
     if constexpr (PACKED) {
         const int64_t nblk = (H + 127) / 128, nks = (I + 63) / 64;
         d.w_stage = nblk * S::QB;
@@ -1144,7 +1188,7 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
     DmaTile<S, PACKED, true> src;
     const int nk1 = (g.H + 63) / 64;
     gemm1_src<S, PACKED>(g, cur, srow, src);
-    dma_prologue<S>(src, ring, 0, nk1, wave);
+    dma_prologue_p<S>(src, ring, 0, nk1, wave);
 
     // wave (rg, cg): gate fragments fn < FN/2 at z columns (cg FN/2 + fn) 16,
     // up fragments fn >= FN/2 at the same z columns of the up half
@@ -1192,7 +1236,7 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
             for (int j = 0; j < S::A_PW; ++j)
                 pin(srow[j]);
             gemm1_src<S, PACKED>(g, nxt, srow, src);
-            dma_prologue<S>(src, ring, 0, nk1, wave);
+            dma_prologue_p<S>(src, ring, 0, nk1, wave);
         }
         // epilogue: bf16 z of the real rows, staged in the ring slot that no
         // DMA touches before the next tile's first barrier (the prologue
@@ -1270,7 +1314,7 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
     cur = unit(cur, kb, ke, part);
     DmaTile<S, PACKED, false> src;
     gemm2_src<S, PACKED>(g, cur, wave, src);
-    dma_prologue<S>(src, ring, kb, ke, wave);
+    dma_prologue_p<S>(src, ring, kb, ke, wave);
 
     int bblk[FN], bchunk[FN];
 #pragma unroll
@@ -1315,7 +1359,7 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
         float* const outf = part ? g.out2 : (float*)g.out;
         if (more) {
             gemm2_src<S, PACKED>(g, nxt, wave, src);
-            dma_prologue<S>(src, ring, nkb, nke, wave);
+            dma_prologue_p<S>(src, ring, nkb, nke, wave);
         }
         // row (strip, g4*4 + r): uniform base of the strip's 16 rows plus this
         // lane's offset, one strip at a time (keeps the addresses out of registers)

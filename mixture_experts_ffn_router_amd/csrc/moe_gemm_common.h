@@ -120,6 +120,7 @@ struct Gemm2Args {
 struct TileRef {
     int e, r0, rows, ntile;     // expert, first padded row, real rows (>= 1), column block
     int base;                   // first padded row of the expert's run
+    int nch;                    // row chunks of the expert (1: this tile alone reads its weights)
 };
 
 constexpr int TILE_GROUP = 8;   // chunks walked together over the column blocks
@@ -164,7 +165,8 @@ struct TileIter {
         const int cnt = s.counts[e], U = (cnt + 15) >> 4, q = U / nch, extra = U - q * nch;
         const int u0 = j * q + min(j, extra);
         const int base = s.offsets[e];
-        t = TileRef{e, base + 16 * u0, min(16 * (q + (j < extra)), cnt - 16 * u0), ntile, base};
+        t = TileRef{e, base + 16 * u0, min(16 * (q + (j < extra)), cnt - 16 * u0), ntile, base,
+                    nch};
         L += per;
         return true;
     }
@@ -195,7 +197,18 @@ __device__ __forceinline__ void dma16(const char* g, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
-                 : "s"(lds), "v"(g)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g)
+                 : "memory");
+}
+
+// The same with the non-temporal cache policy: for weights that no other
+// tile reads, so that streaming them does not evict the operands that
+// neighbouring tiles share through L2.
+__device__ __forceinline__ void dma16_nt(const char* g, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g)
                  : "memory");
 }
 
@@ -204,7 +217,7 @@ __device__ __forceinline__ void dma4(const char* g, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                  :
-                 : "s"(lds), "v"(g)
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(g)
                  : "memory");
 }
 
