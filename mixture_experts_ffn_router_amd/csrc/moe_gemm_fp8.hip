@@ -102,9 +102,18 @@ struct F8Src {
     const char* as;             // BW GEMM1: this lane's activation scale at stage 0 (null: none)
     const char* bs;             // BW: this lane's weight block scale at stage 0 (null: none)
     int K;                      // contraction length
+    bool nt;                    // the weights are read by this tile alone: non-temporal DMAs
 
-    __device__ __forceinline__ void issue(int kt, uint32_t lds, uint32_t, int wave,
+    __device__ __forceinline__ void issue(int kt, uint32_t lds, uint32_t spare, int wave,
                                           bool live) const
+    {
+        issue_p<false>(kt, lds, spare, wave, live);
+    }
+
+    // NT: the weight DMAs with the non-temporal policy
+    template <bool NT>
+    __device__ __forceinline__ void issue_p(int kt, uint32_t lds, uint32_t, int wave,
+                                            bool live) const
     {
         const int lane = threadIdx.x & 63;
         const char* zero = (const char*)g_zero16;
@@ -121,7 +130,10 @@ struct F8Src {
             const int i = wave + S::NW * j;          // block i >> 4 == j >> 1 (wave < 8)
             const char* w = wb[(j * S::NW) >> 4];
             const char* p = (live && w) ? w + kt * w_stage + (i & 15) * 1024 + lane * 16 : zero;
-            dma16(p, lds + S::A_BYTES + i * 1024);
+            if constexpr (NT)
+                dma16_nt(p, lds + S::A_BYTES + i * 1024);
+            else
+                dma16(p, lds + S::A_BYTES + i * 1024);
         }
         if constexpr (ZS) {
             if (wave == 0)
@@ -220,25 +232,54 @@ __device__ __forceinline__ void f8_stage(const char* st, int rg, const int (&bco
     }
 }
 
+// A tile's DMA source with its weight DMAs non-temporal.
+template <typename Src>
+struct F8NtSrc {
+    const Src& s;
+    __device__ __forceinline__ void issue(int kt, uint32_t lds, uint32_t spare, int wave,
+                                          bool live) const
+    {
+        s.template issue_p<true>(kt, lds, spare, wave, live);
+    }
+};
+
+// The first stages of a tile's ring, with the tile's weight cache policy.
+template <typename S, typename Src>
+__device__ __forceinline__ void f8_prologue(const Src& src, char* ring, int nk, int wave)
+{
+    if (__builtin_amdgcn_readfirstlane(src.nt))
+        dma_prologue<S>(F8NtSrc<Src>{src}, ring, 0, nk, wave);
+    else
+        dma_prologue<S>(src, ring, 0, nk, wave);
+}
+
 // The ring over [0, nk) with the MFMAs of the wave's first `live` strips;
-// one instantiation per count keeps the loop body branch free.
+// one instantiation per count and weight cache policy keeps the loop body
+// branch free.
 template <bool ZS, bool BW, int NM = F8_ROWS / 32>
 __device__ __forceinline__ void f8_run(const F8Src<ZS, BW>& src, char* ring, int nk, int wave,
                                        int rg, const int (&bcol)[4], int lane,
                                        f32x4 (&acc)[F8_ROWS / 32][4], int live)
 {
     typedef F8S<ZS, BW> S;
-    if constexpr (NM == 0) {
-        dma_mainloop<S>(src, ring, 0, nk, wave, [](const char*) {});
-    } else {
-        if (live >= NM) {
-            dma_mainloop<S>(src, ring, 0, nk, wave, [&](const char* st) {
+    auto loop = [&](const auto& ss) {
+        if constexpr (NM == 0)
+            dma_mainloop<S>(ss, ring, 0, nk, wave, [](const char*) {});
+        else
+            dma_mainloop<S>(ss, ring, 0, nk, wave, [&](const char* st) {
                 f8_stage<ZS, BW, NM>(st, rg, bcol, lane, acc);
             });
+    };
+    if constexpr (NM > 0) {
+        if (live < NM) {
+            f8_run<ZS, BW, NM - 1>(src, ring, nk, wave, rg, bcol, lane, acc, live);
             return;
         }
-        f8_run<ZS, BW, NM - 1>(src, ring, nk, wave, rg, bcol, lane, acc, live);
     }
+    if (__builtin_amdgcn_readfirstlane(src.nt))
+        loop(F8NtSrc<F8Src<ZS, BW>>{src});
+    else
+        loop(src);
 }
 
 __device__ __forceinline__ void f8_zero(f32x4 (&acc)[F8_ROWS / 32][4])
@@ -284,6 +325,7 @@ __device__ __forceinline__ void f8_gemm1_src(const Gemm1Args& g, const TileRef& 
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nblk = I / 64, nks = (H + 127) / 128;
     d.K = H;
+    d.nt = __builtin_amdgcn_readfirstlane(t.nch) == 1;
     d.w_stage = nblk * F8_BLOCK;
     d.zs = nullptr;
     d.zs_stage = 0;
@@ -339,7 +381,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
         rs[0][tid] = BW ? 1.0f : (rows.sa_row >= 0 ? g.a_scale[rows.sa_row] : 0.0f);
         rws[0][tid] = rows.rw;
     }
-    dma_prologue<S>(src, ring, 0, nk, wave);
+    f8_prologue<S>(src, ring, nk, wave);
 
     // B fragment columns within the stage's 256-column weight tile
     int bcol[4];
@@ -390,7 +432,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
             for (int j = 0; j < S::A_PW; ++j)
                 pin(rows.srow[j]);
             f8_gemm1_src<BW>(g, nxt, rows, src);
-            dma_prologue<S>(src, ring, 0, nk, wave);
+            f8_prologue<S>(src, ring, nk, wave);
             if (tid < S::CH) {
                 rs[parity ^ 1][tid] = sn;
                 rws[parity ^ 1][tid] = rows.rw;
@@ -469,6 +511,7 @@ __device__ __forceinline__ void f8_gemm2_src(const Gemm2Args& g, const TileRef& 
     const int lane = threadIdx.x & 63;
     const int64_t nblk = (H + 127) / 128, nks = I / 128;
     d.K = I;
+    d.nt = __builtin_amdgcn_readfirstlane(t.nch) == 1;
     d.w_stage = nblk * F8_BLOCK;
     d.zs = (const char*)(g.z_scale + t.r0) + lane * 16;
     d.zs_stage = g.zs_ld * 4;
@@ -512,7 +555,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm2_f8(Gemm2Args g)
         return;
     F8Src<true, BW> src;
     f8_gemm2_src<BW>(g, cur, wave, src);
-    dma_prologue<S>(src, ring, 0, nk, wave);
+    f8_prologue<S>(src, ring, nk, wave);
     int bcol[4];
 #pragma unroll
     for (int fn = 0; fn < 4; ++fn)
@@ -543,7 +586,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm2_f8(Gemm2Args g)
         }
         if (more) {
             f8_gemm2_src<BW>(g, nxt, wave, src);
-            dma_prologue<S>(src, ring, 0, nk, wave);
+            f8_prologue<S>(src, ring, nk, wave);
         }
         // epilogue straight from the accumulators: one strip at a time
 #pragma unroll
