@@ -1615,8 +1615,10 @@ static int64_t expected_chunks(const Plan& P)
 }
 
 // Wave columns of the large bf16 GEMM1 tile: 4 (256 columns, 8 waves) when
-// there are a few tiles per CU, else 2.  Tuning override: MOE_GEMM1_WC = 2 | 4,
-// read on every call.
+// there are a few tiles per CU, or when experts hold about one row chunk on
+// average (their weights are read once, and the wide tile halves the column
+// tiles that re-read each chunk's activation rows through L2), else 2.
+// Tuning override: MOE_GEMM1_WC = 2 | 4, read on every call.
 static int gemm1_wave_cols(const Plan& P)
 {
     if (const char* env = getenv("MOE_GEMM1_WC")) {
@@ -1624,6 +1626,9 @@ static int gemm1_wave_cols(const Plan& P)
         if (v == 2 || v == 4)
             return v;
     }
+    const int64_t rows = (P.fmt == MOE_FMT_BATCHED) ? (int64_t)P.E * P.T : (int64_t)P.M * P.K;
+    if (rows <= (int64_t)P.E * P.CH)
+        return 4;
     return expected_chunks(P) * ((P.I + 127) / 128) <= 8 * device_cus() ? 4 : 2;
 }
 
