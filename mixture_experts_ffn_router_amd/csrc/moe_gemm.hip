@@ -1796,6 +1796,12 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
             return P.wpacked ? run_gemm2_dma<5, 4, 3, true>(g, P, s)
                              : run_gemm2_dma<5, 4, 3, false>(g, P, s);
         }
+        // experts of about one row chunk on average: 256-column tiles, so half
+        // as many column tiles re-read each chunk's z rows through L2
+        if (((P.fmt == MOE_FMT_BATCHED) ? (int64_t)P.E * P.T : (int64_t)P.M * P.K) <=
+            (int64_t)P.E * P.CH)
+            return P.wpacked ? run_gemm2_dma<5, 4, 3, true>(g, P, s)
+                             : run_gemm2_dma<5, 4, 3, false>(g, P, s);
         // about one tile per CU: one workgroup per CU with a 4-stage ring keeps
         // three K stages in flight; otherwise two workgroups per CU overlap
         // each other's prologues and epilogues
