@@ -1614,6 +1614,15 @@ static int64_t expected_chunks(const Plan& P)
     return expected_chunks(P.fmt, P.M, P.K, P.E, P.T, P.CH);
 }
 
+// Routed rows per expert at most one tile height on average (over the
+// global experts of a shard, whose items spread over all of them).
+static bool about_one_chunk(const Plan& P)
+{
+    const int64_t rows = (P.fmt == MOE_FMT_BATCHED) ? (int64_t)P.E * P.T : (int64_t)P.M * P.K;
+    const int64_t experts = P.Er > P.E ? P.Er : P.E;
+    return rows <= experts * P.CH;
+}
+
 // Wave columns of the large bf16 GEMM1 tile: 4 (256 columns, 8 waves) when
 // there are a few tiles per CU, or when experts hold about one row chunk on
 // average (their weights are read once, and the wide tile halves the column
@@ -1626,8 +1635,7 @@ static int gemm1_wave_cols(const Plan& P)
         if (v == 2 || v == 4)
             return v;
     }
-    const int64_t rows = (P.fmt == MOE_FMT_BATCHED) ? (int64_t)P.E * P.T : (int64_t)P.M * P.K;
-    if (rows <= (int64_t)P.E * P.CH)
+    if (about_one_chunk(P))
         return 4;
     return expected_chunks(P) * ((P.I + 127) / 128) <= 8 * device_cus() ? 4 : 2;
 }
@@ -1798,8 +1806,7 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
         }
         // experts of about one row chunk on average: 256-column tiles, so half
         // as many column tiles re-read each chunk's z rows through L2
-        if (((P.fmt == MOE_FMT_BATCHED) ? (int64_t)P.E * P.T : (int64_t)P.M * P.K) <=
-            (int64_t)P.E * P.CH)
+        if (about_one_chunk(P))
             return P.wpacked ? run_gemm2_dma<5, 4, 3, true>(g, P, s)
                              : run_gemm2_dma<5, 4, 3, false>(g, P, s);
         // about one tile per CU: one workgroup per CU with a 4-stage ring keeps
