@@ -210,3 +210,22 @@ def test_packed_fp8_batched_skewed(reduce):
         o_ref, _ = oracle.expert_rows(GH.oracle_experts(inp), acts, rows, experts)
         got = packed.reshape(-1, cfg.H)[idx].cpu().numpy()
         GH.compare(cfg, got, o_ref, "packed fp8 batched rows")
+
+
+def test_wide_tiles_mixed_chunk_counts():
+    """About 128 rows per expert on average (the 256-column GEMM tiles) with
+    skewed experts: single-chunk experts stream their weights with the
+    non-temporal policy, multi-chunk ones share them; plain and packed
+    weights agree bit for bit and meet the oracle bar."""
+    dev = GH.device()
+    cfg = W.DEEPSEEK_GROUPED.scaled(name="wide_mixed_chunks", M=256, H=256, I=384, E=16, top_k=8,
+                                    group_count=4, k_group=2)
+    inp = W.make_inputs(cfg, 1011)
+    print(f"[case] {cfg.name}", flush=True)
+    plain, _, _ = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+    packed, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, packed=True)
+    counts = GH.region(ws, info.off_expert_counts, torch.int32, cfg.E)
+    assert counts.sum() <= cfg.E * 160 and counts.max() > 160, counts
+    assert torch.equal(plain, packed)
+    ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    GH.check_output(inp, packed, ids_o, w_o, what="wide tiles, mixed chunks")
