@@ -170,7 +170,7 @@ __device__ __forceinline__ f32x4 mma_f8(const i32x8& a, const i32x8& b, const f3
 }
 
 // One K stage for wave (rg, cg): B fragment fn is column bcol[fn] (a multiple
-// of 16) of the stage's weight tile; the first NM strips of the wave's eight
+// of 16) of the stage's weight tile; the first NM strips of the wave's four
 // hold real rows.  ZS: every product is scaled by its row's z scale before
 // it is accumulated (one MFMA spans exactly one 128-column z group).  BW:
 // scaled by the row's activation block scale times the weight block scale
@@ -189,28 +189,68 @@ __device__ __forceinline__ void f8_stage(const char* st, int rg, const int (&bco
 #pragma unroll
     for (int fn = 0; fn < S::FN; ++fn)
         b[fn] = f8_frag(Bs + bcol[fn] * 128, s16, g);
+    if constexpr (ZS) {
+        // GEMM2's scaled products: strip fm's are scaled and accumulated after
+        // strip fm + 1's MFMAs are issued, so the VALU never waits on a
+        // product just made (each accumulator still takes one scaled product
+        // per stage).  s0 scales fragments fn < FN / 2, s1 the others.  (The
+        // block-scaled GEMM1 keeps the direct order: the extra products
+        // would not fit its registers.)
+        f32x4 tp[S::FN], s0p, s1p;
 #pragma unroll
-    for (int fm = 0; fm < NM; ++fm) {
-        const i32x8 a = f8_frag(As + fm * 2048, s16, g);
-        const int row0 = rg * S::FMW * 16 + fm * 16 + g * 4;
-        if constexpr (ZS) {
-            f32x4 sz = *(const f32x4*)(Ss + row0 * 4);
-            if constexpr (BW) {
-                const float sw = *(const float*)(Ss + S::SW_OFF + (bcol[0] >> 7) * 4);
+        for (int fm = 0; fm < NM; ++fm) {
+            const i32x8 a = f8_frag(As + fm * 2048, s16, g);
+            const int row0 = rg * S::FMW * 16 + fm * 16 + g * 4;
+            f32x4 s0, s1;
+            if constexpr (ZS) {
+                f32x4 sz = *(const f32x4*)(Ss + row0 * 4);
+                if constexpr (BW) {
+                    const float sw = *(const float*)(Ss + S::SW_OFF + (bcol[0] >> 7) * 4);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sz[r] *= sw;
+                    for (int r = 0; r < 4; ++r)
+                        sz[r] *= sw;
+                }
+                s0 = s1 = sz;
+            } else {
+                const f32x4 sa = *(const f32x4*)(Ss + S::SA_OFF + row0 * 4);
+                const float swg = *(const float*)(Ss + S::SW_OFF);
+                const float swu = *(const float*)(Ss + S::SW_OFF + 4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    s0[r] = sa[r] * swg;
+                    s1[r] = sa[r] * swu;
+                }
+            }
+            f32x4 t[S::FN];
+#pragma unroll
+            for (int fn = 0; fn < S::FN; ++fn)
+                t[fn] = mma_f8(a, b[fn], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            if (fm > 0) {
+#pragma unroll
+                for (int fn = 0; fn < S::FN; ++fn)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[fm - 1][fn][r] += tp[fn][r] * (fn < S::FN / 2 ? s0p[r] : s1p[r]);
             }
 #pragma unroll
-            for (int fn = 0; fn < S::FN; ++fn) {
-                const f32x4 t = mma_f8(a, b[fn], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            for (int fn = 0; fn < S::FN; ++fn)
+                tp[fn] = t[fn];
+            s0p = s0;
+            s1p = s1;
+        }
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[fm][fn][r] += t[r] * sz[r];
-            }
-        } else if constexpr (BW) {
+        for (int fn = 0; fn < S::FN; ++fn)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[NM - 1][fn][r] += tp[fn][r] * (fn < S::FN / 2 ? s0p[r] : s1p[r]);
+    } else if constexpr (BW) {
+#pragma unroll
+        for (int fm = 0; fm < NM; ++fm) {
+            const i32x8 a = f8_frag(As + fm * 2048, s16, g);
+            const int row0 = rg * S::FMW * 16 + fm * 16 + g * 4;
             const f32x4 sa = *(const f32x4*)(Ss + S::SA_OFF + row0 * 4);
-            const float swg = *(const float*)(Ss + S::SW_OFF), swu = *(const float*)(Ss + S::SW_OFF + 4);
+            const float swg = *(const float*)(Ss + S::SW_OFF);
+            const float swu = *(const float*)(Ss + S::SW_OFF + 4);
             f32x4 fg, fu;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -222,9 +262,13 @@ __device__ __forceinline__ void f8_stage(const char* st, int rg, const int (&bco
                 const f32x4 t = mma_f8(a, b[fn], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[fm][fn][r] += t[r] * (fn < 2 ? fg[r] : fu[r]);
+                    acc[fm][fn][r] += t[r] * (fn < S::FN / 2 ? fg[r] : fu[r]);
             }
-        } else {
+        }
+    } else {
+#pragma unroll
+        for (int fm = 0; fm < NM; ++fm) {
+            const i32x8 a = f8_frag(As + fm * 2048, s16, g);
 #pragma unroll
             for (int fn = 0; fn < S::FN; ++fn)
                 acc[fm][fn] = mma_f8(a, b[fn], acc[fm][fn]);
