@@ -27,12 +27,17 @@
  *     dims of a [..., H] activation are flattened into M by the caller.
  *   - Expert ids are int32, routing weights float32.
  *   - All argument checks run on the host before anything is enqueued; on
- *     error nothing is enqueued.  Device-side data is not validated:
- *     precomputed topk ids outside [0, E) (or [0, global_experts)) and
- *     expert_map values outside [-1, E) contribute nothing; counts past
- *     max_tokens are clamped.
+ *     error nothing is enqueued.  Device-side data cannot be checked on the
+ *     host; the kernels handle it safely and report it in the workspace's
+ *     device status word (moe_device_status): precomputed topk ids outside
+ *     [0, E) (or [0, global_experts)) and expert_map values outside [-1, E)
+ *     contribute nothing, expert_num_tokens values outside [0, max_tokens]
+ *     are clamped, token_map entries that name no valid row are skipped.
  *   - Thread safety: concurrent calls are safe when they use distinct
- *     workspaces and outputs.
+ *     workspaces and outputs.  The library's only process state is a
+ *     per-device cache of device attributes (compute units, kernel
+ *     occupancy), filled on first use with atomic stores.
+ *   - The library reads no environment variables.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -72,6 +77,34 @@ typedef enum {
     MOE_FMT_BATCHED = 1       /* hidden [E, max_tokens, H] + expert_num_tokens[E]  */
 } moe_format;
 
+/* GEMM tile family of the bf16 (and WNA16) expert GEMMs, for moe_problem's
+ * tile_hint.  MOE_TILE_AUTO lets the library choose from the average routed
+ * rows per expert; the others force one family (tests and tuning sweeps). */
+typedef enum {
+    MOE_TILE_AUTO = 0,
+    MOE_TILE_DMA_160 = 1,     /* 160-row LDS-DMA ring (prefill-sized loads)       */
+    MOE_TILE_REG_64 = 2,      /* 64-row register-staged tile (bf16 only)          */
+    MOE_TILE_REG_16 = 3,      /* 16-row register-staged tile (bf16 only)          */
+    MOE_TILE_DMA_32 = 5,      /* 32-row LDS-DMA ring (decode-sized loads)         */
+    MOE_TILE_DMA_64 = 6       /* 64-row LDS-DMA ring                              */
+} moe_tile_hint;
+
+/* Bits of the device status word (moe_workspace_info.off_status).  Device-side
+ * data that the host cannot check is handled safely on the device, and the
+ * forward records here what it found; the word is rewritten by every forward
+ * (its align / tile-list kernel stores it, later kernels only OR bits in). */
+typedef enum {
+    MOE_DEV_ID_RANGE = 1,       /* a precomputed topk id outside [0, experts routed
+                                   over), or an expert_map value outside [-1, E):
+                                   that routed item got no row                    */
+    MOE_DEV_COUNT_CLAMPED = 2,  /* an expert_num_tokens value outside
+                                   [0, max_tokens], clamped into that range       */
+    MOE_DEV_ROWS_OVERFLOW = 4,  /* batched slabs hold more valid rows than M *
+                                   top_k (with M > 0): nothing was computed       */
+    MOE_DEV_TOKEN_MAP = 8       /* a token_map entry (other than -1) that names no
+                                   valid slab row contributed nothing             */
+} moe_device_status;
+
 /* Memory layout of w13 / w2 (see moe_pack_weights). */
 typedef enum {
     MOE_W_PLAIN = 0,          /* w13 [E, H, 2I], w2 [E, I, H], row-major          */
@@ -81,8 +114,16 @@ typedef enum {
 /* Problem description (host struct).
  *
  *   format       MOE_FMT_CONTIGUOUS or MOE_FMT_BATCHED.
- *   M            tokens.  Contiguous: rows of hidden/out.  Batched: rows of the
- *                token map and of out when batched_reduce is set (else unused).
+ *   M            tokens.  Contiguous: rows of hidden/out.  Batched: the tokens
+ *                behind the slabs: rows of the token map and of out when
+ *                batched_reduce is set.  In the batched format M > 0 promises
+ *                that the slabs hold at most M * top_k valid rows in total
+ *                (each valid slab row is one routed copy of a token); it sizes
+ *                the workspace and guides the tile choice.  M = 0 (only without
+ *                batched_reduce) allows up to E * max_tokens rows.  Slabs that
+ *                break the promise are not computed: the status word gets
+ *                MOE_DEV_ROWS_OVERFLOW, out is zero with batched_reduce and
+ *                left unwritten without.
  *   H, I         hidden and intermediate sizes; w13 is [E, H, 2I], w2 [E, I, H].
  *                Both must be multiples of 16; the fp8 path needs I % 128 == 0.
  *   E, top_k     experts (1..1024) and experts per token (1..E, <= 32).
@@ -159,6 +200,18 @@ typedef enum {
  *                128 x 128 block and one activation scale per token and 128
  *                columns (see moe_args).  Needs w_layout = MOE_W_PACKED.
  *                Other block sizes: MOE_ERR_UNSUPPORTED.
+ *   tile_hint    a moe_tile_hint.  MOE_TILE_AUTO (0): the library's choice.
+ *                Other values force one GEMM tile family (for tests and tuning
+ *                sweeps): bf16 weights take any family, WNA16 weights the
+ *                LDS-DMA ones (MOE_TILE_DMA_*); f32 and fp8 weights need 0
+ *                (MOE_ERR_UNSUPPORTED otherwise).  Unknown values:
+ *                MOE_ERR_INVALID_ARG.  Results stay within the tolerances
+ *                whatever the family; the workspace size may change with it.
+ *   gemm1_wave_cols
+ *                0: the library's choice.  2 or 4: the width of the first GEMM's
+ *                tile in the 160-row bf16 family (2 x 64 or 4 x 64 weight
+ *                columns a wave row); ignored by the other families.  Other
+ *                values: MOE_ERR_INVALID_ARG.
  */
 typedef struct {
     int32_t format;
@@ -174,6 +227,8 @@ typedef struct {
     int32_t apply_weight_on_input;
     int32_t chunk_tokens;
     int32_t fp8_block;
+    int32_t tile_hint;
+    int32_t gemm1_wave_cols;
 } moe_problem;
 
 /* Workspace layout chosen by the library for one problem.  All offsets are
@@ -194,7 +249,15 @@ typedef struct {
  *   aq / aq_scale: fp8 activation codes and per-row scales (fp8 weights)
  *   z [max_sorted_len, I]: SiLU(gate)*up per padded row (bf16 or f32; fp8
  *       codes + per-(row, 128-column) float scales z_scale on the fp8 path)
- *   o [M*top_k, H] (contiguous): each routed item's expert output, float.  */
+ *   o [max_sorted_len, H] (contiguous, and batched with batched_reduce):
+ *       each routed item's expert output at its padded position, float
+ *   o2 [max_sorted_len, H]: when the second GEMM runs as two K halves, the
+ *       second half's partial outputs (the item's output is then o + o2);
+ *       off_o2 = 0 when it does not
+ *   status [1] int32: the device status word, an OR of moe_device_status
+ *       bits, 0 when the device found nothing to report.
+ * The layout depends on the problem and on the compute-unit count of the
+ * device (a device attribute query; no device work).  */
 typedef struct {
     size_t bytes;
     int32_t block_m;
@@ -202,11 +265,13 @@ typedef struct {
     int64_t max_sorted_len;
     size_t off_topk_ids, off_topk_weights, off_expert_counts, off_expert_offsets, off_sorted_ids,
         off_expert_ids, off_num_post_padded, off_aq, off_aq_scale, off_z, off_z_scale, off_o;
+    size_t off_o2, off_status;
 } moe_workspace_info;
 
-/* Fills *info for problem *p (host only, no device work).  The caller then
- * provides a device buffer of info->bytes, 256-byte aligned.  Returns MOE_OK,
- * MOE_ERR_INVALID_ARG or MOE_ERR_UNSUPPORTED (same checks as moe_forward). */
+/* Fills *info for problem *p (host only, no device work; reads the current
+ * device's compute-unit count).  The caller then provides a device buffer of
+ * info->bytes, 256-byte aligned.  Returns MOE_OK, MOE_ERR_INVALID_ARG or
+ * MOE_ERR_UNSUPPORTED (same checks as moe_forward). */
 int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* info);
 
 /* Device pointers of one forward (host struct; NULL where unused).
@@ -220,7 +285,12 @@ int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* info);
  *   expert_num_tokens batched: [E] int32 valid rows per slab.
  *   token_map, token_map_w
  *                     batched_reduce: [M, top_k] flat slab row e*max_tokens+i
- *                     holding token t's j-th routed copy, and its weight.
+ *                     holding token t's j-th routed copy, and its weight; -1
+ *                     for a copy that has no row here (served by another
+ *                     expert-parallel rank), which contributes nothing.  Other
+ *                     entries that name no valid slab row (outside
+ *                     [0, E*max_tokens), or i >= expert_num_tokens[e])
+ *                     contribute nothing and set MOE_DEV_TOKEN_MAP.
  *   w13, w2           [E, H, 2I] (gate = columns [0, I), up = [I, 2I)), [E, I, H];
  *                     MOE_U4 codes two per byte along the last dimension, the
  *                     even column in the low nibble: [E, H, I], [E, I, H / 2].

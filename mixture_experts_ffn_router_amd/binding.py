@@ -21,6 +21,9 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3FN, MOE_U8, MOE_U4 = 0, 1, 2, 3, 4
 MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID, MOE_ROUTE_PRECOMPUTED = 0, 1, 2
 MOE_FMT_CONTIGUOUS, MOE_FMT_BATCHED = 0, 1
 MOE_W_PLAIN, MOE_W_PACKED = 0, 1
+MOE_TILE_AUTO, MOE_TILE_DMA_160, MOE_TILE_REG_64, MOE_TILE_REG_16 = 0, 1, 2, 3
+MOE_TILE_DMA_32, MOE_TILE_DMA_64 = 5, 6
+MOE_DEV_ID_RANGE, MOE_DEV_COUNT_CLAMPED, MOE_DEV_ROWS_OVERFLOW, MOE_DEV_TOKEN_MAP = 1, 2, 4, 8
 
 EXPORTED = ("moe_workspace_shapes", "moe_forward", "moe_forward_timed", "moe_packed_weight_bytes",
             "moe_pack_weights", "moe_status_string", "moe_version")
@@ -39,7 +42,8 @@ class moe_problem(ctypes.Structure):
                 ("has_w2_bias", ctypes.c_int32), ("batched_reduce", ctypes.c_int32),
                 ("w_layout", ctypes.c_int32), ("global_experts", ctypes.c_int32),
                 ("apply_weight_on_input", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
-                ("fp8_block", ctypes.c_int32)]
+                ("fp8_block", ctypes.c_int32), ("tile_hint", ctypes.c_int32),
+                ("gemm1_wave_cols", ctypes.c_int32)]
 
 
 class moe_workspace_info(ctypes.Structure):
@@ -48,7 +52,7 @@ class moe_workspace_info(ctypes.Structure):
         (n, ctypes.c_size_t) for n in (
             "off_topk_ids", "off_topk_weights", "off_expert_counts", "off_expert_offsets",
             "off_sorted_ids", "off_expert_ids", "off_num_post_padded", "off_aq", "off_aq_scale",
-            "off_z", "off_z_scale", "off_o")]
+            "off_z", "off_z_scale", "off_o", "off_o2", "off_status")]
 
 
 class moe_args(ctypes.Structure):
@@ -212,6 +216,8 @@ class Problem:
     apply_weight_on_input: bool = False
     chunk_tokens: int = 0
     fp8_block: int = 0
+    tile_hint: int = MOE_TILE_AUTO
+    gemm1_wave_cols: int = 0
 
     def c(self) -> moe_problem:
         return moe_problem(self.fmt, self.M, self.H, self.I, self.E, self.top_k, self.max_tokens,
@@ -221,7 +227,7 @@ class Problem:
                            int(self.has_w13_bias), int(self.has_w2_bias),
                            int(self.batched_reduce), int(self.w_layout), int(self.global_experts),
                            int(self.apply_weight_on_input), int(self.chunk_tokens),
-                           int(self.fp8_block))
+                           int(self.fp8_block), int(self.tile_hint), int(self.gemm1_wave_cols))
 
 
 @dataclass
@@ -291,6 +297,13 @@ def allocate_workspace(problem: Problem, device):
     return ws, info
 
 
+def device_status(workspace, info: moe_workspace_info) -> int:
+    """The device status word of the last forward on `workspace` (an OR of
+    the MOE_DEV_* bits); synchronises through the device-to-host copy."""
+    off = int(info.off_status)
+    return int(workspace[off:off + 4].view(__import__("torch").int32).item())
+
+
 def current_stream_handle(device=None) -> int:
     import torch
     return torch.cuda.current_stream(device).cuda_stream
@@ -302,7 +315,7 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
               w2_bias=None, topk_ids=None, topk_weights=None, w13_scale=None, w2_scale=None,
               out_dtype=None, out=None, workspace=None, expert_map=None,
               apply_weight_on_input=False, chunk_tokens=0, fp8_block=0, w13_zero=None,
-              w2_zero=None):
+              w2_zero=None, tile_hint=MOE_TILE_AUTO, gemm1_wave_cols=0):
     """Contiguous-format forward on torch device tensors (the MindIE-SD
     page's fused_moe argument list, single device).  w13 may be a
     PackedWeights (then w2 is ignored).  expert_map [global experts] int32
@@ -311,8 +324,10 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
     scales (w13_scale [E, 2I/128, ceil(H/128)], w2_scale [E, ceil(H/128),
     I/128]).  WNA16 weights come packed (pack_weights(..., wq_bits)) with
     group scales w13_scale [E, ceil(H/128), 2I] / w2_scale [E, ceil(I/128), H]
-    and optional uint8 zero points of the same shapes.  Returns (out,
-    workspace tensor, workspace info)."""
+    and optional uint8 zero points of the same shapes.  tile_hint /
+    gemm1_wave_cols force a GEMM tile family / GEMM1 width (moe_problem's
+    tuning fields; 0 = the library's choice).  Returns (out, workspace
+    tensor, workspace info)."""
     import torch
     M = hidden.shape[0]
     w13, w2, E, H, I, wdt, layout = _weights(w13, w2)
@@ -333,7 +348,7 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
                    w_layout=layout,
                    global_experts=0 if expert_map is None else int(expert_map.numel()),
                    apply_weight_on_input=apply_weight_on_input, chunk_tokens=chunk_tokens,
-                   fp8_block=fp8_block)
+                   fp8_block=fp8_block, tile_hint=tile_hint, gemm1_wave_cols=gemm1_wave_cols)
     if out is None:
         out = torch.empty(M, H, dtype=odt, device=hidden.device)
     if workspace is None:
@@ -352,12 +367,15 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
 def fused_moe_batched(hidden, expert_num_tokens, w13, w2, *, M: int = 0, top_k: int = 1,
                       a_scale=None, w13_scale=None, w2_scale=None, w13_bias=None, w2_bias=None,
                       token_map=None, token_map_w=None, out_dtype=None, out=None,
-                      workspace=None, fp8_block=0, w13_zero=None, w2_zero=None):
+                      workspace=None, fp8_block=0, w13_zero=None, w2_zero=None,
+                      tile_hint=MOE_TILE_AUTO):
     """Batched-format forward: hidden [E, max_tokens, H] + expert_num_tokens [E].
     M, top_k (when M > 0) promise that the slabs hold at most M * top_k valid
-    rows, which bounds the workspace.  With token_map / token_map_w
-    ([M, top_k]) the rows are also weighted and reduced into out [M, H];
-    otherwise out is [E, max_tokens, H]."""
+    rows, which bounds the workspace (slabs that break the promise are not
+    computed; the device status word reports it).  With token_map /
+    token_map_w ([M, top_k]; -1 for a copy with no row here) the rows are
+    also weighted and reduced into out [M, H]; otherwise out is
+    [E, max_tokens, H]."""
     import torch
     E, T, H = hidden.shape
     w13, w2, _, _, I, wdt, layout = _weights(w13, w2)
@@ -370,7 +388,7 @@ def fused_moe_batched(hidden, expert_num_tokens, w13, w2, *, M: int = 0, top_k: 
                    out_dtype=_dtype_code(torch.empty(0, dtype=odt)),
                    routing=MOE_ROUTE_PRECOMPUTED, has_w13_bias=w13_bias is not None,
                    has_w2_bias=w2_bias is not None, batched_reduce=reduce, w_layout=layout,
-                   fp8_block=fp8_block)
+                   fp8_block=fp8_block, tile_hint=tile_hint)
     if out is None:
         shape = (M, H) if reduce else (E, T, H)
         out = torch.empty(shape, dtype=odt, device=hidden.device)

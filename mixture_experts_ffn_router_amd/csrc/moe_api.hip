@@ -7,7 +7,6 @@
 // "Fused MoE Modular Kernel" page.  All checks run on the host before
 // anything is enqueued.
 #include <cmath>
-#include <cstdlib>
 
 #include "moe_internal.h"
 
@@ -76,6 +75,20 @@ static int validate(const moe_problem* p)
         (p->fp8_block != 128 || w != MOE_FP8_E4M3FN || p->w_layout != MOE_W_PACKED))
         return MOE_ERR_UNSUPPORTED;
 
+    // per-call tuning hints (tile family, GEMM1 width); 0 = the library's choice
+    const int th = p->tile_hint;
+    if (th != MOE_TILE_AUTO && th != MOE_TILE_DMA_160 && th != MOE_TILE_REG_64 &&
+        th != MOE_TILE_REG_16 && th != MOE_TILE_DMA_32 && th != MOE_TILE_DMA_64)
+        return MOE_ERR_INVALID_ARG;
+    if (p->gemm1_wave_cols != 0 && p->gemm1_wave_cols != 2 && p->gemm1_wave_cols != 4)
+        return MOE_ERR_INVALID_ARG;
+    if (th != MOE_TILE_AUTO) {
+        if (w != MOE_BF16 && w != MOE_U8 && w != MOE_U4)
+            return MOE_ERR_UNSUPPORTED;
+        if (w != MOE_BF16 && (th == MOE_TILE_REG_64 || th == MOE_TILE_REG_16))
+            return MOE_ERR_UNSUPPORTED;   // WNA16 runs the LDS-DMA families only
+    }
+
     if (p->global_experts < 0 || p->chunk_tokens < 0 || p->apply_weight_on_input < 0 ||
         p->apply_weight_on_input > 1)
         return MOE_ERR_INVALID_ARG;
@@ -127,27 +140,26 @@ static int validate(const moe_problem* p)
 }
 
 // GEMM tile family from the average rows per expert: decode-sized loads use
-// 16-row tiles, mid-sized loads 64-row tiles, prefill-sized loads 160-row
-// tiles so that one tile holds a whole expert of about 128 rows.
+// 32-row DMA tiles, mid-sized loads 64-row tiles, prefill-sized loads 160-row
+// tiles so that one tile holds a whole expert of about 128 rows.  A caller's
+// tile_hint (validated above) forces the family.
 static int choose_tile(const moe_problem* p, int64_t rows_cap)
 {
     if (p->w_dtype == MOE_FP8_E4M3FN)
         return p->w_layout == MOE_W_PACKED ? TILE_FP8_DMA : TILE_FP8;
     if (p->w_dtype == MOE_F32)
         return TILE_DECODE;
-    if (p->w_dtype == MOE_U8 || p->w_dtype == MOE_U4) {   // DMA families only
-        const double avg = (double)rows_cap / p->E;
-        return avg <= 12 ? TILE_DECODE_DMA : avg <= 48 ? TILE_MID_DMA : TILE_PREFILL;
-    }
-    // tuning override: MOE_TILE_CFG = 0 (prefill) | 1 (mid) | 2 (decode) | 4 (decode, DMA)
-    // | 5 (mid, DMA), read on every call
-    if (const char* env = std::getenv("MOE_TILE_CFG")) {
-        const int v = std::atoi(env);
-        if (v == TILE_PREFILL || v == TILE_MID || v == TILE_DECODE || v == TILE_DECODE_DMA ||
-            v == TILE_MID_DMA)
-            return v;
+    switch (p->tile_hint) {
+    case MOE_TILE_DMA_160: return TILE_PREFILL;
+    case MOE_TILE_REG_64: return TILE_MID;
+    case MOE_TILE_REG_16: return TILE_DECODE;
+    case MOE_TILE_DMA_32: return TILE_DECODE_DMA;
+    case MOE_TILE_DMA_64: return TILE_MID_DMA;
+    default: break;
     }
     const double avg = (double)rows_cap / p->E;
+    if (p->w_dtype == MOE_U8 || p->w_dtype == MOE_U4)     // DMA families only
+        return avg <= 12 ? TILE_DECODE_DMA : avg <= 48 ? TILE_MID_DMA : TILE_PREFILL;
     if (avg <= 12)
         return TILE_DECODE_DMA;
     if (avg <= 48)
@@ -159,8 +171,10 @@ static int choose_tile(const moe_problem* p, int64_t rows_cap)
 // position of every routed item in the sorted order.
 enum { INT_CHUNK_OFF = 0, INT_CHUNK_EXPERT = 1, INT_INV = 2, INT_O2 = 3, INT_REGIONS = 4 };
 
-static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_offs = nullptr,
-                  int* cfg_out = nullptr)
+// Workspace layout of problem p on a device with `cus` compute units (the
+// GEMM2 K-split choice, and so the o2 region, depends on it).
+static int layout(const moe_problem* p, int cus, moe_workspace_info* info,
+                  size_t* chunk_offs = nullptr, int* cfg_out = nullptr)
 {
     size_t off_chunk_off = 0, off_chunk_expert = 0, off_inv = 0, off_o2 = 0;
     const int rc = validate(p);
@@ -172,8 +186,10 @@ static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_
     int64_t rows_cap = MK;
     if (batched) {
         rows_cap = (int64_t)p->E * p->max_tokens;
+        // M > 0 promises at most M * top_k valid slab rows (each one routed
+        // copy of a token); the tile-list kernel checks the promise on the device
         if (p->M > 0 && MK < rows_cap)
-            rows_cap = MK;   // every valid slab row is one routed copy of a token
+            rows_cap = MK;
     }
     const int BM = ALIGN_BM;
     const int64_t max_sorted = rows_cap + (int64_t)p->E * (BM - 1);
@@ -196,6 +212,7 @@ static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_
     w.off_sorted_ids = take((size_t)max_sorted * 4);
     w.off_expert_ids = take((size_t)w.max_blocks * 4);
     w.off_num_post_padded = take(4);
+    w.off_status = take(4);
     off_chunk_off = take((size_t)(p->E + 1) * 4);
     off_chunk_expert = take((size_t)w.max_blocks * 4);
     off_inv = take(batched ? 0 : (size_t)MK * 4);
@@ -216,8 +233,9 @@ static int layout(const moe_problem* p, moe_workspace_info* info, size_t* chunk_
     const bool split = p->w_dtype != MOE_U8 && p->w_dtype != MOE_U4 && gemm2_k_split(
         cfg, p->format, p->batched_reduce,
         expected_chunks(p->format, chunk_rows(p), p->top_k, p->E, p->max_tokens, tile_rows(cfg)),
-        p->H, p->I, device_cus());
+        p->H, p->I, cus);
     off_o2 = take(split ? (size_t)orows * p->H * 4 : 0);
+    w.off_o2 = split ? off_o2 : 0;
     w.bytes = off;
     *info = w;
     if (chunk_offs) {
@@ -262,6 +280,7 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
     P.wq = (p->w_dtype == MOE_U8) ? 8 : (p->w_dtype == MOE_U4) ? 4 : 0;
     P.BM = w.block_m;
     P.cfg = cfg;
+    P.g1wc = p->gemm1_wave_cols;
     P.CH = tile_rows(cfg);
     P.chunk_off = (int32_t*)(ws + chunk_offs[INT_CHUNK_OFF]);
     P.chunk_expert = (int32_t*)(ws + chunk_offs[INT_CHUNK_EXPERT]);
@@ -286,6 +305,8 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
     P.o = (float*)(ws + w.off_o);
     P.g2split = chunk_offs[INT_O2] != 0;
     P.o2 = P.g2split ? (float*)(ws + chunk_offs[INT_O2]) : nullptr;
+    P.status = (int32_t*)(ws + w.off_status);
+    P.status_or = 0;
     return P;
 }
 
@@ -331,7 +352,9 @@ extern "C" int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* in
 {
     if (!info)
         return MOE_ERR_INVALID_ARG;
-    return layout(p, info);
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    return layout(p, device_cus(dev), info);
 }
 
 static int run_path(const moe_problem* p, const Plan& P, const moe_args& A, hipStream_t s,
@@ -343,7 +366,9 @@ static int forward(const moe_problem* p, const moe_args* a, void* workspace,
     moe_workspace_info w;
     size_t chunk_offs[INT_REGIONS];
     int cfg = 0;
-    int rc = layout(p, &w, chunk_offs, &cfg);
+    const hipStream_t s = (hipStream_t)stream;
+    const int dev = stream_device(s), cus = device_cus(dev);
+    int rc = layout(p, cus, &w, chunk_offs, &cfg);
     if (rc != MOE_OK)
         return rc;
     rc = check_args(p, a);
@@ -352,8 +377,9 @@ static int forward(const moe_problem* p, const moe_args* a, void* workspace,
     if (!workspace || ((uintptr_t)workspace % ALIGN) || workspace_bytes < w.bytes)
         return MOE_ERR_WORKSPACE;
 
-    const hipStream_t s = (hipStream_t)stream;
     Plan P = make_plan(p, w, (char*)workspace, chunk_offs, cfg);
+    P.dev = dev;
+    P.cus = cus;
     P.emap = a->expert_map;
     const bool batched = p->format == MOE_FMT_BATCHED;
     if (!batched && p->M == 0)
@@ -374,6 +400,7 @@ static int forward(const moe_problem* p, const moe_args* a, void* workspace,
     for (int c0 = 0; c0 < p->M; c0 += P.M) {
         Plan Pc = P;
         Pc.M = (p->M - c0 < P.M) ? p->M - c0 : P.M;
+        Pc.status_or = c0 > 0;            // later chunks add their findings
         moe_args ac = *a;
         ac.hidden = (const char*)a->hidden + (size_t)c0 * p->H * aes;
         ac.out = (char*)a->out + (size_t)c0 * p->H * oes;

@@ -1557,8 +1557,8 @@ static hipError_t run_gemm1(const Gemm1Args& a, const Plan& P, hipStream_t s)
     Gemm1Args g = a;
     g.s.n_tiles = (a.I + S::BNZ - 1) / S::BNZ;
     auto kern = k_gemm1<DT, FM, WN>;
-    static int cached = 0;
-    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached)),
+    static std::atomic<int> cached[MAX_DEVICES];
+    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, P)),
         block(256);
     hipLaunchKernelGGL(kern, grid, block, 0, s, g);
     return hipGetLastError();
@@ -1571,8 +1571,8 @@ static hipError_t run_gemm2(const Gemm2Args& a, const Plan& P, hipStream_t s)
     Gemm2Args g = a;
     g.s.n_tiles = (a.H + S::BN - 1) / S::BN;
     auto kern = k_gemm2<DT, FM, WN>;
-    static int cached = 0;
-    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached)),
+    static std::atomic<int> cached[MAX_DEVICES];
+    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, P)),
         block(256);
     hipLaunchKernelGGL(kern, grid, block, 0, s, g);
     return hipGetLastError();
@@ -1586,8 +1586,8 @@ static hipError_t run_gemm1_dma(const Gemm1Args& a, const Plan& P, hipStream_t s
     Gemm1Args g = a;
     g.s.n_tiles = (a.I + BNZ - 1) / BNZ;
     auto kern = k_gemm1_dma<FMW, WC, NS, PACKED, Q>;
-    static int cached = 0;
-    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, S::NT)),
+    static std::atomic<int> cached[MAX_DEVICES];
+    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, P, S::NT)),
         block(S::NT);
     hipLaunchKernelGGL(kern, grid, block, 0, s, g);
     return hipGetLastError();
@@ -1600,8 +1600,8 @@ static hipError_t run_gemm2_dma(const Gemm2Args& a, const Plan& P, hipStream_t s
     Gemm2Args g = a;
     g.s.n_tiles = (a.H + S::BN - 1) / S::BN * g.ksplit;
     auto kern = k_gemm2_dma<FMW, WC, NS, PACKED, Q>;
-    static int cached = 0;
-    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, S::NT)),
+    static std::atomic<int> cached[MAX_DEVICES];
+    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, P, S::NT)),
         block(S::NT);
     hipLaunchKernelGGL(kern, grid, block, 0, s, g);
     return hipGetLastError();
@@ -1626,28 +1626,42 @@ static bool about_one_chunk(const Plan& P)
 // Wave columns of the large bf16 GEMM1 tile: 4 (256 columns, 8 waves) when
 // there are a few tiles per CU, or when experts hold about one row chunk on
 // average (their weights are read once, and the wide tile halves the column
-// tiles that re-read each chunk's activation rows through L2), else 2.
-// Tuning override: MOE_GEMM1_WC = 2 | 4, read on every call.
+// tiles that re-read each chunk's activation rows through L2), else 2.  A
+// caller's gemm1_wave_cols (2 or 4) overrides the choice.
 static int gemm1_wave_cols(const Plan& P)
 {
-    if (const char* env = getenv("MOE_GEMM1_WC")) {
-        const int v = atoi(env);
-        if (v == 2 || v == 4)
-            return v;
-    }
+    if (P.g1wc == 2 || P.g1wc == 4)
+        return P.g1wc;
     if (about_one_chunk(P))
         return 4;
-    return expected_chunks(P) * ((P.I + 127) / 128) <= 8 * device_cus() ? 4 : 2;
+    return expected_chunks(P) * ((P.I + 127) / 128) <= 8 * (int64_t)P.cus ? 4 : 2;
 }
 
-int device_cus()
+int stream_device(hipStream_t s)
 {
-    static int cus = 0;
+    int dev = 0;
+    if (s) {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice(s, &d) == hipSuccess)
+            return (int)d;
+        (void)hipGetLastError();
+    }
+    (void)hipGetDevice(&dev);
+    return dev;
+}
+
+int device_cus(int dev)
+{
+    static std::atomic<int> cache[MAX_DEVICES];
+    const int slot = (dev >= 0 && dev < MAX_DEVICES) ? dev : -1;
+    int cus = slot >= 0 ? cache[slot].load(std::memory_order_relaxed) : 0;
     if (cus == 0) {
-        int dev = 0, n = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            (void)hipGetLastError();
         cus = n > 0 ? n : 256;
+        if (slot >= 0)
+            cache[slot].store(cus, std::memory_order_relaxed);
     }
     return cus;
 }
@@ -1812,7 +1826,7 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
         // about one tile per CU: one workgroup per CU with a 4-stage ring keeps
         // three K stages in flight; otherwise two workgroups per CU overlap
         // each other's prologues and epilogues
-        if (expected_chunks(P) * ((P.H + 127) / 128) <= device_cus() * 5 / 4)
+        if (expected_chunks(P) * ((P.H + 127) / 128) <= (int64_t)P.cus * 5 / 4)
             return P.wpacked ? run_gemm2_dma<5, 2, 4, true>(g, P, s)
                              : run_gemm2_dma<5, 2, 4, false>(g, P, s);
         return P.wpacked ? run_gemm2_dma<5, 2, 2, true>(g, P, s)

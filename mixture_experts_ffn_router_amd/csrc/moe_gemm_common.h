@@ -3,6 +3,8 @@
 // LDS-DMA helpers and the DMA ring loop.  gfx950 only.
 #pragma once
 
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -291,18 +293,22 @@ __device__ __forceinline__ void pin(const T& v)
 
 // Persistent grid: every workgroup the device holds at once (a multiple of
 // the 8 XCDs), capped by the largest possible tile count.  Each kernel
-// instance queries its occupancy once; `cached` is that instance's slot.
+// instance queries its occupancy once per device; `cache` is that instance's
+// per-device slot array (zero = not yet known).  Two threads may both query
+// and store: they store the same value.
 template <typename K>
-static unsigned persistent_grid(K kernel, int64_t max_tiles, int& cached, int threads = 256)
+static unsigned persistent_grid(K kernel, int64_t max_tiles, std::atomic<int>* cache,
+                                const Plan& P, int threads = 256)
 {
-    if (cached == 0) {
-        int dev = 0, cus = 0, occ = 0;
-        (void)hipGetDevice(&dev);
-        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int slot = (P.dev >= 0 && P.dev < MAX_DEVICES) ? P.dev : 0;
+    int per_cu = cache[slot].load(std::memory_order_relaxed);
+    if (per_cu == 0) {
+        int occ = 0;
         (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0);
-        cached = (cus > 0 ? cus : 256) * (occ > 0 ? occ : 1);
+        per_cu = occ > 0 ? occ : 1;
+        cache[slot].store(per_cu, std::memory_order_relaxed);
     }
-    int64_t g = cached;
+    int64_t g = (int64_t)P.cus * per_cu;
     const int64_t cap = (max_tiles + 7) / 8 * 8;
     if (g > cap)
         g = cap;

@@ -735,8 +735,8 @@ static hipError_t run_gemm1_f8(const Gemm1Args& a, const Plan& P, hipStream_t s)
     Gemm1Args g = a;
     g.s.n_tiles = a.I / 128;
     auto kern = k_gemm1_f8<BW>;
-    static int cached = 0;
-    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, S::NT)),
+    static std::atomic<int> cached[MAX_DEVICES];
+    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, P, S::NT)),
         block(S::NT);
     hipLaunchKernelGGL(kern, grid, block, 0, s, g);
     return hipGetLastError();
@@ -749,8 +749,8 @@ static hipError_t run_gemm2_f8(const Gemm2Args& a, const Plan& P, hipStream_t s)
     Gemm2Args g = a;
     g.s.n_tiles = (a.H + S::BN - 1) / S::BN;
     auto kern = k_gemm2_f8<BW>;
-    static int cached = 0;
-    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, S::NT)),
+    static std::atomic<int> cached[MAX_DEVICES];
+    const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, P, S::NT)),
         block(S::NT);
     hipLaunchKernelGGL(kern, grid, block, 0, s, g);
     return hipGetLastError();

@@ -213,6 +213,8 @@ struct Plan {
     int BM;                         // align granularity: each expert run padded to BM rows
     int CH;                         // rows per GEMM tile (a multiple of BM)
     int cfg;                        // GEMM tile family (see moe_gemm.hip)
+    int g1wc;                       // 160-row bf16 family: GEMM1 wave columns (2 | 4)
+    int dev, cus;                   // device of the launch stream and its compute units
     int64_t rows_cap;               // upper bound of valid routed rows
     int64_t max_sorted;             // rows_cap + E * (BM - 1)
     int max_blocks;                 // max_sorted / BM
@@ -236,6 +238,9 @@ struct Plan {
     float* o;
     float* o2;                      // GEMM2 split in K: the second half's partial outputs
     int g2split;                    // GEMM2 runs as two K halves (o + o2)
+    int32_t* status;                // device status word (moe_device_status bits)
+    int status_or;                  // 0: the align stage stores the word; 1: ORs into it
+                                    // (later chunks of a chunked forward)
 };
 
 // Row stride of the group-major fp8 z scales: every padded position plus one
@@ -261,8 +266,14 @@ inline int64_t expected_chunks(int fmt, int64_t M, int K, int E, int T, int CH)
     return active > fill ? active : fill;
 }
 
-// Compute units of the current device (cached after the first query).
-int device_cus();
+// Devices whose attributes the library caches (device ordinals below this).
+constexpr int MAX_DEVICES = 64;
+
+// Device of a launch stream (the current device for the null stream).
+int stream_device(hipStream_t s);
+
+// Compute units of device `dev` (queried once per device, then cached).
+int device_cus(int dev);
 
 // GEMM2 of the 160-row bf16 family runs with 256-column tiles split in two K
 // halves when whole tiles would not cover the CUs and K is long: the halves

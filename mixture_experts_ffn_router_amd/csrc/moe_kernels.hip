@@ -1,6 +1,8 @@
 // Bandwidth kernels of the fused MoE forward for gfx950: router (top-k),
 // align (permute metadata), batched tile list, per-row fp8 quantisation and
 // the top-k weight-and-reduce (unpermute).  None of them uses MFMA.
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -349,40 +351,72 @@ struct AlignOut {
     int64_t max_sorted;
     const int32_t* emap;        // [Er] global -> local expert (-1: elsewhere), or null
     int Er;                     // range of the routed ids
+    int32_t* status;            // device status word
+    int status_or;              // 0: store the align's findings; 1: OR them in
 };
 
-// LDS scratch of align_items (ints), after the item batch.
+// The align stage's findings -> the device status word (one thread).
+__device__ __forceinline__ void align_status(const AlignOut& O, int bits)
+{
+    if (O.status_or)
+        *O.status |= bits;      // a later chunk: stream order leaves no other writer
+    else
+        *O.status = bits;
+}
+
+// LDS scratch of align_items (ints), after the item batch: per-wave counts,
+// three prefix arrays, scan totals, and one flag word.
 __host__ __device__ constexpr int align_scratch_ints(int E)
 {
-    return ALIGN_WAVES * E + 3 * (E + 1) + ALIGN_WAVES;
+    return ALIGN_WAVES * E + 3 * (E + 1) + ALIGN_WAVES + 1;
 }
 
 // Item i of ids_g[b0 ..) -> ids_s[i] as a local expert id: through the
-// expert map when there is one; ids outside the routed range, unmapped
-// experts and map values outside [0, E) become -1 (no row).  All threads.
-__device__ void align_load(const int32_t* __restrict__ ids_g, int b0, int len, int* ids_s,
+// expert map when there is one.  Unmapped experts (map value -1) become -1
+// (no row); so do ids outside the routed range and map values outside
+// [-1, E), for which the function returns true (in the threads that saw
+// one).  All threads.
+__device__ bool align_load(const int32_t* __restrict__ ids_g, int b0, int len, int* ids_s,
                            const AlignOut& O)
 {
     const int tid = threadIdx.x, E = O.E;
+    bool bad = false;
     for (int i0 = 0; i0 < len; i0 += 1024 * 8) {
         int v[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int i = i0 + u * 1024 + tid;
-            v[u] = (i < len) ? ids_g[b0 + i] : -1;
+            v[u] = (i < len) ? ids_g[b0 + i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * 1024 + tid;
+            if (i < len && (v[u] < 0 || v[u] >= O.Er)) {
+                bad = true;
+                v[u] = -1;
+            }
         }
         if (O.emap) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                v[u] = (v[u] >= 0 && v[u] < O.Er) ? O.emap[v[u]] : -1;
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * 1024 + tid;
+                if (i < len && v[u] >= 0) {
+                    v[u] = O.emap[v[u]];
+                    if (v[u] < -1 || v[u] >= E) {
+                        bad = true;
+                        v[u] = -1;
+                    }
+                }
+            }
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int i = i0 + u * 1024 + tid;
             if (i < len)
-                ids_s[i] = (v[u] >= 0 && v[u] < E) ? v[u] : -1;
+                ids_s[i] = v[u];
         }
     }
+    return bad;
 }
 
 // Per-wave counts of ids_s[0, len): wave w owns [w ch, (w+1) ch) and
@@ -489,14 +523,18 @@ __device__ void align_items(const int32_t* __restrict__ ids_g, int n, int* ids_s
     int* run = offs + (E + 1);                  // [E + 1] next free position (pass 2)
     int* choff = run + (E + 1);                 // [E + 1] chunk prefix
     int* tot = choff + (E + 1);                 // [ALIGN_WAVES]
+    int* bad = tot + ALIGN_WAVES;               // [1] an out-of-range id was seen
     const int tid = threadIdx.x;
     const int nb = (n + cap - 1) / cap;
+    if (tid == 0)
+        *bad = 0;
+    __syncthreads();
 
     // pass 1: per-expert totals
     int total_e = 0;
     if (nb <= 1) {
-        if (ids_g)
-            align_load(ids_g, 0, n, ids_s, O);
+        if (ids_g && align_load(ids_g, 0, n, ids_s, O))
+            atomicOr(bad, 1);
         __syncthreads();
         align_count_waves(ids_s, n, cnt, E);
         if (tid < E)
@@ -508,7 +546,8 @@ __device__ void align_items(const int32_t* __restrict__ ids_g, int n, int* ids_s
         for (int b = 0; b < nb; ++b) {
             const int b0 = b * cap, len = min(cap, n - b0);
             __syncthreads();
-            align_load(ids_g, b0, len, ids_s, O);
+            if (align_load(ids_g, b0, len, ids_s, O))
+                atomicOr(bad, 1);
             __syncthreads();
             for (int i = tid; i < len; i += 1024) {
                 const int e = ids_s[i];
@@ -534,6 +573,9 @@ __device__ void align_items(const int32_t* __restrict__ ids_g, int n, int* ids_s
         }
         align_scatter(ids_s, b0, len, cnt, run, O);
     }
+    __syncthreads();
+    if (tid == 0)
+        align_status(O, *bad ? MOE_DEV_ID_RANGE : 0);
 }
 
 // ---- the same align over many workgroups, for large batches of routed
@@ -551,11 +593,13 @@ __global__ void __launch_bounds__(1024) k_align_count(const int32_t* __restrict_
 {
     extern __shared__ int sh[];
     int* ids_s = sh;                            // [ALIGN_BLOCK]
-    int* cnt = sh + ALIGN_BLOCK;                // [E]
+    int* cnt = sh + ALIGN_BLOCK;                // [E + 1]: counts, then the block's flag
     const int b0 = blockIdx.x * ALIGN_BLOCK, len = min(ALIGN_BLOCK, Mk - b0);
-    for (int i = threadIdx.x; i < O.E; i += 1024)
+    for (int i = threadIdx.x; i <= O.E; i += 1024)
         cnt[i] = 0;
-    align_load(ids, b0, len, ids_s, O);
+    __syncthreads();
+    if (align_load(ids, b0, len, ids_s, O))
+        atomicOr(&cnt[O.E], 1);
     __syncthreads();
     for (int i = threadIdx.x; i < len; i += 1024) {
         const int e = ids_s[i];
@@ -563,8 +607,8 @@ __global__ void __launch_bounds__(1024) k_align_count(const int32_t* __restrict_
             atomicAdd(&cnt[e], 1);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < O.E; e += 1024)
-        hist[(int64_t)blockIdx.x * O.E + e] = cnt[e];
+    for (int e = threadIdx.x; e <= O.E; e += 1024)
+        hist[(int64_t)blockIdx.x * (O.E + 1) + e] = cnt[e];
 }
 
 __global__ void __launch_bounds__(1024) k_align_layout(int nblk, AlignOut O,
@@ -579,15 +623,21 @@ __global__ void __launch_bounds__(1024) k_align_layout(int nblk, AlignOut O,
     int total_e = 0;
     if (e < E)
         for (int b = 0; b < nblk; ++b)
-            total_e += hist[(int64_t)b * E + e];
+            total_e += hist[(int64_t)b * (E + 1) + e];
     align_layout(total_e, offs, run, choff, tot, O);
     if (e < E) {
         int base = run[e];
         for (int b = 0; b < nblk; ++b) {
-            const int c = hist[(int64_t)b * E + e];
-            hist[(int64_t)b * E + e] = base;
+            const int c = hist[(int64_t)b * (E + 1) + e];
+            hist[(int64_t)b * (E + 1) + e] = base;
             base += c;
         }
+    }
+    if (e == 0) {
+        int bad = 0;
+        for (int b = 0; b < nblk; ++b)
+            bad |= hist[(int64_t)b * (E + 1) + E];
+        align_status(O, bad ? MOE_DEV_ID_RANGE : 0);
     }
 }
 
@@ -602,8 +652,8 @@ __global__ void __launch_bounds__(1024) k_align_scatter(const int32_t* __restric
     int* run = cnt + ALIGN_WAVES * E;           // [E]
     const int b0 = blockIdx.x * ALIGN_BLOCK, len = min(ALIGN_BLOCK, Mk - b0);
     for (int e = threadIdx.x; e < E; e += 1024)
-        run[e] = hist[(int64_t)blockIdx.x * E + e];
-    align_load(ids, b0, len, ids_s, O);
+        run[e] = hist[(int64_t)blockIdx.x * (E + 1) + e];
+    (void)align_load(ids, b0, len, ids_s, O);   // k_align_count reported its findings
     __syncthreads();
     align_count_waves(ids_s, len, cnt, E);
     align_scatter(ids_s, b0, len, cnt, run, O);
@@ -614,7 +664,7 @@ static AlignOut align_out(const Plan& P)
     return AlignOut{P.counts,     P.offsets,       P.sorted_ids,  P.expert_ids, P.npp,
                     P.chunk_off,  P.chunk_expert,  P.inv,         P.E,          P.BM,
                     P.CH,         (int)P.sentinel, P.max_blocks,  P.max_sorted, P.emap,
-                    P.Er};
+                    P.Er,         P.status,        P.status_or};
 }
 
 __global__ void __launch_bounds__(1024) k_align(const int32_t* __restrict__ ids, int Mk, int cap,
@@ -624,11 +674,26 @@ __global__ void __launch_bounds__(1024) k_align(const int32_t* __restrict__ ids,
     align_items(ids, Mk, sh, cap, sh + cap, O);
 }
 
-static hipError_t set_lds(const void* kernel, size_t bytes)
+// Kernels launched with more than 64 KiB of dynamic LDS need the limit
+// raised first.  It is raised once per kernel and device to the most a
+// workgroup may hold (160 KiB on gfx950), so a forward makes no attribute
+// call once the device has seen one (graph capture included).
+constexpr int LDS_MAX = 160 * 1024;
+
+static hipError_t set_lds(const void* kernel, size_t bytes, int dev, std::atomic<int>* done)
 {
     if (bytes <= 65536)
         return hipSuccess;
-    return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (bytes > (size_t)LDS_MAX)
+        return hipErrorInvalidValue;
+    const int slot = (dev >= 0 && dev < MAX_DEVICES) ? dev : 0;
+    if (done[slot].load(std::memory_order_acquire))
+        return hipSuccess;
+    const hipError_t e =
+        hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_MAX);
+    if (e == hipSuccess)
+        done[slot].store(1, std::memory_order_release);
+    return e;
 }
 
 hipError_t launch_align(const Plan& P, const int32_t* ids, hipStream_t s)
@@ -639,14 +704,15 @@ hipError_t launch_align(const Plan& P, const int32_t* ids, hipStream_t s)
         const int nblk = (Mk + ALIGN_BLOCK - 1) / ALIGN_BLOCK;
         int32_t* hist = (int32_t*)P.o;
         const AlignOut O = align_out(P);
-        const size_t l1 = sizeof(int) * ((size_t)ALIGN_BLOCK + P.E);
+        const size_t l1 = sizeof(int) * ((size_t)ALIGN_BLOCK + P.E + 1);
         const size_t l2 = sizeof(int) * (3 * ((size_t)P.E + 1) + ALIGN_WAVES);
         const size_t l3 = sizeof(int) * ((size_t)ALIGN_BLOCK + (size_t)(ALIGN_WAVES + 1) * P.E);
-        hipError_t e = set_lds((const void*)k_align_count, l1);
+        static std::atomic<int> d1[MAX_DEVICES], d2[MAX_DEVICES], d3[MAX_DEVICES];
+        hipError_t e = set_lds((const void*)k_align_count, l1, P.dev, d1);
         if (e == hipSuccess)
-            e = set_lds((const void*)k_align_layout, l2);
+            e = set_lds((const void*)k_align_layout, l2, P.dev, d2);
         if (e == hipSuccess)
-            e = set_lds((const void*)k_align_scatter, l3);
+            e = set_lds((const void*)k_align_scatter, l3, P.dev, d3);
         if (e != hipSuccess)
             return e;
         hipLaunchKernelGGL(k_align_count, dim3(nblk), dim3(1024), l1, s, ids, Mk, O, hist);
@@ -656,7 +722,8 @@ hipError_t launch_align(const Plan& P, const int32_t* ids, hipStream_t s)
     }
     const int cap = Mk < ALIGN_CAP ? (Mk > 0 ? Mk : 1) : ALIGN_CAP;
     const size_t lds = sizeof(int) * ((size_t)cap + align_scratch_ints(P.E));
-    const hipError_t e = set_lds((const void*)k_align, lds);
+    static std::atomic<int> d0[MAX_DEVICES];
+    const hipError_t e = set_lds((const void*)k_align, lds, P.dev, d0);
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL(k_align, dim3(1), dim3(1024), lds, s, ids, Mk, cap, align_out(P));
@@ -667,8 +734,10 @@ hipError_t launch_align(const Plan& P, const int32_t* ids, hipStream_t s)
 // Batched format (vLLM "Fused MoE Modular Kernel" introduction): slab e holds
 // expert_num_tokens[e] valid rows.  Builds the same metadata as align with
 // item r = e*max_tokens + i, so the GEMMs are shared by both formats.  Counts
-// beyond max_tokens are clamped, and runs that would pass the workspace
-// capacity are dropped, so a bad count can never drive an access out of bounds.
+// outside [0, max_tokens] are clamped (MOE_DEV_COUNT_CLAMPED).  Slabs whose
+// runs would pass the workspace capacity (more valid rows than the caller
+// promised) get no rows at all (counts 0, MOE_DEV_ROWS_OVERFLOW), so a bad
+// count can never drive an access out of bounds and a reduce yields zeros.
 __global__ void __launch_bounds__(1024) k_tilelist(const int32_t* __restrict__ ent, int E, int T,
                                                    int BM, int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ offsets,
@@ -677,22 +746,30 @@ __global__ void __launch_bounds__(1024) k_tilelist(const int32_t* __restrict__ e
                                                    int32_t* __restrict__ npp, int sentinel,
                                                    int64_t max_sorted, int max_blocks, int CH,
                                                    int32_t* __restrict__ chunk_off,
-                                                   int32_t* __restrict__ chunk_expert)
+                                                   int32_t* __restrict__ chunk_expert,
+                                                   int32_t* __restrict__ status)
 {
     __shared__ int tot[ALIGN_WAVES];
     __shared__ int sh_start[1025], sh_cnt[1024], choff[1025];
+    __shared__ int sh_clamped;
     const int e = threadIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (threadIdx.x == 0)
+        sh_clamped = 0;
+    __syncthreads();
     int c = 0, padded = 0;
     if (e < E) {
-        c = min(max(ent[e], 0), T);
+        const int raw = ent[e];
+        c = min(max(raw, 0), T);
+        if (c != raw)
+            atomicOr(&sh_clamped, 1);
         padded = (c + BM - 1) / BM * BM;
     }
     int start;
-    const int total = block_exclusive_scan_1024(padded, tot, &start);
+    const int total = block_exclusive_scan_1024(padded, tot, &start);   // (its barrier orders sh_clamped)
     // more rows than the workspace was sized for: process nothing
     const bool fits = (int64_t)total <= max_sorted && total / BM <= max_blocks;
     if (e < E) {
-        counts[e] = c;
+        counts[e] = fits ? c : 0;
         offsets[e] = fits ? start : 0;
         sh_start[e] = start;
         sh_cnt[e] = c;
@@ -701,6 +778,7 @@ __global__ void __launch_bounds__(1024) k_tilelist(const int32_t* __restrict__ e
         offsets[E] = fits ? total : 0;
         sh_start[E] = total;
         *npp = fits ? total : 0;
+        *status = (sh_clamped ? MOE_DEV_COUNT_CLAMPED : 0) | (fits ? 0 : MOE_DEV_ROWS_OVERFLOW);
     }
     write_chunks(fits ? c : 0, CH, E, tot, choff, chunk_off, chunk_expert);
     if (!fits)
@@ -720,7 +798,7 @@ hipError_t launch_tilelist(const Plan& P, const int32_t* ent, hipStream_t s)
 {
     hipLaunchKernelGGL(k_tilelist, dim3(1), dim3(1024), 0, s, ent, P.E, P.T, P.BM, P.counts,
                        P.offsets, P.sorted_ids, P.expert_ids, P.npp, (int)P.sentinel,
-                       P.max_sorted, P.max_blocks, P.CH, P.chunk_off, P.chunk_expert);
+                       P.max_sorted, P.max_blocks, P.CH, P.chunk_off, P.chunk_expert, P.status);
     return hipGetLastError();
 }
 
@@ -907,7 +985,9 @@ hipError_t launch_quant_rows(const Plan& P, const void* hidden, hipStream_t s)
 // rounded once to the output type.  o holds each routed item's expert output
 // at its padded position: contiguous, row = inv[t*top_k + j] (the align
 // kernel's inverse permutation; -1 contributes nothing); batched,
-// row = offsets[e] + i for the slab row e*T + i named by token_map.  When
+// row = offsets[e] + i for the slab row e*T + i named by token_map (-1, or
+// an entry that names no valid slab row, contributes nothing; the latter
+// sets MOE_DEV_TOKEN_MAP).  When
 // GEMM2 ran as two K halves, an item's output is o[row] + o2[row] (that
 // order).  One workgroup per token: the token's item rows and weights are
 // the same for every thread (scalar loads), items without a row are skipped
@@ -918,11 +998,13 @@ hipError_t launch_quant_rows(const Plan& P, const void* hidden, hipStream_t s)
 template <typename TOut, int CPT>
 __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int H, int K,
                                                 const float* __restrict__ w,
-                                                const int32_t* __restrict__ tmap, int T,
+                                                const int32_t* __restrict__ tmap, int T, int E,
                                                 const int32_t* __restrict__ offsets,
+                                                const int32_t* __restrict__ counts,
                                                 const int32_t* __restrict__ inv,
                                                 const float* __restrict__ o2,
-                                                TOut* __restrict__ out)
+                                                TOut* __restrict__ out,
+                                                int32_t* __restrict__ status)
 {
     constexpr int IU = 8 / CPT;             // items in flight together: IU x CPT loads a thread
     const int64_t t = blockIdx.x;
@@ -942,8 +1024,14 @@ __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int
                 wj[u] = 0.0f;
                 if (j < K) {
                     if (tmap) {
+                        // the same entry in every thread: a uniform branch
                         const int flat = tmap[t * K + j];
-                        row[u] = (int64_t)offsets[flat / T] + flat % T;
+                        const int e = (flat >= 0) ? flat / T : 0, i = flat - e * T;
+                        if (flat >= 0 && e < E && i < counts[e])
+                            row[u] = (int64_t)offsets[e] + i;
+                        else if (flat != -1 && c0 == 0 && threadIdx.x == 0 &&
+                                 !(*status & MOE_DEV_ROWS_OVERFLOW))   // (then no row is valid)
+                            atomicOr(status, MOE_DEV_TOKEN_MAP);
                     } else {
                         row[u] = inv[t * K + j];
                     }
@@ -1005,7 +1093,7 @@ static void reduce_launch(const Plan& P, const float* w, const int32_t* tmap, vo
     const dim3 grid((unsigned)P.M), block(256);
 #define MOE_REDUCE(C)                                                                           \
     hipLaunchKernelGGL((k_reduce<TOut, C>), grid, block, 0, s, P.o, P.H, P.K, w, tmap, P.T,    \
-                       P.offsets, P.inv, P.o2, (TOut*)out)
+                       P.E, P.offsets, P.counts, P.inv, P.o2, (TOut*)out, P.status)
     if (per <= 1)
         MOE_REDUCE(1);
     else if (per <= 2)

@@ -25,6 +25,21 @@ TOL_WEIGHT = 1e-5          # routing weights, relative to max(1, routed_scaling_
 WQ_BITS = {"u8": 8, "u4": 4}
 
 
+# Named tile families for the tests (moe_problem.tile_hint / gemm1_wave_cols).
+TILES = {"auto": B.MOE_TILE_AUTO, "dma160": B.MOE_TILE_DMA_160, "reg64": B.MOE_TILE_REG_64,
+         "reg16": B.MOE_TILE_REG_16, "dma32": B.MOE_TILE_DMA_32, "dma64": B.MOE_TILE_DMA_64}
+
+
+def tile_kwargs(name: str) -> dict:
+    """fused_moe keyword arguments forcing a tile family: "dma160", or
+    "dma160/wc2" for that family with the 128-column GEMM1 tile."""
+    fam, _, wc = name.partition("/wc")
+    kw = {"tile_hint": TILES[fam]}
+    if wc:
+        kw["gemm1_wave_cols"] = int(wc)
+    return kw
+
+
 def device():
     assert torch.cuda.is_available(), "GPU tests need a ROCm device"
     return torch.device("cuda:0")
@@ -200,3 +215,94 @@ def check_rounded(out16: torch.Tensor, out32: torch.Tensor):
     ref = out32.to(torch.bfloat16)
     same = out16.view(torch.int16) == ref.view(torch.int16)
     assert bool(same.all()), f"{int((~same).sum())} bf16 outputs are not RNE(float32 result)"
+
+
+# ---------------------------------------------------------------- tile coverage
+# Row heights of the GEMM tile families that can run a weight type: a chunk of
+# an expert's rows is one tile's rows.  Sampling the first and last row of
+# every chunk of every height reaches every (expert, row chunk) tile whatever
+# family the library picks, with all its columns.
+CHUNK_HEIGHTS = {"fp8": (128,), "default": (32, 64, 160)}
+
+
+def chunk_positions(counts: np.ndarray, offsets: np.ndarray, heights) -> tuple:
+    """Padded positions of the first and last real row of every row chunk
+    (expert e's count rows dealt out evenly over ceil(count / CH) chunks in
+    16-row strips, as the GEMM schedule does).  Returns (positions, chunks
+    per height)."""
+    pos, nchunks = set(), {}
+    for CH in heights:
+        n = 0
+        for e in np.nonzero(counts)[0]:
+            c, base = int(counts[e]), int(offsets[e])
+            U = -(-c // 16)
+            nch = -(-c // CH)
+            q, extra = divmod(U, nch)
+            for j in range(nch):
+                u0 = j * q + min(j, extra)
+                rows = min(16 * (q + (j < extra)), c - 16 * u0)
+                pos.add(base + 16 * u0)
+                pos.add(base + 16 * u0 + rows - 1)
+            n += nch
+        nchunks[CH] = n
+    return np.array(sorted(pos), dtype=np.int64), nchunks
+
+
+def expert_output_rows(ws, info, positions, H, dev) -> np.ndarray:
+    """Each sampled routed item's expert output o[p] (+ o2[p] when the second
+    GEMM ran split in K), float32 from the workspace."""
+    rows = info.max_sorted_len
+    o = ws[info.off_o:info.off_o + rows * H * 4].view(torch.float32).view(rows, H)
+    idx = torch.as_tensor(positions, device=dev)
+    got = o[idx]
+    if info.off_o2:
+        o2 = ws[info.off_o2:info.off_o2 + rows * H * 4].view(torch.float32).view(rows, H)
+        got = got + o2[idx]
+    return got.cpu().numpy()
+
+
+def check_tiles_contiguous(inp, ws, info, dev, E_local=None):
+    """Every (expert, row chunk) tile of a contiguous forward: the expert
+    outputs of its first and last rows against the oracle's expert FFN of
+    that token.  Returns the tokens of the sampled items."""
+    cfg = inp["cfg"]
+    E = E_local or cfg.E
+    counts = region(ws, info.off_expert_counts, torch.int32, E)
+    offs = region(ws, info.off_expert_offsets, torch.int32, E + 1)
+    heights = CHUNK_HEIGHTS.get(cfg.weight, CHUNK_HEIGHTS["default"])
+    pos, nch = chunk_positions(counts, offs, heights)
+    npp = int(region(ws, info.off_num_post_padded, torch.int32, 1)[0])
+    sorted_ids = region(ws, info.off_sorted_ids, torch.int32, npp)
+    sid = sorted_ids[pos]
+    assert (sid < cfg.M * cfg.top_k).all(), "a sampled position is padding"
+    experts = np.searchsorted(offs, pos, side="right") - 1
+    tokens = (sid // cfg.top_k).astype(np.int64)
+    print(f"[tiles] {cfg.name}: {len(pos)} item rows over chunks {nch} of "
+          f"{int((counts > 0).sum())} experts", flush=True)
+    acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8", block=cfg.fp8_block)
+    ref, _ = oracle.expert_rows(oracle_experts(inp), acts, tokens, experts.astype(np.int32))
+    got = expert_output_rows(ws, info, pos, cfg.H, dev)
+    compare(cfg, got, ref, "expert rows of every tile")
+    return np.unique(tokens)
+
+
+def check_tiles_batched(inp, ws, info, out, dev):
+    """Every (expert, row chunk) tile of a batched forward without reduce:
+    the first and last rows' outputs against the oracle's expert FFN."""
+    cfg = inp["cfg"]
+    T = inp["max_tokens"]
+    counts = region(ws, info.off_expert_counts, torch.int32, cfg.E)
+    offs = region(ws, info.off_expert_offsets, torch.int32, cfg.E + 1)
+    heights = CHUNK_HEIGHTS.get(cfg.weight, CHUNK_HEIGHTS["default"])
+    pos, nch = chunk_positions(counts, offs, heights)
+    experts = np.searchsorted(offs, pos, side="right") - 1
+    rows = experts * T + (pos - offs[experts])
+    print(f"[tiles] {cfg.name}: {len(pos)} slab rows over chunks {nch} of "
+          f"{int((counts > 0).sum())} experts", flush=True)
+    acts = oracle.Acts(inp["hidden"].cpu(), scale=_cpu(inp.get("a_scale")),
+                       quantize=cfg.weight == "fp8" and inp["hidden"].dtype != torch.float8_e4m3fn,
+                       block=cfg.fp8_block)
+    ref, _ = oracle.expert_rows(oracle_experts(inp), acts, rows, experts.astype(np.int32))
+    got = out.reshape(-1, cfg.H)[torch.as_tensor(rows, device=dev)].float().cpu().numpy()
+    compare(cfg, got, ref, "slab rows of every tile")
+    return rows

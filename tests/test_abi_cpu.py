@@ -130,6 +130,21 @@ def _status(prob):
     (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U8, act_dtype=B.MOE_F32, out_dtype=B.MOE_F32),
      B.MOE_ERR_UNSUPPORTED),
     (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U8, fp8_block=128), B.MOE_ERR_UNSUPPORTED),
+    # per-call tuning hints: tile family (bf16 any, WNA16 the DMA ones), GEMM1 width
+    (dict(tile_hint=B.MOE_TILE_DMA_160), B.MOE_OK),
+    (dict(tile_hint=B.MOE_TILE_REG_16), B.MOE_OK),
+    (dict(tile_hint=B.MOE_TILE_DMA_32, gemm1_wave_cols=2), B.MOE_OK),
+    (dict(tile_hint=4), B.MOE_ERR_INVALID_ARG),
+    (dict(tile_hint=7), B.MOE_ERR_INVALID_ARG),
+    (dict(tile_hint=-1), B.MOE_ERR_INVALID_ARG),
+    (dict(gemm1_wave_cols=3), B.MOE_ERR_INVALID_ARG),
+    (dict(gemm1_wave_cols=4), B.MOE_OK),
+    (dict(w_dtype=B.MOE_FP8_E4M3FN, tile_hint=B.MOE_TILE_DMA_160), B.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=B.MOE_F32, w_dtype=B.MOE_F32, out_dtype=B.MOE_F32,
+          tile_hint=B.MOE_TILE_REG_16), B.MOE_ERR_UNSUPPORTED),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U4, tile_hint=B.MOE_TILE_DMA_64), B.MOE_OK),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U4, tile_hint=B.MOE_TILE_REG_64),
+     B.MOE_ERR_UNSUPPORTED),
 ])
 def test_problem_validation(kw, status):
     assert _status(_prob(**kw)) == status
@@ -267,3 +282,36 @@ def test_block_fp8_activation_scales_are_sized_per_group():
     assert span(per_row) >= 64 * 4
     assert span(per_blk) >= 64 * 3 * 4 > span(per_row)
     assert per_blk.off_aq_scale == per_row.off_aq_scale
+
+
+def test_library_reads_no_environment():
+    """No environment variable can change the library's choices: libmoe.so
+    imports neither getenv nor secure_getenv."""
+    und = subprocess.run(["nm", "-D", "--undefined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert not re.search(r"\b(secure_)?getenv\b", und), "libmoe.so imports getenv"
+
+
+def test_tile_hint_changes_only_what_it_names():
+    """A tile hint may change the workspace (the chosen family decides the
+    second GEMM's K split) but never the align metadata regions."""
+    kw = dict(M=96, H=256, I=1040, E=4, top_k=2)
+    auto = B.moe_workspace_shapes(_prob(**kw).c())
+    forced = B.moe_workspace_shapes(_prob(tile_hint=B.MOE_TILE_DMA_160, **kw).c())
+    reg = B.moe_workspace_shapes(_prob(tile_hint=B.MOE_TILE_REG_64, **kw).c())
+    for f in ("off_topk_ids", "off_expert_counts", "off_sorted_ids", "off_expert_ids",
+              "off_num_post_padded", "off_status", "off_z", "off_o"):
+        assert getattr(auto, f) == getattr(forced, f) == getattr(reg, f), f
+    assert forced.off_o2 != 0            # the 160-row family splits this GEMM2 in K
+    assert reg.off_o2 == 0 and reg.bytes < forced.bytes
+
+
+def test_status_word_has_its_own_region():
+    for kw in [dict(), dict(fmt=B.MOE_FMT_BATCHED, max_tokens=64, batched_reduce=True),
+               dict(fmt=B.MOE_FMT_BATCHED, max_tokens=64)]:
+        info = B.moe_workspace_shapes(_prob(**kw).c())
+        regions = sorted(getattr(info, f) for f, _ in B.moe_workspace_info._fields_
+                         if f.startswith("off_") and getattr(info, f) != 0)
+        assert info.off_status in regions and info.off_status % 256 == 0
+        # no other region starts at the status word's offset (its 4 bytes are its own)
+        assert regions.count(info.off_status) == 1 or info.off_status == 0

@@ -73,19 +73,15 @@ SMALL_BF16 = [
 ]
 
 
-@pytest.mark.parametrize("tile_cfg", ["auto", "0", "0/wc2", "1", "2"])
+@pytest.mark.parametrize("tile", ["auto", "dma160", "dma160/wc2", "reg64", "reg16"])
 @pytest.mark.parametrize("cfg", SMALL_BF16, ids=[c.name for c in SMALL_BF16])
-def test_packed_equals_plain_small(cfg, tile_cfg, monkeypatch):
+def test_packed_equals_plain_small(cfg, tile):
     dev = GH.device()
-    if tile_cfg == "0/wc2":
-        tile_cfg = "0"
-        monkeypatch.setenv("MOE_GEMM1_WC", "2")
-    if tile_cfg != "auto":
-        monkeypatch.setenv("MOE_TILE_CFG", tile_cfg)
+    hint = GH.tile_kwargs(tile)
     inp = W.make_inputs(cfg, 61)
-    print(f"[case] packed {cfg.name} tile_cfg={tile_cfg}", flush=True)
-    plain, _, _ = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
-    packed, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, packed=True)
+    print(f"[case] packed {cfg.name} tile={tile}", flush=True)
+    plain, _, _ = GH.run_contiguous(inp, dev, out_dtype=torch.float32, **hint)
+    packed, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, packed=True, **hint)
     assert torch.equal(plain, packed)
     ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
     GH.check_output(inp, packed, ids_o, w_o, what="packed")

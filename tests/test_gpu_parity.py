@@ -165,47 +165,47 @@ def test_batched_bf16_matches_contiguous():
     GH.compare(cfg, out.float().cpu().numpy(), y, "batched bf16 reduce")
 
 
-@pytest.mark.parametrize("tile_cfg", ["0", "0/wc2", "1", "2", "4", "5"])
+@pytest.mark.parametrize("tile", ["dma160", "dma160/wc2", "reg64", "reg16", "dma32", "dma64"])
 @pytest.mark.parametrize("skew", [False, True])
-def test_tile_families_ragged(tile_cfg, skew, monkeypatch):
-    """Every bf16 tile family (0: 160-row DMA ring, 1 / 2: 64 / 16-row
-    register-staged, 4 / 5: 32 / 64-row DMA ring) on K and column tails
-    (H % 64 = 16, I % 64 = 48) and, with skew, on experts of 200 rows: several
-    row chunks per expert and a partial last strip.  "0/wc2": the 160-row family with the 4-wave,
-    128-column GEMM1 tile instead of the 8-wave one small problems get."""
+def test_tile_families_ragged(tile, skew):
+    """Every bf16 tile family (160-row DMA ring, 64 / 16-row register-staged,
+    32 / 64-row DMA ring) on K and column tails (H % 64 = 16, I % 64 = 48)
+    and, with skew, on experts of 200 rows: several row chunks per expert
+    and a partial last strip.  "dma160/wc2": the 160-row family with the
+    4-wave, 128-column GEMM1 tile instead of the 8-wave one small problems
+    get."""
     dev = GH.device()
-    if tile_cfg == "0/wc2":
-        tile_cfg = "0"
-        monkeypatch.setenv("MOE_GEMM1_WC", "2")
-    monkeypatch.setenv("MOE_TILE_CFG", tile_cfg)
-    cfg = W.MIXTRAL_PREFILL.scaled(name=f"ragged_t{tile_cfg}", M=200, H=208, I=176, E=4)
+    hint = GH.tile_kwargs(tile)
+    cfg = W.MIXTRAL_PREFILL.scaled(name=f"ragged_{tile}", M=200, H=208, I=176, E=4)
     inp = W.make_inputs(cfg, 51)
-    print(f"[case] ragged tile_cfg={tile_cfg} skew={skew}", flush=True)
+    print(f"[case] ragged tile={tile} skew={skew}", flush=True)
     if skew:
         ids = np.stack([np.full(cfg.M, 1), np.full(cfg.M, 2)], 1).astype(np.int32)
         w = np.random.default_rng(4).random((cfg.M, cfg.top_k)).astype(np.float32)
-        out, ws, info = GH.run_contiguous(inp, dev, precomputed=(ids, w), out_dtype=torch.float32)
+        out, ws, info = GH.run_contiguous(inp, dev, precomputed=(ids, w), out_dtype=torch.float32,
+                                          **hint)
         GH.check_routing_and_align(inp, ws, info, ids_o=ids, w_o=w.astype(np.float64))
         GH.check_output(inp, out, ids, w.astype(np.float64), what="ragged skew")
     else:
-        out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+        out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, **hint)
         ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
         GH.check_output(inp, out, ids_o, w_o, what="ragged")
-    out16, _, _ = GH.run_contiguous(inp, dev, precomputed=(ids, w) if skew else None)
+    out16, _, _ = GH.run_contiguous(inp, dev, precomputed=(ids, w) if skew else None, **hint)
     GH.check_rounded(out16, out)
 
 
 @pytest.mark.parametrize("packed", [False, True])
-def test_gemm2_k_split(packed, monkeypatch):
+def test_gemm2_k_split(packed):
     """The 160-row family on a problem whose GEMM2 runs as two K halves
     (I >= 1024, few tiles): I = 1040 also leaves a K tail in the second half,
     and biases check that b2 enters once."""
     dev = GH.device()
-    monkeypatch.setenv("MOE_TILE_CFG", "0")
     cfg = W.MIXTRAL_PREFILL.scaled(name="k_split", M=96, H=256, I=1040, E=4, bias=True)
     inp = W.make_inputs(cfg, 71)
     print(f"[case] gemm2 k split packed={packed}", flush=True)
-    out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, packed=packed)
+    out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, packed=packed,
+                                      **GH.tile_kwargs("dma160"))
+    assert info.off_o2 != 0, "the second GEMM did not run split in K"
     ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
     GH.check_output(inp, out, ids_o, w_o, what="k split")
 
