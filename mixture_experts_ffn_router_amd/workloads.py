@@ -106,7 +106,11 @@ DEEPSEEK_BLOCKFP8 = DEEPSEEK_GROUPED.scaled(name="deepseek_blockfp8", weight="fp
 DECODE_W4A16 = DECODE_SMALL_EXPERTS.scaled(name="decode_e128_w4a16", weight="u4")
 DECODE_W8A16 = DECODE_SMALL_EXPERTS.scaled(name="decode_e128_w8a16", weight="u8", wq_zero=True)
 
-EXTRA = [EP8_SHARD, DEEPSEEK_BLOCKFP8, DECODE_W4A16, DECODE_W8A16]
+# The Mixtral-shaped layer at M = 4096 tokens (about 1024 rows per expert):
+# the compute-bound bf16 prefill shape (the M = 512 shape streams weights).
+MIXTRAL_M4096 = MIXTRAL_PREFILL.scaled(name="mixtral_prefill_m4096_bf16", M=4096)
+
+EXTRA = [EP8_SHARD, DEEPSEEK_BLOCKFP8, DECODE_W4A16, DECODE_W8A16, MIXTRAL_M4096]
 BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
 
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -173,6 +177,29 @@ def quantize_weight_wna16(w: torch.Tensor, bits: int, zero: bool, G: int = 128):
     return q.contiguous(), s.to(torch.float32), (z.to(torch.uint8) if zero else None)
 
 
+def _draw_hidden_logits(cfg: MoeConfig, gen, device):
+    """The first draws of every workload: hidden, then the router logits
+    (+ per-expert offsets)."""
+    M, H, E = cfg.M, cfg.H, cfg.E
+    hidden = _randn((M, H), gen, device, dtype=_TORCH_DT[cfg.act])
+    logits = _randn((M, E), gen, device)
+    if cfg.expert_bias_var > 0:
+        logits += _randn((E,), gen, device, std=math.sqrt(cfg.expert_bias_var))[None, :]
+    if cfg.zipf_s > 0:
+        perm = torch.randperm(E, generator=gen, device=device)
+        offset = -cfg.zipf_s * torch.log(perm.to(torch.float32) + 1.0)
+        logits += offset[None, :]
+    return hidden, logits.to(_TORCH_DT[cfg.logits_dtype])
+
+
+def make_logits(cfg: MoeConfig, seed: int, device="cpu") -> torch.Tensor:
+    """The router logits make_inputs(cfg, seed, device) draws, without the
+    weights (the same generator stream, so the same values on one device)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return _draw_hidden_logits(cfg, gen, device)[1]
+
+
 def make_inputs(cfg: MoeConfig, seed: int, device="cpu") -> dict:
     """Draws every input of one forward.  Order of draws: hidden, logits
     (+ offsets), w13, w2, w13_bias, w2_bias."""
@@ -182,15 +209,7 @@ def make_inputs(cfg: MoeConfig, seed: int, device="cpu") -> dict:
     act_dt = _TORCH_DT[cfg.act]
     out = {"cfg": cfg, "seed": seed}
 
-    hidden = _randn((M, H), gen, device, dtype=act_dt)
-    logits = _randn((M, E), gen, device)
-    if cfg.expert_bias_var > 0:
-        logits += _randn((E,), gen, device, std=math.sqrt(cfg.expert_bias_var))[None, :]
-    if cfg.zipf_s > 0:
-        perm = torch.randperm(E, generator=gen, device=device)
-        offset = -cfg.zipf_s * torch.log(perm.to(torch.float32) + 1.0)
-        logits += offset[None, :]
-    logits = logits.to(_TORCH_DT[cfg.logits_dtype])
+    hidden, logits = _draw_hidden_logits(cfg, gen, device)
 
     w_dt = torch.float32 if cfg.weight in ("fp8", "u8", "u4") else _TORCH_DT[cfg.weight]
     if cfg.local_experts:                       # the shard's experts only

@@ -1,7 +1,10 @@
 """Parity at the full workload sizes, in the launch configuration the
-benchmark times.  Every routing / align result is compared bit for bit; the
-oracle computes a sample of output rows one by one (first, last and random
-tokens), which keeps each case within a minute."""
+benchmark times.  Every routing / align result is compared bit for bit.
+Outputs are checked tile by tile: for every (expert, row chunk) tile of
+every chunk height the GEMM families use, the expert output of the chunk's
+first and last routed rows (all columns) against the oracle's expert FFN;
+then the final output of a token sample (first, last, and tokens of those
+items) against the oracle's weighted sum."""
 import numpy as np
 import pytest
 import torch
@@ -15,10 +18,19 @@ pytestmark = pytest.mark.gpu
 FULL = [W.TINY_F32, W.MIXTRAL_PREFILL, W.DECODE_SMALL_EXPERTS, W.DEEPSEEK_GROUPED]
 
 
-def _sample_tokens(M, n=16, seed=0):
+def _token_sample(M, item_tokens, n=32, seed=0):
+    """First and last token plus up to n tokens that own sampled tile rows."""
     rng = np.random.default_rng(seed)
-    extra = rng.choice(np.arange(1, max(M - 1, 1)), size=min(n, max(M - 2, 0)), replace=False)
-    return np.unique(np.concatenate([[0, M - 1], extra])).astype(np.int64)
+    pick = rng.choice(item_tokens, size=min(n, item_tokens.size), replace=False)
+    return np.unique(np.concatenate([[0, M - 1], pick])).astype(np.int64)
+
+
+def _margin(inp):
+    """The k_group-boundary near-tie report on the logits this run used."""
+    cfg = inp["cfg"]
+    if cfg.group_count > 1 and cfg.group_select_mode == 1:
+        from test_routing_margin import margin_report
+        margin_report(inp["logits"].cpu(), cfg)
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
@@ -30,11 +42,17 @@ def test_full_size_contiguous(cfg):
     out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
     print(f"[case] {cfg.name} ran; block_m={info.block_m}", flush=True)
     ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    assert GH.B.device_status(ws, info) == 0
+    _margin(inp)
     counts = np.bincount(ids_o.ravel(), minlength=cfg.E)
     print(f"[case] {cfg.name} active experts={int((counts > 0).sum())} "
           f"rows/expert max={counts.max()} min={counts.min()}", flush=True)
-    tokens = None if cfg.M <= 64 else _sample_tokens(cfg.M)
-    GH.check_output(inp, out, ids_o, w_o, tokens=tokens, what="full")
+    if cfg.M <= 64:
+        GH.check_output(inp, out, ids_o, w_o, what="full")
+    else:
+        item_tokens = GH.check_tiles_contiguous(inp, ws, info, dev)
+        GH.check_output(inp, out, ids_o, w_o, tokens=_token_sample(cfg.M, item_tokens),
+                        what="full")
     if cfg.out_dtype == "bf16":
         out16, _, _ = GH.run_contiguous(inp, dev)
         GH.check_rounded(out16, out)
@@ -52,23 +70,22 @@ def test_full_size_batched_fp8(packed):
           f"total={counts.sum()}", flush=True)
     out, ws, info = GH.run_batched(inp, dev, out_dtype=torch.float32, packed=packed)
     GH.check_batched_tilelist(inp, ws, info)
-    rows, experts = GH.batched_rows(inp, sample=48)
-    acts = oracle.Acts(inp["hidden"].cpu(), quantize=True)
-    o_ref, _ = oracle.expert_rows(GH.oracle_experts(inp), acts, rows, experts)
-    got = out.reshape(-1, cfg.H)[torch.as_tensor(rows, device=dev)].cpu().numpy()
-    GH.compare(cfg, got, o_ref, "full batched rows")
+    assert GH.B.device_status(ws, info) == 0
+    rows = GH.check_tiles_batched(inp, ws, info, out, dev)
     out16, _, _ = GH.run_batched(inp, dev, packed=packed)
     idx = torch.as_tensor(rows, device=dev)
     GH.check_rounded(out16.reshape(-1, cfg.H)[idx], out.reshape(-1, cfg.H)[idx])
     # invalid (NaN-filled) rows never leak into valid outputs
-    assert torch.isfinite(out.reshape(-1, cfg.H)[idx]).all()
+    valid = torch.as_tensor(GH.batched_rows(inp)[0], device=dev)
+    assert torch.isfinite(out.reshape(-1, cfg.H)[valid]).all()
 
 
 def test_full_size_ep8_shard():
     """One rank of the DeepSeek-like layer under 8-way expert parallelism
     (32768 tokens routed over 256 experts, 32 held here), in the launch
     configuration the benchmark times: global ids and local align bit for
-    bit, sampled output rows against the oracle's partial sums."""
+    bit, every tile's rows and sampled output rows against the oracle's
+    partial sums."""
     cfg = W.EP8_SHARD
     dev = GH.device()
     seed = 1100 + W.EXTRA.index(cfg)
@@ -86,9 +103,12 @@ def test_full_size_ep8_shard():
     assert npp == npp_o
     assert np.array_equal(GH.region(ws, info.off_expert_counts, torch.int32, E), counts_o)
     assert np.array_equal(GH.region(ws, info.off_sorted_ids, torch.int32, npp), sorted_o)
+    assert GH.B.device_status(ws, info) == 0
+    _margin(inp)
     print(f"[case] {cfg.name} local rows={int(counts_o.sum())} max/expert={counts_o.max()}",
           flush=True)
-    tokens = _sample_tokens(M)
+    item_tokens = GH.check_tiles_contiguous(inp, ws, info, dev, E_local=E)
+    tokens = _token_sample(M, item_tokens)
     acts = oracle.Acts(inp["hidden"].cpu())
     y, _ = oracle.forward_tokens(GH.oracle_experts(inp), acts, ids_o, w_o, tokens=tokens,
                                  expert_map=emap_np)
@@ -106,6 +126,8 @@ def test_full_size_block_fp8():
     out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
     print(f"[case] {cfg.name} ran", flush=True)
     ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
-    GH.check_output(inp, out, ids_o, w_o, tokens=_sample_tokens(cfg.M), what="full block fp8")
+    item_tokens = GH.check_tiles_contiguous(inp, ws, info, dev)
+    GH.check_output(inp, out, ids_o, w_o, tokens=_token_sample(cfg.M, item_tokens),
+                    what="full block fp8")
     out16, _, _ = GH.run_contiguous(inp, dev)
     GH.check_rounded(out16, out)

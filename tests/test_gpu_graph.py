@@ -1,0 +1,119 @@
+"""moe_forward inside a HIP graph.
+
+The boundary allocates nothing, never synchronises the host and enqueues
+all its work on the caller's stream (the split into a sizing call and an
+apply call on the vLLM "Fused MoE Modular Kernel" page, workspace_shapes()
+section), so one forward can be captured once and replayed.  Each case
+captures the forward with torch.cuda.graph, replays it several times with
+unrelated eager work and host synchronisations in between, and requires
+every replay's output and align metadata to equal the eager forward's bit
+for bit (the path is deterministic: no atomics in any value path)."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as GH
+from mixture_experts_ffn_router_amd import binding as B
+from mixture_experts_ffn_router_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("decode_dma32", W.DECODE_SMALL_EXPERTS.scaled(name="g_decode", M=8, H=256, I=128, E=32,
+                                                   top_k=4)),
+    ("prefill_dma160_ksplit", W.MIXTRAL_PREFILL.scaled(name="g_prefill", M=96, H=256, I=1040,
+                                                       E=4, bias=True)),
+    ("grouped_multiblock_align", W.DEEPSEEK_GROUPED.scaled(name="g_grouped", M=2304, H=128,
+                                                           I=128, E=64)),
+    ("fp8_contiguous", W.MIXTRAL_PREFILL.scaled(name="g_fp8", M=200, H=256, I=256,
+                                                weight="fp8")),
+    ("batched_fp8_reduce", W.BATCHED_FP8.scaled(name="g_batched", M=96, H=256, I=256, E=8)),
+]
+
+
+def _problem_and_args(inp, dev):
+    """(problem, args, out, keep-alive tensors) of one forward, marshalled
+    once so the captured launch and the eager one see the same pointers."""
+    cfg = inp["cfg"]
+    keep = []
+
+    def d(t):
+        if t is None:
+            return None
+        t = t.to(dev).contiguous()
+        keep.append(t)
+        return t
+
+    w13, w2 = d(inp["w13"]), d(inp["w2"])
+    out_dt = torch.float32
+    if cfg.fmt == "batched":
+        hidden = d(inp["hidden"])
+        tmap, tmw = d(inp["token_map"]), d(inp["token_map_w"])
+        prob = B.Problem(M=cfg.M, H=cfg.H, I=cfg.I, E=cfg.E, top_k=cfg.top_k,
+                         fmt=B.MOE_FMT_BATCHED, max_tokens=inp["max_tokens"],
+                         act_dtype=B._dtype_code(hidden), w_dtype=B._dtype_code(w13),
+                         out_dtype=B.MOE_F32, routing=B.MOE_ROUTE_PRECOMPUTED,
+                         batched_reduce=True)
+        out = torch.empty(cfg.M, cfg.H, dtype=out_dt, device=dev)
+        args = B.make_args(hidden, w13, w2, out, expert_num_tokens=d(inp["expert_num_tokens"]),
+                           token_map=tmap, token_map_w=tmw, w13_scale=d(inp.get("w13_scale")),
+                           w2_scale=d(inp.get("w2_scale")))
+    else:
+        hidden = d(inp["hidden"])
+        logits = d(inp["logits"])
+        prob = B.Problem(M=cfg.M, H=cfg.H, I=cfg.I, E=cfg.E, top_k=cfg.top_k,
+                         act_dtype=B._dtype_code(hidden), w_dtype=B._dtype_code(w13),
+                         out_dtype=B._dtype_code(torch.empty(0, dtype=out_dt)),
+                         logits_dtype=B._dtype_code(logits),
+                         routing=B.MOE_ROUTE_SIGMOID if cfg.scoring == "sigmoid"
+                         else B.MOE_ROUTE_SOFTMAX, renormalize=cfg.renormalize,
+                         group_count=cfg.group_count, k_group=cfg.k_group,
+                         group_select_mode=cfg.group_select_mode,
+                         routed_scaling_factor=cfg.routed_scaling_factor,
+                         has_w13_bias=inp["w13_bias"] is not None,
+                         has_w2_bias=inp["w2_bias"] is not None)
+        out = torch.empty(cfg.M, cfg.H, dtype=out_dt, device=dev)
+        args = B.make_args(hidden, w13, w2, out, router_logits=logits,
+                           w13_bias=d(inp["w13_bias"]), w2_bias=d(inp["w2_bias"]),
+                           w13_scale=d(inp.get("w13_scale")), w2_scale=d(inp.get("w2_scale")))
+    return prob, args, out, keep
+
+
+@pytest.mark.parametrize("name,cfg", CASES, ids=[c[0] for c in CASES])
+def test_forward_replays_from_a_graph(name, cfg):
+    dev = GH.device()
+    inp = W.make_inputs(cfg, 401)
+    prob, args, out, keep = _problem_and_args(inp, dev)
+    ws, info = B.allocate_workspace(prob, dev)
+    cprob = prob.c()
+    print(f"[case] graph {name}", flush=True)
+
+    # eager forward (also initialises the library's per-device state)
+    B.moe_forward(cprob, args, ws.data_ptr(), ws.numel(), B.current_stream_handle(dev))
+    torch.cuda.synchronize()
+    ref = out.clone()
+    npp = int(GH.region(ws, info.off_num_post_padded, torch.int32, 1)[0])
+    ref_sorted = GH.region(ws, info.off_sorted_ids, torch.int32, npp).copy()
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            B.moe_forward(cprob, args, ws.data_ptr(), ws.numel(), s.cuda_stream)
+    torch.cuda.current_stream(dev).wait_stream(s)
+    torch.cuda.synchronize()
+
+    junk = torch.randn(512, 512, device=dev)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        ws[info.off_sorted_ids:info.off_sorted_ids + 4 * npp].fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        junk = junk @ junk.t() / 512.0              # unrelated eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {rep} differs from the eager forward"
+        got = GH.region(ws, info.off_sorted_ids, torch.int32, npp)
+        assert np.array_equal(got, ref_sorted), f"replay {rep}: sorted ids differ"
+        assert B.device_status(ws, info) == 0
+    del g, keep

@@ -198,6 +198,68 @@ def test_route_rejects_pages_constraints():
 
 # ----------------------------------------------------------------- align
 
+# ----------------------------------------------------------------- group keys
+
+def _group_logits(M, E, seed, tied=False):
+    g = torch.Generator().manual_seed(seed)
+    lg = torch.randn(M, E, generator=g)
+    if tied:                                   # integer logits: many exact ties
+        lg = torch.round(lg * 2)
+    return lg.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("tied", [False, True])
+def test_group_keys_mode0_is_the_group_max_logit(tied):
+    lg = _group_logits(300, 64, 11, tied)
+    keys = oracle.group_keys(lg, 8, 0)
+    ref = lg.float().view(300, 8, 8).amax(dim=2).numpy()
+    assert np.array_equal(keys, ref)
+
+
+@pytest.mark.parametrize("G", [4, 8, 16])
+def test_group_keys_sigmoid_top2_sum_matches_torch_float64(G):
+    """Mode 1 with sigmoid scores: the sum of each group's two largest
+    scores (torch sigmoid and topk in float64), to the float32 rounding of
+    the two scores and their sum."""
+    M, E = 400, 128
+    lg = _group_logits(M, E, 12)
+    keys = oracle.group_keys(lg, G, 1, scoring="sigmoid").astype(np.float64)
+    p = torch.sigmoid(lg.double()).view(M, G, E // G)
+    ref = p.topk(2, dim=2).values.sum(dim=2).numpy()
+    assert np.abs(keys - ref).max() <= 3e-7 * np.abs(ref).max()
+    assert np.all(np.abs(keys - ref) <= 3e-7 * ref)
+
+
+@pytest.mark.parametrize("G", [4, 8])
+def test_group_keys_softmax_top2_sum_matches_torch_float64(G):
+    """Mode 1 with softmax scores.  The key is the top-2 sum of exp(s - max)
+    (the softmax numerators: dividing by the token's common denominator
+    orders groups the same way), so key / sum_e exp(s_e - max) must equal
+    the top-2 sum of torch.softmax in float64."""
+    M, E = 400, 64
+    lg = _group_logits(M, E, 13)
+    keys = oracle.group_keys(lg, G, 1, scoring="softmax").astype(np.float64)
+    x = lg.double()
+    denom = torch.exp(x - x.amax(dim=1, keepdim=True)).sum(dim=1).numpy()
+    ref = torch.softmax(x, dim=1).view(M, G, E // G).topk(2, dim=2).values.sum(dim=2).numpy()
+    rel = np.abs(keys / denom[:, None] - ref) / ref
+    assert rel.max() <= 3e-7, rel.max()
+
+
+def test_group_keys_rank_groups_as_route_selects_them():
+    """The k_group groups with the largest keys (ties to the lower index)
+    contain every expert route() selects, on random and on tied logits."""
+    for tied in (False, True):
+        lg = _group_logits(500, 64, 14, tied)
+        for scoring in ("sigmoid", "softmax"):
+            keys = oracle.group_keys(lg, 8, 1, scoring=scoring)
+            ids, _ = oracle.route(lg, 6, scoring=scoring, group_count=8, k_group=3,
+                                  group_select_mode=1)
+            order = np.argsort(-keys, axis=1, kind="stable")[:, :3]
+            for t in range(lg.shape[0]):
+                assert set((ids[t] // 8).tolist()) <= set(order[t].tolist()), (t, scoring, tied)
+
+
 @pytest.mark.parametrize("Mk,E,BM", [(1, 1, 16), (37, 5, 16), (1024, 8, 64), (4096, 64, 32),
                                      (3000, 256, 16), (200, 8, 1)])
 def test_align_against_stable_argsort(Mk, E, BM):
