@@ -4,15 +4,21 @@
 One step = one moe_forward over the whole batch: router -> align ->
 [fp8 quant] -> grouped GEMM W13 + SiLU*up -> grouped GEMM W2 -> top-k
 weight-and-reduce, on seeded synthetic inputs already resident in HBM.
-Prints one JSON line.  Default workload: the Mixtral-shaped prefill
-(M 512, H 4096, I 14336, E 8, top-2, bf16).
+Prints one JSON line.  Default workload: the DeepSeek-V3-like layer with
+grouped sigmoid routing (M 4096, H 7168, I 2048, E 256, top-8, bf16), the
+largest configuration that fits one GPU.
 
-The `roofline` object covers the dominant kernel (the W13 GEMM): its
-algorithmic bytes per launch (active experts' w13 + activation rows read
-once + z written once) over its average duration, timed with HIP events
-recorded on the launch stream around that kernel in every timed step.
+The `roofline` object covers the dominant kernel (the W13 GEMM).  Its
+algorithmic bytes per launch are the weights of the experts that received
+rows (+ their biases and scales) plus the activation rows read once; its
+output z is an intermediate of this implementation, reported separately as
+`materialised_bytes`.  `achieved` divides the bytes (or, where the kernel is
+MFMA-bound, 2 x rows x H x 2I FLOPs) by the kernel's average duration, timed
+with HIP events recorded on the launch stream around that kernel in every
+timed step; `profile_avg_ms` is the same kernel's average from the committed
+rocprofv3 summary when it was taken on the current GEMM sources.
 `cpu_baseline` times the CPU oracle (test infrastructure, untuned) on a
-bounded token sample of the same workload on this host.
+bounded token sample of the same workload on all of this host's cores.
 """
 import argparse
 import dataclasses
@@ -35,7 +41,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_prefill_bf16")
+    ap.add_argument("--workload", default="deepseek_grouped_sigmoid_bf16")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="tokens (or batched rows) the CPU oracle leg computes")
@@ -269,25 +275,48 @@ def main():
     t_mfma = flops / (MFMA_PEAK_TFLOPS[dt_key] * 1e12)
     t_step = float(np.median(step_ms)) * 1e-3
 
-    # dominant kernel: W13 GEMM
-    g1_bytes = w13_b + (scale_b // 2 if scale_b else 0) + x_b + z_b
+    # dominant kernel: W13 GEMM.  Algorithmic bytes: active experts' w13
+    # (+ its scales / zero points and bias) and the activation rows it reads
+    # once (fp8: the quantised codes and their scales); z is materialised.
+    if cfg.weight == "fp8":
+        a_scales = (-(-cfg.H // 128) if cfg.fp8_block else 1) * 4
+        x_g1 = x_rows * (cfg.H + a_scales)
+    else:
+        x_g1 = x_b
+    w13_extra = 0
+    if wq_bits:
+        w13_extra = active * -(-cfg.H // 128) * 2 * cfg.I * (4 + (1 if cfg.wq_zero else 0))
+    elif cfg.weight == "fp8":
+        w13_extra = active * ((2 * cfg.I // 128) * -(-cfg.H // 128) if cfg.fp8_block
+                              else 2 * cfg.I) * 4
+    if cfg.bias:
+        w13_extra += active * 2 * cfg.I * aes
+    g1_bytes = w13_b + w13_extra + x_g1
+    z_scales = valid_rows * (cfg.I // 128) * 4 if cfg.weight == "fp8" else 0
+    materialised = z_b + z_scales
     g1_ms = stage_ms.get("gemm1", float("nan"))
     g1_flops = 2.0 * valid_rows * cfg.H * 2 * cfg.I
-    g1_gbs = g1_bytes / (g1_ms * 1e-3) / 1e9
     g1_bound = "hbm" if g1_flops / g1_bytes < (MFMA_PEAK_TFLOPS[dt_key] * 1e12) / (
         HBM_PEAK_GBS * 1e9) else "mfma"
-    if g1_bound == "hbm":
-        roof = {"bound": "hbm", "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(g1_gbs / HBM_PEAK_GBS, 4)}
-    else:
-        tf = g1_flops / (g1_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_PEAK_TFLOPS[dt_key],
-                "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS[dt_key], 4)}
-    traffic, kname, tsrc = profile_traffic(cfg.name)
-    roof.update({"kernel": kname or "GEMM1 (grouped W13 GEMM + SiLU*up)",
-                 "algorithmic_bytes_per_launch": int(g1_bytes),
-                 "avg_launch_ms": round(g1_ms, 4), "traffic": traffic,
-                 "traffic_source": tsrc})
+    traffic, kname, tsrc, prof_ms = profile_traffic(cfg.name)
+
+    def achieved(ms):
+        if g1_bound == "hbm":
+            return g1_bytes / (ms * 1e-3) / 1e9
+        return g1_flops / (ms * 1e-3) / 1e12
+    a = achieved(g1_ms)
+    peak = HBM_PEAK_GBS if g1_bound == "hbm" else MFMA_PEAK_TFLOPS[dt_key]
+    roof = {"bound": g1_bound, "achieved": round(a, 1), "peak": peak,
+            "unit": "GB/s" if g1_bound == "hbm" else "TFLOP/s", "frac": round(a / peak, 4),
+            "traffic": traffic,
+            "kernel": kname or "GEMM1 (grouped W13 GEMM + SiLU*up)",
+            "algorithmic_bytes_per_launch": int(g1_bytes),
+            "algorithmic_flops_per_launch": g1_flops,
+            "materialised_bytes": int(materialised),
+            "avg_launch_ms": round(g1_ms, 4),
+            "profile_avg_ms": None if prof_ms is None else round(prof_ms, 4),
+            "frac_at_profile_ms": None if prof_ms is None else round(achieved(prof_ms) / peak, 4),
+            "traffic_source": tsrc}
 
     tokens = cfg.M
     value = tokens / (ms_per_step * 1e-3)
@@ -343,8 +372,9 @@ def gemm_source_sha():
 
 def profile_traffic(workload):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size),
-    or (None, None, None) when no summary was taken on the current GEMM source."""
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size)
+    and that kernel's average duration there, or Nones when no summary was
+    taken on the current GEMM source."""
     import glob
     import re
     sha = gemm_source_sha()
@@ -354,16 +384,38 @@ def profile_traffic(workload):
         h = re.search(r"^source_sha256: ([0-9a-f]{64})", text, re.M)
         t = re.search(r"^traffic_bytes_per_launch: (\d+)", text, re.M)
         k = re.search(r"^dominant_kernel: (.+)$", text, re.M)
+        d = re.search(r"^avg_duration_us: ([0-9.]+)", text, re.M)
         if h and t and k and h.group(1) == sha:
-            return int(t.group(1)), k.group(1).strip(), os.path.relpath(path, ROOT)
-    return None, None, None
+            return (int(t.group(1)), k.group(1).strip(), os.path.relpath(path, ROOT),
+                    float(d.group(1)) * 1e-3 if d else None)
+    return None, None, None, None
+
+
+def host_cpu():
+    """(model name, logical CPUs this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return model, n
 
 
 def cpu_baseline(cfg, inp, info, sample):
     import numpy as np
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
-    print(f"[bench] cpu oracle leg on {threads} threads", file=sys.stderr, flush=True)
+    model, ncpu = host_cpu()
+    threads = ncpu                        # every core this process may use
+    print(f"[bench] cpu oracle leg on {threads} threads ({model})", file=sys.stderr, flush=True)
+    host = {"cpu_model": model, "logical_cpus": ncpu}
     ex = oracle.Experts(inp["w13"].cpu(), inp["w2"].cpu(),
                         None if inp.get("w13_scale") is None else inp["w13_scale"].cpu(),
                         None if inp.get("w2_scale") is None else inp["w2_scale"].cpu(),
@@ -386,10 +438,10 @@ def cpu_baseline(cfg, inp, info, sample):
         dt = time.perf_counter() - t0
         # tokens/s equivalent: each token is top_k routed rows
         return {"value": round(n / cfg.top_k / dt, 2), "unit": "tokens/s", "cores": used,
-                "kind": "oracle",
+                "kind": "oracle", **host,
                 "sample": f"{n} of {int(counts.sum())} valid batched rows (every "
                           f"{max(1, rows.size // n)}th), {dt:.1f}s; tokens = rows / top_k"}
-    n = min(sample or 512, cfg.M)
+    n = min(sample or 1024, cfg.M)
     logits = inp["logits"].cpu()
     t0 = time.perf_counter()
     ids, w = oracle.route(logits, cfg.top_k, scoring=cfg.scoring, renormalize=cfg.renormalize,
@@ -403,6 +455,7 @@ def cpu_baseline(cfg, inp, info, sample):
                                     expert_map=emap)
     dt = time.perf_counter() - t0
     return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            **host,
             "sample": f"routing + align of all {cfg.M} tokens, expert FFN of the first {n} "
                       f"tokens, {dt:.1f}s"}
 
