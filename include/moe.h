@@ -54,7 +54,9 @@ typedef enum {
     MOE_ERR_INVALID_ARG = -1, /* shape / range / null-pointer violation            */
     MOE_ERR_UNSUPPORTED = -2, /* valid request this build does not implement        */
     MOE_ERR_WORKSPACE = -3,   /* workspace null, misaligned (256 B) or too small    */
-    MOE_ERR_LAUNCH = -4       /* a kernel launch failed (hipGetLastError)           */
+    MOE_ERR_LAUNCH = -4,      /* a kernel launch failed (hipGetLastError)           */
+    MOE_ERR_STATIC_LIMIT = -5 /* moe_forward_static: the problem's workspace exceeds
+                                 MOE_STATIC_WORKSPACE_BYTES                        */
 } moe_status;
 
 typedef enum {
@@ -420,6 +422,28 @@ int moe_forward_timed(const moe_problem* p, const moe_args* a, void* workspace,
 int moe_packed_weight_bytes(const moe_problem* p, size_t* w13_bytes, size_t* w2_bytes);
 int moe_pack_weights(const moe_problem* p, const void* w13, const void* w2, void* w13_packed,
                      void* w2_packed, void* stream);
+
+/* Allocation-free forward, for callers that cannot allocate device memory
+ * or hand over a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  The same path and results as
+ * moe_forward, with the workspace in a device array that the library holds
+ * on every GPU it runs on (MOE_STATIC_WORKSPACE_BYTES each, until the process
+ * ends).  The caller passes inputs and outputs only; the call allocates and
+ * frees nothing.  Its first call on a device looks up that device's copy of
+ * the array (a symbol query with the stream's device made current, then
+ * restored); later calls only launch kernels.
+ *   - Problems whose workspace (moe_workspace_shapes) exceeds
+ *     MOE_STATIC_WORKSPACE_BYTES return MOE_ERR_STATIC_LIMIT with nothing
+ *     enqueued; chunk_tokens bounds the workspace of a long batch.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; no region needs to start at zero (each kernel writes
+ *     what a later kernel of the same call reads).  Calls that overlap on
+ *     one GPU (different streams, or different host threads) race on the
+ *     array: serialise them.  The intermediates are not handed out.
+ *   - Other errors as moe_forward; MOE_ERR_LAUNCH also when the array's
+ *     device address cannot be obtained. */
+#define MOE_STATIC_WORKSPACE_BYTES ((size_t)128 << 20)
+int moe_forward_static(const moe_problem* p, const moe_args* a, void* stream);
 
 /* Static English description of a status code. */
 const char* moe_status_string(int status);

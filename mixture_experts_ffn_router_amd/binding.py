@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 # enums of moe.h
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 0, -1, -2, -3, -4
+MOE_ERR_STATIC_LIMIT = -5
+MOE_STATIC_WORKSPACE_BYTES = 128 << 20
 MOE_F32, MOE_BF16, MOE_FP8_E4M3FN, MOE_U8, MOE_U4 = 0, 1, 2, 3, 4
 MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID, MOE_ROUTE_PRECOMPUTED = 0, 1, 2
 MOE_FMT_CONTIGUOUS, MOE_FMT_BATCHED = 0, 1
@@ -26,7 +28,7 @@ MOE_TILE_DMA_32, MOE_TILE_DMA_64 = 5, 6
 MOE_DEV_ID_RANGE, MOE_DEV_COUNT_CLAMPED, MOE_DEV_ROWS_OVERFLOW, MOE_DEV_TOKEN_MAP = 1, 2, 4, 8
 
 EXPORTED = ("moe_workspace_shapes", "moe_forward", "moe_forward_timed", "moe_packed_weight_bytes",
-            "moe_pack_weights", "moe_status_string", "moe_version")
+            "moe_pack_weights", "moe_forward_static", "moe_status_string", "moe_version")
 STAGES = ("router", "align", "quant", "gemm1", "gemm2", "reduce")
 
 
@@ -99,6 +101,9 @@ def load() -> ctypes.CDLL:
         lib.moe_packed_weight_bytes.restype = ctypes.c_int
         lib.moe_pack_weights.argtypes = [ctypes.POINTER(moe_problem)] + [ctypes.c_void_p] * 5
         lib.moe_pack_weights.restype = ctypes.c_int
+        lib.moe_forward_static.argtypes = [ctypes.POINTER(moe_problem), ctypes.POINTER(moe_args),
+                                           ctypes.c_void_p]
+        lib.moe_forward_static.restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         lib.moe_version.argtypes = []
@@ -129,6 +134,14 @@ def moe_forward(problem: moe_problem, args: moe_args, workspace: int, workspace_
                             workspace_bytes, ctypes.c_void_p(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_forward")
+
+
+def moe_forward_static(problem: moe_problem, args: moe_args, stream: int) -> None:
+    """The allocation-free forward (workspace in the library's static array)."""
+    rc = load().moe_forward_static(ctypes.byref(problem), ctypes.byref(args),
+                                   ctypes.c_void_p(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_forward_static")
 
 
 def moe_packed_weight_bytes(problem: moe_problem):
@@ -315,7 +328,7 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
               w2_bias=None, topk_ids=None, topk_weights=None, w13_scale=None, w2_scale=None,
               out_dtype=None, out=None, workspace=None, expert_map=None,
               apply_weight_on_input=False, chunk_tokens=0, fp8_block=0, w13_zero=None,
-              w2_zero=None, tile_hint=MOE_TILE_AUTO, gemm1_wave_cols=0):
+              w2_zero=None, tile_hint=MOE_TILE_AUTO, gemm1_wave_cols=0, static=False):
     """Contiguous-format forward on torch device tensors (the MindIE-SD
     page's fused_moe argument list, single device).  w13 may be a
     PackedWeights (then w2 is ignored).  expert_map [global experts] int32
@@ -326,8 +339,10 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
     group scales w13_scale [E, ceil(H/128), 2I] / w2_scale [E, ceil(I/128), H]
     and optional uint8 zero points of the same shapes.  tile_hint /
     gemm1_wave_cols force a GEMM tile family / GEMM1 width (moe_problem's
-    tuning fields; 0 = the library's choice).  Returns (out, workspace
-    tensor, workspace info)."""
+    tuning fields; 0 = the library's choice).  static=True runs the
+    allocation-free entry point (moe_forward_static: the library's own
+    device array as workspace; workspace and info are then None).  Returns
+    (out, workspace tensor, workspace info)."""
     import torch
     M = hidden.shape[0]
     w13, w2, E, H, I, wdt, layout = _weights(w13, w2)
@@ -351,14 +366,17 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
                    fp8_block=fp8_block, tile_hint=tile_hint, gemm1_wave_cols=gemm1_wave_cols)
     if out is None:
         out = torch.empty(M, H, dtype=odt, device=hidden.device)
-    if workspace is None:
-        workspace, info = allocate_workspace(prob, hidden.device)
-    else:
-        info = moe_workspace_shapes(prob.c())
     args = make_args(hidden, w13, w2, out, router_logits=router_logits, topk_ids=topk_ids,
                      topk_weights=topk_weights, w13_bias=w13_bias, w2_bias=w2_bias,
                      w13_scale=w13_scale, w2_scale=w2_scale, expert_map=expert_map,
                      w13_zero=w13_zero, w2_zero=w2_zero)
+    if static:
+        moe_forward_static(prob.c(), args, current_stream_handle(hidden.device))
+        return out, None, None
+    if workspace is None:
+        workspace, info = allocate_workspace(prob, hidden.device)
+    else:
+        info = moe_workspace_shapes(prob.c())
     moe_forward(prob.c(), args, workspace.data_ptr(), workspace.numel(),
                 current_stream_handle(hidden.device))
     return out, workspace, info
@@ -368,7 +386,7 @@ def fused_moe_batched(hidden, expert_num_tokens, w13, w2, *, M: int = 0, top_k: 
                       a_scale=None, w13_scale=None, w2_scale=None, w13_bias=None, w2_bias=None,
                       token_map=None, token_map_w=None, out_dtype=None, out=None,
                       workspace=None, fp8_block=0, w13_zero=None, w2_zero=None,
-                      tile_hint=MOE_TILE_AUTO):
+                      tile_hint=MOE_TILE_AUTO, static=False):
     """Batched-format forward: hidden [E, max_tokens, H] + expert_num_tokens [E].
     M, top_k (when M > 0) promise that the slabs hold at most M * top_k valid
     rows, which bounds the workspace (slabs that break the promise are not
@@ -392,14 +410,17 @@ def fused_moe_batched(hidden, expert_num_tokens, w13, w2, *, M: int = 0, top_k: 
     if out is None:
         shape = (M, H) if reduce else (E, T, H)
         out = torch.empty(shape, dtype=odt, device=hidden.device)
-    if workspace is None:
-        workspace, info = allocate_workspace(prob, hidden.device)
-    else:
-        info = moe_workspace_shapes(prob.c())
     args = make_args(hidden, w13, w2, out, a_scale=a_scale, expert_num_tokens=expert_num_tokens,
                      token_map=token_map, token_map_w=token_map_w, w13_bias=w13_bias,
                      w2_bias=w2_bias, w13_scale=w13_scale, w2_scale=w2_scale,
                      w13_zero=w13_zero, w2_zero=w2_zero)
+    if static:
+        moe_forward_static(prob.c(), args, current_stream_handle(hidden.device))
+        return out, None, None
+    if workspace is None:
+        workspace, info = allocate_workspace(prob, hidden.device)
+    else:
+        info = moe_workspace_shapes(prob.c())
     moe_forward(prob.c(), args, workspace.data_ptr(), workspace.numel(),
                 current_stream_handle(hidden.device))
     return out, workspace, info

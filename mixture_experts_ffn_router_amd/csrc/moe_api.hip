@@ -6,7 +6,9 @@
 // validation"); the workspace_shapes / apply split follows the vLLM
 // "Fused MoE Modular Kernel" page.  All checks run on the host before
 // anything is enqueued.
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -479,6 +481,65 @@ extern "C" int moe_forward_timed(const moe_problem* p, const moe_args* a, void* 
     return forward(p, a, workspace, workspace_bytes, stream, events);
 }
 
+// ---------------------------------------------------------------- allocation-free forward
+// The workspace of moe_forward_static: one array per device, loaded with the
+// library's code object.  Host code never uses its name as an address (on
+// the host it is only a handle); the device address comes from a symbol
+// query, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_WORKSPACE_BYTES];
+
+static std::atomic<void*> g_scratch[MAX_DEVICES];
+static std::mutex g_scratch_mu;
+
+// Device address of `scratch` on device dev (queried on first use).
+static int scratch_address(int dev, void** out)
+{
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return MOE_ERR_UNSUPPORTED;
+    void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!ptr) {
+            int prev = -1;
+            if (hipGetDevice(&prev) != hipSuccess || (prev != dev && hipSetDevice(dev) != hipSuccess)) {
+                (void)hipGetLastError();
+                return MOE_ERR_LAUNCH;
+            }
+            const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (prev != dev)
+                (void)hipSetDevice(prev);
+            if (e != hipSuccess || !ptr || (uintptr_t)ptr % ALIGN) {
+                (void)hipGetLastError();
+                return MOE_ERR_LAUNCH;
+            }
+            g_scratch[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return MOE_OK;
+}
+
+extern "C" int moe_forward_static(const moe_problem* p, const moe_args* a, void* stream)
+{
+    const hipStream_t s = (hipStream_t)stream;
+    const int dev = stream_device(s);
+    moe_workspace_info w;
+    int rc = layout(p, device_cus(dev), &w);
+    if (rc != MOE_OK)
+        return rc;
+    rc = check_args(p, a);
+    if (rc != MOE_OK)
+        return rc;
+    if (w.bytes > MOE_STATIC_WORKSPACE_BYTES)
+        return MOE_ERR_STATIC_LIMIT;
+    void* ws = nullptr;
+    rc = scratch_address(dev, &ws);
+    if (rc != MOE_OK)
+        return rc;
+    return forward(p, a, ws, MOE_STATIC_WORKSPACE_BYTES, stream, nullptr);
+}
+
 // Packed weight sizes: 16 KiB blocks.  bf16: 64 weight rows x 128 weight
 // columns (w13: 64 gate + 64 up columns per block); fp8: 128 weight columns x
 // 128 K values (w13: 64 gate + 64 up columns).
@@ -551,6 +612,7 @@ extern "C" const char* moe_status_string(int status)
     case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
     case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_STATIC_LIMIT: return "problem needs more workspace than the static array holds";
     default: return "unknown status";
     }
 }

@@ -158,9 +158,9 @@ def check_output(inp: dict, out: torch.Tensor, ids_o, w_o, tokens=None, what="")
     return compare(cfg, got, y, what)
 
 
-def run_batched(inp: dict, dev, reduce=False, out_dtype=None, packed=False):
+def run_batched(inp: dict, dev, reduce=False, out_dtype=None, packed=False, **extra):
     cfg = inp["cfg"]
-    kw = {"out_dtype": out_dtype}
+    kw = {"out_dtype": out_dtype, **extra}
     w13, w2 = inp["w13"].to(dev), inp["w2"].to(dev)
     if cfg.fp8_block:
         packed = True

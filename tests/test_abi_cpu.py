@@ -315,3 +315,23 @@ def test_status_word_has_its_own_region():
         assert info.off_status in regions and info.off_status % 256 == 0
         # no other region starts at the status word's offset (its 4 bytes are its own)
         assert regions.count(info.off_status) == 1 or info.off_status == 0
+
+
+def test_static_entry_refuses_problems_beyond_its_array():
+    """moe_forward_static sizes the problem on the host and refuses one whose
+    workspace exceeds MOE_STATIC_WORKSPACE_BYTES before any device work
+    (fake pointers are never touched); chunk_tokens brings it back in."""
+    big = _prob(M=20000, H=1024, I=1024, top_k=2, routing=B.MOE_ROUTE_PRECOMPUTED)
+    assert B.moe_workspace_shapes(big.c()).bytes > B.MOE_STATIC_WORKSPACE_BYTES
+    args = _args(topk_ids=4096, topk_weights=4096)
+    lib = B.load()
+    assert lib.moe_forward_static(ctypes.byref(big.c()), ctypes.byref(args), None) == \
+        B.MOE_ERR_STATIC_LIMIT
+    assert "static" in B.moe_status_string(B.MOE_ERR_STATIC_LIMIT)
+    big.chunk_tokens = 4096
+    assert B.moe_workspace_shapes(big.c()).bytes <= B.MOE_STATIC_WORKSPACE_BYTES
+    # argument errors come first, as in moe_forward
+    assert lib.moe_forward_static(ctypes.byref(_prob(top_k=0).c()), ctypes.byref(args), None) \
+        == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_static(ctypes.byref(_prob().c()), ctypes.byref(_args(hidden=None)),
+                                  None) == B.MOE_ERR_INVALID_ARG
