@@ -192,6 +192,44 @@ def _draw_hidden_logits(cfg: MoeConfig, gen, device):
     return hidden, logits.to(_TORCH_DT[cfg.logits_dtype])
 
 
+AWQ_ORDER = (0, 2, 4, 6, 1, 3, 5, 7)      # AWQ word slot i holds column 8 c + AWQ_ORDER[i]
+
+
+def pack_wq_checkpoint(codes: torch.Tensor, zeros, bits: int, fmt: str):
+    """Packs one code per byte [E, K, N] (and zero points [E, ng, N], or
+    None) into a checkpoint's int32 words, as the quantiser that wrote the
+    checkpoint did: "gptq" packs 32 / bits rows of a column into a word
+    ([E, K * bits / 32, N]) and zero points along N ([E, ng, N * bits / 32]);
+    "awq" (4-bit) packs 8 columns of a row into a word in the order
+    AWQ_ORDER ([E, K, N / 8]), zero points alike.  Slot i of a word is bits
+    [bits * i, bits * (i + 1))."""
+    per = 32 // bits
+    c = codes.to(torch.int64)
+
+    def along_last(t, order):
+        t = t.reshape(*t.shape[:-1], t.shape[-1] // per, per)
+        w = torch.zeros(t.shape[:-1], dtype=torch.int64)
+        for i, col in enumerate(order):
+            w |= t[..., col] << (bits * i)
+        return w
+
+    if fmt == "gptq":
+        E, K, N = c.shape
+        t = c.reshape(E, K // per, per, N)
+        w = torch.zeros(E, K // per, N, dtype=torch.int64)
+        for i in range(per):
+            w |= t[:, :, i, :] << (bits * i)
+        zw = None if zeros is None else along_last(zeros.to(torch.int64), range(per))
+    elif fmt == "awq":
+        assert bits == 4
+        w = along_last(c, AWQ_ORDER)
+        zw = None if zeros is None else along_last(zeros.to(torch.int64), AWQ_ORDER)
+    else:
+        raise ValueError(fmt)
+    to32 = lambda t: None if t is None else ((t + 2 ** 31) % 2 ** 32 - 2 ** 31).to(torch.int32)
+    return to32(w), to32(zw)
+
+
 def make_logits(cfg: MoeConfig, seed: int, device="cpu") -> torch.Tensor:
     """The router logits make_inputs(cfg, seed, device) draws, without the
     weights (the same generator stream, so the same values on one device)."""

@@ -91,6 +91,8 @@ def load() -> ctypes.CDLL:
     lib.oracle_expert_rows.argtypes = [ctypes.POINTER(_Experts), ctypes.POINTER(_Acts), P, P,
                                        i64, P, i32]
     lib.oracle_expert_rows.restype = ctypes.c_int
+    lib.oracle_unpack_wq.argtypes = [i32, i32, i64, i64, i64, i64, P, P, i32, P, P]
+    lib.oracle_unpack_wq.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -223,6 +225,37 @@ def align(topk_ids, E, block_m, expert_map=None):
         raise ValueError("oracle_align: id out of range")
     n = int(npp[0])
     return counts, sorted_ids[:n].copy(), expert_ids[: n // block_m].copy(), n
+
+
+# ---------------------------------------------------------------- GPTQ / AWQ codes
+
+GPTQ, AWQ = 1, 2
+
+
+def unpack_wq(fmt: str, bits: int, qweight, qzeros=None, K=None, N=None, group=128,
+              zero_adjust=0):
+    """GPTQ- or AWQ-packed int32 codes of E experts -> the oracle's plain
+    WNA16 codes ([E, K, N] bytes for 8 bits, [E, K, N/2] two a byte for 4)
+    and zero points [E, ceil(K/group), N] (or None).  fmt: "gptq" | "awq"."""
+    lib = load()
+    qw = _np(qweight).astype(np.int32, copy=False)
+    qw = np.ascontiguousarray(qw)
+    E = qw.shape[0]
+    per = 32 // bits
+    code = {"gptq": GPTQ, "awq": AWQ}[fmt]
+    if K is None:
+        K = qw.shape[1] * per if code == GPTQ else qw.shape[1]
+    if N is None:
+        N = qw.shape[2] if code == GPTQ else qw.shape[2] * 8
+    codes = np.zeros((E, K, N if bits == 8 else N // 2), np.uint8)
+    ng = -(-K // group)
+    qz = None if qzeros is None else np.ascontiguousarray(_np(qzeros).astype(np.int32, copy=False))
+    zeros = None if qz is None else np.empty((E, ng, N), np.uint8)
+    rc = lib.oracle_unpack_wq(code, bits, E, K, N, group, qw.ctypes.data, _ptr(qz),
+                              int(zero_adjust), codes.ctypes.data, _ptr(zeros))
+    if rc != 0:
+        raise ValueError("oracle_unpack_wq: unsupported layout")
+    return codes, zeros
 
 
 # ---------------------------------------------------------------- expert FFN

@@ -425,6 +425,92 @@ static double wq_weight(const oracle_experts* W, const void* w, const float* sca
     return (double)(wq_code(W, w, (int64_t)e * K + k, N, n) - z) * (double)scale[gi];
 }
 
+/* GPTQ and AWQ checkpoints ship WNA16 codes packed into int32 words
+ * (FlagGems walkthrough, "WNA16" section, which names both layouts without
+ * giving their bit order).  The reading taken here, per K x N weight of one
+ * expert (per = 32 / bits codes a word, the code at word bits
+ * [bits * i, bits * (i + 1))):
+ *   GPTQ   qweight [K / per][N]: word (r, n), slot i = row per * r + i of
+ *          column n (rows packed along K);
+ *          qzeros [ng][N / per]: word (g, c), slot i = the zero point of
+ *          column per * c + i in group g (packed along N in order);
+ *   AWQ    (4-bit) qweight [K][N / 8]: word (k, c), slot i = column
+ *          8 c + AWQ_ORDER[i] of row k, AWQ_ORDER = {0, 2, 4, 6, 1, 3, 5, 7};
+ *          qzeros [ng][N / 8] the same way.
+ * zero_adjust is added to every stored zero point (checkpoints of the
+ * earlier GPTQ format store z - 1).
+ * Output: the oracle's plain codes (OR_U8: one byte a code, [K][N]; OR_U4:
+ * two a byte along N, even column in the low nibble, [K][N / 2]) and the
+ * zero points as one byte per group and column [ng][N] (when qzeros is
+ * given).  Returns 0, or -1 for an unsupported combination. */
+enum { OR_GPTQ = 1, OR_AWQ = 2 };
+
+static int packed_slot(const int32_t* words, int64_t idx, int bits, int slot)
+{
+    const uint32_t w = (uint32_t)words[idx];
+    return (int)((w >> (bits * slot)) & ((1u << bits) - 1u));
+}
+
+int oracle_unpack_wq(int32_t format, int32_t bits, int64_t E, int64_t K, int64_t N, int64_t group,
+                     const int32_t* qweight, const int32_t* qzeros, int32_t zero_adjust,
+                     uint8_t* codes, uint8_t* zeros)
+{
+    static const int awq_order[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+    const int per = 32 / bits;
+    const int64_t ng = (K + group - 1) / group;
+    if ((bits != 4 && bits != 8) || (format != OR_GPTQ && format != OR_AWQ) || group < 1)
+        return -1;
+    if (format == OR_AWQ && bits != 4)
+        return -1;
+    if ((format == OR_GPTQ && K % per) || (format == OR_AWQ && N % 8) ||
+        (qzeros && N % per) || (bits == 4 && N % 2))
+        return -1;
+    for (int64_t e = 0; e < E; ++e) {
+        for (int64_t k = 0; k < K; ++k) {
+            for (int64_t n = 0; n < N; ++n) {
+                int q;
+                if (format == OR_GPTQ) {
+                    const int64_t idx = (e * (K / per) + k / per) * N + n;
+                    q = packed_slot(qweight, idx, bits, (int)(k % per));
+                } else {
+                    /* column n sits in word n / 8 at the slot whose order entry is n % 8 */
+                    int slot = 0;
+                    while (awq_order[slot] != (int)(n % 8))
+                        ++slot;
+                    q = packed_slot(qweight, (e * K + k) * (N / 8) + n / 8, bits, slot);
+                }
+                if (bits == 8) {
+                    codes[(e * K + k) * N + n] = (uint8_t)q;
+                } else {
+                    uint8_t* b = codes + (e * K + k) * (N / 2) + n / 2;
+                    if (n % 2 == 0)
+                        *b = (uint8_t)((*b & 0xF0) | q);
+                    else
+                        *b = (uint8_t)((*b & 0x0F) | (q << 4));
+                }
+            }
+        }
+        if (!qzeros || !zeros)
+            continue;
+        for (int64_t g = 0; g < ng; ++g) {
+            for (int64_t n = 0; n < N; ++n) {
+                int z;
+                if (format == OR_GPTQ) {
+                    z = packed_slot(qzeros, (e * ng + g) * (N / per) + n / per, bits,
+                                    (int)(n % per));
+                } else {
+                    int slot = 0;
+                    while (awq_order[slot] != (int)(n % 8))
+                        ++slot;
+                    z = packed_slot(qzeros, (e * ng + g) * (N / 8) + n / 8, bits, slot);
+                }
+                zeros[(e * ng + g) * N + n] = (uint8_t)((z + zero_adjust) & ((1 << bits) - 1));
+            }
+        }
+    }
+    return 0;
+}
+
 typedef struct {
     int32_t dtype;            /* OR_F32, OR_BF16, OR_FP8 (codes + per-row scale) */
     const void* data;         /* [rows][H]                                       */

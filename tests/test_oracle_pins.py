@@ -559,13 +559,15 @@ def _wq_dequant(codes, scale, zero, bits, group, K, N):
     return (c.double() - zk) * sk
 
 
-@pytest.mark.parametrize("bits,zero", [(8, True), (8, False), (4, True), (4, False)])
-def test_wna16_equals_dequantised_product(bits, zero):
-    """WNA16 (int8_w8a16 / int4_w4a16 with group scales and zero points):
-    against torch float64 on dequantised weights.  H 320 gives a short last
-    K group; biases included."""
-    g = torch.Generator().manual_seed(40 + bits + int(zero))
-    M, H, I, E, G = 6, 320, 256, 3, 128
+@pytest.mark.parametrize("bits,zero,G", [(8, True, 128), (8, False, 128), (4, True, 128),
+                                         (4, False, 128), (4, True, 32), (8, False, 64),
+                                         (4, False, 64), (8, True, 32)])
+def test_wna16_equals_dequantised_product(bits, zero, G):
+    """WNA16 (int8_w8a16 / int4_w4a16 with group scales and zero points,
+    groups of 32, 64 or 128 K rows): against torch float64 on dequantised
+    weights.  H 320 gives a short last K group; biases included."""
+    g = torch.Generator().manual_seed(40 + bits + int(zero) + G)
+    M, H, I, E = 6, 320, 256, 3
     hi = 2 ** bits
     x = _bf(torch.randn(M, H, generator=g))
     q13 = torch.randint(0, hi, (E, H, 2 * I), generator=g)
@@ -612,6 +614,53 @@ def test_wna16_int4_nibble_order_and_default_zero():
     out, _ = oracle.expert_rows(ex, oracle.Acts(np.array([[1.0, 0.0]], np.float32)), [0], [0])
     silu = 2.0 / (1.0 + math.exp(-2.0))
     assert np.allclose(out[0], [silu * -3.0, 0.0], rtol=1e-14)
+
+
+# ----------------------------------------------------------------- GPTQ / AWQ words
+
+def test_gptq_awq_hand_worked_words():
+    """One int32 word 0x76543210 (slot i holds the value i).  GPTQ packs K
+    rows: rows 0..7 of the column get 0..7.  AWQ packs columns in the order
+    0, 2, 4, 6, 1, 3, 5, 7: slot i goes to column AWQ_ORDER[i], so columns
+    0..7 read 0, 4, 1, 5, 2, 6, 3, 7.  8-bit GPTQ: 0x04030201 puts 1..4 in
+    rows 0..3.  Zero words pack along N the same way, and zero_adjust adds
+    one to each stored zero."""
+    w = np.int32(0x76543210)
+    codes, _ = oracle.unpack_wq("gptq", 4, np.full((1, 1, 2), w, np.int32))
+    assert codes.shape == (1, 8, 1)                           # two columns a byte
+    assert [codes[0, k, 0] & 15 for k in range(8)] == list(range(8))
+    assert [codes[0, k, 0] >> 4 for k in range(8)] == list(range(8))
+    codes, zeros = oracle.unpack_wq("awq", 4, np.full((1, 1, 1), w, np.int32),
+                                    qzeros=np.full((1, 1, 1), w, np.int32), K=1, N=8, group=1)
+    cols = [(codes[0, 0, n // 2] >> (4 * (n % 2))) & 15 for n in range(8)]
+    assert cols == [0, 4, 1, 5, 2, 6, 3, 7]
+    assert list(zeros[0, 0]) == [0, 4, 1, 5, 2, 6, 3, 7]
+    codes, zeros = oracle.unpack_wq("gptq", 8, np.full((1, 1, 1), 0x04030201, np.int32),
+                                    qzeros=np.full((1, 1, 1), 0x04030201, np.int32), K=4, N=4,
+                                    group=4, zero_adjust=1)
+    assert list(codes[0, :, 0]) == [1, 2, 3, 4]
+    assert list(zeros[0, 0]) == [2, 3, 4, 5]                  # stored z - 1, adjusted back
+    # GPTQ 4-bit zero words pack along N in order
+    _, zeros = oracle.unpack_wq("gptq", 4, np.zeros((1, 1, 8), np.int32),
+                                qzeros=np.full((1, 1, 1), w, np.int32), K=8, N=8, group=8)
+    assert list(zeros[0, 0]) == list(range(8))
+
+
+@pytest.mark.parametrize("fmt,bits", [("gptq", 4), ("gptq", 8), ("awq", 4)])
+def test_gptq_awq_unpack_inverts_the_checkpoint_packing(fmt, bits):
+    """Codes and zero points packed by the workload generator's GPTQ / AWQ
+    packers unpack to the plain codes they came from (random codes, several
+    experts, K not a multiple of the group)."""
+    from mixture_experts_ffn_router_amd import workloads as W
+    g = torch.Generator().manual_seed(50 + bits + len(fmt))
+    E, K, N, G = 3, 96, 40, 64
+    q = torch.randint(0, 2 ** bits, (E, K, N), generator=g).to(torch.uint8)
+    z = torch.randint(0, 2 ** bits, (E, -(-K // G), N), generator=g).to(torch.uint8)
+    qw, qz = W.pack_wq_checkpoint(q, z, bits, fmt)
+    codes, zeros = oracle.unpack_wq(fmt, bits, qw, qzeros=qz, K=K, N=N, group=G)
+    plain = q.numpy() if bits == 8 else (q[..., 0::2] | (q[..., 1::2] << 4)).numpy()
+    assert np.array_equal(codes, plain)
+    assert np.array_equal(zeros, z.numpy())
 
 
 def test_batched_rows_reduce_equals_contiguous():
