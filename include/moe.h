@@ -139,10 +139,11 @@ typedef enum {
  *                MOE_U8 / MOE_U4: WNA16 weights (the walkthrough's "WNA16"
  *                section, int8_w8a16 / int4_w4a16) with bf16 activations:
  *                weight = (q - z) * s, q the unsigned code, one float scale s
- *                and one zero point z per group of 128 K rows and output
+ *                and one zero point z per group of wq_group K rows and output
  *                column (z = 2^(bits-1) when no zero points are given); the
  *                weights are dequantised to bf16 inside the GEMMs, which
  *                accumulate in float32.  Needs w_layout = MOE_W_PACKED.
+ *                GPTQ / AWQ checkpoints: moe_repack_wna16 first.
  *   out_dtype    MOE_F32 or MOE_BF16.  f32 activations need f32 out.
  *   logits_dtype MOE_F32 or MOE_BF16 (contiguous, routing != PRECOMPUTED).
  *   routing, renormalize, group_count, k_group, group_select_mode,
@@ -214,6 +215,10 @@ typedef enum {
  *                tile in the 160-row bf16 family (2 x 64 or 4 x 64 weight
  *                columns a wave row); ignored by the other families.  Other
  *                values: MOE_ERR_INVALID_ARG.
+ *   wq_group     MOE_U8 / MOE_U4 weights: K rows per scale group, 32, 64 or 128
+ *                (0 means 128; the group sizes of GPTQ / AWQ checkpoints).
+ *                Other values MOE_ERR_UNSUPPORTED; other weight types need 0
+ *                (MOE_ERR_INVALID_ARG).
  */
 typedef struct {
     int32_t format;
@@ -231,6 +236,7 @@ typedef struct {
     int32_t fp8_block;
     int32_t tile_hint;
     int32_t gemm1_wave_cols;
+    int32_t wq_group;
 } moe_problem;
 
 /* Workspace layout chosen by the library for one problem.  All offsets are
@@ -298,8 +304,9 @@ int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* info);
  *                     even column in the low nibble: [E, H, I], [E, I, H / 2].
  *   w13_bias, w2_bias [E, 2I], [E, H] when has_*_bias.
  *   w13_scale, w2_scale
- *                     MOE_U8 / MOE_U4 weights: float per 128-row K group and
- *                     column, [E, ceil(H / 128), 2I] and [E, ceil(I / 128), H].
+ *                     MOE_U8 / MOE_U4 weights: float per K group (G = wq_group
+ *                     rows) and column, [E, ceil(H / G), 2I] and
+ *                     [E, ceil(I / G), H].
  *                     fp8 weights: float per output channel, [E, 2I] and [E, H];
  *                     with fp8_block = 128 one float per 128 x 128 block,
  *                     [E, 2I / 128, ceil(H / 128)] and [E, ceil(H / 128), I / 128]
@@ -366,6 +373,39 @@ typedef enum {
  * moe_forward. */
 int moe_forward_timed(const moe_problem* p, const moe_args* a, void* workspace,
                       size_t workspace_bytes, void* stream, void** events);
+
+/* Checkpoint layouts of WNA16 codes, for moe_repack_wna16. */
+typedef enum {
+    MOE_WQ_GPTQ = 1,          /* codes packed along K into int32 words            */
+    MOE_WQ_AWQ = 2            /* codes packed along N, interleaved (4-bit only)   */
+} moe_wq_format;
+
+/* Converts the int32-packed codes of a GPTQ or AWQ checkpoint (the
+ * walkthrough's "WNA16" section names both layouts) into the plain WNA16
+ * layout that moe_pack_weights takes, for E experts of one K x N weight
+ * (w13: K = H, N = 2I; w2: K = I, N = H).  per = 32 / bits codes share a
+ * word; code slot i of a word is bits [bits * i, bits * (i + 1)).
+ *   MOE_WQ_GPTQ (bits 4 or 8): qweight [E, K / per, N], word (r, n) holding
+ *     rows per * r + i of column n; qzeros [E, ceil(K / group), N / per],
+ *     word (g, c) holding columns per * c + i.
+ *   MOE_WQ_AWQ (bits 4): qweight [E, K, N / 8], word (k, c) holding column
+ *     8 c + {0, 2, 4, 6, 1, 3, 5, 7}[i] of row k in slot i; qzeros
+ *     [E, ceil(K / group), N / 8] the same way.
+ * Writes `codes` (bits 8: [E, K, N] bytes; bits 4: [E, K, N / 2], two codes
+ * a byte along N, the even column in the low nibble) and, when qzeros is
+ * given, `zeros` [E, ceil(K / group), N] uint8: each stored zero point plus
+ * zero_adjust, modulo 2^bits (1 for checkpoints that store z - 1, else 0).
+ * The checkpoints' scales are already [E, ceil(K / group), N] (convert them
+ * to float32); act-order permutations (g_idx) are not taken.  Device
+ * buffers, caller-owned, not overlapping; enqueued on `stream`.  Returns
+ * MOE_OK; MOE_ERR_INVALID_ARG for a null pointer (zeros null with qzeros
+ * given), a non-positive size, K not a multiple of per (GPTQ), N not a
+ * multiple of 8 (AWQ) or of per (GPTQ zero points), N odd with 4 bits;
+ * MOE_ERR_UNSUPPORTED for bits other than 4 / 8, AWQ with 8 bits, a group
+ * other than 32 / 64 / 128, or an unknown format; MOE_ERR_LAUNCH. */
+int moe_repack_wna16(int format, int bits, int E, int K, int N, int group,
+                     const int32_t* qweight, const int32_t* qzeros, int zero_adjust,
+                     uint8_t* codes, uint8_t* zeros, void* stream);
 
 /* Packed weights.  The expert weights are constant across calls, so a caller
  * can re-lay them out once, at load time, into the order in which the grouped

@@ -28,7 +28,9 @@ MOE_TILE_DMA_32, MOE_TILE_DMA_64 = 5, 6
 MOE_DEV_ID_RANGE, MOE_DEV_COUNT_CLAMPED, MOE_DEV_ROWS_OVERFLOW, MOE_DEV_TOKEN_MAP = 1, 2, 4, 8
 
 EXPORTED = ("moe_workspace_shapes", "moe_forward", "moe_forward_timed", "moe_packed_weight_bytes",
-            "moe_pack_weights", "moe_forward_static", "moe_status_string", "moe_version")
+            "moe_pack_weights", "moe_forward_static", "moe_repack_wna16", "moe_status_string",
+            "moe_version")
+MOE_WQ_GPTQ, MOE_WQ_AWQ = 1, 2
 STAGES = ("router", "align", "quant", "gemm1", "gemm2", "reduce")
 
 
@@ -45,7 +47,7 @@ class moe_problem(ctypes.Structure):
                 ("w_layout", ctypes.c_int32), ("global_experts", ctypes.c_int32),
                 ("apply_weight_on_input", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
                 ("fp8_block", ctypes.c_int32), ("tile_hint", ctypes.c_int32),
-                ("gemm1_wave_cols", ctypes.c_int32)]
+                ("gemm1_wave_cols", ctypes.c_int32), ("wq_group", ctypes.c_int32)]
 
 
 class moe_workspace_info(ctypes.Structure):
@@ -104,6 +106,9 @@ def load() -> ctypes.CDLL:
         lib.moe_forward_static.argtypes = [ctypes.POINTER(moe_problem), ctypes.POINTER(moe_args),
                                            ctypes.c_void_p]
         lib.moe_forward_static.restype = ctypes.c_int
+        lib.moe_repack_wna16.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 2 + [
+            ctypes.c_int] + [ctypes.c_void_p] * 3
+        lib.moe_repack_wna16.restype = ctypes.c_int
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         lib.moe_version.argtypes = []
@@ -231,6 +236,7 @@ class Problem:
     fp8_block: int = 0
     tile_hint: int = MOE_TILE_AUTO
     gemm1_wave_cols: int = 0
+    wq_group: int = 0
 
     def c(self) -> moe_problem:
         return moe_problem(self.fmt, self.M, self.H, self.I, self.E, self.top_k, self.max_tokens,
@@ -240,7 +246,8 @@ class Problem:
                            int(self.has_w13_bias), int(self.has_w2_bias),
                            int(self.batched_reduce), int(self.w_layout), int(self.global_experts),
                            int(self.apply_weight_on_input), int(self.chunk_tokens),
-                           int(self.fp8_block), int(self.tile_hint), int(self.gemm1_wave_cols))
+                           int(self.fp8_block), int(self.tile_hint), int(self.gemm1_wave_cols),
+                           int(self.wq_group))
 
 
 @dataclass
@@ -279,6 +286,31 @@ def pack_weights(w13, w2, wq_bits: int = 0) -> PackedWeights:
     moe_pack_weights(prob, _ptr(w13), _ptr(w2), p13.data_ptr(), p2.data_ptr(),
                      current_stream_handle(w13.device))
     return PackedWeights(p13, p2, E, H, I, wdt)
+
+
+def repack_wna16(fmt: str, bits: int, qweight, qzeros=None, K=None, N=None, group=128,
+                 zero_adjust=0):
+    """GPTQ / AWQ checkpoint codes (int32 device tensors, [E, ...] as in
+    moe.h) -> (plain WNA16 codes uint8, zero points uint8 [E, ceil(K/group), N]
+    or None), ready for pack_weights(..., wq_bits=bits)."""
+    import torch
+    code = {"gptq": MOE_WQ_GPTQ, "awq": MOE_WQ_AWQ}[fmt]
+    per = 32 // bits
+    E = qweight.shape[0]
+    if K is None:
+        K = qweight.shape[1] * per if code == MOE_WQ_GPTQ else qweight.shape[1]
+    if N is None:
+        N = qweight.shape[2] if code == MOE_WQ_GPTQ else qweight.shape[2] * 8
+    dev = qweight.device
+    codes = torch.empty(E, K, N if bits == 8 else N // 2, dtype=torch.uint8, device=dev)
+    zeros = None if qzeros is None else torch.empty(E, -(-K // group), N, dtype=torch.uint8,
+                                                    device=dev)
+    rc = load().moe_repack_wna16(code, bits, E, K, N, group, _ptr(qweight), _ptr(qzeros),
+                                 int(zero_adjust), _ptr(codes), _ptr(zeros),
+                                 ctypes.c_void_p(current_stream_handle(dev)))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_repack_wna16")
+    return codes, zeros
 
 
 def _weights(w13, w2):
@@ -328,7 +360,8 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
               w2_bias=None, topk_ids=None, topk_weights=None, w13_scale=None, w2_scale=None,
               out_dtype=None, out=None, workspace=None, expert_map=None,
               apply_weight_on_input=False, chunk_tokens=0, fp8_block=0, w13_zero=None,
-              w2_zero=None, tile_hint=MOE_TILE_AUTO, gemm1_wave_cols=0, static=False):
+              w2_zero=None, tile_hint=MOE_TILE_AUTO, gemm1_wave_cols=0, static=False,
+              wq_group=0):
     """Contiguous-format forward on torch device tensors (the MindIE-SD
     page's fused_moe argument list, single device).  w13 may be a
     PackedWeights (then w2 is ignored).  expert_map [global experts] int32
@@ -363,7 +396,8 @@ def fused_moe(hidden, w13, w2, router_logits=None, *, top_k: int, renormalize: b
                    w_layout=layout,
                    global_experts=0 if expert_map is None else int(expert_map.numel()),
                    apply_weight_on_input=apply_weight_on_input, chunk_tokens=chunk_tokens,
-                   fp8_block=fp8_block, tile_hint=tile_hint, gemm1_wave_cols=gemm1_wave_cols)
+                   fp8_block=fp8_block, tile_hint=tile_hint, gemm1_wave_cols=gemm1_wave_cols,
+                   wq_group=wq_group)
     if out is None:
         out = torch.empty(M, H, dtype=odt, device=hidden.device)
     args = make_args(hidden, w13, w2, out, router_logits=router_logits, topk_ids=topk_ids,
@@ -386,7 +420,7 @@ def fused_moe_batched(hidden, expert_num_tokens, w13, w2, *, M: int = 0, top_k: 
                       a_scale=None, w13_scale=None, w2_scale=None, w13_bias=None, w2_bias=None,
                       token_map=None, token_map_w=None, out_dtype=None, out=None,
                       workspace=None, fp8_block=0, w13_zero=None, w2_zero=None,
-                      tile_hint=MOE_TILE_AUTO, static=False):
+                      tile_hint=MOE_TILE_AUTO, static=False, wq_group=0):
     """Batched-format forward: hidden [E, max_tokens, H] + expert_num_tokens [E].
     M, top_k (when M > 0) promise that the slabs hold at most M * top_k valid
     rows, which bounds the workspace (slabs that break the promise are not
@@ -406,7 +440,7 @@ def fused_moe_batched(hidden, expert_num_tokens, w13, w2, *, M: int = 0, top_k: 
                    out_dtype=_dtype_code(torch.empty(0, dtype=odt)),
                    routing=MOE_ROUTE_PRECOMPUTED, has_w13_bias=w13_bias is not None,
                    has_w2_bias=w2_bias is not None, batched_reduce=reduce, w_layout=layout,
-                   fp8_block=fp8_block, tile_hint=tile_hint)
+                   fp8_block=fp8_block, tile_hint=tile_hint, wq_group=wq_group)
     if out is None:
         shape = (M, H) if reduce else (E, T, H)
         out = torch.empty(shape, dtype=odt, device=hidden.device)

@@ -77,6 +77,14 @@ static int validate(const moe_problem* p)
         (p->fp8_block != 128 || w != MOE_FP8_E4M3FN || p->w_layout != MOE_W_PACKED))
         return MOE_ERR_UNSUPPORTED;
 
+    // WNA16 scale groups of 32, 64 or 128 K rows (0: 128)
+    if (p->wq_group != 0) {
+        if (w != MOE_U8 && w != MOE_U4)
+            return MOE_ERR_INVALID_ARG;
+        if (p->wq_group != 32 && p->wq_group != 64 && p->wq_group != 128)
+            return MOE_ERR_UNSUPPORTED;
+    }
+
     // per-call tuning hints (tile family, GEMM1 width); 0 = the library's choice
     const int th = p->tile_hint;
     if (th != MOE_TILE_AUTO && th != MOE_TILE_DMA_160 && th != MOE_TILE_REG_64 &&
@@ -280,6 +288,7 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
     P.wpacked = p->w_layout == MOE_W_PACKED ? 1 : 0;
     P.blk = p->fp8_block ? 1 : 0;
     P.wq = (p->w_dtype == MOE_U8) ? 8 : (p->w_dtype == MOE_U4) ? 4 : 0;
+    P.wq_gsh = (p->wq_group == 32) ? 0 : (p->wq_group == 64) ? 1 : 2;
     P.BM = w.block_m;
     P.cfg = cfg;
     P.g1wc = p->gemm1_wave_cols;
@@ -602,6 +611,28 @@ extern "C" int moe_pack_weights(const moe_problem* p, const void* w13, const voi
         err = launch_pack_weights(p->E, p->H, p->I, w13, w2, w13_packed, w2_packed,
                                   (hipStream_t)stream);
     return err == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+extern "C" int moe_repack_wna16(int format, int bits, int E, int K, int N, int group,
+                                const int32_t* qweight, const int32_t* qzeros, int zero_adjust,
+                                uint8_t* codes, uint8_t* zeros, void* stream)
+{
+    if (format != MOE_WQ_GPTQ && format != MOE_WQ_AWQ)
+        return MOE_ERR_UNSUPPORTED;
+    if ((bits != 4 && bits != 8) || (format == MOE_WQ_AWQ && bits != 4))
+        return MOE_ERR_UNSUPPORTED;
+    if (group != 32 && group != 64 && group != 128)
+        return MOE_ERR_UNSUPPORTED;
+    if (E < 1 || K < 1 || N < 1 || !qweight || !codes || (qzeros && !zeros))
+        return MOE_ERR_INVALID_ARG;
+    const int per = 32 / bits;
+    if ((format == MOE_WQ_GPTQ && K % per) || (format == MOE_WQ_AWQ && N % 8) ||
+        (qzeros && N % per) || (bits == 4 && N % 2))
+        return MOE_ERR_INVALID_ARG;
+    (void)hipGetLastError();   // a stale error of an earlier, unrelated call
+    const hipError_t e = launch_repack_wq(format, bits, E, K, N, (K + group - 1) / group, qweight,
+                                          qzeros, zero_adjust, codes, zeros, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }
 
 extern "C" const char* moe_status_string(int status)

@@ -634,15 +634,19 @@ __global__ void __launch_bounds__(256) k_gemm2(Gemm2Args g)
 // WNA16 (Q = 8 or 4 code bits; the walkthrough's "WNA16" section): the
 // weight block of a stage is 128 columns x 64 K of codes in fragment order
 // (8 or 4 KiB, see the packed layout in moe.h), followed by the stage's
-// group scales (128 floats, 1 KiB slot) and zero points (128 bytes, 1 KiB
-// slot), both DMA'd from the plain [E, K / 128, N] grids.  The 160-row tile
-// dequantises its B fragments to bf16 right after their LDS read (w =
-// (q - z) * s as one FMA q * s + (-z s) on the float code, then a packed RNE
-// conversion); the small-row tiles feed the raw codes to the MFMAs and
-// apply s and z per stage (DmaFrag::raw_codes).
-template <int FMW_, int WC_, int NS_, int Q_ = 0>
+// group scales (1 KiB slot) and zero points (1 KiB slot), DMA'd from the
+// plain [E, ceil(K / G), N] grids.  With groups of 64 or 128 K rows the
+// stage lies inside one group (128 floats, 128 bytes); with groups of 32
+// (G2) it spans two, one per MFMA step, and the slots hold both (the second
+// at +512 / +128 bytes).  The 160-row tile dequantises its B fragments to
+// bf16 right after their LDS read (w = (q - z) * s as one FMA q * s + (-z s)
+// on the float code, then a packed RNE conversion); the small-row tiles feed
+// the raw codes to the MFMAs and apply s and z per group
+// (DmaFrag::raw_codes).
+template <int FMW_, int WC_, int NS_, int Q_ = 0, int G2_ = 0>
 struct DS {
     static constexpr int FMW = FMW_, WC = WC_, NS = NS_, Q = Q_;
+    static constexpr int G2 = G2_;                       // WNA16: two scale groups a stage
     static constexpr int NW = 2 * WC, NT = 64 * NW;      // waves, threads
     static constexpr int FN = 4;                         // 16-column fragments per wave
     static constexpr int CH = 32 * FMW;                  // rows per tile
@@ -670,6 +674,7 @@ struct DS {
     static_assert((NS - 2) * D < 64, "vmcnt range");
     static_assert(Q == 0 || Q == 8 || Q == 4, "code width");
     static_assert(Q == 0 || NB == 1, "a WNA16 tile holds one weight block");
+    static_assert(G2 == 0 || Q != 0, "scale groups are a WNA16 notion");
 };
 
 // DMA sources of one tile.  Wave w issues the A DMAs i = w + NW j (tile rows
@@ -695,6 +700,7 @@ struct DmaTile {
     const char* qs;             // WNA16: this lane's 16 scale bytes of group 0, or null
     const char* qz;             //   and its 16 zero-point bytes, or null
     int64_t qs_g, qz_g;         //   bytes from one K group to the next
+    int gsh;                    //   log2(group / 32): the stage's first group is (2 kt) >> gsh
 
     bool nt;                    // the weights are read by this tile alone: non-temporal DMAs
 
@@ -753,11 +759,17 @@ struct DmaTile {
                 dma16(p, lds + S::A_BYTES + i * 1024);
         }
         if constexpr (S::Q != 0) {
-            const int grp = kt >> 1;            // 128-row K groups, 64-row stages
+            // the group of the stage's first 32 K rows; with G2 the lanes of
+            // the second half of each DMA (scales: 32-63, zero points: 8-15)
+            // point one group further, which exists while its rows start inside K
+            const int grp = (2 * kt) >> gsh;
+            const bool second_ok = !S::G2 || kt * 64 + 32 < K;
             if (wave == 0)
-                dma16((live && qs) ? qs + grp * qs_g : zero, lds + S::SZ_OFF);
+                dma16((live && qs && (lane < 32 || second_ok)) ? qs + grp * qs_g : zero,
+                      lds + S::SZ_OFF);
             else if (wave == 1)
-                dma16((live && qz) ? qz + grp * qz_g : zero, lds + S::SZ_OFF + 1024);
+                dma16((live && qz && (lane < 8 || second_ok)) ? qz + grp * qz_g : zero,
+                      lds + S::SZ_OFF + 1024);
         }
     }
 };
@@ -880,27 +892,32 @@ struct DmaFrag {
         const char* Bs = st + S::A_BYTES;
         if constexpr (S::Q != 0 && S::FMW <= 2) {
             constexpr float ZDEF = (S::Q == 8) ? 128.0f : 8.0f;
-            float sc[S::FN], szn[S::FN];
+            constexpr int NG = S::G2 ? 2 : 1;            // scale groups in the stage
+            float sc[NG][S::FN], szn[NG][S::FN];
 #pragma unroll
-            for (int fn = 0; fn < S::FN; ++fn) {
-                sc[fn] = *(const float*)(st + s_off[fn]);
-                const float z = hz ? (float)*(const uint8_t*)(st + S::SZ_OFF + 1024 +
-                                                              (s_off[fn] - S::SZ_OFF) / 4)
-                                   : ZDEF;
-                szn[fn] = -(z + RAW_OFF) * sc[fn];
-            }
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int fn = 0; fn < S::FN; ++fn) {
+                    sc[gi][fn] = *(const float*)(st + s_off[fn] + gi * 512);
+                    const float z = hz ? (float)*(const uint8_t*)(st + S::SZ_OFF + 1024 + gi * 128 +
+                                                                  (s_off[fn] - S::SZ_OFF) / 4)
+                                       : ZDEF;
+                    szn[gi][fn] = -(z + RAW_OFF) * sc[gi][fn];
+                }
             const i32x4 ones_bits = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};
             const bf16x8 ones = __builtin_bit_cast(bf16x8, ones_bits);
             f32x4 pq[NM][S::FN], rs[NM];
 #pragma unroll
-            for (int fm = 0; fm < NM; ++fm) {
-                rs[fm] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int fn = 0; fn < S::FN; ++fn)
-                    pq[fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            }
-#pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
+                if (ks == 0 || S::G2) {
+#pragma unroll
+                    for (int fm = 0; fm < NM; ++fm) {
+                        rs[fm] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int fn = 0; fn < S::FN; ++fn)
+                            pq[fm][fn] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    }
+                }
                 bf16x8 a[NM], b[S::FN];
 #pragma unroll
                 for (int fn = 0; fn < S::FN; ++fn)
@@ -916,32 +933,39 @@ struct DmaFrag {
                         pq[fm][fn] =
                             __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[fn], pq[fm][fn], 0, 0, 0);
                 }
+                if (ks == 1 || S::G2) {                  // a scale group is complete
+                    const int gi = S::G2 ? ks : 0;
+#pragma unroll
+                    for (int fm = 0; fm < NM; ++fm)
+#pragma unroll
+                        for (int fn = 0; fn < S::FN; ++fn)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                acc[fm][fn][r] += sc[gi][fn] * pq[fm][fn][r] + szn[gi][fn] * rs[fm][r];
+                }
             }
-#pragma unroll
-            for (int fm = 0; fm < NM; ++fm)
-#pragma unroll
-                for (int fn = 0; fn < S::FN; ++fn)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[fm][fn][r] += sc[fn] * pq[fm][fn][r] + szn[fn] * rs[fm][r];
             return;
         } else if constexpr (S::Q != 0) {
             constexpr float ZDEF = (S::Q == 8) ? 128.0f : 8.0f;
-            float sc[S::FN], bz[S::FN];
+            constexpr int NG = S::G2 ? 2 : 1;            // scale groups in the stage
+            float sc[NG][S::FN], bz[NG][S::FN];
 #pragma unroll
-            for (int fn = 0; fn < S::FN; ++fn) {
-                sc[fn] = *(const float*)(st + s_off[fn]);
-                const float z = hz ? (float)*(const uint8_t*)(st + S::SZ_OFF + 1024 +
-                                                              (s_off[fn] - S::SZ_OFF) / 4)
-                                   : ZDEF;
-                bz[fn] = -z * sc[fn];
-            }
+            for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                for (int fn = 0; fn < S::FN; ++fn) {
+                    sc[gi][fn] = *(const float*)(st + s_off[fn] + gi * 512);
+                    const float z = hz ? (float)*(const uint8_t*)(st + S::SZ_OFF + 1024 + gi * 128 +
+                                                                  (s_off[fn] - S::SZ_OFF) / 4)
+                                       : ZDEF;
+                    bz[gi][fn] = -z * sc[gi][fn];
+                }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
+                const int gi = S::G2 ? ks : 0;
                 bf16x8 a[NM], b[S::FN];
 #pragma unroll
                 for (int fn = 0; fn < S::FN; ++fn)
-                    b[fn] = dequant(st + b_off[fn] + ks * 64 * S::Q, sc[fn], bz[fn]);
+                    b[fn] = dequant(st + b_off[fn] + ks * 64 * S::Q, sc[gi][fn], bz[gi][fn]);
 #pragma unroll
                 for (int fm = 0; fm < NM; ++fm)
                     a[fm] = __builtin_bit_cast(bf16x8, *(const i32x4*)(As + fm * 2048 + a_off[ks]));
@@ -1071,19 +1095,24 @@ __device__ __forceinline__ void gemm1_src(const Gemm1Args& g, const TileRef& t,
         if constexpr (S::Q != 0) {
             // the block's group scales / zero points: gate z columns n0 .. n0 + 63
             // (block columns 0-63), then the up ones (64-127); lanes 0-31 take 4
-            // scales each, lanes 0-7 16 zero points each
-            const int64_t ngk = (H + 127) / 128, base = (int64_t)t.e * ngk * N;
+            // scales each, lanes 0-7 16 zero points each; with G2 lanes 32-63 and
+            // 8-15 take the same columns of the next group
+            const int G = 32 << g.wq_gsh;
+            const int64_t ngk = (H + G - 1) / G, base = (int64_t)t.e * ngk * N;
+            d.gsh = g.wq_gsh;
             d.qs_g = (int64_t)N * 4;
             d.qz_g = N;
-            if (lane < 32) {
-                const int c = n0 + 4 * (lane & 15);
+            if (lane < 32 || S::G2) {
+                const int l = lane & 31, c = n0 + 4 * (l & 15);
                 if (c < I)
-                    d.qs = (const char*)(g.w13_scale + base + (lane < 16 ? c : I + c));
+                    d.qs = (const char*)(g.w13_scale + base + (l < 16 ? c : I + c) +
+                                         (lane >= 32 ? N : 0));
             }
-            if (lane < 8 && g.w13_zero) {
-                const int c = n0 + 16 * (lane & 3);
+            if ((lane < 8 || (S::G2 && lane < 16)) && g.w13_zero) {
+                const int l = lane & 7, c = n0 + 16 * (l & 3);
                 if (c < I)
-                    d.qz = (const char*)(g.w13_zero + base + (lane < 4 ? c : I + c));
+                    d.qz = (const char*)(g.w13_zero + base + (l < 4 ? c : I + c) +
+                                         (lane >= 8 ? N : 0));
             }
         }
     } else {
@@ -1125,13 +1154,17 @@ __device__ __forceinline__ void gemm2_src(const Gemm2Args& g, const TileRef& t, 
         }
         if constexpr (S::Q != 0) {
             // the block's group scales / zero points: columns c0 .. c0 + 127
-            const int64_t ngi = (I + 127) / 128, base = (int64_t)t.e * ngi * H;
+            // (with G2 the upper lanes take the next group's)
+            const int G = 32 << g.wq_gsh;
+            const int64_t ngi = (I + G - 1) / G, base = (int64_t)t.e * ngi * H;
+            d.gsh = g.wq_gsh;
             d.qs_g = (int64_t)H * 4;
             d.qz_g = H;
-            if (lane < 32 && c0 + 4 * lane < H)
-                d.qs = (const char*)(g.w2_scale + base + c0 + 4 * lane);
-            if (lane < 8 && g.w2_zero && c0 + 16 * lane < H)
-                d.qz = (const char*)(g.w2_zero + base + c0 + 16 * lane);
+            const int ls = lane & 31, lz = lane & 7;
+            if ((lane < 32 || S::G2) && c0 + 4 * ls < H)
+                d.qs = (const char*)(g.w2_scale + base + c0 + 4 * ls + (lane >= 32 ? H : 0));
+            if ((lane < 8 || (S::G2 && lane < 16)) && g.w2_zero && c0 + 16 * lz < H)
+                d.qz = (const char*)(g.w2_zero + base + c0 + 16 * lz + (lane >= 8 ? H : 0));
         }
     } else {
         d.wb[0] = (const char*)g.w2 + (int64_t)t.e * I * H * 2;
@@ -1166,11 +1199,11 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[S::FMW][S::FN])
 // the next tile's first stages are issued and the current tile's epilogue
 // (bias, SiLU(gate) * up, bf16 z stores straight from the accumulators) runs
 // while they are in flight.
-template <int FMW, int WC, int NS, bool PACKED, int Q = 0>
+template <int FMW, int WC, int NS, bool PACKED, int Q = 0, int G2 = 0>
 __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
     k_gemm1_dma(Gemm1Args g)
 {
-    typedef DS<FMW, WC, NS, Q> S;
+    typedef DS<FMW, WC, NS, Q, G2> S;
     constexpr int FN = S::FN;
     constexpr int FH = FN / 2;
     __shared__ __attribute__((aligned(16))) char ring[S::RING];
@@ -1283,11 +1316,11 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
 
 // Persistent GEMM2 over this workgroup's tiles, pipelined across tiles like
 // GEMM1; the epilogue (bias, output rows) runs straight from the accumulators.
-template <int FMW, int WC, int NS, bool PACKED, int Q = 0>
+template <int FMW, int WC, int NS, bool PACKED, int Q = 0, int G2 = 0>
 __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
     k_gemm2_dma(Gemm2Args g)
 {
-    typedef DS<FMW, WC, NS, Q> S;
+    typedef DS<FMW, WC, NS, Q, G2> S;
     constexpr int FN = S::FN;
     __shared__ __attribute__((aligned(16))) char ring[S::RING];
     const int lane = threadIdx.x & 63;
@@ -1549,6 +1582,87 @@ hipError_t launch_pack_weights_wq(int bits, int E, int H, int I, const void* w13
                      : pack_wq<4>(E, H, I, w13, w2, p13, p2, s);
 }
 
+// ---------------------------------------------------------------- GPTQ / AWQ codes
+// Checkpoint int32 words -> the plain WNA16 codes (the layouts are spelled
+// out next to moe_repack_wna16 in moe.h).  One thread per output byte (one
+// 8-bit code, or the two 4-bit codes of columns 2p, 2p + 1), then one per
+// zero point.  In an AWQ word, column 8c + j sits in slot (j >> 1) + 4 (j & 1).
+template <int BITS, bool AWQ>
+__device__ __forceinline__ int wq_checkpoint_code(const int32_t* __restrict__ qw, int64_t e,
+                                                  int64_t K, int64_t N, int64_t k, int64_t n)
+{
+    constexpr int PER = 32 / BITS;
+    uint32_t w;
+    int slot;
+    if constexpr (AWQ) {
+        w = (uint32_t)qw[(e * K + k) * (N / 8) + n / 8];
+        slot = (int)((n & 7) >> 1) + 4 * (int)(n & 1);
+    } else {
+        w = (uint32_t)qw[(e * (K / PER) + k / PER) * N + n];
+        slot = (int)(k % PER);
+    }
+    return (int)((w >> (BITS * slot)) & ((1u << BITS) - 1u));
+}
+
+template <int BITS, bool AWQ>
+__global__ void __launch_bounds__(256) k_repack_wq(const int32_t* __restrict__ qw,
+                                                   const int32_t* __restrict__ qz, int zero_adjust,
+                                                   int64_t E, int64_t K, int64_t N, int64_t ng,
+                                                   uint8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ zeros)
+{
+    constexpr int PER = 32 / BITS;
+    const int64_t per_row = (BITS == 8) ? N : N / 2;        // output bytes per K row
+    const int64_t nc = E * K * per_row, nz = qz ? E * ng * N : 0;
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < nc + nz;
+         q += (int64_t)gridDim.x * 256) {
+        if (q < nc) {
+            const int64_t row = q / per_row, b = q % per_row;
+            const int64_t e = row / K, k = row % K;
+            if constexpr (BITS == 8) {
+                codes[q] = (uint8_t)wq_checkpoint_code<8, AWQ>(qw, e, K, N, k, b);
+            } else {
+                const int lo = wq_checkpoint_code<4, AWQ>(qw, e, K, N, k, 2 * b);
+                const int hi = wq_checkpoint_code<4, AWQ>(qw, e, K, N, k, 2 * b + 1);
+                codes[q] = (uint8_t)(lo | (hi << 4));
+            }
+        } else {
+            const int64_t zq = q - nc, n = zq % N, eg = zq / N;    // eg = e * ng + g
+            uint32_t w;
+            int slot;
+            if constexpr (AWQ) {
+                w = (uint32_t)qz[eg * (N / 8) + n / 8];
+                slot = (int)((n & 7) >> 1) + 4 * (int)(n & 1);
+            } else {
+                w = (uint32_t)qz[eg * (N / PER) + n / PER];
+                slot = (int)(n % PER);
+            }
+            const int z = (int)((w >> (BITS * slot)) & ((1u << BITS) - 1u));
+            zeros[zq] = (uint8_t)((z + zero_adjust) & ((1 << BITS) - 1));
+        }
+    }
+}
+
+hipError_t launch_repack_wq(int format, int bits, int64_t E, int64_t K, int64_t N, int64_t ng,
+                            const int32_t* qw, const int32_t* qz, int zero_adjust,
+                            uint8_t* codes, uint8_t* zeros, hipStream_t s)
+{
+    const int64_t n = E * K * (bits == 8 ? N : N / 2) + (qz ? E * ng * N : 0);
+    const int64_t b = (n + 255) / 256;
+    const dim3 grid((unsigned)(b < 65536 ? (b > 0 ? b : 1) : 65536)), block(256);
+    const bool awq = format == MOE_WQ_AWQ;
+    if (bits == 8)
+        hipLaunchKernelGGL((k_repack_wq<8, false>), grid, block, 0, s, qw, qz, zero_adjust, E, K,
+                           N, ng, codes, zeros);
+    else if (awq)
+        hipLaunchKernelGGL((k_repack_wq<4, true>), grid, block, 0, s, qw, qz, zero_adjust, E, K,
+                           N, ng, codes, zeros);
+    else
+        hipLaunchKernelGGL((k_repack_wq<4, false>), grid, block, 0, s, qw, qz, zero_adjust, E, K,
+                           N, ng, codes, zeros);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- launchers
 template <int DT, int FM, int WN>
 static hipError_t run_gemm1(const Gemm1Args& a, const Plan& P, hipStream_t s)
@@ -1578,14 +1692,14 @@ static hipError_t run_gemm2(const Gemm2Args& a, const Plan& P, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int FMW, int WC, int NS, bool PACKED, int Q = 0>
+template <int FMW, int WC, int NS, bool PACKED, int Q = 0, int G2 = 0>
 static hipError_t run_gemm1_dma(const Gemm1Args& a, const Plan& P, hipStream_t s)
 {
-    typedef DS<FMW, WC, NS, Q> S;
+    typedef DS<FMW, WC, NS, Q, G2> S;
     constexpr int BNZ = S::BN / 2;
     Gemm1Args g = a;
     g.s.n_tiles = (a.I + BNZ - 1) / BNZ;
-    auto kern = k_gemm1_dma<FMW, WC, NS, PACKED, Q>;
+    auto kern = k_gemm1_dma<FMW, WC, NS, PACKED, Q, G2>;
     static std::atomic<int> cached[MAX_DEVICES];
     const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, P, S::NT)),
         block(S::NT);
@@ -1593,13 +1707,13 @@ static hipError_t run_gemm1_dma(const Gemm1Args& a, const Plan& P, hipStream_t s
     return hipGetLastError();
 }
 
-template <int FMW, int WC, int NS, bool PACKED, int Q = 0>
+template <int FMW, int WC, int NS, bool PACKED, int Q = 0, int G2 = 0>
 static hipError_t run_gemm2_dma(const Gemm2Args& a, const Plan& P, hipStream_t s)
 {
-    typedef DS<FMW, WC, NS, Q> S;
+    typedef DS<FMW, WC, NS, Q, G2> S;
     Gemm2Args g = a;
     g.s.n_tiles = (a.H + S::BN - 1) / S::BN * g.ksplit;
-    auto kern = k_gemm2_dma<FMW, WC, NS, PACKED, Q>;
+    auto kern = k_gemm2_dma<FMW, WC, NS, PACKED, Q, G2>;
     static std::atomic<int> cached[MAX_DEVICES];
     const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, P, S::NT)),
         block(S::NT);
@@ -1684,24 +1798,25 @@ static Sched make_sched(const Plan& P)
 //   TILE_MID       4 strips, CH 64
 //   TILE_DECODE    1 strip,  CH 16: a few rows per expert
 //   TILE_FP8       8 strips, CH 128, 128-column z groups
-// WNA16 (Q code bits) runs the DMA tile families with one weight block a tile.
-template <int Q>
+// WNA16 (Q code bits) runs the DMA tile families with one weight block a
+// tile; G2: groups of 32 K rows, two to a 64-row stage.
+template <int Q, int G2>
 static hipError_t launch_gemm1_wq(const Gemm1Args& g, const Plan& P, hipStream_t s)
 {
     switch (P.cfg) {
-    case TILE_DECODE_DMA: return run_gemm1_dma<1, 2, 4, true, Q>(g, P, s);
-    case TILE_MID_DMA: return run_gemm1_dma<2, 2, 3, true, Q>(g, P, s);
-    default: return run_gemm1_dma<5, 2, 2, true, Q>(g, P, s);
+    case TILE_DECODE_DMA: return run_gemm1_dma<1, 2, 4, true, Q, G2>(g, P, s);
+    case TILE_MID_DMA: return run_gemm1_dma<2, 2, 3, true, Q, G2>(g, P, s);
+    default: return run_gemm1_dma<5, 2, 2, true, Q, G2>(g, P, s);
     }
 }
 
-template <int Q>
+template <int Q, int G2>
 static hipError_t launch_gemm2_wq(const Gemm2Args& g, const Plan& P, hipStream_t s)
 {
     switch (P.cfg) {
-    case TILE_DECODE_DMA: return run_gemm2_dma<1, 2, 4, true, Q>(g, P, s);
-    case TILE_MID_DMA: return run_gemm2_dma<2, 2, 3, true, Q>(g, P, s);
-    default: return run_gemm2_dma<5, 2, 2, true, Q>(g, P, s);
+    case TILE_DECODE_DMA: return run_gemm2_dma<1, 2, 4, true, Q, G2>(g, P, s);
+    case TILE_MID_DMA: return run_gemm2_dma<2, 2, 3, true, Q, G2>(g, P, s);
+    default: return run_gemm2_dma<5, 2, 2, true, Q, G2>(g, P, s);
     }
 }
 
@@ -1745,10 +1860,11 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, const float* row_w, hi
         return P.wpacked ? launch_gemm1_fp8(g, P, s) : run_gemm1<MOE_FP8_E4M3FN, 8, 32>(g, P, s);
     if (P.wdt == MOE_F32)
         return run_gemm1<MOE_F32, 1, 16>(g, P, s);
+    g.wq_gsh = P.wq_gsh;
     if (P.wq == 8)
-        return launch_gemm1_wq<8>(g, P, s);
+        return P.wq_gsh ? launch_gemm1_wq<8, 0>(g, P, s) : launch_gemm1_wq<8, 1>(g, P, s);
     if (P.wq == 4)
-        return launch_gemm1_wq<4>(g, P, s);
+        return P.wq_gsh ? launch_gemm1_wq<4, 0>(g, P, s) : launch_gemm1_wq<4, 1>(g, P, s);
     switch (P.cfg) {
     case TILE_PREFILL:
         // a few tiles per CU (few experts, wide I): 256-column tiles, 8 waves and
@@ -1807,10 +1923,11 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
         return P.wpacked ? launch_gemm2_fp8(g, P, s) : run_gemm2<MOE_FP8_E4M3FN, 8, 32>(g, P, s);
     if (P.wdt == MOE_F32)
         return run_gemm2<MOE_F32, 1, 16>(g, P, s);
+    g.wq_gsh = P.wq_gsh;
     if (P.wq == 8)
-        return launch_gemm2_wq<8>(g, P, s);
+        return P.wq_gsh ? launch_gemm2_wq<8, 0>(g, P, s) : launch_gemm2_wq<8, 1>(g, P, s);
     if (P.wq == 4)
-        return launch_gemm2_wq<4>(g, P, s);
+        return P.wq_gsh ? launch_gemm2_wq<4, 0>(g, P, s) : launch_gemm2_wq<4, 1>(g, P, s);
     switch (P.cfg) {
     case TILE_PREFILL:
         if (P.g2split) {   // 256-column tiles over two K halves

@@ -58,8 +58,9 @@ struct Gemm1Args {
     const void* w13;            // [E, H, 2I], or packed blocks (bf16 / fp8 block layouts)
     int w_packed;               // 1: w13 is in the packed block layout
     const float* w13_scale;     // fp8: [E, 2I], or block-wise [E][2I/128][ceil(H/128)];
-                                // WNA16: [E][ceil(H/128)][2I] group scales
+                                // WNA16: [E][ceil(H/G)][2I] group scales
     const uint8_t* w13_zero;    // WNA16: zero points like w13_scale, or null
+    int wq_gsh;                 // WNA16: log2(K rows per scale group / 32)
     const void* b13;            // [E, 2I] or null
     int bias_dt;
     int H, I;
@@ -86,8 +87,9 @@ struct Gemm2Args {
     const void* w2;             // [E, I, H], or packed blocks (bf16 / fp8 block layouts)
     int w_packed;               // 1: w2 is in the packed block layout
     const float* w2_scale;      // fp8: [E, H], or block-wise [E][ceil(H/128)][I/128];
-                                // WNA16: [E][ceil(I/128)][H] group scales
+                                // WNA16: [E][ceil(I/G)][H] group scales
     const uint8_t* w2_zero;     // WNA16: zero points like w2_scale, or null
+    int wq_gsh;                 // WNA16: log2(K rows per scale group / 32)
     int blk;                    // fp8: block-wise scales
     const void* b2;             // [E, H] or null
     int bias_dt;

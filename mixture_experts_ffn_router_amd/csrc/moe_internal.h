@@ -210,6 +210,7 @@ struct Plan {
     int blk;                        // fp8: block-wise scales (128 x 128 weight blocks,
                                     // activation scales per row and 128 columns)
     int wq;                         // WNA16 weight code bits (8 or 4), 0 otherwise
+    int wq_gsh;                     // WNA16: log2(K rows per scale group / 32): 0, 1 or 2
     int BM;                         // align granularity: each expert run padded to BM rows
     int CH;                         // rows per GEMM tile (a multiple of BM)
     int cfg;                        // GEMM tile family (see moe_gemm.hip)
@@ -250,6 +251,11 @@ inline int64_t zs_ld(int64_t max_sorted) { return max_sorted + 256; }
 // WNA16 packed weight codes (moe_gemm.hip): bits 8 or 4
 hipError_t launch_pack_weights_wq(int bits, int E, int H, int I, const void* w13, const void* w2,
                                   void* p13, void* p2, hipStream_t s);
+
+// GPTQ / AWQ checkpoint codes -> plain WNA16 codes (moe_gemm.hip)
+hipError_t launch_repack_wq(int format, int bits, int64_t E, int64_t K, int64_t N, int64_t ng,
+                            const int32_t* qw, const int32_t* qz, int zero_adjust,
+                            uint8_t* codes, uint8_t* zeros, hipStream_t s);
 
 // fp8 packed weights (moe_gemm_fp8.hip)
 hipError_t launch_pack_weights_fp8(int E, int H, int I, const void* w13, const void* w2,

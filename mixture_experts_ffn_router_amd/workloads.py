@@ -42,6 +42,7 @@ class MoeConfig:
                                      # blocks, activations per token and 128 columns)
     wq_zero: bool = False            # u8 / u4 (WNA16): per-group zero points (asymmetric);
                                      # False: symmetric codes around 2^(bits-1)
+    wq_group: int = 128              # u8 / u4 (WNA16): K rows per scale group (32, 64, 128)
     scoring: str = "softmax"         # softmax | sigmoid
     renormalize: bool = True
     group_count: int = 1
@@ -259,10 +260,11 @@ def make_inputs(cfg: MoeConfig, seed: int, device="cpu") -> dict:
     w2 = _randn((E, I, H), gen, device, std=1.0 / math.sqrt(I), dtype=w_dt)
     if cfg.weight in ("u8", "u4"):
         bits = 8 if cfg.weight == "u8" else 4
-        out["w13"], out["w13_scale"], out["w13_zero"] = quantize_weight_wna16(w13, bits,
-                                                                               cfg.wq_zero)
+        out["w13"], out["w13_scale"], out["w13_zero"] = quantize_weight_wna16(
+            w13, bits, cfg.wq_zero, cfg.wq_group)
         del w13
-        out["w2"], out["w2_scale"], out["w2_zero"] = quantize_weight_wna16(w2, bits, cfg.wq_zero)
+        out["w2"], out["w2_scale"], out["w2_zero"] = quantize_weight_wna16(w2, bits, cfg.wq_zero,
+                                                                           cfg.wq_group)
         del w2
     elif cfg.weight == "fp8":
         quant = quantize_weight_fp8_blocks if cfg.fp8_block else quantize_weight_fp8

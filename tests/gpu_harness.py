@@ -69,6 +69,7 @@ def run_contiguous(inp: dict, dev, precomputed=None, out=None, inplace=False, ou
     bits = WQ_BITS.get(cfg.weight, 0)
     if bits:
         packed = True                   # WNA16 codes run packed
+        kw["wq_group"] = cfg.wq_group
     if packed:
         w13, w2 = B.pack_weights(w13, w2, wq_bits=bits), None
     for name in ("w13_bias", "w2_bias", "w13_scale", "w2_scale", "w13_zero", "w2_zero"):
@@ -130,6 +131,7 @@ def oracle_experts(inp: dict) -> oracle.Experts:
                           _cpu(inp.get("w2_scale")), _cpu(inp.get("w13_bias")),
                           _cpu(inp.get("w2_bias")), requant_z=cfg.weight == "fp8",
                           block=cfg.fp8_block, bits=WQ_BITS.get(cfg.weight, 0),
+                          group=cfg.wq_group,
                           w13_zero=_cpu(inp.get("w13_zero")), w2_zero=_cpu(inp.get("w2_zero")))
 
 
@@ -168,6 +170,7 @@ def run_batched(inp: dict, dev, reduce=False, out_dtype=None, packed=False, **ex
     bits = WQ_BITS.get(cfg.weight, 0)
     if bits:
         packed = True
+        kw["wq_group"] = cfg.wq_group
     if packed:
         w13, w2 = B.pack_weights(w13, w2, wq_bits=bits), None
     for name in ("w13_scale", "w2_scale", "w13_bias", "w2_bias", "w13_zero", "w2_zero"):

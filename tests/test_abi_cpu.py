@@ -145,6 +145,13 @@ def _status(prob):
     (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U4, tile_hint=B.MOE_TILE_DMA_64), B.MOE_OK),
     (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U4, tile_hint=B.MOE_TILE_REG_64),
      B.MOE_ERR_UNSUPPORTED),
+    # WNA16 scale groups of 32 / 64 / 128 K rows
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U4, wq_group=32), B.MOE_OK),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U8, wq_group=64), B.MOE_OK),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U8, wq_group=128), B.MOE_OK),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U4, wq_group=16), B.MOE_ERR_UNSUPPORTED),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U4, wq_group=256), B.MOE_ERR_UNSUPPORTED),
+    (dict(wq_group=64), B.MOE_ERR_INVALID_ARG),                            # bf16 weights
 ])
 def test_problem_validation(kw, status):
     assert _status(_prob(**kw)) == status
@@ -335,3 +342,31 @@ def test_static_entry_refuses_problems_beyond_its_array():
         == B.MOE_ERR_INVALID_ARG
     assert lib.moe_forward_static(ctypes.byref(_prob().c()), ctypes.byref(_args(hidden=None)),
                                   None) == B.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 4, 2, 64, 32, 128), B.MOE_OK),
+    ((2, 4, 2, 64, 32, 64), B.MOE_OK),
+    ((1, 8, 2, 64, 32, 32), B.MOE_OK),
+    ((2, 8, 2, 64, 32, 128), B.MOE_ERR_UNSUPPORTED),         # AWQ is 4-bit
+    ((1, 2, 2, 64, 32, 128), B.MOE_ERR_UNSUPPORTED),
+    ((3, 4, 2, 64, 32, 128), B.MOE_ERR_UNSUPPORTED),
+    ((1, 4, 2, 64, 32, 100), B.MOE_ERR_UNSUPPORTED),
+    ((1, 4, 2, 60, 32, 128), B.MOE_ERR_INVALID_ARG),         # GPTQ: K % 8
+    ((2, 4, 2, 64, 36, 128), B.MOE_ERR_INVALID_ARG),         # AWQ: N % 8
+    ((1, 4, 0, 64, 32, 128), B.MOE_ERR_INVALID_ARG),
+])
+def test_repack_validation(args, status):
+    """Argument checks of moe_repack_wna16 on the host (OK cases are checked
+    with null buffers, which fail before any device work)."""
+    lib = B.load()
+    fmt, bits, E, K, N, G = args
+    fake = 4096                               # never dereferenced
+    if status == B.MOE_OK:
+        assert lib.moe_repack_wna16(fmt, bits, E, K, N, G, None, None, 0, fake, None,
+                                    None) == B.MOE_ERR_INVALID_ARG
+        assert lib.moe_repack_wna16(fmt, bits, E, K, N, G, fake, fake, 0, fake, None,
+                                    None) == B.MOE_ERR_INVALID_ARG
+    else:
+        assert lib.moe_repack_wna16(fmt, bits, E, K, N, G, fake, None, 0, fake, None,
+                                    None) == status

@@ -26,6 +26,21 @@ WQ_SMALL = [
     # 256 rows per expert (160-row tiles, two chunks), grouped sigmoid routing
     W.DEEPSEEK_GROUPED.scaled(name="w8_prefill", M=512, H=256, I=256, E=8, top_k=4,
                               group_count=4, k_group=2, weight="u8"),
+    # scale groups of 32 and 64 K rows (GPTQ / AWQ group sizes) on every tile
+    # family; H 352 and I 272 leave short last groups and a stage whose second
+    # 32-row group is past K
+    W.DECODE_SMALL_EXPERTS.scaled(name="w4z_g32_decode", M=8, H=352, I=272, E=32, top_k=4,
+                                  weight="u4", wq_zero=True, wq_group=32),
+    W.DECODE_SMALL_EXPERTS.scaled(name="w8_g64_decode", M=8, H=352, I=272, E=32, top_k=4,
+                                  weight="u8", wq_group=64),
+    W.MIXTRAL_PREFILL.scaled(name="w8z_g32_mid", M=64, H=256, I=384, E=8, weight="u8",
+                             wq_zero=True, bias=True, wq_group=32),
+    W.MIXTRAL_PREFILL.scaled(name="w4_g64_mid", M=64, H=256, I=384, E=8, weight="u4",
+                             wq_group=64),
+    W.DEEPSEEK_GROUPED.scaled(name="w4z_g32_prefill", M=512, H=352, I=272, E=8, top_k=4,
+                              group_count=4, k_group=2, weight="u4", wq_zero=True, wq_group=32),
+    W.DEEPSEEK_GROUPED.scaled(name="w8z_g64_prefill", M=512, H=256, I=256, E=8, top_k=4,
+                              group_count=4, k_group=2, weight="u8", wq_zero=True, wq_group=64),
 ]
 
 
@@ -125,3 +140,51 @@ def test_wna16_full_size_decode(name):
     out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
     ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
     GH.check_output(inp, out, ids_o, w_o, what="full wna16")
+
+
+# GPTQ / AWQ checkpoints: int32 code words -> moe_repack_wna16 -> the packed
+# layout -> the forward, against the oracle's own unpacking of the same words.
+CHECKPOINTS = [("gptq", 4, 128, True, 1), ("gptq", 4, 32, False, 0), ("gptq", 8, 64, True, 1),
+               ("awq", 4, 128, True, 0), ("awq", 4, 64, True, 0), ("awq", 4, 32, False, 0)]
+
+
+@pytest.mark.parametrize("fmt,bits,G,zero,adjust", CHECKPOINTS,
+                         ids=[f"{c[0]}{c[1]}_g{c[2]}{'_z' if c[3] else ''}" for c in CHECKPOINTS])
+def test_checkpoint_codes_repacked(fmt, bits, G, zero, adjust):
+    """Codes and zero points of a synthetic checkpoint (the workload
+    generator's packers write GPTQ / AWQ words; GPTQ with adjust 1 stores
+    z - 1) re-packed on the device equal the oracle's unpacking bit for bit,
+    and the forward on them meets the oracle's bar."""
+    import oracle
+    dev = GH.device()
+    cfg = W.MIXTRAL_PREFILL.scaled(name=f"ckpt_{fmt}{bits}_g{G}", M=48, H=256, I=320, E=8,
+                                   weight=f"u{bits}", wq_zero=zero, wq_group=G)
+    inp = W.make_inputs(cfg, 4200 + bits + G)
+    words = {}
+    for name in ("w13", "w2"):
+        q = inp[name]
+        if bits == 4:                                   # one code a byte for the packer
+            q = torch.stack([q & 15, q >> 4], -1).reshape(*q.shape[:-1], -1)
+        z = inp[f"{name}_zero"]
+        stored = None if z is None else ((z.to(torch.int64) - adjust) % (1 << bits)).to(
+            torch.uint8)
+        words[name] = W.pack_wq_checkpoint(q, stored, bits, fmt)
+    print(f"[case] checkpoint {fmt} bits={bits} group={G} zero={zero}", flush=True)
+    for name, (K, N) in (("w13", (cfg.H, 2 * cfg.I)), ("w2", (cfg.I, cfg.H))):
+        qw, qz = words[name]
+        codes, zeros = B.repack_wna16(fmt, bits, qw.to(dev), None if qz is None else qz.to(dev),
+                                      K=K, N=N, group=G, zero_adjust=adjust)
+        ref_c, ref_z = oracle.unpack_wq(fmt, bits, qw, qzeros=qz, K=K, N=N, group=G,
+                                        zero_adjust=adjust)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes.cpu().numpy(), ref_c), name
+        assert np.array_equal(inp[name].numpy(), ref_c), name      # the generator's codes
+        if zero:
+            assert np.array_equal(zeros.cpu().numpy(), ref_z), name
+            assert np.array_equal(inp[f"{name}_zero"].numpy(), ref_z), name
+        inp[name] = torch.from_numpy(ref_c)
+        if zero:
+            inp[f"{name}_zero"] = torch.from_numpy(ref_z)
+    out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+    ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    GH.check_output(inp, out, ids_o, w_o, what=f"{fmt} checkpoint")
