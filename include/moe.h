@@ -88,7 +88,8 @@ typedef enum {
     MOE_TILE_REG_64 = 2,      /* 64-row register-staged tile (bf16 only)          */
     MOE_TILE_REG_16 = 3,      /* 16-row register-staged tile (bf16 only)          */
     MOE_TILE_DMA_32 = 5,      /* 32-row LDS-DMA ring (decode-sized loads)         */
-    MOE_TILE_DMA_64 = 6       /* 64-row LDS-DMA ring                              */
+    MOE_TILE_DMA_64 = 6,      /* 64-row LDS-DMA ring                              */
+    MOE_TILE_DMA_256 = 7      /* 256-row LDS-DMA ring (bf16 only; compute-bound)  */
 } moe_tile_hint;
 
 /* Bits of the device status word (moe_workspace_info.off_status).  Device-side

@@ -24,7 +24,7 @@ MOE_ROUTE_SOFTMAX, MOE_ROUTE_SIGMOID, MOE_ROUTE_PRECOMPUTED = 0, 1, 2
 MOE_FMT_CONTIGUOUS, MOE_FMT_BATCHED = 0, 1
 MOE_W_PLAIN, MOE_W_PACKED = 0, 1
 MOE_TILE_AUTO, MOE_TILE_DMA_160, MOE_TILE_REG_64, MOE_TILE_REG_16 = 0, 1, 2, 3
-MOE_TILE_DMA_32, MOE_TILE_DMA_64 = 5, 6
+MOE_TILE_DMA_32, MOE_TILE_DMA_64, MOE_TILE_DMA_256 = 5, 6, 7
 MOE_DEV_ID_RANGE, MOE_DEV_COUNT_CLAMPED, MOE_DEV_ROWS_OVERFLOW, MOE_DEV_TOKEN_MAP = 1, 2, 4, 8
 
 EXPORTED = ("moe_workspace_shapes", "moe_forward", "moe_forward_timed", "moe_packed_weight_bytes",

@@ -88,15 +88,17 @@ static int validate(const moe_problem* p)
     // per-call tuning hints (tile family, GEMM1 width); 0 = the library's choice
     const int th = p->tile_hint;
     if (th != MOE_TILE_AUTO && th != MOE_TILE_DMA_160 && th != MOE_TILE_REG_64 &&
-        th != MOE_TILE_REG_16 && th != MOE_TILE_DMA_32 && th != MOE_TILE_DMA_64)
+        th != MOE_TILE_REG_16 && th != MOE_TILE_DMA_32 && th != MOE_TILE_DMA_64 &&
+        th != MOE_TILE_DMA_256)
         return MOE_ERR_INVALID_ARG;
     if (p->gemm1_wave_cols != 0 && p->gemm1_wave_cols != 2 && p->gemm1_wave_cols != 4)
         return MOE_ERR_INVALID_ARG;
     if (th != MOE_TILE_AUTO) {
         if (w != MOE_BF16 && w != MOE_U8 && w != MOE_U4)
             return MOE_ERR_UNSUPPORTED;
-        if (w != MOE_BF16 && (th == MOE_TILE_REG_64 || th == MOE_TILE_REG_16))
-            return MOE_ERR_UNSUPPORTED;   // WNA16 runs the LDS-DMA families only
+        if (w != MOE_BF16 &&
+            (th == MOE_TILE_REG_64 || th == MOE_TILE_REG_16 || th == MOE_TILE_DMA_256))
+            return MOE_ERR_UNSUPPORTED;   // WNA16 runs the 32 / 64 / 160-row DMA families
     }
 
     if (p->global_experts < 0 || p->chunk_tokens < 0 || p->apply_weight_on_input < 0 ||
@@ -165,6 +167,7 @@ static int choose_tile(const moe_problem* p, int64_t rows_cap)
     case MOE_TILE_REG_16: return TILE_DECODE;
     case MOE_TILE_DMA_32: return TILE_DECODE_DMA;
     case MOE_TILE_DMA_64: return TILE_MID_DMA;
+    case MOE_TILE_DMA_256: return TILE_PREFILL_BIG;
     default: break;
     }
     const double avg = (double)rows_cap / p->E;
@@ -174,7 +177,8 @@ static int choose_tile(const moe_problem* p, int64_t rows_cap)
         return TILE_DECODE_DMA;
     if (avg <= 48)
         return TILE_MID;
-    return TILE_PREFILL;
+    // a few hundred rows per expert or more: compute-bound, 256-row tiles
+    return avg >= 384 ? TILE_PREFILL_BIG : TILE_PREFILL;
 }
 
 // Internal workspace regions beyond moe_workspace_info: chunk tables and the

@@ -1273,40 +1273,54 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
         }
         // epilogue: bf16 z of the real rows, staged in the ring slot that no
         // DMA touches before the next tile's first barrier (the prologue
-        // above fills slots 0 .. NS-2), then written as 16-byte row chunks
+        // above fills slots 0 .. NS-2), then written as 16-byte row chunks.
+        // A tile whose z does not fit one slot (256 rows) stages it one row
+        // group at a time.
         constexpr int ZS = S::BN / 2 + 8;               // staged row, bf16 elements
-        static_assert(S::CH * ZS * 2 + S::CH * 4 <= S::STAGE, "z staging fits in one ring slot");
+        constexpr int ZP = (S::CH * ZS * 2 + S::CH * 4 <= S::STAGE) ? 1 : 2;   // passes
+        constexpr int ZR = S::CH / ZP;                  // rows staged per pass
+        static_assert(ZR * ZS * 2 + S::CH * 4 <= S::STAGE, "z staging fits in one ring slot");
+        static_assert(ZP == 1 || ZR == S::FMW * 16, "a pass stages one row group");
         u16* Zs = (u16*)(ring + (S::NS - 1) * S::STAGE);
-        float* rws = (float*)(ring + (S::NS - 1) * S::STAGE + S::CH * ZS * 2);
+        float* rws = (float*)(ring + (S::NS - 1) * S::STAGE + ZR * ZS * 2);
         if (g.row_w) {          // routing weights of the tile's rows, applied to z
             for (int t = threadIdx.x; t < S::CH; t += S::NT)
                 rws[t] = (t < cur.rows) ? gemm1_row_w(g, (int64_t)cur.r0 + t) : 0.0f;
             __syncthreads();
         }
+        constexpr int CPR = S::BN / 16;                 // 16-byte chunks per z row
 #pragma unroll
-        for (int fn = 0; fn < FH; ++fn) {
-            const int zc = (cg * FH + fn) * 16 + s16;
+        for (int pass = 0; pass < ZP; ++pass) {
+            if (ZP == 1 || rg == pass) {
 #pragma unroll
-            for (int fm = 0; fm < FMW; ++fm) {
-                if (rg * FMW + fm >= strips)
-                    continue;
+                for (int fn = 0; fn < FH; ++fn) {
+                    const int zc = (cg * FH + fn) * 16 + s16;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = (rg * FMW + fm) * 16 + g4 * 4 + r;
-                    float zv = silu_mul(acc[fm][fn][r] + bg[fn], acc[fm][fn + FH][r] + bu[fn]);
-                    if (g.row_w)
-                        zv *= rws[row];
-                    Zs[row * ZS + zc] = f32_to_bf16(zv);
+                    for (int fm = 0; fm < FMW; ++fm) {
+                        if (rg * FMW + fm >= strips)
+                            continue;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int row = (rg * FMW + fm) * 16 + g4 * 4 + r;
+                            float zv = silu_mul(acc[fm][fn][r] + bg[fn],
+                                                acc[fm][fn + FH][r] + bu[fn]);
+                            if (g.row_w)
+                                zv *= rws[row];
+                            Zs[(row - pass * ZR) * ZS + zc] = f32_to_bf16(zv);
+                        }
+                    }
                 }
             }
-        }
-        __syncthreads();
-        constexpr int CPR = S::BN / 16;                 // 16-byte chunks per z row
-        for (int q = threadIdx.x; q < cur.rows * CPR; q += S::NT) {
-            const int row = q / CPR, c8 = (q % CPR) * 8;
-            if (n0 + c8 < I)
-                *(i32x4*)((u16*)g.z + ((int64_t)cur.r0 + row) * I + n0 + c8) =
-                    *(const i32x4*)(Zs + row * ZS + c8);
+            __syncthreads();
+            const int r_lo = pass * ZR, nr = min(cur.rows - r_lo, ZR);
+            for (int q = threadIdx.x; q < nr * CPR; q += S::NT) {
+                const int row = q / CPR, c8 = (q % CPR) * 8;
+                if (n0 + c8 < I)
+                    *(i32x4*)((u16*)g.z + ((int64_t)cur.r0 + r_lo + row) * I + n0 + c8) =
+                        *(const i32x4*)(Zs + row * ZS + c8);
+            }
+            if (pass + 1 < ZP)
+                __syncthreads();                        // the next pass reuses the staging rows
         }
         if (!more)
             break;
@@ -1866,6 +1880,12 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, const float* row_w, hi
     if (P.wq == 4)
         return P.wq_gsh ? launch_gemm1_wq<4, 0>(g, P, s) : launch_gemm1_wq<4, 1>(g, P, s);
     switch (P.cfg) {
+    case TILE_PREFILL_BIG:
+        // about a thousand rows per expert: 256 x 256 tiles, 8 waves of
+        // 128 x 64, a 2-stage ring (half the fragment reads per MFMA of the
+        // 160-row tiles)
+        return P.wpacked ? run_gemm1_dma<8, 4, 2, true>(g, P, s)
+                         : run_gemm1_dma<8, 4, 2, false>(g, P, s);
     case TILE_PREFILL:
         // a few tiles per CU (few experts, wide I): 256-column tiles, 8 waves and
         // a 3-stage ring at one workgroup per CU stream the weights fastest;
@@ -1929,6 +1949,9 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
     if (P.wq == 4)
         return P.wq_gsh ? launch_gemm2_wq<4, 0>(g, P, s) : launch_gemm2_wq<4, 1>(g, P, s);
     switch (P.cfg) {
+    case TILE_PREFILL_BIG:
+        return P.wpacked ? run_gemm2_dma<8, 4, 2, true>(g, P, s)
+                         : run_gemm2_dma<8, 4, 2, false>(g, P, s);
     case TILE_PREFILL:
         if (P.g2split) {   // 256-column tiles over two K halves
             g.ksplit = 2;

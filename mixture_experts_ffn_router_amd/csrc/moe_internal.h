@@ -179,7 +179,8 @@ enum {
     TILE_FP8 = 3,          // fp8 register-staged, 128 rows
     TILE_DECODE_DMA = 4,   // LDS-DMA ring, 32 rows
     TILE_MID_DMA = 5,      // LDS-DMA ring, 64 rows
-    TILE_FP8_DMA = 6       // fp8 LDS-DMA ring on packed fp8 weights, F8_ROWS rows
+    TILE_FP8_DMA = 6,      // fp8 LDS-DMA ring on packed fp8 weights, F8_ROWS rows
+    TILE_PREFILL_BIG = 7   // LDS-DMA ring, 256 rows x 256 columns (compute-bound loads)
 };
 constexpr int ALIGN_BM = 16;                 // expert runs are padded to 16 rows
 constexpr int F8_ROWS = 128;                 // rows per tile of the fp8 LDS-DMA GEMMs
@@ -192,6 +193,7 @@ inline int tile_rows(int cfg)
     case TILE_DECODE_DMA: return 32;
     case TILE_MID_DMA: return 64;
     case TILE_FP8_DMA: return F8_ROWS;
+    case TILE_PREFILL_BIG: return 256;
     default: return 16;
     }
 }

@@ -27,7 +27,8 @@ WQ_BITS = {"u8": 8, "u4": 4}
 
 # Named tile families for the tests (moe_problem.tile_hint / gemm1_wave_cols).
 TILES = {"auto": B.MOE_TILE_AUTO, "dma160": B.MOE_TILE_DMA_160, "reg64": B.MOE_TILE_REG_64,
-         "reg16": B.MOE_TILE_REG_16, "dma32": B.MOE_TILE_DMA_32, "dma64": B.MOE_TILE_DMA_64}
+         "reg16": B.MOE_TILE_REG_16, "dma32": B.MOE_TILE_DMA_32, "dma64": B.MOE_TILE_DMA_64,
+         "dma256": B.MOE_TILE_DMA_256}
 
 
 def tile_kwargs(name: str) -> dict:
@@ -225,7 +226,7 @@ def check_rounded(out16: torch.Tensor, out32: torch.Tensor):
 # an expert's rows is one tile's rows.  Sampling the first and last row of
 # every chunk of every height reaches every (expert, row chunk) tile whatever
 # family the library picks, with all its columns.
-CHUNK_HEIGHTS = {"fp8": (128,), "default": (32, 64, 160)}
+CHUNK_HEIGHTS = {"fp8": (128,), "default": (32, 64, 160, 256)}
 
 
 def chunk_positions(counts: np.ndarray, offsets: np.ndarray, heights) -> tuple:

@@ -135,7 +135,7 @@ def _status(prob):
     (dict(tile_hint=B.MOE_TILE_REG_16), B.MOE_OK),
     (dict(tile_hint=B.MOE_TILE_DMA_32, gemm1_wave_cols=2), B.MOE_OK),
     (dict(tile_hint=4), B.MOE_ERR_INVALID_ARG),
-    (dict(tile_hint=7), B.MOE_ERR_INVALID_ARG),
+    (dict(tile_hint=8), B.MOE_ERR_INVALID_ARG),
     (dict(tile_hint=-1), B.MOE_ERR_INVALID_ARG),
     (dict(gemm1_wave_cols=3), B.MOE_ERR_INVALID_ARG),
     (dict(gemm1_wave_cols=4), B.MOE_OK),
@@ -144,6 +144,9 @@ def _status(prob):
           tile_hint=B.MOE_TILE_REG_16), B.MOE_ERR_UNSUPPORTED),
     (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U4, tile_hint=B.MOE_TILE_DMA_64), B.MOE_OK),
     (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U4, tile_hint=B.MOE_TILE_REG_64),
+     B.MOE_ERR_UNSUPPORTED),
+    (dict(tile_hint=B.MOE_TILE_DMA_256), B.MOE_OK),
+    (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U8, tile_hint=B.MOE_TILE_DMA_256),
      B.MOE_ERR_UNSUPPORTED),
     # WNA16 scale groups of 32 / 64 / 128 K rows
     (dict(w_layout=B.MOE_W_PACKED, w_dtype=B.MOE_U4, wq_group=32), B.MOE_OK),

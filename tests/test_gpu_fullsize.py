@@ -115,6 +115,24 @@ def test_full_size_ep8_shard():
     GH.compare(cfg, out.cpu().numpy()[tokens], y, what="ep8 shard")
 
 
+def test_full_size_mixtral_m4096():
+    """The Mixtral-shaped layer at M 4096 (about 1024 rows per expert: the
+    256-row tiles), every tile's rows and a token sample."""
+    cfg = W.MIXTRAL_M4096
+    dev = GH.device()
+    seed = 1100 + W.EXTRA.index(cfg)
+    print(f"[case] {cfg.name} seed={seed} generating", flush=True)
+    inp = W.make_inputs(cfg, seed, device=dev)
+    out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+    ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    assert GH.B.device_status(ws, info) == 0
+    item_tokens = GH.check_tiles_contiguous(inp, ws, info, dev)
+    GH.check_output(inp, out, ids_o, w_o, tokens=_token_sample(cfg.M, item_tokens),
+                    what="full mixtral m4096")
+    out16, _, _ = GH.run_contiguous(inp, dev)
+    GH.check_rounded(out16, out)
+
+
 def test_full_size_block_fp8():
     """The DeepSeek-like layer with block-wise fp8 weights (128 x 128 blocks)
     and in-path per (token, 128 columns) activation quantisation."""

@@ -73,7 +73,7 @@ SMALL_BF16 = [
 ]
 
 
-@pytest.mark.parametrize("tile", ["auto", "dma160", "dma160/wc2", "reg64", "reg16"])
+@pytest.mark.parametrize("tile", ["auto", "dma160", "dma160/wc2", "reg64", "reg16", "dma256"])
 @pytest.mark.parametrize("cfg", SMALL_BF16, ids=[c.name for c in SMALL_BF16])
 def test_packed_equals_plain_small(cfg, tile):
     dev = GH.device()

@@ -165,7 +165,8 @@ def test_batched_bf16_matches_contiguous():
     GH.compare(cfg, out.float().cpu().numpy(), y, "batched bf16 reduce")
 
 
-@pytest.mark.parametrize("tile", ["dma160", "dma160/wc2", "reg64", "reg16", "dma32", "dma64"])
+@pytest.mark.parametrize("tile", ["dma160", "dma160/wc2", "reg64", "reg16", "dma32", "dma64",
+                                  "dma256"])
 @pytest.mark.parametrize("skew", [False, True])
 def test_tile_families_ragged(tile, skew):
     """Every bf16 tile family (160-row DMA ring, 64 / 16-row register-staged,

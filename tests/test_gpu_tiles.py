@@ -63,7 +63,7 @@ def test_bf16_many_chunks_many_tiles(shape):
     ids, w = skewed_routing()
     y = _oracle_y(inp, ids, w, cfg.name)
     outs = {}
-    for tile in ("auto", "dma160/wc2", "dma160/wc4"):
+    for tile in ("auto", "dma160/wc2", "dma160/wc4", "dma256"):
         for packed in (False, True):
             print(f"[case] {cfg.name} tile={tile} packed={packed}", flush=True)
             out, ws, info = GH.run_contiguous(inp, dev, precomputed=(ids, w),
