@@ -619,6 +619,10 @@ __global__ void __launch_bounds__(256) k_gemm2(Gemm2Args g)
 // weight fragment by two.  WC = 2: 128 columns, 4 waves, two workgroups per
 // CU; WC = 4: 256 columns, 8 waves, one workgroup per CU with a deeper ring
 // and half the activation traffic per weight byte.
+// Layout L = 1 (decode-sized loads, a row or two per expert): one row group
+// of WC waves, each with FMW strips (CH = 16 * FMW rows) and two fragments
+// (BN = 32 * WC columns), so every wave shares the single live strip's work
+// instead of the second row group's waves idling.
 //
 // LDS layout of a stage (no padding: a DMA fills 1024 contiguous bytes):
 //   A  [CH rows][128 B]: 16-byte slot s of row r holds K chunk s ^ ((r>>1)&7),
@@ -643,14 +647,16 @@ __global__ void __launch_bounds__(256) k_gemm2(Gemm2Args g)
 // on the float code, then a packed RNE conversion); the small-row tiles feed
 // the raw codes to the MFMAs and apply s and z per group
 // (DmaFrag::raw_codes).
-template <int FMW_, int WC_, int NS_, int Q_ = 0, int G2_ = 0>
+template <int FMW_, int WC_, int NS_, int Q_ = 0, int G2_ = 0, int L_ = 0>
 struct DS {
     static constexpr int FMW = FMW_, WC = WC_, NS = NS_, Q = Q_;
     static constexpr int G2 = G2_;                       // WNA16: two scale groups a stage
-    static constexpr int NW = 2 * WC, NT = 64 * NW;      // waves, threads
-    static constexpr int FN = 4;                         // 16-column fragments per wave
-    static constexpr int CH = 32 * FMW;                  // rows per tile
-    static constexpr int BN = 64 * WC;                   // weight columns per tile
+    static constexpr int L = L_;                         // wave layout (see above)
+    static constexpr int RG = L ? 1 : 2;                 // row groups of waves
+    static constexpr int NW = RG * WC, NT = 64 * NW;     // waves, threads
+    static constexpr int FN = L ? 2 : 4;                 // 16-column fragments per wave
+    static constexpr int CH = 16 * FMW * RG;             // rows per tile
+    static constexpr int BN = 16 * FN * WC;              // weight columns per tile
     static constexpr int NB = BN / 128;                  // 128-column weight blocks per tile
     static constexpr int RB = 256;                       // bytes per weight row of a block
     // bytes of one 128-column weight block per K stage: bf16 rows, or codes
@@ -1199,11 +1205,11 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[S::FMW][S::FN])
 // the next tile's first stages are issued and the current tile's epilogue
 // (bias, SiLU(gate) * up, bf16 z stores straight from the accumulators) runs
 // while they are in flight.
-template <int FMW, int WC, int NS, bool PACKED, int Q = 0, int G2 = 0>
-__global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
+template <int FMW, int WC, int NS, bool PACKED, int Q = 0, int G2 = 0, int L = 0>
+__global__ void __launch_bounds__((DS<FMW, WC, NS, Q, G2, L>::NT), 2)
     k_gemm1_dma(Gemm1Args g)
 {
-    typedef DS<FMW, WC, NS, Q, G2> S;
+    typedef DS<FMW, WC, NS, Q, G2, L> S;
     constexpr int FN = S::FN;
     constexpr int FH = FN / 2;
     __shared__ __attribute__((aligned(16))) char ring[S::RING];
@@ -1330,11 +1336,11 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
 
 // Persistent GEMM2 over this workgroup's tiles, pipelined across tiles like
 // GEMM1; the epilogue (bias, output rows) runs straight from the accumulators.
-template <int FMW, int WC, int NS, bool PACKED, int Q = 0, int G2 = 0>
-__global__ void __launch_bounds__((DS<FMW, WC, NS>::NT), 2)
+template <int FMW, int WC, int NS, bool PACKED, int Q = 0, int G2 = 0, int L = 0>
+__global__ void __launch_bounds__((DS<FMW, WC, NS, Q, G2, L>::NT), 2)
     k_gemm2_dma(Gemm2Args g)
 {
-    typedef DS<FMW, WC, NS, Q, G2> S;
+    typedef DS<FMW, WC, NS, Q, G2, L> S;
     constexpr int FN = S::FN;
     __shared__ __attribute__((aligned(16))) char ring[S::RING];
     const int lane = threadIdx.x & 63;
@@ -1706,14 +1712,14 @@ static hipError_t run_gemm2(const Gemm2Args& a, const Plan& P, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int FMW, int WC, int NS, bool PACKED, int Q = 0, int G2 = 0>
+template <int FMW, int WC, int NS, bool PACKED, int Q = 0, int G2 = 0, int L = 0>
 static hipError_t run_gemm1_dma(const Gemm1Args& a, const Plan& P, hipStream_t s)
 {
-    typedef DS<FMW, WC, NS, Q, G2> S;
+    typedef DS<FMW, WC, NS, Q, G2, L> S;
     constexpr int BNZ = S::BN / 2;
     Gemm1Args g = a;
     g.s.n_tiles = (a.I + BNZ - 1) / BNZ;
-    auto kern = k_gemm1_dma<FMW, WC, NS, PACKED, Q, G2>;
+    auto kern = k_gemm1_dma<FMW, WC, NS, PACKED, Q, G2, L>;
     static std::atomic<int> cached[MAX_DEVICES];
     const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, P, S::NT)),
         block(S::NT);
@@ -1721,13 +1727,13 @@ static hipError_t run_gemm1_dma(const Gemm1Args& a, const Plan& P, hipStream_t s
     return hipGetLastError();
 }
 
-template <int FMW, int WC, int NS, bool PACKED, int Q = 0, int G2 = 0>
+template <int FMW, int WC, int NS, bool PACKED, int Q = 0, int G2 = 0, int L = 0>
 static hipError_t run_gemm2_dma(const Gemm2Args& a, const Plan& P, hipStream_t s)
 {
-    typedef DS<FMW, WC, NS, Q, G2> S;
+    typedef DS<FMW, WC, NS, Q, G2, L> S;
     Gemm2Args g = a;
     g.s.n_tiles = (a.H + S::BN - 1) / S::BN * g.ksplit;
-    auto kern = k_gemm2_dma<FMW, WC, NS, PACKED, Q, G2>;
+    auto kern = k_gemm2_dma<FMW, WC, NS, PACKED, Q, G2, L>;
     static std::atomic<int> cached[MAX_DEVICES];
     const dim3 grid(persistent_grid(kern, (int64_t)P.max_blocks * g.s.n_tiles, cached, P, S::NT)),
         block(S::NT);
@@ -1818,7 +1824,7 @@ template <int Q, int G2>
 static hipError_t launch_gemm1_wq(const Gemm1Args& g, const Plan& P, hipStream_t s)
 {
     switch (P.cfg) {
-    case TILE_DECODE_DMA: return run_gemm1_dma<1, 2, 4, true, Q, G2>(g, P, s);
+    case TILE_DECODE_DMA: return run_gemm1_dma<2, 4, 4, true, Q, G2, 1>(g, P, s);
     case TILE_MID_DMA: return run_gemm1_dma<2, 2, 3, true, Q, G2>(g, P, s);
     default: return run_gemm1_dma<5, 2, 2, true, Q, G2>(g, P, s);
     }
@@ -1828,7 +1834,7 @@ template <int Q, int G2>
 static hipError_t launch_gemm2_wq(const Gemm2Args& g, const Plan& P, hipStream_t s)
 {
     switch (P.cfg) {
-    case TILE_DECODE_DMA: return run_gemm2_dma<1, 2, 4, true, Q, G2>(g, P, s);
+    case TILE_DECODE_DMA: return run_gemm2_dma<2, 4, 4, true, Q, G2, 1>(g, P, s);
     case TILE_MID_DMA: return run_gemm2_dma<2, 2, 3, true, Q, G2>(g, P, s);
     default: return run_gemm2_dma<5, 2, 2, true, Q, G2>(g, P, s);
     }
@@ -1898,8 +1904,8 @@ hipError_t launch_gemm1(const Plan& P, const moe_args& A, const float* row_w, hi
                          : run_gemm1_dma<5, 2, 2, false>(g, P, s);
     case TILE_MID: return run_gemm1<MOE_BF16, 4, 16>(g, P, s);
     case TILE_DECODE_DMA:
-        return P.wpacked ? run_gemm1_dma<1, 2, 4, true>(g, P, s)
-                         : run_gemm1_dma<1, 2, 4, false>(g, P, s);
+        return P.wpacked ? run_gemm1_dma<2, 4, 4, true, 0, 0, 1>(g, P, s)
+                         : run_gemm1_dma<2, 4, 4, false, 0, 0, 1>(g, P, s);
     case TILE_MID_DMA:
         return P.wpacked ? run_gemm1_dma<2, 2, 3, true>(g, P, s)
                          : run_gemm1_dma<2, 2, 3, false>(g, P, s);
@@ -1973,8 +1979,8 @@ hipError_t launch_gemm2(const Plan& P, const moe_args& A, hipStream_t s)
                          : run_gemm2_dma<5, 2, 2, false>(g, P, s);
     case TILE_MID: return run_gemm2<MOE_BF16, 4, 32>(g, P, s);
     case TILE_DECODE_DMA:
-        return P.wpacked ? run_gemm2_dma<1, 2, 4, true>(g, P, s)
-                         : run_gemm2_dma<1, 2, 4, false>(g, P, s);
+        return P.wpacked ? run_gemm2_dma<2, 4, 4, true, 0, 0, 1>(g, P, s)
+                         : run_gemm2_dma<2, 4, 4, false, 0, 0, 1>(g, P, s);
     case TILE_MID_DMA:
         return P.wpacked ? run_gemm2_dma<2, 2, 3, true>(g, P, s)
                          : run_gemm2_dma<2, 2, 3, false>(g, P, s);
