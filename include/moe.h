@@ -439,9 +439,10 @@ int moe_repack_wna16(int format, int bits, int E, int K, int N, int group,
  *   (K), 8 KiB of 8-bit or 4 KiB of 4-bit codes, in the order the GEMM's
  *   bf16 MFMA fragments read them: for column group f (16 columns), K half h
  *   (32 rows) and lane l = 16 a + c (column 16 f + c, rows 32 h + 8 a ..
- *   + 7), the lane's 8 codes are one 8-byte (U8) or 4-byte (U4, code i in
- *   nibble i & 1 of byte i / 2, low nibble first) run at offset
- *   ((2 f + h) * 64 + l) * 8 or * 4.
+ *   + 7), the lane's 8 codes are one 8-byte (U8: code i in byte i) or 4-byte
+ *   (U4: code i in nibble i / 2 + 4 (i & 1) of the little-endian word, so
+ *   bytes 0-3 hold codes (0, 2), (4, 6), (1, 3), (5, 7), low nibble first)
+ *   run at offset ((2 f + h) * 64 + l) * 8 or * 4.
  *   w13: block (e, kt, j), kt < ceil(H / 64), j < ceil(I / 64), j fastest;
  *        block columns 0-63 are gate columns 64 j .., 64-127 up columns
  *        I + 64 j ...

@@ -832,8 +832,9 @@ struct DmaFrag {
 
     // Raw form of a WNA16 fragment for the small-row tiles: the 8 codes as
     // exact bf16 integers, 4-bit ones offset by 128 (bf16 bits 0x4300 | q are
-    // 128 + q, built two at a time with one byte permute and one OR), 8-bit
-    // ones converted through float.  A 64-row K stage lies inside one
+    // 128 + q: after one mask of the low and one of the high nibbles, each
+    // pair is one byte permute of the codes with a register of 0x43 bytes),
+    // 8-bit ones converted through float.  A 64-row K stage lies inside one
     // 128-row scale group, so the stage's products are exactly
     // s (A Q - (z + offset) A 1): P = A Q and the row sums R = A 1 run on the
     // MFMAs and the scale / zero point are applied per stage to the
@@ -842,16 +843,18 @@ struct DmaFrag {
     __device__ __forceinline__ static bf16x8 raw_codes(const char* p)
     {
         if constexpr (S::Q == 4) {
+            // packed order: code i in nibble i / 2 + 4 (i & 1), so lo's bytes
+            // are codes (0, 4, 1, 5) and hi's (2, 6, 3, 7)
             const uint32_t c = *(const uint32_t*)p;
             const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+            const uint32_t k43 = 0x43434343u;
+            // word q = bytes (code 2q, 0x43, code 2q + 1, 0x43); selector bytes
+            // 0-3 pick the code register's bytes, 4 a 0x43 byte
             i32x4 v;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                // bytes (lo_q, 0, hi_q, 0): codes 2q and 2q + 1 in the two halves
-                const uint32_t sel = (uint32_t)q | (0x0Cu << 8) | ((uint32_t)(4 + q) << 16) |
-                                     (0x0Cu << 24);
-                v[q] = (int)(__builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u);
-            }
+            v[0] = (int)__builtin_amdgcn_perm(k43, lo, 0x04020400u);
+            v[1] = (int)__builtin_amdgcn_perm(k43, hi, 0x04020400u);
+            v[2] = (int)__builtin_amdgcn_perm(k43, lo, 0x04030401u);
+            v[3] = (int)__builtin_amdgcn_perm(k43, hi, 0x04030401u);
             return __builtin_bit_cast(bf16x8, v);
         } else {
             const i32x2 c = *(const i32x2*)p;
@@ -873,14 +876,15 @@ struct DmaFrag {
             for (int i = 0; i < 8; ++i)
                 w[i] = fmaf((float)(((uint32_t)c[i >> 2] >> (8 * (i & 3))) & 255u), sc, bz);
         } else {
-            // code i is nibble i & 1 of byte i / 2: even codes from the low
-            // nibbles, odd ones from the high nibbles, byte by byte
+            // code i is nibble i / 2 + 4 (i & 1): lo's bytes hold codes
+            // (0, 4, 1, 5), hi's (2, 6, 3, 7)
             const uint32_t c = *(const uint32_t*)p;
             const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+            constexpr int LO_CODE[4] = {0, 4, 1, 5}, HI_CODE[4] = {2, 6, 3, 7};
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                w[2 * b] = fmaf((float)((lo >> (8 * b)) & 255u), sc, bz);
-                w[2 * b + 1] = fmaf((float)((hi >> (8 * b)) & 255u), sc, bz);
+                w[LO_CODE[b]] = fmaf((float)((lo >> (8 * b)) & 255u), sc, bz);
+                w[HI_CODE[b]] = fmaf((float)((hi >> (8 * b)) & 255u), sc, bz);
             }
         }
         bf16x8 v;
@@ -1566,10 +1570,14 @@ __global__ void __launch_bounds__(256) k_pack_wq(const uint8_t* __restrict__ w, 
             const uint32_t hi = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
             *(i32x2*)(out + q * 8) = i32x2{(int)lo, (int)hi};
         } else {
+            // code i in nibble i / 2 + 4 (i & 1): the low nibbles of bytes
+            // 0 and 2 are codes 0 and 1, their high nibbles codes 2 and 3,
+            // bytes 1 and 3 the same for codes 4-7 (one byte permute then
+            // lays a pair of codes out as two bf16 values, see raw_codes)
             uint32_t v = 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                v |= code[i] << (4 * i);                // code i: nibble i & 1 of byte i / 2
+                v |= code[i] << (4 * (i / 2 + 4 * (i & 1)));
             *(uint32_t*)(out + q * 4) = v;
         }
     }

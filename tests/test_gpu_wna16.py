@@ -78,7 +78,8 @@ def test_wna16_batched():
 def _fragment_order(codes, bits, w13, H, I):
     """numpy reference of the documented packed order: blocks (e, kt, j) of
     128 columns x 64 K rows; lane group ((2 f + h) * 64 + l) holds column
-    16 f + l % 16 and K rows 64 kt + 32 h + 8 (l // 16) + 0..7."""
+    16 f + l % 16 and K rows 64 kt + 32 h + 8 (l // 16) + 0..7 (8-bit: one
+    byte each; 4-bit: row i of the eight in nibble i // 2 + 4 (i % 2))."""
     c = codes.astype(np.int64)
     if bits == 4:
         c = np.stack([c & 15, c >> 4], -1).reshape(*c.shape[:-1], -1)
@@ -108,7 +109,11 @@ def _fragment_order(codes, bits, w13, H, I):
     v = np.concatenate(out)
     if bits == 8:
         return v.astype(np.uint8).ravel()
-    return (v[:, 0::2] | (v[:, 1::2] << 4)).astype(np.uint8).ravel()
+    # 4-bit: code i in nibble i // 2 + 4 * (i % 2) of the lane's 32-bit word
+    word = np.zeros(v.shape[0], np.int64)
+    for i in range(8):
+        word |= v[:, i] << (4 * (i // 2 + 4 * (i % 2)))
+    return word.astype("<u4").view(np.uint8).ravel()
 
 
 @pytest.mark.parametrize("bits", [8, 4])
