@@ -722,10 +722,27 @@ struct DmaTile {
     __device__ __forceinline__ void issue_p(int kt, uint32_t lds, uint32_t spare, int wave,
                                             bool live) const
     {
+        issue_part_p<NT, 0, S::D>(kt, lds, spare, wave, live);
+    }
+
+    // DMAs [J0, J1) of the wave's D for stage kt: the A DMAs first, then the
+    // weight DMAs; the range that ends at D also carries the WNA16 scale DMAs
+    template <int J0, int J1>
+    __device__ __forceinline__ void issue_part(int kt, uint32_t lds, uint32_t spare, int wave,
+                                               bool live) const
+    {
+        issue_part_p<false, J0, J1>(kt, lds, spare, wave, live);
+    }
+
+    template <bool NT, int J0, int J1>
+    __device__ __forceinline__ void issue_part_p(int kt, uint32_t lds, uint32_t spare, int wave,
+                                                 bool live) const
+    {
+        static_assert(0 <= J0 && J0 <= J1 && J1 <= S::D, "DMA range");
         const int lane = threadIdx.x & 63;
         const char* zero = (const char*)g_zero16;
 #pragma unroll
-        for (int j = 0; j < S::A_PW; ++j) {
+        for (int j = J0; j < J1 && j < S::A_PW; ++j) {
             const int i = wave + S::NW * j;
             const int row = 8 * i + (lane >> 3);
             const int c = (lane & 7) ^ ((row >> 1) & 7);
@@ -734,7 +751,8 @@ struct DmaTile {
             dma16(p, (!S::A_SPARE || i < S::A_INS) ? lds + i * 1024 : spare);
         }
 #pragma unroll
-        for (int j = 0; j < S::B_PW; ++j) {
+        for (int jb = (J0 > S::A_PW ? J0 : S::A_PW); jb < J1; ++jb) {
+            const int j = jb - S::A_PW;
             const int i = wave + S::NW * j;
             const int bb = i / S::IPB, k = 4 * (i & 15) + (lane >> 4);
             const char* p = zero;
@@ -764,7 +782,7 @@ struct DmaTile {
             else
                 dma16(p, lds + S::A_BYTES + i * 1024);
         }
-        if constexpr (S::Q != 0) {
+        if constexpr (S::Q != 0 && J1 == S::D) {
             // the group of the stage's first 32 K rows; with G2 the lanes of
             // the second half of each DMA (scales: 32-63, zero points: 8-15)
             // point one group further, which exists while its rows start inside K
@@ -894,12 +912,22 @@ struct DmaFrag {
         return v;
     }
 
-    // the MFMAs of the wave's first NM strips (the others hold only padding)
-    template <int NM>
-    __device__ __forceinline__ void stage(const char* st, int rg, f32x4 (&acc)[S::FMW][S::FN]) const
+    // the MFMAs of the wave's first NM strips (the others hold only padding),
+    // with the D DMAs of the ring's refill issued through issue(lo, hi)
+    template <int NM, typename Issue>
+    __device__ __forceinline__ void stage(const char* st, int rg, f32x4 (&acc)[S::FMW][S::FN],
+                                          Issue&& issue) const
     {
         const char* As = st + rg * S::FMW * 2048;
         const char* Bs = st + S::A_BYTES;
+        // where the refill goes out: a two-stage ring leaves a refill just one
+        // stage to land, and the decode layout is bound by that latency, so
+        // there it goes first; the deeper bf16 prefill rings spread it over the
+        // first half's MFMAs, so that the DMA issue overlaps MFMA work instead
+        // of delaying the stage's first fragment reads
+        constexpr bool SPREAD = S::Q == 0 && S::NS >= 3 && S::L == 0;
+        if constexpr (!SPREAD)
+            issue(IC<0>{}, IC<S::D>{});
         if constexpr (S::Q != 0 && S::FMW <= 2) {
             constexpr float ZDEF = (S::Q == 8) ? 128.0f : 8.0f;
             constexpr int NG = S::G2 ? 2 : 1;            // scale groups in the stage
@@ -1002,6 +1030,22 @@ struct DmaFrag {
 #pragma unroll
             for (int fm = 0; fm < NM; ++fm)
                 a[fm] = __builtin_bit_cast(bf16x8, *(const i32x4*)(As + fm * 2048 + a_off[ks]));
+            if constexpr (SPREAD) {
+                if (ks == 0) {
+                    // one share of the DMAs after each strip's MFMAs
+                    static_for<0, NM>([&](auto fmc) {
+                        constexpr int fm = decltype(fmc)::value;
+#pragma unroll
+                        for (int fn = 0; fn < S::FN; ++fn)
+                            acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[fm], b[fn], acc[fm][fn], 0, 0, 0);
+                        constexpr int lo = fm * S::D / NM, hi = (fm + 1) * S::D / NM;
+                        if constexpr (hi > lo)
+                            issue(IC<lo>{}, IC<hi>{});
+                        __builtin_amdgcn_sched_barrier(0);
+                    });
+                    continue;
+                }
+            }
 #pragma unroll
             for (int fm = 0; fm < NM; ++fm)
 #pragma unroll
@@ -1021,6 +1065,12 @@ struct NtSrc {
                                           bool live) const
     {
         s.template issue_p<true>(kt, lds, spare, wave, live);
+    }
+    template <int J0, int J1>
+    __device__ __forceinline__ void issue_part(int kt, uint32_t lds, uint32_t spare, int wave,
+                                               bool live) const
+    {
+        s.template issue_part_p<true, J0, J1>(kt, lds, spare, wave, live);
     }
 };
 
@@ -1045,10 +1095,12 @@ __device__ __forceinline__ void dma_run(const Src& src, char* ring, int kb, int 
 {
     auto loop = [&](const auto& ss) {
         if constexpr (NM == 0)
-            dma_mainloop<S>(ss, ring, kb, ke, wave, [](const char*) {});
+            dma_mainloop_split<S>(ss, ring, kb, ke, wave,
+                                  [](const char*, auto&& issue) { issue(IC<0>{}, IC<S::D>{}); });
         else
-            dma_mainloop<S>(ss, ring, kb, ke, wave,
-                            [&](const char* st) { fr.template stage<NM>(st, rg, acc); });
+            dma_mainloop_split<S>(ss, ring, kb, ke, wave, [&](const char* st, auto&& issue) {
+                fr.template stage<NM>(st, rg, acc, issue);
+            });
     };
     if constexpr (NM > 0) {
         if (live < NM) {

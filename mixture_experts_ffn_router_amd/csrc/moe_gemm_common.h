@@ -4,6 +4,7 @@
 #pragma once
 
 #include <atomic>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -272,6 +273,49 @@ __device__ __forceinline__ void dma_mainloop(const Src& src, char* ring, int kb,
         slot = (slot == S::NS - 1) ? 0 : slot + 1;
     }
     wait_vmcnt<0>();                                // the fillers land before the ring is reused
+    __syncthreads();
+}
+
+// A compile-time int argument (the bounds of a DMA range).
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// f(IC<i>{}) for i = B .. E - 1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (B < E) {
+        f(IC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// The same ring with the refill handed to compute(stage, issue): compute
+// calls issue(IC<lo>{}, IC<hi>{}) for consecutive ranges that cover the D
+// DMAs of the refill exactly once, where it wants them among its fragment
+// reads and MFMAs.  The refill is the same as dma_mainloop's, only later in
+// the iteration, so one constant wait still serves every iteration.
+template <typename S, typename Src, typename F>
+__device__ __forceinline__ void dma_mainloop_split(const Src& src, char* ring, int kb, int ke,
+                                                   int wave, F&& compute)
+{
+    const uint32_t ring_lds = lds_u32(ring);
+    int slot = 0;                                   // (kt - kb) % NS
+    for (int kt = kb; kt < ke; ++kt) {
+        wait_vmcnt<(S::NS - 2) * S::D>();
+        __syncthreads();
+        const int nx = kt + S::NS - 1;
+        const int nslot = (slot == 0) ? S::NS - 1 : slot - 1;   // (nx - kb) % NS
+        const uint32_t dst = ring_lds + nslot * S::STAGE;
+        const bool live = nx < ke;
+        auto issue = [&](auto lo, auto hi) {
+            src.template issue_part<decltype(lo)::value, decltype(hi)::value>(
+                nx, dst, ring_lds + S::NS * S::STAGE, wave, live);
+        };
+        compute(ring + slot * S::STAGE, issue);
+        slot = (slot == S::NS - 1) ? 0 : slot + 1;
+    }
+    wait_vmcnt<0>();
     __syncthreads();
 }
 
