@@ -103,12 +103,18 @@ __device__ __forceinline__ void route_token(const RouteArgs& R, const float (&s)
     if constexpr (LPT == 64) {
         if (R.G > 1) {
             const int per = R.E / R.G;
-            // lane g < G forms the key of group g
-            KeyVal gkey{0u, 0u, 0.0f};
-            if (lane < R.G) {
-                const float* sg = grow + lane * per;
-                float a = -INFINITY, b = -INFINITY;
-                for (int i = 0; i < per; ++i) {
+            // the two largest logits of each group (a >= b, as a multiset):
+            // Q lanes per group (a power of two, G Q <= 64) each scan every
+            // Q-th logit of it, then the Q pairs merge by shuffles; lane g then
+            // takes group g's pair and forms its key
+            int qs = 0;
+            while ((R.G << (qs + 1)) <= 64)
+                ++qs;
+            const int Q = 1 << qs;
+            float a = -INFINITY, b = -INFINITY;
+            if (lane < (R.G << qs)) {
+                const float* sg = grow + (lane >> qs) * per;
+                for (int i = lane & (Q - 1); i < per; i += Q) {
                     const float v = sg[i];
                     if (v > a) {
                         b = a;
@@ -117,6 +123,16 @@ __device__ __forceinline__ void route_token(const RouteArgs& R, const float (&s)
                         b = v;
                     }
                 }
+            }
+            for (int o = 1; o < Q; o <<= 1) {
+                const float a2 = __shfl_xor(a, o, 64), b2 = __shfl_xor(b, o, 64);
+                b = fmaxf(fminf(a, a2), fmaxf(b, b2));
+                a = fmaxf(a, a2);
+            }
+            a = __shfl(a, (lane << qs) & 63, 64);
+            b = __shfl(b, (lane << qs) & 63, 64);
+            KeyVal gkey{0u, 0u, 0.0f};
+            if (lane < R.G) {
                 float key;
                 if (R.gmode == 0) {
                     key = a;
