@@ -38,6 +38,13 @@
  *     per-device cache of device attributes (compute units, kernel
  *     occupancy), filled on first use with atomic stores.
  *   - The library reads no environment variables.
+ *   - Two builds export this same ABI: libmoe.so, and libmoe_checked.so, a
+ *     bounds-checked build for debugging (moe_version() ends in "checked").
+ *     In the latter every index the kernels take from device data (the GEMM
+ *     tile table, sorted ids behind row gathers and output rows, the reduce's
+ *     row map) is checked against its buffer first; an index outside it is
+ *     not used and sets MOE_DEV_BOUNDS.  With valid inputs both builds give
+ *     the same results bit for bit.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -104,8 +111,12 @@ typedef enum {
                                    [0, max_tokens], clamped into that range       */
     MOE_DEV_ROWS_OVERFLOW = 4,  /* batched slabs hold more valid rows than M *
                                    top_k (with M > 0): nothing was computed       */
-    MOE_DEV_TOKEN_MAP = 8       /* a token_map entry (other than -1) that names no
+    MOE_DEV_TOKEN_MAP = 8,      /* a token_map entry (other than -1) that names no
                                    valid slab row contributed nothing             */
+    MOE_DEV_BOUNDS = 16         /* bounds-checked build (libmoe_checked.so) only:
+                                   a GEMM tile, gathered row or reduce row taken
+                                   from device data fell outside its buffer; that
+                                   tile or row was skipped                        */
 } moe_device_status;
 
 /* Memory layout of w13 / w2 (see moe_pack_weights). */

@@ -7,6 +7,7 @@ this module raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -14,6 +15,7 @@ from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
+LIB_CHECKED_PATH = os.path.join(_HERE, "libmoe_checked.so")
 
 # enums of moe.h
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 0, -1, -2, -3, -4
@@ -26,6 +28,7 @@ MOE_W_PLAIN, MOE_W_PACKED = 0, 1
 MOE_TILE_AUTO, MOE_TILE_DMA_160, MOE_TILE_REG_64, MOE_TILE_REG_16 = 0, 1, 2, 3
 MOE_TILE_DMA_32, MOE_TILE_DMA_64, MOE_TILE_DMA_256 = 5, 6, 7
 MOE_DEV_ID_RANGE, MOE_DEV_COUNT_CLAMPED, MOE_DEV_ROWS_OVERFLOW, MOE_DEV_TOKEN_MAP = 1, 2, 4, 8
+MOE_DEV_BOUNDS = 16             # bounds-checked build only
 
 EXPORTED = ("moe_workspace_shapes", "moe_forward", "moe_forward_timed", "moe_packed_weight_bytes",
             "moe_pack_weights", "moe_forward_static", "moe_repack_wna16", "moe_status_string",
@@ -73,48 +76,71 @@ class MoeError(RuntimeError):
 
 
 _lib: Optional[ctypes.CDLL] = None
+_opened: dict = {}
+
+
+def _open(path: str) -> ctypes.CDLL:
+    """dlopens one build of the library and declares its entry points."""
+    if path in _opened:
+        return _opened[path]
+    try:   # share torch's HIP runtime (same SONAME) when torch is present
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m mixture_experts_ffn_router_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.moe_workspace_shapes.argtypes = [ctypes.POINTER(moe_problem),
+                                         ctypes.POINTER(moe_workspace_info)]
+    lib.moe_workspace_shapes.restype = ctypes.c_int
+    lib.moe_forward.argtypes = [ctypes.POINTER(moe_problem), ctypes.POINTER(moe_args),
+                                ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_timed.argtypes = [ctypes.POINTER(moe_problem), ctypes.POINTER(moe_args),
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.POINTER(ctypes.c_void_p)]
+    lib.moe_forward_timed.restype = ctypes.c_int
+    lib.moe_packed_weight_bytes.argtypes = [ctypes.POINTER(moe_problem),
+                                            ctypes.POINTER(ctypes.c_size_t),
+                                            ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_packed_weight_bytes.restype = ctypes.c_int
+    lib.moe_pack_weights.argtypes = [ctypes.POINTER(moe_problem)] + [ctypes.c_void_p] * 5
+    lib.moe_pack_weights.restype = ctypes.c_int
+    lib.moe_forward_static.argtypes = [ctypes.POINTER(moe_problem), ctypes.POINTER(moe_args),
+                                       ctypes.c_void_p]
+    lib.moe_forward_static.restype = ctypes.c_int
+    lib.moe_repack_wna16.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 2 + [
+        ctypes.c_int] + [ctypes.c_void_p] * 3
+    lib.moe_repack_wna16.restype = ctypes.c_int
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_version.argtypes = []
+    lib.moe_version.restype = ctypes.c_char_p
+    _opened[path] = lib
+    return lib
 
 
 def load() -> ctypes.CDLL:
     """Loads the in-tree libmoe.so; raises if it has not been built."""
     global _lib
     if _lib is None:
-        try:   # share torch's HIP runtime (same SONAME) when torch is present
-            import torch  # noqa: F401
-        except ImportError:
-            pass
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -m mixture_experts_ffn_router_amd.build`")
-        lib = ctypes.CDLL(LIB_PATH)
-        lib.moe_workspace_shapes.argtypes = [ctypes.POINTER(moe_problem),
-                                             ctypes.POINTER(moe_workspace_info)]
-        lib.moe_workspace_shapes.restype = ctypes.c_int
-        lib.moe_forward.argtypes = [ctypes.POINTER(moe_problem), ctypes.POINTER(moe_args),
-                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-        lib.moe_forward.restype = ctypes.c_int
-        lib.moe_forward_timed.argtypes = [ctypes.POINTER(moe_problem), ctypes.POINTER(moe_args),
-                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                          ctypes.POINTER(ctypes.c_void_p)]
-        lib.moe_forward_timed.restype = ctypes.c_int
-        lib.moe_packed_weight_bytes.argtypes = [ctypes.POINTER(moe_problem),
-                                                ctypes.POINTER(ctypes.c_size_t),
-                                                ctypes.POINTER(ctypes.c_size_t)]
-        lib.moe_packed_weight_bytes.restype = ctypes.c_int
-        lib.moe_pack_weights.argtypes = [ctypes.POINTER(moe_problem)] + [ctypes.c_void_p] * 5
-        lib.moe_pack_weights.restype = ctypes.c_int
-        lib.moe_forward_static.argtypes = [ctypes.POINTER(moe_problem), ctypes.POINTER(moe_args),
-                                           ctypes.c_void_p]
-        lib.moe_forward_static.restype = ctypes.c_int
-        lib.moe_repack_wna16.argtypes = [ctypes.c_int] * 6 + [ctypes.c_void_p] * 2 + [
-            ctypes.c_int] + [ctypes.c_void_p] * 3
-        lib.moe_repack_wna16.restype = ctypes.c_int
-        lib.moe_status_string.argtypes = [ctypes.c_int]
-        lib.moe_status_string.restype = ctypes.c_char_p
-        lib.moe_version.argtypes = []
-        lib.moe_version.restype = ctypes.c_char_p
-        _lib = lib
+        _lib = _open(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def checked_library():
+    """Runs the enclosed calls on the bounds-checked build, libmoe_checked.so
+    (same ABI and results; indices taken from device data are checked against
+    their buffers and a miss sets MOE_DEV_BOUNDS in the device status word)."""
+    global _lib
+    prev = load()
+    _lib = _open(LIB_CHECKED_PATH)
+    try:
+        yield _lib
+    finally:
+        _lib = prev
 
 
 def moe_status_string(status: int) -> str:

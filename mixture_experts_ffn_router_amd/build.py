@@ -1,9 +1,14 @@
-"""Builds libmoe.so (HIP, gfx950) in-tree with hipcc.
+"""Builds libmoe.so (HIP, gfx950) in-tree with hipcc, and its bounds-checked
+twin libmoe_checked.so.
 
-Each source is compiled to an object in parallel, then linked into one
-shared library next to this file.  Every HIP compile disables the packed
-fp32 instructions (-packed-fp32-ops); the host pass warns that it does not
-know that feature, which is harmless.
+Each source is compiled to an object in parallel (both variants at once),
+then each variant is linked into one shared library next to this file.  The
+checked variant is compiled with MOE_CHECKED: its kernels check the indices
+they take from device data (tile table, sorted ids, reduce row map) against
+their buffers and report a miss in the device status word (MOE_DEV_BOUNDS)
+instead of making the access.  Every HIP compile disables the packed fp32
+instructions (-packed-fp32-ops); the host pass warns that it does not know
+that feature, which is harmless.
 """
 from __future__ import annotations
 
@@ -19,6 +24,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
+LIB_CHECKED = os.path.join(HERE, "libmoe_checked.so")
+VARIANTS = {"release": ([], LIB), "checked": (["-DMOE_CHECKED"], LIB_CHECKED)}
 SOURCES = ["moe_api.hip", "moe_kernels.hip", "moe_gemm.hip", "moe_gemm_fp8.hip"]
 ARCH = "gfx950"
 
@@ -37,30 +44,39 @@ COMMON_FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
+def _compile(src: str, variant: str, verbose: bool) -> str:
+    out_dir = os.path.join(BUILD_DIR, variant)
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, *VARIANTS[variant][0], "-I", INCLUDE, "-I", CSRC, "-c",
            os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed on {src}")
+        raise RuntimeError(f"hipcc failed on {src} ({variant})")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every HIP source for gfx950 and links libmoe.so (always rebuilds)."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every HIP source for gfx950 and links libmoe.so and
+    libmoe_checked.so (always rebuilds); returns the release library's path."""
+    jobs = [(src, v) for v in VARIANTS for src in SOURCES]
+    for v in VARIANTS:
+        os.makedirs(os.path.join(BUILD_DIR, v), exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], j[1], verbose), jobs))
+    for v, (_, lib) in VARIANTS.items():
+        _link([o for (src, vv), o in zip(jobs, objs) if vv == v], lib, verbose)
     return LIB
 
 

@@ -652,4 +652,4 @@ extern "C" const char* moe_status_string(int status)
     }
 }
 
-extern "C" const char* moe_version(void) { return "0.1.0"; }
+extern "C" const char* moe_version(void) { return CHECKED ? "0.1.0 checked" : "0.1.0"; }

@@ -229,7 +229,7 @@ __device__ __forceinline__ void gemm1_tile(const Gemm1Args& g, char* smem, int e
                 src = p;
             } else {
                 const int sid = g.s.sorted[p];
-                if (sid < g.s.sentinel)
+                if (sid < g.s.sentinel && in_bounds(sid, g.s.sentinel, g.s.status))
                     src = sid / g.a_div;
             }
             if (src >= 0)
@@ -343,7 +343,7 @@ __device__ __forceinline__ void gemm1_tile(const Gemm1Args& g, char* smem, int e
                         sa = g.a_scale[p];
                     } else {
                         const int sid = g.s.sorted[p];
-                        if (sid < g.s.sentinel)
+                        if (sid < g.s.sentinel && in_bounds(sid, g.s.sentinel, g.s.status))
                             sa = g.a_scale[sid / g.a_div];
                     }
                     hg = hg * sa * sg;
@@ -564,7 +564,7 @@ __device__ __forceinline__ void gemm2_tile(const Gemm2Args& g, char* smem, int e
             continue;
         const int64_t p = (int64_t)r0 + row;
         const int sid = g.s.sorted[p];
-        if (sid >= g.s.sentinel)
+        if (sid >= g.s.sentinel || !in_bounds(sid, g.s.sentinel, g.s.status))
             continue;
         const float* src = Os + row * S::O_STRIDE + cl;
         const int64_t dst_row = (g.out_mode == 2) ? p : (int64_t)sid;
@@ -1451,6 +1451,11 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS, Q, G2, L>::NT), 2)
         // batched slabs, to out[e * T + (r0 - base) + row]
         const int64_t dst0 = (g.out_mode == 2) ? (int64_t)cur.r0
                                                : (int64_t)cur.e * g.T + (cur.r0 - cur.base);
+        // (checked build: the output rows must lie in o, or in the slabs)
+        const bool dst_ok =
+            in_bounds(dst0, g.out_mode == 2 ? g.s.cap : (int64_t)g.s.E * g.T, g.s.status) &&
+            in_bounds(dst0 + cur.rows - 1, g.out_mode == 2 ? g.s.cap : (int64_t)g.s.E * g.T,
+                      g.s.status);
         float bias[FN];   // the bias belongs to the first K half only
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
@@ -1476,7 +1481,7 @@ __global__ void __launch_bounds__((DS<FMW, WC, NS, Q, G2, L>::NT), 2)
 #pragma unroll
         for (int fm = 0; fm < FMW; ++fm) {
             const int strip = rg * FMW + fm;
-            if (strip >= strips)
+            if (strip >= strips || !dst_ok)
                 continue;
             const int64_t base = (dst0 + strip * 16) * H;
 #pragma unroll
@@ -1870,6 +1875,9 @@ static Sched make_sched(const Plan& P)
     s.sorted = P.sorted_ids;
     s.sentinel = (int)P.sentinel;
     s.E = P.E;
+    s.cap = P.max_sorted;
+    s.max_chunks = P.max_blocks;
+    s.status = P.status;
     return s;
 }
 

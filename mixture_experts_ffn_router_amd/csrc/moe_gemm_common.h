@@ -46,6 +46,9 @@ struct Sched {
     const int32_t* sorted;
     int sentinel;
     int E, n_tiles;
+    int64_t cap;                // padded positions in the workspace (checked build)
+    int max_chunks;             // entries of chunk_expert (checked build)
+    int32_t* status;            // device status word (checked build)
 };
 
 struct Gemm1Args {
@@ -77,7 +80,7 @@ __device__ __forceinline__ float gemm1_row_w(const Gemm1Args& g, int64_t p)
     if (!g.row_w)
         return 1.0f;
     const int sid = g.s.sorted[p];
-    return sid < g.s.sentinel ? g.row_w[sid] : 0.0f;
+    return (sid < g.s.sentinel && in_bounds(sid, g.s.sentinel, g.s.status)) ? g.row_w[sid] : 0.0f;
 }
 
 struct Gemm2Args {
@@ -147,9 +150,29 @@ struct TileIter {
 
     __device__ __forceinline__ bool next(const Sched& s, TileRef& t)
     {
-        if (L >= hi)
+        // the checked build skips a tile whose expert or rows lie outside the
+        // workspace (the release build's tile table comes from align itself)
+        while (!next_tile(s, t)) {
+        }
+        return t.rows > 0;
+    }
+
+    // false: tile skipped, try the next; true with t.rows == 0: no tiles left
+    __device__ __forceinline__ bool next_tile(const Sched& s, TileRef& t)
+    {
+        if (L >= hi) {
+            t.rows = 0;
+            return true;
+        }
+        if (!in_bounds(L / nt, s.max_chunks, s.status)) {
+            L += per;
             return false;
+        }
         const int e = s.chunk_expert[L / nt];
+        if (!in_bounds(e, s.E, s.status)) {
+            L += per;
+            return false;
+        }
         const int c0 = s.chunk_off[e], nch = s.chunk_off[e + 1] - c0;
         const int local = L - c0 * nt;
         // chunk group: full groups of TILE_GROUP chunks, then the remainder
@@ -173,6 +196,11 @@ struct TileIter {
         t = TileRef{e, base + 16 * u0, min(16 * (q + (j < extra)), cnt - 16 * u0), ntile, base,
                     nch};
         L += per;
+        if constexpr (CHECKED) {
+            if (!(t.rows > 0 && in_bounds(t.r0, s.cap, s.status) &&
+                  in_bounds((int64_t)t.r0 + t.rows - 1, s.cap, s.status)))
+                return false;
+        }
         return true;
     }
 };
@@ -324,7 +352,10 @@ __device__ __forceinline__ void dma_mainloop_split(const Src& src, char* ring, i
 __device__ __forceinline__ int64_t gemm1_src_row(const Gemm1Args& g, int r0, int row)
 {
     const int64_t p = (int64_t)r0 + row;
-    return g.a_ident ? p : (int64_t)(g.s.sorted[p] / g.a_div);
+    if (g.a_ident)
+        return p;
+    const int sid = g.s.sorted[p];
+    return in_bounds(sid, g.s.sentinel, g.s.status) ? (int64_t)(sid / g.a_div) : -1;
 }
 
 // Makes the compiler hold v in a register here.  Values loaded from global

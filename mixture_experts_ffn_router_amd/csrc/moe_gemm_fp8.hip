@@ -612,6 +612,11 @@ __global__ void __launch_bounds__(512, 1) k_gemm2_f8(Gemm2Args g)
         const int strips = (cur.rows + 15) >> 4;
         const int64_t dst0 = (g.out_mode == 2) ? (int64_t)cur.r0
                                                : (int64_t)cur.e * g.T + (cur.r0 - cur.base);
+        // (checked build: the output rows must lie in o, or in the slabs)
+        const bool dst_ok =
+            in_bounds(dst0, g.out_mode == 2 ? g.s.cap : (int64_t)g.s.E * g.T, g.s.status) &&
+            in_bounds(dst0 + cur.rows - 1, g.out_mode == 2 ? g.s.cap : (int64_t)g.s.E * g.T,
+                      g.s.status);
         float sw[4], bias[4];
 #pragma unroll
         for (int fn = 0; fn < 4; ++fn) {
@@ -636,7 +641,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm2_f8(Gemm2Args g)
 #pragma unroll
         for (int fm = 0; fm < S::FMW; ++fm) {
             const int strip = rg * S::FMW + fm;
-            if (strip >= strips)
+            if (strip >= strips || !dst_ok)
                 continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {

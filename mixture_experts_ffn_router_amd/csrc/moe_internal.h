@@ -246,6 +246,34 @@ struct Plan {
                                     // (later chunks of a chunked forward)
 };
 
+// Bounds-checked build (compiled with MOE_CHECKED into libmoe_checked.so):
+// indices that kernels take from device data (the tile table, sorted ids, the
+// reduce's row map) are checked against their buffers, and one outside is
+// skipped and reported in the status word (MOE_DEV_BOUNDS) instead of being
+// accessed.  The release build compiles the checks away: there these indices
+// come from the library's own align and tile-list kernels.
+#ifdef MOE_CHECKED
+constexpr bool CHECKED = true;
+#else
+constexpr bool CHECKED = false;
+#endif
+
+#ifdef __HIPCC__
+// v in [0, n); in the checked build a miss sets MOE_DEV_BOUNDS
+__device__ __forceinline__ bool in_bounds(int64_t v, int64_t n, int32_t* status)
+{
+    if constexpr (!CHECKED) {
+        return true;
+    } else {
+        if (v >= 0 && v < n)
+            return true;
+        if (status)
+            atomicOr(status, (int32_t)MOE_DEV_BOUNDS);
+        return false;
+    }
+}
+#endif
+
 // Row stride of the group-major fp8 z scales: every padded position plus one
 // GEMM tile of rows, so a tile may read its rows' scales as one block.
 inline int64_t zs_ld(int64_t max_sorted) { return max_sorted + 256; }

@@ -1020,7 +1020,7 @@ __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int
                                                 const int32_t* __restrict__ inv,
                                                 const float* __restrict__ o2,
                                                 TOut* __restrict__ out,
-                                                int32_t* __restrict__ status)
+                                                int32_t* __restrict__ status, int64_t cap)
 {
     constexpr int IU = 8 / CPT;             // items in flight together: IU x CPT loads a thread
     const int64_t t = blockIdx.x;
@@ -1051,6 +1051,9 @@ __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ o, int
                     } else {
                         row[u] = inv[t * K + j];
                     }
+                    // (checked build: a row outside o contributes nothing)
+                    if (row[u] >= 0 && !in_bounds(row[u], cap, status))
+                        row[u] = -1;
                     wj[u] = w ? w[t * K + j] : 1.0f;
                 }
             }
@@ -1109,7 +1112,8 @@ static void reduce_launch(const Plan& P, const float* w, const int32_t* tmap, vo
     const dim3 grid((unsigned)P.M), block(256);
 #define MOE_REDUCE(C)                                                                           \
     hipLaunchKernelGGL((k_reduce<TOut, C>), grid, block, 0, s, P.o, P.H, P.K, w, tmap, P.T,    \
-                       P.E, P.offsets, P.counts, P.inv, P.o2, (TOut*)out, P.status)
+                       P.E, P.offsets, P.counts, P.inv, P.o2, (TOut*)out, P.status,        \
+                       P.max_sorted)
     if (per <= 1)
         MOE_REDUCE(1);
     else if (per <= 2)

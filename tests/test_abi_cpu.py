@@ -28,6 +28,39 @@ def test_library_exports_every_declared_function():
     assert B.moe_version().count(".") == 2
 
 
+def test_checked_build_matches_release_abi():
+    """libmoe_checked.so (the bounds-checked build) exports the same entry
+    points, says so in its version, imports no getenv, and sizes workspaces
+    exactly as libmoe.so does."""
+    nm = subprocess.run(["nm", "-D", "--defined-only", B.LIB_CHECKED_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    for name in B.EXPORTED:
+        assert re.search(rf"\bT {name}$", nm, re.M), name
+    und = subprocess.run(["nm", "-D", "--undefined-only", B.LIB_CHECKED_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    assert not re.search(r"\b(secure_)?getenv\b", und)
+    assert not B.moe_version().endswith("checked")
+    probs = [_prob(M=96, H=256, I=1040, E=4, top_k=2),
+             _prob(M=64, H=512, I=256, E=8, top_k=2, w_layout=B.MOE_W_PACKED,
+                   w_dtype=B.MOE_FP8_E4M3FN, fp8_block=128)]
+    release = [B.moe_workspace_shapes(p.c()) for p in probs]
+    with B.checked_library():
+        assert B.moe_version().endswith("checked")
+        checked = [B.moe_workspace_shapes(p.c()) for p in probs]
+    assert not B.moe_version().endswith("checked")
+    for r, c in zip(release, checked):
+        assert bytes(r) == bytes(c)
+
+
+def test_device_status_bits_match_header():
+    body = re.search(r"typedef enum \{(.*?)\} moe_device_status;", open(HEADER).read(), re.S)
+    vals = dict(re.findall(r"(MOE_DEV_\w+)\s*=\s*(\d+)", body.group(1)))
+    assert {k: int(v) for k, v in vals.items()} == {
+        "MOE_DEV_ID_RANGE": B.MOE_DEV_ID_RANGE, "MOE_DEV_COUNT_CLAMPED": B.MOE_DEV_COUNT_CLAMPED,
+        "MOE_DEV_ROWS_OVERFLOW": B.MOE_DEV_ROWS_OVERFLOW, "MOE_DEV_TOKEN_MAP": B.MOE_DEV_TOKEN_MAP,
+        "MOE_DEV_BOUNDS": B.MOE_DEV_BOUNDS}
+
+
 def test_struct_layout_matches_header(tmp_path):
     fields = {"moe_problem": B.moe_problem, "moe_workspace_info": B.moe_workspace_info,
               "moe_args": B.moe_args}
