@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import gpu_harness as GH
+from mixture_experts_ffn_router_amd import binding as B
 from mixture_experts_ffn_router_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -83,6 +84,37 @@ def test_edge_cases(case):
         out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
         ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
         GH.check_output(inp, out, ids_o, w_o, what=case)
+
+
+EDGE_FORMATS = {"fp8": dict(weight="fp8"), "fp8_block": dict(weight="fp8", fp8_block=128),
+                "w4z": dict(weight="u4", wq_zero=True), "w8": dict(weight="u8")}
+
+
+@pytest.mark.parametrize("case", ["one_token", "topk_equals_E", "all_to_one_expert"])
+@pytest.mark.parametrize("fmt", list(EDGE_FORMATS))
+def test_edge_cases_quantised(case, fmt):
+    """The edge cases above on every quantised weight format: a single token,
+    top_k = E (every expert active), and all items on two experts (the rest
+    empty) against the oracle."""
+    dev = GH.device()
+    base = W.MIXTRAL_PREFILL.scaled(name=f"{case}_{fmt}", M=40, H=256, I=256, E=8,
+                                    **EDGE_FORMATS[fmt])
+    cfg = {"one_token": base.scaled(M=1), "topk_equals_E": base.scaled(E=4, top_k=4)}.get(
+        case, base)
+    inp = W.make_inputs(cfg, 33 + list(EDGE_FORMATS).index(fmt))
+    print(f"[case] edge {case} {fmt}", flush=True)
+    if case == "all_to_one_expert":
+        ids = np.stack([np.full(cfg.M, 5), np.full(cfg.M, 6)], 1).astype(np.int32)
+        w = np.random.default_rng(4).random((cfg.M, cfg.top_k)).astype(np.float32)
+        out, ws, info = GH.run_contiguous(inp, dev, precomputed=(ids, w),
+                                          out_dtype=torch.float32)
+        GH.check_routing_and_align(inp, ws, info, ids_o=ids, w_o=w.astype(np.float64))
+        GH.check_output(inp, out, ids, w.astype(np.float64), what=f"{case} {fmt}")
+    else:
+        out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
+        ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+        GH.check_output(inp, out, ids_o, w_o, what=f"{case} {fmt}")
+    assert B.device_status(ws, info) == 0
 
 
 def test_inplace_and_deterministic():
