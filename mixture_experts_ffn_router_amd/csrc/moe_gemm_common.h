@@ -108,9 +108,10 @@ struct Gemm2Args {
 
 // ---------------------------------------------------------------- tile schedule
 // Persistent, XCD-aware schedule.  Workgroups are dealt round-robin over the
-// 8 XCDs (workgroup b runs on XCD b % 8), so XCD x is given the contiguous
-// range [x R/8, (x+1) R/8) of the R logical tiles and walks it with its own
-// workgroups: neighbouring tiles run together on one XCD and share its L2.
+// 8 XCDs (workgroup b runs on XCD b % 8), so XCD x is given a contiguous
+// eighth of the R logical tiles (whole row chunks when there are many) and
+// walks it with its own workgroups: neighbouring tiles run together on one
+// XCD and share its L2.
 //
 // Sharing through L2 only works between tiles that stream the same operand
 // within a few K stages of each other (at full HBM rate an XCD's 4 MB L2
@@ -140,11 +141,24 @@ struct TileIter {
     __device__ __forceinline__ explicit TileIter(const Sched& s)
     {
         nt = s.n_tiles;
-        const int R = s.chunk_off[s.E] * nt;
+        const int C = s.chunk_off[s.E];
         const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
         per = gridDim.x >> 3;
-        const int lo = (int)(((int64_t)R * xcd) >> 3);
-        hi = (int)(((int64_t)R * (xcd + 1)) >> 3);
+        // with 64 row chunks or more, XCD x takes whole chunks (all their
+        // column tiles): a chunk's tiles then never straddle two XCDs' ranges,
+        // and where an XCD's workgroups are a multiple of the column tiles
+        // (the DeepSeek-like layer's W13 GEMM: 32 and 16) never two of its
+        // rounds, so its activation rows are fetched once per round.  Fewer
+        // chunks are shared out by tiles, for balance.
+        int lo;
+        if (C >= 64) {
+            lo = (int)(((int64_t)C * xcd) >> 3) * nt;
+            hi = (int)(((int64_t)C * (xcd + 1)) >> 3) * nt;
+        } else {
+            const int R = C * nt;
+            lo = (int)(((int64_t)R * xcd) >> 3);
+            hi = (int)(((int64_t)R * (xcd + 1)) >> 3);
+        }
         L = lo + slot;
     }
 
