@@ -112,13 +112,30 @@ struct F8Src {
 
     // NT: the weight DMAs with the non-temporal policy
     template <bool NT>
-    __device__ __forceinline__ void issue_p(int kt, uint32_t lds, uint32_t, int wave,
+    __device__ __forceinline__ void issue_p(int kt, uint32_t lds, uint32_t spare, int wave,
                                             bool live) const
     {
+        issue_part_p<NT, 0, S::D>(kt, lds, spare, wave, live);
+    }
+
+    template <int J0, int J1>
+    __device__ __forceinline__ void issue_part(int kt, uint32_t lds, uint32_t spare, int wave,
+                                               bool live) const
+    {
+        issue_part_p<false, J0, J1>(kt, lds, spare, wave, live);
+    }
+
+    // DMAs [J0, J1) of the wave's D for stage kt: the A DMAs first, then the
+    // weight DMAs; the range that ends at D also carries the scale DMAs
+    template <bool NT, int J0, int J1>
+    __device__ __forceinline__ void issue_part_p(int kt, uint32_t lds, uint32_t, int wave,
+                                                 bool live) const
+    {
+        static_assert(0 <= J0 && J0 <= J1 && J1 <= S::D, "DMA range");
         const int lane = threadIdx.x & 63;
         const char* zero = (const char*)g_zero16;
 #pragma unroll
-        for (int j = 0; j < S::A_PW; ++j) {
+        for (int j = J0; j < J1 && j < S::A_PW; ++j) {
             const int i = wave + S::NW * j;
             const int row = 8 * i + (lane >> 3);
             const int c = f8_chunk(lane & 7, row);
@@ -126,7 +143,8 @@ struct F8Src {
             dma16(ok ? ap[j] + kt * 128 : zero, lds + i * 1024);
         }
 #pragma unroll
-        for (int j = 0; j < S::B_PW; ++j) {
+        for (int jb = (J0 > S::A_PW ? J0 : S::A_PW); jb < J1; ++jb) {
+            const int j = jb - S::A_PW;
             const int i = wave + S::NW * j;          // block i >> 4 == j >> 1 (wave < 8)
             const char* w = wb[(j * S::NW) >> 4];
             const char* p = (live && w) ? w + kt * w_stage + (i & 15) * 1024 + lane * 16 : zero;
@@ -135,6 +153,8 @@ struct F8Src {
             else
                 dma16(p, lds + S::A_BYTES + i * 1024);
         }
+        if constexpr (J1 < S::D)
+            return;
         if constexpr (ZS) {
             if (wave == 0)
                 dma16(live ? zs + kt * zs_stage : zero, lds + S::A_BYTES + S::B_BYTES);
@@ -176,9 +196,12 @@ __device__ __forceinline__ f32x4 mma_f8(const i32x8& a, const i32x8& b, const f3
 // scaled by the row's activation block scale times the weight block scale
 // of its columns (GEMM1: fragments 0, 1 are gate columns, 2, 3 up columns;
 // GEMM2: the wave's 64 columns lie in block bcol[0] / 128 of the tile).
-template <bool ZS, bool BW, int NM>
+// The D DMAs of the ring's refill go out through issue(lo, hi), one share
+// after each strip's MFMAs, so that their issue overlaps MFMA work instead
+// of delaying the stage's fragment reads.
+template <bool ZS, bool BW, int NM, typename Issue>
 __device__ __forceinline__ void f8_stage(const char* st, int rg, const int (&bcol)[4], int lane,
-                                         f32x4 (&acc)[F8_ROWS / 32][4])
+                                         f32x4 (&acc)[F8_ROWS / 32][4], Issue&& issue)
 {
     typedef F8S<ZS, BW> S;
     const int s16 = lane & 15, g = lane >> 4;
@@ -189,6 +212,29 @@ __device__ __forceinline__ void f8_stage(const char* st, int rg, const int (&bco
 #pragma unroll
     for (int fn = 0; fn < S::FN; ++fn)
         b[fn] = f8_frag(Bs + bcol[fn] * 128, s16, g);
+    // strip fm's A fragment is read before strip fm - 1's MFMAs (two held at a time)
+    i32x8 a[2];
+    a[0] = f8_frag(As, s16, g);
+    auto next_a = [&](auto fmc) {
+        constexpr int fm = decltype(fmc)::value;
+        if constexpr (fm + 1 < NM)
+            a[(fm + 1) & 1] = f8_frag(As + (fm + 1) * 2048, s16, g);
+    };
+    // one share of the refill after strip fm's MFMAs (SPREAD: the plain
+    // GEMM1), else the whole refill first: the scaled stages run out of
+    // registers holding the DMA addresses across their MFMAs, and GEMM2
+    // measured no faster spread
+    constexpr bool SPREAD = !BW && !ZS;
+    if constexpr (!SPREAD)
+        issue(IC<0>{}, IC<S::D>{});
+    auto share = [&](auto fmc) {
+        constexpr int fm = decltype(fmc)::value;
+        constexpr int lo = fm * S::D / NM, hi = (fm + 1) * S::D / NM;
+        if constexpr (SPREAD && hi > lo)
+            issue(IC<lo>{}, IC<hi>{});
+        if constexpr (SPREAD)
+            __builtin_amdgcn_sched_barrier(0);
+    };
     if constexpr (ZS) {
         // GEMM2's scaled products: strip fm's are scaled and accumulated after
         // strip fm + 1's MFMAs are issued, so the VALU never waits on a
@@ -197,35 +243,22 @@ __device__ __forceinline__ void f8_stage(const char* st, int rg, const int (&bco
         // block-scaled GEMM1 keeps the direct order: the extra products
         // would not fit its registers.)
         f32x4 tp[S::FN], s0p, s1p;
-#pragma unroll
-        for (int fm = 0; fm < NM; ++fm) {
-            const i32x8 a = f8_frag(As + fm * 2048, s16, g);
+        static_for<0, NM>([&](auto fmc) {
+            constexpr int fm = decltype(fmc)::value;
             const int row0 = rg * S::FMW * 16 + fm * 16 + g * 4;
-            f32x4 s0, s1;
-            if constexpr (ZS) {
-                f32x4 sz = *(const f32x4*)(Ss + row0 * 4);
-                if constexpr (BW) {
-                    const float sw = *(const float*)(Ss + S::SW_OFF + (bcol[0] >> 7) * 4);
+            f32x4 sz = *(const f32x4*)(Ss + row0 * 4);
+            if constexpr (BW) {
+                const float sw = *(const float*)(Ss + S::SW_OFF + (bcol[0] >> 7) * 4);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        sz[r] *= sw;
-                }
-                s0 = s1 = sz;
-            } else {
-                const f32x4 sa = *(const f32x4*)(Ss + S::SA_OFF + row0 * 4);
-                const float swg = *(const float*)(Ss + S::SW_OFF);
-                const float swu = *(const float*)(Ss + S::SW_OFF + 4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    s0[r] = sa[r] * swg;
-                    s1[r] = sa[r] * swu;
-                }
+                for (int r = 0; r < 4; ++r)
+                    sz[r] *= sw;
             }
+            next_a(fmc);
             f32x4 t[S::FN];
 #pragma unroll
             for (int fn = 0; fn < S::FN; ++fn)
-                t[fn] = mma_f8(a, b[fn], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-            if (fm > 0) {
+                t[fn] = mma_f8(a[fm & 1], b[fn], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+            if constexpr (fm > 0) {
 #pragma unroll
                 for (int fn = 0; fn < S::FN; ++fn)
 #pragma unroll
@@ -235,18 +268,18 @@ __device__ __forceinline__ void f8_stage(const char* st, int rg, const int (&bco
 #pragma unroll
             for (int fn = 0; fn < S::FN; ++fn)
                 tp[fn] = t[fn];
-            s0p = s0;
-            s1p = s1;
-        }
+            s0p = sz;
+            s1p = sz;
+            share(fmc);
+        });
 #pragma unroll
         for (int fn = 0; fn < S::FN; ++fn)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 acc[NM - 1][fn][r] += tp[fn][r] * (fn < S::FN / 2 ? s0p[r] : s1p[r]);
     } else if constexpr (BW) {
-#pragma unroll
-        for (int fm = 0; fm < NM; ++fm) {
-            const i32x8 a = f8_frag(As + fm * 2048, s16, g);
+        static_for<0, NM>([&](auto fmc) {
+            constexpr int fm = decltype(fmc)::value;
             const int row0 = rg * S::FMW * 16 + fm * 16 + g * 4;
             const f32x4 sa = *(const f32x4*)(Ss + S::SA_OFF + row0 * 4);
             const float swg = *(const float*)(Ss + S::SW_OFF);
@@ -257,22 +290,25 @@ __device__ __forceinline__ void f8_stage(const char* st, int rg, const int (&bco
                 fg[r] = sa[r] * swg;
                 fu[r] = sa[r] * swu;
             }
+            next_a(fmc);
 #pragma unroll
             for (int fn = 0; fn < S::FN; ++fn) {
-                const f32x4 t = mma_f8(a, b[fn], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                const f32x4 t = mma_f8(a[fm & 1], b[fn], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     acc[fm][fn][r] += t[r] * (fn < S::FN / 2 ? fg[r] : fu[r]);
             }
-        }
+            share(fmc);
+        });
     } else {
-#pragma unroll
-        for (int fm = 0; fm < NM; ++fm) {
-            const i32x8 a = f8_frag(As + fm * 2048, s16, g);
+        static_for<0, NM>([&](auto fmc) {
+            constexpr int fm = decltype(fmc)::value;
+            next_a(fmc);
 #pragma unroll
             for (int fn = 0; fn < S::FN; ++fn)
-                acc[fm][fn] = mma_f8(a, b[fn], acc[fm][fn]);
-        }
+                acc[fm][fn] = mma_f8(a[fm & 1], b[fn], acc[fm][fn]);
+            share(fmc);
+        });
     }
 }
 
@@ -284,6 +320,12 @@ struct F8NtSrc {
                                           bool live) const
     {
         s.template issue_p<true>(kt, lds, spare, wave, live);
+    }
+    template <int J0, int J1>
+    __device__ __forceinline__ void issue_part(int kt, uint32_t lds, uint32_t spare, int wave,
+                                               bool live) const
+    {
+        s.template issue_part_p<true, J0, J1>(kt, lds, spare, wave, live);
     }
 };
 
@@ -308,10 +350,11 @@ __device__ __forceinline__ void f8_run(const F8Src<ZS, BW>& src, char* ring, int
     typedef F8S<ZS, BW> S;
     auto loop = [&](const auto& ss) {
         if constexpr (NM == 0)
-            dma_mainloop<S>(ss, ring, 0, nk, wave, [](const char*) {});
+            dma_mainloop_split<S>(ss, ring, 0, nk, wave,
+                                  [](const char*, auto&& issue) { issue(IC<0>{}, IC<S::D>{}); });
         else
-            dma_mainloop<S>(ss, ring, 0, nk, wave, [&](const char* st) {
-                f8_stage<ZS, BW, NM>(st, rg, bcol, lane, acc);
+            dma_mainloop_split<S>(ss, ring, 0, nk, wave, [&](const char* st, auto&& issue) {
+                f8_stage<ZS, BW, NM>(st, rg, bcol, lane, acc, issue);
             });
     };
     if constexpr (NM > 0) {
