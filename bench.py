@@ -34,6 +34,11 @@ sys.path.insert(0, ROOT)
 METRIC = "fused-MoE fwd tokens/s + active TFLOP/s (or HBM GB/s), % of roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}
+# the largest configuration that fits one GPU: the headline
+DEFAULT_WORKLOAD = "deepseek_grouped_sigmoid_bf16"
+# the other problem configurations, summarised in the default line
+OTHER_CONFIGS = ("tiny_f32", "mixtral_prefill_bf16", "decode_e128_bf16", "batched_fp8_skewed")
+OTHER_STEPS, OTHER_WARMUP = 10, 3
 
 
 def parse():
@@ -41,11 +46,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="deepseek_grouped_sigmoid_bf16")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="tokens (or batched rows) the CPU oracle leg computes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="time the default workload only (no per-configuration summaries)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB, 5 times (the "
                          "reference point for scaling HBM byte counters), then exit")
@@ -111,7 +118,46 @@ def main():
         print(json.dumps({"copy_probe_bytes": src.numel(), "launches": 5}), flush=True)
         return
     cfg = W.BY_NAME[args.workload]
-    seed = args.seed if args.seed is not None else (
+    res, inp, info = measure(cfg, args.steps, args.warmup, args.seed, time_plain=True)
+
+    # ---- the other problem configurations, fewer steps each (default run only):
+    # one summary per workload in the same line, so that every configuration's
+    # throughput and roofline fraction is measured by the same invocation
+    if args.workload == DEFAULT_WORKLOAD and not args.no_other_configs:
+        res["configs"] = {}
+        for name in OTHER_CONFIGS:
+            torch.cuda.empty_cache()
+            r, _, _ = measure(W.BY_NAME[name], OTHER_STEPS, OTHER_WARMUP, None, time_plain=False)
+            res["configs"][name] = summary(r)
+        torch.cuda.empty_cache()
+
+    # ---- CPU oracle leg (rank 0, N = 1 only)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, info, args.cpu_sample)
+    print(json.dumps(res), flush=True)
+
+
+def summary(r):
+    """The figures of one workload's measurement kept in the headline line."""
+    roof = r["roofline"]
+    return {"ms_per_step": r["ms_per_step"], "tokens_per_s": r["value"], "steps": r["steps"],
+            "dtype": r["dtype"], "stage_ms": r["stage_ms"],
+            "gemm1": {k: roof[k] for k in ("bound", "achieved", "peak", "unit", "frac",
+                                           "kernel")},
+            "path_roofline_frac": r["path_roofline"]["frac"],
+            "active_tflops": r["active_tflops"], "hbm_gbs_path": r["hbm_gbs_path"]}
+
+
+def measure(cfg, steps, warmup, seed, time_plain):
+    """Times `steps` forwards of workload `cfg` after `warmup` untimed ones;
+    returns (result dict, inputs, workspace info)."""
+    import numpy as np
+    import torch
+    from mixture_experts_ffn_router_amd import binding as B
+    from mixture_experts_ffn_router_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    seed = seed if seed is not None else (
         1000 + W.CONFIGS.index(cfg) if cfg in W.CONFIGS else 1100 + W.EXTRA.index(cfg))
     print(f"[bench] {cfg.name}: generating inputs (seed {seed})", file=sys.stderr, flush=True)
     inp = W.make_inputs(cfg, seed, device=dev)
@@ -194,22 +240,22 @@ def main():
             B.moe_forward(p, a, ws.data_ptr(), ws.numel(), stream)
 
     # ---- warmup
-    run_steps(cprob, cargs, args.warmup)
+    run_steps(cprob, cargs, warmup)
     torch.cuda.synchronize()
 
     # ---- timed steps: K back-to-back forwards between two synchronisations
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run_steps(cprob, cargs, args.steps)
+    run_steps(cprob, cargs, steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / steps
 
     # ---- the same steps again with HIP events on the launch stream around
     # every step and every kernel stage (per-kernel durations, roofline)
-    step_ev = [(hip.create(), hip.create()) for _ in range(args.steps)]
-    stage_ev = [[hip.create() for _ in range(2 * nst)] for _ in range(args.steps)]
-    for k in range(args.steps):
+    step_ev = [(hip.create(), hip.create()) for _ in range(steps)]
+    stage_ev = [[hip.create() for _ in range(2 * nst)] for _ in range(steps)]
+    for k in range(steps):
         rec(ctypes.c_void_p(step_ev[k][0]), ctypes.c_void_p(stream))
         B.moe_forward_timed(cprob, cargs, ws.data_ptr(), ws.numel(), stream, stage_ev[k])
         rec(ctypes.c_void_p(step_ev[k][1]), ctypes.c_void_p(stream))
@@ -225,13 +271,13 @@ def main():
 
     # ---- plain weight layout, for reference (same steps, same clock)
     plain_ms = None
-    if pack_ms is not None and layout0 == B.MOE_W_PLAIN:   # some forms run packed only
+    if time_plain and pack_ms is not None and layout0 == B.MOE_W_PLAIN:   # some run packed only
         run_steps(plain_prob, plain_args, 2)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        run_steps(plain_prob, plain_args, args.steps)
+        run_steps(plain_prob, plain_args, steps)
         torch.cuda.synchronize()
-        plain_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        plain_ms = (time.perf_counter() - t0) * 1e3 / steps
     hip.close()
 
     # ---- accounting
@@ -322,7 +368,7 @@ def main():
     value = tokens / (ms_per_step * 1e-3)
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3", "u8": "w8a16_bf16",
                   "u4": "w4a16_bf16"}[cfg.weight],
@@ -350,10 +396,7 @@ def main():
         "roofline": roof,
     }
 
-    # ---- CPU oracle leg (rank 0, N = 1 only)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, info, args.cpu_sample)
-    print(json.dumps(res), flush=True)
+    return res, inp, info
 
 
 GEMM_SOURCES = ("moe_gemm_common.h", "moe_gemm.hip", "moe_gemm_fp8.hip")
