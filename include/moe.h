@@ -294,7 +294,10 @@ typedef struct {
  * MOE_ERR_UNSUPPORTED (same checks as moe_forward). */
 int moe_workspace_shapes(const moe_problem* p, moe_workspace_info* info);
 
-/* Device pointers of one forward (host struct; NULL where unused).
+/* Device pointers of one forward (host struct; NULL where unused).  A
+ * contiguous forward with M = 0 reads and writes no token array: hidden,
+ * out, router_logits and topk_ids / topk_weights may then be NULL, and it
+ * returns MOE_OK with nothing enqueued.
  *   hidden            contiguous [M, H]; batched [E, max_tokens, H]
  *                     (rows past expert_num_tokens[e] are never read).
  *   a_scale           batched fp8 activations: [E, max_tokens] per-row scales,

@@ -327,9 +327,12 @@ static Plan make_plan(const moe_problem* p, const moe_workspace_info& w, char* w
 
 static int check_args(const moe_problem* p, const moe_args* a)
 {
-    if (!a || !a->w13 || !a->w2 || !a->out)
+    if (!a || !a->w13 || !a->w2)
         return MOE_ERR_INVALID_ARG;
-    if (!a->hidden)
+    // a contiguous forward of no tokens touches no token array (they have no
+    // rows and may be null)
+    const bool no_tokens = p->format == MOE_FMT_CONTIGUOUS && p->M == 0;
+    if (!no_tokens && (!a->out || !a->hidden))
         return MOE_ERR_INVALID_ARG;
     if ((p->has_w13_bias && !a->w13_bias) || (p->has_w2_bias && !a->w2_bias))
         return MOE_ERR_INVALID_ARG;
@@ -350,6 +353,8 @@ static int check_args(const moe_problem* p, const moe_args* a)
     }
     if (p->global_experts > 0 && !a->expert_map)
         return MOE_ERR_INVALID_ARG;
+    if (no_tokens)
+        return MOE_OK;
     if (p->routing == MOE_ROUTE_PRECOMPUTED) {
         if (!a->topk_ids || !a->topk_weights)
             return MOE_ERR_INVALID_ARG;

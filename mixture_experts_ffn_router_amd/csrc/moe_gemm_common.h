@@ -37,6 +37,53 @@ __device__ __forceinline__ float silu_mul(float g, float u)
 // a code by one step only where z / scale lies within an ulp of a rounding tie.
 __device__ __forceinline__ float zq_scale(float amax) { return (amax > 0.0f) ? amax / 448.0f : 1.0f; }
 
+// 4 x 4 transpose inside each quad of lanes (two DPP butterflies): lane
+// 4a + q holding v[r] = X[r][q] (column q of the quad's 4 x 4 block, row r)
+// ends up holding v[c] = X[q][c] (row q, columns c).  A 16 x 16 MFMA result
+// fragment then gives every lane four consecutive columns of one row, which
+// it stores as one 16-byte (float) or 8-byte (bf16) row piece.  Every lane
+// of the quad must be active.
+__device__ __forceinline__ float dpp_xor1(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor2(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ void quad_transpose(f32x4& v, int lane)
+{
+    const bool odd = lane & 1, hi = lane & 2;
+    // lanes q, q ^ 1 swap the elements whose index parity differs from theirs
+    float r0 = dpp_xor1(odd ? v[0] : v[1]), r1 = dpp_xor1(odd ? v[2] : v[3]);
+    v[0] = odd ? r0 : v[0];
+    v[1] = odd ? v[1] : r0;
+    v[2] = odd ? r1 : v[2];
+    v[3] = odd ? v[3] : r1;
+    // lanes q, q ^ 2 the same for bit 1
+    r0 = dpp_xor2(hi ? v[0] : v[2]);
+    r1 = dpp_xor2(hi ? v[1] : v[3]);
+    v[0] = hi ? r0 : v[0];
+    v[2] = hi ? v[2] : r0;
+    v[1] = hi ? r1 : v[1];
+    v[3] = hi ? v[3] : r1;
+}
+
+// Four consecutive output values of one row: 16 bytes of float, or 8 bytes
+// of bf16 (round to nearest even), at element index o of out.
+__device__ __forceinline__ void store_row4(void* out, int64_t o, bool bf16, const f32x4& v)
+{
+    if (bf16) {
+        const uint32_t lo = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *(i32x2*)((u16*)out + o) = i32x2{(int)lo, (int)hi};
+    } else {
+        *(f32x4*)((float*)out + o) = v;
+    }
+}
+
 // ---------------------------------------------------------------- arguments
 struct Sched {
     const int32_t* counts;      // [E] real rows per expert
@@ -104,6 +151,8 @@ struct Gemm2Args {
     void* out;
     int ksplit;                 // 2: column block ntile = 2 c + h covers K half h;
     float* out2;                //    half 1 writes its float partials here, without bias
+    int vec_out;                // bf16 out rows stored as 8-byte pieces of 4 values
+                                // (quad_transpose) instead of one value a lane
 };
 
 // ---------------------------------------------------------------- tile schedule

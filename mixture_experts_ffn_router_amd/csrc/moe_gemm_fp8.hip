@@ -681,6 +681,33 @@ __global__ void __launch_bounds__(512, 1) k_gemm2_f8(Gemm2Args g)
             f8_prologue<S>(src, ring, nk, wave);
         }
         // epilogue straight from the accumulators: one strip at a time
+        const bool obf = g.out_mode == 1 && g.out_dt == MOE_BF16;
+        if (g.vec_out) {
+            // each fragment's 4 x 4 lane quads transposed: lane (g4, 4a + q)
+            // stores row 4 g4 + q of the strip, columns 4a .. 4a + 3
+            const int q = s16 & 3;
+#pragma unroll
+            for (int fm = 0; fm < S::FMW; ++fm) {
+                const int strip = rg * S::FMW + fm;
+                if (strip >= strips || !dst_ok)
+                    continue;
+                const int row = strip * 16 + g4 * 4 + q;
+                const int64_t base = (dst0 + row) * H + c0 + (s16 & ~3);
+#pragma unroll
+                for (int fn = 0; fn < 4; ++fn) {
+                    if (c0 + bcol[fn] >= H)
+                        continue;
+                    f32x4 v;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] = acc[fm][fn][r] * sw[fn] + bias[fn];
+                    quad_transpose(v, lane);
+                    if (row < cur.rows)
+                        store_row4(g.out, base + bcol[fn], obf, v);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
 #pragma unroll
         for (int fm = 0; fm < S::FMW; ++fm) {
             const int strip = rg * S::FMW + fm;
@@ -698,13 +725,14 @@ __global__ void __launch_bounds__(512, 1) k_gemm2_f8(Gemm2Args g)
                     if (c >= H)
                         continue;
                     const float v = acc[fm][fn][r] * sw[fn] + bias[fn];
-                    if (g.out_mode == 1 && g.out_dt == MOE_BF16)
+                    if (obf)
                         ((u16*)g.out)[base + c] = f32_to_bf16(v);
                     else
                         ((float*)g.out)[base + c] = v;
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
         }
         if (!more)
             break;

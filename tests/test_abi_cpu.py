@@ -248,6 +248,16 @@ def test_forward_rejects_missing_pointers(kw, pkw, status):
     assert rc == status
 
 
+def test_forward_of_no_tokens_needs_no_token_arrays():
+    """A contiguous forward with M = 0 reads and writes no token array: with
+    hidden, out and the routing inputs null it returns MOE_OK before any
+    device work (the same pointers are required as soon as M > 0)."""
+    none = dict(hidden=None, out=None, router_logits=None)
+    assert B.moe_forward_status(_prob(M=0).c(), _args(**none), 1 << 20, 1 << 40, 0) == B.MOE_OK
+    assert B.moe_forward_status(_prob(M=1).c(), _args(**none), 1 << 20, 1 << 40, 0) == \
+        B.MOE_ERR_INVALID_ARG
+
+
 def test_forward_rejects_bad_workspace():
     p = _prob()
     info = B.moe_workspace_shapes(p.c())

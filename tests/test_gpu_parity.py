@@ -178,6 +178,30 @@ def test_batched_fp8_small(reduce):
         del T
 
 
+@pytest.mark.parametrize("weight", ["fp8", "bf16"])
+def test_batched_out_alignment(weight):
+    """bf16 slab rows are stored as 8-byte pieces when the output is 8-byte
+    aligned and one value a lane otherwise: an output view one element past
+    an aligned buffer gives the same bits in every valid row, and the rows
+    past each expert's count stay as they were."""
+    dev = GH.device()
+    cfg = BATCHED_SMALL.scaled(name=f"batched_align_{weight}", weight=weight)
+    inp = W.make_inputs(cfg, 1007)
+    E, T, H = cfg.E, inp["max_tokens"], cfg.H
+    print(f"[case] batched output alignment {weight}", flush=True)
+    ref, _, _ = GH.run_batched(inp, dev)
+    buf = torch.full((E * T * H + 1,), 3.0, dtype=torch.bfloat16, device=dev)
+    shifted = buf[1:].view(E, T, H)
+    assert shifted.data_ptr() % 8 != 0
+    GH.run_batched(inp, dev, out=shifted)
+    rows, _ = GH.batched_rows(inp)
+    idx = torch.as_tensor(rows, device=dev)
+    assert torch.equal(shifted.reshape(-1, H)[idx], ref.reshape(-1, H)[idx])
+    untouched = torch.ones(E * T, dtype=torch.bool, device=dev)
+    untouched[idx] = False
+    assert bool((shifted.reshape(-1, H)[untouched] == 3.0).all())
+
+
 def test_batched_bf16_matches_contiguous():
     """bf16 batched rows equal the contiguous path's expert rows."""
     dev = GH.device()
@@ -313,3 +337,31 @@ def test_fp8_activation_codes_bit_exact(H):
             assert np.array_equal(q[p:p + c], q_ref.reshape(c, H)), e
             assert np.array_equal(s[p:p + c], np.asarray(s_ref, np.float32)), e
         p += -(-c // BM) * BM
+
+
+@pytest.mark.parametrize("weight", ["bf16", "fp8"])
+def test_empty_inputs(weight):
+    """No tokens: a contiguous forward with M = 0 returns at once, and batched
+    slabs whose expert_num_tokens are all zero leave every slab row as it was
+    (no tile is computed)."""
+    dev = GH.device()
+    E, H, I, T = 8, 128, 256, 32
+    cfg = W.MIXTRAL_PREFILL.scaled(name=f"empty_{weight}", M=0, H=H, I=I, E=E, weight=weight)
+    print(f"[case] empty contiguous {weight}", flush=True)
+    inp = W.make_inputs(cfg.scaled(M=4), 51)          # weights; the token arrays are cut to 0
+    w13, w2 = inp["w13"].to(dev), inp["w2"].to(dev)
+    kw = {k: inp[k].to(dev) for k in ("w13_scale", "w2_scale") if inp.get(k) is not None}
+    hidden = torch.zeros(0, H, dtype=torch.bfloat16, device=dev)
+    logits = torch.zeros(0, E, dtype=torch.bfloat16, device=dev)
+    out, ws, info = B.fused_moe(hidden, w13, w2, logits, top_k=2, **kw)
+    torch.cuda.synchronize()
+    assert out.shape == (0, H)
+
+    print(f"[case] empty batched slabs {weight}", flush=True)
+    slabs = torch.randn(E, T, H, device=dev).to(torch.bfloat16)
+    counts = torch.zeros(E, dtype=torch.int32, device=dev)
+    sentinel = torch.full((E, T, H), 7.0, dtype=torch.bfloat16, device=dev)
+    out = sentinel.clone()
+    B.fused_moe_batched(slabs, counts, w13, w2, out=out, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, sentinel), "an empty expert's slab rows were written"
