@@ -32,10 +32,16 @@ __device__ __forceinline__ float silu_mul(float g, float u)
 }
 
 // fp8 requantisation of z per (row, 128 columns): scale = amax / 448 (1 for
-// an all-zero group); the codes are RNE(z * rcp(scale)) with the hardware
-// reciprocal (1 ulp), one per group: against an exact division this can move
-// a code by one step only where z / scale lies within an ulp of a rounding tie.
-__device__ __forceinline__ float zq_scale(float amax) { return (amax > 0.0f) ? amax / 448.0f : 1.0f; }
+// an all-zero group), formed as amax times the float nearest 1 / 448 (within
+// an ulp of the quotient; GEMM2 dequantises with the same stored scale); the
+// codes are RNE(z * rcp(scale)) with the hardware reciprocal (1 ulp), one per
+// group: against exact arithmetic this can move a code by one step only where
+// z / scale lies within an ulp or two of a rounding tie, and the group's
+// largest value still lands on code 448 (the codes there are 32 apart).
+__device__ __forceinline__ float zq_scale(float amax)
+{
+    return (amax > 0.0f) ? amax * (1.0f / 448.0f) : 1.0f;
+}
 
 // 4 x 4 transpose inside each quad of lanes (two DPP butterflies): lane
 // 4a + q holding v[r] = X[r][q] (column q of the quad's 4 x 4 block, row r)

@@ -446,8 +446,10 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
 {
     typedef F8S<false, BW> S;
     __shared__ __attribute__((aligned(16))) char ring[S::RING];
-    __shared__ float rs[2][S::CH];                  // activation row scales, by tile parity
-    __shared__ float rws[2][S::CH];                 // routing weights of the rows (z scale)
+    __shared__ __attribute__((aligned(16))) float rs[2][S::CH];    // activation row scales, by
+                                                                    // tile parity
+    __shared__ __attribute__((aligned(16))) float rws[2][S::CH];   // routing weights of the rows
+                                                                    // (z scale; 1 without)
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rg = wave / S::CG, cg = wave % S::CG;
@@ -530,29 +532,56 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
         // LDS, fp8 codes staged in the ring slot no DMA touches before the next
         // tile's first barrier, then 16-byte row stores
         uint8_t* zst = (uint8_t*)(ring + (S::NS - 1) * S::STAGE);           // [CH][128]
-        float* amx = (float*)(ring + (S::NS - 1) * S::STAGE + S::CH * 128);  // [4][CH]
+        float* amx = (float*)(ring + (S::NS - 1) * S::STAGE + S::CH * 128);  // [CH][4 cg]
         // pass 1: z of (strip fm, fragment fn < 2, row r) replaces the gate
-        // accumulator; row amax over this wave's 32 z columns
+        // accumulator (the routing weight is 1 without row weights); mb[v],
+        // v = 4 fm + r, is the largest |z| of that row among this lane's two
+        // columns, as float bits (non-negative floats order like their bits)
+        static_assert(S::FMW == 4, "16 row values a lane");
+        uint32_t mb[16];
 #pragma unroll
         for (int fm = 0; fm < S::FMW; ++fm) {
+            const int row0 = rg * S::FMW * 16 + fm * 16 + g4 * 4;
+            const f32x4 sa = *(const f32x4*)&rs[parity][row0];
+            const f32x4 rw = *(const f32x4*)&rws[parity][row0];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = rg * S::FMW * 16 + fm * 16 + g4 * 4 + r;
-                const float sa = rs[parity][row], rw = rws[parity][row];
-                float m = 0.0f;
+                uint32_t m = 0;
 #pragma unroll
                 for (int fn = 0; fn < 2; ++fn) {
-                    const float hg = acc[fm][fn][r] * sa * sg[fn];
-                    const float hu = acc[fm][fn + 2][r] * sa * su[fn];
-                    acc[fm][fn][r] = silu_mul(hg + bg[fn], hu + bu[fn]);
-                    if (g.row_w)
-                        acc[fm][fn][r] *= rw;
-                    m = fmaxf(m, fabsf(acc[fm][fn][r]));
+                    const float hg = acc[fm][fn][r] * sa[r] * sg[fn];
+                    const float hu = acc[fm][fn + 2][r] * sa[r] * su[fn];
+                    acc[fm][fn][r] = silu_mul(hg + bg[fn], hu + bu[fn]) * rw[r];
+                    m = max(m, __float_as_uint(fabsf(acc[fm][fn][r])));
                 }
-                m = grp_max<16>(m);
-                if (s16 == 0)
-                    amx[cg * S::CH + row] = m;
+                mb[fm * 4 + r] = m;
             }
+        }
+        // the 16 lanes of each lane row share rows: a reduce-scatter over them
+        // (partners 15 - i, 7 - i, i ^ 2, i ^ 1) leaves lane i with the row
+        // maximum of value v = i over this wave's 32 columns
+        {
+            const bool b3 = lane & 8, b2 = lane & 4, b1 = lane & 2, b0 = lane & 1;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t keep = b3 ? mb[k + 8] : mb[k], send = b3 ? mb[k] : mb[k + 8];
+                mb[k] = max(keep, dpp_u32<DPP_MIRROR16>(send));
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t keep = b2 ? mb[k + 4] : mb[k], send = b2 ? mb[k] : mb[k + 4];
+                mb[k] = max(keep, dpp_u32<DPP_MIRROR8>(send));
+            }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const uint32_t keep = b1 ? mb[k + 2] : mb[k], send = b1 ? mb[k] : mb[k + 2];
+                mb[k] = max(keep, dpp_u32<DPP_XOR2>(send));
+            }
+            const uint32_t keep = b0 ? mb[1] : mb[0], send = b0 ? mb[0] : mb[1];
+            const uint32_t m = max(keep, dpp_u32<DPP_XOR1>(send));
+            // value v = s16: strip v / 4, row v % 4 of the lane row g4
+            amx[(rg * S::FMW * 16 + (s16 >> 2) * 16 + g4 * 4 + (s16 & 3)) * 4 + cg] =
+                __uint_as_float(m);
         }
         __syncthreads();
         // pass 2: the row scale over all 128 z columns, the codes
@@ -561,8 +590,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = rg * S::FMW * 16 + fm * 16 + g4 * 4 + r;
-                const float amax = fmaxf(fmaxf(amx[row], amx[S::CH + row]),
-                                         fmaxf(amx[2 * S::CH + row], amx[3 * S::CH + row]));
+                const f32x4 a4 = *(const f32x4*)(amx + row * 4);
+                const float amax = fmaxf(fmaxf(a4[0], a4[1]), fmaxf(a4[2], a4[3]));
                 const float sc = zq_scale(amax), rc = __builtin_amdgcn_rcpf(sc);
                 const uint32_t q = cvt_fp8x2(acc[fm][0][r] * rc, acc[fm][1][r] * rc);
                 zst[row * 128 + cg * 32 + s16] = (uint8_t)q;
