@@ -93,6 +93,17 @@ def load() -> ctypes.CDLL:
     lib.oracle_expert_rows.restype = ctypes.c_int
     lib.oracle_unpack_wq.argtypes = [i32, i32, i64, i64, i64, i64, P, P, i32, P, P]
     lib.oracle_unpack_wq.restype = ctypes.c_int
+    lib.oracle_fp8_tie_alt.argtypes = [ctypes.c_float, ctypes.c_float]
+    lib.oracle_fp8_tie_alt.restype = ctypes.c_int
+    lib.oracle_max_ties.argtypes = []
+    lib.oracle_max_ties.restype = ctypes.c_int
+    lib.oracle_forward_tokens_ties.argtypes = [ctypes.POINTER(_Experts), ctypes.POINTER(_Acts),
+                                               i32, P, P, P, i64, P, i32, P, i32,
+                                               ctypes.c_float, P, P]
+    lib.oracle_forward_tokens_ties.restype = ctypes.c_int
+    lib.oracle_expert_rows_ties.argtypes = [ctypes.POINTER(_Experts), ctypes.POINTER(_Acts), P,
+                                            P, i64, P, i32, ctypes.c_float, P, P]
+    lib.oracle_expert_rows_ties.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -330,12 +341,34 @@ class Acts:
         self.s = _Acts(dt, _ptr(self.data), _ptr(self.scale), int(quantize), int(block))
 
 
+class Ties:
+    """fp8 z codes decided within a relative window of a rounding tie, per
+    output row: count[n] such codes, and delta[n, i] (i < min(count[n],
+    MAX_TIES)) the change of output row n if code i were rounded the other
+    way.  Either rounding of such a code is a correct result; the output is
+    linear in z, so any subset of the deltas may be added."""
+
+    def __init__(self, count: np.ndarray, delta: np.ndarray):
+        self.count, self.delta = count, delta
+
+
+def fp8_tie_alt(t: float, window: float) -> int:
+    """The fp8 code across the rounding midpoint within `window` (relative)
+    of t, or -1."""
+    return int(load().oracle_fp8_tie_alt(float(t), float(window)))
+
+
+def max_ties() -> int:
+    return int(load().oracle_max_ties())
+
+
 def forward_tokens(experts: Experts, acts: Acts, topk_ids, topk_w, tokens=None, nthreads=0,
-                   expert_map=None, weight_on_input=False):
+                   expert_map=None, weight_on_input=False, tie_window=0.0):
     """y[n] = sum_j w[t,j] f_{id[t,j]}(x_t) for t = tokens[n]; float64 [n, H].
     expert_map [global experts]: ids are global and map to experts' rows, -1
     for experts held elsewhere (left out).  weight_on_input: w scales z_r and
-    the expert outputs are summed unweighted.  Returns (y, threads_used)."""
+    the expert outputs are summed unweighted.  Returns (y, threads_used), or
+    (y, threads_used, Ties) with tie_window > 0 (fp8 experts)."""
     lib = load()
     emap = None if expert_map is None else _np(expert_map, np.int32)
     ids = _np(topk_ids, np.int32)
@@ -343,6 +376,15 @@ def forward_tokens(experts: Experts, acts: Acts, topk_ids, topk_w, tokens=None, 
     M, K = ids.shape
     tok = np.arange(M, dtype=np.int64) if tokens is None else _np(tokens, np.int64).ravel()
     y = np.empty((tok.size, experts.H), np.float64)
+    if tie_window > 0:
+        cnt = np.zeros(tok.size, np.int32)
+        dl = np.zeros((tok.size, max_ties(), experts.H), np.float64)
+        used = lib.oracle_forward_tokens_ties(ctypes.byref(experts.s), ctypes.byref(acts.s), K,
+                                              ids.ctypes.data, w.ctypes.data, tok.ctypes.data,
+                                              tok.size, y.ctypes.data, int(nthreads), _ptr(emap),
+                                              int(bool(weight_on_input)), float(tie_window),
+                                              cnt.ctypes.data, dl.ctypes.data)
+        return y, used, Ties(cnt, dl)
     used = lib.oracle_forward_tokens(ctypes.byref(experts.s), ctypes.byref(acts.s), K,
                                      ids.ctypes.data, w.ctypes.data, tok.ctypes.data, tok.size,
                                      y.ctypes.data, int(nthreads), _ptr(emap),
@@ -350,13 +392,23 @@ def forward_tokens(experts: Experts, acts: Acts, topk_ids, topk_w, tokens=None, 
     return y, used
 
 
-def expert_rows(experts: Experts, acts: Acts, rows, expert_of_row, nthreads=0):
-    """out[n] = f_{expert_of_row[n]}(activation row rows[n]); float64 [n, H]."""
+def expert_rows(experts: Experts, acts: Acts, rows, expert_of_row, nthreads=0, tie_window=0.0):
+    """out[n] = f_{expert_of_row[n]}(activation row rows[n]); float64 [n, H].
+    Returns (out, threads_used), or (out, threads_used, Ties) with
+    tie_window > 0 (fp8 experts)."""
     lib = load()
     r = _np(rows, np.int64).ravel()
     e = _np(expert_of_row, np.int32).ravel()
     assert r.size == e.size
     out = np.empty((r.size, experts.H), np.float64)
+    if tie_window > 0:
+        cnt = np.zeros(r.size, np.int32)
+        dl = np.zeros((r.size, max_ties(), experts.H), np.float64)
+        used = lib.oracle_expert_rows_ties(ctypes.byref(experts.s), ctypes.byref(acts.s),
+                                           r.ctypes.data, e.ctypes.data, r.size, out.ctypes.data,
+                                           int(nthreads), float(tie_window), cnt.ctypes.data,
+                                           dl.ctypes.data)
+        return out, used, Ties(cnt, dl)
     used = lib.oracle_expert_rows(ctypes.byref(experts.s), ctypes.byref(acts.s), r.ctypes.data,
                                   e.ctypes.data, r.size, out.ctypes.data, int(nthreads))
     return out, used

@@ -558,10 +558,39 @@ static void load_row(const oracle_acts* A, int64_t H, int64_t row, double* x, fl
     }
 }
 
+/* Codes decided near a rounding tie.  Whoever computes t = z / scale in a
+ * different order, or with a different exp / reciprocal, gets a t that
+ * differs in its last bits, and where t lies that close to the midpoint
+ * between two fp8 values both roundings are correct answers.  Returns the
+ * code that t * (1 + window) or t * (1 - window) rounds to when it differs
+ * from t's own code (the neighbour across the nearby midpoint), else -1. */
+int oracle_fp8_tie_alt(float t, float window)
+{
+    const uint8_t c = oracle_fp8_encode(t);
+    const uint8_t up = oracle_fp8_encode(t * (1.0f + window));
+    const uint8_t dn = oracle_fp8_encode(t * (1.0f - window));
+    if (up != c)
+        return up;
+    if (dn != c)
+        return dn;
+    return -1;
+}
+
+/* Near-tie z codes of one expert row: where each sits in z and how much the
+ * dequantised z value changes (alternative minus chosen) if the other code is
+ * taken.  n counts every near-tie code, also past ORACLE_MAX_TIES. */
+#define ORACLE_MAX_TIES 8
+typedef struct {
+    int32_t n;
+    int64_t k[ORACLE_MAX_TIES];
+    double dz[ORACLE_MAX_TIES];
+} tie_rec;
+
 /* z requantisation for the fp8 path: each 128-column group of a row gets
  * its own scale (the block-wise granularity of the "FP8 W8A8" section);
- * codes are decided in float32 as the device does. */
-static void requant_z(double* z, int64_t I)
+ * codes are decided in float32 as the device does.  With window > 0 the
+ * codes within that relative distance of a rounding tie go into tr. */
+static void requant_z(double* z, int64_t I, float window, tie_rec* tr)
 {
     for (int64_t g0 = 0; g0 < I; g0 += 128) {
         int64_t n = (I - g0 < 128) ? I - g0 : 128;
@@ -572,17 +601,61 @@ static void requant_z(double* z, int64_t I)
                 amax = fabsf(zf[i]);
         }
         sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
-        for (int64_t i = 0; i < n; ++i)
-            z[g0 + i] = fp8_table[oracle_fp8_encode(zf[i] / sc)] * (double)sc;
+        for (int64_t i = 0; i < n; ++i) {
+            const uint8_t c = oracle_fp8_encode(zf[i] / sc);
+            z[g0 + i] = fp8_table[c] * (double)sc;
+            if (window > 0.0f && tr) {
+                const int alt = oracle_fp8_tie_alt(zf[i] / sc, window);
+                if (alt >= 0) {
+                    if (tr->n < ORACLE_MAX_TIES) {
+                        tr->k[tr->n] = g0 + i;
+                        tr->dz[tr->n] = (fp8_table[alt] - fp8_table[c]) * (double)sc;
+                    }
+                    tr->n++;
+                }
+            }
+        }
+    }
+}
+
+/* o += zi * (row i of expert e's dequantised W2). */
+static void add_w2_row(const oracle_experts* W, int e, int64_t i, double zi, double* o)
+{
+    const int64_t H = W->H, I = W->I;
+    const int64_t base = ((int64_t)e * I + i) * H;
+    if (W->w_dtype == OR_F32) {
+        const float* w = (const float*)W->w2 + base;
+        for (int64_t c = 0; c < H; ++c)
+            o[c] += zi * (double)w[c];
+    } else if (W->w_dtype == OR_BF16) {
+        const uint16_t* w = (const uint16_t*)W->w2 + base;
+        for (int64_t c = 0; c < H; ++c)
+            o[c] += zi * bf16_bits_to_double(w[c]);
+    } else if (W->w_dtype == OR_U8 || W->w_dtype == OR_U4) {
+        for (int64_t c = 0; c < H; ++c)
+            o[c] += zi * wq_weight(W, W->w2, W->w2_scale, W->w2_zero, e, I, H, i, c);
+    } else if (W->block > 0) {
+        /* scale of weight (i, c): block (c / B, i / B) of expert e */
+        const int64_t B = W->block, nbn = (H + B - 1) / B, nbk = (I + B - 1) / B;
+        const uint8_t* w = (const uint8_t*)W->w2 + base;
+        const float* sc = W->w2_scale + (int64_t)e * nbn * nbk + i / B;
+        for (int64_t c = 0; c < H; ++c)
+            o[c] += zi * (fp8_table[w[c]] * (double)sc[(c / B) * nbk]);
+    } else {
+        const uint8_t* w = (const uint8_t*)W->w2 + base;
+        const float* sc = W->w2_scale + (int64_t)e * H;
+        for (int64_t c = 0; c < H; ++c)
+            o[c] += zi * (fp8_table[w[c]] * (double)sc[c]);
     }
 }
 
 /* o = f_e(x): h = W13_e^T x + b13_e; z = a * SiLU(h[:I]) * h[I:]; o = W2_e^T z + b2_e.
  * a = zscale: 1, or the routing weight when it is applied to the first
  * layer's output (the walkthrough's apply_router_weight_on_input, sec. 1.2).
- * scratch: h[2I], z[I]. */
+ * scratch: h[2I], z[I].  window / tr: near-tie z codes (fp8 path), see
+ * requant_z. */
 static void expert_ffn(const oracle_experts* W, int e, const double* x, double* h, double* z,
-                       double* o, double zscale)
+                       double* o, double zscale, float window, tie_rec* tr)
 {
     const int64_t H = W->H, I = W->I, N = 2 * (int64_t)W->I;
 
@@ -625,38 +698,12 @@ static void expert_ffn(const oracle_experts* W, int e, const double* x, double* 
         z[i] = zscale * (g / (1.0 + exp(-g)) * u); /* SiLU(g) = g * sigmoid(g) */
     }
     if (W->requant_z)
-        requant_z(z, I);
+        requant_z(z, I, window, tr);
 
     for (int64_t c = 0; c < H; ++c)
         o[c] = 0.0;
-    for (int64_t i = 0; i < I; ++i) {
-        const double zi = z[i];
-        const int64_t base = ((int64_t)e * I + i) * H;
-        if (W->w_dtype == OR_F32) {
-            const float* w = (const float*)W->w2 + base;
-            for (int64_t c = 0; c < H; ++c)
-                o[c] += zi * (double)w[c];
-        } else if (W->w_dtype == OR_BF16) {
-            const uint16_t* w = (const uint16_t*)W->w2 + base;
-            for (int64_t c = 0; c < H; ++c)
-                o[c] += zi * bf16_bits_to_double(w[c]);
-        } else if (W->w_dtype == OR_U8 || W->w_dtype == OR_U4) {
-            for (int64_t c = 0; c < H; ++c)
-                o[c] += zi * wq_weight(W, W->w2, W->w2_scale, W->w2_zero, e, I, H, i, c);
-        } else if (W->block > 0) {
-            /* scale of weight (i, c): block (c / B, i / B) of expert e */
-            const int64_t B = W->block, nbn = (H + B - 1) / B, nbk = (I + B - 1) / B;
-            const uint8_t* w = (const uint8_t*)W->w2 + base;
-            const float* sc = W->w2_scale + (int64_t)e * nbn * nbk + i / B;
-            for (int64_t c = 0; c < H; ++c)
-                o[c] += zi * (fp8_table[w[c]] * (double)sc[(c / B) * nbk]);
-        } else {
-            const uint8_t* w = (const uint8_t*)W->w2 + base;
-            const float* sc = W->w2_scale + (int64_t)e * H;
-            for (int64_t c = 0; c < H; ++c)
-                o[c] += zi * (fp8_table[w[c]] * (double)sc[c]);
-        }
-    }
+    for (int64_t i = 0; i < I; ++i)
+        add_w2_row(W, e, i, z[i], o);
     if (W->w2_bias)
         for (int64_t c = 0; c < H; ++c)
             o[c] += bias_at(W, W->w2_bias, (int64_t)e * H + c);
@@ -670,10 +717,29 @@ static void expert_ffn(const oracle_experts* W, int e, const double* x, double* 
  * (y is then this rank's partial sum).  weight_on_input: the routing weight
  * scales z_r and the expert outputs are summed unweighted.
  * nthreads <= 0 keeps the OpenMP default.  Returns the thread count used. */
-int oracle_forward_tokens(const oracle_experts* W, const oracle_acts* A, int32_t top_k,
+/* Near-tie deltas of one output row: each recorded tie t of an expert row
+ * (scaled by `scale`, the routing weight the row enters the output with)
+ * becomes delta slot *used (while there is one): scale * dz_t * W2_e row k_t,
+ * the change of the output if that code were rounded the other way. */
+static void tie_deltas(const oracle_experts* W, int e, const tie_rec* tr, double scale,
+                       double* delta, int32_t* used)
+{
+    const int64_t H = W->H;
+    const int n = tr->n < ORACLE_MAX_TIES ? tr->n : ORACLE_MAX_TIES;
+    for (int t = 0; t < n && *used < ORACLE_MAX_TIES; ++t) {
+        double* d = delta + (int64_t)(*used) * H;
+        for (int64_t c = 0; c < H; ++c)
+            d[c] = 0.0;
+        add_w2_row(W, e, tr->k[t], scale * tr->dz[t], d);
+        ++*used;
+    }
+}
+
+static int forward_tokens(const oracle_experts* W, const oracle_acts* A, int32_t top_k,
                           const int32_t* topk_ids, const double* topk_w, const int64_t* tokens,
                           int64_t n_tokens, double* y, int32_t nthreads,
-                          const int32_t* expert_map, int32_t weight_on_input)
+                          const int32_t* expert_map, int32_t weight_on_input, float window,
+                          int32_t* tie_count, double* tie_delta)
 {
     int used = 1;
     fp8_table_init();
@@ -698,6 +764,7 @@ int oracle_forward_tokens(const oracle_experts* W, const oracle_acts* A, int32_t
         for (int64_t n = 0; n < n_tokens; ++n) {
             const int64_t t = tokens[n];
             double* yt = y + n * H;
+            int32_t ties = 0, used = 0;
             load_row(A, H, t, x, xf, q);
             for (int64_t c = 0; c < H; ++c)
                 yt[c] = 0.0;
@@ -705,18 +772,26 @@ int oracle_forward_tokens(const oracle_experts* W, const oracle_acts* A, int32_t
                 const int g = topk_ids[t * top_k + j];
                 const int e = expert_map ? expert_map[g] : g;
                 const double wj = topk_w[t * top_k + j];
+                tie_rec tr = {0};
                 if (e < 0)
                     continue;                       /* held by another rank */
                 if (weight_on_input) {
-                    expert_ffn(W, e, x, h, z, o, wj);
+                    expert_ffn(W, e, x, h, z, o, wj, window, &tr);
                     for (int64_t c = 0; c < H; ++c)
                         yt[c] += o[c];
                 } else {
-                    expert_ffn(W, e, x, h, z, o, 1.0);
+                    expert_ffn(W, e, x, h, z, o, 1.0, window, &tr);
                     for (int64_t c = 0; c < H; ++c)
                         yt[c] += wj * o[c];
                 }
+                if (tie_count) {
+                    ties += tr.n;
+                    tie_deltas(W, e, &tr, weight_on_input ? 1.0 : wj,
+                               tie_delta + n * ORACLE_MAX_TIES * H, &used);
+                }
             }
+            if (tie_count)
+                tie_count[n] = ties;
         }
         free(x);
         free(xf);
@@ -728,10 +803,58 @@ int oracle_forward_tokens(const oracle_experts* W, const oracle_acts* A, int32_t
     return used;
 }
 
+int oracle_forward_tokens(const oracle_experts* W, const oracle_acts* A, int32_t top_k,
+                          const int32_t* topk_ids, const double* topk_w, const int64_t* tokens,
+                          int64_t n_tokens, double* y, int32_t nthreads,
+                          const int32_t* expert_map, int32_t weight_on_input)
+{
+    return forward_tokens(W, A, top_k, topk_ids, topk_w, tokens, n_tokens, y, nthreads,
+                          expert_map, weight_on_input, 0.0f, NULL, NULL);
+}
+
+/* oracle_forward_tokens that also reports the fp8 z codes decided within a
+ * relative `window` of a rounding tie (see oracle_fp8_tie_alt): tie_count[n]
+ * is the number of such codes behind token n's output, and tie_delta
+ * [n_tokens][ORACLE_MAX_TIES][H] the change of y[n] if the i-th of them were
+ * rounded the other way (the first ORACLE_MAX_TIES; any subset of them gives
+ * an equally correct output, since GEMM2 and the reduction are linear in z). */
+int oracle_forward_tokens_ties(const oracle_experts* W, const oracle_acts* A, int32_t top_k,
+                               const int32_t* topk_ids, const double* topk_w,
+                               const int64_t* tokens, int64_t n_tokens, double* y,
+                               int32_t nthreads, const int32_t* expert_map,
+                               int32_t weight_on_input, float window, int32_t* tie_count,
+                               double* tie_delta)
+{
+    return forward_tokens(W, A, top_k, topk_ids, topk_w, tokens, n_tokens, y, nthreads,
+                          expert_map, weight_on_input, window, tie_count, tie_delta);
+}
+
+int oracle_max_ties(void) { return ORACLE_MAX_TIES; }
+
+static int expert_rows(const oracle_experts* W, const oracle_acts* A, const int64_t* rows,
+                       const int32_t* experts, int64_t n_rows, double* out, int32_t nthreads,
+                       float window, int32_t* tie_count, double* tie_delta);
+
 /* Any list of (activation row, expert) pairs: out[n][H] = f_{experts[n]}(row rows[n]).
  * Serves the batched format, where row = e * max_tokens + i for i < count_e. */
 int oracle_expert_rows(const oracle_experts* W, const oracle_acts* A, const int64_t* rows,
                        const int32_t* experts, int64_t n_rows, double* out, int32_t nthreads)
+{
+    return expert_rows(W, A, rows, experts, n_rows, out, nthreads, 0.0f, NULL, NULL);
+}
+
+/* oracle_expert_rows with the near-tie report of oracle_forward_tokens_ties. */
+int oracle_expert_rows_ties(const oracle_experts* W, const oracle_acts* A, const int64_t* rows,
+                            const int32_t* experts, int64_t n_rows, double* out,
+                            int32_t nthreads, float window, int32_t* tie_count,
+                            double* tie_delta)
+{
+    return expert_rows(W, A, rows, experts, n_rows, out, nthreads, window, tie_count, tie_delta);
+}
+
+static int expert_rows(const oracle_experts* W, const oracle_acts* A, const int64_t* rows,
+                       const int32_t* experts, int64_t n_rows, double* out, int32_t nthreads,
+                       float window, int32_t* tie_count, double* tie_delta)
 {
     int used = 1;
     fp8_table_init();
@@ -753,8 +876,14 @@ int oracle_expert_rows(const oracle_experts* W, const oracle_acts* A, const int6
 #endif
 #pragma omp for schedule(dynamic, 1)
         for (int64_t n = 0; n < n_rows; ++n) {
+            tie_rec tr = {0};
+            int32_t used = 0;
             load_row(A, H, rows[n], x, xf, q);
-            expert_ffn(W, experts[n], x, h, z, out + n * H, 1.0);
+            expert_ffn(W, experts[n], x, h, z, out + n * H, 1.0, window, &tr);
+            if (tie_count) {
+                tie_count[n] = tr.n;
+                tie_deltas(W, experts[n], &tr, 1.0, tie_delta + n * ORACLE_MAX_TIES * H, &used);
+            }
         }
         free(x);
         free(xf);

@@ -830,3 +830,77 @@ def test_weight_on_input_with_b2_closed_form():
     diff = ((1.0 - w)[:, :, None] * b2.double().numpy()[ids]).sum(1)
     assert np.allclose(y_in - y_out, diff, rtol=1e-10, atol=1e-12)
     assert np.abs(diff).max() > 1e-3
+
+
+def test_fp8_tie_alternative_codes():
+    """Near-tie codes: the code on the other side of a rounding midpoint
+    within the window, against torch's float8_e4m3fn cast of t * (1 +- w)
+    (values on the E4M3FN grid: ... 320, 352, 384, 416, 448; midpoint 368)."""
+    dec = lambda c: float(oracle.fp8_decode(np.array([c], np.uint8))[0])
+    w = 1e-4
+    assert dec(oracle.fp8_tie_alt(368.0 * (1 - 1e-6), w)) == 384.0     # chose 352
+    assert dec(oracle.fp8_tie_alt(368.0 * (1 + 1e-6), w)) == 352.0     # chose 384
+    assert dec(oracle.fp8_tie_alt(368.0, w)) == 352.0                  # exact tie: even 384
+    assert dec(oracle.fp8_tie_alt(-368.0 * (1 - 1e-6), w)) == -384.0
+    assert oracle.fp8_tie_alt(352.0, w) == -1                          # a code itself
+    assert oracle.fp8_tie_alt(600.0, w) == -1 and oracle.fp8_tie_alt(448.0, w) == -1
+    assert dec(oracle.fp8_tie_alt(2.0 ** -10 * (1 + 1e-6), w)) == 0.0  # subnormal midpoint
+    assert oracle.fp8_tie_alt(368.0 * (1 - 1e-6), 0.0) == -1
+    rng = np.random.default_rng(5)
+    t = np.float32(rng.choice([-1.0, 1.0], 4000) * np.exp(rng.uniform(-9, 6, 4000)))
+    for win in (1e-3, 3e-2):
+        tt = torch.from_numpy(t)
+        c0 = tt.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        up = (tt * np.float32(1 + win)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        dn = (tt * np.float32(1 - win)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        ref = np.where(up != c0, up.astype(np.int64), np.where(dn != c0, dn.astype(np.int64), -1))
+        got = np.array([oracle.fp8_tie_alt(float(v), win) for v in t])
+        assert np.array_equal(got, ref)
+
+
+def test_near_tie_deltas_are_single_code_flips():
+    """The near-tie report of the fp8 z requantisation: the output is the
+    plain one bit for bit, and every reported delta is the output change of
+    rounding that one z code the other way -- rebuilt in torch float64 from
+    the float32 z, its group scale and the cast of t * (1 +- w)."""
+    g = torch.Generator().manual_seed(29)
+    M, H, I, E, win = 4, 64, 256, 2, 2e-2
+    x = _bf(torch.randn(M, H, generator=g))
+    W13 = torch.randn(E, H, 2 * I, generator=g) / 8
+    W2 = torch.randn(E, I, H, generator=g) / 16
+    ids = np.array([[0, 1], [1, 0], [0, 1], [1, 1]], np.int32)
+    w = np.array([[0.7, 0.3], [0.6, 0.4], [1.0, 0.5], [0.2, 0.8]])
+    ex = oracle.Experts(W13, W2, requant_z=True)
+    acts = oracle.Acts(x, quantize=True)
+    y0, _ = oracle.forward_tokens(ex, acts, ids, w)
+    y, _, ties = oracle.forward_tokens(ex, acts, ids, w, tie_window=win)
+    assert np.array_equal(y, y0)
+    _, _, none = oracle.forward_tokens(ex, acts, ids, w, tie_window=1e-9)
+    assert none.count.sum() <= ties.count.sum()
+    MT = oracle.max_ties()
+    for t in range(M):
+        xf = x[t].float()
+        sx = xf.abs().max() / 448.0
+        xq = (xf / sx).to(torch.float8_e4m3fn).double() * sx.double()
+        want = []
+        for j in range(ids.shape[1]):
+            e = ids[t, j]
+            h = xq @ W13[e].double()
+            z = (torch.nn.functional.silu(h[:I]) * h[I:]).float()
+            for g0 in range(0, I, 128):
+                sz = z[g0:g0 + 128].abs().max() / 448.0
+                tz = z[g0:g0 + 128] / sz
+                c0 = tz.to(torch.float8_e4m3fn)
+                for k in range(128):
+                    alt = None
+                    for f in (1 + win, 1 - win):
+                        ck = (tz[k:k + 1] * np.float32(f)).to(torch.float8_e4m3fn)
+                        if alt is None and ck.view(torch.uint8)[0] != c0.view(torch.uint8)[k]:
+                            alt = ck
+                    if alt is not None:
+                        dz = (alt.double()[0] - c0.double()[k]) * sz.double()
+                        want.append(w[t, j] * dz * W2[e][g0 + k].double())
+        assert ties.count[t] == len(want)
+        for i in range(min(len(want), MT)):
+            assert np.allclose(ties.delta[t, i], want[i].numpy(), rtol=1e-12, atol=1e-15)
+    assert ties.count.max() > 0
