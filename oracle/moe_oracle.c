@@ -558,12 +558,14 @@ static void load_row(const oracle_acts* A, int64_t H, int64_t row, double* x, fl
     }
 }
 
-/* Codes decided near a rounding tie.  Whoever computes t = z / scale in a
- * different order, or with a different exp / reciprocal, gets a t that
- * differs in its last bits, and where t lies that close to the midpoint
- * between two fp8 values both roundings are correct answers.  Returns the
- * code that t * (1 + window) or t * (1 - window) rounds to when it differs
- * from t's own code (the neighbour across the nearby midpoint), else -1. */
+/* Codes decided near a rounding tie, for the re-quantisation of the
+ * intermediate z on the fp8 path (FlagGems walkthrough, "FP8 W8A8").
+ * Whoever computes t = z / scale in a different order, or with a different
+ * exp / reciprocal, gets a t that differs in its last bits, and where t lies
+ * that close to the midpoint between two fp8 values both roundings are
+ * correct answers.  Returns the code that t * (1 + window) or
+ * t * (1 - window) rounds to when it differs from t's own code (the
+ * neighbour across the nearby midpoint), else -1. */
 int oracle_fp8_tie_alt(float t, float window)
 {
     const uint8_t c = oracle_fp8_encode(t);
