@@ -74,16 +74,17 @@ def test_block_fp8_batched_bf16_activations(reduce):
     ex = GH.oracle_experts(inp)
     acts = oracle.Acts(inp["hidden"].cpu(), quantize=True, block=128)
     if reduce:
-        y, _ = oracle.forward_tokens(ex, oracle.Acts(inp["tokens"].cpu(), quantize=True,
-                                                     block=128),
-                                     inp["topk_ids"].cpu().numpy(),
-                                     inp["token_map_w"].cpu().double().numpy())
-        GH.compare(BATCHED_BLOCK, out.cpu().numpy(), y, "batched block reduce")
+        y, _, ties = oracle.forward_tokens(ex, oracle.Acts(inp["tokens"].cpu(), quantize=True,
+                                                           block=128),
+                                           inp["topk_ids"].cpu().numpy(),
+                                           inp["token_map_w"].cpu().double().numpy(),
+                                           tie_window=GH.TIE_WINDOW)
+        GH.compare(BATCHED_BLOCK, out.cpu().numpy(), y, "batched block reduce", ties=ties)
     else:
         rows, experts = GH.batched_rows(inp)
-        ref, _ = oracle.expert_rows(ex, acts, rows, experts)
+        ref, _, ties = oracle.expert_rows(ex, acts, rows, experts, tie_window=GH.TIE_WINDOW)
         got = out.reshape(-1, BATCHED_BLOCK.H)[torch.as_tensor(rows, device=out.device)]
-        GH.compare(BATCHED_BLOCK, got.cpu().numpy(), ref, "batched block rows")
+        GH.compare(BATCHED_BLOCK, got.cpu().numpy(), ref, "batched block rows", ties=ties)
 
 
 def test_block_fp8_batched_prequantised_activations():
@@ -111,6 +112,6 @@ def test_block_fp8_batched_prequantised_activations():
     rows, experts = GH.batched_rows(inp)
     ex = GH.oracle_experts(inp)
     acts = oracle.Acts(codes.cpu(), scale=sc.cpu(), block=128)
-    ref, _ = oracle.expert_rows(ex, acts, rows, experts)
+    ref, _, ties = oracle.expert_rows(ex, acts, rows, experts, tie_window=GH.TIE_WINDOW)
     got = out.reshape(-1, H)[torch.as_tensor(rows, device=out.device)]
-    GH.compare(cfg, got.cpu().numpy(), ref, "batched block prequantised")
+    GH.compare(cfg, got.cpu().numpy(), ref, "batched block prequantised", ties=ties)

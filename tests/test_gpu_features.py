@@ -70,9 +70,8 @@ def test_expert_shard_parity(case):
     assert np.array_equal(GH.region(ws, info.off_expert_ids, torch.int32, npp // info.block_m),
                           eids_o)
     # this shard's partial sums
-    acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8")
-    y, _ = oracle.forward_tokens(GH.oracle_experts(loc), acts, ids_o, w_o, expert_map=emap)
-    GH.compare(cfg, out.float().cpu().numpy(), y, what=name)
+    y, ties = GH.ref_tokens(loc, ids_o, w_o, expert_map=emap)
+    GH.compare(cfg, out.float().cpu().numpy(), y, what=name, ties=ties)
 
 
 def test_expert_shards_sum_to_the_full_layer():
@@ -117,9 +116,8 @@ def test_weight_on_input_parity(cfg, packed):
     out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, packed=packed,
                                       apply_weight_on_input=True)
     ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
-    acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8")
-    y, _ = oracle.forward_tokens(GH.oracle_experts(inp), acts, ids_o, w_o, weight_on_input=True)
-    GH.compare(cfg, out.float().cpu().numpy(), y, what="weight on input")
+    y, ties = GH.ref_tokens(inp, ids_o, w_o, weight_on_input=True)
+    GH.compare(cfg, out.float().cpu().numpy(), y, what="weight on input", ties=ties)
 
 
 @pytest.mark.parametrize("routing", ["router", "precomputed", "inplace"])

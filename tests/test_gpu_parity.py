@@ -158,24 +158,15 @@ def test_batched_fp8_small(reduce):
         flat16 = out16.reshape(-1, BATCHED_SMALL.H)[torch.as_tensor(rows, device=out.device)]
         GH.check_rounded(flat16, flat32)
     GH.check_batched_tilelist(inp, ws, info)
-    ex = GH.oracle_experts(inp)
     import oracle
     acts = oracle.Acts(inp["hidden"].cpu(), quantize=True)
-    o_ref, _ = oracle.expert_rows(ex, acts, rows, experts)
+    o_ref, ties = GH.ref_rows(inp, acts, rows, experts)
     if not reduce:
         got = out.float().cpu().numpy().reshape(-1, BATCHED_SMALL.H)[rows]
-        GH.compare(BATCHED_SMALL, got, o_ref, "batched rows")
+        GH.compare(BATCHED_SMALL, got, o_ref, "batched rows", ties=ties)
     else:
-        T = inp["max_tokens"]
-        tmap = inp["token_map"].cpu().numpy().astype(np.int64)
-        pos = {r: i for i, r in enumerate(rows)}
-        wts = inp["token_map_w"].cpu().numpy().astype(np.float64)
-        y = np.zeros((BATCHED_SMALL.M, BATCHED_SMALL.H))
-        for t in range(BATCHED_SMALL.M):
-            for j in range(BATCHED_SMALL.top_k):
-                y[t] += wts[t, j] * o_ref[pos[tmap[t, j]]]
-        GH.compare(BATCHED_SMALL, out.float().cpu().numpy(), y, "batched reduce")
-        del T
+        y, yties = GH.reduce_rows(inp, rows, o_ref, ties)
+        GH.compare(BATCHED_SMALL, out.float().cpu().numpy(), y, "batched reduce", ties=yties)
 
 
 @pytest.mark.parametrize("weight", ["fp8", "bf16"])
