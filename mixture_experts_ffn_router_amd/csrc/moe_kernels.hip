@@ -768,7 +768,7 @@ __global__ void __launch_bounds__(1024) k_tilelist(const int32_t* __restrict__ e
     __shared__ int tot[ALIGN_WAVES];
     __shared__ int sh_start[1025], sh_cnt[1024], choff[1025];
     __shared__ int sh_clamped;
-    const int e = threadIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = threadIdx.x;
     if (threadIdx.x == 0)
         sh_clamped = 0;
     __syncthreads();
@@ -785,34 +785,47 @@ __global__ void __launch_bounds__(1024) k_tilelist(const int32_t* __restrict__ e
     // more rows than the workspace was sized for: process nothing
     const bool fits = (int64_t)total <= max_sorted && total / BM <= max_blocks;
     if (e < E) {
-        counts[e] = fits ? c : 0;
-        offsets[e] = fits ? start : 0;
         sh_start[e] = start;
         sh_cnt[e] = c;
     }
-    if (threadIdx.x == 0) {
-        offsets[E] = fits ? total : 0;
+    if (threadIdx.x == 0)
         sh_start[E] = total;
-        *npp = fits ? total : 0;
-        *status = (sh_clamped ? MOE_DEV_COUNT_CLAMPED : 0) | (fits ? 0 : MOE_DEV_ROWS_OVERFLOW);
+    // workgroup 0 writes the per-expert metadata and the chunk tables
+    if (blockIdx.x == 0) {
+        if (e < E) {
+            counts[e] = fits ? c : 0;
+            offsets[e] = fits ? start : 0;
+        }
+        if (threadIdx.x == 0) {
+            offsets[E] = fits ? total : 0;
+            *npp = fits ? total : 0;
+            *status = (sh_clamped ? MOE_DEV_COUNT_CLAMPED : 0) | (fits ? 0 : MOE_DEV_ROWS_OVERFLOW);
+        }
+        write_chunks(fits ? c : 0, CH, E, tot, choff, chunk_off, chunk_expert);
     }
-    write_chunks(fits ? c : 0, CH, E, tot, choff, chunk_off, chunk_expert);
+    __syncthreads();
     if (!fits)
         return;
-    for (int b = threadIdx.x; b < total / BM; b += 1024)
-        expert_ids[b] = upper_index(sh_start, E, b * BM);
-    // each wave fills the runs of experts wave, wave+16, ...
-    for (int x = wave; x < E; x += ALIGN_WAVES) {
-        const int st = sh_start[x], cx = sh_cnt[x];
-        const int pe = (cx + BM - 1) / BM * BM;
-        for (int i = lane; i < pe; i += 64)
-            sorted[st + i] = (i < cx) ? x * T + i : sentinel;
+    if (blockIdx.x == 0)
+        for (int b = threadIdx.x; b < total / BM; b += 1024)
+            expert_ids[b] = upper_index(sh_start, E, b * BM);
+    // the sorted ids: every workgroup fills its share of the padded positions,
+    // each position finding its expert run by a binary search of the starts
+    const int per = (total + gridDim.x - 1) / gridDim.x;
+    const int p1 = min(total, (int)(blockIdx.x + 1) * per);
+    for (int p = blockIdx.x * per + threadIdx.x; p < p1; p += 1024) {
+        const int x = upper_index(sh_start, E, p), i = p - sh_start[x];
+        sorted[p] = (i < sh_cnt[x]) ? x * T + i : sentinel;
     }
 }
 
 hipError_t launch_tilelist(const Plan& P, const int32_t* ent, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_tilelist, dim3(1), dim3(1024), 0, s, ent, P.E, P.T, P.BM, P.counts,
+    // one workgroup per 4096 padded positions the workspace holds (up to 64):
+    // each recomputes the layout from the counts and fills its share
+    const int64_t nb = (P.max_sorted + 4095) / 4096;
+    const dim3 grid((unsigned)(nb < 1 ? 1 : nb > 64 ? 64 : nb));
+    hipLaunchKernelGGL(k_tilelist, grid, dim3(1024), 0, s, ent, P.E, P.T, P.BM, P.counts,
                        P.offsets, P.sorted_ids, P.expert_ids, P.npp, (int)P.sentinel,
                        P.max_sorted, P.max_blocks, P.CH, P.chunk_off, P.chunk_expert, P.status);
     return hipGetLastError();
