@@ -38,7 +38,7 @@ MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "fp8": 5033.2}
 DEFAULT_WORKLOAD = "deepseek_grouped_sigmoid_bf16"
 # the other problem configurations, summarised in the default line
 OTHER_CONFIGS = ("tiny_f32", "mixtral_prefill_bf16", "decode_e128_bf16", "batched_fp8_skewed")
-OTHER_STEPS, OTHER_WARMUP = 10, 3
+OTHER_STEPS, OTHER_WARMUP = 20, 5
 
 
 def parse():
@@ -120,7 +120,7 @@ def main():
     cfg = W.BY_NAME[args.workload]
     res, inp, info = measure(cfg, args.steps, args.warmup, args.seed, time_plain=True)
 
-    # ---- the other problem configurations, fewer steps each (default run only):
+    # ---- the other problem configurations (default run only):
     # one summary per workload in the same line, so that every configuration's
     # throughput and roofline fraction is measured by the same invocation
     if args.workload == DEFAULT_WORKLOAD and not args.no_other_configs:
