@@ -276,6 +276,10 @@ ROUTE_PATHS = [
     ("e96_groups_of_12", 400, 96, 6, "sigmoid", 8),
     # grouped keys by shuffles over 8-lane groups, softmax top-2 sums, 4 of 6 groups
     ("e192_six_groups", 400, 192, 6, "softmax", 6),
+    # the largest top_k (32) the boundary takes, over the most experts (1024)
+    ("topk32_e1024", 40, 1024, 32, "softmax", 1),
+    # top_k = 32 = k_group x experts a group: every expert of the 4 chosen groups
+    ("topk32_grouped_e64", 64, 64, 32, "sigmoid", 8),
 ]
 
 
