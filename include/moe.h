@@ -444,8 +444,9 @@ int moe_repack_wna16(int format, int bits, int E, int K, int N, int group,
  *   128 kt + 16 q .. + 15 with p = s ^ ((n >> 1) & 7), q = 2 (p & 3) + (p >> 2)
  *   (the even 16-row chunks before the odd ones, then the column's XOR).
  *   w13: block (e, kt, j), kt < ceil(H / 128), j < I / 64, j fastest; block
- *        columns 0-63 are gate columns 64 j .., 64-127 the up columns
- *        I + 64 j ...
+ *        columns 0-63 hold gate columns 64 j .., 64-127 the up columns
+ *        I + 64 j .., each half in 32-column groups: block column
+ *        32 h + 16 f + s (f < 2, s < 16) of a half is its column 32 h + 2 s + f.
  *   w2:  block (e, kt, j), kt < I / 128, j < ceil(H / 128); block column n
  *        is weight column 128 j + n.
  *   The per-channel scales are not packed.

@@ -382,7 +382,9 @@ __device__ __forceinline__ void f8_zero(f32x4 (&acc)[F8_ROWS / 32][4])
 // Tile (expert, row chunk, ntile): z columns 128 ntile .. +127, i.e. the
 // gate and up columns of packed blocks 2 ntile and 2 ntile + 1 (each 64 gate
 // + 64 up columns).  Wave (rg, cg) owns z columns 32 cg .. +31: gate
-// fragments fn = 0, 1 and the matching up fragments fn = 2, 3.
+// fragments fn = 0, 1 and the matching up fragments fn = 2, 3.  The packing
+// orders each 32 columns so that lane l of fragment f holds column
+// 32 cg + 2 (l % 16) + f: a lane's two z columns of a row are adjacent.
 struct F8G1Src {
     int srow[F8S<false>::A_PW];     // per-lane A source rows, -1: padding
     int sa_row;                     // thread t < CH: source row of tile row t, -1: none
@@ -493,7 +495,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
         float sg[2], su[2], bg[2], bu[2];
 #pragma unroll
         for (int fn = 0; fn < 2; ++fn) {
-            const int n = z0 + cg * 32 + fn * 16 + s16;
+            const int n = z0 + cg * 32 + 2 * s16 + fn;
             sg[fn] = BW ? 1.0f : g.w13_scale[(int64_t)cur.e * N + n];
             su[fn] = BW ? 1.0f : g.w13_scale[(int64_t)cur.e * N + I + n];
             bg[fn] = bu[fn] = 0.0f;
@@ -533,6 +535,7 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
         // tile's first barrier, then 16-byte row stores
         uint8_t* zst = (uint8_t*)(ring + (S::NS - 1) * S::STAGE);           // [CH][128]
         float* amx = (float*)(ring + (S::NS - 1) * S::STAGE + S::CH * 128);  // [CH][4 cg]
+        static_assert(S::CH * 128 + S::CH * 16 + S::NW * 64 * 4 <= S::STAGE, "epilogue LDS");
         // pass 1: z of (strip fm, fragment fn < 2, row r) replaces the gate
         // accumulator (the routing weight is 1 without row weights); mb[v],
         // v = 4 fm + r, is the largest |z| of that row among this lane's two
@@ -584,20 +587,31 @@ __global__ void __launch_bounds__(512, 1) k_gemm1_f8(Gemm1Args g)
                 __uint_as_float(m);
         }
         __syncthreads();
-        // pass 2: the row scale over all 128 z columns, the codes
+        // pass 2: lane i of each lane row forms the scale of value v = i (the
+        // row whose maxima it holds) and passes the reciprocal to its lane row
+        // through the wave's own LDS slots; then the codes, the lane's two
+        // adjacent columns of a row as one 16-bit write
+        float* rcs = amx + S::CH * 4 + wave * 64;                           // [4 g4][16 v]
+        {
+            const int row = rg * S::FMW * 16 + (s16 >> 2) * 16 + g4 * 4 + (s16 & 3);
+            const f32x4 a4 = *(const f32x4*)(amx + row * 4);
+            const float amax = fmaxf(fmaxf(a4[0], a4[1]), fmaxf(a4[2], a4[3]));
+            const float sc = zq_scale(amax);
+            rcs[g4 * 16 + s16] = __builtin_amdgcn_rcpf(sc);
+            if (cg == 0 && row < cur.rows)
+                g.z_scale[(int64_t)cur.ntile * g.zs_ld + cur.r0 + row] = sc;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
         for (int fm = 0; fm < S::FMW; ++fm) {
+            const f32x4 rc = *(const f32x4*)(rcs + g4 * 16 + fm * 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = rg * S::FMW * 16 + fm * 16 + g4 * 4 + r;
-                const f32x4 a4 = *(const f32x4*)(amx + row * 4);
-                const float amax = fmaxf(fmaxf(a4[0], a4[1]), fmaxf(a4[2], a4[3]));
-                const float sc = zq_scale(amax), rc = __builtin_amdgcn_rcpf(sc);
-                const uint32_t q = cvt_fp8x2(acc[fm][0][r] * rc, acc[fm][1][r] * rc);
-                zst[row * 128 + cg * 32 + s16] = (uint8_t)q;
-                zst[row * 128 + cg * 32 + 16 + s16] = (uint8_t)(q >> 8);
-                if (cg == 0 && s16 == 0 && row < cur.rows)
-                    g.z_scale[(int64_t)cur.ntile * g.zs_ld + cur.r0 + row] = sc;
+                *(uint16_t*)(zst + row * 128 + cg * 32 + 2 * s16) =
+                    (uint16_t)cvt_fp8x2(acc[fm][0][r] * rc[r], acc[fm][1][r] * rc[r]);
             }
         }
         __syncthreads();
@@ -774,7 +788,8 @@ __global__ void __launch_bounds__(512, 1) k_gemm2_f8(Gemm2Args g)
 // above.  One thread per 16-byte slot of the output: it gathers 16 K values
 // of one weight column; rows past K and columns past N are zeros.
 //   w13 [E, H, 2I]: block (e, kt, j), kt < ceil(H/128), j < I/64: columns
-//     0-63 = gate columns 64 j .., 64-127 = up columns I + 64 j ..
+//     0-63 = gate columns 64 j .., 64-127 = up columns I + 64 j .., each half
+//     in 32-column groups whose column 16 f + s is the group's column 2 s + f
 //   w2 [E, I, H]: block (e, kt, j), kt < I/128, j < ceil(H/128): columns 128 j ..
 template <bool W13>
 __global__ void __launch_bounds__(256) k_pack_f8(const uint8_t* __restrict__ w, int H, int I,
@@ -793,7 +808,10 @@ __global__ void __launch_bounds__(256) k_pack_f8(const uint8_t* __restrict__ w, 
         int col;
         bool valid;
         if constexpr (W13) {
-            col = (c < 64) ? 64 * j + c : I + 64 * j + (c - 64);
+            // within each 32 columns of a half, block column 16 f + s holds
+            // weight column 2 s + f (see the GEMM1 epilogue)
+            const int h = c & 63, pc = (h & 32) | ((h & 15) << 1) | ((h >> 4) & 1);
+            col = (c < 64) ? 64 * j + pc : I + 64 * j + pc;
             valid = true;
         } else {
             col = 128 * j + c;

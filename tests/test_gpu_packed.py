@@ -119,7 +119,8 @@ def test_packed_batched_bf16():
 def _ref_pack_f8(w, gate_up):
     """The documented fp8 layout, written out with numpy: 16 KiB blocks of 128
     columns x 128 K bytes; column c's 16-byte slot s holds K chunk 2 (p & 3) + (p >> 2),
-    p = s ^ ((c >> 1) & 7)."""
+    p = s ^ ((c >> 1) & 7).  w13 halves: block column 32 h + 16 f + s of a half
+    is the half's column 32 h + 2 s + f."""
     E, K, N = w.shape
     half = N // 2
     nblk = half // 64 if gate_up else -(-N // 128)
@@ -128,7 +129,9 @@ def _ref_pack_f8(w, gate_up):
     for j in range(nblk):
         for c in range(128):
             if gate_up:
-                col = 64 * j + c if c < 64 else half + 64 * j + (c - 64)
+                h = c % 64
+                pc = 32 * (h // 32) + 2 * (h % 16) + (h % 32) // 16
+                col = 64 * j + pc if c < 64 else half + 64 * j + pc
             else:
                 col = 128 * j + c
                 if col >= N:
