@@ -268,7 +268,8 @@ typedef struct {
  *   num_post_padded [1] int32
  *   aq / aq_scale: fp8 activation codes and per-row scales (fp8 weights)
  *   z [max_sorted_len, I]: SiLU(gate)*up per padded row (bf16 or f32; fp8
- *       codes + per-(row, 128-column) float scales z_scale on the fp8 path)
+ *       codes on the fp8 path, with float scales per (row, 128 columns) in
+ *       z_scale [I / 128][max_sorted_len + 256], group-major)
  *   o [max_sorted_len, H] (contiguous, and batched with batched_reduce):
  *       each routed item's expert output at its padded position, float
  *   o2 [max_sorted_len, H]: when the second GEMM runs as two K halves, the

@@ -104,6 +104,9 @@ def load() -> ctypes.CDLL:
     lib.oracle_expert_rows_ties.argtypes = [ctypes.POINTER(_Experts), ctypes.POINTER(_Acts), P,
                                             P, i64, P, i32, ctypes.c_float, P, P]
     lib.oracle_expert_rows_ties.restype = ctypes.c_int
+    lib.oracle_expert_z_codes.argtypes = [ctypes.POINTER(_Experts), ctypes.POINTER(_Acts), P, P,
+                                          i64, ctypes.c_float, P, P, P, i32]
+    lib.oracle_expert_z_codes.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -412,3 +415,23 @@ def expert_rows(experts: Experts, acts: Acts, rows, expert_of_row, nthreads=0, t
     used = lib.oracle_expert_rows(ctypes.byref(experts.s), ctypes.byref(acts.s), r.ctypes.data,
                                   e.ctypes.data, r.size, out.ctypes.data, int(nthreads))
     return out, used
+
+
+def expert_z_codes(experts: Experts, acts: Acts, rows, expert_of_row, tie_window=0.0,
+                   nthreads=0):
+    """The fp8 path's re-quantised z of each (activation row, expert) pair:
+    (codes uint8 [n, I], scales float32 [n, ceil(I/128)], alt int16 [n, I]),
+    alt the other code of a code within tie_window of a rounding tie, else -1."""
+    lib = load()
+    r = _np(rows, np.int64).ravel()
+    e = _np(expert_of_row, np.int32).ravel()
+    assert r.size == e.size
+    I = experts.I
+    G = (I + 127) // 128
+    codes = np.empty((r.size, I), np.uint8)
+    scales = np.empty((r.size, G), np.float32)
+    alt = np.empty((r.size, I), np.int16)
+    lib.oracle_expert_z_codes(ctypes.byref(experts.s), ctypes.byref(acts.s), r.ctypes.data,
+                              e.ctypes.data, r.size, float(tie_window), codes.ctypes.data,
+                              scales.ctypes.data, alt.ctypes.data, int(nthreads))
+    return codes, scales, alt

@@ -588,33 +588,48 @@ typedef struct {
     double dz[ORACLE_MAX_TIES];
 } tie_rec;
 
+/* Codes of one 128-column group of z (n <= 128 values) on the fp8 path: the
+ * group's scale *sc = amax / 448 (1 for an all-zero group) and each code
+ * decided in float32 as the device does, RNE(z / scale).  alt (may be NULL):
+ * with window > 0 the other code of a near-tie code (oracle_fp8_tie_alt),
+ * else -1. */
+static void z_group_codes(const double* z, int64_t n, float window, uint8_t* codes, float* sc,
+                          int16_t* alt)
+{
+    float zf[128], amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        zf[i] = (float)z[i];
+        if (fabsf(zf[i]) > amax)
+            amax = fabsf(zf[i]);
+    }
+    *sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        codes[i] = oracle_fp8_encode(zf[i] / *sc);
+        if (alt)
+            alt[i] = (int16_t)((window > 0.0f) ? oracle_fp8_tie_alt(zf[i] / *sc, window) : -1);
+    }
+}
+
 /* z requantisation for the fp8 path: each 128-column group of a row gets
  * its own scale (the block-wise granularity of the "FP8 W8A8" section);
- * codes are decided in float32 as the device does.  With window > 0 the
- * codes within that relative distance of a rounding tie go into tr. */
+ * z is replaced by its dequantised codes.  With window > 0 the codes within
+ * that relative distance of a rounding tie go into tr. */
 static void requant_z(double* z, int64_t I, float window, tie_rec* tr)
 {
     for (int64_t g0 = 0; g0 < I; g0 += 128) {
-        int64_t n = (I - g0 < 128) ? I - g0 : 128;
-        float zf[128], amax = 0.0f, sc;
+        const int64_t n = (I - g0 < 128) ? I - g0 : 128;
+        uint8_t c[128];
+        int16_t alt[128];
+        float sc;
+        z_group_codes(z + g0, n, (tr ? window : 0.0f), c, &sc, alt);
         for (int64_t i = 0; i < n; ++i) {
-            zf[i] = (float)z[g0 + i];
-            if (fabsf(zf[i]) > amax)
-                amax = fabsf(zf[i]);
-        }
-        sc = (amax > 0.0f) ? amax / 448.0f : 1.0f;
-        for (int64_t i = 0; i < n; ++i) {
-            const uint8_t c = oracle_fp8_encode(zf[i] / sc);
-            z[g0 + i] = fp8_table[c] * (double)sc;
-            if (window > 0.0f && tr) {
-                const int alt = oracle_fp8_tie_alt(zf[i] / sc, window);
-                if (alt >= 0) {
-                    if (tr->n < ORACLE_MAX_TIES) {
-                        tr->k[tr->n] = g0 + i;
-                        tr->dz[tr->n] = (fp8_table[alt] - fp8_table[c]) * (double)sc;
-                    }
-                    tr->n++;
+            z[g0 + i] = fp8_table[c[i]] * (double)sc;
+            if (alt[i] >= 0) {
+                if (tr->n < ORACLE_MAX_TIES) {
+                    tr->k[tr->n] = g0 + i;
+                    tr->dz[tr->n] = (fp8_table[alt[i]] - fp8_table[c[i]]) * (double)sc;
                 }
+                tr->n++;
             }
         }
     }
@@ -651,13 +666,12 @@ static void add_w2_row(const oracle_experts* W, int e, int64_t i, double zi, dou
     }
 }
 
-/* o = f_e(x): h = W13_e^T x + b13_e; z = a * SiLU(h[:I]) * h[I:]; o = W2_e^T z + b2_e.
- * a = zscale: 1, or the routing weight when it is applied to the first
- * layer's output (the walkthrough's apply_router_weight_on_input, sec. 1.2).
- * scratch: h[2I], z[I].  window / tr: near-tie z codes (fp8 path), see
- * requant_z. */
-static void expert_ffn(const oracle_experts* W, int e, const double* x, double* h, double* z,
-                       double* o, double zscale, float window, tie_rec* tr)
+/* h = W13_e^T x + b13_e and z = a * SiLU(h[:I]) * h[I:] of one expert row,
+ * before any requantisation.  a = zscale: 1, or the routing weight when it
+ * is applied to the first layer's output (the walkthrough's
+ * apply_router_weight_on_input, sec. 1.2).  h[2I], z[I]. */
+static void expert_hz(const oracle_experts* W, int e, const double* x, double* h, double* z,
+                      double zscale)
 {
     const int64_t H = W->H, I = W->I, N = 2 * (int64_t)W->I;
 
@@ -699,6 +713,17 @@ static void expert_ffn(const oracle_experts* W, int e, const double* x, double* 
         const double g = h[i], u = h[I + i];
         z[i] = zscale * (g / (1.0 + exp(-g)) * u); /* SiLU(g) = g * sigmoid(g) */
     }
+}
+
+/* o = f_e(x): h and z as expert_hz; on the fp8 path z re-quantised
+ * (requant_z); o = W2_e^T z + b2_e.  scratch: h[2I], z[I].  window / tr:
+ * near-tie z codes (fp8 path), see requant_z. */
+static void expert_ffn(const oracle_experts* W, int e, const double* x, double* h, double* z,
+                       double* o, double zscale, float window, tie_rec* tr)
+{
+    const int64_t H = W->H, I = W->I;
+
+    expert_hz(W, e, x, h, z, zscale);
     if (W->requant_z)
         requant_z(z, I, window, tr);
 
@@ -885,6 +910,52 @@ static int expert_rows(const oracle_experts* W, const oracle_acts* A, const int6
             if (tie_count) {
                 tie_count[n] = tr.n;
                 tie_deltas(W, experts[n], &tr, 1.0, tie_delta + n * ORACLE_MAX_TIES * H, &used);
+            }
+        }
+        free(x);
+        free(xf);
+        free(q);
+        free(h);
+        free(z);
+    }
+    return used;
+}
+
+/* The fp8 path's re-quantised intermediate for any list of (activation row,
+ * expert) pairs (the "FP8 W8A8" section's per-group codes of z): codes[n][I]
+ * and scales[n][ceil(I/128)] as requant_z decides them, and alt[n][I] the
+ * other code of each near-tie code (relative window, oracle_fp8_tie_alt),
+ * else -1.  Returns the thread count used. */
+int oracle_expert_z_codes(const oracle_experts* W, const oracle_acts* A, const int64_t* rows,
+                          const int32_t* experts, int64_t n_rows, float window, uint8_t* codes,
+                          float* scales, int16_t* alt, int32_t nthreads)
+{
+    int used = 1;
+    fp8_table_init();
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel
+    {
+        const int64_t H = W->H, I = W->I, G = (I + 127) / 128;
+        double* x = (double*)malloc(sizeof(double) * H);
+        float* xf = (float*)malloc(sizeof(float) * H);
+        uint8_t* q = (uint8_t*)malloc(H);
+        double* h = (double*)malloc(sizeof(double) * 2 * I);
+        double* z = (double*)malloc(sizeof(double) * I);
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < n_rows; ++n) {
+            load_row(A, H, rows[n], x, xf, q);
+            expert_hz(W, experts[n], x, h, z, 1.0);
+            for (int64_t g = 0; g < G; ++g) {
+                const int64_t g0 = g * 128, m = (I - g0 < 128) ? I - g0 : 128;
+                z_group_codes(z + g0, m, window, codes + n * I + g0, scales + n * G + g,
+                              alt + n * I + g0);
             }
         }
         free(x);

@@ -904,3 +904,50 @@ def test_near_tie_deltas_are_single_code_flips():
         for i in range(min(len(want), MT)):
             assert np.allclose(ties.delta[t, i], want[i].numpy(), rtol=1e-12, atol=1e-15)
     assert ties.count.max() > 0
+
+
+def test_z_codes_match_torch_cast_per_group():
+    """The fp8 path's re-quantised z itself -- codes, group scales and
+    near-tie alternatives of (row, expert) pairs -- against torch: h in
+    float64 from the dequantised operands (per-channel weight scales, b13),
+    z = SiLU(gate) * up cast to float32, each 128-column group (the last one
+    short, I = 320) scaled by amax / 448 and cast to float8_e4m3fn, the
+    alternatives from the casts of t * (1 +- w)."""
+    g = torch.Generator().manual_seed(31)
+    R, H, I, E, win = 6, 64, 320, 3, 1e-2
+    x = _bf(torch.randn(R, H, generator=g))
+    q13 = _fp8(torch.randn(E, H, 2 * I, generator=g) * 8)
+    q2 = _fp8(torch.randn(E, I, H, generator=g) * 8)
+    s13 = (torch.rand(E, 2 * I, generator=g) + 0.01) / 64
+    s2 = torch.rand(E, H, generator=g) + 0.01
+    b13 = torch.randn(E, 2 * I, generator=g) / 4
+    ex = oracle.Experts(q13, q2, s13, s2, b13, None, requant_z=True)
+    acts = oracle.Acts(x, quantize=True)
+    rows = np.array([0, 1, 2, 3, 4, 5, 0, 3])
+    experts = np.array([0, 1, 2, 0, 1, 2, 2, 1])
+    codes, scales, alt = oracle.expert_z_codes(ex, acts, rows, experts, tie_window=win)
+    assert codes.shape == (len(rows), I) and scales.shape == (len(rows), 3)
+    n_alt = 0
+    for n in range(len(rows)):
+        xf = x[rows[n]].float()
+        sx = xf.abs().max() / 448.0
+        xq = (xf / sx).to(torch.float8_e4m3fn).double() * sx.double()
+        e = experts[n]
+        h = xq @ (q13[e].double() * s13[e].double()[None, :]) + b13[e].double()
+        z = (torch.nn.functional.silu(h[:I]) * h[I:]).float()
+        for gi, g0 in enumerate(range(0, I, 128)):
+            blk = z[g0:g0 + 128]
+            sz = blk.abs().max() / 448.0
+            assert scales[n, gi] == np.float32(sz.item())
+            tz = blk / sz
+            c = tz.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            up = (tz * np.float32(1 + win)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            dn = (tz * np.float32(1 - win)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            ref_alt = np.where(up != c, up.astype(np.int64),
+                               np.where(dn != c, dn.astype(np.int64), -1))
+            assert np.array_equal(codes[n, g0:g0 + len(blk)], c)
+            assert np.array_equal(alt[n, g0:g0 + len(blk)], ref_alt)
+            n_alt += int((ref_alt >= 0).sum())
+    assert n_alt > 0                                  # the window finds some near-ties
+    _, _, none = oracle.expert_z_codes(ex, acts, rows, experts)
+    assert (none == -1).all()
