@@ -107,6 +107,9 @@ def load() -> ctypes.CDLL:
     lib.oracle_expert_z_codes.argtypes = [ctypes.POINTER(_Experts), ctypes.POINTER(_Acts), P, P,
                                           i64, ctypes.c_float, P, P, P, i32]
     lib.oracle_expert_z_codes.restype = ctypes.c_int
+    lib.oracle_expert_z.argtypes = [ctypes.POINTER(_Experts), ctypes.POINTER(_Acts), P, P, i64,
+                                    P, i32]
+    lib.oracle_expert_z.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -415,6 +418,19 @@ def expert_rows(experts: Experts, acts: Acts, rows, expert_of_row, nthreads=0, t
     used = lib.oracle_expert_rows(ctypes.byref(experts.s), ctypes.byref(acts.s), r.ctypes.data,
                                   e.ctypes.data, r.size, out.ctypes.data, int(nthreads))
     return out, used
+
+
+def expert_z(experts: Experts, acts: Acts, rows, expert_of_row, nthreads=0):
+    """z = SiLU(gate) * up of each (activation row, expert) pair before any
+    requantisation; float64 [n, I]."""
+    lib = load()
+    r = _np(rows, np.int64).ravel()
+    e = _np(expert_of_row, np.int32).ravel()
+    assert r.size == e.size
+    z = np.empty((r.size, experts.I), np.float64)
+    lib.oracle_expert_z(ctypes.byref(experts.s), ctypes.byref(acts.s), r.ctypes.data,
+                        e.ctypes.data, r.size, z.ctypes.data, int(nthreads))
+    return z
 
 
 def expert_z_codes(experts: Experts, acts: Acts, rows, expert_of_row, tie_window=0.0,

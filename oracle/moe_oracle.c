@@ -966,3 +966,39 @@ int oracle_expert_z_codes(const oracle_experts* W, const oracle_acts* A, const i
     }
     return used;
 }
+
+/* z = a * SiLU(h[:I]) * h[I:] (a = 1) of any list of (activation row,
+ * expert) pairs, before any requantisation: z[n][I].  Returns the thread
+ * count used. */
+int oracle_expert_z(const oracle_experts* W, const oracle_acts* A, const int64_t* rows,
+                    const int32_t* experts, int64_t n_rows, double* zout, int32_t nthreads)
+{
+    int used = 1;
+    fp8_table_init();
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#endif
+#pragma omp parallel
+    {
+        const int64_t H = W->H, I = W->I;
+        double* x = (double*)malloc(sizeof(double) * H);
+        float* xf = (float*)malloc(sizeof(float) * H);
+        uint8_t* q = (uint8_t*)malloc(H);
+        double* h = (double*)malloc(sizeof(double) * 2 * I);
+#ifdef _OPENMP
+#pragma omp single
+        used = omp_get_num_threads();
+#endif
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < n_rows; ++n) {
+            load_row(A, H, rows[n], x, xf, q);
+            expert_hz(W, experts[n], x, h, zout + n * I, 1.0);
+        }
+        free(x);
+        free(xf);
+        free(q);
+        free(h);
+    }
+    return used;
+}

@@ -30,6 +30,27 @@ TOL_WEIGHT = 1e-5          # routing weights, relative to max(1, routed_scaling_
 TIE_WINDOW = 1e-4
 # WNA16 (u8 / u4 codes, bf16 activations) is held to the bf16 bound
 WQ_BITS = {"u8": 8, "u4": 4}
+# z, the intermediate the first GEMM writes, read back from the workspace and
+# compared with the oracle's z (before any requantisation).  float32 / bf16 z:
+# within Z_REL of its own magnitude (bf16: one ulp, 2^-7 at the start of a
+# binade; the storage rounding takes up to half of it, and a z the device
+# forms in float32 next to a rounding midpoint may round to the other
+# neighbour) plus Z_RMS of its row's RMS (the device sums the products in
+# float32, and where they cancel h keeps only their absolute error).  fp8 z:
+# see check_z_codes.  (WNA16's 160-row tile rounds the dequantised weights to
+# bf16 before its MFMAs, a difference of the operands rather than of the
+# arithmetic; its z is checked through the outputs only.)
+Z_REL = {2: 2.0 ** -7, 4: 1e-5}
+Z_RMS = 1e-3
+# fp8 z: the group scales within Z_SCALE_RTOL; every code the oracle's or one
+# E4M3FN step from it (plus Z_ABS_TOL in code units, for the subnormal codes
+# of values below about 3e-5 of the group's amax), and at most Z_MAX_FRAC of
+# all codes (Z_MAX_ITEM_FRAC of one item's) differing.  A wrong column, row,
+# group, scale, bias or gate / up order moves most codes by many steps.
+Z_SCALE_RTOL = 2e-4
+Z_ABS_TOL = 0.01
+Z_MAX_FRAC = 0.01
+Z_MAX_ITEM_FRAC = 0.05
 
 
 # Named tile families for the tests (moe_problem.tile_hint / gemm1_wave_cols).
@@ -350,6 +371,78 @@ def expert_output_rows(ws, info, positions, H, dev) -> np.ndarray:
     return got.cpu().numpy()
 
 
+def _z_elem_bytes(cfg) -> int:
+    return 1 if cfg.weight == "fp8" else (4 if cfg.act == "f32" else 2)
+
+
+def z_rows(ws, info, cfg, positions, dev) -> np.ndarray:
+    """The workspace's z rows at padded positions: fp8 codes (uint8), else
+    float values."""
+    I, es = cfg.I, _z_elem_bytes(cfg)
+    raw = ws[info.off_z:info.off_z + info.max_sorted_len * I * es]
+    dt = {1: torch.uint8, 2: torch.bfloat16, 4: torch.float32}[es]
+    z = raw.view(dt).view(info.max_sorted_len, I)[torch.as_tensor(positions, device=dev)]
+    return z.cpu().numpy() if es == 1 else z.float().cpu().numpy()
+
+
+def _fp8_decode(c):
+    return torch.from_numpy(np.ascontiguousarray(c)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _fp8_step(v):
+    """The E4M3FN spacing at magnitude v (2^-9 below the normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -6)))
+    return 2.0 ** (e - 3)
+
+
+def check_z_codes(inp, ws, info, acts, rows, experts, positions, dev, what):
+    """fp8 path: the z codes and group scales at `positions` against the
+    oracle's for (activation row, expert) pairs (rows, experts)."""
+    cfg = inp["cfg"]
+    I = cfg.I
+    G = I // 128
+    zs_ld = info.max_sorted_len + 256                    # group-major [I/128][zs_ld]
+    sall = region(ws, info.off_z_scale, torch.float32, G * zs_ld).reshape(G, zs_ld)
+    codes, scales, alt = oracle.expert_z_codes(oracle_experts(inp), acts, rows, experts,
+                                               tie_window=TIE_WINDOW)
+    got = z_rows(ws, info, cfg, positions, dev)
+    got_s = sall[:, positions].T
+    srel = np.abs(got_s.astype(np.float64) / scales - 1.0).max()
+    assert srel <= Z_SCALE_RTOL, f"{what}: z scales differ by {srel:.2e} relative"
+    t_or, t_dev = _fp8_decode(codes), _fp8_decode(got)
+    diff = got != codes
+    far = np.abs(t_dev - t_or) > _fp8_step(np.maximum(np.abs(t_or), np.abs(t_dev))) + Z_ABS_TOL
+    ties = int((diff & (alt >= 0) & (got.astype(np.int16) == alt)).sum())
+    print(f"[z] {what}: {got.size} codes, {int(diff.sum())} differ ({ties} of them at "
+          f"reported near-ties, {int((alt >= 0).sum())} reported), scale rel {srel:.1e}",
+          flush=True)
+    bad = np.argwhere(far)
+    assert bad.size == 0, (f"{what}: {len(bad)} z codes more than a step off, first (item, "
+                           f"column) {bad[:5].tolist()}")
+    assert diff.mean() <= Z_MAX_FRAC, f"{what}: {diff.mean():.3%} of the codes differ"
+    worst = diff.mean(axis=1).max()
+    assert worst <= Z_MAX_ITEM_FRAC, f"{what}: {worst:.3%} of one item's codes differ"
+
+
+def check_z(inp, ws, info, acts, rows, experts, positions, dev, what):
+    """z at `positions` against the oracle's z of (activation row, expert)
+    pairs; fp8 codes through check_z_codes; WNA16 not compared (see Z_RMS)."""
+    cfg = inp["cfg"]
+    if cfg.weight in WQ_BITS:
+        return
+    if cfg.weight == "fp8":
+        check_z_codes(inp, ws, info, acts, rows, experts, positions, dev, what)
+        return
+    ref = oracle.expert_z(oracle_experts(inp), acts, rows, experts)
+    got = z_rows(ws, info, cfg, positions, dev)
+    rms = np.sqrt(np.mean(ref ** 2, axis=1, keepdims=True))
+    tol = Z_REL[_z_elem_bytes(cfg)] * np.abs(ref) + Z_RMS * rms
+    ratio = np.abs(got - ref) / tol
+    print(f"[z] {what}: {got.size} values, max error {ratio.max():.3f} of the bound", flush=True)
+    bad = np.argwhere(ratio > 1.0)
+    assert bad.size == 0, f"{what}: {len(bad)} z values off, first (item, column) {bad[:5].tolist()}"
+
+
 def check_tiles_contiguous(inp, ws, info, dev, E_local=None):
     """Every (expert, row chunk) tile of a contiguous forward: the expert
     outputs of its first and last rows against the oracle's expert FFN of
@@ -369,6 +462,8 @@ def check_tiles_contiguous(inp, ws, info, dev, E_local=None):
     print(f"[tiles] {cfg.name}: {len(pos)} item rows over chunks {nch} of "
           f"{int((counts > 0).sum())} experts", flush=True)
     acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8", block=cfg.fp8_block)
+    check_z(inp, ws, info, acts, tokens, experts.astype(np.int32), pos, dev,
+            "z rows of every tile")
     ref, ties = ref_rows(inp, acts, tokens, experts.astype(np.int32))
     got = expert_output_rows(ws, info, pos, cfg.H, dev)
     compare(cfg, got, ref, "expert rows of every tile", ties=ties)
@@ -391,6 +486,8 @@ def check_tiles_batched(inp, ws, info, out, dev):
     acts = oracle.Acts(inp["hidden"].cpu(), scale=_cpu(inp.get("a_scale")),
                        quantize=cfg.weight == "fp8" and inp["hidden"].dtype != torch.float8_e4m3fn,
                        block=cfg.fp8_block)
+    check_z(inp, ws, info, acts, rows, experts.astype(np.int32), pos, dev,
+            "z rows of every tile")
     ref, ties = ref_rows(inp, acts, rows, experts.astype(np.int32))
     got = out.reshape(-1, cfg.H)[torch.as_tensor(rows, device=dev)].float().cpu().numpy()
     compare(cfg, got, ref, "slab rows of every tile", ties=ties)

@@ -951,3 +951,37 @@ def test_z_codes_match_torch_cast_per_group():
     assert n_alt > 0                                  # the window finds some near-ties
     _, _, none = oracle.expert_z_codes(ex, acts, rows, experts)
     assert (none == -1).all()
+
+
+def test_expert_z_matches_torch_float64():
+    """The intermediate z = SiLU(gate) * up of (row, expert) pairs, before any
+    requantisation, against torch float64 from the same operands: bf16
+    weights with b13, and per-channel fp8 weights on quantised rows."""
+    g = torch.Generator().manual_seed(32)
+    R, H, I, E = 5, 64, 96, 3
+    x = _bf(torch.randn(R, H, generator=g))
+    rows = np.array([0, 1, 2, 3, 4, 2])
+    experts = np.array([0, 1, 2, 2, 0, 1])
+    W13 = _bf(torch.randn(E, H, 2 * I, generator=g) / 8)
+    b13 = _bf(torch.randn(E, 2 * I, generator=g) / 4)
+    W2 = _bf(torch.randn(E, I, H, generator=g) / 8)
+    z = oracle.expert_z(oracle.Experts(W13, W2, None, None, b13, None), oracle.Acts(x),
+                        rows, experts)
+    for n in range(len(rows)):
+        e = experts[n]
+        h = x[rows[n]].double() @ W13[e].double() + b13[e].double()
+        ref = torch.nn.functional.silu(h[:I]) * h[I:]
+        assert np.allclose(z[n], ref.numpy(), rtol=1e-12, atol=1e-14)
+    q13 = _fp8(torch.randn(E, H, 2 * I, generator=g) * 8)
+    s13 = (torch.rand(E, 2 * I, generator=g) + 0.01) / 64
+    q2 = _fp8(torch.randn(E, I, H, generator=g) * 8)
+    zq = oracle.expert_z(oracle.Experts(q13, q2, s13, torch.ones(E, H), requant_z=True),
+                         oracle.Acts(x, quantize=True), rows, experts)
+    for n in range(len(rows)):
+        e = experts[n]
+        xf = x[rows[n]].float()
+        sx = xf.abs().max() / 448.0
+        xq = (xf / sx).to(torch.float8_e4m3fn).double() * sx.double()
+        h = xq @ (q13[e].double() * s13[e].double()[None, :])
+        ref = torch.nn.functional.silu(h[:I]) * h[I:]      # before the requantisation
+        assert np.allclose(zq[n], ref.numpy(), rtol=1e-12, atol=1e-14)
