@@ -51,7 +51,8 @@ class _Experts(ctypes.Structure):
                 ("bias_dtype", ctypes.c_int32), ("w13_bias", ctypes.c_void_p),
                 ("w2_bias", ctypes.c_void_p), ("requant_z", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("group", ctypes.c_int32),
-                ("w13_zero", ctypes.c_void_p), ("w2_zero", ctypes.c_void_p)]
+                ("w13_zero", ctypes.c_void_p), ("w2_zero", ctypes.c_void_p),
+                ("wq_bf16", ctypes.c_int32), ("z_bf16", ctypes.c_int32)]
 
 
 class _Acts(ctypes.Structure):
@@ -285,10 +286,15 @@ class Experts:
     WNA16 (bits 8 or 4): unsigned codes, w13 [E, H, 2I] / w2 [E, I, H] bytes
     (bits 4: two per byte along the last dim, even column in the low nibble,
     so [E, H, I] / [E, I, H/2]); scales [E, ceil(K/group), N] float; zero
-    points the same shape as uint8, or None for 2^(bits-1)."""
+    points the same shape as uint8, or None for 2^(bits-1).  wq_bf16: the
+    dequantised weights (q - z) s formed in float32 and rounded to bf16 (the
+    reading in which the dequantised weight is the compute type), instead of
+    exact.  z_bf16: z held in bf16 before the second GEMM (without
+    requant_z)."""
 
     def __init__(self, w13, w2, w13_scale=None, w2_scale=None, w13_bias=None, w2_bias=None,
-                 requant_z=False, block=0, bits=0, group=128, w13_zero=None, w2_zero=None):
+                 requant_z=False, block=0, bits=0, group=128, w13_zero=None, w2_zero=None,
+                 wq_bf16=False, z_bf16=False):
         self.w13, self.w2 = _np(w13), _np(w2)
         E, H, N = self.w13.shape
         if bits == 4:
@@ -325,7 +331,7 @@ class Experts:
         self.s = _Experts(H, I, E, wd, _ptr(self.w13), _ptr(self.w2), _ptr(self.w13_scale),
                           _ptr(self.w2_scale), bias_dt, _ptr(self.b13), _ptr(self.b2),
                           int(requant_z), int(block), int(group), _ptr(self.z13),
-                          _ptr(self.z2))
+                          _ptr(self.z2), int(wq_bf16), int(z_bf16))
         self.H, self.I, self.E = H, I, E
 
 

@@ -402,6 +402,11 @@ typedef struct {
     int32_t group;            /* OR_U8 / OR_U4: K rows per scale group          */
     const uint8_t* w13_zero;  /* OR_U8 / OR_U4: [E][ceil(H/group)][2I] or NULL  */
     const uint8_t* w2_zero;   /*   [E][ceil(I/group)][H] or NULL (2^(bits-1))   */
+    int32_t wq_bf16;          /* OR_U8 / OR_U4: 0 the exact weight (q - z) s;   */
+                              /*   1 that weight formed in float32, then rounded */
+                              /*   to bf16 (the compute type)                    */
+    int32_t z_bf16;           /* 1: z is held in bf16 (the compute type) before */
+                              /*   the second GEMM (without requant_z)          */
 } oracle_experts;
 
 /* WNA16 weight codes: OR_U8 one unsigned byte per weight, [E][K][N];
@@ -416,13 +421,32 @@ static int wq_code(const oracle_experts* W, const void* w, int64_t row, int64_t 
 }
 
 /* Dequantised WNA16 weight (k, n) of expert e: (q - z) * s of its K group. */
+/* x rounded to the nearest bf16, ties to even (finite x). */
+static double round_bf16(float x)
+{
+    uint32_t b;
+    memcpy(&b, &x, 4);
+    b = (b + 0x7fffu + ((b >> 16) & 1u)) & 0xffff0000u;
+    memcpy(&x, &b, 4);
+    return (double)x;
+}
+
+/* Dequantised WNA16 weight (FlagGems walkthrough, "WNA16" section: group
+ * scales and zero points; its "fused_experts_impl" section, special
+ * quantisation formats: the public entry dequantises the codes to
+ * hidden_states.dtype before the generic kernel runs).  wq_bf16 selects that
+ * reading, (q - z) s in float32 rounded to bf16; without it the weight is
+ * exact. */
 static double wq_weight(const oracle_experts* W, const void* w, const float* scale,
                         const uint8_t* zero, int e, int64_t K, int64_t N, int64_t k, int64_t n)
 {
     const int64_t G = W->group, ng = (K + G - 1) / G;
     const int64_t gi = ((int64_t)e * ng + k / G) * N + n;
     const int z = zero ? zero[gi] : (W->w_dtype == OR_U8 ? 128 : 8);
-    return (double)(wq_code(W, w, (int64_t)e * K + k, N, n) - z) * (double)scale[gi];
+    const int q = wq_code(W, w, (int64_t)e * K + k, N, n);
+    if (W->wq_bf16)
+        return round_bf16((float)(q - z) * scale[gi]);
+    return (double)(q - z) * (double)scale[gi];
 }
 
 /* GPTQ and AWQ checkpoints ship WNA16 codes packed into int32 words
@@ -716,7 +740,9 @@ static void expert_hz(const oracle_experts* W, int e, const double* x, double* h
 }
 
 /* o = f_e(x): h and z as expert_hz; on the fp8 path z re-quantised
- * (requant_z); o = W2_e^T z + b2_e.  scratch: h[2I], z[I].  window / tr:
+ * (requant_z), with z_bf16 z held in bf16 (the walkthrough's
+ * "fused_experts_impl" keeps the activation output, intermediate_cache2, in
+ * the compute type); o = W2_e^T z + b2_e.  scratch: h[2I], z[I].  window / tr:
  * near-tie z codes (fp8 path), see requant_z. */
 static void expert_ffn(const oracle_experts* W, int e, const double* x, double* h, double* z,
                        double* o, double zscale, float window, tie_rec* tr)
@@ -726,6 +752,9 @@ static void expert_ffn(const oracle_experts* W, int e, const double* x, double* 
     expert_hz(W, e, x, h, z, zscale);
     if (W->requant_z)
         requant_z(z, I, window, tr);
+    else if (W->z_bf16)
+        for (int64_t i = 0; i < I; ++i)
+            z[i] = round_bf16((float)z[i]);
 
     for (int64_t c = 0; c < H; ++c)
         o[c] = 0.0;

@@ -1,9 +1,11 @@
 """WNA16 (8- and 4-bit weight codes with group scales and zero points, bf16
 activations) against the CPU oracle, and the packed code layout bit for bit.
 
-Outputs within the bf16 bound (2e-2 x RMS of the oracle's double result):
-the GEMMs dequantise each weight to bf16, which is the precision of the bf16
-path's weights; routing and align bit for bit as everywhere else."""
+Outputs within the bf16 bound (2e-2 x RMS of the oracle's double result),
+against the oracle fed the weights the path computes with: the exact
+dequantised weights (small-row tiles) or those weights in bf16 (the 160-row
+tile); gpu_harness.Readings holds both and the closer one is taken.  Routing
+and align bit for bit as everywhere else."""
 import numpy as np
 import pytest
 import torch
@@ -69,10 +71,9 @@ def test_wna16_batched():
     out, ws, info = GH.run_batched(inp, dev, out_dtype=torch.float32)
     GH.check_batched_tilelist(inp, ws, info)
     rows, experts = GH.batched_rows(inp)
-    ref, _ = oracle.expert_rows(GH.oracle_experts(inp), oracle.Acts(inp["hidden"].cpu()), rows,
-                                experts)
+    ref, alt = GH.ref_rows(inp, oracle.Acts(inp["hidden"].cpu()), rows, experts)
     got = out.reshape(-1, cfg.H)[torch.as_tensor(rows, device=out.device)]
-    GH.compare(cfg, got.cpu().numpy(), ref, "batched w4")
+    GH.compare(cfg, got.cpu().numpy(), ref, "batched w4", ties=alt)
 
 
 def _fragment_order(codes, bits, w13, H, I):

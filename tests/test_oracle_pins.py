@@ -597,6 +597,82 @@ def test_wna16_equals_dequantised_product(bits, zero, G):
     assert np.allclose(y, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("bits,zero,G", [(8, False, 32), (4, True, 128), (8, True, 64)])
+def test_wna16_bf16_dequant_reading(bits, zero, G):
+    """The reading in which each dequantised WNA16 weight is the compute type:
+    (q - z) s formed in float32, then rounded to bf16 -- against torch's
+    float32 product and bfloat16 cast, then a float64 dense FFN; and the
+    reading differs from the exact one."""
+    g = torch.Generator().manual_seed(60 + bits + int(zero) + G)
+    M, H, I, E = 5, 208, 192, 3
+    hi = 2 ** bits
+    x = _bf(torch.randn(M, H, generator=g))
+    q13 = torch.randint(0, hi, (E, H, 2 * I), generator=g)
+    q2 = torch.randint(0, hi, (E, I, H), generator=g)
+    s13 = (torch.rand(E, -(-H // G), 2 * I, generator=g) + 0.5) / (hi * 8)
+    s2 = (torch.rand(E, -(-I // G), H, generator=g) + 0.5) / (hi * 8)
+    z13 = torch.randint(0, hi, s13.shape, generator=g).to(torch.uint8) if zero else None
+    z2 = torch.randint(0, hi, s2.shape, generator=g).to(torch.uint8) if zero else None
+
+    def pack(q):
+        q = q.to(torch.uint8)
+        return q if bits == 8 else (q[..., 0::2] | (q[..., 1::2] << 4))
+
+    def deq_bf16(codes, scale, zero_pts, K, N):
+        c = torch.as_tensor(codes).to(torch.int64)
+        if bits == 4:
+            c = torch.stack([c & 15, c >> 4], dim=-1).reshape(*c.shape[:-1], N)
+        z = (torch.full(scale.shape, 2 ** (bits - 1), dtype=torch.int64) if zero_pts is None
+             else zero_pts.to(torch.int64))
+        zk = z.repeat_interleave(G, dim=-2)[..., :K, :]
+        sk = scale.float().repeat_interleave(G, dim=-2)[..., :K, :]
+        return ((c - zk).float() * sk).to(torch.bfloat16).double()
+
+    ids, w = oracle.route(torch.randn(M, E, generator=g), 2, renormalize=True)
+    kw = dict(bits=bits, group=G, w13_zero=z13, w2_zero=z2)
+    y, _ = oracle.forward_tokens(oracle.Experts(pack(q13), pack(q2), s13, s2, wq_bf16=True, **kw),
+                                 oracle.Acts(x), ids, w)
+    y_exact, _ = oracle.forward_tokens(oracle.Experts(pack(q13), pack(q2), s13, s2, **kw),
+                                       oracle.Acts(x), ids, w)
+    d13 = deq_bf16(pack(q13), s13, z13, H, 2 * I)
+    d2 = deq_bf16(pack(q2), s2, z2, I, H)
+    ref = np.zeros((M, H))
+    for t in range(M):
+        for j in range(2):
+            e = ids[t, j]
+            ref[t] += w[t, j] * _dense_ffn(x[t:t + 1].double(), d13[e], d2[e]).numpy()[0]
+    assert np.allclose(y, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+    assert not np.allclose(y, y_exact, rtol=1e-6, atol=0)
+
+
+def test_z_held_in_bf16_reading():
+    """z_bf16: z is rounded to bf16 (via float32) before the second GEMM, as
+    the walkthrough's intermediate cache in the compute type holds it --
+    against a torch float64 rebuild with the same casts; it differs from the
+    unrounded reading."""
+    g = torch.Generator().manual_seed(61)
+    M, H, I, E = 5, 64, 96, 3
+    x = _bf(torch.randn(M, H, generator=g))
+    W13 = _bf(torch.randn(E, H, 2 * I, generator=g) / 8)
+    W2 = _bf(torch.randn(E, I, H, generator=g) / 8)
+    b13 = _bf(torch.randn(E, 2 * I, generator=g) / 4)
+    b2 = _bf(torch.randn(E, H, generator=g) / 4)
+    ids, w = oracle.route(torch.randn(M, E, generator=g), 2, renormalize=True)
+    y, _ = oracle.forward_tokens(oracle.Experts(W13, W2, None, None, b13, b2, z_bf16=True),
+                                 oracle.Acts(x), ids, w)
+    y0, _ = oracle.forward_tokens(oracle.Experts(W13, W2, None, None, b13, b2),
+                                  oracle.Acts(x), ids, w)
+    ref = np.zeros((M, H))
+    for t in range(M):
+        for j in range(2):
+            e = ids[t, j]
+            h = x[t].double() @ W13[e].double() + b13[e].double()
+            z = (torch.nn.functional.silu(h[:I]) * h[I:]).float().to(torch.bfloat16).double()
+            ref[t] += w[t, j] * (z @ W2[e].double() + b2[e].double()).numpy()
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-13)
+    assert not np.allclose(y, y0, rtol=1e-6, atol=0)
+
+
 def test_wna16_int4_nibble_order_and_default_zero():
     """A hand-made int4 expert: one K row whose byte 0x5A holds column 0 = 10
     (low nibble) and column 1 = 5 (high nibble); with the default zero point
