@@ -18,7 +18,7 @@ from mixture_experts_ffn_router_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_CASES = 160
 
 
 def draw(i: int) -> tuple:
