@@ -490,6 +490,19 @@ def check_z(inp, ws, info, acts, rows, experts, positions, dev, what):
     assert bad.size == 0, f"{what}: {len(bad)} z values off, first (item, column) {bad[:5].tolist()}"
 
 
+def check_z_all_contiguous(inp, ws, info, ids_o, dev, what):
+    """check_z over every routed item of a contiguous forward (its padded
+    position, token and expert from the workspace's sorted ids)."""
+    cfg = inp["cfg"]
+    npp = int(region(ws, info.off_num_post_padded, torch.int32, 1)[0])
+    sorted_ids = region(ws, info.off_sorted_ids, torch.int32, npp)
+    pos = np.nonzero(sorted_ids < cfg.M * cfg.top_k)[0]
+    r = sorted_ids[pos]
+    tokens, experts = (r // cfg.top_k).astype(np.int64), ids_o.reshape(-1)[r]
+    acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8", block=cfg.fp8_block)
+    check_z(inp, ws, info, acts, tokens, experts.astype(np.int32), pos, dev, what)
+
+
 def check_tiles_contiguous(inp, ws, info, dev, E_local=None):
     """Every (expert, row chunk) tile of a contiguous forward: the expert
     outputs of its first and last rows against the oracle's expert FFN of

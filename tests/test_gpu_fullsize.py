@@ -48,6 +48,7 @@ def test_full_size_contiguous(cfg):
     print(f"[case] {cfg.name} active experts={int((counts > 0).sum())} "
           f"rows/expert max={counts.max()} min={counts.min()}", flush=True)
     if cfg.M <= 64:
+        GH.check_z_all_contiguous(inp, ws, info, ids_o, dev, "full, every item's z")
         GH.check_output(inp, out, ids_o, w_o, what="full")
     else:
         item_tokens = GH.check_tiles_contiguous(inp, ws, info, dev)

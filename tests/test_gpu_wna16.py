@@ -145,6 +145,7 @@ def test_wna16_full_size_decode(name):
     inp = W.make_inputs(cfg, seed, device=dev)
     out, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32)
     ids_o, w_o = GH.check_routing_and_align(inp, ws, info)
+    GH.check_z_all_contiguous(inp, ws, info, ids_o, dev, "full wna16, every item's z")
     GH.check_output(inp, out, ids_o, w_o, what="full wna16")
 
 

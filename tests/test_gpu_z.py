@@ -39,13 +39,7 @@ def test_z_contiguous(case):
     inp = W.make_inputs(cfg, 4100 + CONTIG.index(case))
     _, ws, info = GH.run_contiguous(inp, dev, out_dtype=torch.float32, packed=packed)
     ids_o, _ = GH.check_routing_and_align(inp, ws, info)
-    npp = int(GH.region(ws, info.off_num_post_padded, torch.int32, 1)[0])
-    sorted_ids = GH.region(ws, info.off_sorted_ids, torch.int32, npp)
-    pos = np.nonzero(sorted_ids < cfg.M * cfg.top_k)[0]
-    r = sorted_ids[pos]
-    tokens, experts = (r // cfg.top_k).astype(np.int64), ids_o.reshape(-1)[r]
-    acts = oracle.Acts(inp["hidden"].cpu(), quantize=cfg.weight == "fp8", block=cfg.fp8_block)
-    GH.check_z(inp, ws, info, acts, tokens, experts, pos, dev, cfg.name)
+    GH.check_z_all_contiguous(inp, ws, info, ids_o, dev, cfg.name)
 
 
 @pytest.mark.parametrize("weight", ["fp8", "bf16"])
