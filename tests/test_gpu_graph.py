@@ -28,6 +28,12 @@ CASES = [
     ("fp8_contiguous", W.MIXTRAL_PREFILL.scaled(name="g_fp8", M=200, H=256, I=256,
                                                 weight="fp8")),
     ("batched_fp8_reduce", W.BATCHED_FP8.scaled(name="g_batched", M=96, H=256, I=256, E=8)),
+    ("fp8_block_packed", W.MIXTRAL_PREFILL.scaled(name="g_fp8_block", M=160, H=256, I=256,
+                                                  E=8, weight="fp8", fp8_block=128)),
+    ("wna16_u4_decode", W.DECODE_SMALL_EXPERTS.scaled(name="g_w4", M=8, H=256, I=256, E=32,
+                                                      top_k=4, weight="u4", wq_zero=True)),
+    ("wna16_u8_g32_prefill", W.MIXTRAL_PREFILL.scaled(name="g_w8", M=400, H=256, I=256, E=4,
+                                                      weight="u8", wq_group=32, bias=True)),
 ]
 
 
@@ -45,6 +51,14 @@ def _problem_and_args(inp, dev):
         return t
 
     w13, w2 = d(inp["w13"]), d(inp["w2"])
+    bits = GH.WQ_BITS.get(cfg.weight, 0)
+    if bits or cfg.fp8_block:              # WNA16 codes and block-wise fp8 run packed
+        pw = B.pack_weights(w13, w2, wq_bits=bits)
+        torch.cuda.synchronize()
+        w13, w2, wdt, layout = pw.w13, pw.w2, pw.w_dtype, B.MOE_W_PACKED
+        keep += [w13, w2]
+    else:
+        wdt, layout = B._dtype_code(w13), B.MOE_W_PLAIN
     out_dt = torch.float32
     if cfg.fmt == "batched":
         hidden = d(inp["hidden"])
@@ -62,7 +76,8 @@ def _problem_and_args(inp, dev):
         hidden = d(inp["hidden"])
         logits = d(inp["logits"])
         prob = B.Problem(M=cfg.M, H=cfg.H, I=cfg.I, E=cfg.E, top_k=cfg.top_k,
-                         act_dtype=B._dtype_code(hidden), w_dtype=B._dtype_code(w13),
+                         act_dtype=B._dtype_code(hidden), w_dtype=wdt, w_layout=layout,
+                         fp8_block=cfg.fp8_block, wq_group=cfg.wq_group if bits else 0,
                          out_dtype=B._dtype_code(torch.empty(0, dtype=out_dt)),
                          logits_dtype=B._dtype_code(logits),
                          routing=B.MOE_ROUTE_SIGMOID if cfg.scoring == "sigmoid"
@@ -75,7 +90,8 @@ def _problem_and_args(inp, dev):
         out = torch.empty(cfg.M, cfg.H, dtype=out_dt, device=dev)
         args = B.make_args(hidden, w13, w2, out, router_logits=logits,
                            w13_bias=d(inp["w13_bias"]), w2_bias=d(inp["w2_bias"]),
-                           w13_scale=d(inp.get("w13_scale")), w2_scale=d(inp.get("w2_scale")))
+                           w13_scale=d(inp.get("w13_scale")), w2_scale=d(inp.get("w2_scale")),
+                           w13_zero=d(inp.get("w13_zero")), w2_zero=d(inp.get("w2_zero")))
     return prob, args, out, keep
 
 
