@@ -35,6 +35,11 @@ CONTIGUOUS = [
                                                  weight="fp8"), dict(packed=True)),
     ("w4a16_zero", W.DECODE_SMALL_EXPERTS.scaled(name="chk_w4", M=8, H=320, I=256, E=32,
                                                  top_k=4, weight="u4", wq_zero=True), {}),
+    ("w8a16_g32_dma160", W.MIXTRAL_PREFILL.scaled(name="chk_w8", M=400, H=256, I=256, E=4,
+                                                  weight="u8", wq_group=32, bias=True),
+     GH.tile_kwargs("dma160")),
+    ("fp8_block", W.MIXTRAL_PREFILL.scaled(name="chk_fp8_block", M=300, H=208, I=256, E=4,
+                                           weight="fp8", fp8_block=128, bias=True), {}),
 ]
 
 
