@@ -15,7 +15,7 @@ from mixture_experts_ffn_router_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 40
+N_CASES = 80
 
 
 def draw(i: int) -> W.MoeConfig:
